@@ -1,0 +1,200 @@
+"""Prefill attention of the oracle: block-scaled QK^T, FP8 P and V, bf16 selected tiles.
+
+TEST INFRASTRUCTURE: only the tests, the smoke check and the benchmark's
+CPU-baseline leg may use this module. Shares no code with the GPU path.
+
+Sources:
+  * "MpFA QK4V8" (hotelren.com 6111405) sections 2.1-2.2 and 3.2-3.3: QK^T in
+    4-bit with the per-group scales applied inside the product, V in 8-bit,
+    softmax running max and sum kept in FP32 (here: float64 throughout).
+  * "ThriftAttention" (ai-feeds.com summary), Method step 3: selected tiles are
+    computed in high precision, the others in FP4, and both are merged through
+    one online-softmax running max and sum.
+  * "BitDecoding-FP4" (sns.style digest): the probabilities are quantized with
+    a scale kept safe from underflow (here one scale per query row and
+    128-key tile, taken from that tile's own row maximum).
+  * "General notes on quantization" (zdszero), GEMM factoring: a low-precision
+    product rescaled by the product of the operand scales; merging two scales
+    into one (used to fold V's per-token scale into P).
+
+Computation per (batch b, query head h, query row r), key head kv = h // (Hq/Hkv),
+offset off = Lk - Lq (query r sits at key position off + r), scale = 1/sqrt(d),
+tiles of 128 keys; column c of tile j is unmasked when not causal or c <= r + off:
+  1. S_rc = scale * sum_d q~_rd k~_cd with the dequantized quantized Q/K, or
+     with the original bf16 Q/K when tile j is selected.
+  2. m~_rj = max of S_rc over the unmasked columns of tile j; P'_rc = exp(S_rc - m~_rj)
+     (0 for masked columns).
+  3. Unselected tile: sigma_j = max of s_v over the tile's keys, w_c = 448 s_v[c] / sigma_j,
+     P^_rc = E4M3(P'_rc w_c) (one rounding from the float64 value),
+     T_rj = (sigma_j / 448) sum_c P^_rc E4M3value(Vcode_c).
+     Selected tile: T_rj = sum_c bf16(P'_rc) v_c with the original bf16 V.
+  4. m_r = max_j m~_rj, D_r = sum_j e^(m~_rj - m_r) sum_c P'_rc (unquantized P'),
+     N_r = sum_j e^(m~_rj - m_r) T_rj; O_r = N_r / D_r (returned as float32),
+     LSE_r = m_r + ln D_r.
+Because P' and P^ depend only on their own tile's maximum, the result does not
+depend on the order in which tiles are visited; `attend_rows_online` computes
+the same thing with a running maximum and sum.
+"""
+import numpy as np
+
+from .formats import E4M3_MAX, bf16_round, e4m3_decode, e4m3_encode, fp32
+
+TILE = 128
+
+
+def _tile_terms(S, unmasked, sel, vq_vals, s_v, v_orig, round_p=True):
+    """Per-row (m~, sum P', T) of one key tile. S: [R, n] float64 scores (already scaled)."""
+    S = np.where(unmasked, S, -np.inf)
+    has = unmasked.any(axis=1)
+    m = np.where(has, S.max(axis=1, initial=-np.inf), 0.0)
+    P = np.where(unmasked, np.exp(S - m[:, None]), 0.0)
+    l = P.sum(axis=1)
+    if sel:
+        Pt = bf16_round(P) if round_p else P
+        T = Pt @ v_orig
+    else:
+        sigma = float(np.max(s_v))
+        w = E4M3_MAX * s_v.astype(np.float64) / sigma
+        Pw = P * w[None, :]
+        Ph = e4m3_decode(e4m3_encode(Pw)) if round_p else Pw
+        T = (sigma / E4M3_MAX) * (Ph @ vq_vals)
+    return np.where(has, m, -np.inf), l, T
+
+
+def _row_tiles(rows, Lq, Lk, causal, tile=TILE):
+    """Key tiles visited by a group of rows from one q-tile (those holding an unmasked pair)."""
+    off = Lk - Lq
+    nk = Lk // tile
+    i = rows[0] // tile
+    if not causal:
+        return list(range(nk))
+    return [j for j in range(nk) if tile * j <= off + tile * i + tile - 1]
+
+
+def attend_rows(rows, q_rows, k_deq, v_codes, s_v, scale, Lq, Lk, causal,
+                q_orig_rows=None, k_orig=None, v_orig=None, sel_row=None, round_p=True,
+                tile_order=None):
+    """Two-pass O8 for a group of query rows that all lie in one 128-row q-tile.
+
+    rows: [R] query indices; q_rows: [R, d] dequantized Q; k_deq: [Lk, d];
+    v_codes: [Lk, d] E4M3 codes; s_v: [Lk] float32; sel_row: [nk] bool for
+    this q-tile (None = nothing selected). Returns (O [R, d] float64, LSE [R]).
+    """
+    rows = np.asarray(rows)
+    off = Lk - Lq
+    vq_vals = e4m3_decode(v_codes)
+    tiles = _row_tiles(rows, Lq, Lk, causal)
+    if tile_order is not None:
+        tiles = [tiles[t] for t in tile_order]
+    ms, ls, Ts = [], [], []
+    for j in tiles:
+        cs = np.arange(j * TILE, (j + 1) * TILE)
+        unmasked = np.ones((len(rows), TILE), dtype=bool) if not causal else (cs[None, :] <= rows[:, None] + off)
+        sel = bool(sel_row[j]) if sel_row is not None else False
+        if sel:
+            S = scale * (q_orig_rows @ k_orig[cs].T)
+        else:
+            S = scale * (q_rows @ k_deq[cs].T)
+        m, l, T = _tile_terms(S, unmasked, sel, vq_vals[cs], s_v[cs],
+                              v_orig[cs] if sel else None, round_p)
+        ms.append(m); ls.append(l); Ts.append(T)
+    M = np.stack(ms, axis=0)                       # [J, R]
+    mrow = M.max(axis=0)
+    f = np.exp(M - mrow[None, :])                  # e^(m~_j - m), 0 for empty tiles
+    D = (f * np.stack(ls, axis=0)).sum(axis=0)
+    N = (f[:, :, None] * np.stack(Ts, axis=0)).sum(axis=0)
+    return N / D[:, None], mrow + np.log(D)
+
+
+def attend_rows_online(rows, q_rows, k_deq, v_codes, s_v, scale, Lq, Lk, causal,
+                       q_orig_rows=None, k_orig=None, v_orig=None, sel_row=None, round_p=True,
+                       tile_order=None):
+    """The same computation as attend_rows with a running max m, sum l and accumulator acc.
+
+    For each tile: m_new = max(m, m~); acc = acc e^(m - m_new) + T e^(m~ - m_new);
+    l = l e^(m - m_new) + (sum P') e^(m~ - m_new).
+    """
+    rows = np.asarray(rows)
+    off = Lk - Lq
+    vq_vals = e4m3_decode(v_codes)
+    tiles = _row_tiles(rows, Lq, Lk, causal)
+    if tile_order is not None:
+        tiles = [tiles[t] for t in tile_order]
+    R, d = len(rows), v_codes.shape[1]
+    m = np.full(R, -np.inf)
+    l = np.zeros(R)
+    acc = np.zeros((R, d))
+    for j in tiles:
+        cs = np.arange(j * TILE, (j + 1) * TILE)
+        unmasked = np.ones((R, TILE), dtype=bool) if not causal else (cs[None, :] <= rows[:, None] + off)
+        sel = bool(sel_row[j]) if sel_row is not None else False
+        S = scale * ((q_orig_rows @ k_orig[cs].T) if sel else (q_rows @ k_deq[cs].T))
+        mt, lt, T = _tile_terms(S, unmasked, sel, vq_vals[cs], s_v[cs],
+                                v_orig[cs] if sel else None, round_p)
+        m_new = np.maximum(m, mt)
+        a_old = np.where(np.isfinite(m), np.exp(m - m_new), 0.0)
+        a_new = np.where(np.isfinite(mt), np.exp(mt - m_new), 0.0)
+        acc = acc * a_old[:, None] + T * a_new[:, None]
+        l = l * a_old + lt * a_new
+        m = m_new
+    return acc / l[:, None], m + np.log(l)
+
+
+def attention_prefill(q_deq, k_deq, v_codes, s_v, causal, scale=None,
+                      q_orig=None, k_orig=None, v_orig=None, bitmap=None,
+                      rows=None, heads=None, round_p=True):
+    """O8 over a batch: q_deq [B, Hq, Lq, d]; k_deq [B, Hkv, Lk, d]; v_codes [B, Hkv, Lk, d]
+    (E4M3 codes, token-major); s_v [B, Hkv, Lk]; optional originals (bf16 values as float64)
+    and bitmap [B, Hq, nq, nk].
+
+    rows: optional array of query rows to compute (default all); heads: optional
+    list of (b, h) pairs (default all). Returns (O float32 [B, Hq, R, d],
+    LSE float32 [B, Hq, R]) with R = len(rows); heads not listed stay zero.
+    """
+    B, Hq, Lq, d = q_deq.shape
+    Hkv, Lk = k_deq.shape[1], k_deq.shape[2]
+    group = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    rows = np.arange(Lq) if rows is None else np.asarray(rows)
+    heads = [(b, h) for b in range(B) for h in range(Hq)] if heads is None else heads
+    O = np.zeros((B, Hq, len(rows), d), dtype=np.float32)
+    LSE = np.zeros((B, Hq, len(rows)), dtype=np.float32)
+    qtile = rows // TILE
+    for (b, h) in heads:
+        kv = h // group
+        for i in np.unique(qtile):
+            sel_idx = np.nonzero(qtile == i)[0]
+            rr = rows[sel_idx]
+            sel_row = bitmap[b, h, i] if bitmap is not None else None
+            o, lse = attend_rows(
+                rr, q_deq[b, h, rr], k_deq[b, kv], v_codes[b, kv], s_v[b, kv], scale, Lq, Lk, causal,
+                q_orig_rows=None if q_orig is None else q_orig[b, h, rr],
+                k_orig=None if k_orig is None else k_orig[b, kv],
+                v_orig=None if v_orig is None else v_orig[b, kv],
+                sel_row=sel_row, round_p=round_p)
+            O[b, h, sel_idx] = fp32(o)
+            LSE[b, h, sel_idx] = fp32(lse)
+    return O, LSE
+
+
+def attention_reference(q, k, v, causal, scale=None):
+    """Unquantized softmax(scale q k^T + mask) v in float64 (q: [..., Lq, d], k/v: [..., Lk, d]).
+
+    Used to report the error that quantization adds; not a parity gate.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    Lq, d = q.shape[-2], q.shape[-1]
+    Lk = k.shape[-2]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    S = scale * (q @ np.swapaxes(k, -1, -2))
+    if causal:
+        r = np.arange(Lq)[:, None]
+        c = np.arange(Lk)[None, :]
+        S = np.where(c <= r + (Lk - Lq), S, -np.inf)
+    S = S - S.max(axis=-1, keepdims=True)
+    P = np.exp(S)
+    return (P @ v) / P.sum(axis=-1, keepdims=True)

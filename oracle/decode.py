@@ -1,0 +1,101 @@
+"""Decode attention of the oracle over a paged NVFP4 KV cache with a dual-residual query.
+
+TEST INFRASTRUCTURE: only the tests, the smoke check and the benchmark's
+CPU-baseline leg may use this module. Shares no code with the GPU path.
+
+Source: "BitDecoding-FP4: native FP4 KV-cache decoding" (sns.style digest):
+the KV cache is stored in 4-bit microscaling form in pages; the query is split
+into two FP4 tensors, the second carrying the residual of the first; the
+probabilities are quantized with a scale that cannot underflow to zero; the
+query heads sharing one key head (GQA) are processed together. "MpFA QK4V8"
+(hotelren.com 6111405) section 3.3: FP32-or-better running max and sum.
+
+Computation per (batch b, query head h), key head kv = h // (Hq/Hkv), keys
+c in [0, L_b) (the query attends to every cached token), scale = 1/sqrt(d):
+  q^ = dequant(Q1) + dequant(Q2) (float64); k^, v^ = NVFP4-dequantized cache rows;
+  S_c = scale * q^ . k^_c; tiles of 128 keys from position 0 (the last may be partial);
+  per tile: m~ = max S_c, P'_c = exp(S_c - m~), P^_c = E4M3(448 P'_c),
+  T = (1/448) sum_c P^_c v^_c;
+  m = max m~, D = sum e^(m~ - m) sum P', N = sum e^(m~ - m) T, O = N / D (float32).
+The page table maps logical page p of sequence b (tokens 64p .. 64p+63) to a
+physical page; a physical page holds [Hkv][64][...] rows.
+"""
+import numpy as np
+
+from .formats import E4M3_MAX, e4m3_decode, e4m3_encode, fp32
+from .quant import nvfp4_dequantize
+
+TILE = 128
+
+
+def gather_pages(pages, page_table_b, L, page_size, kvh):
+    """Logical rows [L, ...] of key head kvh for one sequence, read through its page table."""
+    c = np.arange(L)
+    phys = np.asarray(page_table_b)[c // page_size]
+    return pages[phys, kvh, c % page_size]
+
+
+def decode_one(q_hat, k_hat, v_hat, scale, chunk=None, round_p=True):
+    """O for one query row against L keys. chunk: optional split length (multiple of 128) whose
+    partial results (m, l, O) are merged afterwards; the merged result equals the single pass."""
+    L = k_hat.shape[0]
+    if chunk is None:
+        chunk = max(L, 1)
+    assert chunk % TILE == 0 or chunk >= L
+    parts = []
+    for s0 in range(0, L, chunk):
+        ms, ls, Ts = [], [], []
+        for t0 in range(s0, min(s0 + chunk, L), TILE):
+            cs = np.arange(t0, min(t0 + TILE, L, s0 + chunk))
+            S = scale * (k_hat[cs] @ q_hat)
+            m = S.max()
+            P = np.exp(S - m)
+            Ph = e4m3_decode(e4m3_encode(E4M3_MAX * P)) if round_p else E4M3_MAX * P
+            ms.append(m); ls.append(P.sum()); Ts.append((Ph @ v_hat[cs]) / E4M3_MAX)
+        M = np.array(ms)
+        mm = M.max()
+        f = np.exp(M - mm)
+        parts.append((mm, (f * np.array(ls)).sum(), (f[:, None] * np.array(Ts)).sum(axis=0)))
+    mm = max(p[0] for p in parts)
+    D = sum(np.exp(p[0] - mm) * p[1] for p in parts)
+    N = sum(np.exp(p[0] - mm) * p[2] for p in parts)
+    return N / D
+
+
+def dequant_query(q1, q2):
+    """q^ = dequant(Q1) + dequant(Q2) for NVFP4 pairs ((codes, sb, st) with groups = rows)."""
+    return nvfp4_dequantize(*q1) + nvfp4_dequantize(*q2)
+
+
+def decode_paged(q1, q2, k_pages, v_pages, k_tscale, v_tscale, page_table, ctx_len,
+                 Hq, Hkv, page_size=64, scale=None, pairs=None, chunk=None, round_p=True):
+    """O9 through the page table.
+
+    q1, q2: (codes [B*Hq, 1, d/2], block scales [B*Hq, 1, d/16], tensor scales [B*Hq]).
+    k_pages / v_pages: (codes [P, Hkv, page_size, d/2], block scales [P, Hkv, page_size, d/16]).
+    k_tscale / v_tscale: [B, Hkv] float32. Returns O float32 [B, Hq, d]; pairs (optional)
+    restricts the computed (b, h) pairs, the rest stay zero.
+    """
+    B = len(ctx_len)
+    d = 2 * q1[0].shape[-1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    group = Hq // Hkv
+    qhat = dequant_query(q1, q2).reshape(B, Hq, d)
+    O = np.zeros((B, Hq, d), dtype=np.float32)
+    pairs = [(b, h) for b in range(B) for h in range(Hq)] if pairs is None else pairs
+    cache = {}
+    for (b, h) in pairs:
+        kv = h // group
+        L = int(ctx_len[b])
+        if (b, kv) not in cache:
+            kc = gather_pages(k_pages[0], page_table[b], L, page_size, kv)
+            ks = gather_pages(k_pages[1], page_table[b], L, page_size, kv)
+            vc = gather_pages(v_pages[0], page_table[b], L, page_size, kv)
+            vs = gather_pages(v_pages[1], page_table[b], L, page_size, kv)
+            k_hat = nvfp4_dequantize(kc[None], ks[None], np.array([k_tscale[b, kv]]))[0]
+            v_hat = nvfp4_dequantize(vc[None], vs[None], np.array([v_tscale[b, kv]]))[0]
+            cache = {(b, kv): (k_hat, v_hat)}
+        k_hat, v_hat = cache[(b, kv)]
+        O[b, h] = fp32(decode_one(qhat[b, h], k_hat, v_hat, scale, chunk=chunk, round_p=round_p))
+    return O

@@ -1,0 +1,98 @@
+"""Pins of the oracle's paged decode: paging, split and GQA invariances, SDPA limit, brute force."""
+import numpy as np
+import torch
+
+import bruteforce as bf
+import workloads as W
+from oracle import decode as Dd
+from oracle import quant as Q
+
+SMALL = W.C3.scaled(B=3, Hq=8, Hkv=2, ctx_lo=200, ctx_hi=700)
+
+
+def build_cache(cfg, seed=0):
+    """Quantize K and V per (sequence, key head) and scatter rows into pages through the page table."""
+    lay = W.decode_layout(cfg, seed)
+    d, ps = cfg.d, cfg.page_size
+    P = lay.num_pages
+    kc = np.zeros((P, cfg.Hkv, ps, d // 2), np.uint8); ks = np.zeros((P, cfg.Hkv, ps, d // 16), np.uint8)
+    vc = np.zeros_like(kc); vs = np.zeros_like(ks)
+    kt = np.zeros((cfg.B, cfg.Hkv), np.float32); vt = np.zeros_like(kt)
+    logical = {}
+    for b in range(cfg.B):
+        L = int(lay.ctx_len[b])
+        c = np.arange(L)
+        phys = lay.page_table[b].numpy()[c // ps]
+        for h in range(cfg.Hkv):
+            for tensor, (codes, scales, ts) in [(W.T_K, (kc, ks, kt)), (W.T_V, (vc, vs, vt))]:
+                x = W.decode_kv_head(cfg, tensor, b, h, L, seed).double().numpy()
+                qc, qs, qt = Q.nvfp4_quantize(x[None])
+                codes[phys, h, c % ps] = qc[0]
+                scales[phys, h, c % ps] = qs[0]
+                ts[b, h] = qt[0]
+                logical[(tensor, b, h)] = (x, Q.nvfp4_dequantize(qc, qs, qt)[0])
+    q = W.decode_query(cfg, seed).double().numpy()
+    q1, q2 = Q.dual_residual_quantize(q.reshape(cfg.B * cfg.Hq, 1, d))
+    return lay, (kc, ks), (vc, vs), kt, vt, q, q1, q2, logical
+
+
+def test_paged_equals_contiguous_and_sdpa_limit():
+    cfg = SMALL
+    lay, kp, vp, kt, vt, q, q1, q2, logical = build_cache(cfg)
+    O = Dd.decode_paged(q1, q2, kp, vp, kt, vt, lay.page_table.numpy(), lay.ctx_len.numpy(), cfg.Hq, cfg.Hkv)
+    On = Dd.decode_paged(q1, q2, kp, vp, kt, vt, lay.page_table.numpy(), lay.ctx_len.numpy(), cfg.Hq, cfg.Hkv,
+                         round_p=False)
+    qhat = Dd.dequant_query(q1, q2).reshape(cfg.B, cfg.Hq, cfg.d)
+    g = cfg.Hq // cfg.Hkv
+    for b in range(cfg.B):
+        for h in range(cfg.Hq):
+            kh = logical[(W.T_K, b, h // g)][1]
+            vh = logical[(W.T_V, b, h // g)][1]
+            # contiguous logical rows, same computation
+            ref = Dd.decode_one(qhat[b, h], kh, vh, 1 / np.sqrt(cfg.d))
+            assert np.abs(O[b, h] - ref).max() <= 1e-6 * np.abs(ref).max()
+            # without P rounding: plain softmax attention over the dequantized cache
+            sd = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(qhat[b, h][None, None]), torch.from_numpy(kh[None]), torch.from_numpy(vh[None]),
+                scale=1 / np.sqrt(cfg.d)).numpy()[0, 0]
+            assert np.abs(On[b, h] - sd).max() <= 1e-6 * np.abs(sd).max()
+
+
+def test_split_merge_equals_single_pass():
+    cfg = SMALL
+    lay, kp, vp, kt, vt, q, q1, q2, logical = build_cache(cfg)
+    qhat = Dd.dequant_query(q1, q2).reshape(cfg.B, cfg.Hq, cfg.d)
+    kh = logical[(W.T_K, 1, 0)][1]; vh = logical[(W.T_V, 1, 0)][1]
+    one = Dd.decode_one(qhat[1, 2], kh, vh, 0.1)
+    for chunk in [128, 256, 384]:
+        sp = Dd.decode_one(qhat[1, 2], kh, vh, 0.1, chunk=chunk)
+        assert np.abs(sp - one).max() <= 1e-12 * np.abs(one).max()
+
+
+def test_bruteforce_decode():
+    cfg = SMALL.scaled(B=1, ctx_lo=300, ctx_hi=300)
+    lay, kp, vp, kt, vt, q, q1, q2, logical = build_cache(cfg)
+    O = Dd.decode_paged(q1, q2, kp, vp, kt, vt, lay.page_table.numpy(), lay.ctx_len.numpy(), cfg.Hq, cfg.Hkv,
+                        pairs=[(0, 0), (0, 5)])
+    # brute force dequantizes the query from its own NVFP4 loops and attends by loops
+    for h in [0, 5]:
+        qv = np.zeros(cfg.d)
+        for (c, s, t) in (q1, q2):
+            codes = [[int(x) for pair in row for x in (pair & 15, pair >> 4)] for row in c[h]]
+            qv += np.array(bf.nvfp4_values(codes, s[h].tolist(), float(t[h]))[0])
+        K = logical[(W.T_K, 0, h // 4)][1].tolist()
+        V = logical[(W.T_V, 0, h // 4)][1].tolist()
+        ref = bf.decode_row(qv.tolist(), K, V, 1 / np.sqrt(cfg.d))
+        assert np.abs(O[0, h] - np.array(ref)).max() <= 1e-6 * np.abs(ref).max()
+
+
+def test_dual_residual_query_cuts_logit_error():
+    cfg = SMALL
+    lay, kp, vp, kt, vt, q, q1, q2, logical = build_cache(cfg)
+    x1 = Q.nvfp4_dequantize(*q1).reshape(cfg.B, cfg.Hq, cfg.d)
+    x12 = Dd.dequant_query(q1, q2).reshape(cfg.B, cfg.Hq, cfg.d)
+    kh = logical[(W.T_K, 0, 0)][1]
+    l0 = kh @ q[0, 0]
+    e1 = np.linalg.norm(kh @ x1[0, 0] - l0) / np.linalg.norm(l0)
+    e2 = np.linalg.norm(kh @ x12[0, 0] - l0) / np.linalg.norm(l0)
+    assert e2 < 0.25 * e1

@@ -1,0 +1,190 @@
+"""Pins of the oracle's quantizers: closed forms vs definitions, round-trip bounds, brute force, invariants."""
+import math
+import os
+
+import numpy as np
+import torch
+
+import bruteforce as bf
+from oracle import formats as F
+from oracle import quant as Q
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _blocks():
+    out = {}
+    for line in open(os.path.join(GOLDEN, "block_sizes.txt")):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            name, n, sfmt, tfmt = line.split()
+            out[name] = (int(n), sfmt, tfmt)
+    return out
+
+
+def test_block_sizes_match_pages():
+    b = _blocks()
+    assert b["mxfp4"][0] == Q.MX_BLOCK and b["nvfp4"][0] == Q.NV_BLOCK
+
+
+def test_mx_exponent_closed_form_vs_definition():
+    """e(amax) == the smallest e with 6 * 2^e >= amax, over every float32 exponent and many mantissas."""
+    rng = np.random.default_rng(0)
+    amax = []
+    for E in range(-149, 128):
+        for m in list(rng.integers(0, 1 << 23, 64)) + [0, 1, (1 << 22), (1 << 23) - 1, 0x400000, 0x3FFFFF]:
+            v = np.ldexp(1.0 + m / 2.0 ** 23, E) if E >= -126 else np.ldexp(float(m), -149)
+            if 0 < v < 3.4e38:
+                amax.append(v)
+    amax = np.array(amax, dtype=np.float32).astype(np.float64)
+    got = Q.mx_scale_exponent(amax)
+    ref = np.array([bf.mx_exponent(float(a)) for a in amax])
+    assert np.array_equal(got, ref)
+    # exactly at 6 * 2^e the power e itself is chosen; just above it, e + 1
+    for e in range(-100, 100):
+        assert Q.mx_scale_exponent(6.0 * 2.0 ** e) == e
+        assert Q.mx_scale_exponent(np.nextafter(np.float32(6.0 * 2.0 ** e), np.float32(np.inf))) == e + 1
+    assert Q.mx_scale_exponent(0.0) == -127
+
+
+def test_mx_scale_puts_block_max_in_3_to_6():
+    rng = np.random.default_rng(1)
+    x = (rng.standard_normal((4000, 32)) * np.exp2(rng.uniform(-20, 20, (4000, 1)))).astype(np.float32)
+    codes, scales = Q.mxfp4_quantize(x)
+    amax = np.abs(x).max(axis=1)
+    e = scales[:, 0].astype(np.int64) - 127
+    r = amax * np.exp2(-e.astype(np.float64))
+    assert np.all(r > 3) and np.all(r <= 6)
+    top = np.abs(F.e2m1_decode(F.unpack_nibbles(codes))).max(axis=1)
+    assert set(np.unique(top).tolist()) <= {3.0, 4.0, 6.0}
+
+
+def test_mxfp4_round_trip_bound():
+    """|x - x^| <= 2^e * {0.25, 0.5, 1} in the bands |x 2^-e| <= 2, <= 4, <= 6 (X ~ s Q)."""
+    rng = np.random.default_rng(2)
+    x = (rng.standard_normal((2000, 128)) * np.exp2(rng.uniform(-8, 8, (2000, 1)))).astype(np.float32).astype(np.float64)
+    codes, scales = Q.mxfp4_quantize(x)
+    xh = Q.mxfp4_dequantize(codes, scales)
+    s = np.repeat(np.exp2(scales.astype(np.int64) - 127.0), 32, axis=1)
+    a = np.abs(x) / s
+    bound = np.where(a <= 2, 0.25, np.where(a <= 4, 0.5, 1.0)) * s
+    assert np.all(np.abs(x - xh) <= bound)
+
+
+def test_mxfp4_vs_bruteforce():
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal((6, 64)) * np.array([1, 1e-3, 40, 0, 1e-39, 7])[:, None]).astype(np.float32)
+    x[3] = 0.0
+    x[5, :32] = -0.0
+    codes, scales = Q.mxfp4_quantize(x)
+    cu = F.unpack_nibbles(codes)
+    for r in range(x.shape[0]):
+        c, s = bf.mxfp4_row([float(v) for v in x[r]])
+        assert cu[r].tolist() == c
+        assert scales[r].tolist() == s
+
+
+def test_nvfp4_vs_bruteforce_and_invariants():
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal((3, 5, 64)) * np.exp2(rng.uniform(-6, 6, (3, 5, 1)))).astype(np.float32)
+    x[1, 2, 16:32] = 0.0
+    x[2] *= 0.0
+    codes, sb, st = Q.nvfp4_quantize(x)
+    for g in range(3):
+        c, s, t = bf.nvfp4_group([[float(v) for v in row] for row in x[g]])
+        assert np.float32(t) == st[g]
+        assert F.unpack_nibbles(codes[g]).tolist() == c
+        assert sb[g].tolist() == s
+    assert st[2] == 1.0 and np.all((F.unpack_nibbles(codes[2]) & 7) == 0)
+    # the block holding the tensor maximum gets the largest scale code (448 = 0x7E) up to one step
+    for g in range(2):
+        top = sb[g].max()
+        assert top in (0x7D, 0x7E)
+    # reconstruction error is bounded by half a grid step at the block's scale, plus float32 slack
+    xh = Q.nvfp4_dequantize(codes, sb, st)
+    scale = (F.e4m3_decode(sb) * st[:, None, None]).repeat(16, axis=2)
+    a = np.abs(x) / np.where(scale > 0, scale, 1)
+    half = np.where(a <= 2, 0.25, np.where(a <= 4, 0.5, 1.0))
+    over = np.maximum(a - 6, 0)                        # values above 6 * scale saturate
+    ok = np.abs(x - xh) <= (half + over) * scale * (1 + 1e-6) + 1e-30
+    assert np.all(ok | (scale == 0))
+
+
+def test_nvfp4_idempotent():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((2, 4, 32)).astype(np.float32)
+    c, sb, st = Q.nvfp4_quantize(x)
+    xh = Q.nvfp4_dequantize(c, sb, st)
+    c2, sb2, st2 = Q.nvfp4_quantize(xh)
+    assert np.array_equal(Q.nvfp4_dequantize(c2, sb2, st2), xh)
+
+
+def test_dual_residual_reduces_error():
+    rng = np.random.default_rng(6)
+    q = torch.randn(64, 1, 128, generator=torch.Generator().manual_seed(0)).to(torch.bfloat16).float().numpy()
+    (c1, s1, t1), (c2, s2, t2) = Q.dual_residual_quantize(q)
+    x1 = Q.nvfp4_dequantize(c1, s1, t1)
+    x2 = Q.nvfp4_dequantize(c2, s2, t2)
+    e1 = np.linalg.norm(q - x1, axis=-1)
+    e2 = np.linalg.norm(q - x1 - x2, axis=-1)
+    assert np.all(e2 <= e1)
+    assert np.median(e2 / e1) < 0.25
+    # query-logit error against random keys drops as well
+    k = rng.standard_normal((1000, 128))
+    l0 = q[:, 0] @ k.T
+    r1 = np.linalg.norm(x1[:, 0] @ k.T - l0) / np.linalg.norm(l0)
+    r2 = np.linalg.norm((x1 + x2)[:, 0] @ k.T - l0) / np.linalg.norm(l0)
+    assert r2 < 0.25 * r1
+
+
+def test_fp8_token_vs_torch():
+    rng = np.random.default_rng(7)
+    v = (rng.standard_normal((500, 128)) * np.exp2(rng.uniform(-10, 10, (500, 1)))).astype(np.float32)
+    v[3] = 0.0
+    codes, sv = Q.fp8_per_token_quantize(v)
+    q = (v / sv[:, None]).astype(np.float32)
+    ref = torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes, ref)
+    assert sv[3] == 1.0 and np.all(codes[3] == 0)
+    for r in range(4):
+        c, s = bf.fp8_token([float(x) for x in v[r]])
+        assert np.float32(s) == sv[r] and codes[r].tolist() == c
+    # the largest element of every nonzero row maps to 448 (code 0x7E), possibly one step below
+    top = codes[np.arange(500) != 3].astype(np.int64) & 0x7F
+    assert set(np.unique(top.max(axis=1)).tolist()) <= {0x7D, 0x7E}
+
+
+def test_hadamard_orthogonal_and_norm_preserving():
+    H = Q.sylvester_hadamard(128)
+    assert np.array_equal(H @ H.T, 128 * np.eye(128))
+    assert np.array_equal(H, H.T)
+    # recursive definition checked entry-wise: H[i, j] = (-1)^popcount(i & j)
+    i = np.arange(128)
+    assert np.array_equal(H, (-1.0) ** np.array([[bin(a & b).count("1") for b in i] for a in i]))
+    rng = np.random.default_rng(8)
+    x = torch.from_numpy(rng.standard_normal((50, 128)).astype(np.float32)).to(torch.bfloat16).double().numpy()
+    y = Q.hadamard_rotate(x)
+    assert np.allclose(np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1), rtol=1e-6)
+    yy = x @ H / math.sqrt(128)
+    assert np.allclose(yy @ yy.T, x @ x.T, rtol=1e-12, atol=1e-9)
+    assert np.array_equal(y, yy.astype(np.float32).astype(np.float64))
+
+
+def test_row_norm2_vs_exact_sum():
+    rng = np.random.default_rng(9)
+    x = torch.from_numpy((rng.standard_normal((3000, 128)) * 3).astype(np.float32)).to(torch.bfloat16).float().numpy()
+    n = Q.row_norm2(x)
+    exact = np.array([math.fsum(float(v) ** 2 for v in row) for row in x])
+    assert np.array_equal(n, exact.astype(np.float32))
+
+
+def test_zero_and_tiny_blocks_are_defined():
+    x = np.zeros((1, 2, 64), dtype=np.float32)
+    x[0, 1, :] = -0.0
+    c, s = Q.mxfp4_quantize(x)
+    assert np.all(s == 0) and np.all(F.unpack_nibbles(c)[0, 0] == 0) and np.all(F.unpack_nibbles(c)[0, 1] == 8)
+    c, sb, st = Q.nvfp4_quantize(x)
+    assert st[0] == 1.0 and np.all(sb == 0)
+    v = np.full((1, 64), 1e-42, dtype=np.float32)
+    c, s = Q.mxfp4_quantize(v)
+    assert not np.any(np.isnan(Q.mxfp4_dequantize(c, s)))
