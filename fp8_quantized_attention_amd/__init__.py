@@ -1,0 +1,285 @@
+"""Python binding of libfa4 (block-scaled low-bit fused attention on MI355X / gfx950).
+
+Argument marshalling only: every step of the path runs in the HIP kernels behind the C ABI declared
+in include/fa4.h. torch provides device memory and the current HIP stream. If the built library is
+missing, importing this package raises: there is no fallback implementation.
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libfa4.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m fp8_quantized_attention_amd.build` "
+                      "(or __graft_entry__.build()) first")
+lib = ctypes.CDLL(LIB_PATH)
+
+FA4_OK, FA4_ERR_NULL, FA4_ERR_SHAPE, FA4_ERR_UNSUPPORTED, FA4_ERR_ALIGN, FA4_ERR_WORKSPACE, FA4_ERR_HIP = range(7)
+FA4_F32, FA4_BF16 = 0, 1
+FA4_MXFP4, FA4_NVFP4, FA4_FP8_TOKEN = 0, 1, 2
+FA4_HADAMARD128, FA4_DUAL_RESIDUAL = 1, 2
+
+EXPORTS = ["fa4_quantize_blockscaled", "fa4_select_tiles", "fa4_attn_fwd", "fa4_decode_workspace_bytes",
+           "fa4_decode_paged", "fa4_status_string", "fa4_last_error"]
+
+_p = ctypes.c_void_p
+_i32, _i64, _u32, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_float
+
+
+class QInput(ctypes.Structure):
+    _fields_ = [("x", _p), ("dtype", _i32), ("d", _i32), ("outer", _i64), ("heads", _i32), ("rows", _i64),
+                ("stride_outer", _i64), ("stride_head", _i64), ("stride_row", _i64),
+                ("row_counts", _p), ("page_table", _p), ("page_size", _i32), ("max_pages", _i32),
+                ("num_pages", _i64)]
+
+
+class QOutput(ctypes.Structure):
+    _fields_ = [("fmt", _i32), ("codes", _p), ("block_scales", _p), ("scales", _p), ("fold_w", _p),
+                ("fold_sigma", _p)]
+
+
+class AttnArgs(ctypes.Structure):
+    _fields_ = [("fmt", _i32), ("q_codes", _p), ("q_scales", _p), ("q_tscale", _p),
+                ("k_codes", _p), ("k_scales", _p), ("k_tscale", _p), ("v_codes", _p), ("v_scales", _p),
+                ("v_fold_w", _p), ("v_fold_sigma", _p), ("q_bf16", _p), ("k_bf16", _p), ("v_bf16", _p), ("bitmap", _p),
+                ("B", _i32), ("Hq", _i32), ("Hkv", _i32), ("Lq", _i32), ("Lk", _i32), ("d", _i32),
+                ("causal", _i32), ("softmax_scale", _f32), ("o", _p), ("lse", _p)]
+
+
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [("q1_codes", _p), ("q1_scales", _p), ("q1_tscale", _p),
+                ("q2_codes", _p), ("q2_scales", _p), ("q2_tscale", _p),
+                ("k_codes", _p), ("k_scales", _p), ("v_codes", _p), ("v_scales", _p),
+                ("k_tscale", _p), ("v_tscale", _p), ("page_table", _p), ("ctx_len", _p),
+                ("B", _i32), ("Hq", _i32), ("Hkv", _i32), ("d", _i32), ("page_size", _i32), ("max_pages", _i32),
+                ("num_pages", _i64), ("softmax_scale", _f32), ("o", _p)]
+
+
+lib.fa4_quantize_blockscaled.argtypes = [ctypes.POINTER(QInput), _u32, ctypes.POINTER(QOutput),
+                                         ctypes.POINTER(QOutput), _p, _p]
+lib.fa4_quantize_blockscaled.restype = ctypes.c_int
+lib.fa4_select_tiles.argtypes = [_p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p]
+lib.fa4_select_tiles.restype = ctypes.c_int
+lib.fa4_attn_fwd.argtypes = [ctypes.POINTER(AttnArgs), _p]
+lib.fa4_attn_fwd.restype = ctypes.c_int
+lib.fa4_decode_workspace_bytes.argtypes = [ctypes.POINTER(DecodeArgs)]
+lib.fa4_decode_workspace_bytes.restype = ctypes.c_size_t
+lib.fa4_decode_paged.argtypes = [ctypes.POINTER(DecodeArgs), _p, ctypes.c_size_t, _p]
+lib.fa4_decode_paged.restype = ctypes.c_int
+lib.fa4_status_string.argtypes = [ctypes.c_int]
+lib.fa4_status_string.restype = ctypes.c_char_p
+lib.fa4_last_error.argtypes = []
+lib.fa4_last_error.restype = ctypes.c_char_p
+
+
+class Fa4Error(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        detail = lib.fa4_last_error().decode()
+        super().__init__(f"{where}: {lib.fa4_status_string(status).decode()} ({status}): {detail}")
+
+
+def _check(status, where):
+    if status != FA4_OK:
+        raise Fa4Error(status, where)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return FA4_F32
+    if t.dtype == torch.bfloat16:
+        return FA4_BF16
+    raise TypeError(f"unsupported input dtype {t.dtype}")
+
+
+# ---------------------------------------------------------------------------------------------------- quantize
+
+def quantize(x, fmt, hadamard=False, dual=False, row_norms=False, fold=None):
+    """Quantize a [outer, heads, rows, d] tensor (float32 or bf16, contiguous on the GPU).
+
+    Returns a dict: codes [outer, heads, rows, d/2 or d] uint8, block_scales (MXFP4: d/32, NVFP4: d/16
+    per row), scales (NVFP4: [outer*heads] tensor scales; FP8: per-row), and with dual=True the
+    residual's 'codes2', 'block_scales2', 'scales2'; with row_norms=True 'norm2' [outer, heads, rows];
+    FP8 per-token output also carries the attention fold data 'fold_w' [outer, heads, rows] and
+    'fold_sigma' [outer, heads, rows/128] (default: when rows is a multiple of 128).
+    """
+    assert x.is_cuda and x.is_contiguous() and x.dim() == 4
+    O, H, R, d = x.shape
+    dev = x.device
+    u8 = dict(dtype=torch.uint8, device=dev)
+    out = {}
+    if fmt == FA4_FP8_TOKEN:
+        out["codes"] = torch.empty(O, H, R, d, **u8)
+        out["scales"] = torch.empty(O, H, R, dtype=torch.float32, device=dev)
+        bs = None
+    else:
+        out["codes"] = torch.empty(O, H, R, d // 2, **u8)
+        out["block_scales"] = bs = torch.empty(O, H, R, d // (32 if fmt == FA4_MXFP4 else 16), **u8)
+        out["scales"] = torch.empty(O * H, dtype=torch.float32, device=dev) if fmt == FA4_NVFP4 else None
+    qin = QInput(x.data_ptr(), _dtype_code(x), d, O, H, R, H * R * d, R * d, d, None, None, 0, 0, 0)
+    if fold is None:
+        fold = fmt == FA4_FP8_TOKEN and R % 128 == 0 and R > 0
+    if fold:
+        out["fold_w"] = torch.empty(O, H, R, dtype=torch.float32, device=dev)
+        out["fold_sigma"] = torch.empty(O, H, R // 128, dtype=torch.float32, device=dev)
+    qout = QOutput(fmt, out["codes"].data_ptr(), _ptr(bs), _ptr(out["scales"]), _ptr(out.get("fold_w")),
+                   _ptr(out.get("fold_sigma")))
+    res = None
+    if dual:
+        out["codes2"] = torch.empty_like(out["codes"])
+        out["block_scales2"] = torch.empty_like(out["block_scales"])
+        out["scales2"] = torch.empty_like(out["scales"])
+        res = QOutput(fmt, out["codes2"].data_ptr(), out["block_scales2"].data_ptr(), out["scales2"].data_ptr(),
+                      None, None)
+    if row_norms:
+        out["norm2"] = torch.empty(O, H, R, dtype=torch.float32, device=dev)
+    flags = (FA4_HADAMARD128 if hadamard else 0) | (FA4_DUAL_RESIDUAL if dual else 0)
+    _check(lib.fa4_quantize_blockscaled(ctypes.byref(qin), flags, ctypes.byref(qout),
+                                        ctypes.byref(res) if res is not None else None,
+                                        _ptr(out.get("norm2")), _stream()), "fa4_quantize_blockscaled")
+    return out
+
+
+def quantize_paged(x, fmt, ctx_len, page_table, num_pages, page_size=64):
+    """Quantize a padded [B, Hkv, Lmax, d] cache tensor (rows r < ctx_len[b] exist) into pages.
+
+    Returns codes [num_pages, Hkv, page_size, d/2], block_scales [num_pages, Hkv, page_size, d/16],
+    scales [B*Hkv] (NVFP4 tensor scale per (sequence, key head)).
+    """
+    assert fmt == FA4_NVFP4 and x.is_cuda and x.is_contiguous()
+    B, H, R, d = x.shape
+    dev = x.device
+    out = {
+        "codes": torch.zeros(num_pages, H, page_size, d // 2, dtype=torch.uint8, device=dev),
+        "block_scales": torch.zeros(num_pages, H, page_size, d // 16, dtype=torch.uint8, device=dev),
+        "scales": torch.empty(B * H, dtype=torch.float32, device=dev),
+    }
+    qin = QInput(x.data_ptr(), _dtype_code(x), d, B, H, R, H * R * d, R * d, d, ctx_len.data_ptr(),
+                 page_table.data_ptr(), page_size, page_table.shape[1], num_pages)
+    qout = QOutput(fmt, out["codes"].data_ptr(), out["block_scales"].data_ptr(), out["scales"].data_ptr(), None, None)
+    _check(lib.fa4_quantize_blockscaled(ctypes.byref(qin), 0, ctypes.byref(qout), None, None, _stream()),
+           "fa4_quantize_blockscaled(paged)")
+    return out
+
+
+# ---------------------------------------------------------------------------------------------------- select
+
+def select_tiles(q_norm2, k_norm2, causal, num=5, den=100):
+    """q_norm2 [B, Hq, Lq], k_norm2 [B, Hkv, Lk] -> (bitmap [B, Hq, Lq/128, Lk/128] uint8, counts [B, Hq])."""
+    B, Hq, Lq = q_norm2.shape
+    Hkv, Lk = k_norm2.shape[1], k_norm2.shape[2]
+    bitmap = torch.empty(B, Hq, Lq // 128, Lk // 128, dtype=torch.uint8, device=q_norm2.device)
+    counts = torch.empty(B, Hq, dtype=torch.int32, device=q_norm2.device)
+    _check(lib.fa4_select_tiles(q_norm2.data_ptr(), k_norm2.data_ptr(), B, Hq, Hkv, Lq, Lk, int(causal),
+                                num, den, bitmap.data_ptr(), counts.data_ptr(), _stream()), "fa4_select_tiles")
+    return bitmap, counts
+
+
+# ---------------------------------------------------------------------------------------------------- attention
+
+def attn_fwd(q, k, v, causal, fmt, Hq, Hkv, Lq, Lk, d, B=1, bitmap=None, q_bf16=None, k_bf16=None,
+             v_bf16=None, softmax_scale=None, want_lse=True, out=None, lse=None):
+    """Prefill attention from quantized operands (dicts as returned by quantize()).
+
+    q/k hold MXFP4 or NVFP4 codes and scales, v holds FP8 per-token codes and scales.
+    Returns (o [B, Hq, Lq, d] float32, lse [B, Hq, Lq] float32 or None).
+    """
+    dev = q["codes"].device
+    if out is None:
+        out = torch.empty(B, Hq, Lq, d, dtype=torch.float32, device=dev)
+    if want_lse and lse is None:
+        lse = torch.empty(B, Hq, Lq, dtype=torch.float32, device=dev)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    a = AttnArgs(fmt, q["codes"].data_ptr(), q["block_scales"].data_ptr(), _ptr(q.get("scales")),
+                 k["codes"].data_ptr(), k["block_scales"].data_ptr(), _ptr(k.get("scales")),
+                 v["codes"].data_ptr(), v["scales"].data_ptr(), v["fold_w"].data_ptr(), v["fold_sigma"].data_ptr(),
+                 _ptr(q_bf16), _ptr(k_bf16), _ptr(v_bf16), _ptr(bitmap),
+                 B, Hq, Hkv, Lq, Lk, d, int(causal), softmax_scale, out.data_ptr(), _ptr(lse if want_lse else None))
+    _check(lib.fa4_attn_fwd(ctypes.byref(a), _stream()), "fa4_attn_fwd")
+    return out, (lse if want_lse else None)
+
+
+# ---------------------------------------------------------------------------------------------------- decode
+
+def decode_args(q1, q2, kcache, vcache, page_table, ctx_len, Hq, Hkv, d=128, page_size=64, softmax_scale=None,
+                out=None):
+    B = ctx_len.shape[0]
+    if out is None:
+        out = torch.empty(B, Hq, d, dtype=torch.float32, device=ctx_len.device)
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    a = DecodeArgs(q1["codes"].data_ptr(), q1["block_scales"].data_ptr(), q1["scales"].data_ptr(),
+                   q2["codes"].data_ptr(), q2["block_scales"].data_ptr(), q2["scales"].data_ptr(),
+                   kcache["codes"].data_ptr(), kcache["block_scales"].data_ptr(),
+                   vcache["codes"].data_ptr(), vcache["block_scales"].data_ptr(),
+                   kcache["scales"].data_ptr(), vcache["scales"].data_ptr(),
+                   page_table.data_ptr(), ctx_len.data_ptr(), B, Hq, Hkv, d, page_size, page_table.shape[1],
+                   kcache["codes"].shape[0], softmax_scale, out.data_ptr())
+    return a, out
+
+
+def decode_workspace(a, device):
+    n = lib.fa4_decode_workspace_bytes(ctypes.byref(a))
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def decode_paged(q1, q2, kcache, vcache, page_table, ctx_len, Hq, Hkv, d=128, page_size=64, softmax_scale=None,
+                 workspace=None, out=None):
+    """Decode attention for one query token per sequence. q1/q2: NVFP4 dicts of the dual-residual query
+    ([B, Hq, 1, d] rows); kcache / vcache: paged NVFP4 dicts from quantize_paged()."""
+    a, out = decode_args(q1, q2, kcache, vcache, page_table, ctx_len, Hq, Hkv, d, page_size, softmax_scale, out)
+    if workspace is None:
+        workspace = decode_workspace(a, ctx_len.device)
+    _check(lib.fa4_decode_paged(ctypes.byref(a), workspace.data_ptr(), workspace.numel(), _stream()),
+           "fa4_decode_paged")
+    return out
+
+
+# ---------------------------------------------------------------------------------------------------- pipelines
+
+def prefill(q, k, v, causal, fmt=FA4_MXFP4, hadamard=False, select=None, softmax_scale=None, want_lse=True):
+    """Whole prefill path: quantize Q/K (MXFP4 or NVFP4, optional Hadamard), V to FP8 per token,
+    optionally select the top num/den tiles for bf16 (select=(num, den)), then fused attention.
+
+    q [B, Hq, Lq, d], k / v [B, Hkv, Lk, d]: contiguous float32 or bf16 CUDA tensors (bf16 needed for
+    selection, whose tiles read the originals). Returns a dict with 'o', 'lse', 'bitmap', 'counts',
+    and the quantized operands 'q', 'k', 'v'.
+    """
+    B, Hq, Lq, d = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    sel = select is not None
+    qq = quantize(q, fmt, hadamard=hadamard, row_norms=sel)
+    kq = quantize(k, fmt, hadamard=hadamard, row_norms=sel)
+    vq = quantize(v, FA4_FP8_TOKEN)
+    bitmap = counts = None
+    if sel:
+        bitmap, counts = select_tiles(qq["norm2"], kq["norm2"], causal, select[0], select[1])
+    o, lse = attn_fwd(qq, kq, vq, causal, fmt, Hq, Hkv, Lq, Lk, d, B=B, bitmap=bitmap,
+                      q_bf16=q if sel else None, k_bf16=k if sel else None, v_bf16=v if sel else None,
+                      softmax_scale=softmax_scale, want_lse=want_lse)
+    return {"o": o, "lse": lse, "bitmap": bitmap, "counts": counts, "q": qq, "k": kq, "v": vq}
+
+
+def decode(q, kcache, vcache, page_table, ctx_len, Hkv, softmax_scale=None, workspace=None, out=None):
+    """One decode step: q [B, Hq, d] (bf16 or float32) -> dual-residual NVFP4 -> paged attention.
+    Returns (o [B, Hq, d] float32, the quantized query dict)."""
+    B, Hq, d = q.shape
+    qq = quantize(q.reshape(B, Hq, 1, d), FA4_NVFP4, dual=True)
+    q1 = {"codes": qq["codes"], "block_scales": qq["block_scales"], "scales": qq["scales"]}
+    q2 = {"codes": qq["codes2"], "block_scales": qq["block_scales2"], "scales": qq["scales2"]}
+    o = decode_paged(q1, q2, kcache, vcache, page_table, ctx_len, Hq, Hkv, d, softmax_scale=softmax_scale,
+                     workspace=workspace, out=out)
+    return o, qq

@@ -1,0 +1,421 @@
+// Fused prefill attention for gfx950: block-scaled 4-bit QK^T and FP8 PV on the scaled MFMA,
+// FP32 online softmax, optional bf16 tiles chosen by the tile selector.
+//
+// Sources: "MpFA QK4V8" sections 2.1-2.2 and 3.2-3.4 (QK in 4 bits with the per-group scales applied
+// inside the product, V in 8 bits, FP32 running max and sum, tiling); "ThriftAttention" Method step 3
+// (selected tiles in high precision merged through the same online softmax); "BitDecoding-FP4"
+// (probability scales safe from underflow; transposed softmax); "General notes on quantization"
+// (a low-precision product rescaled by the merged operand scales).
+//
+// Work decomposition: one workgroup = one 128-query tile of one (batch, head); 4 waves of 32 queries.
+// K/V tiles of 128 keys are staged in LDS and visited in order (tiles above the causal diagonal are
+// skipped). Everything is computed transposed, S^T = K Q^T and O^T = V^T P^T, with 32x32 MFMA tiles:
+// a lane then owns one query (column l%32) and 64 of a tile's 128 keys, so the row max and sum are
+// in-lane plus one exchange with lane l^32, and the per-query rescale of O is a per-lane scalar.
+//
+// Probabilities: P' = exp(S - m~) against the tile's own row max m~ (<= 1, never underflows as a
+// whole). For FP8 tiles the per-token V scale s_v[c] is folded into P before rounding:
+// P^ = E4M3(P' * 448 s_v[c] / sigma), sigma = max s_v of the tile, so V's codes enter the MFMA as-is
+// and the tile contributes (sigma/448) * e^(m~ - m) * (P^ . Vcode). That per-query factor beta is
+// split as beta = 2^k * f, f in [1, 2): 2^k rides on the E8M0 operand scale of P^T inside the MFMA
+// and f becomes the accumulator's unit u (O_true = u * O_acc), so one multiply per O element per
+// tile keeps the accumulator exact. The denominator uses the unrounded P'.
+#include "fa4_device.h"
+#include "fa4_internal.h"
+
+namespace fa4 {
+
+constexpr int ATT_THREADS = 256;
+constexpr int K4_RS = 80;     // LDS row stride (bytes) of 4-bit K codes (64 B + pad, conflict-free b128 reads)
+constexpr int V8_RS = 144;    // LDS row stride of FP8 V rows (128 B + pad)
+constexpr int H16_RS = 272;   // LDS row stride of 16-bit rows (256 B + pad)
+constexpr float LOG2E = 1.4426950408889634f;
+
+struct AttnArgs {
+  const uint8_t *qc, *qs; const float *qt;
+  const uint8_t *kc, *ks; const float *kt;
+  const uint8_t *vc; const float *vs;
+  const float *vw, *vsig;
+  const uint16_t *qb, *kb, *vb;
+  const uint8_t *bitmap;
+  int B, Hq, Hkv, Lq, Lk, causal;
+  float scale;
+  float *o, *lse;
+};
+
+typedef __attribute__((address_space(3))) v2i lds_v2i;
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+__device__ __forceinline__ v2i lds_tr8(const uint8_t *p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i *)(p));
+}
+__device__ __forceinline__ v4s lds_tr16(const uint8_t *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(p));
+}
+
+// LDS layout (dynamic): [K area | V area | s_v]. The K area holds 4-bit K codes plus E8M0 scales
+// (MXFP4 tiles) or 16-bit K rows (bf16 originals / exact NVFP4 values in fp16); the V area holds FP8
+// V rows or, when bf16 tiles can occur, 16-bit V rows. Quantized and 16-bit tiles never overlap in time.
+template <int QF, bool SEL>
+struct AttnLds {
+  static constexpr int K4 = 128 * K4_RS + 128 * 4;
+  static constexpr int K16 = 128 * H16_RS;
+  static constexpr int KA = (QF == FA4_NVFP4 || SEL) ? (K16 > K4 ? K16 : K4) : K4;
+  static constexpr int VA = SEL ? 128 * H16_RS : 128 * V8_RS;
+  static constexpr int BYTES = KA + VA + 128 * 4;
+};
+
+// Split beta > 0 into 2^k * f with f in [1, 2); k clamped to [-127, 127].
+__device__ __forceinline__ void split_pow2(float beta, int *k, float *f) {
+  const uint32_t b = __float_as_uint(beta);
+  int e = (int)((b >> 23) & 0xffu) - 127;
+  if (e < -126) { *k = -127; *f = 0.0f; return; }       // negligible (or zero) contribution
+  *k = e > 127 ? 127 : e;
+  *f = __uint_as_float((b & 0x807fffffu) | (127u << 23));
+}
+
+template <int D, int QF, bool CAUSAL, bool SEL>
+__global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
+  constexpr int NDB = D / 32;        // 32-row blocks of d in O^T
+  typedef AttnLds<QF, SEL> L;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  uint8_t *const k4 = lds;                       // 4-bit K codes, row stride K4_RS
+  uint8_t *const ksc = lds + 128 * K4_RS;         // E8M0 K scales, 4 bytes per row
+  uint8_t *const k16 = lds;                      // 16-bit K rows, stride H16_RS
+  uint8_t *const vq = lds + L::KA;               // FP8 V rows, stride V8_RS
+  uint8_t *const v16 = lds + L::KA;              // bf16 V rows, stride H16_RS
+  float *const svs = reinterpret_cast<float *>(lds + L::KA + L::VA);
+
+  const int nq = a.Lq / 128, nk = a.Lk / 128;
+  const int qt = nq - 1 - (int)blockIdx.x;          // longest causal rows first
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int kvh = h / (a.Hq / a.Hkv);
+  const int off = a.Lk - a.Lq;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hh = lane >> 5, col = lane & 31;
+  const int qrow = qt * 128 + wave * 32 + col;      // this lane's query (B-operand column)
+  const int64_t bhq = (int64_t)b * a.Hq + h, bhk = (int64_t)b * a.Hkv + kvh;
+
+  // ---- query operand, held in registers for the whole key loop
+  v8i qop4[D / 64];
+  int qsc4[D / 64];
+  v8h qop16[8];
+  float cs_q = a.scale * LOG2E;           // score -> log2 units, quantized tiles
+  const float cs_b = a.scale * LOG2E;     // same for bf16 tiles
+  if (QF == FA4_MXFP4) {
+#pragma unroll
+    for (int s = 0; s < D / 64; s++) {
+      const v4i t = *reinterpret_cast<const v4i *>(a.qc + (bhq * a.Lq + qrow) * (D / 2) + 32 * s + 16 * hh);
+      qop4[s] = (v8i){t[0], t[1], t[2], t[3], 0, 0, 0, 0};
+      qsc4[s] = a.qs[(bhq * a.Lq + qrow) * (D / 32) + 2 * s + hh];
+    }
+  } else {
+    // exact NVFP4 values code * s_b in fp16; the tensor scales move into cs_q
+#pragma unroll
+    for (int s = 0; s < 8; s++) {
+      const uint32_t w = *reinterpret_cast<const uint32_t *>(a.qc + (bhq * a.Lq + qrow) * 64 + 8 * s + 4 * hh);
+      const float sb = e4m3_value(a.qs[(bhq * a.Lq + qrow) * 8 + s]);
+#pragma unroll
+      for (int j = 0; j < 8; j++) qop16[s][j] = (_Float16)(e2m1_value((w >> (4 * j)) & 15u) * sb);
+    }
+    cs_q *= a.qt[bhq] * a.kt[bhk];
+  }
+
+  int kt_end = nk;
+  if (CAUSAL) kt_end = min(nk, (off + qt * 128 + 127) / 128 + 1);
+
+  float m = -INFINITY, lsum = 0.0f, unit = 1.0f;
+  v16f acc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; i++) acc[i] = (v16f){};
+
+  for (int kt = 0; kt < kt_end; kt++) {
+    bool sel = false;
+    if (SEL) sel = a.bitmap[(bhq * nq + qt) * nk + kt] != 0;
+    const int64_t krow0 = bhk * a.Lk + (int64_t)kt * 128;
+    __syncthreads();
+    // ---------------- stage the tile in LDS
+    if (sel) {
+      for (int c = tid; c < 128 * (D / 8); c += ATT_THREADS) {     // 16-byte chunks of bf16 rows
+        const int r = c / (D / 8), j = c % (D / 8);
+        *reinterpret_cast<v4i *>(k16 + r * H16_RS + 16 * j) =
+            *reinterpret_cast<const v4i *>(a.kb + (krow0 + r) * D + 8 * j);
+        *reinterpret_cast<v4i *>(v16 + r * H16_RS + 16 * j) =
+            *reinterpret_cast<const v4i *>(a.vb + (krow0 + r) * D + 8 * j);
+      }
+    } else {
+      if (QF == FA4_MXFP4) {
+        for (int c = tid; c < 128 * (D / 32); c += ATT_THREADS) {  // 16-byte chunks of code rows
+          const int r = c / (D / 32), j = c % (D / 32);
+          *reinterpret_cast<v4i *>(k4 + r * K4_RS + 16 * j) =
+              *reinterpret_cast<const v4i *>(a.kc + (krow0 + r) * (D / 2) + 16 * j);
+        }
+        if (tid < 128) {
+          if (D == 128) *reinterpret_cast<uint32_t *>(ksc + tid * 4) =
+              *reinterpret_cast<const uint32_t *>(a.ks + (krow0 + tid) * 4);
+          else *reinterpret_cast<uint16_t *>(ksc + tid * 4) =
+              *reinterpret_cast<const uint16_t *>(a.ks + (krow0 + tid) * 2);
+        }
+        for (int c = tid; c < 128 * (D / 16); c += ATT_THREADS) {
+          const int r = c / (D / 16), j = c % (D / 16);
+          *reinterpret_cast<v4i *>(vq + r * V8_RS + 16 * j) =
+              *reinterpret_cast<const v4i *>(a.vc + (krow0 + r) * D + 16 * j);
+        }
+      } else {
+        // NVFP4 K -> exact fp16 values in LDS (each thread: half a row, 64 elements)
+        {
+          const int r = tid >> 1, half = tid & 1;
+          const uint8_t *src = a.kc + (krow0 + r) * 64 + 32 * half;
+          const uint32_t sbw = *reinterpret_cast<const uint32_t *>(a.ks + (krow0 + r) * 8 + 4 * half);
+#pragma unroll
+          for (int blk = 0; blk < 4; blk++) {
+            const uint2 w = *reinterpret_cast<const uint2 *>(src + 8 * blk);
+            const float sb = e4m3_value((sbw >> (8 * blk)) & 0xffu);
+            v8h lo, hi;
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+              lo[j] = (_Float16)(e2m1_value((w.x >> (4 * j)) & 15u) * sb);
+              hi[j] = (_Float16)(e2m1_value((w.y >> (4 * j)) & 15u) * sb);
+            }
+            *reinterpret_cast<v8h *>(k16 + r * H16_RS + 2 * (64 * half + 16 * blk)) = lo;
+            *reinterpret_cast<v8h *>(k16 + r * H16_RS + 2 * (64 * half + 16 * blk + 8)) = hi;
+          }
+        }
+        for (int c = tid; c < 128 * (D / 16); c += ATT_THREADS) {
+          const int r = c / (D / 16), j = c % (D / 16);
+          *reinterpret_cast<v4i *>(vq + r * V8_RS + 16 * j) =
+              *reinterpret_cast<const v4i *>(a.vc + (krow0 + r) * D + 16 * j);
+        }
+      }
+      if (tid < 128) svs[tid] = a.vw[krow0 + tid];      // per-key fold factor w_c
+    }
+    __syncthreads();
+
+    // ---------------- S^T = K Q^T : 4 blocks of 32 keys x this wave's 32 queries
+    v16f S[4];
+    if (sel) {
+      v8bf qb[8];
+#pragma unroll
+      for (int s = 0; s < 8; s++)
+        qb[s] = *reinterpret_cast<const v8bf *>(a.qb + (bhq * a.Lq + qrow) * D + 16 * s + 8 * hh);
+#pragma unroll
+      for (int kb = 0; kb < 4; kb++) {
+        S[kb] = (v16f){};
+#pragma unroll
+        for (int s = 0; s < 8; s++) {
+          const v8bf kop = *reinterpret_cast<const v8bf *>(k16 + (32 * kb + col) * H16_RS + 32 * s + 16 * hh);
+          S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qb[s], S[kb], 0, 0, 0);
+        }
+      }
+    } else if (QF == FA4_MXFP4) {
+#pragma unroll
+      for (int kb = 0; kb < 4; kb++) {
+        S[kb] = (v16f){};
+        const int key = 32 * kb + col;
+        const uint32_t scw = *reinterpret_cast<const uint32_t *>(ksc + key * 4);
+#pragma unroll
+        for (int s = 0; s < D / 64; s++) {
+          const v4i t = *reinterpret_cast<const v4i *>(k4 + key * K4_RS + 32 * s + 16 * hh);
+          const v8i kop = (v8i){t[0], t[1], t[2], t[3], 0, 0, 0, 0};
+          const int ksc = (int)((scw >> (8 * (2 * s + hh))) & 0xffu);
+          S[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop, qop4[s], S[kb], 4, 4, 0, ksc, 0, qsc4[s]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 4; kb++) {
+        S[kb] = (v16f){};
+#pragma unroll
+        for (int s = 0; s < 8; s++) {
+          const v8h kop = *reinterpret_cast<const v8h *>(k16 + (32 * kb + col) * H16_RS + 32 * s + 16 * hh);
+          S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop, qop16[s], S[kb], 0, 0, 0);
+        }
+      }
+    }
+
+    // ---------------- softmax step (this lane: query qrow, keys 32kb + 8(i/4) + 4hh + i%4)
+    const float cs = sel ? cs_b : cs_q;
+    const bool diag = CAUSAL && (kt * 128 + 127 > off + qt * 128);
+    const int qpos = qrow + off;
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        if (diag) {
+          const int key = kt * 128 + 32 * kb + 8 * (i / 4) + 4 * hh + (i % 4);
+          if (key > qpos) S[kb][i] = -INFINITY;
+        }
+        mt = fmaxf(mt, S[kb][i]);
+      }
+    mt = fmaxf(mt, shfl_xor_f(mt, 32));
+    const float mt_x = mt * cs;                      // tile max in log2 units
+    const float m_new = fmaxf(m, mt_x);
+    const float alpha = exp2f(m - m_new);            // 0 on the first tile
+    const float betae = exp2f(mt_x - m_new);
+    // (S - m~) is exact at the row maximum, so P' = 1 there exactly, as in the definition
+    float tsum = 0.0f;
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        const float p = __builtin_amdgcn_exp2f((S[kb][i] - mt) * cs);
+        S[kb][i] = p;
+        tsum += p;
+      }
+    lsum = lsum * alpha + tsum * betae;
+    m = m_new;
+
+    float beta = betae;
+    if (!sel) {
+      const float sig = a.vsig[bhk * nk + kt];
+      beta = betae * (sig * (1.0f / 448.0f));
+#pragma unroll
+      for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; a4++) {
+          const float4 w4 = *reinterpret_cast<const float4 *>(&svs[32 * kb + 8 * a4 + 4 * hh]);
+          S[kb][4 * a4 + 0] *= w4.x;
+          S[kb][4 * a4 + 1] *= w4.y;
+          S[kb][4 * a4 + 2] *= w4.z;
+          S[kb][4 * a4 + 3] *= w4.w;
+        }
+    }
+    int k2;
+    float f;
+    split_pow2(beta, &k2, &f);
+    float rho;
+    if (f == 0.0f) {
+      // the tile's weight is below 2^-126 of one accumulator unit: it adds nothing representable.
+      // Its probabilities are zeroed instead of branching, so every lane still feeds the MFMA and
+      // the cross-lane LDS reads below.
+      rho = alpha;
+#pragma unroll
+      for (int kb = 0; kb < 4; kb++) S[kb] = (v16f){};
+    } else {
+      rho = alpha * unit / f;
+      unit = f;
+    }
+#pragma unroll
+    for (int i = 0; i < NDB; i++) acc[i] *= rho;
+
+    // ---------------- O^T += V^T P^T
+    if (sel) {
+#pragma unroll
+      for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+        for (int p = 0; p < 2; p++) {
+          v8s pbs;
+#pragma unroll
+          for (int j = 0; j < 8; j++) pbs[j] = (short)float_to_bf16_bits(ldexpf(S[kb][8 * p + j], k2));
+          const v8bf pb = __builtin_bit_cast(v8bf, pbs);
+#pragma unroll
+          for (int mb = 0; mb < NDB; mb++) {
+            v4s r[2];
+#pragma unroll
+            for (int v = 0; v < 2; v++) {
+              // source lane (16q + a + 4t): key 32kb + 16p + 8v + 4g + t, d 32mb + 16(q%2) + 4a
+              const int q4 = lane >> 4, aa = lane & 3, t = (lane >> 2) & 3;
+              const int key = 32 * kb + 16 * p + 8 * v + 4 * (q4 >> 1) + t;
+              const int dd = 32 * mb + 16 * (q4 & 1) + 4 * aa;
+              r[v] = lds_tr16(v16 + key * H16_RS + 2 * dd);
+            }
+            // whole-vector reinterpretation (inserting bit-cast elements one at a time miscompiles)
+            const v8bf vop = __builtin_bit_cast(v8bf, (v8s)__builtin_shufflevector(r[0], r[1], 0, 1, 2, 3, 4, 5, 6, 7));
+            acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb, acc[mb], 0, 0, 0);
+          }
+        }
+    } else {
+      const uint8_t *vt = vq;
+#pragma unroll
+      for (int t = 0; t < 2; t++) {
+        v8i pop;
+#pragma unroll
+        for (int half = 0; half < 2; half++)
+#pragma unroll
+          for (int w = 0; w < 4; w++) {
+            const v16f &sv = S[2 * t + half];
+            int x = __builtin_amdgcn_cvt_pk_fp8_f32(sv[4 * w], sv[4 * w + 1], 0, false);
+            x = __builtin_amdgcn_cvt_pk_fp8_f32(sv[4 * w + 2], sv[4 * w + 3], x, true);
+            pop[4 * half + w] = x;
+          }
+#pragma unroll
+        for (int mb = 0; mb < NDB; mb++) {
+          v8i vop;
+#pragma unroll
+          for (int u = 0; u < 4; u++) {
+            // source lane (16q + a + 2t'): key 64t + 32(u/2) + 16(u%2) + 8(t'/4) + 4g + t'%4,
+            //                              d 32mb + 16(q%2) + 8a
+            const int q4 = lane >> 4, aa = lane & 1, tp = (lane >> 1) & 7;
+            const int key = 64 * t + 32 * (u >> 1) + 16 * (u & 1) + 8 * (tp >> 2) + 4 * (q4 >> 1) + (tp & 3);
+            const int dd = 32 * mb + 16 * (q4 & 1) + 8 * aa;
+            const v2i r = lds_tr8(vt + key * V8_RS + dd);
+            vop[2 * u] = r[0];
+            vop[2 * u + 1] = r[1];
+          }
+          acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, pop, acc[mb], 0, 0, 0, 127, 0, k2 + 127);
+        }
+      }
+    }
+  }
+
+  // ---------------- epilogue: O = u * O_acc / l, LSE = m ln2 + ln l
+  const float l = lsum + shfl_xor_f(lsum, 32);
+  const float fin = unit / l;
+  float *orow = a.o + (bhq * a.Lq + qrow) * D;
+#pragma unroll
+  for (int mb = 0; mb < NDB; mb++)
+#pragma unroll
+    for (int a4 = 0; a4 < 4; a4++) {
+      const float4 v = make_float4(acc[mb][4 * a4] * fin, acc[mb][4 * a4 + 1] * fin,
+                                   acc[mb][4 * a4 + 2] * fin, acc[mb][4 * a4 + 3] * fin);
+      *reinterpret_cast<float4 *>(orow + 32 * mb + 8 * a4 + 4 * hh) = v;
+    }
+  if (a.lse && hh == 0) a.lse[bhq * a.Lq + qrow] = m * 0.6931471805599453f + logf(l);
+}
+
+// Kernels whose LDS exceeds the default dynamic limit are opted in (idempotent, cheap).
+template <int D, int QF, bool CAUSAL, bool SEL>
+static hipError_t allow_lds() {
+  return hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_fwd_kernel<D, QF, CAUSAL, SEL>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, AttnLds<QF, SEL>::BYTES);
+}
+
+template <int D, int QF>
+static hipError_t launch_attn_t(const AttnArgs &x, bool causal, bool sel, hipStream_t s) {
+  dim3 grid(x.Lq / 128, x.Hq, x.B);
+  hipError_t e = causal ? (sel ? allow_lds<D, QF, true, true>() : allow_lds<D, QF, true, false>())
+                        : (sel ? allow_lds<D, QF, false, true>() : allow_lds<D, QF, false, false>());
+  if (e != hipSuccess) return e;
+  const size_t l1 = AttnLds<QF, true>::BYTES, l0 = AttnLds<QF, false>::BYTES;
+  if (causal) {
+    if (sel) hipLaunchKernelGGL((attn_fwd_kernel<D, QF, true, true>), grid, dim3(ATT_THREADS), l1, s, x);
+    else hipLaunchKernelGGL((attn_fwd_kernel<D, QF, true, false>), grid, dim3(ATT_THREADS), l0, s, x);
+  } else {
+    if (sel) hipLaunchKernelGGL((attn_fwd_kernel<D, QF, false, true>), grid, dim3(ATT_THREADS), l1, s, x);
+    else hipLaunchKernelGGL((attn_fwd_kernel<D, QF, false, false>), grid, dim3(ATT_THREADS), l0, s, x);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn(const fa4_attn_args *p, hipStream_t s) {
+  AttnArgs x;
+  x.qc = p->q_codes; x.qs = p->q_scales; x.qt = p->q_tscale;
+  x.kc = p->k_codes; x.ks = p->k_scales; x.kt = p->k_tscale;
+  x.vc = p->v_codes; x.vs = p->v_scales;
+  x.vw = p->v_fold_w; x.vsig = p->v_fold_sigma;
+  x.qb = p->q_bf16; x.kb = p->k_bf16; x.vb = p->v_bf16;
+  x.bitmap = p->bitmap;
+  x.B = p->B; x.Hq = p->Hq; x.Hkv = p->Hkv; x.Lq = p->Lq; x.Lk = p->Lk; x.causal = p->causal;
+  x.scale = p->softmax_scale;
+  x.o = p->o; x.lse = p->lse;
+  if (x.B == 0 || x.Hq == 0 || x.Lq == 0) return hipSuccess;
+  const bool causal = p->causal != 0, sel = p->bitmap != nullptr;
+  if (p->fmt == FA4_MXFP4) {
+    if (p->d == 64) return launch_attn_t<64, FA4_MXFP4>(x, causal, false, s);
+    return launch_attn_t<128, FA4_MXFP4>(x, causal, sel, s);
+  }
+  return launch_attn_t<128, FA4_NVFP4>(x, causal, sel, s);
+}
+
+}  // namespace fa4

@@ -1,0 +1,198 @@
+// Host side of the C ABI: argument validation, error reporting and dispatch to the kernel launchers.
+// Every check runs before anything is enqueued; a failed check returns its status and records a
+// thread-local message for fa4_last_error().
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "fa4_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fa4_status fail(fa4_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+fa4_status ok() {
+  g_last_error.clear();
+  return FA4_OK;
+}
+
+fa4_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return ok();
+  return fail(FA4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+#define REQUIRE(cond, st, ...) \
+  do {                         \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+// The attention kernel stages tiles in up to ~70 KB of LDS; kernels above the default dynamic limit
+// are opted in once per process.
+}  // namespace
+
+extern "C" {
+
+const char *fa4_status_string(int s) {
+  switch (s) {
+    case FA4_OK: return "ok";
+    case FA4_ERR_NULL: return "null pointer";
+    case FA4_ERR_SHAPE: return "invalid shape";
+    case FA4_ERR_UNSUPPORTED: return "unsupported combination";
+    case FA4_ERR_ALIGN: return "misaligned pointer";
+    case FA4_ERR_WORKSPACE: return "workspace too small";
+    case FA4_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char *fa4_last_error(void) { return g_last_error.c_str(); }
+
+fa4_status fa4_quantize_blockscaled(const fa4_qinput *in, uint32_t flags, const fa4_qoutput *out,
+                                    const fa4_qoutput *residual, float *row_norm2, void *stream) {
+  REQUIRE(in && out, FA4_ERR_NULL, "quantize: input or output descriptor is NULL");
+  REQUIRE(in->dtype == FA4_F32 || in->dtype == FA4_BF16, FA4_ERR_UNSUPPORTED, "quantize: dtype %d", in->dtype);
+  REQUIRE(in->d == 64 || in->d == 128, FA4_ERR_UNSUPPORTED, "quantize: d=%d (64 or 128)", in->d);
+  REQUIRE(out->fmt == FA4_MXFP4 || out->fmt == FA4_NVFP4 || out->fmt == FA4_FP8_TOKEN,
+          FA4_ERR_UNSUPPORTED, "quantize: format %d", out->fmt);
+  REQUIRE((flags & ~(uint32_t)(FA4_HADAMARD128 | FA4_DUAL_RESIDUAL)) == 0, FA4_ERR_UNSUPPORTED,
+          "quantize: unknown flags 0x%x", flags);
+  REQUIRE(in->outer >= 0 && in->heads >= 1 && in->rows >= 0, FA4_ERR_SHAPE,
+          "quantize: outer=%lld heads=%d rows=%lld", (long long)in->outer, in->heads, (long long)in->rows);
+  const int64_t groups = in->outer * in->heads;
+  REQUIRE(groups <= 65535, FA4_ERR_SHAPE, "quantize: %lld groups (at most 65535)", (long long)groups);
+  REQUIRE(in->rows <= (int64_t)1 << 31, FA4_ERR_SHAPE, "quantize: rows=%lld", (long long)in->rows);
+  if (groups == 0 || (in->rows == 0 && out->fmt != FA4_NVFP4)) return ok();
+  REQUIRE(in->rows == 0 || in->x, FA4_ERR_NULL, "quantize: x is NULL");
+  REQUIRE(out->codes || in->rows == 0, FA4_ERR_NULL, "quantize: codes is NULL");
+  if (out->fmt != FA4_FP8_TOKEN && in->rows > 0)
+    REQUIRE(out->block_scales, FA4_ERR_NULL, "quantize: block_scales is NULL");
+  if (out->fmt == FA4_NVFP4) REQUIRE(out->scales, FA4_ERR_NULL, "quantize: NVFP4 tensor scales are NULL");
+  if (out->fmt == FA4_FP8_TOKEN) REQUIRE(out->scales, FA4_ERR_NULL, "quantize: FP8 per-token scales NULL");
+  if (flags & FA4_HADAMARD128) {
+    REQUIRE(in->d == 128, FA4_ERR_UNSUPPORTED, "quantize: Hadamard rotation needs d=128");
+    REQUIRE(out->fmt != FA4_FP8_TOKEN, FA4_ERR_UNSUPPORTED, "quantize: Hadamard rotation with FP8 output");
+  }
+  if (flags & FA4_DUAL_RESIDUAL) {
+    REQUIRE(out->fmt == FA4_NVFP4, FA4_ERR_UNSUPPORTED, "quantize: dual residual needs NVFP4");
+    REQUIRE(residual && residual->scales && (in->rows == 0 || (residual->codes && residual->block_scales)),
+            FA4_ERR_NULL, "quantize: dual residual output missing");
+    REQUIRE(residual->fmt == FA4_NVFP4, FA4_ERR_UNSUPPORTED, "quantize: residual format must be NVFP4");
+    REQUIRE(aligned(residual->codes, 4) && aligned(residual->block_scales, 4) && aligned(residual->scales, 4),
+            FA4_ERR_ALIGN, "quantize: residual outputs must be 4-byte aligned");
+  }
+  const size_t esz = in->dtype == FA4_F32 ? 4 : 2;
+  REQUIRE(in->rows == 0 || aligned(in->x, 4 * esz), FA4_ERR_ALIGN, "quantize: x must be %zu-byte aligned", 4 * esz);
+  REQUIRE(in->stride_outer % 4 == 0 && in->stride_head % 4 == 0 && in->stride_row % 4 == 0, FA4_ERR_ALIGN,
+          "quantize: strides must be multiples of 4 elements");
+  REQUIRE(in->stride_outer >= 0 && in->stride_head >= 0 && in->stride_row >= in->d, FA4_ERR_SHAPE,
+          "quantize: strides must be non-negative and stride_row >= d");
+  REQUIRE(aligned(out->codes, 4) && aligned(out->block_scales, 4) && aligned(out->scales, 4), FA4_ERR_ALIGN,
+          "quantize: outputs must be 4-byte aligned");
+  if (in->page_table) {
+    REQUIRE(in->page_size > 0 && in->max_pages > 0 && in->num_pages > 0, FA4_ERR_SHAPE,
+            "quantize: paged output needs page_size, max_pages and num_pages > 0");
+    REQUIRE(in->rows <= (int64_t)in->page_size * in->max_pages, FA4_ERR_SHAPE,
+            "quantize: rows=%lld exceed max_pages*page_size", (long long)in->rows);
+    REQUIRE(row_norm2 == nullptr, FA4_ERR_UNSUPPORTED, "quantize: row norms need unpaged output");
+  }
+  REQUIRE(aligned(row_norm2, 4), FA4_ERR_ALIGN, "quantize: row_norm2 must be 4-byte aligned");
+  if (out->fold_w || out->fold_sigma) {
+    REQUIRE(out->fmt == FA4_FP8_TOKEN, FA4_ERR_UNSUPPORTED, "quantize: fold outputs need FP8_TOKEN");
+    REQUIRE(out->fold_w && out->fold_sigma, FA4_ERR_NULL, "quantize: fold_w and fold_sigma go together");
+    REQUIRE(in->rows % 128 == 0 && !in->page_table && !in->row_counts, FA4_ERR_UNSUPPORTED,
+            "quantize: fold outputs need unpaged, non-ragged rows in multiples of 128");
+    REQUIRE(aligned(out->fold_w, 4) && aligned(out->fold_sigma, 4), FA4_ERR_ALIGN, "quantize: fold alignment");
+  }
+  return hip_status(fa4::launch_quantize(in, flags, out, residual, row_norm2, (hipStream_t)stream),
+                    "quantize launch");
+}
+
+fa4_status fa4_select_tiles(const float *q_norm2, const float *k_norm2, int32_t B, int32_t Hq, int32_t Hkv,
+                            int32_t Lq, int32_t Lk, int32_t causal, int32_t num, int32_t den,
+                            uint8_t *bitmap, int32_t *counts, void *stream) {
+  REQUIRE(B >= 0 && Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0, FA4_ERR_SHAPE,
+          "select: B=%d Hq=%d Hkv=%d (Hq must be a multiple of Hkv)", B, Hq, Hkv);
+  REQUIRE(Lq > 0 && Lk > 0 && Lq % 128 == 0 && Lk % 128 == 0, FA4_ERR_SHAPE,
+          "select: Lq=%d Lk=%d must be positive multiples of 128", Lq, Lk);
+  REQUIRE(Lq / 128 <= 1024 && Lk / 128 <= 4096, FA4_ERR_SHAPE, "select: at most 1024 x 4096 tiles");
+  REQUIRE(!causal || Lq <= Lk, FA4_ERR_SHAPE, "select: causal needs Lq <= Lk");
+  REQUIRE(den > 0 && num >= 0 && num <= den, FA4_ERR_SHAPE, "select: fraction %d/%d", num, den);
+  REQUIRE(B <= 65535 && Hq <= 65535, FA4_ERR_SHAPE, "select: grid too large");
+  if (B == 0) return ok();
+  REQUIRE(q_norm2 && k_norm2 && bitmap, FA4_ERR_NULL, "select: q_norm2, k_norm2 and bitmap are required");
+  REQUIRE(aligned(q_norm2, 4) && aligned(k_norm2, 4) && aligned(counts, 4), FA4_ERR_ALIGN, "select: alignment");
+  return hip_status(fa4::launch_select(q_norm2, k_norm2, B, Hq, Hkv, Lq, Lk, causal != 0, num, den, bitmap,
+                                       counts, (hipStream_t)stream),
+                    "select launch");
+}
+
+fa4_status fa4_attn_fwd(const fa4_attn_args *a, void *stream) {
+  REQUIRE(a, FA4_ERR_NULL, "attn: args is NULL");
+  REQUIRE(a->fmt == FA4_MXFP4 || a->fmt == FA4_NVFP4, FA4_ERR_UNSUPPORTED, "attn: Q/K format %d", a->fmt);
+  REQUIRE(a->B >= 0 && a->Hq >= 1 && a->Hkv >= 1 && a->Hq % a->Hkv == 0, FA4_ERR_SHAPE,
+          "attn: B=%d Hq=%d Hkv=%d", a->B, a->Hq, a->Hkv);
+  REQUIRE(a->Lq >= 0 && a->Lk > 0 && a->Lq % 128 == 0 && a->Lk % 128 == 0, FA4_ERR_SHAPE,
+          "attn: Lq=%d Lk=%d must be multiples of 128 (Lk > 0)", a->Lq, a->Lk);
+  REQUIRE(!a->causal || a->Lq <= a->Lk, FA4_ERR_SHAPE, "attn: causal needs Lq <= Lk");
+  REQUIRE(a->Lq / 128 <= 65535 && a->Hq <= 65535 && a->B <= 65535, FA4_ERR_SHAPE, "attn: grid too large");
+  if (a->fmt == FA4_MXFP4)
+    REQUIRE(a->d == 128 || (a->d == 64 && !a->bitmap), FA4_ERR_UNSUPPORTED,
+            "attn: MXFP4 supports d=128, or d=64 without tile selection (d=%d)", a->d);
+  else
+    REQUIRE(a->d == 128, FA4_ERR_UNSUPPORTED, "attn: NVFP4 needs d=128 (d=%d)", a->d);
+  if (a->B == 0 || a->Lq == 0) return ok();
+  REQUIRE(a->q_codes && a->q_scales && a->k_codes && a->k_scales && a->v_codes && a->v_scales && a->o &&
+              a->v_fold_w && a->v_fold_sigma,
+          FA4_ERR_NULL, "attn: a required pointer is NULL");
+  if (a->fmt == FA4_NVFP4) REQUIRE(a->q_tscale && a->k_tscale, FA4_ERR_NULL, "attn: NVFP4 tensor scales NULL");
+  if (a->bitmap) REQUIRE(a->q_bf16 && a->k_bf16 && a->v_bf16, FA4_ERR_NULL, "attn: bf16 originals needed with a bitmap");
+  const void *ptrs[] = {a->q_codes, a->q_scales, a->k_codes, a->k_scales, a->v_codes, a->v_scales, a->o,
+                        a->lse, a->q_bf16, a->k_bf16, a->v_bf16, a->q_tscale, a->k_tscale, a->v_fold_w,
+                        a->v_fold_sigma};
+  for (const void *p : ptrs) REQUIRE(aligned(p, 16), FA4_ERR_ALIGN, "attn: every pointer must be 16-byte aligned");
+  REQUIRE(a->softmax_scale > 0.0f, FA4_ERR_SHAPE, "attn: softmax_scale must be positive");
+  return hip_status(fa4::launch_attn(a, (hipStream_t)stream), "attention launch");
+}
+
+size_t fa4_decode_workspace_bytes(const fa4_decode_args *a) {
+  if (!a || a->B <= 0 || a->Hkv <= 0 || a->max_pages <= 0) return 0;
+  return fa4::decode_workspace_bytes(a);
+}
+
+fa4_status fa4_decode_paged(const fa4_decode_args *a, void *ws, size_t ws_bytes, void *stream) {
+  REQUIRE(a, FA4_ERR_NULL, "decode: args is NULL");
+  REQUIRE(a->d == 128, FA4_ERR_UNSUPPORTED, "decode: d=%d (128)", a->d);
+  REQUIRE(a->page_size == 64, FA4_ERR_UNSUPPORTED, "decode: page_size=%d (64)", a->page_size);
+  REQUIRE(a->B >= 0 && a->Hkv >= 1 && a->Hq == 4 * a->Hkv, FA4_ERR_UNSUPPORTED,
+          "decode: needs Hq = 4 Hkv (Hq=%d Hkv=%d)", a->Hq, a->Hkv);
+  REQUIRE(a->max_pages >= 1 && a->num_pages >= 1, FA4_ERR_SHAPE, "decode: max_pages and num_pages >= 1");
+  REQUIRE(a->B <= 65535 && a->Hkv <= 65535 && a->Hq <= 65535, FA4_ERR_SHAPE, "decode: grid too large");
+  REQUIRE((int64_t)a->max_pages * 64 <= ((int64_t)1 << 30), FA4_ERR_SHAPE, "decode: context too long");
+  if (a->B == 0) return ok();
+  REQUIRE(a->q1_codes && a->q1_scales && a->q1_tscale && a->q2_codes && a->q2_scales && a->q2_tscale &&
+              a->k_codes && a->k_scales && a->v_codes && a->v_scales && a->k_tscale && a->v_tscale &&
+              a->page_table && a->ctx_len && a->o,
+          FA4_ERR_NULL, "decode: a required pointer is NULL");
+  const void *ptrs16[] = {a->q1_codes, a->q2_codes, a->k_codes, a->v_codes};
+  for (const void *p : ptrs16) REQUIRE(aligned(p, 16), FA4_ERR_ALIGN, "decode: code arrays must be 16-byte aligned");
+  const void *ptrs8[] = {a->q1_scales, a->q2_scales, a->k_scales, a->v_scales};
+  for (const void *p : ptrs8) REQUIRE(aligned(p, 8), FA4_ERR_ALIGN, "decode: scale arrays must be 8-byte aligned");
+  const size_t need = fa4::decode_workspace_bytes(a);
+  REQUIRE(ws && ws_bytes >= need, FA4_ERR_WORKSPACE, "decode: workspace %zu bytes, %zu needed", ws_bytes, need);
+  REQUIRE(aligned(ws, 256), FA4_ERR_ALIGN, "decode: workspace must be 256-byte aligned");
+  return hip_status(fa4::launch_decode(a, ws, (hipStream_t)stream), "decode launch");
+}
+
+}  // extern "C"

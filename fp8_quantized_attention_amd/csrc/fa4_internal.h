@@ -1,0 +1,18 @@
+// Internal declarations shared by the host-side C ABI and the kernel translation units.
+#pragma once
+#include <hip/hip_runtime.h>
+#include "../../include/fa4.h"
+
+namespace fa4 {
+
+// Each launcher enqueues its kernels on `s` and returns the first launch error (hipSuccess if none).
+// Arguments have been validated by the caller.
+hipError_t launch_quantize(const fa4_qinput *in, uint32_t flags, const fa4_qoutput *out,
+                           const fa4_qoutput *residual, float *row_norm2, hipStream_t s);
+hipError_t launch_select(const float *qn, const float *kn, int B, int Hq, int Hkv, int Lq, int Lk,
+                         int causal, int num, int den, uint8_t *bitmap, int32_t *counts, hipStream_t s);
+hipError_t launch_attn(const fa4_attn_args *a, hipStream_t s);
+size_t decode_workspace_bytes(const fa4_decode_args *a);
+hipError_t launch_decode(const fa4_decode_args *a, void *ws, hipStream_t s);
+
+}  // namespace fa4

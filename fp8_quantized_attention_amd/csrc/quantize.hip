@@ -1,0 +1,329 @@
+// Block-scaled quantizer kernels for gfx950: MXFP4, NVFP4 (tensor-amax pre-pass, dual residual),
+// FP8 per-token V, optional 128-point Hadamard rotation and squared row norms.
+//
+// Sources: "MXFP vs NVFP4" (tqpw.cn 81738) sections 2.1-2.2 (block structures) and 3.1 (a fused
+// quantization kernel computing in registers with coalesced global access); "BitDecoding-FP4"
+// (dual-residual query, Hadamard rotation of keys); "General notes on quantization" (X ~ s * Q,
+// per-token and per-group scales); "MpFA QK4V8" section 5.1 (zero maxima must not give a zero scale).
+//
+// Layout of the work: a row of d elements is spread over d/4 lanes, 4 consecutive elements per lane
+// (d = 128: 32 lanes, two rows per wave; d = 64: 16 lanes, four rows per wave). Loads are 16 B
+// (float) or 8 B (bf16) per lane and the packed codes of a row are written as one contiguous run,
+// so both directions are coalesced. Block maxima come from xor-shuffles inside the 8 (MX) or 4 (NV)
+// lanes of a block. A workgroup owns a chunk of rows of one group, so the NVFP4 tensor maximum is
+// reduced in LDS and published with one atomicMax per workgroup (max is order-independent, so the
+// result is deterministic).
+#include "fa4_device.h"
+#include "fa4_internal.h"
+
+namespace fa4 {
+
+constexpr int QUANT_THREADS = 256;
+constexpr int QUANT_CHUNK = 256;     // rows per workgroup
+
+// 1/sqrt(128) as the float64 nearest to 1/fl64(sqrt(128)).
+#define FA4_RSQRT128 0x1.6a09e667f3bccp-4
+
+struct QArgs {
+  const void *x;
+  int64_t outer, rows;
+  int heads;
+  int64_t so, sh, sr;
+  const int32_t *row_counts;
+  const int32_t *page_table;
+  int page_size, max_pages;
+  int64_t num_pages;
+  uint8_t *codes, *bscales;
+  float *scales;        // NVFP4: running max then tensor scale per group; FP8: per row
+  uint8_t *rcodes, *rbscales;
+  float *rscales;       // residual (dual) tensor maxima / scales
+  float *norm2;
+  float *fold_w, *fold_sigma;
+};
+
+template <int DT>
+__device__ __forceinline__ void load4(const void *x, int64_t off, float v[4]) {
+  if (DT == 0) {
+    const float4 t = *reinterpret_cast<const float4 *>(static_cast<const float *>(x) + off);
+    v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+  } else {
+    const uint2 t = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(x) + off);
+    v[0] = bf16_bits_to_float(t.x & 0xffffu); v[1] = bf16_bits_to_float(t.x >> 16);
+    v[2] = bf16_bits_to_float(t.y & 0xffffu); v[3] = bf16_bits_to_float(t.y >> 16);
+  }
+}
+
+// In-place Sylvester Hadamard transform of a 128-row held 4 per lane over 32 lanes, float64,
+// then scaled by 1/sqrt(128) and rounded once to float32.
+__device__ __forceinline__ void hadamard128(float v[4]) {
+  double a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
+  double b0 = a0 + a1, b1 = a0 - a1, b2 = a2 + a3, b3 = a2 - a3;       // distance 1
+  a0 = b0 + b2; a2 = b0 - b2; a1 = b1 + b3; a3 = b1 - b3;               // distance 2
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int m = 1; m < 32; m <<= 1) {                                     // distance 4 .. 64
+    const double p0 = shfl_xor_d(a0, m), p1 = shfl_xor_d(a1, m), p2 = shfl_xor_d(a2, m),
+                 p3 = shfl_xor_d(a3, m);
+    if (lane & m) { a0 = p0 - a0; a1 = p1 - a1; a2 = p2 - a2; a3 = p3 - a3; }
+    else          { a0 = a0 + p0; a1 = a1 + p1; a2 = a2 + p2; a3 = a3 + p3; }
+  }
+  v[0] = (float)(a0 * FA4_RSQRT128); v[1] = (float)(a1 * FA4_RSQRT128);
+  v[2] = (float)(a2 * FA4_RSQRT128); v[3] = (float)(a3 * FA4_RSQRT128);
+}
+
+// max over the lanes of an aligned group of `n` lanes (n a power of two <= 32)
+__device__ __forceinline__ float group_max(float v, int n) {
+  for (int m = 1; m < n; m <<= 1) v = fmaxf(v, shfl_xor_f(v, m));
+  return v;
+}
+
+// NVFP4 codes of 4 elements given the tensor scale; also returns the dequantized values (float64).
+__device__ __forceinline__ uint32_t nv_codes4(const float v[4], float st, uint32_t *sb_out,
+                                              double xh[4]) {
+  float am = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+  am = group_max(am, 4);                                    // 16-element block = 4 lanes
+  const float six_st = 6.0f * st;
+  const uint32_t sb = e4m3_encode(am / six_st);
+  const float sbv = e4m3_value(sb);
+  const float denom = sbv * st;
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    uint32_t ci;
+    if (sb == 0u) ci = (__float_as_uint(v[i]) >> 28) & 8u;
+    else ci = e2m1_encode(v[i] / denom);
+    c |= ci << (4 * i);
+    xh[i] = (double)(e2m1_value(ci) * sbv) * (double)st;
+  }
+  *sb_out = sb;
+  return c;
+}
+
+__device__ __forceinline__ float tensor_scale_from_max(float amax) {
+  return amax == 0.0f ? 1.0f : amax / 2688.0f;
+}
+
+// PASS: 0 = group maxima (NVFP4), 1 = codes (+ residual maxima when DUAL), 2 = residual codes.
+template <int D, int DT, int FMT, int PASS, bool HAD, bool DUAL, bool NORM>
+__global__ void __launch_bounds__(QUANT_THREADS) quantize_kernel(QArgs a) {
+  constexpr int LPR = D / 4;              // lanes per row
+  constexpr int RPW = 64 / LPR;           // rows per wave
+  constexpr int RPB = RPW * (QUANT_THREADS / 64);
+  __shared__ float red[QUANT_THREADS / 64];
+
+  const int g = blockIdx.y;               // group = o * heads + h
+  const int64_t o = g / a.heads;
+  const int h = g - (int)o * a.heads;
+  int64_t nrows = a.rows;
+  if (a.row_counts) nrows = min<int64_t>(nrows, (int64_t)a.row_counts[o]);
+  const int64_t r0 = (int64_t)blockIdx.x * QUANT_CHUNK;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane / LPR, li = lane % LPR;
+
+  float st = 1.0f, rst = 1.0f;
+  if (FMT == FA4_NVFP4 && PASS >= 1) {
+    st = tensor_scale_from_max(a.scales[g]);
+    if (PASS == 2) rst = tensor_scale_from_max(a.rscales[g]);
+  }
+  float gmax = 0.0f;
+
+  for (int64_t rr = r0 + wave * RPW + sub; rr < r0 + QUANT_CHUNK; rr += RPB) {
+    const bool active = rr < nrows;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (active) load4<DT>(a.x, o * a.so + h * a.sh + rr * a.sr + li * 4, v);
+    // rows are processed by whole lane groups, so inactive lanes only feed zeros to the shuffles
+    if (NORM && PASS <= 1) {
+      double s = ((double)v[0] * v[0] + (double)v[1] * v[1]) + ((double)v[2] * v[2] + (double)v[3] * v[3]);
+      for (int m = 1; m < LPR; m <<= 1) s = s + shfl_xor_d(s, m);
+      if (active && li == 0) a.norm2[(int64_t)g * a.rows + rr] = (float)s;
+    }
+    if (HAD) hadamard128(v);
+    int64_t orow = (int64_t)g * a.rows + rr;
+    bool store = active;
+    if (a.page_table) {
+      // only rows that exist read the page table; a page id outside the cache drops the row
+      const int pg = active ? a.page_table[o * a.max_pages + rr / a.page_size] : 0;
+      store = active && pg >= 0 && (int64_t)pg < a.num_pages;
+      orow = ((int64_t)(store ? pg : 0) * a.heads + h) * a.page_size + rr % a.page_size;
+    }
+    if (FMT == FA4_MXFP4) {
+      float am = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+      am = group_max(am, 8);                                  // 32-element block = 8 lanes
+      const int e = mx_exponent(am);
+      const float mul = pow2_neg(e);
+      uint32_t c = 0;
+#pragma unroll
+      for (int i = 0; i < 4; i++) c |= e2m1_encode(v[i] * mul) << (4 * i);
+      if (store) {
+        *reinterpret_cast<uint16_t *>(a.codes + orow * (D / 2) + li * 2) = (uint16_t)c;
+        if ((li & 7) == 0) a.bscales[orow * (D / 32) + li / 8] = (uint8_t)(e + 127);
+      }
+    } else if (FMT == FA4_FP8_TOKEN) {
+      float am = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+      am = group_max(am, LPR);
+      const float s = am == 0.0f ? 1.0f : am / 448.0f;
+      const uint32_t c = e4m3_encode2(v[0] / s, v[1] / s) | (e4m3_encode2(v[2] / s, v[3] / s) << 16);
+      if (store) {
+        *reinterpret_cast<uint32_t *>(a.codes + orow * D + li * 4) = c;
+        if (li == 0) a.scales[orow] = s;
+      }
+    } else {  // NVFP4
+      if (PASS == 0) {
+        float am = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+        gmax = fmaxf(gmax, active ? am : 0.0f);
+      } else {
+        uint32_t sb;
+        double xh[4];
+        const uint32_t c = nv_codes4(v, st, &sb, xh);
+        if (PASS == 1) {
+          if (store) {
+            *reinterpret_cast<uint16_t *>(a.codes + orow * (D / 2) + li * 2) = (uint16_t)c;
+            if ((li & 3) == 0) a.bscales[orow * (D / 16) + li / 4] = (uint8_t)sb;
+          }
+          if (DUAL) {
+            float am = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; i++) am = fmaxf(am, fabsf((float)((double)v[i] - xh[i])));
+            gmax = fmaxf(gmax, active ? am : 0.0f);
+          }
+        } else {  // PASS 2: residual codes
+          float rv[4];
+#pragma unroll
+          for (int i = 0; i < 4; i++) rv[i] = (float)((double)v[i] - xh[i]);
+          uint32_t rsb;
+          double rxh[4];
+          const uint32_t rc = nv_codes4(rv, rst, &rsb, rxh);
+          if (store) {
+            *reinterpret_cast<uint16_t *>(a.rcodes + orow * (D / 2) + li * 2) = (uint16_t)rc;
+            if ((li & 3) == 0) a.rbscales[orow * (D / 16) + li / 4] = (uint8_t)rsb;
+          }
+        }
+      }
+    }
+  }
+  if (FMT == FA4_NVFP4 && (PASS == 0 || (PASS == 1 && DUAL))) {
+    for (int m = 1; m < 64; m <<= 1) gmax = fmaxf(gmax, shfl_xor_f(gmax, m));
+    if (lane == 0) red[wave] = gmax;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float m = red[0];
+      for (int w = 1; w < QUANT_THREADS / 64; w++) m = fmaxf(m, red[w]);
+      float *dst = PASS == 0 ? a.scales : a.rscales;
+      // non-negative floats order like their bit patterns
+      atomicMax(reinterpret_cast<unsigned int *>(dst + g), __float_as_uint(m));
+    }
+  }
+}
+
+// Fold data of FP8 per-token V for the attention kernel: per 128-row tile, sigma = max of the row
+// scales and, per row, w = 448 s / sigma computed in float64 and rounded to float32 with round-to-odd.
+// Round-to-odd to 24 bits followed by a round-to-nearest to E4M3's 4 bits gives the same code as
+// rounding the float64 value directly (the intermediate keeps more than 4 + 2 bits), which matters
+// because bf16 inputs make 448 s / sigma land on or next to E4M3 rounding midpoints.
+__global__ void __launch_bounds__(128) fold_kernel(const float *scales, float *fold_w, float *fold_sigma,
+                                                   int64_t rows) {
+  __shared__ float red[2];
+  const int64_t g = blockIdx.y, tile = blockIdx.x;
+  const int t = threadIdx.x;
+  const int64_t row = g * rows + tile * 128 + t;
+  const float sv = scales[row];
+  float m = sv;
+  for (int k = 1; k < 64; k <<= 1) m = fmaxf(m, shfl_xor_f(m, k));
+  if ((t & 63) == 0) red[t >> 6] = m;
+  __syncthreads();
+  const float sigma = fmaxf(red[0], red[1]);
+  const double w64 = 448.0 * (double)sv / (double)sigma;
+  float w = __double2float_rz(w64);
+  if ((double)w != w64) w = __uint_as_float(__float_as_uint(w) | 1u);
+  fold_w[row] = w;
+  if (t == 0) fold_sigma[g * (rows / 128) + tile] = sigma;
+}
+
+__global__ void fill_zero_kernel(float *p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.0f;
+}
+
+__global__ void finalize_tensor_scale_kernel(float *p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = tensor_scale_from_max(p[i]);
+}
+
+template <int D, int DT, int FMT, int PASS, bool HAD, bool DUAL>
+static hipError_t launch_q(const QArgs &a, int64_t groups, bool norm, hipStream_t s) {
+  if (a.rows == 0 || groups == 0) return hipSuccess;       // nothing to read (NVFP4 scales still finalize)
+  dim3 grid((unsigned)((a.rows + QUANT_CHUNK - 1) / QUANT_CHUNK), (unsigned)groups);
+  if (norm)
+    hipLaunchKernelGGL((quantize_kernel<D, DT, FMT, PASS, HAD, DUAL, true>), grid, dim3(QUANT_THREADS), 0, s, a);
+  else
+    hipLaunchKernelGGL((quantize_kernel<D, DT, FMT, PASS, HAD, DUAL, false>), grid, dim3(QUANT_THREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D, int DT>
+static hipError_t quantize_dispatch(const QArgs &a, int fmt, bool had, bool dual, int64_t groups,
+                                    bool norm, hipStream_t s) {
+  hipError_t e = hipSuccess;
+  const unsigned small = (unsigned)((groups + 255) / 256);
+  if (fmt == FA4_MXFP4) {
+    if (had) return launch_q<D, DT, FA4_MXFP4, 1, true, false>(a, groups, norm, s);
+    return launch_q<D, DT, FA4_MXFP4, 1, false, false>(a, groups, norm, s);
+  }
+  if (fmt == FA4_FP8_TOKEN) {
+    if ((e = launch_q<D, DT, FA4_FP8_TOKEN, 1, false, false>(a, groups, norm, s)) != hipSuccess) return e;
+    if (a.fold_w && a.rows > 0 && groups > 0) {
+      hipLaunchKernelGGL(fold_kernel, dim3((unsigned)(a.rows / 128), (unsigned)groups), dim3(128), 0, s,
+                         a.scales, a.fold_w, a.fold_sigma, a.rows);
+      e = hipGetLastError();
+    }
+    return e;
+  }
+  // NVFP4: zero the group maxima, reduce them, quantize, turn maxima into tensor scales
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(small), dim3(256), 0, s, a.scales, groups);
+  if (dual) hipLaunchKernelGGL(fill_zero_kernel, dim3(small), dim3(256), 0, s, a.rscales, groups);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (had) {
+    if ((e = launch_q<D, DT, FA4_NVFP4, 0, true, false>(a, groups, norm, s)) != hipSuccess) return e;
+    if (dual) {
+      if ((e = launch_q<D, DT, FA4_NVFP4, 1, true, true>(a, groups, false, s)) != hipSuccess) return e;
+      if ((e = launch_q<D, DT, FA4_NVFP4, 2, true, true>(a, groups, false, s)) != hipSuccess) return e;
+    } else if ((e = launch_q<D, DT, FA4_NVFP4, 1, true, false>(a, groups, false, s)) != hipSuccess) {
+      return e;
+    }
+  } else {
+    if ((e = launch_q<D, DT, FA4_NVFP4, 0, false, false>(a, groups, norm, s)) != hipSuccess) return e;
+    if (dual) {
+      if ((e = launch_q<D, DT, FA4_NVFP4, 1, false, true>(a, groups, false, s)) != hipSuccess) return e;
+      if ((e = launch_q<D, DT, FA4_NVFP4, 2, false, true>(a, groups, false, s)) != hipSuccess) return e;
+    } else if ((e = launch_q<D, DT, FA4_NVFP4, 1, false, false>(a, groups, false, s)) != hipSuccess) {
+      return e;
+    }
+  }
+  hipLaunchKernelGGL(finalize_tensor_scale_kernel, dim3(small), dim3(256), 0, s, a.scales, groups);
+  if (dual) hipLaunchKernelGGL(finalize_tensor_scale_kernel, dim3(small), dim3(256), 0, s, a.rscales, groups);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const fa4_qinput *in, uint32_t flags, const fa4_qoutput *out,
+                           const fa4_qoutput *res, float *norm2, hipStream_t s) {
+  QArgs a;
+  a.x = in->x; a.outer = in->outer; a.rows = in->rows; a.heads = in->heads;
+  a.so = in->stride_outer; a.sh = in->stride_head; a.sr = in->stride_row;
+  a.row_counts = in->row_counts; a.page_table = in->page_table;
+  a.page_size = in->page_size; a.max_pages = in->max_pages; a.num_pages = in->num_pages;
+  a.codes = out->codes; a.bscales = out->block_scales; a.scales = out->scales;
+  a.rcodes = res ? res->codes : nullptr; a.rbscales = res ? res->block_scales : nullptr;
+  a.rscales = res ? res->scales : nullptr;
+  a.norm2 = norm2;
+  a.fold_w = out->fold_w; a.fold_sigma = out->fold_sigma;
+  const int64_t groups = in->outer * in->heads;
+  const bool had = flags & FA4_HADAMARD128, dual = flags & FA4_DUAL_RESIDUAL, norm = norm2 != nullptr;
+  if (in->d == 128) {
+    return in->dtype == FA4_F32 ? quantize_dispatch<128, 0>(a, out->fmt, had, dual, groups, norm, s)
+                                : quantize_dispatch<128, 1>(a, out->fmt, had, dual, groups, norm, s);
+  }
+  return in->dtype == FA4_F32 ? quantize_dispatch<64, 0>(a, out->fmt, false, dual, groups, norm, s)
+                              : quantize_dispatch<64, 1>(a, out->fmt, false, dual, groups, norm, s);
+}
+
+}  // namespace fa4

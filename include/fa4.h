@@ -1,0 +1,218 @@
+/*
+ * fa4.h - block-scaled low-bit fused attention on AMD MI355X (gfx950): the C ABI.
+ *
+ * Four entry points make up the path:
+ *   fa4_quantize_blockscaled  Q/K -> 4-bit E2M1 with block scales (MXFP4 or NVFP4), V -> FP8 E4M3
+ *   fa4_select_tiles          ThriftAttention-style choice of the 128x128 tiles computed in bf16
+ *   fa4_attn_fwd              fused prefill attention (scaled-MFMA QK^T and PV, FP32 online softmax)
+ *   fa4_decode_paged          decode attention over a paged NVFP4 KV cache
+ *
+ * Conventions shared by every call:
+ *   - Every pointer in an argument struct is a DEVICE pointer owned by the caller and must stay valid
+ *     until the work enqueued on `stream` has finished. The library allocates nothing and keeps no
+ *     state apart from a thread-local error string.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Calls enqueue work and return at once.
+ *   - Arguments are validated before anything is enqueued; a failed check returns its status and
+ *     enqueues nothing. fa4_last_error() then names the failed check. Launch failures return
+ *     FA4_ERR_HIP; faults inside a kernel surface at the caller's next synchronisation.
+ *   - Inputs must be finite; non-finite inputs give unspecified values but never out-of-bounds access.
+ *   - All reductions are deterministic: equal inputs give bitwise-equal outputs.
+ *   - Element sizes: codes are bytes; 4-bit codes are packed two per byte, element 2i in bits 3:0 and
+ *     element 2i+1 in bits 7:4. E2M1 value grid: {0, 0.5, 1, 1.5, 2, 3, 4, 6} with a sign bit.
+ *     E4M3 is the OCP "fn" variant (largest finite 448, no infinities). E8M0 byte c means 2^(c-127).
+ */
+#ifndef FA4_H
+#define FA4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA4_OK = 0,
+  FA4_ERR_NULL = 1,          /* a required pointer is NULL                              */
+  FA4_ERR_SHAPE = 2,         /* a size is out of range or inconsistent                   */
+  FA4_ERR_UNSUPPORTED = 3,   /* a valid but unimplemented combination (format, d, flags) */
+  FA4_ERR_ALIGN = 4,         /* a pointer is not aligned as documented                   */
+  FA4_ERR_WORKSPACE = 5,     /* workspace missing or smaller than required               */
+  FA4_ERR_HIP = 6            /* the HIP runtime reported an error                        */
+} fa4_status;
+
+enum { FA4_F32 = 0, FA4_BF16 = 1 };                      /* input element types       */
+enum { FA4_MXFP4 = 0, FA4_NVFP4 = 1, FA4_FP8_TOKEN = 2 }; /* quantized formats         */
+enum { FA4_HADAMARD128 = 1u << 0, FA4_DUAL_RESIDUAL = 1u << 1 }; /* quantizer flags    */
+
+/* ------------------------------------------------------------------------------------------------
+ * Quantization.
+ *
+ * Source pages: "MXFP vs NVFP4" (tqpw.cn 81738) sections 2.1-2.2 (MXFP4: 32-element blocks with an
+ * E8M0 scale; NVFP4: 16-element blocks with an E4M3 scale and an FP32 tensor scale);
+ * "General notes on quantization" (zdszero) (X ~ s * Q; per-token / per-group / per-tensor scales);
+ * "BitDecoding-FP4" (dual-residual query quantization, Hadamard rotation before key quantization);
+ * "MpFA QK4V8" sections 2.1-2.2 (Q and K in 4 bits, V in 8 bits).
+ *
+ * Input rows: the tensor is a set of groups g = o * heads + h (o < outer, h < heads), each holding
+ * `rows` rows of d elements; row r of group (o, h) starts at element
+ *     o * stride_outer + h * stride_head + r * stride_row        (element strides, not bytes).
+ * row_counts (optional, [outer] int32): only rows r < row_counts[o] exist (a ragged batch).
+ * page_table (optional, [outer][max_pages] int32): write rows into a paged cache; row r of group
+ * (o, h) goes to output row (page_table[o][r / page_size] * heads + h) * page_size + r % page_size.
+ * Without a page table, row r of group g goes to output row g * rows + r.
+ *
+ * Formats (per output row of d elements):
+ *   FA4_MXFP4: codes [d/2] bytes; block_scales [d/32] E8M0: per 32 elements, amax = max|x|, scale =
+ *              the smallest power of two 2^e with 6 * 2^e >= amax (e = -127 if amax = 0), codes =
+ *              E2M1(x * 2^-e) rounded to nearest even. `scales` unused (may be NULL).
+ *   FA4_NVFP4: codes [d/2]; block_scales [d/16] E4M3; scales = tensor scale per group [outer*heads]
+ *              float: s_t = amax_group / 2688 (1 if zero), s_b = E4M3(amax_block / (6 s_t)),
+ *              codes = E2M1(x / (E4M3value(s_b) * s_t)) (float32, IEEE division); value = code*s_b*s_t.
+ *   FA4_FP8_TOKEN: codes [d] E4M3; scales = per-row float [out rows]: s = amax_row / 448 (1 if zero),
+ *              codes = E4M3(x / s). block_scales unused.
+ * flags: FA4_HADAMARD128 rotates each row by the Sylvester Hadamard matrix H_128 / sqrt(128) (float64,
+ *        rounded to float32) before quantizing (d must be 128; NVFP4 or MXFP4 only).
+ *        FA4_DUAL_RESIDUAL (NVFP4 only): `out` receives Q1 = NVFP4(x) and `residual` receives
+ *        Q2 = NVFP4(float32(x - dequant(Q1))), with its own tensor scales.
+ * fold_w / fold_sigma (FP8_TOKEN, optional, unpaged, rows a multiple of 128): the data that folds the
+ *        per-token V scale into the attention probabilities. For each 128-row tile j of a group,
+ *        fold_sigma[j] = sigma = max of the tile's scales, and for each row c, fold_w[c] = the float64
+ *        quotient 448 * s[c] / sigma rounded to float32 with round-to-odd (truncate, then set the last
+ *        bit if inexact), so that one later round-to-nearest to E4M3 of 1 * fold_w[c] equals the E4M3
+ *        rounding of the float64 quotient itself. fa4_attn_fwd consumes both arrays.
+ * row_norm2 (optional, [outer*heads*rows] float, unpaged only): squared L2 norm of each UNROTATED
+ *        input row, float64 pairwise (binary-tree) sum over d, rounded to float32.
+ * During the call the tensor-scale array holds intermediate maxima; it holds s_t when the work ends.
+ * Requirements: d in {64, 128}; codes, block_scales 4-byte aligned; x aligned to its element size
+ * times 4; strides multiples of 4 elements. Returns FA4_ERR_* without enqueuing on a failed check.
+ */
+typedef struct {
+  const void *x;               /* input elements (FA4_F32 float or FA4_BF16 bf16 bits)            */
+  int32_t dtype;               /* FA4_F32 or FA4_BF16                                             */
+  int32_t d;                   /* row length: 64 or 128                                           */
+  int64_t outer;               /* number of outer indices o                                       */
+  int32_t heads;               /* heads per outer index                                           */
+  int64_t rows;                /* rows per group (the maximum when row_counts is given)            */
+  int64_t stride_outer, stride_head, stride_row;   /* element strides                             */
+  const int32_t *row_counts;   /* optional [outer]                                                */
+  const int32_t *page_table;   /* optional [outer][max_pages]                                     */
+  int32_t page_size, max_pages;
+  int64_t num_pages;           /* pages in the output cache (paged output only)                   */
+} fa4_qinput;
+
+typedef struct {
+  int32_t fmt;                 /* FA4_MXFP4, FA4_NVFP4 or FA4_FP8_TOKEN                           */
+  uint8_t *codes;
+  uint8_t *block_scales;
+  float *scales;               /* NVFP4: [outer*heads] tensor scales; FP8_TOKEN: [out rows]       */
+  float *fold_w;               /* FP8_TOKEN, optional: [out rows] P-fold factor w (see below)     */
+  float *fold_sigma;           /* FP8_TOKEN, optional: [out rows / 128] tile maximum of the scales */
+} fa4_qoutput;
+
+fa4_status fa4_quantize_blockscaled(const fa4_qinput *in, uint32_t flags, const fa4_qoutput *out,
+                                    const fa4_qoutput *residual, float *row_norm2, void *stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * Tile selection.
+ *
+ * Source page: "ThriftAttention" (ai-feeds.com summary), Method step 2 and Limitations: 128x128
+ * query-key tiles are scored cheaply from norms and the top ~5% are computed in high precision.
+ *
+ * q_norm2 [B][Hq][Lq], k_norm2 [B][Hkv][Lk]: squared row norms (fa4_quantize_blockscaled's row_norm2).
+ * a_i = max q_norm2 over q-tile i, b_j = max k_norm2 over k-tile j (key head h / (Hq/Hkv));
+ * score_ij = float32(a_i * b_j). Candidates are the valid tiles: all tiles if !causal, else those with
+ * 128 j <= (Lk - Lq) + 128 i + 127 (query i sits at key position Lk - Lq + i). Per (b, h) the
+ * k = ceil(num * N_valid / den) best candidates are chosen, ordered by score (descending) then by
+ * linear index i * (Lk/128) + j (ascending), so the choice is unique.
+ * Output: bitmap [B][Hq][Lq/128][Lk/128] bytes (1 = bf16 tile), counts [B][Hq] int32 (optional).
+ * Requirements: Lq, Lk multiples of 128; Lq/128 <= 1024; Lk/128 <= 4096; Hq % Hkv == 0;
+ * 0 <= num <= den, den > 0.
+ */
+fa4_status fa4_select_tiles(const float *q_norm2, const float *k_norm2, int32_t B, int32_t Hq,
+                            int32_t Hkv, int32_t Lq, int32_t Lk, int32_t causal, int32_t num,
+                            int32_t den, uint8_t *bitmap, int32_t *counts, void *stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * Prefill attention.
+ *
+ * Source pages: "MpFA QK4V8" sections 2.1-2.2, 3.2-3.4 (4-bit QK^T with in-kernel block scales, 8-bit
+ * PV, FP32 online softmax, tiling); "ThriftAttention" Method step 3 (selected tiles in high precision
+ * merged through the same online softmax); "BitDecoding-FP4" (probabilities quantized with a scale
+ * that cannot underflow); "General notes on quantization" (scale factoring / merging of scales).
+ *
+ * For query row r of head h (key head kv = h / (Hq/Hkv), query position Lk - Lq + r) and each
+ * 128-key tile j holding an unmasked key (key c unmasked if !causal or c <= r + Lk - Lq):
+ *   S = softmax_scale * q~ . k~ with the dequantized Q/K codes (or the bf16 originals if selected);
+ *   m~ = tile row max, P' = exp(S - m~);
+ *   unselected: sigma = max s_v over the tile, w_c = 448 s_v[c] / sigma, P^ = E4M3(P' w_c),
+ *               T = (sigma / 448) * sum_c P^ * E4M3value(Vcode_c)     (FP8 x FP8 products);
+ *   selected:   T = sum_c bf16(P') * v_c with the bf16 originals;
+ *   O = sum_j e^(m~_j - m) T_j / sum_j e^(m~_j - m) sum_c P'   (m = max_j m~_j), LSE = m + ln(denominator).
+ * Layouts: q_codes [B][Hq][Lq][d/2], q_scales [B][Hq][Lq][d/32] (MXFP4) or [d/16] (NVFP4) with
+ * q_tscale [B*Hq]; k_* likewise over [B][Hkv][Lk]; v_codes [B][Hkv][Lk][d] E4M3 with v_scales
+ * [B][Hkv][Lk], v_fold_w [B][Hkv][Lk] and v_fold_sigma [B][Hkv][Lk/128] (the quantizer's fold
+ * outputs: P' * w_c is formed as P' * v_fold_w[c], with P' exactly 1 at a tile's row maximum); q_bf16 [B][Hq][Lq][d], k_bf16 / v_bf16 [B][Hkv][Lk][d] (bf16 bits; required when
+ * bitmap is given); bitmap [B][Hq][Lq/128][Lk/128] or NULL; o [B][Hq][Lq][d] float; lse [B][Hq][Lq]
+ * float or NULL. Requirements: d = 128 (or 64 for MXFP4 without a bitmap); Lq, Lk multiples of 128;
+ * Lq <= Lk when causal; Hq % Hkv == 0; every pointer 16-byte aligned.
+ */
+typedef struct {
+  int32_t fmt;                                  /* FA4_MXFP4 or FA4_NVFP4 (format of Q and K) */
+  const uint8_t *q_codes, *q_scales; const float *q_tscale;
+  const uint8_t *k_codes, *k_scales; const float *k_tscale;
+  const uint8_t *v_codes; const float *v_scales;
+  const float *v_fold_w, *v_fold_sigma;        /* fa4_quantize_blockscaled's FP8 fold outputs     */
+  const uint16_t *q_bf16, *k_bf16, *v_bf16;
+  const uint8_t *bitmap;
+  int32_t B, Hq, Hkv, Lq, Lk, d, causal;
+  float softmax_scale;
+  float *o;
+  float *lse;
+} fa4_attn_args;
+
+fa4_status fa4_attn_fwd(const fa4_attn_args *a, void *stream);
+
+/* ------------------------------------------------------------------------------------------------
+ * Paged decode.
+ *
+ * Source page: "BitDecoding-FP4" (sns.style digest): native FP4 KV-cache decode over pages, dual-
+ * residual query (q ~ Q1 + Q2, both FP4), underflow-aware probability scaling, query heads of one
+ * GQA group stacked into one matrix-core tile.
+ *
+ * For sequence b and query head h (key head kv = h / (Hq/Hkv)) over keys c < ctx_len[b]:
+ *   q^ = dequant(Q1) + dequant(Q2); S_c = softmax_scale * q^ . k^_c with the NVFP4-dequantized keys;
+ *   per 128-key tile (from position 0, the last one partial): m~ = tile max, P' = exp(S - m~),
+ *   P^ = E4M3(448 P'), T = (1/448) sum_c P^ v^_c; O = sum e^(m~-m) T / sum e^(m~-m) sum P'.
+ * Layouts: q1_codes/q2_codes [B][Hq][d/2], q1_scales/q2_scales [B][Hq][d/16] E4M3, q1_tscale/
+ * q2_tscale [B*Hq]; k_codes/v_codes [num_pages][Hkv][page_size][d/2], k_scales/v_scales
+ * [num_pages][Hkv][page_size][d/16]; k_tscale/v_tscale [B][Hkv]; page_table [B][max_pages] (entries
+ * past ceil(ctx_len[b]/page_size) are not read); o [B][Hq][d] float.
+ * The work is split over key ranges; partial results go to a caller-provided workspace of
+ * fa4_decode_workspace_bytes(a) bytes (256-byte aligned) and are merged by a second kernel.
+ * Requirements: d = 128; page_size = 64; Hq / Hkv = 4; 1 <= ctx_len[b] <= max_pages * page_size.
+ */
+typedef struct {
+  const uint8_t *q1_codes, *q1_scales; const float *q1_tscale;
+  const uint8_t *q2_codes, *q2_scales; const float *q2_tscale;
+  const uint8_t *k_codes, *k_scales, *v_codes, *v_scales;
+  const float *k_tscale, *v_tscale;
+  const int32_t *page_table, *ctx_len;
+  int32_t B, Hq, Hkv, d, page_size, max_pages;
+  int64_t num_pages;
+  float softmax_scale;
+  float *o;
+} fa4_decode_args;
+
+size_t fa4_decode_workspace_bytes(const fa4_decode_args *a);
+fa4_status fa4_decode_paged(const fa4_decode_args *a, void *workspace, size_t workspace_bytes,
+                            void *stream);
+
+/* ------------------------------------------------------------------------------------------------ */
+const char *fa4_status_string(int status);   /* static text of a status code                        */
+const char *fa4_last_error(void);            /* detail of this thread's last failed call ("" if none) */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FA4_H */

@@ -1,0 +1,121 @@
+"""Oracle-side construction of reference results for the workloads (CPU only, float64).
+
+Everything here starts from workloads.py's seeded inputs and calls only oracle/; nothing comes from
+the GPU path. Per-head helpers keep the full-size workloads affordable: only the heads whose rows are
+sampled are quantized and attended on the CPU.
+"""
+import numpy as np
+
+import workloads as W
+from oracle import attention as A
+from oracle import decode as Dd
+from oracle import quant as Q
+from oracle import selection as S
+
+# Parity bar for attention outputs: relative L2 and max-abs relative to max|O|.
+REL_L2 = 1e-3
+MAX_ABS = 2e-3
+
+
+def rel_errors(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300)
+    mx = np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-300)
+    return rel, mx
+
+
+def assert_parity(got, ref, what=""):
+    rel, mx = rel_errors(got, ref)
+    assert rel <= REL_L2 and mx <= MAX_ABS, f"{what}: rel-L2 {rel:.3e} max-abs/max {mx:.3e}"
+    return rel, mx
+
+
+def quant_head(cfg, x, rotate):
+    """Dequantized Q or K values of one head ([L, d] float64) under the workload's Q/K format."""
+    xr = Q.hadamard_rotate(x) if rotate else x
+    if cfg.qk_fmt == "mxfp4":
+        return Q.mxfp4_dequantize(*Q.mxfp4_quantize(xr))
+    return Q.nvfp4_dequantize(*Q.nvfp4_quantize(xr[None]))[0]
+
+
+def prefill_reference(cfg, seed, heads, rows, select=None, q_all=None, k_all=None, v_all=None):
+    """Oracle O and LSE for the listed (b, h) pairs and query rows.
+
+    select = (num, den) enables tile selection (norms, tile maxima and top-k from the oracle).
+    q_all/k_all/v_all: optional host tensors already generated (else chunks are regenerated).
+    Returns (O [len(heads), R, d], LSE [len(heads), R], bitmaps {(b, h): [nq, nk]}).
+    """
+    group = cfg.Hq // cfg.Hkv
+    rows = np.asarray(rows)
+    outs, lses, bitmaps = [], [], {}
+    kv_cache = {}
+    for (b, h) in heads:
+        kvh = h // group
+        q = (q_all[b, h] if q_all is not None else W.prefill_head(cfg, W.T_Q, b, h, seed)).double().numpy()
+        if (b, kvh) not in kv_cache:
+            k = (k_all[b, kvh] if k_all is not None else W.prefill_head(cfg, W.T_K, b, kvh, seed)).double().numpy()
+            v = (v_all[b, kvh] if v_all is not None else W.prefill_head(cfg, W.T_V, b, kvh, seed)).double().numpy()
+            kd = quant_head(cfg, k, cfg.hadamard)
+            vc, sv = Q.fp8_per_token_quantize(v)
+            kn = Q.row_norm2(k)
+            kv_cache = {(b, kvh): (k, v, kd, vc, sv, kn)}
+        k, v, kd, vc, sv, kn = kv_cache[(b, kvh)]
+        qd = quant_head(cfg, q, cfg.hadamard)
+        bm = None
+        if select is not None:
+            qn = Q.row_norm2(q)
+            bm, _ = S.select_tiles(qn[None, None], kn[None, None], cfg.Lq, cfg.Lk, cfg.causal, select[0], select[1])
+            bm = bm[0, 0]
+            bitmaps[(b, h)] = bm
+        O, L = A.attention_prefill(qd[None, None], kd[None, None], vc[None, None], sv[None, None], cfg.causal,
+                                   q_orig=q[None, None], k_orig=k[None, None], v_orig=v[None, None],
+                                   bitmap=None if bm is None else bm[None, None], rows=rows)
+        outs.append(O[0, 0]); lses.append(L[0, 0])
+    return np.stack(outs), np.stack(lses), bitmaps
+
+
+def decode_cache(cfg, layout, seed, pairs_only=None):
+    """Oracle NVFP4 pages of K and V, quantized per (sequence, key head) and scattered by the page table.
+
+    pairs_only: optional set of (b, kvh) to build (others stay zero). Returns
+    ((kc, ks), (vc, vs), k_tscale, v_tscale, dequantized logical rows {(tensor, b, kvh): [L, d]}).
+    """
+    d, ps = cfg.d, cfg.page_size
+    P = layout.num_pages
+    kc = np.zeros((P, cfg.Hkv, ps, d // 2), np.uint8); ks = np.zeros((P, cfg.Hkv, ps, d // 16), np.uint8)
+    vc = np.zeros_like(kc); vs = np.zeros_like(ks)
+    kt = np.zeros((cfg.B, cfg.Hkv), np.float32); vt = np.zeros_like(kt)
+    logical = {}
+    for b in range(cfg.B):
+        L = int(layout.ctx_len[b])
+        c = np.arange(L)
+        phys = layout.page_table[b].numpy()[c // ps]
+        for h in range(cfg.Hkv):
+            if pairs_only is not None and (b, h) not in pairs_only:
+                continue
+            for tensor, (codes, scales, ts) in [(W.T_K, (kc, ks, kt)), (W.T_V, (vc, vs, vt))]:
+                x = W.decode_kv_head(cfg, tensor, b, h, L, seed).double().numpy()
+                qc, qs, qt = Q.nvfp4_quantize(x[None])
+                codes[phys, h, c % ps] = qc[0]
+                scales[phys, h, c % ps] = qs[0]
+                ts[b, h] = qt[0]
+                logical[(tensor, b, h)] = Q.nvfp4_dequantize(qc, qs, qt)[0]
+    return (kc, ks), (vc, vs), kt, vt, logical
+
+
+def decode_query_quant(cfg, seed):
+    q = W.decode_query(cfg, seed).double().numpy()
+    return q, Q.dual_residual_quantize(q.reshape(cfg.B * cfg.Hq, 1, cfg.d))
+
+
+def decode_reference(cfg, seed, layout, pairs, logical, q1, q2):
+    """Oracle O for the listed (b, h) pairs from contiguous dequantized rows."""
+    qhat = Dd.dequant_query(q1, q2).reshape(cfg.B, cfg.Hq, cfg.d)
+    group = cfg.Hq // cfg.Hkv
+    out = []
+    for (b, h) in pairs:
+        kh = logical[(W.T_K, b, h // group)]
+        vh = logical[(W.T_V, b, h // group)]
+        out.append(Dd.decode_one(qhat[b, h], kh, vh, 1.0 / np.sqrt(cfg.d)).astype(np.float32))
+    return np.stack(out)

@@ -1,0 +1,157 @@
+"""The C ABI without a GPU: the library loads, exports what include/fa4.h declares, the ctypes mirror
+matches the C struct layouts, and invalid arguments are rejected before anything is enqueued."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa4.h")
+
+fa4 = pytest.importorskip("fp8_quantized_attention_amd")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa4_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    names = _declared_functions()
+    assert set(names) == set(fa4.EXPORTS)
+    for n in names:
+        assert hasattr(fa4.lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", fa4.LIB_PATH], capture_output=True, text=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}\b", out), f"{n} not exported"
+
+
+def test_struct_layouts_match_header(tmp_path):
+    structs = {"fa4_qinput": fa4.QInput, "fa4_qoutput": fa4.QOutput, "fa4_attn_args": fa4.AttnArgs,
+               "fa4_decode_args": fa4.DecodeArgs}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'printf("{cname} %zu\\n", sizeof({cname}));')
+        for fname, _ in py._fields_:
+            lines.append(f'printf("{cname}.{fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines.append("return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-o", str(exe), str(src)], check=True)
+    got = dict(l.split() for l in subprocess.run([str(exe)], capture_output=True, text=True).stdout.split("\n") if l)
+    for cname, py in structs.items():
+        assert int(got[cname]) == ctypes.sizeof(py), cname
+        for fname, _ in py._fields_:
+            assert int(got[f"{cname}.{fname}"]) == getattr(py, fname).offset, f"{cname}.{fname}"
+
+
+def test_status_strings():
+    assert fa4.lib.fa4_status_string(0) == b"ok"
+    assert fa4.lib.fa4_status_string(fa4.FA4_ERR_WORKSPACE) == b"workspace too small"
+
+
+def _q(**kw):
+    base = dict(x=16, dtype=fa4.FA4_BF16, d=128, outer=1, heads=2, rows=256, stride_outer=2 * 256 * 128,
+                stride_head=256 * 128, stride_row=128, row_counts=None, page_table=None, page_size=0,
+                max_pages=0, num_pages=0)
+    base.update(kw)
+    return fa4.QInput(*[base[f] for f, _ in fa4.QInput._fields_])
+
+
+def _call_q(qin, fmt=fa4.FA4_MXFP4, flags=0, codes=256, bs=256, sc=256, res=None, norm=None):
+    qout = fa4.QOutput(fmt, codes, bs, sc)
+    return fa4.lib.fa4_quantize_blockscaled(ctypes.byref(qin), flags, ctypes.byref(qout),
+                                            ctypes.byref(res) if res is not None else None, norm, None)
+
+
+def test_quantize_rejects_before_launch():
+    assert fa4.lib.fa4_quantize_blockscaled(None, 0, None, None, None, None) == fa4.FA4_ERR_NULL
+    assert _call_q(_q(d=96)) == fa4.FA4_ERR_UNSUPPORTED
+    assert _call_q(_q(dtype=7)) == fa4.FA4_ERR_UNSUPPORTED
+    assert _call_q(_q(), fmt=9) == fa4.FA4_ERR_UNSUPPORTED
+    assert _call_q(_q(x=None)) == fa4.FA4_ERR_NULL
+    assert _call_q(_q(x=18)) == fa4.FA4_ERR_ALIGN
+    assert _call_q(_q(stride_row=130)) == fa4.FA4_ERR_ALIGN
+    assert _call_q(_q(), codes=None) == fa4.FA4_ERR_NULL
+    assert _call_q(_q(), fmt=fa4.FA4_NVFP4, sc=None) == fa4.FA4_ERR_NULL
+    assert _call_q(_q(d=64), flags=fa4.FA4_HADAMARD128) == fa4.FA4_ERR_UNSUPPORTED
+    assert _call_q(_q(), flags=fa4.FA4_DUAL_RESIDUAL) == fa4.FA4_ERR_UNSUPPORTED          # needs NVFP4
+    assert _call_q(_q(), fmt=fa4.FA4_NVFP4, flags=fa4.FA4_DUAL_RESIDUAL) == fa4.FA4_ERR_NULL
+    assert _call_q(_q(), flags=1 << 5) == fa4.FA4_ERR_UNSUPPORTED
+    assert _call_q(_q(outer=70000)) == fa4.FA4_ERR_SHAPE
+    assert _call_q(_q(page_table=64, page_size=64, max_pages=2, num_pages=4)) == fa4.FA4_ERR_SHAPE  # rows > 128
+    assert b"rows=256" in fa4.lib.fa4_last_error()
+    qout = fa4.QOutput(fa4.FA4_MXFP4, 256, 256, 256, 256, 256)                # fold data needs FP8
+    assert fa4.lib.fa4_quantize_blockscaled(ctypes.byref(_q()), 0, ctypes.byref(qout), None, None, None) \
+        == fa4.FA4_ERR_UNSUPPORTED
+    qout = fa4.QOutput(fa4.FA4_FP8_TOKEN, 256, None, 256, 256, 256)
+    assert fa4.lib.fa4_quantize_blockscaled(ctypes.byref(_q(rows=200)), 0, ctypes.byref(qout), None, None, None) \
+        == fa4.FA4_ERR_UNSUPPORTED
+    assert _call_q(_q(rows=0)) == fa4.FA4_OK                # nothing to do, no launch
+    assert fa4.lib.fa4_last_error() == b""
+
+
+def _attn(**kw):
+    base = dict(fmt=fa4.FA4_MXFP4, q_codes=256, q_scales=256, q_tscale=None, k_codes=256, k_scales=256,
+                k_tscale=None, v_codes=256, v_scales=256, v_fold_w=256, v_fold_sigma=256, q_bf16=None, k_bf16=None, v_bf16=None, bitmap=None,
+                B=1, Hq=4, Hkv=2, Lq=256, Lk=512, d=128, causal=1, softmax_scale=0.088, o=256, lse=None)
+    base.update(kw)
+    return fa4.AttnArgs(*[base[f] for f, _ in fa4.AttnArgs._fields_])
+
+
+def test_attention_rejects_before_launch():
+    call = lambda a: fa4.lib.fa4_attn_fwd(ctypes.byref(a), None)
+    assert fa4.lib.fa4_attn_fwd(None, None) == fa4.FA4_ERR_NULL
+    assert call(_attn(fmt=5)) == fa4.FA4_ERR_UNSUPPORTED
+    assert call(_attn(Hq=3)) == fa4.FA4_ERR_SHAPE
+    assert call(_attn(Lq=200)) == fa4.FA4_ERR_SHAPE
+    assert call(_attn(Lq=1024, Lk=512)) == fa4.FA4_ERR_SHAPE          # causal with Lq > Lk
+    assert call(_attn(d=96)) == fa4.FA4_ERR_UNSUPPORTED
+    assert call(_attn(d=64, bitmap=256)) == fa4.FA4_ERR_UNSUPPORTED
+    assert call(_attn(fmt=fa4.FA4_NVFP4, d=64)) == fa4.FA4_ERR_UNSUPPORTED
+    assert call(_attn(fmt=fa4.FA4_NVFP4)) == fa4.FA4_ERR_NULL         # tensor scales missing
+    assert call(_attn(bitmap=256)) == fa4.FA4_ERR_NULL                # bf16 originals missing
+    assert call(_attn(o=None)) == fa4.FA4_ERR_NULL
+    assert call(_attn(v_fold_w=None)) == fa4.FA4_ERR_NULL
+    assert call(_attn(v_codes=264)) == fa4.FA4_ERR_ALIGN
+    assert call(_attn(softmax_scale=0.0)) == fa4.FA4_ERR_SHAPE
+    assert call(_attn(Lq=0)) == fa4.FA4_OK
+
+
+def test_select_rejects_before_launch():
+    f = fa4.lib.fa4_select_tiles
+    assert f(256, 256, 1, 4, 3, 256, 256, 1, 5, 100, 256, None, None) == fa4.FA4_ERR_SHAPE
+    assert f(256, 256, 1, 4, 2, 200, 256, 1, 5, 100, 256, None, None) == fa4.FA4_ERR_SHAPE
+    assert f(256, 256, 1, 4, 2, 256, 256, 1, 101, 100, 256, None, None) == fa4.FA4_ERR_SHAPE
+    assert f(256, 256, 1, 4, 2, 256, 128, 1, 5, 100, 256, None, None) == fa4.FA4_ERR_SHAPE
+    assert f(256, 256, 1, 4, 2, 128 * 2048, 128 * 2048, 0, 5, 100, 256, None, None) == fa4.FA4_ERR_SHAPE
+    assert f(None, 256, 1, 4, 2, 256, 256, 1, 5, 100, 256, None, None) == fa4.FA4_ERR_NULL
+
+
+def _dec(**kw):
+    base = dict(q1_codes=256, q1_scales=256, q1_tscale=256, q2_codes=256, q2_scales=256, q2_tscale=256,
+                k_codes=256, k_scales=256, v_codes=256, v_scales=256, k_tscale=256, v_tscale=256,
+                page_table=256, ctx_len=256, B=4, Hq=32, Hkv=8, d=128, page_size=64, max_pages=8, num_pages=32,
+                softmax_scale=0.088, o=256)
+    base.update(kw)
+    return fa4.DecodeArgs(*[base[f] for f, _ in fa4.DecodeArgs._fields_])
+
+
+def test_decode_rejects_before_launch():
+    call = lambda a, ws=512, n=1 << 30: fa4.lib.fa4_decode_paged(ctypes.byref(a), ws, n, None)
+    a = _dec()
+    need = fa4.lib.fa4_decode_workspace_bytes(ctypes.byref(a))
+    assert need == 4 * 8 * 1 * 4 * 130 * 4
+    assert call(_dec(d=64)) == fa4.FA4_ERR_UNSUPPORTED
+    assert call(_dec(page_size=32)) == fa4.FA4_ERR_UNSUPPORTED
+    assert call(_dec(Hq=16)) == fa4.FA4_ERR_UNSUPPORTED
+    assert call(_dec(k_codes=None)) == fa4.FA4_ERR_NULL
+    assert call(_dec(k_codes=264)) == fa4.FA4_ERR_ALIGN
+    assert call(a, ws=512, n=need - 1) == fa4.FA4_ERR_WORKSPACE
+    assert call(a, ws=None, n=need) == fa4.FA4_ERR_WORKSPACE
+    assert call(a, ws=520, n=need) == fa4.FA4_ERR_ALIGN
+    assert call(_dec(B=0)) == fa4.FA4_OK

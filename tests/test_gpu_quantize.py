@@ -1,0 +1,149 @@
+"""GPU quantizers vs the oracle: codes, block scales, tensor scales, per-token scales and row norms
+must match bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import quant as Q
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fa4():
+    import fp8_quantized_attention_amd as m
+    return m
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _special_rows(d=128, rows=64, seed=0):
+    """float32 rows mixing zeros, signed zeros, tiny and huge magnitudes and exact E2M1 ties."""
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((rows, d)) * np.exp2(rng.integers(-30, 30, (rows, 1)))).astype(np.float32)
+    x[0] = 0.0
+    x[1] = -0.0
+    x[2] = 1e-40                                   # subnormal
+    x[3, :32] = [6.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.25, -0.75, -1.25, -1.75, -2.5, -3.5, -5.0, 5.5,
+                 0.0, -0.0, 3.0, 4.0, 1.5, 0.5, 1.0, 2.0, -6.0, 6.0, 0.1, -0.1, 2.75, 4.5, 5.25, 0.3]
+    x[4] = 3.0e38
+    x[5, ::2] = 0.0
+    x[6] = np.float32(6.0) * np.float32(2.0 ** -126)
+    return x
+
+
+def test_mxfp4_tiny_fp32_d64(fa4):
+    q, k, v = W.prefill_inputs(W.C0)
+    out = fa4.quantize(q.cuda(), fa4.FA4_MXFP4, row_norms=True)
+    codes, scales = Q.mxfp4_quantize(q.numpy())
+    assert np.array_equal(_np(out["codes"]), codes)
+    assert np.array_equal(_np(out["block_scales"]), scales)
+    assert np.array_equal(_np(out["norm2"]), Q.row_norm2(q.numpy()))
+
+
+def test_mxfp4_bf16_outliers_and_special_values(fa4):
+    cfg = W.C1.scaled(Hq=2, Hkv=2, Lq=512, Lk=512)
+    _, k, _ = W.prefill_inputs(cfg)
+    out = fa4.quantize(k.cuda(), fa4.FA4_MXFP4, row_norms=True)
+    kf = k.float().numpy()
+    codes, scales = Q.mxfp4_quantize(kf)
+    assert np.array_equal(_np(out["codes"]), codes)
+    assert np.array_equal(_np(out["block_scales"]), scales)
+    assert np.array_equal(_np(out["norm2"]), Q.row_norm2(kf))
+    x = _special_rows()[None, None]
+    out = fa4.quantize(torch.from_numpy(x).cuda(), fa4.FA4_MXFP4)
+    codes, scales = Q.mxfp4_quantize(x)
+    assert np.array_equal(_np(out["codes"]), codes)
+    assert np.array_equal(_np(out["block_scales"]), scales)
+
+
+def _round_to_odd_f32(x64):
+    """float64 -> float32 with round-to-odd: truncate toward zero, then set the last bit if inexact."""
+    f = x64.astype(np.float32)
+    over = np.abs(f.astype(np.float64)) > np.abs(x64)
+    f = np.where(over, np.nextafter(f, np.float32(0)), f).astype(np.float32)
+    inexact = f.astype(np.float64) != x64
+    return np.where(inexact, (f.view(np.uint32) | 1).view(np.float32), f)
+
+
+def test_fp8_per_token(fa4):
+    cfg = W.C1.scaled(Hq=2, Hkv=2, Lq=512, Lk=512)
+    _, _, v = W.prefill_inputs(cfg)
+    out = fa4.quantize(v.cuda(), fa4.FA4_FP8_TOKEN)
+    codes, sv = Q.fp8_per_token_quantize(v.float().numpy())
+    assert np.array_equal(_np(out["codes"]), codes)
+    assert np.array_equal(_np(out["scales"]), sv)
+    # fold data: sigma = tile max of s_v; w = 448 s_v / sigma (float64) rounded to float32 by round-to-odd
+    tiles = sv.reshape(1, 2, -1, 128)
+    sigma = tiles.max(axis=-1)
+    w64 = 448.0 * tiles.astype(np.float64) / sigma[..., None].astype(np.float64)
+    assert np.array_equal(_np(out["fold_sigma"]), sigma)
+    assert np.array_equal(_np(out["fold_w"]), _round_to_odd_f32(w64).reshape(1, 2, -1))
+    x = _special_rows(seed=1)[None, None]
+    x[0, 0, 4] = 1e30                                # stays finite through the per-token scale
+    out = fa4.quantize(torch.from_numpy(x).cuda(), fa4.FA4_FP8_TOKEN)
+    codes, sv = Q.fp8_per_token_quantize(x)
+    assert np.array_equal(_np(out["codes"]), codes)
+    assert np.array_equal(_np(out["scales"]), sv)
+
+
+@pytest.mark.parametrize("hadamard", [False, True])
+def test_nvfp4_tensor_block_scales_and_hadamard(fa4, hadamard):
+    cfg = W.C4.scaled(Hq=8, Hkv=2, Lq=256, Lk=1024)
+    q, k, _ = W.prefill_inputs(cfg)
+    for x in (q, k):
+        out = fa4.quantize(x.cuda(), fa4.FA4_NVFP4, hadamard=hadamard, row_norms=True)
+        xf = x.float().numpy().astype(np.float64)
+        xr = Q.hadamard_rotate(xf) if hadamard else xf
+        B, H, L, d = x.shape
+        codes, sb, st = Q.nvfp4_quantize(xr.reshape(B * H, L, d))
+        assert np.array_equal(_np(out["scales"]), st)
+        assert np.array_equal(_np(out["block_scales"]).reshape(B * H, L, -1), sb)
+        assert np.array_equal(_np(out["codes"]).reshape(B * H, L, -1), codes)
+        assert np.array_equal(_np(out["norm2"]), Q.row_norm2(xf))
+
+
+def test_nvfp4_special_values_and_empty(fa4):
+    x = _special_rows(seed=2).reshape(2, 32, 128)[None]
+    out = fa4.quantize(torch.from_numpy(np.ascontiguousarray(x)).cuda(), fa4.FA4_NVFP4)
+    codes, sb, st = Q.nvfp4_quantize(x[0])
+    assert np.array_equal(_np(out["scales"]), st)
+    assert np.array_equal(_np(out["block_scales"])[0], sb)
+    assert np.array_equal(_np(out["codes"])[0], codes)
+    empty = torch.zeros(1, 3, 0, 128, device="cuda")
+    out = fa4.quantize(empty, fa4.FA4_NVFP4)
+    assert np.array_equal(_np(out["scales"]), np.ones(3, np.float32))
+
+
+def test_dual_residual_query(fa4):
+    q = W.decode_query(W.C3)                          # [64, 32, 128] bf16
+    out = fa4.quantize(q.reshape(64, 32, 1, 128).cuda(), fa4.FA4_NVFP4, dual=True)
+    (c1, s1, t1), (c2, s2, t2) = Q.dual_residual_quantize(q.float().numpy().reshape(64 * 32, 1, 128))
+    assert np.array_equal(_np(out["scales"]), t1) and np.array_equal(_np(out["scales2"]), t2)
+    assert np.array_equal(_np(out["block_scales"]).reshape(2048, 1, -1), s1)
+    assert np.array_equal(_np(out["block_scales2"]).reshape(2048, 1, -1), s2)
+    assert np.array_equal(_np(out["codes"]).reshape(2048, 1, -1), c1)
+    assert np.array_equal(_np(out["codes2"]).reshape(2048, 1, -1), c2)
+
+
+def test_paged_kv_cache(fa4):
+    from oracle_cases import decode_cache
+    cfg = W.C3.scaled(B=3, Hq=8, Hkv=2, ctx_lo=200, ctx_hi=700)
+    lay = W.decode_layout(cfg)
+    (kc, ks), (vc, vs), kt, vt, _ = decode_cache(cfg, lay, 0)
+    ctx = lay.ctx_len.cuda()
+    pt = lay.page_table.cuda()
+    for tensor, (rc, rs, rt) in [(W.T_K, (kc, ks, kt)), (W.T_V, (vc, vs, vt))]:
+        x = W.decode_kv_padded(cfg, lay, tensor, device="cuda")
+        out = fa4.quantize_paged(x, fa4.FA4_NVFP4, ctx, pt, lay.num_pages)
+        assert np.array_equal(_np(out["scales"]).reshape(cfg.B, cfg.Hkv), rt)
+        # compare every row that exists
+        for b in range(cfg.B):
+            L = int(lay.ctx_len[b])
+            c = np.arange(L)
+            phys = lay.page_table[b].numpy()[c // 64]
+            assert np.array_equal(_np(out["codes"])[phys, :, c % 64], rc[phys, :, c % 64])
+            assert np.array_equal(_np(out["block_scales"])[phys, :, c % 64], rs[phys, :, c % 64])
