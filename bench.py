@@ -1,0 +1,175 @@
+#!/usr/bin/env python3
+"""Benchmark of block-scaled low-bit fused attention on one MI355X.
+
+One step = the whole prefill path on the 4K causal workload (B=1, H=32, L=4096, d=128): MXFP4
+quantization of Q and K, FP8 per-token quantization of V (with its P-fold data) and the fused
+attention kernel, inputs resident in HBM. `value` is prefill attention TFLOP/s over the step
+(algorithmic flops: 4 d per unmasked query-key pair). The same line carries:
+  roofline      the attention kernel alone: its algorithmic flops / its average launch time (HIP
+                events on the launch stream) against the dense MXFP4 MFMA peak;
+  decode        the paged NVFP4 decode step (64 sequences, 32 -> 8 GQA heads, contexts 8K-32K):
+                KV-cache GB/s, and the decode kernels' HBM roofline;
+  cpu_baseline  the CPU oracle (float64 numpy) on a bounded sample of the same workload.
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-decode] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+METRIC = "prefill attn TFLOP/s + decode KV GB/s, as % of MXFP4-MFMA / HBM peak"
+MXFP4_PEAK_TFLOPS = 10100.0          # dense MFMA, FP4/FP6
+HBM_PEAK_GBS = 8000.0
+
+
+def causal_pairs(Lq, Lk, causal):
+    if not causal:
+        return Lq * Lk
+    off = Lk - Lq
+    return sum(min(Lk, off + r + 1) for r in range(Lq))
+
+
+def prefill_flops(cfg):
+    return 4.0 * cfg.d * causal_pairs(cfg.Lq, cfg.Lk, cfg.causal) * cfg.B * cfg.Hq
+
+
+def time_prefill(fa4, cfg, steps, warmup, select):
+    q, k, v = (t.cuda() for t in W.prefill_inputs(cfg))
+    fmt = fa4.FA4_MXFP4 if cfg.qk_fmt == "mxfp4" else fa4.FA4_NVFP4
+    run = fa4.PrefillRunner(q, k, v, cfg.causal, fmt=fmt, hadamard=cfg.hadamard, select=select)
+    for _ in range(warmup):
+        run.run()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0.record()
+    for i in range(steps):
+        run.quantize()
+        ev[i][0].record()
+        run.attention()
+        ev[i][1].record()
+    t1.record()
+    torch.cuda.synchronize()
+    step_ms = t0.elapsed_time(t1) / steps
+    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    return step_ms, attn_ms
+
+
+def time_decode(fa4, cfg, steps, warmup):
+    lay = W.decode_layout(cfg)
+    ctx, pt = lay.ctx_len.cuda(), lay.page_table.cuda()
+    caches = []
+    for tensor in (W.T_K, W.T_V):
+        x = W.decode_kv_padded(cfg, lay, tensor, device="cuda")
+        caches.append(fa4.quantize_paged(x, fa4.FA4_NVFP4, ctx, pt, lay.num_pages))
+        del x
+    torch.cuda.empty_cache()
+    q = W.decode_query(cfg).cuda()
+    run = fa4.DecodeRunner(q, caches[0], caches[1], pt, ctx, cfg.Hkv)
+    for _ in range(warmup):
+        run.run()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0.record()
+    for i in range(steps):
+        run.quantize()
+        ev[i][0].record()
+        run.attention()
+        ev[i][1].record()
+    t1.record()
+    torch.cuda.synchronize()
+    step_ms = t0.elapsed_time(t1) / steps
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    kv_bytes = float(lay.ctx_len.double().sum()) * cfg.Hkv * 2 * (cfg.d // 2 + cfg.d // 16)
+    return step_ms, kern_ms, kv_bytes, int(lay.ctx_len.sum())
+
+
+def cpu_baseline(cfg, heads):
+    """The oracle as it stands on `heads` query heads of the workload (quantize + attend every row)."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from oracle_cases import prefill_reference
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count()
+    t = time.time()
+    prefill_reference(cfg, 0, [(0, h) for h in range(heads)], np.arange(cfg.Lq))
+    secs = time.time() - t
+    flops = prefill_flops(cfg) * heads / (cfg.B * cfg.Hq)
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{heads} of {cfg.Hq} heads, all {cfg.Lq} query rows (quantize Q/K/V + attention), "
+                      f"{secs:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=W.C1.name,
+                    choices=[c.name for c in W.WORKLOADS if isinstance(c, W.Prefill)])
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=8)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import fp8_quantized_attention_amd as fa4
+
+    cfg = next(c for c in W.WORKLOADS if c.name == args.workload)
+    select = (5, 100) if cfg.select else None
+    step_ms, attn_ms = time_prefill(fa4, cfg, args.steps, args.warmup, select)
+    flops = prefill_flops(cfg)
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": flops / (step_ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4+fp8" if cfg.qk_fmt == "mxfp4" else "nvfp4+fp8",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "Lq": cfg.Lq, "Lk": cfg.Lk,
+                   "d": cfg.d, "causal": cfg.causal, "qk_format": cfg.qk_fmt, "hadamard": cfg.hadamard,
+                   "bf16_tiles": "5%" if select else "none", "algorithmic_flops": flops},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / MXFP4_PEAK_TFLOPS, "traffic": None, "kernel": "attn_fwd_kernel",
+                     "kernel_ms": attn_ms},
+    }
+    print(f"[bench] prefill {cfg.name}: step {step_ms:.4f} ms, attention {attn_ms:.4f} ms", file=sys.stderr,
+          flush=True)
+    if not args.no_decode:
+        d_step, d_kern, kv_bytes, tokens = time_decode(fa4, W.C3, args.steps, args.warmup)
+        gbs = kv_bytes / (d_kern * 1e-3) / 1e9
+        line["decode"] = {
+            "metric": "decode KV GB/s", "workload": W.C3.name, "value": kv_bytes / (d_step * 1e-3) / 1e9,
+            "unit": "GB/s", "ms_per_step": d_step, "kv_bytes": kv_bytes, "context_tokens": tokens,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "decode_split+combine",
+                         "kernel_ms": d_kern}}
+        print(f"[bench] decode: step {d_step:.4f} ms, kernels {d_kern:.4f} ms, {gbs:.0f} GB/s", file=sys.stderr,
+              flush=True)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, min(args.cpu_heads, cfg.Hq))
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

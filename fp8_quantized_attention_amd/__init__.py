@@ -283,3 +283,117 @@ def decode(q, kcache, vcache, page_table, ctx_len, Hkv, softmax_scale=None, work
     o = decode_paged(q1, q2, kcache, vcache, page_table, ctx_len, Hq, Hkv, d, softmax_scale=softmax_scale,
                      workspace=workspace, out=out)
     return o, qq
+
+
+# ---------------------------------------------------------------------------------------------------- runners
+
+class PrefillRunner:
+    """Preallocated prefill path for repeated calls on fixed shapes (benchmarks, serving loops).
+
+    Builds every ABI argument struct once; run() enqueues the quantizer, selector and attention calls
+    on the current stream with no allocation. Inputs are read from the tensors given here, so refill
+    them in place to change the data.
+    """
+
+    def __init__(self, q, k, v, causal, fmt=FA4_MXFP4, hadamard=False, select=None, softmax_scale=None):
+        self.q, self.k, self.v = q, k, v
+        B, Hq, Lq, d = q.shape
+        Hkv, Lk = k.shape[1], k.shape[2]
+        dev = q.device
+        self.sel = select is not None
+        self.causal, self.fmt, self.select = causal, fmt, select
+        self.flags = FA4_HADAMARD128 if hadamard else 0
+        u8, f32 = dict(dtype=torch.uint8, device=dev), dict(dtype=torch.float32, device=dev)
+        nb = d // (32 if fmt == FA4_MXFP4 else 16)
+        self.qq = {"codes": torch.empty(B, Hq, Lq, d // 2, **u8), "block_scales": torch.empty(B, Hq, Lq, nb, **u8),
+                   "scales": torch.empty(B * Hq, **f32) if fmt == FA4_NVFP4 else None,
+                   "norm2": torch.empty(B, Hq, Lq, **f32) if self.sel else None}
+        self.kq = {"codes": torch.empty(B, Hkv, Lk, d // 2, **u8), "block_scales": torch.empty(B, Hkv, Lk, nb, **u8),
+                   "scales": torch.empty(B * Hkv, **f32) if fmt == FA4_NVFP4 else None,
+                   "norm2": torch.empty(B, Hkv, Lk, **f32) if self.sel else None}
+        self.vq = {"codes": torch.empty(B, Hkv, Lk, d, **u8), "scales": torch.empty(B, Hkv, Lk, **f32),
+                   "fold_w": torch.empty(B, Hkv, Lk, **f32), "fold_sigma": torch.empty(B, Hkv, Lk // 128, **f32)}
+        self.o = torch.empty(B, Hq, Lq, d, **f32)
+        self.lse = torch.empty(B, Hq, Lq, **f32)
+        self.bitmap = torch.empty(B, Hq, Lq // 128, Lk // 128, **u8) if self.sel else None
+        self.counts = torch.empty(B, Hq, dtype=torch.int32, device=dev) if self.sel else None
+
+        def qin(x):
+            O, H, R, dd = x.shape
+            return QInput(x.data_ptr(), _dtype_code(x), dd, O, H, R, H * R * dd, R * dd, dd, None, None, 0, 0, 0)
+
+        def qout(fm, t):
+            return QOutput(fm, t["codes"].data_ptr(), _ptr(t.get("block_scales")), _ptr(t.get("scales")),
+                           _ptr(t.get("fold_w")), _ptr(t.get("fold_sigma")))
+
+        self._qi = [qin(q), qin(k), qin(v)]
+        self._qo = [qout(fmt, self.qq), qout(fmt, self.kq), qout(FA4_FP8_TOKEN, self.vq)]
+        self._norms = [_ptr(self.qq["norm2"]), _ptr(self.kq["norm2"]), None]
+        self._fl = [self.flags, self.flags, 0]
+        if softmax_scale is None:
+            softmax_scale = 1.0 / math.sqrt(d)
+        self._attn = AttnArgs(fmt, self.qq["codes"].data_ptr(), self.qq["block_scales"].data_ptr(),
+                              _ptr(self.qq["scales"]), self.kq["codes"].data_ptr(),
+                              self.kq["block_scales"].data_ptr(), _ptr(self.kq["scales"]),
+                              self.vq["codes"].data_ptr(), self.vq["scales"].data_ptr(),
+                              self.vq["fold_w"].data_ptr(), self.vq["fold_sigma"].data_ptr(),
+                              q.data_ptr() if self.sel else None, k.data_ptr() if self.sel else None,
+                              v.data_ptr() if self.sel else None, _ptr(self.bitmap),
+                              B, Hq, Hkv, Lq, Lk, d, int(causal), softmax_scale, self.o.data_ptr(),
+                              self.lse.data_ptr())
+        self.shape = (B, Hq, Hkv, Lq, Lk, d)
+
+    def quantize(self, stream=None):
+        s = _stream() if stream is None else stream
+        for i in range(3):
+            _check(lib.fa4_quantize_blockscaled(ctypes.byref(self._qi[i]), self._fl[i], ctypes.byref(self._qo[i]),
+                                                None, self._norms[i], s), "fa4_quantize_blockscaled")
+        if self.sel:
+            B, Hq, Hkv, Lq, Lk, d = self.shape
+            _check(lib.fa4_select_tiles(self.qq["norm2"].data_ptr(), self.kq["norm2"].data_ptr(), B, Hq, Hkv, Lq, Lk,
+                                        int(self.causal), self.select[0], self.select[1], self.bitmap.data_ptr(),
+                                        self.counts.data_ptr(), s), "fa4_select_tiles")
+
+    def attention(self, stream=None):
+        _check(lib.fa4_attn_fwd(ctypes.byref(self._attn), _stream() if stream is None else stream), "fa4_attn_fwd")
+
+    def run(self):
+        self.quantize()
+        self.attention()
+        return self.o
+
+
+class DecodeRunner:
+    """Preallocated decode step: dual-residual NVFP4 query quantization plus paged attention."""
+
+    def __init__(self, q, kcache, vcache, page_table, ctx_len, Hkv, softmax_scale=None):
+        B, Hq, d = q.shape
+        dev = q.device
+        self.q = q
+        u8, f32 = dict(dtype=torch.uint8, device=dev), dict(dtype=torch.float32, device=dev)
+        self.q1 = {"codes": torch.empty(B, Hq, 1, d // 2, **u8), "block_scales": torch.empty(B, Hq, 1, d // 16, **u8),
+                   "scales": torch.empty(B * Hq, **f32)}
+        self.q2 = {k: torch.empty_like(t) for k, t in self.q1.items()}
+        self._qi = QInput(q.data_ptr(), _dtype_code(q), d, B, Hq, 1, Hq * d, d, d, None, None, 0, 0, 0)
+        self._qo = QOutput(FA4_NVFP4, self.q1["codes"].data_ptr(), self.q1["block_scales"].data_ptr(),
+                           self.q1["scales"].data_ptr(), None, None)
+        self._qr = QOutput(FA4_NVFP4, self.q2["codes"].data_ptr(), self.q2["block_scales"].data_ptr(),
+                           self.q2["scales"].data_ptr(), None, None)
+        self.args, self.o = decode_args(self.q1, self.q2, kcache, vcache, page_table, ctx_len, Hq, Hkv, d,
+                                        softmax_scale=softmax_scale)
+        self.ws = decode_workspace(self.args, dev)
+        self._keep = (kcache, vcache, page_table, ctx_len)
+
+    def quantize(self, stream=None):
+        _check(lib.fa4_quantize_blockscaled(ctypes.byref(self._qi), FA4_DUAL_RESIDUAL, ctypes.byref(self._qo),
+                                            ctypes.byref(self._qr), None, _stream() if stream is None else stream),
+               "fa4_quantize_blockscaled")
+
+    def attention(self, stream=None):
+        _check(lib.fa4_decode_paged(ctypes.byref(self.args), self.ws.data_ptr(), self.ws.numel(),
+                                    _stream() if stream is None else stream), "fa4_decode_paged")
+
+    def run(self):
+        self.quantize()
+        self.attention()
+        return self.o
