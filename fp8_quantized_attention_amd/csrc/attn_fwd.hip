@@ -53,17 +53,41 @@ __device__ __forceinline__ v4s lds_tr16(const uint8_t *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)(p));
 }
 
-// LDS layout (dynamic): [K area | V area | s_v]. The K area holds 4-bit K codes plus E8M0 scales
-// (MXFP4 tiles) or 16-bit K rows (bf16 originals / exact NVFP4 values in fp16); the V area holds FP8
-// V rows or, when bf16 tiles can occur, 16-bit V rows. Quantized and 16-bit tiles never overlap in time.
-template <int QF, bool SEL>
+// LDS layout (dynamic).
+// MXFP4 tiles are double-buffered and filled by direct global->LDS loads (each wave-wide 16-byte load
+// writes 1 KB of LDS contiguously, lane L at +16 L). Buffer b starts at b * QBUF and holds
+//   [KC: 128 rows x D/2 code bytes | KS: E8M0 scales, D/32 bytes per row (512 B) | VC: 128 rows x D
+//    FP8 bytes | W: 128 floats of P-fold factors w_c].
+// The 16-byte chunks of a K row are XOR-swizzled by kswz(r) and those of a V row by vswz(r), so the
+// QK operand reads (16 rows x one chunk per 16 lanes) and the transposed V reads (16 rows x two
+// chunks per instruction) spread over all LDS banks.
+// bf16 tiles (and the fp16 values of NVFP4 K) use 16-bit rows with stride H16_RS in a separate
+// layout [K16 | V] that overlaps the quantized buffers; those tiles are staged synchronously.
+template <int D, int QF, bool SEL>
 struct AttnLds {
-  static constexpr int K4 = 128 * K4_RS + 128 * 4;
+  static constexpr int KC = 128 * (D / 2);
+  static constexpr int KS = 512;
+  static constexpr int VC = 128 * D;
+  static constexpr int QBUF = KC + KS + VC + 512;
+  static constexpr int QBYTES = (QF == FA4_MXFP4) ? 2 * QBUF : 0;
   static constexpr int K16 = 128 * H16_RS;
-  static constexpr int KA = (QF == FA4_NVFP4 || SEL) ? (K16 > K4 ? K16 : K4) : K4;
-  static constexpr int VA = SEL ? 128 * H16_RS : 128 * V8_RS;
-  static constexpr int BYTES = KA + VA + 128 * 4;
+  static constexpr int V16 = SEL ? 128 * H16_RS : 128 * V8_RS;
+  static constexpr int HBYTES = (QF == FA4_NVFP4 || SEL) ? K16 + V16 + 512 : 0;
+  static constexpr int BYTES = QBYTES > HBYTES ? QBYTES : HBYTES;
 };
+template <int D>
+__device__ __forceinline__ int kswz(int r) { return D == 128 ? ((r >> 2) & 3) : ((r >> 3) & 1); }
+template <int D>
+__device__ __forceinline__ int vswz(int r) { return D == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ __forceinline__ void dma16(const void *g, uint8_t *l) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t *)l, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void *g, uint8_t *l) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t *)l, 4, 0, 0);
+}
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Split beta > 0 into 2^k * f with f in [1, 2); k clamped to [-127, 127].
 __device__ __forceinline__ void split_pow2(float beta, int *k, float *f) {
@@ -74,26 +98,251 @@ __device__ __forceinline__ void split_pow2(float beta, int *k, float *f) {
   *f = __uint_as_float((b & 0x807fffffu) | (127u << 23));
 }
 
+
+// Per-lane LDS byte offsets of every operand read of a tile step. All the XOR swizzles depend only on
+// the lane (the tile-varying parts of a key index are multiples of 16 or 32), so each read is
+// base + lane offset + a compile-time immediate and only these few registers stay live.
+struct LaneOff {
+  int k[2];      // MX K codes, per 64-d step s (key = col)
+  int ks;        // MX K scales
+  int v[4];      // MX V (transposed FP8 reads), per 32-row block mb of d
+  int w;         // fold factors
+  int k16;       // 16-bit K rows
+  int v16;       // bf16 V rows (transposed 16-bit reads)
+  int v8;        // NVFP4 tiles' FP8 V rows (stride V8_RS)
+};
+
+template <int D>
+__device__ __forceinline__ LaneOff lane_offsets(int lane) {
+  LaneOff o;
+  const int hh = lane >> 5, col = lane & 31, q4 = lane >> 4;
+#pragma unroll
+  for (int s = 0; s < 2; s++) o.k[s] = col * (D / 2) + 16 * ((2 * s + hh) ^ kswz<D>(col));
+  o.ks = col * (D == 128 ? 4 : 2);
+  {
+    const int aa = lane & 1, tp = (lane >> 1) & 7;
+    const int kl = 8 * (tp >> 2) + 4 * (q4 >> 1) + (tp & 3);       // key within its 16-key run
+#pragma unroll
+    for (int mb = 0; mb < 4; mb++) o.v[mb] = kl * D + 16 * ((2 * mb + (q4 & 1)) ^ vswz<D>(kl)) + 8 * aa;
+    o.v8 = kl * V8_RS + 16 * (q4 & 1) + 8 * aa;
+  }
+  o.w = 16 * hh;
+  o.k16 = col * H16_RS + 16 * hh;
+  {
+    const int aa = lane & 3, t = (lane >> 2) & 3;
+    o.v16 = (4 * (q4 >> 1) + t) * H16_RS + 2 * (16 * (q4 & 1) + 4 * aa);
+  }
+  return o;
+}
+
+// One 128-key tile for this wave's 32 queries: S^T = K Q^T, softmax step, O^T += V^T P^T.
+// MASK: the tile crosses the causal diagonal (keys past the query position get -inf).
+// sel: a selected tile, computed from the bf16 originals (QK^T and PV on bf16 MFMA).
+template <int D, int QF, bool MASK, bool sel>
+__device__ __forceinline__ void tile_step(const AttnArgs &a, const LaneOff &lo, int kt, int lane, int hh, int col, int qrow,
+                                          int off, int64_t bhq, int64_t bhk, int nk, float cs_q, float cs_b,
+                                          const v8i *qop4, const int *qsc4, const v8h *qop16, const uint8_t *k4,
+                                          const uint8_t *ksc, const uint8_t *k16, const uint8_t *vq,
+                                          const uint8_t *v16, const float *svs, float &m, float &lsum, float &unit,
+                                          v16f *acc) {
+  constexpr int NDB = D / 32;
+  v16f S[4];
+  if (sel) {
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++) S[kb] = (v16f){};
+#pragma unroll
+    for (int s = 0; s < 8; s++) {
+      const v8bf qb = *reinterpret_cast<const v8bf *>(a.qb + (bhq * a.Lq + qrow) * D + 16 * s + 8 * hh);
+#pragma unroll
+      for (int kb = 0; kb < 4; kb++) {
+        const v8bf kop = *reinterpret_cast<const v8bf *>(k16 + lo.k16 + 32 * kb * H16_RS + 32 * s);
+        S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qb, S[kb], 0, 0, 0);
+      }
+    }
+  } else if (QF == FA4_MXFP4) {
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++) {
+      S[kb] = (v16f){};
+      const uint32_t scw = D == 128 ? *reinterpret_cast<const uint32_t *>(ksc + lo.ks + 128 * kb)
+                                    : *reinterpret_cast<const uint16_t *>(ksc + lo.ks + 64 * kb);
+#pragma unroll
+      for (int s = 0; s < D / 64; s++) {
+        const v4i t = *reinterpret_cast<const v4i *>(k4 + lo.k[s] + 32 * kb * (D / 2));
+        const v8i kop = (v8i){t[0], t[1], t[2], t[3], 0, 0, 0, 0};
+        const int kscl = (int)((scw >> (8 * (2 * s + hh))) & 0xffu);
+        S[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop, qop4[s], S[kb], 4, 4, 0, kscl, 0, qsc4[s]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++) S[kb] = (v16f){};
+#pragma unroll
+    for (int s = 0; s < 8; s++)
+#pragma unroll
+      for (int kb = 0; kb < 4; kb++) {
+        const v8h kop = *reinterpret_cast<const v8h *>(k16 + lo.k16 + 32 * kb * H16_RS + 32 * s);
+        S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop, qop16[s], S[kb], 0, 0, 0);
+      }
+  }
+
+  // ---- softmax step (this lane: query qrow, keys 32kb + 8(i/4) + 4hh + i%4)
+  const float cs = sel ? cs_b : cs_q;
+  if (MASK) {
+    const int qpos = qrow + off;
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        const int key = kt * 128 + 32 * kb + 8 * (i / 4) + 4 * hh + (i % 4);
+        if (key > qpos) S[kb][i] = -INFINITY;
+      }
+  }
+  float mt = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+    for (int i = 0; i < 16; i++) mt = fmaxf(mt, S[kb][i]);
+  mt = fmaxf(mt, shfl_xor_f(mt, 32));
+  const float mt_x = mt * cs;                      // tile max in log2 units
+  const float m_new = fmaxf(m, mt_x);
+  const float alpha = exp2f(m - m_new);            // 0 on the first tile
+  const float betae = exp2f(mt_x - m_new);
+  // (S - m~) is exact at the row maximum, so P' = 1 there exactly, as in the definition
+  float tsum = 0.0f;
+#pragma unroll
+  for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      const float p = __builtin_amdgcn_exp2f((S[kb][i] - mt) * cs);
+      S[kb][i] = p;
+      tsum += p;
+    }
+  lsum = lsum * alpha + tsum * betae;
+  m = m_new;
+
+  float beta = betae;
+  if (!sel) {
+    const float sig = a.vsig[bhk * nk + kt];
+    beta = betae * (sig * (1.0f / 448.0f));
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; a4++) {
+        const float4 w4 = *reinterpret_cast<const float4 *>(reinterpret_cast<const uint8_t *>(svs) + lo.w +
+                                                            4 * (32 * kb + 8 * a4));
+        S[kb][4 * a4 + 0] *= w4.x;
+        S[kb][4 * a4 + 1] *= w4.y;
+        S[kb][4 * a4 + 2] *= w4.z;
+        S[kb][4 * a4 + 3] *= w4.w;
+      }
+  }
+  int k2;
+  float f;
+  split_pow2(beta, &k2, &f);
+  float rho;
+  if (f == 0.0f) {
+    // the tile's weight is below 2^-126 of one accumulator unit: it adds nothing representable.
+    // Its probabilities are zeroed instead of branching, so every lane still feeds the MFMA and
+    // the cross-lane LDS reads below.
+    rho = alpha;
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++) S[kb] = (v16f){};
+  } else {
+    rho = alpha * unit * __builtin_amdgcn_rcpf(f);   // f in [1, 2): rcp is within 1 ulp
+    unit = f;
+  }
+#pragma unroll
+  for (int i = 0; i < NDB; i++) acc[i] *= rho;
+
+  // ---- O^T += V^T P^T
+  if (sel) {
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+      for (int p = 0; p < 2; p++) {
+        v8s pbs;
+#pragma unroll
+        for (int j = 0; j < 8; j++) pbs[j] = (short)float_to_bf16_bits(ldexpf(S[kb][8 * p + j], k2));
+        const v8bf pb = __builtin_bit_cast(v8bf, pbs);
+#pragma unroll
+        for (int mb = 0; mb < NDB; mb++) {
+          v4s r[2];
+#pragma unroll
+          for (int v = 0; v < 2; v++)   // source lane (16q + a + 4t): key 32kb + 16p + 8v + 4g + t, d 32mb + 16(q%2) + 4a
+            r[v] = lds_tr16(v16 + lo.v16 + (32 * kb + 16 * p + 8 * v) * H16_RS + 64 * mb);
+          // whole-vector reinterpretation (inserting bit-cast elements one at a time miscompiles)
+          const v8bf vop = __builtin_bit_cast(v8bf, (v8s)__builtin_shufflevector(r[0], r[1], 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb, acc[mb], 0, 0, 0);
+        }
+      }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+      v8i pop;
+#pragma unroll
+      for (int half = 0; half < 2; half++)
+#pragma unroll
+        for (int w = 0; w < 4; w++) {
+          const v16f &sv = S[2 * t + half];
+          int x = __builtin_amdgcn_cvt_pk_fp8_f32(sv[4 * w], sv[4 * w + 1], 0, false);
+          x = __builtin_amdgcn_cvt_pk_fp8_f32(sv[4 * w + 2], sv[4 * w + 3], x, true);
+          pop[4 * half + w] = x;
+        }
+#pragma unroll
+      for (int mb = 0; mb < NDB; mb++) {
+        v8i vop;
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+          // source lane (16q + a + 2t'): key 64t + 32(u/2) + 16(u%2) + 8(t'/4) + 4g + t'%4,
+          //                              d 32mb + 16(q%2) + 8a
+          const int krun = 64 * t + 32 * (u >> 1) + 16 * (u & 1);
+          const v2i r = QF == FA4_MXFP4 ? lds_tr8(vq + lo.v[mb] + krun * D)
+                                        : lds_tr8(vq + lo.v8 + krun * V8_RS + 32 * mb);
+          vop[2 * u] = r[0];
+          vop[2 * u + 1] = r[1];
+        }
+        acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, pop, acc[mb], 0, 0, 0, 127, 0, k2 + 127);
+      }
+    }
+  }
+}
+
 template <int D, int QF, bool CAUSAL, bool SEL>
 __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
   constexpr int NDB = D / 32;        // 32-row blocks of d in O^T
-  typedef AttnLds<QF, SEL> L;
+  typedef AttnLds<D, QF, SEL> L;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  uint8_t *const k4 = lds;                       // 4-bit K codes, row stride K4_RS
-  uint8_t *const ksc = lds + 128 * K4_RS;         // E8M0 K scales, 4 bytes per row
-  uint8_t *const k16 = lds;                      // 16-bit K rows, stride H16_RS
-  uint8_t *const vq = lds + L::KA;               // FP8 V rows, stride V8_RS
-  uint8_t *const v16 = lds + L::KA;              // bf16 V rows, stride H16_RS
-  float *const svs = reinterpret_cast<float *>(lds + L::KA + L::VA);
+  uint8_t *const k16 = lds;                              // 16-bit K rows, stride H16_RS
+  uint8_t *const v16 = lds + L::K16;                     // bf16 V rows (stride H16_RS) / NVFP4 tiles' FP8 V
+  float *const hsv = reinterpret_cast<float *>(lds + L::K16 + L::V16);   // w_c of NVFP4 tiles
 
   const int nq = a.Lq / 128, nk = a.Lk / 128;
-  const int qt = nq - 1 - (int)blockIdx.x;          // longest causal rows first
-  const int h = blockIdx.y, b = blockIdx.z;
+  // Work order: one block per (q-tile, batch, head), dispatched longest causal rows first. Blocks are
+  // handed to the 8 XCDs round-robin, so when the key-head groups split evenly over the XCDs, all the
+  // query heads of one key head land on the same XCD and share its L2 copy of K and V.
+  int qt, h, b;
+  {
+    const int L = blockIdx.x, gq = a.Hq / a.Hkv, nb = a.B * a.Hkv;
+    if (nb % 8 == 0) {
+      const int x = L & 7, r = L >> 3, per = (nb / 8) * gq;
+      const int level = r / per, rem = r - level * per;
+      const int bhk = x + 8 * (rem / gq);
+      b = bhk / a.Hkv;
+      h = (bhk - b * a.Hkv) * gq + rem % gq;
+      qt = nq - 1 - level;
+    } else {
+      const int level = L / (a.B * a.Hq), rem = L - level * (a.B * a.Hq);
+      b = rem / a.Hq;
+      h = rem - b * a.Hq;
+      qt = nq - 1 - level;
+    }
+  }
   const int kvh = h / (a.Hq / a.Hkv);
   const int off = a.Lk - a.Lq;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, col = lane & 31;
   const int qrow = qt * 128 + wave * 32 + col;      // this lane's query (B-operand column)
+  const LaneOff lo = lane_offsets<D>(lane);
   const int64_t bhq = (int64_t)b * a.Hq + h, bhk = (int64_t)b * a.Hkv + kvh;
 
   // ---- query operand, held in registers for the whole key loop
@@ -129,236 +378,141 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < NDB; i++) acc[i] = (v16f){};
 
-  for (int kt = 0; kt < kt_end; kt++) {
-    bool sel = false;
-    if (SEL) sel = a.bitmap[(bhq * nq + qt) * nk + kt] != 0;
+  auto is_sel = [&](int kt) -> bool { return SEL && a.bitmap[(bhq * nq + qt) * nk + kt] != 0; };
+  auto copy_bf16 = [&](int kt) {
     const int64_t krow0 = bhk * a.Lk + (int64_t)kt * 128;
-    __syncthreads();
-    // ---------------- stage the tile in LDS
-    if (sel) {
-      for (int c = tid; c < 128 * (D / 8); c += ATT_THREADS) {     // 16-byte chunks of bf16 rows
-        const int r = c / (D / 8), j = c % (D / 8);
-        *reinterpret_cast<v4i *>(k16 + r * H16_RS + 16 * j) =
-            *reinterpret_cast<const v4i *>(a.kb + (krow0 + r) * D + 8 * j);
-        *reinterpret_cast<v4i *>(v16 + r * H16_RS + 16 * j) =
-            *reinterpret_cast<const v4i *>(a.vb + (krow0 + r) * D + 8 * j);
+    for (int c = tid; c < 128 * (D / 8); c += ATT_THREADS) {     // 16-byte chunks of bf16 rows
+      const int r = c / (D / 8), j = c % (D / 8);
+      const v4i kx = *reinterpret_cast<const v4i *>(a.kb + (krow0 + r) * D + 8 * j);
+      const v4i vx = *reinterpret_cast<const v4i *>(a.vb + (krow0 + r) * D + 8 * j);
+      *reinterpret_cast<v4i *>(k16 + r * H16_RS + 16 * j) = kx;
+      *reinterpret_cast<v4i *>(v16 + r * H16_RS + 16 * j) = vx;
+    }
+  };
+// One tile step; MASKV must be a constant. With Lq and Lk multiples of 128 the only tile that crosses
+// the causal diagonal is the last one, so loops run MASKV = false and the diagonal tile is peeled.
+// One tile step; MASKV and SELV must be constants. With Lq and Lk multiples of 128 the only tile that
+// crosses the causal diagonal is the last one.
+#define FA4_TILE_STEP(MASKV, SELV, KT, KC, KS, VC, W)                                                         \
+  tile_step<D, QF, MASKV, SELV>(a, lo, KT, lane, hh, col, qrow, off, bhq, bhk, nk, cs_q, cs_b, qop4, qsc4, qop16, \
+                                KC, KS, k16, VC, v16, W, m, lsum, unit, acc)
+
+  // Tiles are visited in two passes: first every tile computed from the quantized operands, then the
+  // selected (bf16) tiles. The result does not depend on the order (each tile's probabilities use its
+  // own row maximum), and each pass then holds one code path only.
+  const int last = kt_end - 1;
+  auto next_quant = [&](int kt) -> int {        // first non-selected tile >= kt, or kt_end
+    if (SEL)
+      while (kt < kt_end && is_sel(kt)) kt++;
+    return kt;
+  };
+  if (QF == FA4_MXFP4) {
+    // ---- quantized tiles: direct global->LDS loads into a double buffer, one tile ahead
+    auto issue = [&](int kt, int b) {
+      uint8_t *base = lds + b * L::QBUF;
+      const int64_t krow0 = bhk * a.Lk + (int64_t)kt * 128;
+      constexpr int KI = L::KC / 1024 / 4, VI = L::VC / 1024 / 4;   // wave-loads per wave
+#pragma unroll
+      for (int e = 0; e < KI; e++) {
+        const int i = wave * KI + e;
+        const int r = i * (1024 / (D / 2)) + lane / (D / 32), p = lane % (D / 32);
+        dma16(a.kc + (krow0 + r) * (D / 2) + 16 * (p ^ kswz<D>(r)), base + 1024 * i);
       }
-    } else {
-      if (QF == FA4_MXFP4) {
-        for (int c = tid; c < 128 * (D / 32); c += ATT_THREADS) {  // 16-byte chunks of code rows
-          const int r = c / (D / 32), j = c % (D / 32);
-          *reinterpret_cast<v4i *>(k4 + r * K4_RS + 16 * j) =
-              *reinterpret_cast<const v4i *>(a.kc + (krow0 + r) * (D / 2) + 16 * j);
-        }
-        if (tid < 128) {
-          if (D == 128) *reinterpret_cast<uint32_t *>(ksc + tid * 4) =
-              *reinterpret_cast<const uint32_t *>(a.ks + (krow0 + tid) * 4);
-          else *reinterpret_cast<uint16_t *>(ksc + tid * 4) =
-              *reinterpret_cast<const uint16_t *>(a.ks + (krow0 + tid) * 2);
+#pragma unroll
+      for (int e = 0; e < VI; e++) {
+        const int i = wave * VI + e;
+        const int r = i * (1024 / D) + lane / (D / 16), p = lane % (D / 16);
+        dma16(a.vc + (krow0 + r) * D + 16 * (p ^ vswz<D>(r)), base + L::KC + L::KS + 1024 * i);
+      }
+      if (D == 128) {
+        if (wave < 2) dma4(a.ks + (krow0 + 64 * wave + lane) * 4, base + L::KC + 256 * wave);
+      } else if (wave == 0) {
+        dma4(a.ks + krow0 * 2 + 4 * lane, base + L::KC);
+      }
+      if (wave >= 2) dma4(a.vw + krow0 + 64 * (wave - 2) + lane, base + L::KC + L::KS + L::VC + 256 * (wave - 2));
+    };
+    int b = 0;
+    int kt = next_quant(0);
+    if (kt < kt_end) issue(kt, 0);
+    const int stop = CAUSAL ? last : kt_end;   // the diagonal tile is peeled below
+    while (kt < stop) {
+      const int nxt = next_quant(kt + 1);
+      wait_vmem();
+      __syncthreads();                   // tile kt landed (all waves' loads); the previous tile is consumed
+      if (nxt < kt_end) issue(nxt, b ^ 1);   // in flight during this tile's compute
+      const uint8_t *base = lds + b * L::QBUF;
+      FA4_TILE_STEP(false, false, kt, base, base + L::KC, base + L::KC + L::KS,
+                    reinterpret_cast<const float *>(base + L::KC + L::KS + L::VC));
+      b ^= 1;
+      kt = nxt;
+    }
+    if (CAUSAL && kt == last) {
+      wait_vmem();
+      __syncthreads();
+      const uint8_t *base = lds + b * L::QBUF;
+      FA4_TILE_STEP(true, false, kt, base, base + L::KC, base + L::KC + L::KS,
+                    reinterpret_cast<const float *>(base + L::KC + L::KS + L::VC));
+    }
+  } else {
+    // ---- NVFP4 tiles: K expanded to exact fp16 values in LDS, staged synchronously
+    auto stage_nv = [&](int kt) {
+      const int64_t krow0 = bhk * a.Lk + (int64_t)kt * 128;
+      __syncthreads();
+      {
+        const int r = tid >> 1, half = tid & 1;
+        const v4i c0 = *reinterpret_cast<const v4i *>(a.kc + (krow0 + r) * 64 + 32 * half);
+        const v4i c1 = *reinterpret_cast<const v4i *>(a.kc + (krow0 + r) * 64 + 32 * half + 16);
+        const uint32_t sbw = *reinterpret_cast<const uint32_t *>(a.ks + (krow0 + r) * 8 + 4 * half);
+#pragma unroll
+        for (int blk = 0; blk < 4; blk++) {
+          const v4i &cc = blk < 2 ? c0 : c1;
+          const uint32_t w0 = (uint32_t)cc[2 * (blk & 1)], w1 = (uint32_t)cc[2 * (blk & 1) + 1];
+          const _Float16 sb = (_Float16)e4m3_value((sbw >> (8 * blk)) & 0xffu);
+          v8h lo8, hi8;
+#pragma unroll
+          for (int j = 0; j < 8; j++) {
+            lo8[j] = (_Float16)e2m1_value((w0 >> (4 * j)) & 15u) * sb;
+            hi8[j] = (_Float16)e2m1_value((w1 >> (4 * j)) & 15u) * sb;
+          }
+          *reinterpret_cast<v8h *>(k16 + r * H16_RS + 2 * (64 * half + 16 * blk)) = lo8;
+          *reinterpret_cast<v8h *>(k16 + r * H16_RS + 2 * (64 * half + 16 * blk + 8)) = hi8;
         }
         for (int c = tid; c < 128 * (D / 16); c += ATT_THREADS) {
-          const int r = c / (D / 16), j = c % (D / 16);
-          *reinterpret_cast<v4i *>(vq + r * V8_RS + 16 * j) =
-              *reinterpret_cast<const v4i *>(a.vc + (krow0 + r) * D + 16 * j);
+          const int rr = c / (D / 16), j = c % (D / 16);
+          *reinterpret_cast<v4i *>(v16 + rr * V8_RS + 16 * j) =
+              *reinterpret_cast<const v4i *>(a.vc + (krow0 + rr) * D + 16 * j);
         }
-      } else {
-        // NVFP4 K -> exact fp16 values in LDS (each thread: half a row, 64 elements)
-        {
-          const int r = tid >> 1, half = tid & 1;
-          const uint8_t *src = a.kc + (krow0 + r) * 64 + 32 * half;
-          const uint32_t sbw = *reinterpret_cast<const uint32_t *>(a.ks + (krow0 + r) * 8 + 4 * half);
-#pragma unroll
-          for (int blk = 0; blk < 4; blk++) {
-            const uint2 w = *reinterpret_cast<const uint2 *>(src + 8 * blk);
-            const float sb = e4m3_value((sbw >> (8 * blk)) & 0xffu);
-            v8h lo, hi;
-#pragma unroll
-            for (int j = 0; j < 8; j++) {
-              lo[j] = (_Float16)(e2m1_value((w.x >> (4 * j)) & 15u) * sb);
-              hi[j] = (_Float16)(e2m1_value((w.y >> (4 * j)) & 15u) * sb);
-            }
-            *reinterpret_cast<v8h *>(k16 + r * H16_RS + 2 * (64 * half + 16 * blk)) = lo;
-            *reinterpret_cast<v8h *>(k16 + r * H16_RS + 2 * (64 * half + 16 * blk + 8)) = hi;
-          }
-        }
-        for (int c = tid; c < 128 * (D / 16); c += ATT_THREADS) {
-          const int r = c / (D / 16), j = c % (D / 16);
-          *reinterpret_cast<v4i *>(vq + r * V8_RS + 16 * j) =
-              *reinterpret_cast<const v4i *>(a.vc + (krow0 + r) * D + 16 * j);
-        }
+        if (tid < 128) hsv[tid] = a.vw[krow0 + tid];
       }
-      if (tid < 128) svs[tid] = a.vw[krow0 + tid];      // per-key fold factor w_c
+      __syncthreads();
+    };
+    int kt = next_quant(0);
+    for (; kt < (CAUSAL ? last : kt_end); kt = next_quant(kt + 1)) {
+      stage_nv(kt);
+      FA4_TILE_STEP(false, false, kt, nullptr, nullptr, v16, hsv);
     }
-    __syncthreads();
-
-    // ---------------- S^T = K Q^T : 4 blocks of 32 keys x this wave's 32 queries
-    v16f S[4];
-    if (sel) {
-      v8bf qb[8];
-#pragma unroll
-      for (int s = 0; s < 8; s++)
-        qb[s] = *reinterpret_cast<const v8bf *>(a.qb + (bhq * a.Lq + qrow) * D + 16 * s + 8 * hh);
-#pragma unroll
-      for (int kb = 0; kb < 4; kb++) {
-        S[kb] = (v16f){};
-#pragma unroll
-        for (int s = 0; s < 8; s++) {
-          const v8bf kop = *reinterpret_cast<const v8bf *>(k16 + (32 * kb + col) * H16_RS + 32 * s + 16 * hh);
-          S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qb[s], S[kb], 0, 0, 0);
-        }
-      }
-    } else if (QF == FA4_MXFP4) {
-#pragma unroll
-      for (int kb = 0; kb < 4; kb++) {
-        S[kb] = (v16f){};
-        const int key = 32 * kb + col;
-        const uint32_t scw = *reinterpret_cast<const uint32_t *>(ksc + key * 4);
-#pragma unroll
-        for (int s = 0; s < D / 64; s++) {
-          const v4i t = *reinterpret_cast<const v4i *>(k4 + key * K4_RS + 32 * s + 16 * hh);
-          const v8i kop = (v8i){t[0], t[1], t[2], t[3], 0, 0, 0, 0};
-          const int ksc = (int)((scw >> (8 * (2 * s + hh))) & 0xffu);
-          S[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop, qop4[s], S[kb], 4, 4, 0, ksc, 0, qsc4[s]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < 4; kb++) {
-        S[kb] = (v16f){};
-#pragma unroll
-        for (int s = 0; s < 8; s++) {
-          const v8h kop = *reinterpret_cast<const v8h *>(k16 + (32 * kb + col) * H16_RS + 32 * s + 16 * hh);
-          S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop, qop16[s], S[kb], 0, 0, 0);
-        }
-      }
-    }
-
-    // ---------------- softmax step (this lane: query qrow, keys 32kb + 8(i/4) + 4hh + i%4)
-    const float cs = sel ? cs_b : cs_q;
-    const bool diag = CAUSAL && (kt * 128 + 127 > off + qt * 128);
-    const int qpos = qrow + off;
-    float mt = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 4; kb++)
-#pragma unroll
-      for (int i = 0; i < 16; i++) {
-        if (diag) {
-          const int key = kt * 128 + 32 * kb + 8 * (i / 4) + 4 * hh + (i % 4);
-          if (key > qpos) S[kb][i] = -INFINITY;
-        }
-        mt = fmaxf(mt, S[kb][i]);
-      }
-    mt = fmaxf(mt, shfl_xor_f(mt, 32));
-    const float mt_x = mt * cs;                      // tile max in log2 units
-    const float m_new = fmaxf(m, mt_x);
-    const float alpha = exp2f(m - m_new);            // 0 on the first tile
-    const float betae = exp2f(mt_x - m_new);
-    // (S - m~) is exact at the row maximum, so P' = 1 there exactly, as in the definition
-    float tsum = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < 4; kb++)
-#pragma unroll
-      for (int i = 0; i < 16; i++) {
-        const float p = __builtin_amdgcn_exp2f((S[kb][i] - mt) * cs);
-        S[kb][i] = p;
-        tsum += p;
-      }
-    lsum = lsum * alpha + tsum * betae;
-    m = m_new;
-
-    float beta = betae;
-    if (!sel) {
-      const float sig = a.vsig[bhk * nk + kt];
-      beta = betae * (sig * (1.0f / 448.0f));
-#pragma unroll
-      for (int kb = 0; kb < 4; kb++)
-#pragma unroll
-        for (int a4 = 0; a4 < 4; a4++) {
-          const float4 w4 = *reinterpret_cast<const float4 *>(&svs[32 * kb + 8 * a4 + 4 * hh]);
-          S[kb][4 * a4 + 0] *= w4.x;
-          S[kb][4 * a4 + 1] *= w4.y;
-          S[kb][4 * a4 + 2] *= w4.z;
-          S[kb][4 * a4 + 3] *= w4.w;
-        }
-    }
-    int k2;
-    float f;
-    split_pow2(beta, &k2, &f);
-    float rho;
-    if (f == 0.0f) {
-      // the tile's weight is below 2^-126 of one accumulator unit: it adds nothing representable.
-      // Its probabilities are zeroed instead of branching, so every lane still feeds the MFMA and
-      // the cross-lane LDS reads below.
-      rho = alpha;
-#pragma unroll
-      for (int kb = 0; kb < 4; kb++) S[kb] = (v16f){};
-    } else {
-      rho = alpha * unit / f;
-      unit = f;
-    }
-#pragma unroll
-    for (int i = 0; i < NDB; i++) acc[i] *= rho;
-
-    // ---------------- O^T += V^T P^T
-    if (sel) {
-#pragma unroll
-      for (int kb = 0; kb < 4; kb++)
-#pragma unroll
-        for (int p = 0; p < 2; p++) {
-          v8s pbs;
-#pragma unroll
-          for (int j = 0; j < 8; j++) pbs[j] = (short)float_to_bf16_bits(ldexpf(S[kb][8 * p + j], k2));
-          const v8bf pb = __builtin_bit_cast(v8bf, pbs);
-#pragma unroll
-          for (int mb = 0; mb < NDB; mb++) {
-            v4s r[2];
-#pragma unroll
-            for (int v = 0; v < 2; v++) {
-              // source lane (16q + a + 4t): key 32kb + 16p + 8v + 4g + t, d 32mb + 16(q%2) + 4a
-              const int q4 = lane >> 4, aa = lane & 3, t = (lane >> 2) & 3;
-              const int key = 32 * kb + 16 * p + 8 * v + 4 * (q4 >> 1) + t;
-              const int dd = 32 * mb + 16 * (q4 & 1) + 4 * aa;
-              r[v] = lds_tr16(v16 + key * H16_RS + 2 * dd);
-            }
-            // whole-vector reinterpretation (inserting bit-cast elements one at a time miscompiles)
-            const v8bf vop = __builtin_bit_cast(v8bf, (v8s)__builtin_shufflevector(r[0], r[1], 0, 1, 2, 3, 4, 5, 6, 7));
-            acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb, acc[mb], 0, 0, 0);
-          }
-        }
-    } else {
-      const uint8_t *vt = vq;
-#pragma unroll
-      for (int t = 0; t < 2; t++) {
-        v8i pop;
-#pragma unroll
-        for (int half = 0; half < 2; half++)
-#pragma unroll
-          for (int w = 0; w < 4; w++) {
-            const v16f &sv = S[2 * t + half];
-            int x = __builtin_amdgcn_cvt_pk_fp8_f32(sv[4 * w], sv[4 * w + 1], 0, false);
-            x = __builtin_amdgcn_cvt_pk_fp8_f32(sv[4 * w + 2], sv[4 * w + 3], x, true);
-            pop[4 * half + w] = x;
-          }
-#pragma unroll
-        for (int mb = 0; mb < NDB; mb++) {
-          v8i vop;
-#pragma unroll
-          for (int u = 0; u < 4; u++) {
-            // source lane (16q + a + 2t'): key 64t + 32(u/2) + 16(u%2) + 8(t'/4) + 4g + t'%4,
-            //                              d 32mb + 16(q%2) + 8a
-            const int q4 = lane >> 4, aa = lane & 1, tp = (lane >> 1) & 7;
-            const int key = 64 * t + 32 * (u >> 1) + 16 * (u & 1) + 8 * (tp >> 2) + 4 * (q4 >> 1) + (tp & 3);
-            const int dd = 32 * mb + 16 * (q4 & 1) + 8 * aa;
-            const v2i r = lds_tr8(vt + key * V8_RS + dd);
-            vop[2 * u] = r[0];
-            vop[2 * u + 1] = r[1];
-          }
-          acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, pop, acc[mb], 0, 0, 0, 127, 0, k2 + 127);
-        }
-      }
+    if (CAUSAL && kt == last) {
+      stage_nv(kt);
+      FA4_TILE_STEP(true, false, kt, nullptr, nullptr, v16, hsv);
     }
   }
-
+  if (SEL) {
+    // ---- selected tiles from the bf16 originals
+    for (int kt = 0; kt < (CAUSAL ? last : kt_end); kt++) {
+      if (!is_sel(kt)) continue;          // uniform per workgroup
+      __syncthreads();
+      copy_bf16(kt);
+      __syncthreads();
+      FA4_TILE_STEP(false, true, kt, nullptr, nullptr, nullptr, nullptr);
+    }
+    if (CAUSAL && is_sel(last)) {
+      __syncthreads();
+      copy_bf16(last);
+      __syncthreads();
+      FA4_TILE_STEP(true, true, last, nullptr, nullptr, nullptr, nullptr);
+    }
+  }
+#undef FA4_TILE_STEP
   // ---------------- epilogue: O = u * O_acc / l, LSE = m ln2 + ln l
   const float l = lsum + shfl_xor_f(lsum, 32);
   const float fin = unit / l;
@@ -378,16 +532,16 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
 template <int D, int QF, bool CAUSAL, bool SEL>
 static hipError_t allow_lds() {
   return hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_fwd_kernel<D, QF, CAUSAL, SEL>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, AttnLds<QF, SEL>::BYTES);
+                             hipFuncAttributeMaxDynamicSharedMemorySize, AttnLds<D, QF, SEL>::BYTES);
 }
 
 template <int D, int QF>
 static hipError_t launch_attn_t(const AttnArgs &x, bool causal, bool sel, hipStream_t s) {
-  dim3 grid(x.Lq / 128, x.Hq, x.B);
+  dim3 grid((unsigned)((int64_t)(x.Lq / 128) * x.Hq * x.B));
   hipError_t e = causal ? (sel ? allow_lds<D, QF, true, true>() : allow_lds<D, QF, true, false>())
                         : (sel ? allow_lds<D, QF, false, true>() : allow_lds<D, QF, false, false>());
   if (e != hipSuccess) return e;
-  const size_t l1 = AttnLds<QF, true>::BYTES, l0 = AttnLds<QF, false>::BYTES;
+  const size_t l1 = AttnLds<D, QF, true>::BYTES, l0 = AttnLds<D, QF, false>::BYTES;
   if (causal) {
     if (sel) hipLaunchKernelGGL((attn_fwd_kernel<D, QF, true, true>), grid, dim3(ATT_THREADS), l1, s, x);
     else hipLaunchKernelGGL((attn_fwd_kernel<D, QF, true, false>), grid, dim3(ATT_THREADS), l0, s, x);

@@ -146,7 +146,7 @@ fa4_status fa4_attn_fwd(const fa4_attn_args *a, void *stream) {
   REQUIRE(a->Lq >= 0 && a->Lk > 0 && a->Lq % 128 == 0 && a->Lk % 128 == 0, FA4_ERR_SHAPE,
           "attn: Lq=%d Lk=%d must be multiples of 128 (Lk > 0)", a->Lq, a->Lk);
   REQUIRE(!a->causal || a->Lq <= a->Lk, FA4_ERR_SHAPE, "attn: causal needs Lq <= Lk");
-  REQUIRE(a->Lq / 128 <= 65535 && a->Hq <= 65535 && a->B <= 65535, FA4_ERR_SHAPE, "attn: grid too large");
+  REQUIRE((int64_t)(a->Lq / 128) * a->Hq * a->B < ((int64_t)1 << 31), FA4_ERR_SHAPE, "attn: grid too large");
   if (a->fmt == FA4_MXFP4)
     REQUIRE(a->d == 128 || (a->d == 64 && !a->bitmap), FA4_ERR_UNSUPPORTED,
             "attn: MXFP4 supports d=128, or d=64 without tile selection (d=%d)", a->d);

@@ -19,7 +19,7 @@
 namespace fa4 {
 
 constexpr int QUANT_THREADS = 256;
-constexpr int QUANT_CHUNK = 256;     // rows per workgroup
+constexpr int QUANT_CHUNK = 64;      // rows per workgroup (one group; NVFP4 maxima reduce per workgroup)
 
 // 1/sqrt(128) as the float64 nearest to 1/fl64(sqrt(128)).
 #define FA4_RSQRT128 0x1.6a09e667f3bccp-4
@@ -127,7 +127,10 @@ __global__ void __launch_bounds__(QUANT_THREADS) quantize_kernel(QArgs a) {
   }
   float gmax = 0.0f;
 
-  for (int64_t rr = r0 + wave * RPW + sub; rr < r0 + QUANT_CHUNK; rr += RPB) {
+  // every lane of a wave runs the same number of iterations (the bound is workgroup-uniform), so the
+  // lane-group shuffles below always see all their lanes
+  const int64_t r_end = r0 + min<int64_t>(QUANT_CHUNK, ((max<int64_t>(nrows - r0, 0) + RPB - 1) / RPB) * RPB);
+  for (int64_t rr = r0 + wave * RPW + sub; rr < r_end; rr += RPB) {
     const bool active = rr < nrows;
     float v[4] = {0.f, 0.f, 0.f, 0.f};
     if (active) load4<DT>(a.x, o * a.so + h * a.sh + rr * a.sr + li * 4, v);
