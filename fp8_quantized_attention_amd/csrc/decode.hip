@@ -5,25 +5,30 @@
 // under a scale that cannot underflow, and the query heads of a GQA group stacked into one
 // matrix-core tile. "MpFA QK4V8" section 3.3: the softmax statistics stay in FP32.
 //
-// Work decomposition: the keys of each (sequence, key head) are cut into splits of 512 keys; a
-// workgroup owns one split and each of its 4 waves one 128-key tile (the probability tile). The 8
-// query rows of a GQA group (4 heads x {Q1, Q2}) form the columns of a 16x16x32 fp16 MFMA whose rows
-// are 16 keys: NVFP4 values code * s_b are exact in fp16 (at most 6 significant bits), so K and Q
-// codes are expanded in registers (hardware fp4->fp16 conversion, then one packed multiply by the
-// block scale) and the tensor scales are applied to the fp32 scores. The d axis of the QK product is
-// permuted so that each lane's operand is one 16-byte run of a key's codes. V is expanded into LDS
-// (fp16) and read back transposed (ds_read_b64_tr_b16) as the A operand of O^T = V^T P^T; P^ = E4M3
-// (448 P') is exact in fp16. A tile's (max, sum, P^V) is merged over the 4 waves in LDS and written
-// as the split's partial; a second kernel merges the splits of each (sequence, head).
+// Work decomposition: the keys of each (sequence, key head) are cut into splits of DEC_SPLIT keys; a
+// workgroup owns one split and its 4 waves take the split's 128-key tiles (the probability tiles) in
+// turn. The 8 query rows of a GQA group (4 heads x {Q1, Q2}) form the columns of a 16x16x32 fp16
+// MFMA whose rows are 16 keys: NVFP4 values code * s_b are exact in fp16 (at most 5 significant
+// bits), so K and Q codes are expanded in registers (hardware fp4->fp16 conversion, then one packed
+// multiply by the block scales) and the tensor scales are applied to the fp32 scores. The d axis of
+// the QK product is permuted so that each lane's operand is one 16-byte run of a key's codes.
+// PV is O^T = V^T P^T, whose A operand needs 8 keys of one d in a lane: each lane loads one 4-byte
+// word (8 d values) of 8 key rows and an 8x8 nibble transpose in registers turns them into 8 words
+// of 8 keys each, one per d value, so V never goes through LDS. P^ = E4M3(448 P') is exact in fp16.
+// Both pages of a tile are resolved with wave-uniform page-table reads; the next tile's K and V
+// loads are issued as soon as the registers holding the current tile's codes are consumed, so every
+// wave keeps a tile in flight while it computes. Each tile's (max, sum, P^V) goes to LDS, the tiles
+// of the workgroup are merged into the split's partial, and a second kernel merges the splits.
 #include "fa4_device.h"
 #include "fa4_internal.h"
 
 namespace fa4 {
 
 constexpr int DEC_THREADS = 256;
-constexpr int DEC_SPLIT = 512;            // keys per workgroup (4 tiles of 128)
-constexpr int DEC_PART = 130;             // floats per (split, head) partial: m, l, O[128]
-constexpr int V16_RS = 272;               // LDS row stride (bytes) of fp16 V rows
+constexpr int DEC_TPW = 2;                        // tiles per wave
+constexpr int DEC_SLOTS = 4 * DEC_TPW;            // tiles per workgroup
+constexpr int DEC_SPLIT = 128 * DEC_SLOTS;        // keys per workgroup
+constexpr int DEC_PART = 130;                     // floats per (split, head) partial: m, l, O[128]
 constexpr float DEC_LOG2E = 1.4426950408889634f;
 
 struct DecArgs {
@@ -38,8 +43,6 @@ struct DecArgs {
   float *ws, *o;
 };
 
-typedef __attribute__((address_space(3))) v4s lds_v4s_d;
-
 // 8 E2M1 codes (4 bytes) times an fp16 block scale, as exact fp16 values.
 __device__ __forceinline__ v8h expand8(uint32_t w, _Float16 sb) {
   const v2h s2 = {sb, sb};
@@ -50,157 +53,271 @@ __device__ __forceinline__ v8h expand8(uint32_t w, _Float16 sb) {
   return (v8h){t0[0], t0[1], t1[0], t1[1], t2[0], t2[1], t3[0], t3[1]};
 }
 
+// 8 E2M1 codes, element j scaled by its own fp16 scale (pairs (2i, 2i+1) in sp[i]).
+__device__ __forceinline__ v8h expand8s(uint32_t w, const v2h sp[4]) {
+  const v2h t0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * sp[0];
+  const v2h t1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * sp[1];
+  const v2h t2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * sp[2];
+  const v2h t3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * sp[3];
+  return (v8h){t0[0], t0[1], t1[0], t1[1], t2[0], t2[1], t3[0], t3[1]};
+}
+
 __device__ __forceinline__ _Float16 e4m3_f16(uint32_t code) { return (_Float16)e4m3_value(code); }
 
+// Transpose of an 8x8 matrix of nibbles held as 8 words (word j, nibble e) -> (word e, nibble j):
+// swap the off-diagonal 4x4 blocks (16-bit halves), then the 2x2 blocks inside them (bytes), then
+// the single nibbles.
+__device__ __forceinline__ void transpose8x8_nibbles(uint32_t w[8]) {
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const uint32_t lo = (w[j] & 0xffffu) | (w[j + 4] << 16);
+    const uint32_t hi = (w[j] >> 16) | (w[j + 4] & 0xffff0000u);
+    w[j] = lo;
+    w[j + 4] = hi;
+  }
+#pragma unroll
+  for (int k = 0; k < 4; k++) {
+    const int r = (k & 1) + 4 * (k >> 1);                   // 0, 1, 4, 5
+    const uint32_t x = w[r], y = w[r + 2];
+    w[r] = (x & 0x00ff00ffu) | ((y & 0x00ff00ffu) << 8);
+    w[r + 2] = ((x >> 8) & 0x00ff00ffu) | (y & 0xff00ff00u);
+  }
+#pragma unroll
+  for (int r = 0; r < 8; r += 2) {
+    const uint32_t t = ((w[r] >> 4) ^ w[r + 1]) & 0x0f0f0f0fu;
+    w[r + 1] ^= t;
+    w[r] ^= t << 4;
+  }
+}
+
+// The two 64-key pages of a tile: base pointers of this key head's rows and whether the page holds
+// keys (within the context, id inside the cache). Everything here is wave-uniform; a page without
+// keys points at page 0 (always present), is read like the others and its values are replaced by
+// zeros, so no load sits behind a branch.
+struct TilePages {
+  const uint8_t *kc[2], *ks[2], *vc[2], *vs[2];
+  bool ok[2];
+};
+
+__device__ __forceinline__ TilePages tile_pages(const DecArgs &a, const int32_t *pt, int kvh, int t0, int L) {
+  TilePages tp;
+#pragma unroll
+  for (int p = 0; p < 2; p++) {
+    const int pid = min((t0 >> 6) + p, a.max_pages - 1);
+    const int pg = __builtin_amdgcn_readfirstlane(pt[pid]);
+    const bool ok = t0 + 64 * p < L && pg >= 0 && (int64_t)pg < a.num_pages;
+    const int64_t row0 = ((int64_t)(ok ? pg : 0) * a.Hkv + kvh) * 64;
+    tp.kc[p] = a.kc + row0 * 64;
+    tp.ks[p] = a.ks + row0 * 8;
+    tp.vc[p] = a.vc + row0 * 64;
+    tp.vs[p] = a.vs + row0 * 8;
+    tp.ok[p] = ok;
+  }
+  return tp;
+}
+
+// K of a tile for the QK A operand: block kb (16 keys), lane (g, n) -> key 16 kb + n, codes bytes
+// 16 g .. 16 g + 15 (d = 32 g .. 32 g + 31) and the two block scales of those 32 values (a page
+// without keys gets zero scales, so its values are zeros).
+__device__ __forceinline__ void load_k(const TilePages &tp, int n, int g, v4i kc[8], uint32_t ks[8]) {
+#pragma unroll
+  for (int kb = 0; kb < 8; kb++) {
+    const int p = kb >> 2, row = 16 * (kb & 3) + n;
+    kc[kb] = *reinterpret_cast<const v4i *>(tp.kc[p] + row * 64 + 16 * g);
+    const uint32_t sc = *reinterpret_cast<const uint16_t *>(tp.ks[p] + row * 8 + 2 * g);
+    ks[kb] = tp.ok[p] ? sc : 0u;
+  }
+}
+
+// V of a tile for the PV A operand: quarter q (32 keys), element j of lane (g, n) is the key
+// 32 q + 16 (j / 4) + 4 g + j % 4, whose codes word n (d = 8 n .. 8 n + 7) the lane loads. The
+// quarter's 32 scale rows (256 contiguous bytes) are loaded one word per lane (lane L: key L / 2,
+// blocks 4 (L % 2) .. 4 (L % 2) + 3) and redistributed with lane shuffles when the quarter is used.
+__device__ __forceinline__ void load_v(const TilePages &tp, int lane, int n, int g, uint32_t vc[4][8],
+                                       uint32_t vs[4]) {
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const int p = q >> 1;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const int row = 32 * (q & 1) + 16 * (j >> 2) + 4 * g + (j & 3);
+      vc[q][j] = *reinterpret_cast<const uint32_t *>(tp.vc[p] + row * 64 + 4 * n);
+    }
+    const uint32_t w = *reinterpret_cast<const uint32_t *>(tp.vs[p] + 256 * (q & 1) + 4 * lane);
+    vs[q] = tp.ok[p] ? w : 0u;
+  }
+}
+
+// two E4M3 codes (bits 15:0) -> two fp16 values (exact)
+__device__ __forceinline__ v2h e4m3x2_f16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+}
+
+// lane n of each 16-lane row reads lane n + k of the row (0 past the row's end)
+template <int K>
+__device__ __forceinline__ int row_shl(int v) {
+  return __builtin_amdgcn_mov_dpp(v, 0x100 + K, 0xf, 0xf, true);
+}
+template <int K>
+__device__ __forceinline__ float row_shl_f(float v) {
+  return __int_as_float(row_shl<K>(__float_as_int(v)));
+}
+template <int K>
+__device__ __forceinline__ v8h row_shl_v8h(v8h v) {
+  v4i x = __builtin_bit_cast(v4i, v);
+  x = (v4i){row_shl<K>(x[0]), row_shl<K>(x[1]), row_shl<K>(x[2]), row_shl<K>(x[3])};
+  return __builtin_bit_cast(v8h, x);
+}
+
 __global__ void __launch_bounds__(DEC_THREADS) decode_split_kernel(DecArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t vl[4][32 * V16_RS];   // fp16 V, 32 keys per wave
-  __shared__ float part[4][4][DEC_PART];
+  __shared__ float part[DEC_SLOTS][4][DEC_PART];
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int L = min(a.ctx[b], a.max_pages * 64);
   if (split * DEC_SPLIT >= L) return;                      // uniform per workgroup
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 15, g = lane >> 4;                  // MFMA column (query row) / lane group
-  const int t0 = split * DEC_SPLIT + wave * 128;           // this wave's first key
-  const bool has_tile = t0 < L;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;                  // MFMA column / lane group
+  const int rep = n >> 3;                                  // softmax half: key blocks 4 rep .. 4 rep + 3
   const int32_t *pt = a.pt + (int64_t)b * a.max_pages;
+  // this wave's tiles: split * DEC_SPLIT + 128 (4 it + wave), it = 0 .. DEC_TPW - 1
+  const int tbase = split * DEC_SPLIT + 128 * wave;
 
-  float mt = -INFINITY, lsum = 0.0f;
-  v4f acc[8];
-#pragma unroll
-  for (int i = 0; i < 8; i++) acc[i] = (v4f){0.f, 0.f, 0.f, 0.f};
-
-  if (has_tile) {
-    // ---- query operand: column n = residual (n / 4) of head 4 kvh + n % 4; columns 8..15 are zero.
-    // Physical d of (lane group g, step s, element j) = 32 g + 8 s + j.
-    v8h qop[4];
+  // ---- query operand: column n = residual (n >> 2) & 1 of head 4 kvh + (n & 3); columns 8..15
+  // repeat columns 0..7, so that both halves of each row hold every score and split the softmax.
+  // Physical d of (lane group g, step s, element j) = 32 g + 8 s + j.
+  v8h qop[4];
+  {
     const int hq = kvh * 4 + (n & 3);
-    const bool realq = n < 8;
-    {
-      const uint8_t *qc = (n < 4 ? a.q1c : a.q2c) + ((int64_t)b * a.Hq + hq) * 64 + 16 * g;
-      const uint8_t *qs = (n < 4 ? a.q1s : a.q2s) + ((int64_t)b * a.Hq + hq) * 8 + 2 * g;
-      const v4i w = realq ? *reinterpret_cast<const v4i *>(qc) : (v4i){0, 0, 0, 0};
-      const uint32_t sw = realq ? *reinterpret_cast<const uint16_t *>(qs) : 0u;
+    const bool r2 = n & 4;
+    const uint8_t *qc = (r2 ? a.q2c : a.q1c) + ((int64_t)b * a.Hq + hq) * 64 + 16 * g;
+    const uint8_t *qs = (r2 ? a.q2s : a.q1s) + ((int64_t)b * a.Hq + hq) * 8 + 2 * g;
+    const v4i w = *reinterpret_cast<const v4i *>(qc);
+    const v2h sc = e4m3x2_f16(*reinterpret_cast<const uint16_t *>(qs));
 #pragma unroll
-      for (int s = 0; s < 4; s++) qop[s] = expand8((uint32_t)w[s], e4m3_f16((sw >> (8 * (s >> 1))) & 0xffu));
-    }
-    // ---- S^T = K Q^T for 8 blocks of 16 keys
-    v4f S[8];
-#pragma unroll
-    for (int kb = 0; kb < 8; kb++) {
-      const int key = t0 + 16 * kb + n;
-      v4i w = {0, 0, 0, 0};
-      uint32_t sw = 0;
-      if (key < L) {
-        const int pg = pt[key >> 6];
-        if (pg >= 0 && (int64_t)pg < a.num_pages) {
-          const int64_t row = ((int64_t)pg * a.Hkv + kvh) * 64 + (key & 63);
-          w = *reinterpret_cast<const v4i *>(a.kc + row * 64 + 16 * g);
-          sw = *reinterpret_cast<const uint16_t *>(a.ks + row * 8 + 2 * g);
-        }
-      }
-      S[kb] = (v4f){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; s++) {
-        const v8h kop = expand8((uint32_t)w[s], e4m3_f16((sw >> (8 * (s >> 1))) & 0xffu));
-        S[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop, qop[s], S[kb], 0, 0, 0);
-      }
-    }
-    // ---- scores of head n (lanes n < 4): x = log2e * scale * s_tK * (s_t1 D[n] + s_t2 D[n+4])
-    const int64_t bq = (int64_t)b * a.Hq + kvh * 4 + (n & 3);
-    const float ck = DEC_LOG2E * a.scale * a.kt[(int64_t)b * a.Hkv + kvh];
-    const float c1 = ck * a.q1t[bq], c2 = ck * a.q2t[bq];
-#pragma unroll
-    for (int kb = 0; kb < 8; kb++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const float d2 = __shfl_down(S[kb][i], 4, 16);
-        const int key = t0 + 16 * kb + 4 * g + i;
-        const float x = c1 * S[kb][i] + c2 * d2;
-        S[kb][i] = (n < 4 && key < L) ? x : -INFINITY;
-        mt = fmaxf(mt, S[kb][i]);
-      }
-    mt = fmaxf(mt, shfl_xor_f(mt, 16));
-    mt = fmaxf(mt, shfl_xor_f(mt, 32));
-    // ---- P' = 2^(x - m~), P^ = E4M3(448 P') (exact in fp16); columns >= 4 get zeros
-    v8h pop[4];
-#pragma unroll
-    for (int kb = 0; kb < 8; kb++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const float p = (n < 4) ? __builtin_amdgcn_exp2f(S[kb][i] - mt) : 0.0f;
-        lsum += p;
-        pop[kb >> 1][4 * (kb & 1) + i] = e4m3_f16(e4m3_encode(448.0f * p));
-      }
-    // ---- O^T += V^T P^T, 32 keys at a time through this wave's LDS region
-    uint8_t *vw = vl[wave];
-#pragma unroll
-    for (int ks = 0; ks < 4; ks++) {
-      {
-        const int r = lane & 31, dh = lane >> 5;              // key row r, d half dh (64 elements)
-        const int key = t0 + 32 * ks + r;
-        v4i w[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
-        uint32_t sw = 0;
-        if (key < L) {
-          const int pg = pt[key >> 6];
-          if (pg >= 0 && (int64_t)pg < a.num_pages) {
-            const int64_t row = ((int64_t)pg * a.Hkv + kvh) * 64 + (key & 63);
-            w[0] = *reinterpret_cast<const v4i *>(a.vc + row * 64 + 32 * dh);
-            w[1] = *reinterpret_cast<const v4i *>(a.vc + row * 64 + 32 * dh + 16);
-            sw = *reinterpret_cast<const uint32_t *>(a.vs + row * 8 + 4 * dh);
-          }
-        }
-#pragma unroll
-        for (int c = 0; c < 2; c++)
-#pragma unroll
-          for (int e = 0; e < 4; e++) {
-            const int blk = 2 * c + (e >> 1);                   // 16-element block within the half
-            const v8h vv = expand8((uint32_t)w[c][e], e4m3_f16((sw >> (8 * blk)) & 0xffu));
-            *reinterpret_cast<v8h *>(vw + r * V16_RS + 2 * (64 * dh + 32 * c + 8 * e)) = vv;
-          }
-      }
-      // the region is private to this wave and LDS requests of a wave complete in order; the fence
-      // only stops the compiler from moving the transposed reads above the writes
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const v8h pb = pop[ks];
-#pragma unroll
-      for (int db = 0; db < 8; db++) {
-        // A operand: row d = 16 db + n, keys {4g + t, 16 + 4g + t}; tr16 source lane 16g + aa + 4t
-        const int aa = lane & 3, t = (lane >> 2) & 3;
-        v4s rr[2];
-#pragma unroll
-        for (int v = 0; v < 2; v++) {
-          const int key = 16 * v + 4 * g + t;
-          rr[v] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_d *)(vw + key * V16_RS + 2 * (16 * db + 4 * aa)));
-        }
-        // whole-vector reinterpretation (inserting bit-cast elements one at a time miscompiles)
-        const v8h vop = __builtin_bit_cast(v8h, (v8s)__builtin_shufflevector(rr[0], rr[1], 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pb, acc[db], 0, 0, 0);
-      }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-    lsum += shfl_xor_f(lsum, 16);
-    lsum += shfl_xor_f(lsum, 32);
+    for (int s = 0; s < 4; s++) qop[s] = expand8((uint32_t)w[s], sc[s >> 1]);
   }
-  // ---- per-wave partial -> LDS (lanes n < 4 hold head n; d = 16 db + 4 g + i)
-  if (n < 4) {
-    if (g == 0) { part[wave][n][0] = mt; part[wave][n][1] = lsum; }
+  // scores of head n & 3: x = log2e * scale * s_tK * (s_t1 D[Q1 column] + s_t2 D[Q2 column])
+  const int64_t bq = (int64_t)b * a.Hq + kvh * 4 + (n & 3);
+  const float ck = DEC_LOG2E * a.scale * a.kt[(int64_t)b * a.Hkv + kvh];
+  const float c1 = ck * a.q1t[bq], c2 = ck * a.q2t[bq];
+  // V scale redistribution: (key j of this lane, block n / 2) sits in lane 2 kk_j + n / 8, byte
+  // (n / 2) % 4, kk_j the key's row within its quarter
+  int vs_addr[8];
 #pragma unroll
-    for (int db = 0; db < 8; db++)
+  for (int j = 0; j < 8; j++) vs_addr[j] = 4 * (2 * (16 * (j >> 2) + 4 * g + (j & 3)) + (n >> 3));
+  const int vs_sh = 8 * ((n >> 1) & 3);
+
+#pragma unroll 1
+  for (int it = 0; it < DEC_TPW; it++) {
+    const int t0 = tbase + 512 * it;
+    const int slot = 4 * it + wave;
+    const bool tail = t0 + 128 > L;                        // the tile holds keys past the context
+    v4i kc[8];
+    uint32_t ks[8], vc[4][8], vs[4];
+    if (t0 < L) {
+      const TilePages tp = tile_pages(a, pt, kvh, t0, L);
+      load_k(tp, n, g, kc, ks);
+      load_v(tp, lane, n, g, vc, vs);
+    }
+    float mt = -INFINITY, lsum = 0.0f;
+    v4f acc[8];
 #pragma unroll
-      for (int i = 0; i < 4; i++) part[wave][n][2 + 16 * db + 4 * g + i] = acc[db][i];
+    for (int i = 0; i < 8; i++) acc[i] = (v4f){0.f, 0.f, 0.f, 0.f};
+    if (t0 < L) {
+      // ---- S^T = K Q^T for 8 blocks of 16 keys
+      v4f S[8];
+#pragma unroll
+      for (int kb = 0; kb < 8; kb++) {
+        const v2h sc = e4m3x2_f16(ks[kb]);
+        S[kb] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; s++)
+          S[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(expand8((uint32_t)kc[kb][s], sc[s >> 1]), qop[s], S[kb],
+                                                         0, 0, 0);
+      }
+      // ---- this lane's half: key blocks 4 rep + kk, keys 16 (4 rep + kk) + 4 g + i. Q1 columns
+      // (n & 4 == 0) combine with the Q2 column four lanes up; other lanes carry unused values.
+      float x[4][4];
+#pragma unroll
+      for (int kk = 0; kk < 4; kk++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const float sv = rep ? S[4 + kk][i] : S[kk][i];
+          x[kk][i] = c1 * sv + c2 * row_shl_f<4>(sv);
+        }
+      if (tail) {
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++)
+#pragma unroll
+          for (int i = 0; i < 4; i++)
+            if (t0 + 16 * (4 * rep + kk) + 4 * g + i >= L) x[kk][i] = -INFINITY;
+#pragma unroll
+        for (int q = 0; q < 4; q++)                          // scale word of lane L: key 32 q + L / 2
+          if (t0 + 32 * q + (lane >> 1) >= L) vs[q] = 0u;
+      }
+#pragma unroll
+      for (int kk = 0; kk < 4; kk++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) mt = fmaxf(mt, x[kk][i]);
+      mt = fmaxf(mt, shfl_xor_f(mt, 8));
+      mt = fmaxf(mt, shfl_xor_f(mt, 16));
+      mt = fmaxf(mt, shfl_xor_f(mt, 32));
+      // ---- P' = 2^(x - m~), P^ = E4M3(448 P') (exact in fp16), in the B layout of quarter
+      // 2 rep + kq: element 4 (kk & 1) + i for kk = 2 kq + (kk & 1)
+      v8h popl[2];
+#pragma unroll
+      for (int kq = 0; kq < 2; kq++) {
+        v2h pr[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+          const int kk = 2 * kq + (u >> 1), i0 = 2 * (u & 1);
+          const float p0 = __builtin_amdgcn_exp2f(x[kk][i0] - mt);
+          const float p1 = __builtin_amdgcn_exp2f(x[kk][i0 + 1] - mt);
+          lsum += p0 + p1;
+          pr[u] = e4m3x2_f16(e4m3_encode2(448.0f * p0, 448.0f * p1));
+        }
+        popl[kq] = (v8h){pr[0][0], pr[0][1], pr[1][0], pr[1][1], pr[2][0], pr[2][1], pr[3][0], pr[3][1]};
+      }
+      lsum += shfl_xor_f(lsum, 8);
+      lsum += shfl_xor_f(lsum, 16);
+      lsum += shfl_xor_f(lsum, 32);
+      // ---- O^T += V^T P^T, one 32-key quarter at a time (columns 0..3 carry the 4 heads)
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const v8h pb = q < 2 ? popl[q] : row_shl_v8h<8>(popl[q - 2]);
+        uint32_t w[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) w[j] = vc[q][j];
+        transpose8x8_nibbles(w);                             // w[e]: keys j = 0..7 at d = 8 n + e
+        v2h sp[4];
+#pragma unroll
+        for (int jp = 0; jp < 4; jp++) {
+          const uint32_t s0 = (uint32_t)__builtin_amdgcn_ds_bpermute(vs_addr[2 * jp], (int)vs[q]);
+          const uint32_t s1 = (uint32_t)__builtin_amdgcn_ds_bpermute(vs_addr[2 * jp + 1], (int)vs[q]);
+          sp[jp] = e4m3x2_f16(((s0 >> vs_sh) & 0xffu) | (((s1 >> vs_sh) & 0xffu) << 8));
+        }
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+          acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(expand8s(w[e], sp), pb, acc[e], 0, 0, 0);
+      }
+    }
+    // ---- tile partial -> LDS (lanes n < 4 hold head n; acc[e][i] is d = 32 g + 8 i + e)
+    if (n < 4) {
+      if (g == 0) { part[slot][n][0] = mt; part[slot][n][1] = lsum; }
+#pragma unroll
+      for (int e = 0; e < 8; e++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) part[slot][n][2 + 32 * g + 8 * i + e] = acc[e][i];
+    }
   }
   __syncthreads();
-  // ---- merge the 4 tiles: thread -> (head, two d values)
+  // ---- merge the workgroup's tiles: thread -> (head, two d values)
   {
     const int hd = tid >> 6, d0 = 2 * (tid & 63);
     float mm = -INFINITY;
-    for (int w = 0; w < 4; w++) mm = fmaxf(mm, part[w][hd][0]);
+    for (int w = 0; w < DEC_SLOTS; w++) mm = fmaxf(mm, part[w][hd][0]);
     float l = 0.f, o0 = 0.f, o1 = 0.f;
-    for (int w = 0; w < 4; w++) {
+    for (int w = 0; w < DEC_SLOTS; w++) {
       const float mw = part[w][hd][0];
       if (mw == -INFINITY) continue;
       const float f = __builtin_amdgcn_exp2f(mw - mm);
@@ -216,16 +333,23 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_split_kernel(DecArgs a) {
 }
 
 // Merge the splits of each (sequence, head): O = sum e^(m_s - m) O_s / sum e^(m_s - m) l_s, times
-// the V tensor scale / 448 (P^ carried a factor 448).
+// the V tensor scale / 448 (P^ carried a factor 448). A split's (m, l) are read by all threads of
+// the block alike; the loop is unrolled so that the loads of several splits are in flight at once.
 __global__ void __launch_bounds__(128) decode_combine_kernel(DecArgs a) {
+  __shared__ float red[2];
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int kvh = h / 4, hd = h & 3;
   const int L = min(a.ctx[b], a.max_pages * 64);
   const int ns = (L + DEC_SPLIT - 1) / DEC_SPLIT;
   const float *base = a.ws + (((int64_t)b * a.Hkv + kvh) * a.nsplit * 4 + hd) * DEC_PART;
   float mm = -INFINITY;
-  for (int s = 0; s < ns; s++) mm = fmaxf(mm, base[(int64_t)s * 4 * DEC_PART]);
+  for (int s = d; s < ns; s += 128) mm = fmaxf(mm, base[(int64_t)s * 4 * DEC_PART]);
+  for (int m = 1; m < 64; m <<= 1) mm = fmaxf(mm, shfl_xor_f(mm, m));
+  if ((d & 63) == 0) red[d >> 6] = mm;
+  __syncthreads();
+  mm = fmaxf(red[0], red[1]);
   float l = 0.f, o = 0.f;
+#pragma unroll 8
   for (int s = 0; s < ns; s++) {
     const float *p = base + (int64_t)s * 4 * DEC_PART;
     const float f = __builtin_amdgcn_exp2f(p[0] - mm);
