@@ -25,7 +25,7 @@
 namespace fa4 {
 
 constexpr int DEC_THREADS = 256;
-constexpr int DEC_TPW = 2;                        // tiles per wave
+constexpr int DEC_TPW = 4;                        // tiles per wave
 constexpr int DEC_SLOTS = 4 * DEC_TPW;            // tiles per workgroup
 constexpr int DEC_SPLIT = 128 * DEC_SLOTS;        // keys per workgroup
 constexpr int DEC_PART = 130;                     // floats per (split, head) partial: m, l, O[128]
@@ -207,18 +207,24 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_split_kernel(DecArgs a) {
   for (int j = 0; j < 8; j++) vs_addr[j] = 4 * (2 * (16 * (j >> 2) + 4 * g + (j & 3)) + (n >> 3));
   const int vs_sh = 8 * ((n >> 1) & 3);
 
+  // Software pipeline over the wave's tiles: the next tile's K is requested as soon as this tile's
+  // QK has consumed the K registers, and its V as soon as this tile's PV has consumed V, so each
+  // load overlaps half a tile of compute.
+  v4i kc[8];
+  uint32_t ks[8], vc[4][8], vs[4];
+  if (tbase < L) {
+    const TilePages tp = tile_pages(a, pt, kvh, tbase, L);
+    load_k(tp, n, g, kc, ks);
+    load_v(tp, lane, n, g, vc, vs);
+  }
 #pragma unroll 1
   for (int it = 0; it < DEC_TPW; it++) {
     const int t0 = tbase + 512 * it;
     const int slot = 4 * it + wave;
     const bool tail = t0 + 128 > L;                        // the tile holds keys past the context
-    v4i kc[8];
-    uint32_t ks[8], vc[4][8], vs[4];
-    if (t0 < L) {
-      const TilePages tp = tile_pages(a, pt, kvh, t0, L);
-      load_k(tp, n, g, kc, ks);
-      load_v(tp, lane, n, g, vc, vs);
-    }
+    const bool has_next = it + 1 < DEC_TPW && t0 + 512 < L;
+    TilePages tpn;
+    if (has_next) tpn = tile_pages(a, pt, kvh, t0 + 512, L);
     float mt = -INFINITY, lsum = 0.0f;
     v4f acc[8];
 #pragma unroll
@@ -235,6 +241,8 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_split_kernel(DecArgs a) {
           S[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(expand8((uint32_t)kc[kb][s], sc[s >> 1]), qop[s], S[kb],
                                                          0, 0, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      if (has_next) load_k(tpn, n, g, kc, ks);
       // ---- this lane's half: key blocks 4 rep + kk, keys 16 (4 rep + kk) + 4 g + i. Q1 columns
       // (n & 4 == 0) combine with the Q2 column four lanes up; other lanes carry unused values.
       float x[4][4];
@@ -300,6 +308,8 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_split_kernel(DecArgs a) {
         for (int e = 0; e < 8; e++)
           acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(expand8s(w[e], sp), pb, acc[e], 0, 0, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      if (has_next) load_v(tpn, lane, n, g, vc, vs);
     }
     // ---- tile partial -> LDS (lanes n < 4 hold head n; acc[e][i] is d = 32 g + 8 i + e)
     if (n < 4) {
