@@ -11,8 +11,20 @@ attention kernel, inputs resident in HBM. `value` is prefill attention TFLOP/s o
                 KV-cache GB/s, and the decode kernels' HBM roofline;
   cpu_baseline  the CPU oracle (float64 numpy) on a bounded sample of the same workload.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-decode] [--no-cpu-baseline]
+                       [--copy-probe] [--summarize-counters DIR]
+
+HBM traffic: `--copy-probe` adds one untimed plain device copy of COPY_BYTES, so that a
+`rocprofv3 --pmc FETCH_SIZE` (then `WRITE_SIZE`) run of this script records the counters of the
+measured kernels and of a copy of known size together. `--summarize-counters DIR` turns the
+counter CSVs under DIR into profiles/traffic.json: per kernel, the counter reads per dispatch, each
+scaled by (known copy bytes / what the counter read for the copy), with a hash of the kernel's
+sources. The benchmark reports that traffic only while the sources still hash the same (the
+counters describe the kernel they were taken on), and null otherwise.
 """
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -29,6 +41,75 @@ import workloads as W  # noqa: E402
 METRIC = "prefill attn TFLOP/s + decode KV GB/s, as % of MXFP4-MFMA / HBM peak"
 MXFP4_PEAK_TFLOPS = 10100.0          # dense MFMA, FP4/FP6
 HBM_PEAK_GBS = 8000.0
+COPY_BYTES = 1 << 30                 # calibration copy: reads and writes this many bytes
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "fp8_quantized_attention_amd", "csrc")
+# sources whose change invalidates a kernel's recorded counters
+KERNEL_SOURCES = {
+    "attn_fwd_kernel": ["attn_fwd.hip", "fa4_device.h"],
+    "decode_split_kernel": ["decode.hip", "fa4_device.h"],
+}
+
+
+def sources_sha(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def copy_probe():
+    """One plain device-to-device copy of COPY_BYTES (the counters' calibration kernel)."""
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
+def summarize_counters(root):
+    """Counter CSVs (rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of `bench.py --copy-probe`) ->
+    profiles/traffic.json with per-dispatch bytes for the measured kernels. The calibration copy is
+    the runtime's copy kernel dispatch that moved at least a quarter of COPY_BYTES (the input
+    uploads are far smaller)."""
+    rows = {}                                            # (key, counter) -> {dispatch: KiB}
+    for f in glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            name, ctr, kib = r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])
+            key = next((k for k in KERNEL_SOURCES if k in name), None)
+            if key is None and "copyBuffer" in name and kib * 1024.0 >= COPY_BYTES / 4:
+                key = "copy"
+            if key is not None:
+                d = rows.setdefault((key, ctr), {})
+                d[(f, r["Dispatch_Id"])] = d.get((f, r["Dispatch_Id"]), 0.0) + kib
+    per = {k: sum(d.values()) / len(d) for k, d in rows.items()}
+    fac = {c: COPY_BYTES / (per[("copy", c)] * 1024.0) for c in ("FETCH_SIZE", "WRITE_SIZE") if ("copy", c) in per}
+    out = {"copy_bytes": COPY_BYTES, "copy_kib_raw": {c: per[("copy", c)] for c in fac}, "scale": fac,
+           "kernels": {}}
+    for k in KERNEL_SOURCES:
+        if (k, "FETCH_SIZE") in per and (k, "WRITE_SIZE") in per and len(fac) == 2:
+            fb = per[(k, "FETCH_SIZE")] * 1024.0 * fac["FETCH_SIZE"]
+            wb = per[(k, "WRITE_SIZE")] * 1024.0 * fac["WRITE_SIZE"]
+            out["kernels"][k] = {"fetch_kib_raw": per[(k, "FETCH_SIZE")], "write_kib_raw": per[(k, "WRITE_SIZE")],
+                                 "fetch_bytes": fb, "write_bytes": wb, "traffic_bytes": fb + wb,
+                                 "dispatches": len(rows[(k, "FETCH_SIZE")]), "sources_sha": sources_sha(k)}
+    os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
+    with open(TRAFFIC_JSON, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def recorded_traffic(kernel):
+    """HBM bytes per dispatch recorded for `kernel`, or None when absent or taken on other sources."""
+    try:
+        with open(TRAFFIC_JSON) as fh:
+            rec = json.load(fh)["kernels"][kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    return rec["traffic_bytes"] if rec.get("sources_sha") == sources_sha(kernel) else None
 
 
 def causal_pairs(Lq, Lk, causal):
@@ -122,7 +203,12 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--summarize-counters", metavar="DIR")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
@@ -130,6 +216,8 @@ def main():
 
     cfg = next(c for c in W.WORKLOADS if c.name == args.workload)
     select = (5, 100) if cfg.select else None
+    if args.copy_probe:
+        copy_probe()
     step_ms, attn_ms = time_prefill(fa4, cfg, args.steps, args.warmup, select)
     flops = prefill_flops(cfg)
     achieved = flops / (attn_ms * 1e-3) / 1e12
@@ -150,7 +238,8 @@ def main():
                    "d": cfg.d, "causal": cfg.causal, "qk_format": cfg.qk_fmt, "hadamard": cfg.hadamard,
                    "bf16_tiles": "5%" if select else "none", "algorithmic_flops": flops},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / MXFP4_PEAK_TFLOPS, "traffic": None, "kernel": "attn_fwd_kernel",
+                     "frac": achieved / MXFP4_PEAK_TFLOPS, "traffic": recorded_traffic("attn_fwd_kernel")
+                     if cfg.name == W.C1.name else None, "kernel": "attn_fwd_kernel",
                      "kernel_ms": attn_ms},
     }
     print(f"[bench] prefill {cfg.name}: step {step_ms:.4f} ms, attention {attn_ms:.4f} ms", file=sys.stderr,
@@ -162,7 +251,8 @@ def main():
             "metric": "decode KV GB/s", "workload": W.C3.name, "value": kv_bytes / (d_step * 1e-3) / 1e9,
             "unit": "GB/s", "ms_per_step": d_step, "kv_bytes": kv_bytes, "context_tokens": tokens,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "decode_split+combine",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": recorded_traffic("decode_split_kernel"),
+                         "traffic_kernel": "decode_split_kernel", "kernel": "decode_split+combine",
                          "kernel_ms": d_kern}}
         print(f"[bench] decode: step {d_step:.4f} ms, kernels {d_kern:.4f} ms, {gbs:.0f} GB/s", file=sys.stderr,
               flush=True)
