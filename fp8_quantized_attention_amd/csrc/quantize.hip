@@ -71,6 +71,13 @@ __device__ __forceinline__ void hadamard128(float v[4]) {
   v[2] = (float)(a2 * FA4_RSQRT128); v[3] = (float)(a3 * FA4_RSQRT128);
 }
 
+// E2M1 codes of two values, a in bits 3:0 and b in bits 7:4: the gfx950 conversion rounds to nearest
+// with ties to the even code, saturates at +-6 and keeps the sign bit (so -0 and tiny negatives give
+// the negative-zero code). With a scale of 1 it applies no scaling; callers scale beforehand.
+__device__ __forceinline__ uint32_t e2m1_pair(float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0) & 0xffu;
+}
+
 // max over the lanes of an aligned group of `n` lanes (n a power of two <= 32)
 __device__ __forceinline__ float group_max(float v, int n) {
   for (int m = 1; m < n; m <<= 1) v = fmaxf(v, shfl_xor_f(v, m));
@@ -86,15 +93,16 @@ __device__ __forceinline__ uint32_t nv_codes4(const float v[4], float st, uint32
   const uint32_t sb = e4m3_encode(am / six_st);
   const float sbv = e4m3_value(sb);
   const float denom = sbv * st;
-  uint32_t c = 0;
+  uint32_t c;
+  if (sb == 0u) {                                           // zero block scale: signed zeros
+    c = 0;
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
-    uint32_t ci;
-    if (sb == 0u) ci = (__float_as_uint(v[i]) >> 28) & 8u;
-    else ci = e2m1_encode(v[i] / denom);
-    c |= ci << (4 * i);
-    xh[i] = (double)(e2m1_value(ci) * sbv) * (double)st;
+    for (int i = 0; i < 4; i++) c |= ((__float_as_uint(v[i]) >> 28) & 8u) << (4 * i);
+  } else {
+    c = e2m1_pair(v[0] / denom, v[1] / denom) | (e2m1_pair(v[2] / denom, v[3] / denom) << 8);
   }
+#pragma unroll
+  for (int i = 0; i < 4; i++) xh[i] = (double)(e2m1_value((c >> (4 * i)) & 15u) * sbv) * (double)st;
   *sb_out = sb;
   return c;
 }
@@ -127,13 +135,22 @@ __global__ void __launch_bounds__(QUANT_THREADS) quantize_kernel(QArgs a) {
   }
   float gmax = 0.0f;
 
-  // every lane of a wave runs the same number of iterations (the bound is workgroup-uniform), so the
-  // lane-group shuffles below always see all their lanes
-  const int64_t r_end = r0 + min<int64_t>(QUANT_CHUNK, ((max<int64_t>(nrows - r0, 0) + RPB - 1) / RPB) * RPB);
-  for (int64_t rr = r0 + wave * RPW + sub; rr < r_end; rr += RPB) {
+  // All rows of the chunk are loaded before any is processed, so a wave has its whole share of the
+  // chunk in flight at once. Every lane runs every iteration (rows past the end are inactive and
+  // read nothing), so the lane-group shuffles below always see all their lanes.
+  constexpr int NIT = QUANT_CHUNK / RPB;
+  float vin[NIT][4];
+#pragma unroll
+  for (int it = 0; it < NIT; it++) {
+    const int64_t rr = r0 + it * RPB + wave * RPW + sub;
+    vin[it][0] = vin[it][1] = vin[it][2] = vin[it][3] = 0.0f;
+    if (rr < nrows) load4<DT>(a.x, o * a.so + h * a.sh + rr * a.sr + li * 4, vin[it]);
+  }
+#pragma unroll
+  for (int it = 0; it < NIT; it++) {
+    const int64_t rr = r0 + it * RPB + wave * RPW + sub;
     const bool active = rr < nrows;
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
-    if (active) load4<DT>(a.x, o * a.so + h * a.sh + rr * a.sr + li * 4, v);
+    float v[4] = {vin[it][0], vin[it][1], vin[it][2], vin[it][3]};
     // rows are processed by whole lane groups, so inactive lanes only feed zeros to the shuffles
     if (NORM && PASS <= 1) {
       double s = ((double)v[0] * v[0] + (double)v[1] * v[1]) + ((double)v[2] * v[2] + (double)v[3] * v[3]);
@@ -154,9 +171,7 @@ __global__ void __launch_bounds__(QUANT_THREADS) quantize_kernel(QArgs a) {
       am = group_max(am, 8);                                  // 32-element block = 8 lanes
       const int e = mx_exponent(am);
       const float mul = pow2_neg(e);
-      uint32_t c = 0;
-#pragma unroll
-      for (int i = 0; i < 4; i++) c |= e2m1_encode(v[i] * mul) << (4 * i);
+      const uint32_t c = e2m1_pair(v[0] * mul, v[1] * mul) | (e2m1_pair(v[2] * mul, v[3] * mul) << 8);
       if (store) {
         *reinterpret_cast<uint16_t *>(a.codes + orow * (D / 2) + li * 2) = (uint16_t)c;
         if ((li & 7) == 0) a.bscales[orow * (D / 32) + li / 8] = (uint8_t)(e + 127);
