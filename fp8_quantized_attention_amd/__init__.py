@@ -39,13 +39,13 @@ class QInput(ctypes.Structure):
 
 class QOutput(ctypes.Structure):
     _fields_ = [("fmt", _i32), ("codes", _p), ("block_scales", _p), ("scales", _p), ("fold_w", _p),
-                ("fold_sigma", _p)]
+                ("fold_scale", _p)]
 
 
 class AttnArgs(ctypes.Structure):
     _fields_ = [("fmt", _i32), ("q_codes", _p), ("q_scales", _p), ("q_tscale", _p),
                 ("k_codes", _p), ("k_scales", _p), ("k_tscale", _p), ("v_codes", _p), ("v_scales", _p),
-                ("v_fold_w", _p), ("v_fold_sigma", _p), ("q_bf16", _p), ("k_bf16", _p), ("v_bf16", _p), ("bitmap", _p),
+                ("v_fold_w", _p), ("v_fold_scale", _p), ("q_bf16", _p), ("k_bf16", _p), ("v_bf16", _p), ("bitmap", _p),
                 ("B", _i32), ("Hq", _i32), ("Hkv", _i32), ("Lq", _i32), ("Lk", _i32), ("d", _i32),
                 ("causal", _i32), ("softmax_scale", _f32), ("o", _p), ("lse", _p)]
 
@@ -113,7 +113,7 @@ def quantize(x, fmt, hadamard=False, dual=False, row_norms=False, fold=None):
     per row), scales (NVFP4: [outer*heads] tensor scales; FP8: per-row), and with dual=True the
     residual's 'codes2', 'block_scales2', 'scales2'; with row_norms=True 'norm2' [outer, heads, rows];
     FP8 per-token output also carries the attention fold data 'fold_w' [outer, heads, rows] and
-    'fold_sigma' [outer, heads, rows/128] (default: when rows is a multiple of 128).
+    'fold_scale' [outer, heads, rows/128] (default: when rows is a multiple of 128).
     """
     assert x.is_cuda and x.is_contiguous() and x.dim() == 4
     O, H, R, d = x.shape
@@ -133,9 +133,9 @@ def quantize(x, fmt, hadamard=False, dual=False, row_norms=False, fold=None):
         fold = fmt == FA4_FP8_TOKEN and R % 128 == 0 and R > 0
     if fold:
         out["fold_w"] = torch.empty(O, H, R, dtype=torch.float32, device=dev)
-        out["fold_sigma"] = torch.empty(O, H, R // 128, dtype=torch.float32, device=dev)
+        out["fold_scale"] = torch.empty(O, H, R // 128, dtype=torch.float32, device=dev)
     qout = QOutput(fmt, out["codes"].data_ptr(), _ptr(bs), _ptr(out["scales"]), _ptr(out.get("fold_w")),
-                   _ptr(out.get("fold_sigma")))
+                   _ptr(out.get("fold_scale")))
     res = None
     if dual:
         out["codes2"] = torch.empty_like(out["codes"])
@@ -205,7 +205,7 @@ def attn_fwd(q, k, v, causal, fmt, Hq, Hkv, Lq, Lk, d, B=1, bitmap=None, q_bf16=
         softmax_scale = 1.0 / math.sqrt(d)
     a = AttnArgs(fmt, q["codes"].data_ptr(), q["block_scales"].data_ptr(), _ptr(q.get("scales")),
                  k["codes"].data_ptr(), k["block_scales"].data_ptr(), _ptr(k.get("scales")),
-                 v["codes"].data_ptr(), v["scales"].data_ptr(), v["fold_w"].data_ptr(), v["fold_sigma"].data_ptr(),
+                 v["codes"].data_ptr(), v["scales"].data_ptr(), v["fold_w"].data_ptr(), v["fold_scale"].data_ptr(),
                  _ptr(q_bf16), _ptr(k_bf16), _ptr(v_bf16), _ptr(bitmap),
                  B, Hq, Hkv, Lq, Lk, d, int(causal), softmax_scale, out.data_ptr(), _ptr(lse if want_lse else None))
     _check(lib.fa4_attn_fwd(ctypes.byref(a), _stream()), "fa4_attn_fwd")
@@ -312,7 +312,7 @@ class PrefillRunner:
                    "scales": torch.empty(B * Hkv, **f32) if fmt == FA4_NVFP4 else None,
                    "norm2": torch.empty(B, Hkv, Lk, **f32) if self.sel else None}
         self.vq = {"codes": torch.empty(B, Hkv, Lk, d, **u8), "scales": torch.empty(B, Hkv, Lk, **f32),
-                   "fold_w": torch.empty(B, Hkv, Lk, **f32), "fold_sigma": torch.empty(B, Hkv, Lk // 128, **f32)}
+                   "fold_w": torch.empty(B, Hkv, Lk, **f32), "fold_scale": torch.empty(B, Hkv, Lk // 128, **f32)}
         self.o = torch.empty(B, Hq, Lq, d, **f32)
         self.lse = torch.empty(B, Hq, Lq, **f32)
         self.bitmap = torch.empty(B, Hq, Lq // 128, Lk // 128, **u8) if self.sel else None
@@ -324,7 +324,7 @@ class PrefillRunner:
 
         def qout(fm, t):
             return QOutput(fm, t["codes"].data_ptr(), _ptr(t.get("block_scales")), _ptr(t.get("scales")),
-                           _ptr(t.get("fold_w")), _ptr(t.get("fold_sigma")))
+                           _ptr(t.get("fold_w")), _ptr(t.get("fold_scale")))
 
         self._qi = [qin(q), qin(k), qin(v)]
         self._qo = [qout(fmt, self.qq), qout(fmt, self.kq), qout(FA4_FP8_TOKEN, self.vq)]
@@ -336,7 +336,7 @@ class PrefillRunner:
                               _ptr(self.qq["scales"]), self.kq["codes"].data_ptr(),
                               self.kq["block_scales"].data_ptr(), _ptr(self.kq["scales"]),
                               self.vq["codes"].data_ptr(), self.vq["scales"].data_ptr(),
-                              self.vq["fold_w"].data_ptr(), self.vq["fold_sigma"].data_ptr(),
+                              self.vq["fold_w"].data_ptr(), self.vq["fold_scale"].data_ptr(),
                               q.data_ptr() if self.sel else None, k.data_ptr() if self.sel else None,
                               v.data_ptr() if self.sel else None, _ptr(self.bitmap),
                               B, Hq, Hkv, Lq, Lk, d, int(causal), softmax_scale, self.o.data_ptr(),

@@ -13,13 +13,15 @@
 // a lane then owns one query (column l%32) and 64 of a tile's 128 keys, so the row max and sum are
 // in-lane plus one exchange with lane l^32, and the per-query rescale of O is a per-lane scalar.
 //
-// Probabilities: P' = exp(S - m~) against the tile's own row max m~ (<= 1, never underflows as a
-// whole). For FP8 tiles the per-token V scale s_v[c] is folded into P before rounding:
-// P^ = E4M3(P' * 448 s_v[c] / sigma), sigma = max s_v of the tile, so V's codes enter the MFMA as-is
-// and the tile contributes (sigma/448) * e^(m~ - m) * (P^ . Vcode). That per-query factor beta is
-// split as beta = 2^k * f, f in [1, 2): 2^k rides on the E8M0 operand scale of P^T inside the MFMA
-// and f becomes the accumulator's unit u (O_true = u * O_acc), so one multiply per O element per
-// tile keeps the accumulator exact. The denominator uses the unrounded P'.
+// Probabilities: every per-tile scale is a power of two, like the E8M0 scales of the MX formats. A
+// tile's row reference is r = ceil(max S) in log2 units and P' = 2^(S - r) <= 1 (no whole-tile
+// underflow). For FP8 tiles V's per-token scale is folded into P before rounding:
+// P^ = E4M3(P' * w_c), w_c = s_v[c] 2^-e with 2^e the tile's power-of-two V scale (the smallest with
+// 448 * 2^e >= max s_v), so V's codes enter the MFMA as-is. The tile then contributes
+// 2^(r - m) 2^e (P^ . Vcode) to a running accumulator with reference m: 2^e rides on V^T's E8M0
+// operand scale and 2^(r - m) on P^T's, so the MFMA adds each tile exactly and the accumulator is
+// rescaled (by a power of two) only when a tile's reference exceeds m by more than ACC_HEADROOM. The
+// score transform is one FMA per element, and the denominator uses the unrounded P'.
 #include "fa4_device.h"
 #include "fa4_internal.h"
 
@@ -30,12 +32,13 @@ constexpr int K4_RS = 80;     // LDS row stride (bytes) of 4-bit K codes (64 B +
 constexpr int V8_RS = 144;    // LDS row stride of FP8 V rows (128 B + pad)
 constexpr int H16_RS = 272;   // LDS row stride of 16-bit rows (256 B + pad)
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr float ACC_HEADROOM = 32.0f;   // largest tile weight 2^k allowed before the reference is raised
 
 struct AttnArgs {
   const uint8_t *qc, *qs; const float *qt;
   const uint8_t *kc, *ks; const float *kt;
   const uint8_t *vc; const float *vs;
-  const float *vw, *vsig;
+  const float *vw, *vfs;
   const uint16_t *qb, *kb, *vb;
   const uint8_t *bitmap;
   int B, Hq, Hkv, Lq, Lk, causal;
@@ -89,16 +92,6 @@ __device__ __forceinline__ void dma4(const void *g, uint8_t *l) {
 }
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Split beta > 0 into 2^k * f with f in [1, 2); k clamped to [-127, 127].
-__device__ __forceinline__ void split_pow2(float beta, int *k, float *f) {
-  const uint32_t b = __float_as_uint(beta);
-  int e = (int)((b >> 23) & 0xffu) - 127;
-  if (e < -126) { *k = -127; *f = 0.0f; return; }       // negligible (or zero) contribution
-  *k = e > 127 ? 127 : e;
-  *f = __uint_as_float((b & 0x807fffffu) | (127u << 23));
-}
-
-
 // Per-lane LDS byte offsets of every operand read of a tile step. All the XOR swizzles depend only on
 // the lane (the tile-varying parts of a key index are multiples of 16 or 32), so each read is
 // base + lane offset + a compile-time immediate and only these few registers stay live.
@@ -143,8 +136,7 @@ __device__ __forceinline__ void tile_step(const AttnArgs &a, const LaneOff &lo, 
                                           int off, int64_t bhq, int64_t bhk, int nk, float cs_q, float cs_b,
                                           const v8i *qop4, const int *qsc4, const v8h *qop16, const uint8_t *k4,
                                           const uint8_t *ksc, const uint8_t *k16, const uint8_t *vq,
-                                          const uint8_t *v16, const float *svs, float &m, float &lsum, float &unit,
-                                          v16f *acc) {
+                                          const uint8_t *v16, const float *svs, float &m, float &lsum, v16f *acc) {
   constexpr int NDB = D / 32;
   v16f S[4];
   if (sel) {
@@ -197,33 +189,49 @@ __device__ __forceinline__ void tile_step(const AttnArgs &a, const LaneOff &lo, 
         if (key > qpos) S[kb][i] = -INFINITY;
       }
   }
-  float mt = -INFINITY;
+  // The tile's row reference in log2 units is the smallest integer r >= its largest score, and
+  // P' = 2^(S cs - r) <= 1 (its largest value lies in (1/2, 1]).
+  float mS = -INFINITY;
 #pragma unroll
   for (int kb = 0; kb < 4; kb++)
 #pragma unroll
-    for (int i = 0; i < 16; i++) mt = fmaxf(mt, S[kb][i]);
-  mt = fmaxf(mt, shfl_xor_f(mt, 32));
-  const float mt_x = mt * cs;                      // tile max in log2 units
-  const float m_new = fmaxf(m, mt_x);
-  const float alpha = exp2f(m - m_new);            // 0 on the first tile
-  const float betae = exp2f(mt_x - m_new);
-  // (S - m~) is exact at the row maximum, so P' = 1 there exactly, as in the definition
+    for (int i = 0; i < 16; i++) mS = fmaxf(mS, S[kb][i]);
+  mS = fmaxf(mS, shfl_xor_f(mS, 32));
+  const float r = ceilf(mS * cs);
   float tsum = 0.0f;
 #pragma unroll
   for (int kb = 0; kb < 4; kb++)
 #pragma unroll
     for (int i = 0; i < 16; i++) {
-      const float p = __builtin_amdgcn_exp2f((S[kb][i] - mt) * cs);
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][i], cs, -r));
       S[kb][i] = p;
       tsum += p;
     }
-  lsum = lsum * alpha + tsum * betae;
-  m = m_new;
+  // Running reference m (log2 units, an integer): raised only when a tile's reference exceeds it by
+  // more than ACC_HEADROOM, so the accumulator and the sum (tile weights up to 2^ACC_HEADROOM) stay far
+  // from overflow; raising rescales both by an exact power of two.
+  if (__builtin_amdgcn_ballot_w64(r > m + ACC_HEADROOM) != 0) {   // uniform (always on the first tile)
+    const float m_new = fmaxf(m, r);
+    const float alpha = m == -INFINITY ? 0.0f : __builtin_ldexpf(1.0f, (int)(m - m_new));
+#pragma unroll
+    for (int i = 0; i < NDB; i++) acc[i] *= alpha;
+    lsum *= alpha;
+    m = m_new;
+  }
+  int kB = (int)fmaxf(r - m, -255.0f);         // tile weight 2^kB, kB <= ACC_HEADROOM
+  lsum += __builtin_ldexpf(tsum, kB);
+  if (__builtin_amdgcn_ballot_w64(kB < -127) != 0) {
+    // a weight below 2^-127 (the smallest E8M0 scale) of the reference adds nothing representable:
+    // those rows' probabilities are zeroed so that the clamped scale does not inflate them
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) S[kb][i] = kB < -127 ? 0.0f : S[kb][i];
+    kB = kB < -127 ? -127 : kB;
+  }
 
-  float beta = betae;
   if (!sel) {
-    const float sig = a.vsig[bhk * nk + kt];
-    beta = betae * (sig * (1.0f / 448.0f));
+    // P^ = E4M3(P' w_c) with w_c = s_v[c] 2^-e (exact); the tile's 2^e rides on V's operand scale
 #pragma unroll
     for (int kb = 0; kb < 4; kb++)
 #pragma unroll
@@ -236,23 +244,6 @@ __device__ __forceinline__ void tile_step(const AttnArgs &a, const LaneOff &lo, 
         S[kb][4 * a4 + 3] *= w4.w;
       }
   }
-  int k2;
-  float f;
-  split_pow2(beta, &k2, &f);
-  float rho;
-  if (f == 0.0f) {
-    // the tile's weight is below 2^-126 of one accumulator unit: it adds nothing representable.
-    // Its probabilities are zeroed instead of branching, so every lane still feeds the MFMA and
-    // the cross-lane LDS reads below.
-    rho = alpha;
-#pragma unroll
-    for (int kb = 0; kb < 4; kb++) S[kb] = (v16f){};
-  } else {
-    rho = alpha * unit * __builtin_amdgcn_rcpf(f);   // f in [1, 2): rcp is within 1 ulp
-    unit = f;
-  }
-#pragma unroll
-  for (int i = 0; i < NDB; i++) acc[i] *= rho;
 
   // ---- O^T += V^T P^T
   if (sel) {
@@ -262,7 +253,7 @@ __device__ __forceinline__ void tile_step(const AttnArgs &a, const LaneOff &lo, 
       for (int p = 0; p < 2; p++) {
         v8s pbs;
 #pragma unroll
-        for (int j = 0; j < 8; j++) pbs[j] = (short)float_to_bf16_bits(ldexpf(S[kb][8 * p + j], k2));
+        for (int j = 0; j < 8; j++) pbs[j] = (short)float_to_bf16_bits(__builtin_ldexpf(S[kb][8 * p + j], kB));
         const v8bf pb = __builtin_bit_cast(v8bf, pbs);
 #pragma unroll
         for (int mb = 0; mb < NDB; mb++) {
@@ -276,6 +267,9 @@ __device__ __forceinline__ void tile_step(const AttnArgs &a, const LaneOff &lo, 
         }
       }
   } else {
+    // E8M0 code of the tile's power-of-two scale 2^e (stored as a float; 2^-127 is the subnormal whose
+    // exponent field is 0, matching E8M0 code 0)
+    const int scA = (int)((__float_as_uint(a.vfs[bhk * nk + kt]) >> 23) & 0xffu);
 #pragma unroll
     for (int t = 0; t < 2; t++) {
       v8i pop;
@@ -284,7 +278,7 @@ __device__ __forceinline__ void tile_step(const AttnArgs &a, const LaneOff &lo, 
 #pragma unroll
         for (int w = 0; w < 4; w++) {
           const v16f &sv = S[2 * t + half];
-          int x = __builtin_amdgcn_cvt_pk_fp8_f32(sv[4 * w], sv[4 * w + 1], 0, false);
+          int x = __builtin_amdgcn_cvt_pk_fp8_f32(sv[4 * w], sv[4 * w + 1], __builtin_nondeterministic_value(0), false);
           x = __builtin_amdgcn_cvt_pk_fp8_f32(sv[4 * w + 2], sv[4 * w + 3], x, true);
           pop[4 * half + w] = x;
         }
@@ -301,7 +295,7 @@ __device__ __forceinline__ void tile_step(const AttnArgs &a, const LaneOff &lo, 
           vop[2 * u] = r[0];
           vop[2 * u + 1] = r[1];
         }
-        acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, pop, acc[mb], 0, 0, 0, 127, 0, k2 + 127);
+        acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, pop, acc[mb], 0, 0, 0, scA, 0, kB + 127);
       }
     }
   }
@@ -373,7 +367,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
   int kt_end = nk;
   if (CAUSAL) kt_end = min(nk, (off + qt * 128 + 127) / 128 + 1);
 
-  float m = -INFINITY, lsum = 0.0f, unit = 1.0f;
+  float m = -INFINITY, lsum = 0.0f;
   v16f acc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; i++) acc[i] = (v16f){};
@@ -395,7 +389,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
 // crosses the causal diagonal is the last one.
 #define FA4_TILE_STEP(MASKV, SELV, KT, KC, KS, VC, W)                                                         \
   tile_step<D, QF, MASKV, SELV>(a, lo, KT, lane, hh, col, qrow, off, bhq, bhk, nk, cs_q, cs_b, qop4, qsc4, qop16, \
-                                KC, KS, k16, VC, v16, W, m, lsum, unit, acc)
+                                KC, KS, k16, VC, v16, W, m, lsum, acc)
 
   // Tiles are visited in two passes: first every tile computed from the quantized operands, then the
   // selected (bf16) tiles. The result does not depend on the order (each tile's probabilities use its
@@ -513,9 +507,9 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
     }
   }
 #undef FA4_TILE_STEP
-  // ---------------- epilogue: O = u * O_acc / l, LSE = m ln2 + ln l
+  // ---------------- epilogue: O = O_acc / l, LSE = m ln2 + ln l
   const float l = lsum + shfl_xor_f(lsum, 32);
-  const float fin = unit / l;
+  const float fin = 1.0f / l;
   float *orow = a.o + (bhq * a.Lq + qrow) * D;
 #pragma unroll
   for (int mb = 0; mb < NDB; mb++)
@@ -557,7 +551,7 @@ hipError_t launch_attn(const fa4_attn_args *p, hipStream_t s) {
   x.qc = p->q_codes; x.qs = p->q_scales; x.qt = p->q_tscale;
   x.kc = p->k_codes; x.ks = p->k_scales; x.kt = p->k_tscale;
   x.vc = p->v_codes; x.vs = p->v_scales;
-  x.vw = p->v_fold_w; x.vsig = p->v_fold_sigma;
+  x.vw = p->v_fold_w; x.vfs = p->v_fold_scale;
   x.qb = p->q_bf16; x.kb = p->k_bf16; x.vb = p->v_bf16;
   x.bitmap = p->bitmap;
   x.B = p->B; x.Hq = p->Hq; x.Hkv = p->Hkv; x.Lq = p->Lq; x.Lk = p->Lk; x.causal = p->causal;

@@ -108,12 +108,12 @@ fa4_status fa4_quantize_blockscaled(const fa4_qinput *in, uint32_t flags, const 
     REQUIRE(row_norm2 == nullptr, FA4_ERR_UNSUPPORTED, "quantize: row norms need unpaged output");
   }
   REQUIRE(aligned(row_norm2, 4), FA4_ERR_ALIGN, "quantize: row_norm2 must be 4-byte aligned");
-  if (out->fold_w || out->fold_sigma) {
+  if (out->fold_w || out->fold_scale) {
     REQUIRE(out->fmt == FA4_FP8_TOKEN, FA4_ERR_UNSUPPORTED, "quantize: fold outputs need FP8_TOKEN");
-    REQUIRE(out->fold_w && out->fold_sigma, FA4_ERR_NULL, "quantize: fold_w and fold_sigma go together");
+    REQUIRE(out->fold_w && out->fold_scale, FA4_ERR_NULL, "quantize: fold_w and fold_scale go together");
     REQUIRE(in->rows % 128 == 0 && !in->page_table && !in->row_counts, FA4_ERR_UNSUPPORTED,
             "quantize: fold outputs need unpaged, non-ragged rows in multiples of 128");
-    REQUIRE(aligned(out->fold_w, 4) && aligned(out->fold_sigma, 4), FA4_ERR_ALIGN, "quantize: fold alignment");
+    REQUIRE(aligned(out->fold_w, 4) && aligned(out->fold_scale, 4), FA4_ERR_ALIGN, "quantize: fold alignment");
   }
   return hip_status(fa4::launch_quantize(in, flags, out, residual, row_norm2, (hipStream_t)stream),
                     "quantize launch");
@@ -154,13 +154,13 @@ fa4_status fa4_attn_fwd(const fa4_attn_args *a, void *stream) {
     REQUIRE(a->d == 128, FA4_ERR_UNSUPPORTED, "attn: NVFP4 needs d=128 (d=%d)", a->d);
   if (a->B == 0 || a->Lq == 0) return ok();
   REQUIRE(a->q_codes && a->q_scales && a->k_codes && a->k_scales && a->v_codes && a->v_scales && a->o &&
-              a->v_fold_w && a->v_fold_sigma,
+              a->v_fold_w && a->v_fold_scale,
           FA4_ERR_NULL, "attn: a required pointer is NULL");
   if (a->fmt == FA4_NVFP4) REQUIRE(a->q_tscale && a->k_tscale, FA4_ERR_NULL, "attn: NVFP4 tensor scales NULL");
   if (a->bitmap) REQUIRE(a->q_bf16 && a->k_bf16 && a->v_bf16, FA4_ERR_NULL, "attn: bf16 originals needed with a bitmap");
   const void *ptrs[] = {a->q_codes, a->q_scales, a->k_codes, a->k_scales, a->v_codes, a->v_scales, a->o,
                         a->lse, a->q_bf16, a->k_bf16, a->v_bf16, a->q_tscale, a->k_tscale, a->v_fold_w,
-                        a->v_fold_sigma};
+                        a->v_fold_scale};
   for (const void *p : ptrs) REQUIRE(aligned(p, 16), FA4_ERR_ALIGN, "attn: every pointer must be 16-byte aligned");
   REQUIRE(a->softmax_scale > 0.0f, FA4_ERR_SHAPE, "attn: softmax_scale must be positive");
   return hip_status(fa4::launch_attn(a, (hipStream_t)stream), "attention launch");

@@ -38,7 +38,7 @@ struct QArgs {
   uint8_t *rcodes, *rbscales;
   float *rscales;       // residual (dual) tensor maxima / scales
   float *norm2;
-  float *fold_w, *fold_sigma;
+  float *fold_w, *fold_scale;
 };
 
 template <int DT>
@@ -233,12 +233,23 @@ __global__ void __launch_bounds__(QUANT_THREADS) quantize_kernel(QArgs a) {
   }
 }
 
-// Fold data of FP8 per-token V for the attention kernel: per 128-row tile, sigma = max of the row
-// scales and, per row, w = 448 s / sigma computed in float64 and rounded to float32 with round-to-odd.
-// Round-to-odd to 24 bits followed by a round-to-nearest to E4M3's 4 bits gives the same code as
-// rounding the float64 value directly (the intermediate keeps more than 4 + 2 bits), which matters
-// because bf16 inputs make 448 s / sigma land on or next to E4M3 rounding midpoints.
-__global__ void __launch_bounds__(128) fold_kernel(const float *scales, float *fold_w, float *fold_sigma,
+// Fold data of FP8 per-token V for the attention kernel: per 128-row tile a power-of-two scale 2^e,
+// e the smallest integer with 448 * 2^e >= sigma (sigma = max of the tile's row scales), clamped to
+// [-127, 127], and per row w = s * 2^-e (exact). With sigma = M 2^E, M in [1, 2): e = E - 8 when
+// M <= 1.75 (448 * 2^(E-8) = 1.75 * 2^E) and E - 7 otherwise; a subnormal sigma gives -127.
+__device__ __forceinline__ int fold_exponent(float sigma) {
+  const uint32_t b = __float_as_uint(sigma);
+  const int E = (int)((b >> 23) & 0xffu);
+  if (E == 0) return -127;
+  const int e = E - 127 - 8 + ((b & 0x7fffffu) > 0x600000u ? 1 : 0);
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+// 2^e as a float for e in [-127, 127] (2^-127 is the subnormal 0x00400000).
+__device__ __forceinline__ float pow2_float(int e) {
+  return __uint_as_float(e == -127 ? 0x00400000u : (uint32_t)(e + 127) << 23);
+}
+
+__global__ void __launch_bounds__(128) fold_kernel(const float *scales, float *fold_w, float *fold_scale,
                                                    int64_t rows) {
   __shared__ float red[2];
   const int64_t g = blockIdx.y, tile = blockIdx.x;
@@ -249,12 +260,9 @@ __global__ void __launch_bounds__(128) fold_kernel(const float *scales, float *f
   for (int k = 1; k < 64; k <<= 1) m = fmaxf(m, shfl_xor_f(m, k));
   if ((t & 63) == 0) red[t >> 6] = m;
   __syncthreads();
-  const float sigma = fmaxf(red[0], red[1]);
-  const double w64 = 448.0 * (double)sv / (double)sigma;
-  float w = __double2float_rz(w64);
-  if ((double)w != w64) w = __uint_as_float(__float_as_uint(w) | 1u);
-  fold_w[row] = w;
-  if (t == 0) fold_sigma[g * (rows / 128) + tile] = sigma;
+  const int e = fold_exponent(fmaxf(red[0], red[1]));
+  fold_w[row] = __builtin_ldexpf(sv, -e);
+  if (t == 0) fold_scale[g * (rows / 128) + tile] = pow2_float(e);
 }
 
 __global__ void fill_zero_kernel(float *p, int64_t n) {
@@ -291,7 +299,7 @@ static hipError_t quantize_dispatch(const QArgs &a, int fmt, bool had, bool dual
     if ((e = launch_q<D, DT, FA4_FP8_TOKEN, 1, false, false>(a, groups, norm, s)) != hipSuccess) return e;
     if (a.fold_w && a.rows > 0 && groups > 0) {
       hipLaunchKernelGGL(fold_kernel, dim3((unsigned)(a.rows / 128), (unsigned)groups), dim3(128), 0, s,
-                         a.scales, a.fold_w, a.fold_sigma, a.rows);
+                         a.scales, a.fold_w, a.fold_scale, a.rows);
       e = hipGetLastError();
     }
     return e;
@@ -333,7 +341,7 @@ hipError_t launch_quantize(const fa4_qinput *in, uint32_t flags, const fa4_qoutp
   a.rcodes = res ? res->codes : nullptr; a.rbscales = res ? res->block_scales : nullptr;
   a.rscales = res ? res->scales : nullptr;
   a.norm2 = norm2;
-  a.fold_w = out->fold_w; a.fold_sigma = out->fold_sigma;
+  a.fold_w = out->fold_w; a.fold_scale = out->fold_scale;
   const int64_t groups = in->outer * in->heads;
   const bool had = flags & FA4_HADAMARD128, dual = flags & FA4_DUAL_RESIDUAL, norm = norm2 != nullptr;
   if (in->d == 128) {

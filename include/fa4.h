@@ -75,12 +75,11 @@ enum { FA4_HADAMARD128 = 1u << 0, FA4_DUAL_RESIDUAL = 1u << 1 }; /* quantizer fl
  *        rounded to float32) before quantizing (d must be 128; NVFP4 or MXFP4 only).
  *        FA4_DUAL_RESIDUAL (NVFP4 only): `out` receives Q1 = NVFP4(x) and `residual` receives
  *        Q2 = NVFP4(float32(x - dequant(Q1))), with its own tensor scales.
- * fold_w / fold_sigma (FP8_TOKEN, optional, unpaged, rows a multiple of 128): the data that folds the
+ * fold_w / fold_scale (FP8_TOKEN, optional, unpaged, rows a multiple of 128): the data that folds the
  *        per-token V scale into the attention probabilities. For each 128-row tile j of a group,
- *        fold_sigma[j] = sigma = max of the tile's scales, and for each row c, fold_w[c] = the float64
- *        quotient 448 * s[c] / sigma rounded to float32 with round-to-odd (truncate, then set the last
- *        bit if inexact), so that one later round-to-nearest to E4M3 of 1 * fold_w[c] equals the E4M3
- *        rounding of the float64 quotient itself. fa4_attn_fwd consumes both arrays.
+ *        fold_scale[j] = 2^e (a float), e = the smallest integer with 448 * 2^e >= max of the tile's
+ *        scales (clamped to [-127, 127]), and for each row c, fold_w[c] = s[c] * 2^-e (exact, <= 448).
+ *        fa4_attn_fwd consumes both arrays.
  * row_norm2 (optional, [outer*heads*rows] float, unpaged only): squared L2 norm of each UNROTATED
  *        input row, float64 pairwise (binary-tree) sum over d, rounded to float32.
  * During the call the tensor-scale array holds intermediate maxima; it holds s_t when the work ends.
@@ -107,7 +106,7 @@ typedef struct {
   uint8_t *block_scales;
   float *scales;               /* NVFP4: [outer*heads] tensor scales; FP8_TOKEN: [out rows]       */
   float *fold_w;               /* FP8_TOKEN, optional: [out rows] P-fold factor w (see below)     */
-  float *fold_sigma;           /* FP8_TOKEN, optional: [out rows / 128] tile maximum of the scales */
+  float *fold_scale;           /* FP8_TOKEN, optional: [out rows / 128] tile maximum of the scales */
 } fa4_qoutput;
 
 fa4_status fa4_quantize_blockscaled(const fa4_qinput *in, uint32_t flags, const fa4_qoutput *out,
@@ -144,15 +143,15 @@ fa4_status fa4_select_tiles(const float *q_norm2, const float *k_norm2, int32_t 
  * For query row r of head h (key head kv = h / (Hq/Hkv), query position Lk - Lq + r) and each
  * 128-key tile j holding an unmasked key (key c unmasked if !causal or c <= r + Lk - Lq):
  *   S = softmax_scale * q~ . k~ with the dequantized Q/K codes (or the bf16 originals if selected);
- *   m~ = tile row max, P' = exp(S - m~);
- *   unselected: sigma = max s_v over the tile, w_c = 448 s_v[c] / sigma, P^ = E4M3(P' w_c),
- *               T = (sigma / 448) * sum_c P^ * E4M3value(Vcode_c)     (FP8 x FP8 products);
+ *   all per-tile scales are powers of two: r = ceil(tile row max of S log2(e)), P' = 2^(S log2(e) - r);
+ *   unselected: 2^e = the tile's fold_scale, w_c = s_v[c] 2^-e (fold_w), P^ = E4M3(P' w_c),
+ *               T = 2^e * sum_c P^ * E4M3value(Vcode_c)     (FP8 x FP8 products);
  *   selected:   T = sum_c bf16(P') * v_c with the bf16 originals;
- *   O = sum_j e^(m~_j - m) T_j / sum_j e^(m~_j - m) sum_c P'   (m = max_j m~_j), LSE = m + ln(denominator).
+ *   O = sum_j 2^(r_j - m) T_j / sum_j 2^(r_j - m) sum_c P'   (m = max_j r_j), LSE = m ln 2 + ln(denominator).
  * Layouts: q_codes [B][Hq][Lq][d/2], q_scales [B][Hq][Lq][d/32] (MXFP4) or [d/16] (NVFP4) with
  * q_tscale [B*Hq]; k_* likewise over [B][Hkv][Lk]; v_codes [B][Hkv][Lk][d] E4M3 with v_scales
- * [B][Hkv][Lk], v_fold_w [B][Hkv][Lk] and v_fold_sigma [B][Hkv][Lk/128] (the quantizer's fold
- * outputs: P' * w_c is formed as P' * v_fold_w[c], with P' exactly 1 at a tile's row maximum); q_bf16 [B][Hq][Lq][d], k_bf16 / v_bf16 [B][Hkv][Lk][d] (bf16 bits; required when
+ * [B][Hkv][Lk], v_fold_w [B][Hkv][Lk] and v_fold_scale [B][Hkv][Lk/128] (the quantizer's fold
+ * outputs); q_bf16 [B][Hq][Lq][d], k_bf16 / v_bf16 [B][Hkv][Lk][d] (bf16 bits; required when
  * bitmap is given); bitmap [B][Hq][Lq/128][Lk/128] or NULL; o [B][Hq][Lq][d] float; lse [B][Hq][Lq]
  * float or NULL. Requirements: d = 128 (or 64 for MXFP4 without a bitmap); Lq, Lk multiples of 128;
  * Lq <= Lk when causal; Hq % Hkv == 0; every pointer 16-byte aligned.
@@ -162,7 +161,7 @@ typedef struct {
   const uint8_t *q_codes, *q_scales; const float *q_tscale;
   const uint8_t *k_codes, *k_scales; const float *k_tscale;
   const uint8_t *v_codes; const float *v_scales;
-  const float *v_fold_w, *v_fold_sigma;        /* fa4_quantize_blockscaled's FP8 fold outputs     */
+  const float *v_fold_w, *v_fold_scale;        /* fa4_quantize_blockscaled's FP8 fold outputs     */
   const uint16_t *q_bf16, *k_bf16, *v_bf16;
   const uint8_t *bitmap;
   int32_t B, Hq, Hkv, Lq, Lk, d, causal;

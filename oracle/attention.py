@@ -13,6 +13,9 @@ Sources:
   * "BitDecoding-FP4" (sns.style digest): the probabilities are quantized with
     a scale kept safe from underflow (here one scale per query row and
     128-key tile, taken from that tile's own row maximum).
+  * "MXFP vs NVFP4" (tqpw.cn 81738) section 2.1: MX block scales are pure
+    powers of two (E8M0). The per-tile scales of P and of the folded V scale
+    below are read the same way, as powers of two.
   * "General notes on quantization" (zdszero), GEMM factoring: a low-precision
     product rescaled by the product of the operand scales; merging two scales
     into one (used to fold V's per-token scale into P).
@@ -21,19 +24,22 @@ Computation per (batch b, query head h, query row r), key head kv = h // (Hq/Hkv
 offset off = Lk - Lq (query r sits at key position off + r), scale = 1/sqrt(d),
 tiles of 128 keys; column c of tile j is unmasked when not causal or c <= r + off:
   1. S_rc = scale * sum_d q~_rd k~_cd with the dequantized quantized Q/K, or
-     with the original bf16 Q/K when tile j is selected.
-  2. m~_rj = max of S_rc over the unmasked columns of tile j; P'_rc = exp(S_rc - m~_rj)
-     (0 for masked columns).
-  3. Unselected tile: sigma_j = max of s_v over the tile's keys, w_c = 448 s_v[c] / sigma_j,
-     P^_rc = E4M3(P'_rc w_c) (one rounding from the float64 value),
-     T_rj = (sigma_j / 448) sum_c P^_rc E4M3value(Vcode_c).
+     with the original bf16 Q/K when tile j is selected; X_rc = S_rc log2(e).
+  2. The tile's row scale is a power of two: r_rj = ceil(max of X_rc over the
+     unmasked columns of tile j), and P'_rc = 2^(X_rc - r_rj) (0 for masked
+     columns), so the row's largest P' lies in (1/2, 1].
+  3. Unselected tile: sigma_j = max of s_v over the tile's keys; e_j = the smallest
+     integer with 448 * 2^e_j >= sigma_j (clamped to [-127, 127]);
+     w_c = s_v[c] * 2^-e_j (exact, <= 448); P^_rc = E4M3(P'_rc w_c) (one rounding
+     from the float64 value); T_rj = 2^e_j sum_c P^_rc E4M3value(Vcode_c).
      Selected tile: T_rj = sum_c bf16(P'_rc) v_c with the original bf16 V.
-  4. m_r = max_j m~_rj, D_r = sum_j e^(m~_rj - m_r) sum_c P'_rc (unquantized P'),
-     N_r = sum_j e^(m~_rj - m_r) T_rj; O_r = N_r / D_r (returned as float32),
-     LSE_r = m_r + ln D_r.
-Because P' and P^ depend only on their own tile's maximum, the result does not
-depend on the order in which tiles are visited; `attend_rows_online` computes
-the same thing with a running maximum and sum.
+  4. m_r = max_j r_rj, D_r = sum_j 2^(r_rj - m_r) sum_c P'_rc (unquantized P'),
+     N_r = sum_j 2^(r_rj - m_r) T_rj; O_r = N_r / D_r (returned as float32),
+     LSE_r = m_r ln 2 + ln D_r.
+Without rounding of P, every choice of the per-tile powers of two cancels and
+O is exactly softmax(S) V. Because P' and P^ depend only on their own tile, the
+result does not depend on the order in which tiles are visited;
+`attend_rows_online` computes the same thing with a running maximum and sum.
 """
 import numpy as np
 
@@ -42,23 +48,35 @@ from .formats import E4M3_MAX, bf16_round, e4m3_decode, e4m3_encode, fp32
 TILE = 128
 
 
+def fold_exponent(sigma):
+    """Smallest integer e with 448 * 2^e >= sigma (sigma > 0), clamped to [-127, 127] (exact
+    comparisons: 448 * 2^e is exact in float64)."""
+    e = int(np.ceil(np.log2(sigma / E4M3_MAX)))
+    while E4M3_MAX * 2.0 ** (e - 1) >= sigma:
+        e -= 1
+    while E4M3_MAX * 2.0 ** e < sigma:
+        e += 1
+    return min(max(e, -127), 127)
+
+
 def _tile_terms(S, unmasked, sel, vq_vals, s_v, v_orig, round_p=True):
-    """Per-row (m~, sum P', T) of one key tile. S: [R, n] float64 scores (already scaled)."""
-    S = np.where(unmasked, S, -np.inf)
+    """Per-row (r, sum P', T) of one key tile, r the tile's power-of-two row reference in log2 units.
+    S: [R, n] float64 scores (already scaled)."""
+    X = np.where(unmasked, S * np.log2(np.e), -np.inf)
     has = unmasked.any(axis=1)
-    m = np.where(has, S.max(axis=1, initial=-np.inf), 0.0)
-    P = np.where(unmasked, np.exp(S - m[:, None]), 0.0)
+    r = np.where(has, np.ceil(X.max(axis=1, initial=-np.inf)), 0.0)
+    P = np.where(unmasked, np.exp2(X - r[:, None]), 0.0)
     l = P.sum(axis=1)
     if sel:
         Pt = bf16_round(P) if round_p else P
         T = Pt @ v_orig
     else:
-        sigma = float(np.max(s_v))
-        w = E4M3_MAX * s_v.astype(np.float64) / sigma
+        e = fold_exponent(float(np.max(s_v)))
+        w = s_v.astype(np.float64) * 2.0 ** -e
         Pw = P * w[None, :]
         Ph = e4m3_decode(e4m3_encode(Pw)) if round_p else Pw
-        T = (sigma / E4M3_MAX) * (Ph @ vq_vals)
-    return np.where(has, m, -np.inf), l, T
+        T = 2.0 ** e * (Ph @ vq_vals)
+    return np.where(has, r, -np.inf), l, T
 
 
 def _row_tiles(rows, Lq, Lk, causal, tile=TILE):
@@ -98,12 +116,12 @@ def attend_rows(rows, q_rows, k_deq, v_codes, s_v, scale, Lq, Lk, causal,
         m, l, T = _tile_terms(S, unmasked, sel, vq_vals[cs], s_v[cs],
                               v_orig[cs] if sel else None, round_p)
         ms.append(m); ls.append(l); Ts.append(T)
-    M = np.stack(ms, axis=0)                       # [J, R]
+    M = np.stack(ms, axis=0)                       # [J, R] log2 units
     mrow = M.max(axis=0)
-    f = np.exp(M - mrow[None, :])                  # e^(m~_j - m), 0 for empty tiles
+    f = np.exp2(M - mrow[None, :])                 # 2^(r_j - m), 0 for empty tiles
     D = (f * np.stack(ls, axis=0)).sum(axis=0)
     N = (f[:, :, None] * np.stack(Ts, axis=0)).sum(axis=0)
-    return N / D[:, None], mrow + np.log(D)
+    return N / D[:, None], mrow * np.log(2.0) + np.log(D)
 
 
 def attend_rows_online(rows, q_rows, k_deq, v_codes, s_v, scale, Lq, Lk, causal,
@@ -111,8 +129,8 @@ def attend_rows_online(rows, q_rows, k_deq, v_codes, s_v, scale, Lq, Lk, causal,
                        tile_order=None):
     """The same computation as attend_rows with a running max m, sum l and accumulator acc.
 
-    For each tile: m_new = max(m, m~); acc = acc e^(m - m_new) + T e^(m~ - m_new);
-    l = l e^(m - m_new) + (sum P') e^(m~ - m_new).
+    For each tile (log2 units): m_new = max(m, r); acc = acc 2^(m - m_new) + T 2^(r - m_new);
+    l = l 2^(m - m_new) + (sum P') 2^(r - m_new).
     """
     rows = np.asarray(rows)
     off = Lk - Lq
@@ -132,12 +150,12 @@ def attend_rows_online(rows, q_rows, k_deq, v_codes, s_v, scale, Lq, Lk, causal,
         mt, lt, T = _tile_terms(S, unmasked, sel, vq_vals[cs], s_v[cs],
                                 v_orig[cs] if sel else None, round_p)
         m_new = np.maximum(m, mt)
-        a_old = np.where(np.isfinite(m), np.exp(m - m_new), 0.0)
-        a_new = np.where(np.isfinite(mt), np.exp(mt - m_new), 0.0)
+        a_old = np.where(np.isfinite(m), np.exp2(m - m_new), 0.0)
+        a_new = np.where(np.isfinite(mt), np.exp2(mt - m_new), 0.0)
         acc = acc * a_old[:, None] + T * a_new[:, None]
         l = l * a_old + lt * a_new
         m = m_new
-    return acc / l[:, None], m + np.log(l)
+    return acc / l[:, None], m * np.log(2.0) + np.log(l)
 
 
 def attention_prefill(q_deq, k_deq, v_codes, s_v, causal, scale=None,

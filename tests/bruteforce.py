@@ -157,8 +157,10 @@ def attention_rows(rows, Q, K, Vc, sv, Qo, Ko, Vo, sel, Lq, Lk, causal, scale, r
             for c in cols:
                 a, b = (Qo[r], Ko[c]) if s_sel else (Q[r], K[c])
                 S[c] = scale * sum(a[t] * b[t] for t in range(d))
-            m = max(S.values())
-            P = {c: math.exp(S[c] - m) for c in cols}
+            # row reference: the smallest integer >= the tile's largest score in log2 units
+            x = {c: S[c] / math.log(2.0) for c in cols}
+            m = math.ceil(max(x.values()))
+            P = {c: 2.0 ** (x[c] - m) for c in cols}
             T = [0.0] * d
             if s_sel:
                 for c in cols:
@@ -167,16 +169,19 @@ def attention_rows(rows, Q, K, Vc, sv, Qo, Ko, Vo, sel, Lq, Lk, causal, scale, r
                         T[t] += p * Vo[c][t]
             else:
                 sigma = max(sv[128 * j:128 * j + 128])
+                e = -127                              # smallest e with 448 * 2^e >= sigma
+                while 448.0 * 2.0 ** e < sigma:
+                    e += 1
                 for c in cols:
-                    w = 448.0 * sv[c] / sigma
+                    w = sv[c] * 2.0 ** -e
                     p = e4m3_value(e4m3_encode(P[c] * w)) if round_p else P[c] * w
                     for t in range(d):
                         T[t] += p * e4m3_value(Vc[c][t])
-                T = [sigma / 448.0 * v for v in T]
+                T = [2.0 ** e * v for v in T]
             terms.append((m, sum(P.values()), T))
         mm = max(t[0] for t in terms)
-        D = sum(math.exp(t[0] - mm) * t[1] for t in terms)
-        out.append([sum(math.exp(t[0] - mm) * t[2][k] for t in terms) / D for k in range(d)])
+        D = sum(2.0 ** (t[0] - mm) * t[1] for t in terms)
+        out.append([sum(2.0 ** (t[0] - mm) * t[2][k] for t in terms) / D for k in range(d)])
     return out
 
 

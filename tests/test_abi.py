@@ -97,7 +97,7 @@ def test_quantize_rejects_before_launch():
 
 def _attn(**kw):
     base = dict(fmt=fa4.FA4_MXFP4, q_codes=256, q_scales=256, q_tscale=None, k_codes=256, k_scales=256,
-                k_tscale=None, v_codes=256, v_scales=256, v_fold_w=256, v_fold_sigma=256, q_bf16=None, k_bf16=None, v_bf16=None, bitmap=None,
+                k_tscale=None, v_codes=256, v_scales=256, v_fold_w=256, v_fold_scale=256, q_bf16=None, k_bf16=None, v_bf16=None, bitmap=None,
                 B=1, Hq=4, Hkv=2, Lq=256, Lk=512, d=128, causal=1, softmax_scale=0.088, o=256, lse=None)
     base.update(kw)
     return fa4.AttnArgs(*[base[f] for f, _ in fa4.AttnArgs._fields_])

@@ -138,3 +138,29 @@ def test_empty_bitmap_equals_no_selection_and_error_budget():
     # the x20 key outlier channels dominate their 32-element MXFP4 blocks, so the quantized path is far
     # from unquantized attention on this data (reported, not a gate); bf16 tiles are close to it
     assert err_b < 5e-3 < err_q < 1.0
+
+
+def test_fold_exponent_is_the_smallest_power_of_two():
+    """2^e is the smallest power of two with 448 * 2^e >= sigma (exact powers, neighbours, random)."""
+    rng = np.random.default_rng(3)
+    p = 448.0 * 2.0 ** np.arange(-40, 40)
+    sig = np.concatenate([p, np.nextafter(p, np.inf), np.nextafter(p, 0.0),
+                          rng.random(2000) * 10.0 ** rng.integers(-12, 12, 2000)])
+    for s in sig.astype(np.float32).astype(np.float64):
+        e = A.fold_exponent(float(s))
+        assert 448.0 * 2.0 ** e >= s and 448.0 * 2.0 ** (e - 1) < s
+    assert A.fold_exponent(1e-45) == -127 and A.fold_exponent(448.0) == 0 and A.fold_exponent(449.0) == 1
+
+
+def test_tile_reference_is_a_power_of_two_bound():
+    """Each tile's row reference is an integer (log2 units) and the row's largest P' lies in (1/2, 1]."""
+    rng = np.random.default_rng(4)
+    S = rng.standard_normal((16, 128)) * 5.0
+    unmasked = rng.random((16, 128)) < 0.7
+    unmasked[:, 0] = True
+    r, l, _ = A._tile_terms(S, unmasked, True, None, None, np.zeros((128, 4)), round_p=False)
+    assert np.array_equal(r, np.round(r))
+    X = np.where(unmasked, S * np.log2(np.e), -np.inf)
+    pmax = np.exp2(X.max(axis=1) - r)
+    assert np.all((pmax > 0.5) & (pmax <= 1.0))
+    assert np.allclose(l, np.where(unmasked, np.exp2(X - r[:, None]), 0.0).sum(axis=1), rtol=0, atol=0)

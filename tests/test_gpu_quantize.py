@@ -60,13 +60,12 @@ def test_mxfp4_bf16_outliers_and_special_values(fa4):
     assert np.array_equal(_np(out["block_scales"]), scales)
 
 
-def _round_to_odd_f32(x64):
-    """float64 -> float32 with round-to-odd: truncate toward zero, then set the last bit if inexact."""
-    f = x64.astype(np.float32)
-    over = np.abs(f.astype(np.float64)) > np.abs(x64)
-    f = np.where(over, np.nextafter(f, np.float32(0)), f).astype(np.float32)
-    inexact = f.astype(np.float64) != x64
-    return np.where(inexact, (f.view(np.uint32) | 1).view(np.float32), f)
+def _fold_exponent(sigma):
+    """Smallest e with 448 * 2^e >= sigma, clamped to [-127, 127] (search from the definition)."""
+    e = -127
+    while 448.0 * 2.0 ** e < sigma and e < 127:
+        e += 1
+    return e
 
 
 def test_fp8_per_token(fa4):
@@ -76,12 +75,12 @@ def test_fp8_per_token(fa4):
     codes, sv = Q.fp8_per_token_quantize(v.float().numpy())
     assert np.array_equal(_np(out["codes"]), codes)
     assert np.array_equal(_np(out["scales"]), sv)
-    # fold data: sigma = tile max of s_v; w = 448 s_v / sigma (float64) rounded to float32 by round-to-odd
-    tiles = sv.reshape(1, 2, -1, 128)
-    sigma = tiles.max(axis=-1)
-    w64 = 448.0 * tiles.astype(np.float64) / sigma[..., None].astype(np.float64)
-    assert np.array_equal(_np(out["fold_sigma"]), sigma)
-    assert np.array_equal(_np(out["fold_w"]), _round_to_odd_f32(w64).reshape(1, 2, -1))
+    # fold data: 2^e per tile (the smallest power of two with 448 * 2^e >= the tile max of s_v) and
+    # w = s_v * 2^-e, both exact
+    tiles = sv.reshape(1, 2, -1, 128).astype(np.float64)
+    e = np.vectorize(_fold_exponent)(tiles.max(axis=-1))
+    assert np.array_equal(_np(out["fold_scale"]).astype(np.float64), 2.0 ** e)
+    assert np.array_equal(_np(out["fold_w"]).astype(np.float64), (tiles * 2.0 ** -e[..., None]).reshape(1, 2, -1))
     x = _special_rows(seed=1)[None, None]
     x[0, 0, 4] = 1e30                                # stays finite through the per-token scale
     out = fa4.quantize(torch.from_numpy(x).cuda(), fa4.FA4_FP8_TOKEN)
