@@ -171,7 +171,12 @@ __device__ __forceinline__ v8h row_shl_v8h(v8h v) {
 
 __global__ void __launch_bounds__(DEC_THREADS) decode_split_kernel(DecArgs a) {
   __shared__ float part[DEC_SLOTS][4][DEC_PART];
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  // Workgroup order: (sequence, key head) fastest, split slowest. Workgroups are handed to the 8 XCDs
+  // round-robin, so every XCD gets the same mix of sequences (with 8 key heads, one key head each,
+  // whose pages then stay in that XCD's L2), and the mostly empty trailing splits come last.
+  const int nbk = a.B * a.Hkv;
+  const int split = (int)(blockIdx.x / (unsigned)nbk), bk = (int)(blockIdx.x - (unsigned)split * nbk);
+  const int b = bk / a.Hkv, kvh = bk - b * a.Hkv;
   const int L = min(a.ctx[b], a.max_pages * 64);
   if (split * DEC_SPLIT >= L) return;                      // uniform per workgroup
   const int tid = threadIdx.x, lane = tid & 63;
@@ -393,7 +398,7 @@ size_t decode_workspace_bytes(const fa4_decode_args *p) {
 hipError_t launch_decode(const fa4_decode_args *p, void *ws, hipStream_t s) {
   if (p->B == 0) return hipSuccess;
   const DecArgs x = make_dec(p, ws);
-  hipLaunchKernelGGL(decode_split_kernel, dim3(x.nsplit, x.Hkv, x.B), dim3(DEC_THREADS), 0, s, x);
+  hipLaunchKernelGGL(decode_split_kernel, dim3((unsigned)((int64_t)x.nsplit * x.B * x.Hkv)), dim3(DEC_THREADS), 0, s, x);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(x.Hq, x.B), dim3(128), 0, s, x);
