@@ -123,25 +123,28 @@ def prefill_flops(cfg):
     return 4.0 * cfg.d * causal_pairs(cfg.Lq, cfg.Lk, cfg.causal) * cfg.B * cfg.Hq
 
 
+def _time_loop(fn, n):
+    """Average ms of n back-to-back calls of fn, HIP events on the current (launch) stream."""
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(n):
+        fn()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / n
+
+
 def time_prefill(fa4, cfg, steps, warmup, select):
+    """(ms per whole step, ms per attention launch). The step loop has no events inside it; the
+    attention kernel is timed on its own loop of back-to-back launches over the same inputs."""
     q, k, v = (t.cuda() for t in W.prefill_inputs(cfg))
     fmt = fa4.FA4_MXFP4 if cfg.qk_fmt == "mxfp4" else fa4.FA4_NVFP4
     run = fa4.PrefillRunner(q, k, v, cfg.causal, fmt=fmt, hadamard=cfg.hadamard, select=select)
     for _ in range(warmup):
         run.run()
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    t0.record()
-    for i in range(steps):
-        run.quantize()
-        ev[i][0].record()
-        run.attention()
-        ev[i][1].record()
-    t1.record()
-    torch.cuda.synchronize()
-    step_ms = t0.elapsed_time(t1) / steps
-    attn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    step_ms = _time_loop(run.run, steps)
+    attn_ms = _time_loop(run.attention, steps)
     return step_ms, attn_ms
 
 
@@ -158,19 +161,8 @@ def time_decode(fa4, cfg, steps, warmup):
     run = fa4.DecodeRunner(q, caches[0], caches[1], pt, ctx, cfg.Hkv)
     for _ in range(warmup):
         run.run()
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    t0.record()
-    for i in range(steps):
-        run.quantize()
-        ev[i][0].record()
-        run.attention()
-        ev[i][1].record()
-    t1.record()
-    torch.cuda.synchronize()
-    step_ms = t0.elapsed_time(t1) / steps
-    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    step_ms = _time_loop(run.run, steps)
+    kern_ms = _time_loop(run.attention, steps)
     kv_bytes = float(lay.ctx_len.double().sum()) * cfg.Hkv * 2 * (cfg.d // 2 + cfg.d // 16)
     return step_ms, kern_ms, kv_bytes, int(lay.ctx_len.sum())
 
