@@ -89,17 +89,18 @@ fa4_status fa4_quantize_blockscaled(const fa4_qinput *in, uint32_t flags, const 
     REQUIRE(residual && residual->scales && (in->rows == 0 || (residual->codes && residual->block_scales)),
             FA4_ERR_NULL, "quantize: dual residual output missing");
     REQUIRE(residual->fmt == FA4_NVFP4, FA4_ERR_UNSUPPORTED, "quantize: residual format must be NVFP4");
-    REQUIRE(aligned(residual->codes, 4) && aligned(residual->block_scales, 4) && aligned(residual->scales, 4),
-            FA4_ERR_ALIGN, "quantize: residual outputs must be 4-byte aligned");
+    REQUIRE(aligned(residual->codes, 16) && aligned(residual->block_scales, 4) && aligned(residual->scales, 4),
+            FA4_ERR_ALIGN, "quantize: residual codes must be 16-byte aligned, scales 4-byte aligned");
   }
-  const size_t esz = in->dtype == FA4_F32 ? 4 : 2;
-  REQUIRE(in->rows == 0 || aligned(in->x, 4 * esz), FA4_ERR_ALIGN, "quantize: x must be %zu-byte aligned", 4 * esz);
-  REQUIRE(in->stride_outer % 4 == 0 && in->stride_head % 4 == 0 && in->stride_row % 4 == 0, FA4_ERR_ALIGN,
-          "quantize: strides must be multiples of 4 elements");
+  // every lane reads one 16-byte run of a row (8 bf16 or 4 float values)
+  const int64_t epl = in->dtype == FA4_F32 ? 4 : 8;
+  REQUIRE(in->rows == 0 || aligned(in->x, 16), FA4_ERR_ALIGN, "quantize: x must be 16-byte aligned");
+  REQUIRE(in->stride_outer % epl == 0 && in->stride_head % epl == 0 && in->stride_row % epl == 0, FA4_ERR_ALIGN,
+          "quantize: strides must be multiples of %lld elements (16 bytes)", (long long)epl);
   REQUIRE(in->stride_outer >= 0 && in->stride_head >= 0 && in->stride_row >= in->d, FA4_ERR_SHAPE,
           "quantize: strides must be non-negative and stride_row >= d");
-  REQUIRE(aligned(out->codes, 4) && aligned(out->block_scales, 4) && aligned(out->scales, 4), FA4_ERR_ALIGN,
-          "quantize: outputs must be 4-byte aligned");
+  REQUIRE(aligned(out->codes, 16) && aligned(out->block_scales, 4) && aligned(out->scales, 4), FA4_ERR_ALIGN,
+          "quantize: codes must be 16-byte aligned, scales 4-byte aligned");
   if (in->page_table) {
     REQUIRE(in->page_size > 0 && in->max_pages > 0 && in->num_pages > 0, FA4_ERR_SHAPE,
             "quantize: paged output needs page_size, max_pages and num_pages > 0");

@@ -41,34 +41,57 @@ struct QArgs {
   float *fold_w, *fold_scale;
 };
 
+// Elements per lane: one 16-byte load (8 bf16 or 4 float values).
 template <int DT>
-__device__ __forceinline__ void load4(const void *x, int64_t off, float v[4]) {
+struct Epl {
+  static constexpr int value = DT == 0 ? 4 : 8;
+};
+
+template <int DT, int E>
+__device__ __forceinline__ void load_lane(const void *x, int64_t off, float v[E]) {
   if (DT == 0) {
     const float4 t = *reinterpret_cast<const float4 *>(static_cast<const float *>(x) + off);
     v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
   } else {
-    const uint2 t = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(x) + off);
-    v[0] = bf16_bits_to_float(t.x & 0xffffu); v[1] = bf16_bits_to_float(t.x >> 16);
-    v[2] = bf16_bits_to_float(t.y & 0xffffu); v[3] = bf16_bits_to_float(t.y >> 16);
+    const uint4 t = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + off);
+    const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      v[2 * i] = bf16_bits_to_float(w[i] & 0xffffu);
+      v[2 * i + 1] = bf16_bits_to_float(w[i] >> 16);
+    }
   }
 }
 
-// In-place Sylvester Hadamard transform of a 128-row held 4 per lane over 32 lanes, float64,
-// then scaled by 1/sqrt(128) and rounded once to float32.
-__device__ __forceinline__ void hadamard128(float v[4]) {
-  double a0 = v[0], a1 = v[1], a2 = v[2], a3 = v[3];
-  double b0 = a0 + a1, b1 = a0 - a1, b2 = a2 + a3, b3 = a2 - a3;       // distance 1
-  a0 = b0 + b2; a2 = b0 - b2; a1 = b1 + b3; a3 = b1 - b3;               // distance 2
+// In-place Sylvester Hadamard transform of a 128-element row held E per lane over 128/E lanes,
+// float64, then scaled by 1/sqrt(128) and rounded once to float32. Butterflies at distances below E
+// run inside the lane; the others pair lanes (the lane whose mask bit is clear holds the lower
+// index: a' = a + b there, b' = a - b in its partner).
+template <int E>
+__device__ __forceinline__ void hadamard128(float v[E]) {
+  double a[E];
+#pragma unroll
+  for (int i = 0; i < E; i++) a[i] = v[i];
+#pragma unroll
+  for (int dist = 1; dist < E; dist <<= 1)
+#pragma unroll
+    for (int i = 0; i < E; i++)
+      if ((i & dist) == 0) {
+        const double u = a[i], w = a[i + dist];
+        a[i] = u + w;
+        a[i + dist] = u - w;
+      }
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int m = 1; m < 32; m <<= 1) {                                     // distance 4 .. 64
-    const double p0 = shfl_xor_d(a0, m), p1 = shfl_xor_d(a1, m), p2 = shfl_xor_d(a2, m),
-                 p3 = shfl_xor_d(a3, m);
-    if (lane & m) { a0 = p0 - a0; a1 = p1 - a1; a2 = p2 - a2; a3 = p3 - a3; }
-    else          { a0 = a0 + p0; a1 = a1 + p1; a2 = a2 + p2; a3 = a3 + p3; }
+  for (int m = 1; m < 128 / E; m <<= 1) {
+#pragma unroll
+    for (int i = 0; i < E; i++) {
+      const double p = shfl_xor_d(a[i], m);
+      a[i] = (lane & m) ? p - a[i] : a[i] + p;
+    }
   }
-  v[0] = (float)(a0 * FA4_RSQRT128); v[1] = (float)(a1 * FA4_RSQRT128);
-  v[2] = (float)(a2 * FA4_RSQRT128); v[3] = (float)(a3 * FA4_RSQRT128);
+#pragma unroll
+  for (int i = 0; i < E; i++) v[i] = (float)(a[i] * FA4_RSQRT128);
 }
 
 // E2M1 codes of two values, a in bits 3:0 and b in bits 7:4: the gfx950 conversion rounds to nearest
@@ -78,17 +101,57 @@ __device__ __forceinline__ uint32_t e2m1_pair(float a, float b) {
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0) & 0xffu;
 }
 
+// E2M1 codes of E values (element i in bits 4i+3 .. 4i)
+template <int E>
+__device__ __forceinline__ uint32_t e2m1_lane(const float q[E]) {
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 0; i < E; i += 2) c |= e2m1_pair(q[i], q[i + 1]) << (4 * i);
+  return c;
+}
+
+// x / b rounded to nearest float32 (the IEEE quotient) for E values sharing b, from one correctly
+// rounded reciprocal: with y = RN(1/b) and q = RN(x y) (within 1 ulp of x/b), r = x - b q is exact
+// (FMA) and RN(q + r y) is the correctly rounded x/b (Markstein's theorem; binary arithmetic, no
+// over/underflow). b is a positive normal scale here; quotients below 2^-126 only occur for values
+// whose codes are zeros in every target format, where only the sign matters; the sign is copied from
+// x (the correction step would turn -0 into +0). Scales below 2^-100 (1/b would overflow the
+// theorem's range) use the division itself.
+template <int E>
+__device__ __forceinline__ void div_lane(const float x[E], float b, float q[E]) {
+  if (b < 0x1p-100f) {
+#pragma unroll
+    for (int i = 0; i < E; i++) q[i] = x[i] / b;
+    return;
+  }
+  const float y = 1.0f / b;
+#pragma unroll
+  for (int i = 0; i < E; i++) {
+    const float q0 = x[i] * y;
+    const float r = __builtin_fmaf(-q0, b, x[i]);
+    q[i] = __builtin_copysignf(__builtin_fmaf(r, y, q0), x[i]);   // the quotient has x's sign
+  }
+}
+
 // max over the lanes of an aligned group of `n` lanes (n a power of two <= 32)
 __device__ __forceinline__ float group_max(float v, int n) {
   for (int m = 1; m < n; m <<= 1) v = fmaxf(v, shfl_xor_f(v, m));
   return v;
 }
 
-// NVFP4 codes of 4 elements given the tensor scale; also returns the dequantized values (float64).
-__device__ __forceinline__ uint32_t nv_codes4(const float v[4], float st, uint32_t *sb_out,
-                                              double xh[4]) {
-  float am = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-  am = group_max(am, 4);                                    // 16-element block = 4 lanes
+template <int E>
+__device__ __forceinline__ float lane_amax(const float v[E]) {
+  float m = fabsf(v[0]);
+#pragma unroll
+  for (int i = 1; i < E; i++) m = fmaxf(m, fabsf(v[i]));
+  return m;
+}
+
+// NVFP4 codes of the lane's E elements (one 16-element block spans 16/E lanes) given the tensor
+// scale; also returns the dequantized values (float64).
+template <int E>
+__device__ __forceinline__ uint32_t nv_codes(const float v[E], float st, uint32_t *sb_out, double xh[E]) {
+  const float am = group_max(lane_amax<E>(v), 16 / E);
   const float six_st = 6.0f * st;
   const uint32_t sb = e4m3_encode(am / six_st);
   const float sbv = e4m3_value(sb);
@@ -97,12 +160,14 @@ __device__ __forceinline__ uint32_t nv_codes4(const float v[4], float st, uint32
   if (sb == 0u) {                                           // zero block scale: signed zeros
     c = 0;
 #pragma unroll
-    for (int i = 0; i < 4; i++) c |= ((__float_as_uint(v[i]) >> 28) & 8u) << (4 * i);
+    for (int i = 0; i < E; i++) c |= ((__float_as_uint(v[i]) >> 28) & 8u) << (4 * i);
   } else {
-    c = e2m1_pair(v[0] / denom, v[1] / denom) | (e2m1_pair(v[2] / denom, v[3] / denom) << 8);
+    float qv[E];
+    div_lane<E>(v, denom, qv);
+    c = e2m1_lane<E>(qv);
   }
 #pragma unroll
-  for (int i = 0; i < 4; i++) xh[i] = (double)(e2m1_value((c >> (4 * i)) & 15u) * sbv) * (double)st;
+  for (int i = 0; i < E; i++) xh[i] = (double)(e2m1_value((c >> (4 * i)) & 15u) * sbv) * (double)st;
   *sb_out = sb;
   return c;
 }
@@ -111,10 +176,19 @@ __device__ __forceinline__ float tensor_scale_from_max(float amax) {
   return amax == 0.0f ? 1.0f : amax / 2688.0f;
 }
 
+// store E/2 bytes of packed 4-bit codes (E = 4: 2 bytes, E = 8: 4 bytes)
+template <int E>
+__device__ __forceinline__ void store_nibbles(uint8_t *p, uint32_t c) {
+  if (E == 8) *reinterpret_cast<uint32_t *>(p) = c;
+  else *reinterpret_cast<uint16_t *>(p) = (uint16_t)c;
+}
+
 // PASS: 0 = group maxima (NVFP4), 1 = codes (+ residual maxima when DUAL), 2 = residual codes.
-template <int D, int DT, int FMT, int PASS, bool HAD, bool DUAL, bool NORM>
+// PAGED: rows go to a paged cache through the page table (then NORM is false).
+template <int D, int DT, int FMT, int PASS, bool HAD, bool DUAL, bool NORM, bool PAGED>
 __global__ void __launch_bounds__(QUANT_THREADS) quantize_kernel(QArgs a) {
-  constexpr int LPR = D / 4;              // lanes per row
+  constexpr int E = Epl<DT>::value;       // elements per lane
+  constexpr int LPR = D / E;              // lanes per row
   constexpr int RPW = 64 / LPR;           // rows per wave
   constexpr int RPB = RPW * (QUANT_THREADS / 64);
   __shared__ float red[QUANT_THREADS / 64];
@@ -139,81 +213,98 @@ __global__ void __launch_bounds__(QUANT_THREADS) quantize_kernel(QArgs a) {
   // chunk in flight at once. Every lane runs every iteration (rows past the end are inactive and
   // read nothing), so the lane-group shuffles below always see all their lanes.
   constexpr int NIT = QUANT_CHUNK / RPB;
-  float vin[NIT][4];
+  float vin[NIT][E];
 #pragma unroll
   for (int it = 0; it < NIT; it++) {
     const int64_t rr = r0 + it * RPB + wave * RPW + sub;
-    vin[it][0] = vin[it][1] = vin[it][2] = vin[it][3] = 0.0f;
-    if (rr < nrows) load4<DT>(a.x, o * a.so + h * a.sh + rr * a.sr + li * 4, vin[it]);
+#pragma unroll
+    for (int i = 0; i < E; i++) vin[it][i] = 0.0f;
+    if (rr < nrows) load_lane<DT, E>(a.x, o * a.so + h * a.sh + rr * a.sr + li * E, vin[it]);
   }
 #pragma unroll
   for (int it = 0; it < NIT; it++) {
     const int64_t rr = r0 + it * RPB + wave * RPW + sub;
     const bool active = rr < nrows;
-    float v[4] = {vin[it][0], vin[it][1], vin[it][2], vin[it][3]};
+    float v[E];
+#pragma unroll
+    for (int i = 0; i < E; i++) v[i] = vin[it][i];
     // rows are processed by whole lane groups, so inactive lanes only feed zeros to the shuffles
     if (NORM && PASS <= 1) {
-      double s = ((double)v[0] * v[0] + (double)v[1] * v[1]) + ((double)v[2] * v[2] + (double)v[3] * v[3]);
+      // balanced pairwise tree over the row: in-lane pairs first, then neighbouring lanes
+      double t[E];
+#pragma unroll
+      for (int i = 0; i < E; i++) t[i] = (double)v[i] * v[i];
+#pragma unroll
+      for (int w = 1; w < E; w <<= 1)
+#pragma unroll
+        for (int i = 0; i < E; i += 2 * w) t[i] = t[i] + t[i + w];
+      double s = t[0];
       for (int m = 1; m < LPR; m <<= 1) s = s + shfl_xor_d(s, m);
       if (active && li == 0) a.norm2[(int64_t)g * a.rows + rr] = (float)s;
     }
-    if (HAD) hadamard128(v);
+    if (HAD) hadamard128<E>(v);
     int64_t orow = (int64_t)g * a.rows + rr;
     bool store = active;
-    if (a.page_table) {
+    if (PAGED) {
       // only rows that exist read the page table; a page id outside the cache drops the row
       const int pg = active ? a.page_table[o * a.max_pages + rr / a.page_size] : 0;
       store = active && pg >= 0 && (int64_t)pg < a.num_pages;
       orow = ((int64_t)(store ? pg : 0) * a.heads + h) * a.page_size + rr % a.page_size;
     }
     if (FMT == FA4_MXFP4) {
-      float am = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-      am = group_max(am, 8);                                  // 32-element block = 8 lanes
+      const float am = group_max(lane_amax<E>(v), 32 / E);      // 32-element block = 32/E lanes
       const int e = mx_exponent(am);
       const float mul = pow2_neg(e);
-      const uint32_t c = e2m1_pair(v[0] * mul, v[1] * mul) | (e2m1_pair(v[2] * mul, v[3] * mul) << 8);
+      float sv[E];
+#pragma unroll
+      for (int i = 0; i < E; i++) sv[i] = v[i] * mul;          // exact (a power of two)
+      const uint32_t c = e2m1_lane<E>(sv);
       if (store) {
-        *reinterpret_cast<uint16_t *>(a.codes + orow * (D / 2) + li * 2) = (uint16_t)c;
-        if ((li & 7) == 0) a.bscales[orow * (D / 32) + li / 8] = (uint8_t)(e + 127);
+        store_nibbles<E>(a.codes + orow * (D / 2) + li * (E / 2), c);
+        if ((li % (32 / E)) == 0) a.bscales[orow * (D / 32) + li / (32 / E)] = (uint8_t)(e + 127);
       }
     } else if (FMT == FA4_FP8_TOKEN) {
-      float am = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-      am = group_max(am, LPR);
+      const float am = group_max(lane_amax<E>(v), LPR);
       const float s = am == 0.0f ? 1.0f : am / 448.0f;
-      const uint32_t c = e4m3_encode2(v[0] / s, v[1] / s) | (e4m3_encode2(v[2] / s, v[3] / s) << 16);
+      float qv[E];
+      div_lane<E>(v, s, qv);
+      uint32_t c[E / 4];
+#pragma unroll
+      for (int w = 0; w < E / 4; w++)
+        c[w] = e4m3_encode2(qv[4 * w], qv[4 * w + 1]) | (e4m3_encode2(qv[4 * w + 2], qv[4 * w + 3]) << 16);
       if (store) {
-        *reinterpret_cast<uint32_t *>(a.codes + orow * D + li * 4) = c;
+        if (E == 8) *reinterpret_cast<uint2 *>(a.codes + orow * D + li * 8) = make_uint2(c[0], c[E / 4 - 1]);
+        else *reinterpret_cast<uint32_t *>(a.codes + orow * D + li * 4) = c[0];
         if (li == 0) a.scales[orow] = s;
       }
     } else {  // NVFP4
       if (PASS == 0) {
-        float am = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-        gmax = fmaxf(gmax, active ? am : 0.0f);
+        gmax = fmaxf(gmax, active ? lane_amax<E>(v) : 0.0f);
       } else {
         uint32_t sb;
-        double xh[4];
-        const uint32_t c = nv_codes4(v, st, &sb, xh);
+        double xh[E];
+        const uint32_t c = nv_codes<E>(v, st, &sb, xh);
         if (PASS == 1) {
           if (store) {
-            *reinterpret_cast<uint16_t *>(a.codes + orow * (D / 2) + li * 2) = (uint16_t)c;
-            if ((li & 3) == 0) a.bscales[orow * (D / 16) + li / 4] = (uint8_t)sb;
+            store_nibbles<E>(a.codes + orow * (D / 2) + li * (E / 2), c);
+            if ((li % (16 / E)) == 0) a.bscales[orow * (D / 16) + li / (16 / E)] = (uint8_t)sb;
           }
           if (DUAL) {
             float am = 0.0f;
 #pragma unroll
-            for (int i = 0; i < 4; i++) am = fmaxf(am, fabsf((float)((double)v[i] - xh[i])));
+            for (int i = 0; i < E; i++) am = fmaxf(am, fabsf((float)((double)v[i] - xh[i])));
             gmax = fmaxf(gmax, active ? am : 0.0f);
           }
         } else {  // PASS 2: residual codes
-          float rv[4];
+          float rv[E];
 #pragma unroll
-          for (int i = 0; i < 4; i++) rv[i] = (float)((double)v[i] - xh[i]);
+          for (int i = 0; i < E; i++) rv[i] = (float)((double)v[i] - xh[i]);
           uint32_t rsb;
-          double rxh[4];
-          const uint32_t rc = nv_codes4(rv, rst, &rsb, rxh);
+          double rxh[E];
+          const uint32_t rc = nv_codes<E>(rv, rst, &rsb, rxh);
           if (store) {
-            *reinterpret_cast<uint16_t *>(a.rcodes + orow * (D / 2) + li * 2) = (uint16_t)rc;
-            if ((li & 3) == 0) a.rbscales[orow * (D / 16) + li / 4] = (uint8_t)rsb;
+            store_nibbles<E>(a.rcodes + orow * (D / 2) + li * (E / 2), rc);
+            if ((li % (16 / E)) == 0) a.rbscales[orow * (D / 16) + li / (16 / E)] = (uint8_t)rsb;
           }
         }
       }
@@ -279,10 +370,12 @@ template <int D, int DT, int FMT, int PASS, bool HAD, bool DUAL>
 static hipError_t launch_q(const QArgs &a, int64_t groups, bool norm, hipStream_t s) {
   if (a.rows == 0 || groups == 0) return hipSuccess;       // nothing to read (NVFP4 scales still finalize)
   dim3 grid((unsigned)((a.rows + QUANT_CHUNK - 1) / QUANT_CHUNK), (unsigned)groups);
-  if (norm)
-    hipLaunchKernelGGL((quantize_kernel<D, DT, FMT, PASS, HAD, DUAL, true>), grid, dim3(QUANT_THREADS), 0, s, a);
+  if (a.page_table)                                        // row norms are only written unpaged
+    hipLaunchKernelGGL((quantize_kernel<D, DT, FMT, PASS, HAD, DUAL, false, true>), grid, dim3(QUANT_THREADS), 0, s, a);
+  else if (norm)
+    hipLaunchKernelGGL((quantize_kernel<D, DT, FMT, PASS, HAD, DUAL, true, false>), grid, dim3(QUANT_THREADS), 0, s, a);
   else
-    hipLaunchKernelGGL((quantize_kernel<D, DT, FMT, PASS, HAD, DUAL, false>), grid, dim3(QUANT_THREADS), 0, s, a);
+    hipLaunchKernelGGL((quantize_kernel<D, DT, FMT, PASS, HAD, DUAL, false, false>), grid, dim3(QUANT_THREADS), 0, s, a);
   return hipGetLastError();
 }
 

@@ -83,8 +83,9 @@ enum { FA4_HADAMARD128 = 1u << 0, FA4_DUAL_RESIDUAL = 1u << 1 }; /* quantizer fl
  * row_norm2 (optional, [outer*heads*rows] float, unpaged only): squared L2 norm of each UNROTATED
  *        input row, float64 pairwise (binary-tree) sum over d, rounded to float32.
  * During the call the tensor-scale array holds intermediate maxima; it holds s_t when the work ends.
- * Requirements: d in {64, 128}; codes, block_scales 4-byte aligned; x aligned to its element size
- * times 4; strides multiples of 4 elements. Returns FA4_ERR_* without enqueuing on a failed check.
+ * Requirements: d in {64, 128}; x and codes 16-byte aligned, block and tensor scales 4-byte aligned;
+ * strides multiples of 16 bytes (8 bf16 or 4 float elements). Returns FA4_ERR_* without enqueuing on
+ * a failed check.
  */
 typedef struct {
   const void *x;               /* input elements (FA4_F32 float or FA4_BF16 bf16 bits)            */

@@ -75,7 +75,9 @@ def test_quantize_rejects_before_launch():
     assert _call_q(_q(), fmt=9) == fa4.FA4_ERR_UNSUPPORTED
     assert _call_q(_q(x=None)) == fa4.FA4_ERR_NULL
     assert _call_q(_q(x=18)) == fa4.FA4_ERR_ALIGN
+    assert _call_q(_q(x=24)) == fa4.FA4_ERR_ALIGN                     # 8-byte aligned is not enough
     assert _call_q(_q(stride_row=130)) == fa4.FA4_ERR_ALIGN
+    assert _call_q(_q(stride_row=132)) == fa4.FA4_ERR_ALIGN          # bf16 rows: multiples of 8 elements
     assert _call_q(_q(), codes=None) == fa4.FA4_ERR_NULL
     assert _call_q(_q(), fmt=fa4.FA4_NVFP4, sc=None) == fa4.FA4_ERR_NULL
     assert _call_q(_q(d=64), flags=fa4.FA4_HADAMARD128) == fa4.FA4_ERR_UNSUPPORTED
