@@ -92,6 +92,17 @@ __device__ __forceinline__ void dma4(const void *g, uint8_t *l) {
 }
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// 8 E2M1 codes (4 bytes, low nibble first) times an E4M3 block scale as exact fp16 values (code * s_b
+// has at most 6 significant bits): hardware fp4 -> fp16 conversion, then one packed multiply.
+__device__ __forceinline__ v8h nv_expand8(uint32_t w, _Float16 sb) {
+  const v2h s2 = {sb, sb};
+  const v2h t0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+  const v2h t1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+  const v2h t2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+  const v2h t3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
+  return (v8h){t0[0], t0[1], t1[0], t1[1], t2[0], t2[1], t3[0], t3[1]};
+}
+
 // Per-lane LDS byte offsets of every operand read of a tile step. All the XOR swizzles depend only on
 // the lane (the tile-varying parts of a key index are multiples of 16 or 32), so each read is
 // base + lane offset + a compile-time immediate and only these few registers stay live.
@@ -462,14 +473,8 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
           const v4i &cc = blk < 2 ? c0 : c1;
           const uint32_t w0 = (uint32_t)cc[2 * (blk & 1)], w1 = (uint32_t)cc[2 * (blk & 1) + 1];
           const _Float16 sb = (_Float16)e4m3_value((sbw >> (8 * blk)) & 0xffu);
-          v8h lo8, hi8;
-#pragma unroll
-          for (int j = 0; j < 8; j++) {
-            lo8[j] = (_Float16)e2m1_value((w0 >> (4 * j)) & 15u) * sb;
-            hi8[j] = (_Float16)e2m1_value((w1 >> (4 * j)) & 15u) * sb;
-          }
-          *reinterpret_cast<v8h *>(k16 + r * H16_RS + 2 * (64 * half + 16 * blk)) = lo8;
-          *reinterpret_cast<v8h *>(k16 + r * H16_RS + 2 * (64 * half + 16 * blk + 8)) = hi8;
+          *reinterpret_cast<v8h *>(k16 + r * H16_RS + 2 * (64 * half + 16 * blk)) = nv_expand8(w0, sb);
+          *reinterpret_cast<v8h *>(k16 + r * H16_RS + 2 * (64 * half + 16 * blk + 8)) = nv_expand8(w1, sb);
         }
         for (int c = tid; c < 128 * (D / 16); c += ATT_THREADS) {
           const int rr = c / (D / 16), j = c % (D / 16);
