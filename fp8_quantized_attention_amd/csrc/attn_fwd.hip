@@ -74,8 +74,13 @@ struct AttnLds {
   static constexpr int QBUF = KC + KS + VC + 512;
   static constexpr int QBYTES = (QF == FA4_MXFP4) ? 2 * QBUF : 0;
   static constexpr int K16 = 128 * H16_RS;
-  static constexpr int V16 = SEL ? 128 * H16_RS : 128 * V8_RS;
-  static constexpr int HBYTES = (QF == FA4_NVFP4 || SEL) ? K16 + V16 + 512 : 0;
+  static constexpr int V8 = 128 * V8_RS;                 // NVFP4 tiles' FP8 V rows
+  static constexpr int V16 = 128 * H16_RS;               // selected tiles' bf16 V rows (overlap V8 onwards)
+  // NVFP4 staging of the next tile's raw data: K codes, K scales, V codes, fold factors
+  static constexpr int NVSTAGE = 128 * (D / 2) + 128 * (D / 16) + 128 * D + 512;
+  static constexpr int NBYTES = (QF == FA4_NVFP4) ? K16 + V8 + 512 + NVSTAGE : 0;
+  static constexpr int SBYTES = SEL ? K16 + V16 : 0;
+  static constexpr int HBYTES = NBYTES > SBYTES ? NBYTES : SBYTES;
   static constexpr int BYTES = QBYTES > HBYTES ? QBYTES : HBYTES;
 };
 template <int D>
@@ -319,7 +324,8 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   uint8_t *const k16 = lds;                              // 16-bit K rows, stride H16_RS
   uint8_t *const v16 = lds + L::K16;                     // bf16 V rows (stride H16_RS) / NVFP4 tiles' FP8 V
-  float *const hsv = reinterpret_cast<float *>(lds + L::K16 + L::V16);   // w_c of NVFP4 tiles
+  float *const hsv = reinterpret_cast<float *>(lds + L::K16 + L::V8);    // w_c of NVFP4 tiles
+  uint8_t *const nst = lds + L::K16 + L::V8 + 512;       // NVFP4 staging: [K codes | K scales | V | w]
 
   const int nq = a.Lq / 128, nk = a.Lk / 128;
   // Work order: one block per (q-tile, batch, head), dispatched longest causal rows first. Blocks are
@@ -459,15 +465,32 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
                     reinterpret_cast<const float *>(base + L::KC + L::KS + L::VC));
     }
   } else {
-    // ---- NVFP4 tiles: K expanded to exact fp16 values in LDS, staged synchronously
-    auto stage_nv = [&](int kt) {
+    // ---- NVFP4 tiles: the next tile's raw codes, scales, V and fold factors are brought into a
+    // staging area by direct global->LDS loads while the current tile is computed; at the start of
+    // each tile K is expanded from there to exact fp16 values and V copied next to it.
+    constexpr int SK = 0, SKS = 128 * (D / 2), SV = SKS + 128 * (D / 16), SW = SV + 128 * D;
+    auto issue_nv = [&](int kt) __attribute__((always_inline)) {
       const int64_t krow0 = bhk * a.Lk + (int64_t)kt * 128;
-      __syncthreads();
+      // K codes 8 KB, V 16 KB: linear 1 KB chunks spread over the 4 waves
+#pragma unroll
+      for (int e = 0; e < 2; e++) {
+        const int i = wave * 2 + e;
+        dma16(a.kc + krow0 * (D / 2) + 1024 * i + 16 * lane, nst + SK + 1024 * i);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int i = wave * 4 + e;
+        dma16(a.vc + krow0 * D + 1024 * i + 16 * lane, nst + SV + 1024 * i);
+      }
+      if (wave == 0) dma16(a.ks + krow0 * (D / 16) + 16 * lane, nst + SKS);
+      if (wave >= 2) dma4(a.vw + krow0 + 64 * (wave - 2) + lane, nst + SW + 256 * (wave - 2));
+    };
+    auto expand_nv = [&]() __attribute__((always_inline)) {
       {
         const int r = tid >> 1, half = tid & 1;
-        const v4i c0 = *reinterpret_cast<const v4i *>(a.kc + (krow0 + r) * 64 + 32 * half);
-        const v4i c1 = *reinterpret_cast<const v4i *>(a.kc + (krow0 + r) * 64 + 32 * half + 16);
-        const uint32_t sbw = *reinterpret_cast<const uint32_t *>(a.ks + (krow0 + r) * 8 + 4 * half);
+        const v4i c0 = *reinterpret_cast<const v4i *>(nst + SK + r * 64 + 32 * half);
+        const v4i c1 = *reinterpret_cast<const v4i *>(nst + SK + r * 64 + 32 * half + 16);
+        const uint32_t sbw = *reinterpret_cast<const uint32_t *>(nst + SKS + r * 8 + 4 * half);
 #pragma unroll
         for (int blk = 0; blk < 4; blk++) {
           const v4i &cc = blk < 2 ? c0 : c1;
@@ -476,22 +499,32 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
           *reinterpret_cast<v8h *>(k16 + r * H16_RS + 2 * (64 * half + 16 * blk)) = nv_expand8(w0, sb);
           *reinterpret_cast<v8h *>(k16 + r * H16_RS + 2 * (64 * half + 16 * blk + 8)) = nv_expand8(w1, sb);
         }
-        for (int c = tid; c < 128 * (D / 16); c += ATT_THREADS) {
-          const int rr = c / (D / 16), j = c % (D / 16);
-          *reinterpret_cast<v4i *>(v16 + rr * V8_RS + 16 * j) =
-              *reinterpret_cast<const v4i *>(a.vc + (krow0 + rr) * D + 16 * j);
-        }
-        if (tid < 128) hsv[tid] = a.vw[krow0 + tid];
       }
-      __syncthreads();
+#pragma unroll
+      for (int c = tid; c < 128 * (D / 16); c += ATT_THREADS) {
+        const int rr = c / (D / 16), j = c % (D / 16);
+        *reinterpret_cast<v4i *>(v16 + rr * V8_RS + 16 * j) = *reinterpret_cast<const v4i *>(nst + SV + rr * D + 16 * j);
+      }
+      if (tid < 128) hsv[tid] = reinterpret_cast<const float *>(nst + SW)[tid];
     };
     int kt = next_quant(0);
-    for (; kt < (CAUSAL ? last : kt_end); kt = next_quant(kt + 1)) {
-      stage_nv(kt);
+    if (kt < kt_end) issue_nv(kt);
+    const int stop = CAUSAL ? last : kt_end;   // the diagonal tile is peeled below
+    while (kt < stop) {
+      const int nxt = next_quant(kt + 1);
+      wait_vmem();
+      __syncthreads();                   // staging holds tile kt; the previous tile's K/V are consumed
+      expand_nv();
+      __syncthreads();                   // K/V of tile kt ready; the staging area is free
+      if (nxt < kt_end) issue_nv(nxt);   // in flight during this tile's compute
       FA4_TILE_STEP(false, false, kt, nullptr, nullptr, v16, hsv);
+      kt = nxt;
     }
     if (CAUSAL && kt == last) {
-      stage_nv(kt);
+      wait_vmem();
+      __syncthreads();
+      expand_nv();
+      __syncthreads();
       FA4_TILE_STEP(true, false, kt, nullptr, nullptr, v16, hsv);
     }
   }
