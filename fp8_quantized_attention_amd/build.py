@@ -16,6 +16,8 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # hand-written kernels only; no packed fp32 instructions (see the notes on the target)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs (no AGPR copies around the decode kernel's MFMAs)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     # IEEE float division (the quantizers' rounding depends on it)
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math",
     "-Wall", "-Wno-unused-result", "-Wno-unused-variable",

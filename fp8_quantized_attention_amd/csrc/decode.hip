@@ -90,14 +90,20 @@ __device__ __forceinline__ void transpose8x8_nibbles(uint32_t w[8]) {
   }
 }
 
-// The two 64-key pages of a tile: base pointers of this key head's rows and whether the page holds
-// keys (within the context, id inside the cache). Everything here is wave-uniform; a page without
-// keys points at page 0 (always present), is read like the others and its values are replaced by
-// zeros, so no load sits behind a branch.
+// The two 64-key pages of a tile as buffer resources over this key head's rows of each page (codes
+// 4 KB, scales 512 B per array). A page without keys (past the context, or an id outside the cache)
+// gets a zero-size resource: buffer loads past a resource's size return zeros, so its keys read as
+// zeros and no load sits behind a branch. All of it is wave-uniform (scalar registers); the loads
+// then carry only a 32-bit per-lane offset.
+constexpr int BUF_DWORD3 = 0x00020000;      // raw (untyped) buffer access on gfx9-family targets
+
 struct TilePages {
-  const uint8_t *kc[2], *ks[2], *vc[2], *vs[2];
-  bool ok[2];
+  __amdgpu_buffer_rsrc_t kc[2], ks[2], vc[2], vs[2];
 };
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint8_t *base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), 0, bytes, BUF_DWORD3);
+}
 
 __device__ __forceinline__ TilePages tile_pages(const DecArgs &a, const int32_t *pt, int kvh, int t0, int L) {
   TilePages tp;
@@ -107,25 +113,23 @@ __device__ __forceinline__ TilePages tile_pages(const DecArgs &a, const int32_t 
     const int pg = __builtin_amdgcn_readfirstlane(pt[pid]);
     const bool ok = t0 + 64 * p < L && pg >= 0 && (int64_t)pg < a.num_pages;
     const int64_t row0 = ((int64_t)(ok ? pg : 0) * a.Hkv + kvh) * 64;
-    tp.kc[p] = a.kc + row0 * 64;
-    tp.ks[p] = a.ks + row0 * 8;
-    tp.vc[p] = a.vc + row0 * 64;
-    tp.vs[p] = a.vs + row0 * 8;
-    tp.ok[p] = ok;
+    tp.kc[p] = page_rsrc(a.kc + row0 * 64, ok ? 4096 : 0);
+    tp.ks[p] = page_rsrc(a.ks + row0 * 8, ok ? 512 : 0);
+    tp.vc[p] = page_rsrc(a.vc + row0 * 64, ok ? 4096 : 0);
+    tp.vs[p] = page_rsrc(a.vs + row0 * 8, ok ? 512 : 0);
   }
   return tp;
 }
 
 // K of a tile for the QK A operand: block kb (16 keys), lane (g, n) -> key 16 kb + n, codes bytes
-// 16 g .. 16 g + 15 (d = 32 g .. 32 g + 31) and the two block scales of those 32 values (a page
-// without keys gets zero scales, so its values are zeros).
+// 16 g .. 16 g + 15 (d = 32 g .. 32 g + 31) and the two block scales of those 32 values.
 __device__ __forceinline__ void load_k(const TilePages &tp, int n, int g, v4i kc[8], uint32_t ks[8]) {
+  const int vo_c = n * 64 + 16 * g, vo_s = n * 8 + 2 * g;   // per-lane offsets; the rest is scalar
 #pragma unroll
   for (int kb = 0; kb < 8; kb++) {
-    const int p = kb >> 2, row = 16 * (kb & 3) + n;
-    kc[kb] = *reinterpret_cast<const v4i *>(tp.kc[p] + row * 64 + 16 * g);
-    const uint32_t sc = *reinterpret_cast<const uint16_t *>(tp.ks[p] + row * 8 + 2 * g);
-    ks[kb] = tp.ok[p] ? sc : 0u;
+    const int p = kb >> 2, r0 = 16 * (kb & 3);
+    kc[kb] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(tp.kc[p], vo_c, r0 * 64, 0));
+    ks[kb] = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(tp.ks[p], vo_s, r0 * 8, 0);
   }
 }
 
@@ -135,16 +139,16 @@ __device__ __forceinline__ void load_k(const TilePages &tp, int n, int g, v4i kc
 // blocks 4 (L % 2) .. 4 (L % 2) + 3) and redistributed with lane shuffles when the quarter is used.
 __device__ __forceinline__ void load_v(const TilePages &tp, int lane, int n, int g, uint32_t vc[4][8],
                                        uint32_t vs[4]) {
+  const int vo_c = 4 * g * 64 + 4 * n;                    // per-lane offsets; the rest is scalar
 #pragma unroll
   for (int q = 0; q < 4; q++) {
     const int p = q >> 1;
 #pragma unroll
     for (int j = 0; j < 8; j++) {
-      const int row = 32 * (q & 1) + 16 * (j >> 2) + 4 * g + (j & 3);
-      vc[q][j] = *reinterpret_cast<const uint32_t *>(tp.vc[p] + row * 64 + 4 * n);
+      const int r0 = 32 * (q & 1) + 16 * (j >> 2) + (j & 3);
+      vc[q][j] = __builtin_amdgcn_raw_buffer_load_b32(tp.vc[p], vo_c, r0 * 64, 0);
     }
-    const uint32_t w = *reinterpret_cast<const uint32_t *>(tp.vs[p] + 256 * (q & 1) + 4 * lane);
-    vs[q] = tp.ok[p] ? w : 0u;
+    vs[q] = __builtin_amdgcn_raw_buffer_load_b32(tp.vs[p], 4 * lane, 256 * (q & 1), 0);
   }
 }
 
