@@ -214,15 +214,6 @@ __device__ __forceinline__ void tile_step(const AttnArgs &a, const LaneOff &lo, 
     for (int i = 0; i < 16; i++) mS = fmaxf(mS, S[kb][i]);
   mS = fmaxf(mS, shfl_xor_f(mS, 32));
   const float r = ceilf(mS * cs);
-  float tsum = 0.0f;
-#pragma unroll
-  for (int kb = 0; kb < 4; kb++)
-#pragma unroll
-    for (int i = 0; i < 16; i++) {
-      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][i], cs, -r));
-      S[kb][i] = p;
-      tsum += p;
-    }
   // Running reference m (log2 units, an integer): raised only when a tile's reference exceeds it by
   // more than ACC_HEADROOM, so the accumulator and the sum (tile weights up to 2^ACC_HEADROOM) stay far
   // from overflow; raising rescales both by an exact power of two.
@@ -235,69 +226,72 @@ __device__ __forceinline__ void tile_step(const AttnArgs &a, const LaneOff &lo, 
     m = m_new;
   }
   int kB = (int)fmaxf(r - m, -255.0f);         // tile weight 2^kB, kB <= ACC_HEADROOM
-  lsum += __builtin_ldexpf(tsum, kB);
-  if (__builtin_amdgcn_ballot_w64(kB < -127) != 0) {
-    // a weight below 2^-127 (the smallest E8M0 scale) of the reference adds nothing representable:
-    // those rows' probabilities are zeroed so that the clamped scale does not inflate them
-#pragma unroll
-    for (int kb = 0; kb < 4; kb++)
-#pragma unroll
-      for (int i = 0; i < 16; i++) S[kb][i] = kB < -127 ? 0.0f : S[kb][i];
-    kB = kB < -127 ? -127 : kB;
-  }
+  // A weight below 2^-127 (the smallest E8M0 scale) of the reference adds nothing representable:
+  // those rows take an infinite reference, so that their probabilities are exactly zero and the
+  // clamped scale does not inflate them.
+  const float rr0 = kB < -127 ? INFINITY : r;
+  float tsum = 0.0f;
 
-  if (!sel) {
-    // P^ = E4M3(P' w_c) with w_c = s_v[c] 2^-e (exact); the tile's 2^e rides on V's operand scale
-#pragma unroll
-    for (int kb = 0; kb < 4; kb++)
-#pragma unroll
-      for (int a4 = 0; a4 < 4; a4++) {
-        const float4 w4 = *reinterpret_cast<const float4 *>(reinterpret_cast<const uint8_t *>(svs) + lo.w +
-                                                            4 * (32 * kb + 8 * a4));
-        S[kb][4 * a4 + 0] *= w4.x;
-        S[kb][4 * a4 + 1] *= w4.y;
-        S[kb][4 * a4 + 2] *= w4.z;
-        S[kb][4 * a4 + 3] *= w4.w;
-      }
-  }
-
-  // ---- O^T += V^T P^T
+  // ---- P' = 2^(S cs - r) per element, straight into the operand it feeds (S and P are never both
+  // held whole); then O^T += V^T P^T
   if (sel) {
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][i], cs, -rr0));
+        tsum += p;
+        S[kb][i] = p;
+      }
+    const int kBc = kB < -127 ? -127 : kB;
 #pragma unroll
     for (int kb = 0; kb < 4; kb++)
 #pragma unroll
       for (int p = 0; p < 2; p++) {
         v8s pbs;
 #pragma unroll
-        for (int j = 0; j < 8; j++) pbs[j] = (short)float_to_bf16_bits(__builtin_ldexpf(S[kb][8 * p + j], kB));
+        for (int j = 0; j < 8; j++) pbs[j] = (short)float_to_bf16_bits(__builtin_ldexpf(S[kb][8 * p + j], kBc));
         const v8bf pb = __builtin_bit_cast(v8bf, pbs);
 #pragma unroll
         for (int mb = 0; mb < NDB; mb++) {
-          v4s r[2];
+          v4s rr[2];
 #pragma unroll
           for (int v = 0; v < 2; v++)   // source lane (16q + a + 4t): key 32kb + 16p + 8v + 4g + t, d 32mb + 16(q%2) + 4a
-            r[v] = lds_tr16(v16 + lo.v16 + (32 * kb + 16 * p + 8 * v) * H16_RS + 64 * mb);
+            rr[v] = lds_tr16(v16 + lo.v16 + (32 * kb + 16 * p + 8 * v) * H16_RS + 64 * mb);
           // whole-vector reinterpretation (inserting bit-cast elements one at a time miscompiles)
-          const v8bf vop = __builtin_bit_cast(v8bf, (v8s)__builtin_shufflevector(r[0], r[1], 0, 1, 2, 3, 4, 5, 6, 7));
+          const v8bf vop = __builtin_bit_cast(v8bf, (v8s)__builtin_shufflevector(rr[0], rr[1], 0, 1, 2, 3, 4, 5, 6, 7));
           acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb, acc[mb], 0, 0, 0);
         }
       }
   } else {
-    // E8M0 code of the tile's power-of-two scale 2^e (stored as a float; 2^-127 is the subnormal whose
-    // exponent field is 0, matching E8M0 code 0)
+    // P^ = E4M3(P' w_c) with w_c = s_v[c] 2^-e (exact), packed into the PV B operand
+    v8i pop[2];
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; a4++) {
+        const float4 w4 = *reinterpret_cast<const float4 *>(reinterpret_cast<const uint8_t *>(svs) + lo.w +
+                                                            4 * (32 * kb + 8 * a4));
+        const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
+        float pw[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][4 * a4 + u], cs, -rr0));
+          tsum += p;
+          pw[u] = p * wv[u];
+        }
+        // the first conversion keeps the register's high half, which the second one then writes:
+        // starting from the bits of its own (dead) first input avoids materializing a zero
+        int x = __builtin_amdgcn_cvt_pk_fp8_f32(pw[0], pw[1], __float_as_int(pw[0]), false);
+        x = __builtin_amdgcn_cvt_pk_fp8_f32(pw[2], pw[3], x, true);
+        pop[kb >> 1][4 * (kb & 1) + a4] = x;
+      }
+    const int kBc = kB < -127 ? -127 : kB;
+    // E8M0 code of the tile's power-of-two V scale 2^e (stored as a float; 2^-127 is the subnormal
+    // whose exponent field is 0, matching E8M0 code 0)
     const int scA = (int)((__float_as_uint(a.vfs[bhk * nk + kt]) >> 23) & 0xffu);
 #pragma unroll
     for (int t = 0; t < 2; t++) {
-      v8i pop;
-#pragma unroll
-      for (int half = 0; half < 2; half++)
-#pragma unroll
-        for (int w = 0; w < 4; w++) {
-          const v16f &sv = S[2 * t + half];
-          int x = __builtin_amdgcn_cvt_pk_fp8_f32(sv[4 * w], sv[4 * w + 1], __builtin_nondeterministic_value(0), false);
-          x = __builtin_amdgcn_cvt_pk_fp8_f32(sv[4 * w + 2], sv[4 * w + 3], x, true);
-          pop[4 * half + w] = x;
-        }
 #pragma unroll
       for (int mb = 0; mb < NDB; mb++) {
         v8i vop;
@@ -306,15 +300,16 @@ __device__ __forceinline__ void tile_step(const AttnArgs &a, const LaneOff &lo, 
           // source lane (16q + a + 2t'): key 64t + 32(u/2) + 16(u%2) + 8(t'/4) + 4g + t'%4,
           //                              d 32mb + 16(q%2) + 8a
           const int krun = 64 * t + 32 * (u >> 1) + 16 * (u & 1);
-          const v2i r = QF == FA4_MXFP4 ? lds_tr8(vq + lo.v[mb] + krun * D)
-                                        : lds_tr8(vq + lo.v8 + krun * V8_RS + 32 * mb);
-          vop[2 * u] = r[0];
-          vop[2 * u + 1] = r[1];
+          const v2i rr = QF == FA4_MXFP4 ? lds_tr8(vq + lo.v[mb] + krun * D)
+                                         : lds_tr8(vq + lo.v8 + krun * V8_RS + 32 * mb);
+          vop[2 * u] = rr[0];
+          vop[2 * u + 1] = rr[1];
         }
-        acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, pop, acc[mb], 0, 0, 0, scA, 0, kB + 127);
+        acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, pop[t], acc[mb], 0, 0, 0, scA, 0, kBc + 127);
       }
     }
   }
+  lsum += __builtin_ldexpf(tsum, kB);
 }
 
 template <int D, int QF, bool CAUSAL, bool SEL>
