@@ -207,11 +207,15 @@ __device__ __forceinline__ void tile_step(const AttnArgs &a, const LaneOff &lo, 
   }
   // The tile's row reference in log2 units is the smallest integer r >= its largest score, and
   // P' = 2^(S cs - r) <= 1 (its largest value lies in (1/2, 1]).
-  float mS = -INFINITY;
+  // (max and sum run over independent partial results, so no long dependent chain forms)
+  float mp[4];
 #pragma unroll
-  for (int kb = 0; kb < 4; kb++)
+  for (int kb = 0; kb < 4; kb++) {
+    mp[kb] = S[kb][0];
 #pragma unroll
-    for (int i = 0; i < 16; i++) mS = fmaxf(mS, S[kb][i]);
+    for (int i = 1; i < 16; i++) mp[kb] = fmaxf(mp[kb], S[kb][i]);
+  }
+  float mS = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
   mS = fmaxf(mS, shfl_xor_f(mS, 32));
   const float r = ceilf(mS * cs);
   // Running reference m (log2 units, an integer): raised only when a tile's reference exceeds it by
@@ -230,7 +234,7 @@ __device__ __forceinline__ void tile_step(const AttnArgs &a, const LaneOff &lo, 
   // those rows take an infinite reference, so that their probabilities are exactly zero and the
   // clamped scale does not inflate them.
   const float rr0 = kB < -127 ? INFINITY : r;
-  float tsum = 0.0f;
+  float ts[4] = {0.0f, 0.0f, 0.0f, 0.0f};        // partial sums, one per 16-key group
 
   // ---- P' = 2^(S cs - r) per element, straight into the operand it feeds (S and P are never both
   // held whole); then O^T += V^T P^T
@@ -240,7 +244,7 @@ __device__ __forceinline__ void tile_step(const AttnArgs &a, const LaneOff &lo, 
 #pragma unroll
       for (int i = 0; i < 16; i++) {
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][i], cs, -rr0));
-        tsum += p;
+        ts[kb] += p;
         S[kb][i] = p;
       }
     const int kBc = kB < -127 ? -127 : kB;
@@ -277,7 +281,7 @@ __device__ __forceinline__ void tile_step(const AttnArgs &a, const LaneOff &lo, 
 #pragma unroll
         for (int u = 0; u < 4; u++) {
           const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][4 * a4 + u], cs, -rr0));
-          tsum += p;
+          ts[kb] += p;
           pw[u] = p * wv[u];
         }
         // the first conversion keeps the register's high half, which the second one then writes:
@@ -309,7 +313,7 @@ __device__ __forceinline__ void tile_step(const AttnArgs &a, const LaneOff &lo, 
       }
     }
   }
-  lsum += __builtin_ldexpf(tsum, kB);
+  lsum += __builtin_ldexpf((ts[0] + ts[1]) + (ts[2] + ts[3]), kB);
 }
 
 template <int D, int QF, bool CAUSAL, bool SEL>
