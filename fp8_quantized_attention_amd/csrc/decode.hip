@@ -226,7 +226,7 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_split_kernel(DecArgs a) {
     load_k(tp, n, g, kc, ks);
     load_v(tp, lane, n, g, vc, vs);
   }
-#pragma unroll 1
+#pragma unroll
   for (int it = 0; it < DEC_TPW; it++) {
     const int t0 = tbase + 512 * it;
     const int slot = 4 * it + wave;
