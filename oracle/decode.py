@@ -1,4 +1,4 @@
-"""Decode attention of the oracle over a paged NVFP4 KV cache with a dual-residual query.
+"""Decode attention of the oracle over a paged FP4 KV cache (NVFP4 or MXFP4) with a dual-residual query.
 
 TEST INFRASTRUCTURE: only the tests, the smoke check and the benchmark's
 CPU-baseline leg may use this module. Shares no code with the GPU path.
@@ -12,18 +12,23 @@ query heads sharing one key head (GQA) are processed together. "MpFA QK4V8"
 
 Computation per (batch b, query head h), key head kv = h // (Hq/Hkv), keys
 c in [0, L_b) (the query attends to every cached token), scale = 1/sqrt(d):
-  q^ = dequant(Q1) + dequant(Q2) (float64); k^, v^ = NVFP4-dequantized cache rows;
+  q^ = dequant(Q1) + dequant(Q2) (float64); k^, v^ = dequantized cache rows;
   S_c = scale * q^ . k^_c; tiles of 128 keys from position 0 (the last may be partial);
   per tile: m~ = max S_c, P'_c = exp(S_c - m~), P^_c = E4M3(448 P'_c),
   T = (1/448) sum_c P^_c v^_c;
   m = max m~, D = sum e^(m~ - m) sum P', N = sum e^(m~ - m) T, O = N / D (float32).
 The page table maps logical page p of sequence b (tokens 64p .. 64p+63) to a
 physical page; a physical page holds [Hkv][64][...] rows.
+
+Formats of the cache (the page reports both): NVFP4 (E4M3 scale per 16
+elements along d and an FP32 tensor scale per (sequence, key head)) or MXFP4
+(E8M0 scale per 32 elements along d, no tensor scale). The query residuals take
+the cache's format. The probability steps are the same for both.
 """
 import numpy as np
 
 from .formats import E4M3_MAX, e4m3_decode, e4m3_encode, fp32
-from .quant import nvfp4_dequantize
+from .quant import mxfp4_dequantize, nvfp4_dequantize
 
 TILE = 128
 
@@ -62,26 +67,30 @@ def decode_one(q_hat, k_hat, v_hat, scale, chunk=None, round_p=True):
     return N / D
 
 
-def dequant_query(q1, q2):
-    """q^ = dequant(Q1) + dequant(Q2) for NVFP4 pairs ((codes, sb, st) with groups = rows)."""
-    return nvfp4_dequantize(*q1) + nvfp4_dequantize(*q2)
+def dequant_query(q1, q2, fmt="nvfp4"):
+    """q^ = dequant(Q1) + dequant(Q2): NVFP4 pairs (codes, sb, st) or MXFP4 pairs (codes, E8M0)."""
+    deq = nvfp4_dequantize if fmt == "nvfp4" else mxfp4_dequantize
+    return deq(*q1) + deq(*q2)
 
 
 def decode_paged(q1, q2, k_pages, v_pages, k_tscale, v_tscale, page_table, ctx_len,
-                 Hq, Hkv, page_size=64, scale=None, pairs=None, chunk=None, round_p=True):
+                 Hq, Hkv, page_size=64, scale=None, pairs=None, chunk=None, round_p=True, fmt="nvfp4"):
     """O9 through the page table.
 
-    q1, q2: (codes [B*Hq, 1, d/2], block scales [B*Hq, 1, d/16], tensor scales [B*Hq]).
-    k_pages / v_pages: (codes [P, Hkv, page_size, d/2], block scales [P, Hkv, page_size, d/16]).
-    k_tscale / v_tscale: [B, Hkv] float32. Returns O float32 [B, Hq, d]; pairs (optional)
-    restricts the computed (b, h) pairs, the rest stay zero.
+    fmt "nvfp4": q1, q2 = (codes [B*Hq, 1, d/2], block scales [B*Hq, 1, d/16], tensor scales
+    [B*Hq]); k_pages / v_pages = (codes [P, Hkv, page_size, d/2], block scales [P, Hkv,
+    page_size, d/16]); k_tscale / v_tscale [B, Hkv] float32.
+    fmt "mxfp4": q1, q2 = (codes, E8M0 scales [B*Hq, 1, d/32]); pages hold E8M0 scales
+    [P, Hkv, page_size, d/32]; the tensor-scale arguments are unused.
+    Returns O float32 [B, Hq, d]; pairs (optional) restricts the computed (b, h) pairs, the rest
+    stay zero.
     """
     B = len(ctx_len)
     d = 2 * q1[0].shape[-1]
     if scale is None:
         scale = 1.0 / np.sqrt(d)
     group = Hq // Hkv
-    qhat = dequant_query(q1, q2).reshape(B, Hq, d)
+    qhat = dequant_query(q1, q2, fmt).reshape(B, Hq, d)
     O = np.zeros((B, Hq, d), dtype=np.float32)
     pairs = [(b, h) for b in range(B) for h in range(Hq)] if pairs is None else pairs
     cache = {}
@@ -93,8 +102,12 @@ def decode_paged(q1, q2, k_pages, v_pages, k_tscale, v_tscale, page_table, ctx_l
             ks = gather_pages(k_pages[1], page_table[b], L, page_size, kv)
             vc = gather_pages(v_pages[0], page_table[b], L, page_size, kv)
             vs = gather_pages(v_pages[1], page_table[b], L, page_size, kv)
-            k_hat = nvfp4_dequantize(kc[None], ks[None], np.array([k_tscale[b, kv]]))[0]
-            v_hat = nvfp4_dequantize(vc[None], vs[None], np.array([v_tscale[b, kv]]))[0]
+            if fmt == "nvfp4":
+                k_hat = nvfp4_dequantize(kc[None], ks[None], np.array([k_tscale[b, kv]]))[0]
+                v_hat = nvfp4_dequantize(vc[None], vs[None], np.array([v_tscale[b, kv]]))[0]
+            else:
+                k_hat = mxfp4_dequantize(kc, ks)
+                v_hat = mxfp4_dequantize(vc, vs)
             cache = {(b, kv): (k_hat, v_hat)}
         k_hat, v_hat = cache[(b, kv)]
         O[b, h] = fp32(decode_one(qhat[b, h], k_hat, v_hat, scale, chunk=chunk, round_p=round_p))

@@ -139,6 +139,20 @@ def dual_residual_quantize(q):
     return (c1, sb1, st1), (c2, sb2, st2)
 
 
+def dual_residual_quantize_mx(q):
+    """q ~ Q1 + Q2 with both MXFP4: Q1 = MXFP4(q), r = fl32(q - dequant(Q1)), Q2 = MXFP4(r).
+
+    The query of an MXFP4 KV cache ("BitDecoding-FP4": the query is split into two FP4 tensors of
+    the cache's format, the second carrying the first one's residual). No tensor scales.
+    Returns ((codes1, scales1), (codes2, scales2)).
+    """
+    q32 = fp32(q).astype(np.float64)
+    c1, s1 = mxfp4_quantize(q32)
+    r = fp32(q32 - mxfp4_dequantize(c1, s1)).astype(np.float64)
+    c2, s2 = mxfp4_quantize(r)
+    return (c1, s1), (c2, s2)
+
+
 # ----------------------------------------------------------------------------- FP8 V per token
 
 def fp8_per_token_quantize(v):

@@ -1,5 +1,6 @@
 """Pins of the oracle's paged decode: paging, split and GQA invariances, SDPA limit, brute force."""
 import numpy as np
+import pytest
 import torch
 
 import bruteforce as bf
@@ -10,12 +11,13 @@ from oracle import quant as Q
 SMALL = W.C3.scaled(B=3, Hq=8, Hkv=2, ctx_lo=200, ctx_hi=700)
 
 
-def build_cache(cfg, seed=0):
+def build_cache(cfg, seed=0, fmt="nvfp4"):
     """Quantize K and V per (sequence, key head) and scatter rows into pages through the page table."""
     lay = W.decode_layout(cfg, seed)
     d, ps = cfg.d, cfg.page_size
     P = lay.num_pages
-    kc = np.zeros((P, cfg.Hkv, ps, d // 2), np.uint8); ks = np.zeros((P, cfg.Hkv, ps, d // 16), np.uint8)
+    blk = 16 if fmt == "nvfp4" else 32
+    kc = np.zeros((P, cfg.Hkv, ps, d // 2), np.uint8); ks = np.zeros((P, cfg.Hkv, ps, d // blk), np.uint8)
     vc = np.zeros_like(kc); vs = np.zeros_like(ks)
     kt = np.zeros((cfg.B, cfg.Hkv), np.float32); vt = np.zeros_like(kt)
     logical = {}
@@ -26,23 +28,35 @@ def build_cache(cfg, seed=0):
         for h in range(cfg.Hkv):
             for tensor, (codes, scales, ts) in [(W.T_K, (kc, ks, kt)), (W.T_V, (vc, vs, vt))]:
                 x = W.decode_kv_head(cfg, tensor, b, h, L, seed).double().numpy()
-                qc, qs, qt = Q.nvfp4_quantize(x[None])
-                codes[phys, h, c % ps] = qc[0]
-                scales[phys, h, c % ps] = qs[0]
-                ts[b, h] = qt[0]
-                logical[(tensor, b, h)] = (x, Q.nvfp4_dequantize(qc, qs, qt)[0])
+                if fmt == "nvfp4":
+                    qc, qs, qt = Q.nvfp4_quantize(x[None])
+                    codes[phys, h, c % ps] = qc[0]
+                    scales[phys, h, c % ps] = qs[0]
+                    ts[b, h] = qt[0]
+                    logical[(tensor, b, h)] = (x, Q.nvfp4_dequantize(qc, qs, qt)[0])
+                else:
+                    qc, qs = Q.mxfp4_quantize(x)
+                    codes[phys, h, c % ps] = qc
+                    scales[phys, h, c % ps] = qs
+                    logical[(tensor, b, h)] = (x, Q.mxfp4_dequantize(qc, qs))
     q = W.decode_query(cfg, seed).double().numpy()
-    q1, q2 = Q.dual_residual_quantize(q.reshape(cfg.B * cfg.Hq, 1, d))
+    rows = q.reshape(cfg.B * cfg.Hq, 1, d)
+    q1, q2 = Q.dual_residual_quantize(rows) if fmt == "nvfp4" else Q.dual_residual_quantize_mx(rows)
     return lay, (kc, ks), (vc, vs), kt, vt, q, q1, q2, logical
 
 
-def test_paged_equals_contiguous_and_sdpa_limit():
+FMTS = pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+
+
+@FMTS
+def test_paged_equals_contiguous_and_sdpa_limit(fmt):
     cfg = SMALL
-    lay, kp, vp, kt, vt, q, q1, q2, logical = build_cache(cfg)
-    O = Dd.decode_paged(q1, q2, kp, vp, kt, vt, lay.page_table.numpy(), lay.ctx_len.numpy(), cfg.Hq, cfg.Hkv)
+    lay, kp, vp, kt, vt, q, q1, q2, logical = build_cache(cfg, fmt=fmt)
+    O = Dd.decode_paged(q1, q2, kp, vp, kt, vt, lay.page_table.numpy(), lay.ctx_len.numpy(), cfg.Hq, cfg.Hkv,
+                        fmt=fmt)
     On = Dd.decode_paged(q1, q2, kp, vp, kt, vt, lay.page_table.numpy(), lay.ctx_len.numpy(), cfg.Hq, cfg.Hkv,
-                         round_p=False)
-    qhat = Dd.dequant_query(q1, q2).reshape(cfg.B, cfg.Hq, cfg.d)
+                         round_p=False, fmt=fmt)
+    qhat = Dd.dequant_query(q1, q2, fmt).reshape(cfg.B, cfg.Hq, cfg.d)
     g = cfg.Hq // cfg.Hkv
     for b in range(cfg.B):
         for h in range(cfg.Hq):
@@ -58,15 +72,46 @@ def test_paged_equals_contiguous_and_sdpa_limit():
             assert np.abs(On[b, h] - sd).max() <= 1e-6 * np.abs(sd).max()
 
 
-def test_split_merge_equals_single_pass():
+@FMTS
+def test_split_merge_equals_single_pass(fmt):
     cfg = SMALL
-    lay, kp, vp, kt, vt, q, q1, q2, logical = build_cache(cfg)
-    qhat = Dd.dequant_query(q1, q2).reshape(cfg.B, cfg.Hq, cfg.d)
+    lay, kp, vp, kt, vt, q, q1, q2, logical = build_cache(cfg, fmt=fmt)
+    qhat = Dd.dequant_query(q1, q2, fmt).reshape(cfg.B, cfg.Hq, cfg.d)
     kh = logical[(W.T_K, 1, 0)][1]; vh = logical[(W.T_V, 1, 0)][1]
     one = Dd.decode_one(qhat[1, 2], kh, vh, 0.1)
     for chunk in [128, 256, 384]:
         sp = Dd.decode_one(qhat[1, 2], kh, vh, 0.1, chunk=chunk)
         assert np.abs(sp - one).max() <= 1e-12 * np.abs(one).max()
+
+
+def _bf_codes(packed_row):
+    return [int(x) for pair in packed_row for x in (pair & 15, pair >> 4)]
+
+
+def test_bruteforce_decode_mxfp4():
+    """MXFP4 cache and query residuals re-derived by the brute-force loops, then attended by loops."""
+    cfg = SMALL.scaled(B=1, ctx_lo=300, ctx_hi=300)
+    lay, kp, vp, kt, vt, q, q1, q2, logical = build_cache(cfg, fmt="mxfp4")
+    O = Dd.decode_paged(q1, q2, kp, vp, kt, vt, lay.page_table.numpy(), lay.ctx_len.numpy(), cfg.Hq, cfg.Hkv,
+                        pairs=[(0, 1), (0, 6)], fmt="mxfp4")
+    for h in [1, 6]:
+        row = [float(v) for v in q[0, h]]
+        c1, s1 = bf.mxfp4_row(row)
+        assert c1 == _bf_codes(q1[0][h, 0]) and s1 == q1[1][h, 0].tolist()
+        x1 = bf.mxfp4_row_values(c1, s1)
+        r = [bf.f32(a - b) for a, b in zip(row, x1)]
+        c2, s2 = bf.mxfp4_row(r)
+        assert c2 == _bf_codes(q2[0][h, 0]) and s2 == q2[1][h, 0].tolist()
+        qv = [a + b for a, b in zip(x1, bf.mxfp4_row_values(c2, s2))]
+        kvh = h // 4
+        K, V = [], []
+        for tensor, dst in [(W.T_K, K), (W.T_V, V)]:
+            x = logical[(tensor, 0, kvh)][0]
+            for t in range(x.shape[0]):
+                c, sc = bf.mxfp4_row([float(v) for v in x[t]])
+                dst.append(bf.mxfp4_row_values(c, sc))
+        ref = bf.decode_row(qv, K, V, 1 / np.sqrt(cfg.d))
+        assert np.abs(O[0, h] - np.array(ref)).max() <= 1e-6 * np.abs(ref).max()
 
 
 def test_bruteforce_decode():
@@ -86,11 +131,12 @@ def test_bruteforce_decode():
         assert np.abs(O[0, h] - np.array(ref)).max() <= 1e-6 * np.abs(ref).max()
 
 
-def test_dual_residual_query_cuts_logit_error():
+@FMTS
+def test_dual_residual_query_cuts_logit_error(fmt):
     cfg = SMALL
-    lay, kp, vp, kt, vt, q, q1, q2, logical = build_cache(cfg)
-    x1 = Q.nvfp4_dequantize(*q1).reshape(cfg.B, cfg.Hq, cfg.d)
-    x12 = Dd.dequant_query(q1, q2).reshape(cfg.B, cfg.Hq, cfg.d)
+    lay, kp, vp, kt, vt, q, q1, q2, logical = build_cache(cfg, fmt=fmt)
+    x1 = (Q.nvfp4_dequantize if fmt == "nvfp4" else Q.mxfp4_dequantize)(*q1).reshape(cfg.B, cfg.Hq, cfg.d)
+    x12 = Dd.dequant_query(q1, q2, fmt).reshape(cfg.B, cfg.Hq, cfg.d)
     kh = logical[(W.T_K, 0, 0)][1]
     l0 = kh @ q[0, 0]
     e1 = np.linalg.norm(kh @ x1[0, 0] - l0) / np.linalg.norm(l0)
