@@ -9,6 +9,7 @@ attention kernel, inputs resident in HBM. `value` is prefill attention TFLOP/s o
                 events on the launch stream) against the dense MXFP4 MFMA peak;
   decode        the paged NVFP4 decode step (64 sequences, 32 -> 8 GQA heads, contexts 8K-32K):
                 KV-cache GB/s, and the decode kernels' HBM roofline;
+  decode_mxfp4  the same decode step over an MXFP4 cache (same sequences and values);
   cpu_baseline  the CPU oracle (float64 numpy) on a bounded sample of the same workload.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-decode] [--no-cpu-baseline]
                        [--copy-probe] [--summarize-counters DIR]
@@ -45,9 +46,11 @@ COPY_BYTES = 1 << 30                 # calibration copy: reads and writes this m
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "fp8_quantized_attention_amd", "csrc")
 # sources whose change invalidates a kernel's recorded counters
+# (template argument of the decode kernel: 1 = NVFP4 cache, 0 = MXFP4 cache)
 KERNEL_SOURCES = {
     "attn_fwd_kernel": ["attn_fwd.hip", "fa4_device.h"],
-    "decode_split_kernel": ["decode.hip", "fa4_device.h"],
+    "decode_split_kernel<1>": ["decode.hip", "fa4_device.h"],
+    "decode_split_kernel<0>": ["decode.hip", "fa4_device.h"],
 }
 
 
@@ -151,10 +154,11 @@ def time_prefill(fa4, cfg, steps, warmup, select):
 def time_decode(fa4, cfg, steps, warmup):
     lay = W.decode_layout(cfg)
     ctx, pt = lay.ctx_len.cuda(), lay.page_table.cuda()
+    nv = cfg.kv_fmt == "nvfp4"
     caches = []
     for tensor in (W.T_K, W.T_V):
         x = W.decode_kv_padded(cfg, lay, tensor, device="cuda")
-        caches.append(fa4.quantize_paged(x, fa4.FA4_NVFP4, ctx, pt, lay.num_pages))
+        caches.append(fa4.quantize_paged(x, fa4.FA4_NVFP4 if nv else fa4.FA4_MXFP4, ctx, pt, lay.num_pages))
         del x
     torch.cuda.empty_cache()
     q = W.decode_query(cfg).cuda()
@@ -163,7 +167,8 @@ def time_decode(fa4, cfg, steps, warmup):
         run.run()
     step_ms = _time_loop(run.run, steps)
     kern_ms = _time_loop(run.attention, steps)
-    kv_bytes = float(lay.ctx_len.double().sum()) * cfg.Hkv * 2 * (cfg.d // 2 + cfg.d // 16)
+    # K and V codes plus block scales (d/16 E4M3 or d/32 E8M0 bytes) per (token, key head)
+    kv_bytes = float(lay.ctx_len.double().sum()) * cfg.Hkv * 2 * (cfg.d // 2 + cfg.d // (16 if nv else 32))
     return step_ms, kern_ms, kv_bytes, int(lay.ctx_len.sum())
 
 
@@ -237,17 +242,19 @@ def main():
     print(f"[bench] prefill {cfg.name}: step {step_ms:.4f} ms, attention {attn_ms:.4f} ms", file=sys.stderr,
           flush=True)
     if not args.no_decode:
-        d_step, d_kern, kv_bytes, tokens = time_decode(fa4, W.C3, args.steps, args.warmup)
-        gbs = kv_bytes / (d_kern * 1e-3) / 1e9
-        line["decode"] = {
-            "metric": "decode KV GB/s", "workload": W.C3.name, "value": kv_bytes / (d_step * 1e-3) / 1e9,
-            "unit": "GB/s", "ms_per_step": d_step, "kv_bytes": kv_bytes, "context_tokens": tokens,
-            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "traffic": recorded_traffic("decode_split_kernel"),
-                         "traffic_kernel": "decode_split_kernel", "kernel": "decode_split+combine",
-                         "kernel_ms": d_kern}}
-        print(f"[bench] decode: step {d_step:.4f} ms, kernels {d_kern:.4f} ms, {gbs:.0f} GB/s", file=sys.stderr,
-              flush=True)
+        for key, dcfg in (("decode", W.C3), ("decode_mxfp4", W.C3_MX)):
+            d_step, d_kern, kv_bytes, tokens = time_decode(fa4, dcfg, args.steps, args.warmup)
+            gbs = kv_bytes / (d_kern * 1e-3) / 1e9
+            kname = "decode_split_kernel<1>" if dcfg.kv_fmt == "nvfp4" else "decode_split_kernel<0>"
+            line[key] = {
+                "metric": "decode KV GB/s", "workload": dcfg.name, "value": kv_bytes / (d_step * 1e-3) / 1e9,
+                "unit": "GB/s", "ms_per_step": d_step, "kv_bytes": kv_bytes, "context_tokens": tokens,
+                "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": gbs / HBM_PEAK_GBS, "traffic": recorded_traffic(kname),
+                             "traffic_kernel": kname, "kernel": "decode_split+combine", "kernel_ms": d_kern}}
+            print(f"[bench] {key} ({dcfg.kv_fmt}): step {d_step:.4f} ms, kernels {d_kern:.4f} ms, {gbs:.0f} GB/s",
+                  file=sys.stderr, flush=True)
+            torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, min(args.cpu_heads, cfg.Hq))
     print(json.dumps(line), flush=True)

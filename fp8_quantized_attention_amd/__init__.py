@@ -51,7 +51,7 @@ class AttnArgs(ctypes.Structure):
 
 
 class DecodeArgs(ctypes.Structure):
-    _fields_ = [("q1_codes", _p), ("q1_scales", _p), ("q1_tscale", _p),
+    _fields_ = [("fmt", _i32), ("q1_codes", _p), ("q1_scales", _p), ("q1_tscale", _p),
                 ("q2_codes", _p), ("q2_scales", _p), ("q2_tscale", _p),
                 ("k_codes", _p), ("k_scales", _p), ("v_codes", _p), ("v_scales", _p),
                 ("k_tscale", _p), ("v_tscale", _p), ("page_table", _p), ("ctx_len", _p),
@@ -140,8 +140,8 @@ def quantize(x, fmt, hadamard=False, dual=False, row_norms=False, fold=None):
     if dual:
         out["codes2"] = torch.empty_like(out["codes"])
         out["block_scales2"] = torch.empty_like(out["block_scales"])
-        out["scales2"] = torch.empty_like(out["scales"])
-        res = QOutput(fmt, out["codes2"].data_ptr(), out["block_scales2"].data_ptr(), out["scales2"].data_ptr(),
+        out["scales2"] = torch.empty_like(out["scales"]) if out["scales"] is not None else None
+        res = QOutput(fmt, out["codes2"].data_ptr(), out["block_scales2"].data_ptr(), _ptr(out["scales2"]),
                       None, None)
     if row_norms:
         out["norm2"] = torch.empty(O, H, R, dtype=torch.float32, device=dev)
@@ -155,20 +155,24 @@ def quantize(x, fmt, hadamard=False, dual=False, row_norms=False, fold=None):
 def quantize_paged(x, fmt, ctx_len, page_table, num_pages, page_size=64):
     """Quantize a padded [B, Hkv, Lmax, d] cache tensor (rows r < ctx_len[b] exist) into pages.
 
-    Returns codes [num_pages, Hkv, page_size, d/2], block_scales [num_pages, Hkv, page_size, d/16],
-    scales [B*Hkv] (NVFP4 tensor scale per (sequence, key head)).
+    fmt FA4_NVFP4 or FA4_MXFP4. Returns a dict with 'fmt', codes [num_pages, Hkv, page_size, d/2],
+    block_scales [num_pages, Hkv, page_size, d/16 (NVFP4) or d/32 (MXFP4)] and scales [B*Hkv] (NVFP4
+    tensor scale per (sequence, key head); None for MXFP4).
     """
-    assert fmt == FA4_NVFP4 and x.is_cuda and x.is_contiguous()
+    assert fmt in (FA4_NVFP4, FA4_MXFP4) and x.is_cuda and x.is_contiguous()
     B, H, R, d = x.shape
     dev = x.device
+    nv = fmt == FA4_NVFP4
     out = {
+        "fmt": fmt,
         "codes": torch.zeros(num_pages, H, page_size, d // 2, dtype=torch.uint8, device=dev),
-        "block_scales": torch.zeros(num_pages, H, page_size, d // 16, dtype=torch.uint8, device=dev),
-        "scales": torch.empty(B * H, dtype=torch.float32, device=dev),
+        "block_scales": torch.zeros(num_pages, H, page_size, d // (16 if nv else 32), dtype=torch.uint8,
+                                    device=dev),
+        "scales": torch.empty(B * H, dtype=torch.float32, device=dev) if nv else None,
     }
     qin = QInput(x.data_ptr(), _dtype_code(x), d, B, H, R, H * R * d, R * d, d, ctx_len.data_ptr(),
                  page_table.data_ptr(), page_size, page_table.shape[1], num_pages)
-    qout = QOutput(fmt, out["codes"].data_ptr(), out["block_scales"].data_ptr(), out["scales"].data_ptr(), None, None)
+    qout = QOutput(fmt, out["codes"].data_ptr(), out["block_scales"].data_ptr(), _ptr(out["scales"]), None, None)
     _check(lib.fa4_quantize_blockscaled(ctypes.byref(qin), 0, ctypes.byref(qout), None, None, _stream()),
            "fa4_quantize_blockscaled(paged)")
     return out
@@ -215,17 +219,17 @@ def attn_fwd(q, k, v, causal, fmt, Hq, Hkv, Lq, Lk, d, B=1, bitmap=None, q_bf16=
 # ---------------------------------------------------------------------------------------------------- decode
 
 def decode_args(q1, q2, kcache, vcache, page_table, ctx_len, Hq, Hkv, d=128, page_size=64, softmax_scale=None,
-                out=None):
+                out=None, fmt=FA4_NVFP4):
     B = ctx_len.shape[0]
     if out is None:
         out = torch.empty(B, Hq, d, dtype=torch.float32, device=ctx_len.device)
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(d)
-    a = DecodeArgs(q1["codes"].data_ptr(), q1["block_scales"].data_ptr(), q1["scales"].data_ptr(),
-                   q2["codes"].data_ptr(), q2["block_scales"].data_ptr(), q2["scales"].data_ptr(),
+    a = DecodeArgs(fmt, q1["codes"].data_ptr(), q1["block_scales"].data_ptr(), _ptr(q1.get("scales")),
+                   q2["codes"].data_ptr(), q2["block_scales"].data_ptr(), _ptr(q2.get("scales")),
                    kcache["codes"].data_ptr(), kcache["block_scales"].data_ptr(),
                    vcache["codes"].data_ptr(), vcache["block_scales"].data_ptr(),
-                   kcache["scales"].data_ptr(), vcache["scales"].data_ptr(),
+                   _ptr(kcache.get("scales")), _ptr(vcache.get("scales")),
                    page_table.data_ptr(), ctx_len.data_ptr(), B, Hq, Hkv, d, page_size, page_table.shape[1],
                    kcache["codes"].shape[0], softmax_scale, out.data_ptr())
     return a, out
@@ -237,10 +241,11 @@ def decode_workspace(a, device):
 
 
 def decode_paged(q1, q2, kcache, vcache, page_table, ctx_len, Hq, Hkv, d=128, page_size=64, softmax_scale=None,
-                 workspace=None, out=None):
-    """Decode attention for one query token per sequence. q1/q2: NVFP4 dicts of the dual-residual query
-    ([B, Hq, 1, d] rows); kcache / vcache: paged NVFP4 dicts from quantize_paged()."""
-    a, out = decode_args(q1, q2, kcache, vcache, page_table, ctx_len, Hq, Hkv, d, page_size, softmax_scale, out)
+                 workspace=None, out=None, fmt=FA4_NVFP4):
+    """Decode attention for one query token per sequence. q1/q2: dicts of the dual-residual query
+    ([B, Hq, 1, d] rows); kcache / vcache: paged dicts from quantize_paged(); all in format fmt."""
+    a, out = decode_args(q1, q2, kcache, vcache, page_table, ctx_len, Hq, Hkv, d, page_size, softmax_scale, out,
+                         fmt)
     if workspace is None:
         workspace = decode_workspace(a, ctx_len.device)
     _check(lib.fa4_decode_paged(ctypes.byref(a), workspace.data_ptr(), workspace.numel(), _stream()),
@@ -274,14 +279,15 @@ def prefill(q, k, v, causal, fmt=FA4_MXFP4, hadamard=False, select=None, softmax
 
 
 def decode(q, kcache, vcache, page_table, ctx_len, Hkv, softmax_scale=None, workspace=None, out=None):
-    """One decode step: q [B, Hq, d] (bf16 or float32) -> dual-residual NVFP4 -> paged attention.
-    Returns (o [B, Hq, d] float32, the quantized query dict)."""
+    """One decode step: q [B, Hq, d] (bf16 or float32) -> dual-residual query in the cache's format (NVFP4
+    or MXFP4, from kcache['fmt']) -> paged attention. Returns (o [B, Hq, d] float32, the quantized query)."""
     B, Hq, d = q.shape
-    qq = quantize(q.reshape(B, Hq, 1, d), FA4_NVFP4, dual=True)
+    fmt = kcache.get("fmt", FA4_NVFP4)
+    qq = quantize(q.reshape(B, Hq, 1, d), fmt, dual=True)
     q1 = {"codes": qq["codes"], "block_scales": qq["block_scales"], "scales": qq["scales"]}
     q2 = {"codes": qq["codes2"], "block_scales": qq["block_scales2"], "scales": qq["scales2"]}
     o = decode_paged(q1, q2, kcache, vcache, page_table, ctx_len, Hq, Hkv, d, softmax_scale=softmax_scale,
-                     workspace=workspace, out=out)
+                     workspace=workspace, out=out, fmt=fmt)
     return o, qq
 
 
@@ -364,23 +370,27 @@ class PrefillRunner:
 
 
 class DecodeRunner:
-    """Preallocated decode step: dual-residual NVFP4 query quantization plus paged attention."""
+    """Preallocated decode step: dual-residual query quantization (in the cache's format, NVFP4 or MXFP4)
+    plus paged attention."""
 
     def __init__(self, q, kcache, vcache, page_table, ctx_len, Hkv, softmax_scale=None):
         B, Hq, d = q.shape
         dev = q.device
         self.q = q
+        fmt = kcache.get("fmt", FA4_NVFP4)
+        nv = fmt == FA4_NVFP4
         u8, f32 = dict(dtype=torch.uint8, device=dev), dict(dtype=torch.float32, device=dev)
-        self.q1 = {"codes": torch.empty(B, Hq, 1, d // 2, **u8), "block_scales": torch.empty(B, Hq, 1, d // 16, **u8),
-                   "scales": torch.empty(B * Hq, **f32)}
-        self.q2 = {k: torch.empty_like(t) for k, t in self.q1.items()}
+        self.q1 = {"codes": torch.empty(B, Hq, 1, d // 2, **u8),
+                   "block_scales": torch.empty(B, Hq, 1, d // (16 if nv else 32), **u8),
+                   "scales": torch.empty(B * Hq, **f32) if nv else None}
+        self.q2 = {k: (torch.empty_like(t) if t is not None else None) for k, t in self.q1.items()}
         self._qi = QInput(q.data_ptr(), _dtype_code(q), d, B, Hq, 1, Hq * d, d, d, None, None, 0, 0, 0)
-        self._qo = QOutput(FA4_NVFP4, self.q1["codes"].data_ptr(), self.q1["block_scales"].data_ptr(),
-                           self.q1["scales"].data_ptr(), None, None)
-        self._qr = QOutput(FA4_NVFP4, self.q2["codes"].data_ptr(), self.q2["block_scales"].data_ptr(),
-                           self.q2["scales"].data_ptr(), None, None)
+        self._qo = QOutput(fmt, self.q1["codes"].data_ptr(), self.q1["block_scales"].data_ptr(),
+                           _ptr(self.q1["scales"]), None, None)
+        self._qr = QOutput(fmt, self.q2["codes"].data_ptr(), self.q2["block_scales"].data_ptr(),
+                           _ptr(self.q2["scales"]), None, None)
         self.args, self.o = decode_args(self.q1, self.q2, kcache, vcache, page_table, ctx_len, Hq, Hkv, d,
-                                        softmax_scale=softmax_scale)
+                                        softmax_scale=softmax_scale, fmt=fmt)
         self.ws = decode_workspace(self.args, dev)
         self._keep = (kcache, vcache, page_table, ctx_len)
 

@@ -1,9 +1,16 @@
-// Decode attention over a paged NVFP4 KV cache for gfx950, with a dual-residual NVFP4 query.
+// Decode attention over a paged FP4 KV cache for gfx950 (NVFP4 or MXFP4), with a dual-residual query
+// in the cache's format.
 //
-// Source: "BitDecoding-FP4" (sns.style digest): native FP4 KV-cache decoding over pages, the query
-// split into two FP4 tensors (the second carries the first one's residual), probabilities quantized
-// under a scale that cannot underflow, and the query heads of a GQA group stacked into one
-// matrix-core tile. "MpFA QK4V8" section 3.3: the softmax statistics stay in FP32.
+// Source: "BitDecoding-FP4" (sns.style digest): native FP4 KV-cache decoding over pages (NVFP4 and
+// MXFP4 caches), the query split into two FP4 tensors (the second carries the first one's residual),
+// probabilities quantized under a scale that cannot underflow, and the query heads of a GQA group
+// stacked into one matrix-core tile. "MpFA QK4V8" section 3.3: the softmax statistics stay in FP32.
+//
+// MXFP4 caches: the E8M0 block scales run along d, the contraction axis of QK^T, so K and Q codes go
+// straight into the scaled MFMA (16x16x128, FP4 x FP4, one block scale per lane) with no expansion.
+// For PV the scales run along d, which is not the contraction axis (the keys are), so V is expanded
+// exactly to bf16 (code * 2^e, at most 2 significant bits; the conversion applies a key's scale to the
+// 8 values of its d-run before the 8x8 transpose of 16-bit values) and P^ enters as bf16.
 //
 // Work decomposition: the keys of each (sequence, key head) are cut into splits of DEC_SPLIT keys; a
 // workgroup owns one split and its 4 waves take the split's 128-key tiles (the probability tiles) in
@@ -91,7 +98,7 @@ __device__ __forceinline__ void transpose8x8_nibbles(uint32_t w[8]) {
 }
 
 // The two 64-key pages of a tile as buffer resources over this key head's rows of each page (codes
-// 4 KB, scales 512 B per array). A page without keys (past the context, or an id outside the cache)
+// 4 KB, scales 512 B (NVFP4) or 256 B (MXFP4) per array). A page without keys (past the context, or an id outside the cache)
 // gets a zero-size resource: buffer loads past a resource's size return zeros, so its keys read as
 // zeros and no load sits behind a branch. All of it is wave-uniform (scalar registers); the loads
 // then carry only a 32-bit per-lane offset.
@@ -105,7 +112,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint8_t *base,
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), 0, bytes, BUF_DWORD3);
 }
 
+template <int FMT>
 __device__ __forceinline__ TilePages tile_pages(const DecArgs &a, const int32_t *pt, int kvh, int t0, int L) {
+  constexpr int SB = FMT == FA4_NVFP4 ? 8 : 4;       // scale bytes per row
   TilePages tp;
 #pragma unroll
   for (int p = 0; p < 2; p++) {
@@ -114,9 +123,9 @@ __device__ __forceinline__ TilePages tile_pages(const DecArgs &a, const int32_t 
     const bool ok = t0 + 64 * p < L && pg >= 0 && (int64_t)pg < a.num_pages;
     const int64_t row0 = ((int64_t)(ok ? pg : 0) * a.Hkv + kvh) * 64;
     tp.kc[p] = page_rsrc(a.kc + row0 * 64, ok ? 4096 : 0);
-    tp.ks[p] = page_rsrc(a.ks + row0 * 8, ok ? 512 : 0);
+    tp.ks[p] = page_rsrc(a.ks + row0 * SB, ok ? 64 * SB : 0);
     tp.vc[p] = page_rsrc(a.vc + row0 * 64, ok ? 4096 : 0);
-    tp.vs[p] = page_rsrc(a.vs + row0 * 8, ok ? 512 : 0);
+    tp.vs[p] = page_rsrc(a.vs + row0 * SB, ok ? 64 * SB : 0);
   }
   return tp;
 }
@@ -152,6 +161,46 @@ __device__ __forceinline__ void load_v(const TilePages &tp, int lane, int n, int
   }
 }
 
+// MXFP4 K: as load_k, with the one E8M0 scale of the lane's 32 values (block g of key 16 kb + n).
+__device__ __forceinline__ void load_k_mx(const TilePages &tp, int n, int g, v4i kc[8], uint32_t ks[8]) {
+  const int vo_c = n * 64 + 16 * g, vo_s = n * 4 + g;
+#pragma unroll
+  for (int kb = 0; kb < 8; kb++) {
+    const int p = kb >> 2, r0 = 16 * (kb & 3);
+    kc[kb] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(tp.kc[p], vo_c, r0 * 64, 0));
+    ks[kb] = __builtin_amdgcn_raw_buffer_load_b8(tp.ks[p], vo_s, r0 * 4, 0);
+  }
+}
+
+// MXFP4 V: codes as load_v; the quarter's 32 scale rows (4 bytes each, 128 contiguous bytes) are
+// loaded one row per lane (lane L: key L % 32) and fetched by lane shuffles when the quarter is used.
+__device__ __forceinline__ void load_v_mx(const TilePages &tp, int lane, int n, int g, uint32_t vc[4][8],
+                                          uint32_t vs[4]) {
+  const int vo_c = 4 * g * 64 + 4 * n;
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const int p = q >> 1;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const int r0 = 32 * (q & 1) + 16 * (j >> 2) + (j & 3);
+      vc[q][j] = __builtin_amdgcn_raw_buffer_load_b32(tp.vc[p], vo_c, r0 * 64, 0);
+    }
+    vs[q] = __builtin_amdgcn_raw_buffer_load_b32(tp.vs[p], 4 * (lane & 31), 128 * (q & 1), 0);
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ void load_k_fmt(const TilePages &tp, int n, int g, v4i kc[8], uint32_t ks[8]) {
+  if constexpr (FMT == FA4_NVFP4) load_k(tp, n, g, kc, ks);
+  else load_k_mx(tp, n, g, kc, ks);
+}
+template <int FMT>
+__device__ __forceinline__ void load_v_fmt(const TilePages &tp, int lane, int n, int g, uint32_t vc[4][8],
+                                           uint32_t vs[4]) {
+  if constexpr (FMT == FA4_NVFP4) load_v(tp, lane, n, g, vc, vs);
+  else load_v_mx(tp, lane, n, g, vc, vs);
+}
+
 // two E4M3 codes (bits 15:0) -> two fp16 values (exact)
 __device__ __forceinline__ v2h e4m3x2_f16(uint32_t w) {
   return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
@@ -173,6 +222,7 @@ __device__ __forceinline__ v8h row_shl_v8h(v8h v) {
   return __builtin_bit_cast(v8h, x);
 }
 
+template <int FMT>
 __global__ void __launch_bounds__(DEC_THREADS) decode_split_kernel(DecArgs a) {
   __shared__ float part[DEC_SLOTS][4][DEC_PART];
   // Workgroup order: (sequence, key head) fastest, split slowest. Workgroups are handed to the 8 XCDs
@@ -193,28 +243,44 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_split_kernel(DecArgs a) {
 
   // ---- query operand: column n = residual (n >> 2) & 1 of head 4 kvh + (n & 3); columns 8..15
   // repeat columns 0..7, so that both halves of each row hold every score and split the softmax.
-  // Physical d of (lane group g, step s, element j) = 32 g + 8 s + j.
+  // NVFP4: physical d of (lane group g, step s, element j) = 32 g + 8 s + j. MXFP4: lane group g holds
+  // d = 32 g .. 32 g + 31 (one E8M0 block) as FP4 codes with its scale byte.
   v8h qop[4];
+  v8i qmx = {};
+  int qsc = 0;
   {
     const int hq = kvh * 4 + (n & 3);
     const bool r2 = n & 4;
     const uint8_t *qc = (r2 ? a.q2c : a.q1c) + ((int64_t)b * a.Hq + hq) * 64 + 16 * g;
-    const uint8_t *qs = (r2 ? a.q2s : a.q1s) + ((int64_t)b * a.Hq + hq) * 8 + 2 * g;
     const v4i w = *reinterpret_cast<const v4i *>(qc);
-    const v2h sc = e4m3x2_f16(*reinterpret_cast<const uint16_t *>(qs));
+    if constexpr (FMT == FA4_NVFP4) {
+      const uint8_t *qs = (r2 ? a.q2s : a.q1s) + ((int64_t)b * a.Hq + hq) * 8 + 2 * g;
+      const v2h sc = e4m3x2_f16(*reinterpret_cast<const uint16_t *>(qs));
 #pragma unroll
-    for (int s = 0; s < 4; s++) qop[s] = expand8((uint32_t)w[s], sc[s >> 1]);
+      for (int s = 0; s < 4; s++) qop[s] = expand8((uint32_t)w[s], sc[s >> 1]);
+    } else {
+      qmx = (v8i){w[0], w[1], w[2], w[3], 0, 0, 0, 0};
+      qsc = (r2 ? a.q2s : a.q1s)[((int64_t)b * a.Hq + hq) * 4 + g];
+    }
   }
-  // scores of head n & 3: x = log2e * scale * s_tK * (s_t1 D[Q1 column] + s_t2 D[Q2 column])
+  // scores of head n & 3: x = log2e * scale * s_tK * (s_t1 D[Q1 column] + s_t2 D[Q2 column]) (the
+  // tensor scales are 1 for MXFP4)
   const int64_t bq = (int64_t)b * a.Hq + kvh * 4 + (n & 3);
-  const float ck = DEC_LOG2E * a.scale * a.kt[(int64_t)b * a.Hkv + kvh];
-  const float c1 = ck * a.q1t[bq], c2 = ck * a.q2t[bq];
+  float c1 = DEC_LOG2E * a.scale, c2 = c1;
+  if constexpr (FMT == FA4_NVFP4) {
+    const float ck = c1 * a.kt[(int64_t)b * a.Hkv + kvh];
+    c1 = ck * a.q1t[bq];
+    c2 = ck * a.q2t[bq];
+  }
   // V scale redistribution: (key j of this lane, block n / 2) sits in lane 2 kk_j + n / 8, byte
   // (n / 2) % 4, kk_j the key's row within its quarter
+  // (MXFP4: the key's 4-byte scale row sits in lane kk_j, byte n / 4)
   int vs_addr[8];
 #pragma unroll
-  for (int j = 0; j < 8; j++) vs_addr[j] = 4 * (2 * (16 * (j >> 2) + 4 * g + (j & 3)) + (n >> 3));
-  const int vs_sh = 8 * ((n >> 1) & 3);
+  for (int j = 0; j < 8; j++)
+    vs_addr[j] = FMT == FA4_NVFP4 ? 4 * (2 * (16 * (j >> 2) + 4 * g + (j & 3)) + (n >> 3))
+                                  : 4 * (16 * (j >> 2) + 4 * g + (j & 3));
+  const int vs_sh = FMT == FA4_NVFP4 ? 8 * ((n >> 1) & 3) : 8 * (n >> 2);
 
   // Software pipeline over the wave's tiles: the next tile's K is requested as soon as this tile's
   // QK has consumed the K registers, and its V as soon as this tile's PV has consumed V, so each
@@ -222,9 +288,9 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_split_kernel(DecArgs a) {
   v4i kc[8];
   uint32_t ks[8], vc[4][8], vs[4];
   if (tbase < L) {
-    const TilePages tp = tile_pages(a, pt, kvh, tbase, L);
-    load_k(tp, n, g, kc, ks);
-    load_v(tp, lane, n, g, vc, vs);
+    const TilePages tp = tile_pages<FMT>(a, pt, kvh, tbase, L);
+    load_k_fmt<FMT>(tp, n, g, kc, ks);
+    load_v_fmt<FMT>(tp, lane, n, g, vc, vs);
   }
 #pragma unroll
   for (int it = 0; it < DEC_TPW; it++) {
@@ -233,7 +299,7 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_split_kernel(DecArgs a) {
     const bool tail = t0 + 128 > L;                        // the tile holds keys past the context
     const bool has_next = it + 1 < DEC_TPW && t0 + 512 < L;
     TilePages tpn;
-    if (has_next) tpn = tile_pages(a, pt, kvh, t0 + 512, L);
+    if (has_next) tpn = tile_pages<FMT>(a, pt, kvh, t0 + 512, L);
     float mt = -INFINITY, lsum = 0.0f;
     v4f acc[8];
 #pragma unroll
@@ -243,15 +309,20 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_split_kernel(DecArgs a) {
       v4f S[8];
 #pragma unroll
       for (int kb = 0; kb < 8; kb++) {
-        const v2h sc = e4m3x2_f16(ks[kb]);
         S[kb] = (v4f){0.f, 0.f, 0.f, 0.f};
+        if constexpr (FMT == FA4_NVFP4) {
+          const v2h sc = e4m3x2_f16(ks[kb]);
 #pragma unroll
-        for (int s = 0; s < 4; s++)
-          S[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(expand8((uint32_t)kc[kb][s], sc[s >> 1]), qop[s], S[kb],
-                                                         0, 0, 0);
+          for (int s = 0; s < 4; s++)
+            S[kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(expand8((uint32_t)kc[kb][s], sc[s >> 1]), qop[s],
+                                                           S[kb], 0, 0, 0);
+        } else {
+          const v8i kop = (v8i){kc[kb][0], kc[kb][1], kc[kb][2], kc[kb][3], 0, 0, 0, 0};
+          S[kb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kop, qmx, S[kb], 4, 4, 0, (int)ks[kb], 0, qsc);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (has_next) load_k(tpn, n, g, kc, ks);
+      if (has_next) load_k_fmt<FMT>(tpn, n, g, kc, ks);
       // ---- this lane's half: key blocks 4 rep + kk, keys 16 (4 rep + kk) + 4 g + i. Q1 columns
       // (n & 4 == 0) combine with the Q2 column four lanes up; other lanes carry unused values.
       float x[4][4];
@@ -269,8 +340,8 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_split_kernel(DecArgs a) {
           for (int i = 0; i < 4; i++)
             if (t0 + 16 * (4 * rep + kk) + 4 * g + i >= L) x[kk][i] = -INFINITY;
 #pragma unroll
-        for (int q = 0; q < 4; q++)                          // scale word of lane L: key 32 q + L / 2
-          if (t0 + 32 * q + (lane >> 1) >= L) vs[q] = 0u;
+        for (int q = 0; q < 4; q++)      // scale word of lane L: key 32 q + L / 2 (MXFP4: 32 q + L % 32)
+          if (t0 + 32 * q + (FMT == FA4_NVFP4 ? lane >> 1 : lane & 31) >= L) vs[q] = 0u;
       }
 #pragma unroll
       for (int kk = 0; kk < 4; kk++)
@@ -291,7 +362,12 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_split_kernel(DecArgs a) {
           const float p0 = __builtin_amdgcn_exp2f(x[kk][i0] - mt);
           const float p1 = __builtin_amdgcn_exp2f(x[kk][i0 + 1] - mt);
           lsum += p0 + p1;
-          pr[u] = e4m3x2_f16(e4m3_encode2(448.0f * p0, 448.0f * p1));
+          const uint32_t pc = e4m3_encode2(448.0f * p0, 448.0f * p1);
+          if constexpr (FMT == FA4_NVFP4) {
+            pr[u] = e4m3x2_f16(pc);
+          } else {                                            // bf16 bits in the same registers
+            pr[u] = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pc, 1.0f, false));
+          }
         }
         popl[kq] = (v8h){pr[0][0], pr[0][1], pr[1][0], pr[1][1], pr[2][0], pr[2][1], pr[3][0], pr[3][1]};
       }
@@ -302,23 +378,50 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_split_kernel(DecArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; q++) {
         const v8h pb = q < 2 ? popl[q] : row_shl_v8h<8>(popl[q - 2]);
-        uint32_t w[8];
+        if constexpr (FMT == FA4_NVFP4) {
+          uint32_t w[8];
 #pragma unroll
-        for (int j = 0; j < 8; j++) w[j] = vc[q][j];
-        transpose8x8_nibbles(w);                             // w[e]: keys j = 0..7 at d = 8 n + e
-        v2h sp[4];
+          for (int j = 0; j < 8; j++) w[j] = vc[q][j];
+          transpose8x8_nibbles(w);                             // w[e]: keys j = 0..7 at d = 8 n + e
+          v2h sp[4];
 #pragma unroll
-        for (int jp = 0; jp < 4; jp++) {
-          const uint32_t s0 = (uint32_t)__builtin_amdgcn_ds_bpermute(vs_addr[2 * jp], (int)vs[q]);
-          const uint32_t s1 = (uint32_t)__builtin_amdgcn_ds_bpermute(vs_addr[2 * jp + 1], (int)vs[q]);
-          sp[jp] = e4m3x2_f16(((s0 >> vs_sh) & 0xffu) | (((s1 >> vs_sh) & 0xffu) << 8));
+          for (int jp = 0; jp < 4; jp++) {
+            const uint32_t s0 = (uint32_t)__builtin_amdgcn_ds_bpermute(vs_addr[2 * jp], (int)vs[q]);
+            const uint32_t s1 = (uint32_t)__builtin_amdgcn_ds_bpermute(vs_addr[2 * jp + 1], (int)vs[q]);
+            sp[jp] = e4m3x2_f16(((s0 >> vs_sh) & 0xffu) | (((s1 >> vs_sh) & 0xffu) << 8));
+          }
+#pragma unroll
+          for (int e = 0; e < 8; e++)
+            acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(expand8s(w[e], sp), pb, acc[e], 0, 0, 0);
+        } else {
+          // key j's run of 8 d values -> bf16 with its own scale 2^(code - 127); scale code 0 (blocks
+          // below 6 * 2^-127) is taken as 2^-126 so that the conversion's scale stays a normal float
+          uint32_t kw[8][4];
+#pragma unroll
+          for (int j = 0; j < 8; j++) {
+            const uint32_t sw = (uint32_t)__builtin_amdgcn_ds_bpermute(vs_addr[j], (int)vs[q]);
+            const uint32_t code = (sw >> vs_sh) & 0xffu;
+            const float sc = __uint_as_float((code > 1u ? code : 1u) << 23);
+            kw[j][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(vc[q][j], sc, 0));
+            kw[j][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(vc[q][j], sc, 1));
+            kw[j][2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(vc[q][j], sc, 2));
+            kw[j][3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(vc[q][j], sc, 3));
+          }
+          // 8x8 transpose of 16-bit values: A operand of d = 8 n + e holds keys j = 0..7
+#pragma unroll
+          for (int e = 0; e < 8; e++) {
+            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+            v4i av;
+#pragma unroll
+            for (int jp = 0; jp < 4; jp++)
+              av[jp] = (int)__builtin_amdgcn_perm(kw[2 * jp + 1][e >> 1], kw[2 * jp][e >> 1], sel);
+            acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, av),
+                                                             __builtin_bit_cast(v8bf, pb), acc[e], 0, 0, 0);
+          }
         }
-#pragma unroll
-        for (int e = 0; e < 8; e++)
-          acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(expand8s(w[e], sp), pb, acc[e], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (has_next) load_v(tpn, lane, n, g, vc, vs);
+      if (has_next) load_v_fmt<FMT>(tpn, lane, n, g, vc, vs);
     }
     // ---- tile partial -> LDS (lanes n < 4 hold head n; acc[e][i] is d = 32 g + 8 i + e)
     if (n < 4) {
@@ -375,16 +478,18 @@ __global__ void __launch_bounds__(128) decode_combine_kernel(DecArgs a) {
     l += f * p[1];
     o += f * p[2 + d];
   }
-  const float vts = a.vt[(int64_t)b * a.Hkv + kvh] * (1.0f / 448.0f);
+  const float vts = (a.vt ? a.vt[(int64_t)b * a.Hkv + kvh] : 1.0f) * (1.0f / 448.0f);
   a.o[((int64_t)b * a.Hq + h) * 128 + d] = o / l * vts;
 }
 
 static DecArgs make_dec(const fa4_decode_args *p, void *ws) {
   DecArgs x;
   x.q1c = p->q1_codes; x.q1s = p->q1_scales; x.q2c = p->q2_codes; x.q2s = p->q2_scales;
-  x.q1t = p->q1_tscale; x.q2t = p->q2_tscale;
+  x.q1t = p->fmt == FA4_NVFP4 ? p->q1_tscale : nullptr;
+  x.q2t = p->fmt == FA4_NVFP4 ? p->q2_tscale : nullptr;
   x.kc = p->k_codes; x.ks = p->k_scales; x.vc = p->v_codes; x.vs = p->v_scales;
-  x.kt = p->k_tscale; x.vt = p->v_tscale;
+  const bool nv = p->fmt == FA4_NVFP4;           // MXFP4 has no tensor scales (the pointers are not read)
+  x.kt = nv ? p->k_tscale : nullptr; x.vt = nv ? p->v_tscale : nullptr;
   x.pt = p->page_table; x.ctx = p->ctx_len;
   x.B = p->B; x.Hq = p->Hq; x.Hkv = p->Hkv; x.max_pages = p->max_pages;
   x.nsplit = (p->max_pages * 64 + DEC_SPLIT - 1) / DEC_SPLIT;
@@ -402,7 +507,9 @@ size_t decode_workspace_bytes(const fa4_decode_args *p) {
 hipError_t launch_decode(const fa4_decode_args *p, void *ws, hipStream_t s) {
   if (p->B == 0) return hipSuccess;
   const DecArgs x = make_dec(p, ws);
-  hipLaunchKernelGGL(decode_split_kernel, dim3((unsigned)((int64_t)x.nsplit * x.B * x.Hkv)), dim3(DEC_THREADS), 0, s, x);
+  const dim3 grid((unsigned)((int64_t)x.nsplit * x.B * x.Hkv));
+  if (p->fmt == FA4_MXFP4) hipLaunchKernelGGL(decode_split_kernel<FA4_MXFP4>, grid, dim3(DEC_THREADS), 0, s, x);
+  else hipLaunchKernelGGL(decode_split_kernel<FA4_NVFP4>, grid, dim3(DEC_THREADS), 0, s, x);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(x.Hq, x.B), dim3(128), 0, s, x);

@@ -85,10 +85,12 @@ fa4_status fa4_quantize_blockscaled(const fa4_qinput *in, uint32_t flags, const 
     REQUIRE(out->fmt != FA4_FP8_TOKEN, FA4_ERR_UNSUPPORTED, "quantize: Hadamard rotation with FP8 output");
   }
   if (flags & FA4_DUAL_RESIDUAL) {
-    REQUIRE(out->fmt == FA4_NVFP4, FA4_ERR_UNSUPPORTED, "quantize: dual residual needs NVFP4");
-    REQUIRE(residual && residual->scales && (in->rows == 0 || (residual->codes && residual->block_scales)),
+    REQUIRE(out->fmt == FA4_NVFP4 || out->fmt == FA4_MXFP4, FA4_ERR_UNSUPPORTED,
+            "quantize: dual residual needs NVFP4 or MXFP4");
+    const bool nv = out->fmt == FA4_NVFP4;
+    REQUIRE(residual && (!nv || residual->scales) && (in->rows == 0 || (residual->codes && residual->block_scales)),
             FA4_ERR_NULL, "quantize: dual residual output missing");
-    REQUIRE(residual->fmt == FA4_NVFP4, FA4_ERR_UNSUPPORTED, "quantize: residual format must be NVFP4");
+    REQUIRE(residual->fmt == out->fmt, FA4_ERR_UNSUPPORTED, "quantize: residual format must match the output's");
     REQUIRE(aligned(residual->codes, 16) && aligned(residual->block_scales, 4) && aligned(residual->scales, 4),
             FA4_ERR_ALIGN, "quantize: residual codes must be 16-byte aligned, scales 4-byte aligned");
   }
@@ -174,6 +176,7 @@ size_t fa4_decode_workspace_bytes(const fa4_decode_args *a) {
 
 fa4_status fa4_decode_paged(const fa4_decode_args *a, void *ws, size_t ws_bytes, void *stream) {
   REQUIRE(a, FA4_ERR_NULL, "decode: args is NULL");
+  REQUIRE(a->fmt == FA4_NVFP4 || a->fmt == FA4_MXFP4, FA4_ERR_UNSUPPORTED, "decode: format %d", a->fmt);
   REQUIRE(a->d == 128, FA4_ERR_UNSUPPORTED, "decode: d=%d (128)", a->d);
   REQUIRE(a->page_size == 64, FA4_ERR_UNSUPPORTED, "decode: page_size=%d (64)", a->page_size);
   REQUIRE(a->B >= 0 && a->Hkv >= 1 && a->Hq == 4 * a->Hkv, FA4_ERR_UNSUPPORTED,
@@ -184,14 +187,19 @@ fa4_status fa4_decode_paged(const fa4_decode_args *a, void *ws, size_t ws_bytes,
           "decode: grid too large");
   REQUIRE((int64_t)a->max_pages * 64 <= ((int64_t)1 << 30), FA4_ERR_SHAPE, "decode: context too long");
   if (a->B == 0) return ok();
-  REQUIRE(a->q1_codes && a->q1_scales && a->q1_tscale && a->q2_codes && a->q2_scales && a->q2_tscale &&
-              a->k_codes && a->k_scales && a->v_codes && a->v_scales && a->k_tscale && a->v_tscale &&
-              a->page_table && a->ctx_len && a->o,
+  REQUIRE(a->q1_codes && a->q1_scales && a->q2_codes && a->q2_scales && a->k_codes && a->k_scales &&
+              a->v_codes && a->v_scales && a->page_table && a->ctx_len && a->o,
           FA4_ERR_NULL, "decode: a required pointer is NULL");
+  if (a->fmt == FA4_NVFP4)
+    REQUIRE(a->q1_tscale && a->q2_tscale && a->k_tscale && a->v_tscale, FA4_ERR_NULL,
+            "decode: NVFP4 tensor scales are NULL");
   const void *ptrs16[] = {a->q1_codes, a->q2_codes, a->k_codes, a->v_codes};
   for (const void *p : ptrs16) REQUIRE(aligned(p, 16), FA4_ERR_ALIGN, "decode: code arrays must be 16-byte aligned");
+  // block scales: 8 (NVFP4) or 4 (MXFP4) bytes per row, read in whole rows
+  const size_t sal = a->fmt == FA4_NVFP4 ? 8 : 4;
   const void *ptrs8[] = {a->q1_scales, a->q2_scales, a->k_scales, a->v_scales};
-  for (const void *p : ptrs8) REQUIRE(aligned(p, 8), FA4_ERR_ALIGN, "decode: scale arrays must be 8-byte aligned");
+  for (const void *p : ptrs8)
+    REQUIRE(aligned(p, sal), FA4_ERR_ALIGN, "decode: scale arrays must be %zu-byte aligned", sal);
   const size_t need = fa4::decode_workspace_bytes(a);
   REQUIRE(ws && ws_bytes >= need, FA4_ERR_WORKSPACE, "decode: workspace %zu bytes, %zu needed", ws_bytes, need);
   REQUIRE(aligned(ws, 256), FA4_ERR_ALIGN, "decode: workspace must be 256-byte aligned");

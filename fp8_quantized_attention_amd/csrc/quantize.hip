@@ -1,16 +1,15 @@
-// Block-scaled quantizer kernels for gfx950: MXFP4, NVFP4 (tensor-amax pre-pass, dual residual),
-// FP8 per-token V, optional 128-point Hadamard rotation and squared row norms.
+// Block-scaled quantizer kernels for gfx950: MXFP4, NVFP4 (tensor-amax pre-pass), dual-residual
+// queries in either format, FP8 per-token V, optional 128-point Hadamard rotation and squared row norms.
 //
 // Sources: "MXFP vs NVFP4" (tqpw.cn 81738) sections 2.1-2.2 (block structures) and 3.1 (a fused
 // quantization kernel computing in registers with coalesced global access); "BitDecoding-FP4"
 // (dual-residual query, Hadamard rotation of keys); "General notes on quantization" (X ~ s * Q,
 // per-token and per-group scales); "MpFA QK4V8" section 5.1 (zero maxima must not give a zero scale).
 //
-// Layout of the work: a row of d elements is spread over d/4 lanes, 4 consecutive elements per lane
-// (d = 128: 32 lanes, two rows per wave; d = 64: 16 lanes, four rows per wave). Loads are 16 B
-// (float) or 8 B (bf16) per lane and the packed codes of a row are written as one contiguous run,
-// so both directions are coalesced. Block maxima come from xor-shuffles inside the 8 (MX) or 4 (NV)
-// lanes of a block. A workgroup owns a chunk of rows of one group, so the NVFP4 tensor maximum is
+// Layout of the work: each lane reads one 16-byte run of a row (4 float or 8 bf16 elements), so a row
+// spans d/4 (float) or d/8 (bf16) neighbouring lanes, and the packed codes of a row are written as one
+// contiguous run, so both directions are coalesced. Block maxima come from xor-shuffles inside the
+// lanes of a block (32 or 16 elements). A workgroup owns a chunk of rows of one group, so the NVFP4 tensor maximum is
 // reduced in LDS and published with one atomicMax per workgroup (max is order-independent, so the
 // result is deterministic).
 #include "fa4_device.h"
@@ -263,6 +262,24 @@ __global__ void __launch_bounds__(QUANT_THREADS) quantize_kernel(QArgs a) {
         store_nibbles<E>(a.codes + orow * (D / 2) + li * (E / 2), c);
         if ((li % (32 / E)) == 0) a.bscales[orow * (D / 32) + li / (32 / E)] = (uint8_t)(e + 127);
       }
+      if (DUAL) {
+        // residual r = x - code * 2^e, formed as (x 2^-e - code) * 2^e: the difference is exact (the
+        // code is x 2^-e rounded to a neighbour on the E2M1 grid, |x 2^-e| <= 6), the power-of-two
+        // scaling rounds only a subnormal result, and code * 2^e itself (which can exceed the float
+        // range when e = 126) is never formed. Then MXFP4 of r with its own scales.
+        float rv[E];
+#pragma unroll
+        for (int i = 0; i < E; i++) rv[i] = __builtin_ldexpf(sv[i] - e2m1_value((c >> (4 * i)) & 15u), e);
+        const int re = mx_exponent(group_max(lane_amax<E>(rv), 32 / E));
+        const float rmul = pow2_neg(re);
+#pragma unroll
+        for (int i = 0; i < E; i++) rv[i] *= rmul;
+        const uint32_t rc = e2m1_lane<E>(rv);
+        if (store) {
+          store_nibbles<E>(a.rcodes + orow * (D / 2) + li * (E / 2), rc);
+          if ((li % (32 / E)) == 0) a.rbscales[orow * (D / 32) + li / (32 / E)] = (uint8_t)(re + 127);
+        }
+      }
     } else if (FMT == FA4_FP8_TOKEN) {
       const float am = group_max(lane_amax<E>(v), LPR);
       const float s = am == 0.0f ? 1.0f : am / 448.0f;
@@ -384,7 +401,9 @@ static hipError_t quantize_dispatch(const QArgs &a, int fmt, bool had, bool dual
                                     bool norm, hipStream_t s) {
   hipError_t e = hipSuccess;
   const unsigned small = (unsigned)((groups + 255) / 256);
-  if (fmt == FA4_MXFP4) {
+  if (fmt == FA4_MXFP4) {                    // one pass (the residual needs no tensor scale)
+    if (dual) return had ? launch_q<D, DT, FA4_MXFP4, 1, true, true>(a, groups, norm, s)
+                         : launch_q<D, DT, FA4_MXFP4, 1, false, true>(a, groups, norm, s);
     if (had) return launch_q<D, DT, FA4_MXFP4, 1, true, false>(a, groups, norm, s);
     return launch_q<D, DT, FA4_MXFP4, 1, false, false>(a, groups, norm, s);
   }

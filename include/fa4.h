@@ -5,7 +5,7 @@
  *   fa4_quantize_blockscaled  Q/K -> 4-bit E2M1 with block scales (MXFP4 or NVFP4), V -> FP8 E4M3
  *   fa4_select_tiles          ThriftAttention-style choice of the 128x128 tiles computed in bf16
  *   fa4_attn_fwd              fused prefill attention (scaled-MFMA QK^T and PV, FP32 online softmax)
- *   fa4_decode_paged          decode attention over a paged NVFP4 KV cache
+ *   fa4_decode_paged          decode attention over a paged FP4 (NVFP4 or MXFP4) KV cache
  *
  * Conventions shared by every call:
  *   - Every pointer in an argument struct is a DEVICE pointer owned by the caller and must stay valid
@@ -73,8 +73,9 @@ enum { FA4_HADAMARD128 = 1u << 0, FA4_DUAL_RESIDUAL = 1u << 1 }; /* quantizer fl
  *              codes = E4M3(x / s). block_scales unused.
  * flags: FA4_HADAMARD128 rotates each row by the Sylvester Hadamard matrix H_128 / sqrt(128) (float64,
  *        rounded to float32) before quantizing (d must be 128; NVFP4 or MXFP4 only).
- *        FA4_DUAL_RESIDUAL (NVFP4 only): `out` receives Q1 = NVFP4(x) and `residual` receives
- *        Q2 = NVFP4(float32(x - dequant(Q1))), with its own tensor scales.
+ *        FA4_DUAL_RESIDUAL (NVFP4 or MXFP4): `out` receives Q1 = F(x) and `residual` receives
+ *        Q2 = F(float32(x - dequant(Q1))) in the same format F (`residual->fmt` must equal
+ *        `out->fmt`); NVFP4 residuals get their own tensor scales, MXFP4 ones need none.
  * fold_w / fold_scale (FP8_TOKEN, optional, unpaged, rows a multiple of 128): the data that folds the
  *        per-token V scale into the attention probabilities. For each 128-row tile j of a group,
  *        fold_scale[j] = 2^e (a float), e = the smallest integer with 448 * 2^e >= max of the tile's
@@ -176,23 +177,27 @@ fa4_status fa4_attn_fwd(const fa4_attn_args *a, void *stream);
 /* ------------------------------------------------------------------------------------------------
  * Paged decode.
  *
- * Source page: "BitDecoding-FP4" (sns.style digest): native FP4 KV-cache decode over pages, dual-
- * residual query (q ~ Q1 + Q2, both FP4), underflow-aware probability scaling, query heads of one
- * GQA group stacked into one matrix-core tile.
+ * Source page: "BitDecoding-FP4" (sns.style digest): native FP4 KV-cache decode over pages (NVFP4 and
+ * MXFP4 caches), dual-residual query (q ~ Q1 + Q2, both FP4), underflow-aware probability scaling,
+ * query heads of one GQA group stacked into one matrix-core tile.
  *
  * For sequence b and query head h (key head kv = h / (Hq/Hkv)) over keys c < ctx_len[b]:
- *   q^ = dequant(Q1) + dequant(Q2); S_c = softmax_scale * q^ . k^_c with the NVFP4-dequantized keys;
+ *   q^ = dequant(Q1) + dequant(Q2); S_c = softmax_scale * q^ . k^_c with the dequantized keys;
  *   per 128-key tile (from position 0, the last one partial): m~ = tile max, P' = exp(S - m~),
  *   P^ = E4M3(448 P'), T = (1/448) sum_c P^ v^_c; O = sum e^(m~-m) T / sum e^(m~-m) sum P'.
- * Layouts: q1_codes/q2_codes [B][Hq][d/2], q1_scales/q2_scales [B][Hq][d/16] E4M3, q1_tscale/
- * q2_tscale [B*Hq]; k_codes/v_codes [num_pages][Hkv][page_size][d/2], k_scales/v_scales
- * [num_pages][Hkv][page_size][d/16]; k_tscale/v_tscale [B][Hkv]; page_table [B][max_pages] (entries
- * past ceil(ctx_len[b]/page_size) are not read); o [B][Hq][d] float.
+ * fmt selects the format of Q1, Q2, K and V (all alike):
+ *   FA4_NVFP4: q1_scales/q2_scales [B][Hq][d/16] E4M3 with q1_tscale/q2_tscale [B*Hq];
+ *              k_scales/v_scales [num_pages][Hkv][page_size][d/16] E4M3 with k_tscale/v_tscale [B][Hkv].
+ *   FA4_MXFP4: q1_scales/q2_scales [B][Hq][d/32] E8M0; k_scales/v_scales [num_pages][Hkv][page_size]
+ *              [d/32] E8M0; the four tensor-scale pointers are not read (may be NULL).
+ * Other layouts: q1_codes/q2_codes [B][Hq][d/2]; k_codes/v_codes [num_pages][Hkv][page_size][d/2];
+ * page_table [B][max_pages] (entries past ceil(ctx_len[b]/page_size) are not read); o [B][Hq][d] float.
  * The work is split over key ranges; partial results go to a caller-provided workspace of
  * fa4_decode_workspace_bytes(a) bytes (256-byte aligned) and are merged by a second kernel.
  * Requirements: d = 128; page_size = 64; Hq / Hkv = 4; 1 <= ctx_len[b] <= max_pages * page_size.
  */
 typedef struct {
+  int32_t fmt;                                  /* FA4_NVFP4 or FA4_MXFP4 (Q1, Q2, K and V)     */
   const uint8_t *q1_codes, *q1_scales; const float *q1_tscale;
   const uint8_t *q2_codes, *q2_scales; const float *q2_tscale;
   const uint8_t *k_codes, *k_scales, *v_codes, *v_scales;

@@ -76,14 +76,17 @@ def prefill_reference(cfg, seed, heads, rows, select=None, q_all=None, k_all=Non
 
 
 def decode_cache(cfg, layout, seed, pairs_only=None):
-    """Oracle NVFP4 pages of K and V, quantized per (sequence, key head) and scattered by the page table.
+    """Oracle pages of K and V in cfg.kv_fmt (NVFP4 or MXFP4), quantized per (sequence, key head) and
+    scattered by the page table.
 
     pairs_only: optional set of (b, kvh) to build (others stay zero). Returns
     ((kc, ks), (vc, vs), k_tscale, v_tscale, dequantized logical rows {(tensor, b, kvh): [L, d]}).
     """
     d, ps = cfg.d, cfg.page_size
     P = layout.num_pages
-    kc = np.zeros((P, cfg.Hkv, ps, d // 2), np.uint8); ks = np.zeros((P, cfg.Hkv, ps, d // 16), np.uint8)
+    nv = cfg.kv_fmt == "nvfp4"
+    kc = np.zeros((P, cfg.Hkv, ps, d // 2), np.uint8)
+    ks = np.zeros((P, cfg.Hkv, ps, d // (16 if nv else 32)), np.uint8)
     vc = np.zeros_like(kc); vs = np.zeros_like(ks)
     kt = np.zeros((cfg.B, cfg.Hkv), np.float32); vt = np.zeros_like(kt)
     logical = {}
@@ -96,22 +99,29 @@ def decode_cache(cfg, layout, seed, pairs_only=None):
                 continue
             for tensor, (codes, scales, ts) in [(W.T_K, (kc, ks, kt)), (W.T_V, (vc, vs, vt))]:
                 x = W.decode_kv_head(cfg, tensor, b, h, L, seed).double().numpy()
-                qc, qs, qt = Q.nvfp4_quantize(x[None])
-                codes[phys, h, c % ps] = qc[0]
-                scales[phys, h, c % ps] = qs[0]
-                ts[b, h] = qt[0]
-                logical[(tensor, b, h)] = Q.nvfp4_dequantize(qc, qs, qt)[0]
+                if nv:
+                    qc, qs, qt = Q.nvfp4_quantize(x[None])
+                    codes[phys, h, c % ps] = qc[0]
+                    scales[phys, h, c % ps] = qs[0]
+                    ts[b, h] = qt[0]
+                    logical[(tensor, b, h)] = Q.nvfp4_dequantize(qc, qs, qt)[0]
+                else:
+                    qc, qs = Q.mxfp4_quantize(x)
+                    codes[phys, h, c % ps] = qc
+                    scales[phys, h, c % ps] = qs
+                    logical[(tensor, b, h)] = Q.mxfp4_dequantize(qc, qs)
     return (kc, ks), (vc, vs), kt, vt, logical
 
 
 def decode_query_quant(cfg, seed):
     q = W.decode_query(cfg, seed).double().numpy()
-    return q, Q.dual_residual_quantize(q.reshape(cfg.B * cfg.Hq, 1, cfg.d))
+    rows = q.reshape(cfg.B * cfg.Hq, 1, cfg.d)
+    return q, (Q.dual_residual_quantize(rows) if cfg.kv_fmt == "nvfp4" else Q.dual_residual_quantize_mx(rows))
 
 
 def decode_reference(cfg, seed, layout, pairs, logical, q1, q2):
     """Oracle O for the listed (b, h) pairs from contiguous dequantized rows."""
-    qhat = Dd.dequant_query(q1, q2).reshape(cfg.B, cfg.Hq, cfg.d)
+    qhat = Dd.dequant_query(q1, q2, cfg.kv_fmt).reshape(cfg.B, cfg.Hq, cfg.d)
     group = cfg.Hq // cfg.Hkv
     out = []
     for (b, h) in pairs:

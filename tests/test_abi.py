@@ -81,8 +81,13 @@ def test_quantize_rejects_before_launch():
     assert _call_q(_q(), codes=None) == fa4.FA4_ERR_NULL
     assert _call_q(_q(), fmt=fa4.FA4_NVFP4, sc=None) == fa4.FA4_ERR_NULL
     assert _call_q(_q(d=64), flags=fa4.FA4_HADAMARD128) == fa4.FA4_ERR_UNSUPPORTED
-    assert _call_q(_q(), flags=fa4.FA4_DUAL_RESIDUAL) == fa4.FA4_ERR_UNSUPPORTED          # needs NVFP4
+    assert _call_q(_q(), fmt=fa4.FA4_FP8_TOKEN, flags=fa4.FA4_DUAL_RESIDUAL) == fa4.FA4_ERR_UNSUPPORTED
+    assert _call_q(_q(), flags=fa4.FA4_DUAL_RESIDUAL) == fa4.FA4_ERR_NULL                # residual missing
     assert _call_q(_q(), fmt=fa4.FA4_NVFP4, flags=fa4.FA4_DUAL_RESIDUAL) == fa4.FA4_ERR_NULL
+    res = fa4.QOutput(fa4.FA4_NVFP4, 256, 256, 256)                                      # format mismatch
+    assert _call_q(_q(), flags=fa4.FA4_DUAL_RESIDUAL, res=res) == fa4.FA4_ERR_UNSUPPORTED
+    res = fa4.QOutput(fa4.FA4_MXFP4, 264, 256, None)                                     # MXFP4: no scales
+    assert _call_q(_q(), flags=fa4.FA4_DUAL_RESIDUAL, res=res) == fa4.FA4_ERR_ALIGN
     assert _call_q(_q(), flags=1 << 5) == fa4.FA4_ERR_UNSUPPORTED
     assert _call_q(_q(outer=70000)) == fa4.FA4_ERR_SHAPE
     assert _call_q(_q(page_table=64, page_size=64, max_pages=2, num_pages=4)) == fa4.FA4_ERR_SHAPE  # rows > 128
@@ -135,7 +140,8 @@ def test_select_rejects_before_launch():
 
 
 def _dec(**kw):
-    base = dict(q1_codes=256, q1_scales=256, q1_tscale=256, q2_codes=256, q2_scales=256, q2_tscale=256,
+    base = dict(fmt=fa4.FA4_NVFP4, q1_codes=256, q1_scales=256, q1_tscale=256, q2_codes=256, q2_scales=256,
+                q2_tscale=256,
                 k_codes=256, k_scales=256, v_codes=256, v_scales=256, k_tscale=256, v_tscale=256,
                 page_table=256, ctx_len=256, B=4, Hq=32, Hkv=8, d=128, page_size=64, max_pages=8, num_pages=32,
                 softmax_scale=0.088, o=256)
@@ -157,3 +163,11 @@ def test_decode_rejects_before_launch():
     assert call(a, ws=None, n=need) == fa4.FA4_ERR_WORKSPACE
     assert call(a, ws=520, n=need) == fa4.FA4_ERR_ALIGN
     assert call(_dec(B=0)) == fa4.FA4_OK
+    assert call(_dec(fmt=fa4.FA4_FP8_TOKEN)) == fa4.FA4_ERR_UNSUPPORTED
+    # NVFP4 needs its tensor scales; MXFP4 has none (the pointers are not read) and 4-byte scale rows
+    assert call(_dec(v_tscale=None)) == fa4.FA4_ERR_NULL
+    mx = dict(fmt=fa4.FA4_MXFP4, q1_tscale=None, q2_tscale=None, k_tscale=None, v_tscale=None)
+    assert call(_dec(**mx), ws=512, n=need - 1) == fa4.FA4_ERR_WORKSPACE
+    assert call(_dec(k_scales=260)) == fa4.FA4_ERR_ALIGN
+    assert call(_dec(k_scales=260, **mx), ws=None, n=need) == fa4.FA4_ERR_WORKSPACE
+    assert call(_dec(k_scales=258, **mx)) == fa4.FA4_ERR_ALIGN

@@ -1,4 +1,4 @@
-"""GPU paged decode (dual-residual NVFP4 query over an NVFP4 page cache) vs the oracle."""
+"""GPU paged decode (dual-residual query over an NVFP4 or MXFP4 page cache) vs the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -21,7 +21,8 @@ def _gpu_decode(fa4, cfg, lay, seed=0):
     caches = []
     for tensor in (W.T_K, W.T_V):
         x = W.decode_kv_padded(cfg, lay, tensor, seed, device="cuda")
-        caches.append(fa4.quantize_paged(x, fa4.FA4_NVFP4, ctx, pt, lay.num_pages))
+        fmt = fa4.FA4_NVFP4 if cfg.kv_fmt == "nvfp4" else fa4.FA4_MXFP4
+        caches.append(fa4.quantize_paged(x, fmt, ctx, pt, lay.num_pages))
         del x
     q = W.decode_query(cfg, seed).cuda()
     o, _ = fa4.decode(q, caches[0], caches[1], pt, ctx, cfg.Hkv)
@@ -29,9 +30,13 @@ def _gpu_decode(fa4, cfg, lay, seed=0):
     return o.cpu().numpy(), caches
 
 
+FMTS = pytest.mark.parametrize("base", [W.C3, W.C3_MX], ids=["nvfp4", "mxfp4"])
+
+
+@FMTS
 @pytest.mark.parametrize("ctx", [(200, 700), (1, 130), (128, 128), (511, 513)])
-def test_decode_small_all_pairs(fa4, ctx):
-    cfg = W.C3.scaled(B=5, Hq=8, Hkv=2, ctx_lo=ctx[0], ctx_hi=ctx[1])
+def test_decode_small_all_pairs(fa4, ctx, base):
+    cfg = base.scaled(B=5, Hq=8, Hkv=2, ctx_lo=ctx[0], ctx_hi=ctx[1])
     lay = W.decode_layout(cfg)
     o, _ = _gpu_decode(fa4, cfg, lay)
     _, _, _, _, logical = decode_cache(cfg, lay, 0)
@@ -41,16 +46,18 @@ def test_decode_small_all_pairs(fa4, ctx):
     assert_parity(np.stack([o[b, h] for b, h in pairs]), ref, f"decode ctx {ctx}")
 
 
-def test_decode_deterministic(fa4):
-    cfg = W.C3.scaled(B=4, Hq=8, Hkv=2, ctx_lo=1000, ctx_hi=3000)
+@FMTS
+def test_decode_deterministic(fa4, base):
+    cfg = base.scaled(B=4, Hq=8, Hkv=2, ctx_lo=1000, ctx_hi=3000)
     lay = W.decode_layout(cfg)
     a, _ = _gpu_decode(fa4, cfg, lay)
     b, _ = _gpu_decode(fa4, cfg, lay)
     assert np.array_equal(a, b)
 
 
-def test_full_size_decode_sampled(fa4):
-    cfg = W.C3
+@FMTS
+def test_full_size_decode_sampled(fa4, base):
+    cfg = base
     lay = W.decode_layout(cfg)
     o, _ = _gpu_decode(fa4, cfg, lay)
     rng = np.random.default_rng(3)

@@ -128,17 +128,37 @@ def test_dual_residual_query(fa4):
     assert np.array_equal(_np(out["codes2"]).reshape(2048, 1, -1), c2)
 
 
-def test_paged_kv_cache(fa4):
+@pytest.mark.parametrize("special", [False, True])
+def test_dual_residual_query_mxfp4(fa4, special):
+    """MXFP4 dual residual: Q1 = MXFP4(q), Q2 = MXFP4(fl32(q - dequant(Q1))), bit for bit."""
+    if special:
+        q = torch.from_numpy(_special_rows(rows=64)).reshape(64, 1, 128)
+    else:
+        q = W.decode_query(W.C3).float().reshape(64 * 32, 1, 128)
+    n = q.shape[0]
+    out = fa4.quantize(q.reshape(1, n, 1, 128).contiguous().cuda(), fa4.FA4_MXFP4, dual=True)
+    (c1, s1), (c2, s2) = Q.dual_residual_quantize_mx(q.numpy().reshape(n, 1, 128))
+    assert out["scales"] is None and out["scales2"] is None
+    assert np.array_equal(_np(out["block_scales"]).reshape(n, 1, -1), s1)
+    assert np.array_equal(_np(out["block_scales2"]).reshape(n, 1, -1), s2)
+    assert np.array_equal(_np(out["codes"]).reshape(n, 1, -1), c1)
+    assert np.array_equal(_np(out["codes2"]).reshape(n, 1, -1), c2)
+
+
+@pytest.mark.parametrize("base", [W.C3, W.C3_MX], ids=["nvfp4", "mxfp4"])
+def test_paged_kv_cache(fa4, base):
     from oracle_cases import decode_cache
-    cfg = W.C3.scaled(B=3, Hq=8, Hkv=2, ctx_lo=200, ctx_hi=700)
+    cfg = base.scaled(B=3, Hq=8, Hkv=2, ctx_lo=200, ctx_hi=700)
     lay = W.decode_layout(cfg)
     (kc, ks), (vc, vs), kt, vt, _ = decode_cache(cfg, lay, 0)
     ctx = lay.ctx_len.cuda()
     pt = lay.page_table.cuda()
+    fmt = fa4.FA4_NVFP4 if cfg.kv_fmt == "nvfp4" else fa4.FA4_MXFP4
     for tensor, (rc, rs, rt) in [(W.T_K, (kc, ks, kt)), (W.T_V, (vc, vs, vt))]:
         x = W.decode_kv_padded(cfg, lay, tensor, device="cuda")
-        out = fa4.quantize_paged(x, fa4.FA4_NVFP4, ctx, pt, lay.num_pages)
-        assert np.array_equal(_np(out["scales"]).reshape(cfg.B, cfg.Hkv), rt)
+        out = fa4.quantize_paged(x, fmt, ctx, pt, lay.num_pages)
+        if fmt == fa4.FA4_NVFP4:
+            assert np.array_equal(_np(out["scales"]).reshape(cfg.B, cfg.Hkv), rt)
         # compare every row that exists
         for b in range(cfg.B):
             L = int(lay.ctx_len[b])

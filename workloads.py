@@ -66,6 +66,7 @@ class Decode:
     page_size: int
     ctx_lo: int
     ctx_hi: int
+    kv_fmt: str = "nvfp4"        # format of the paged K/V cache and of the query residuals
 
     def scaled(self, **kw):
         return replace(self, **kw)
@@ -82,6 +83,9 @@ C3 = Decode("decode_paged_nvfp4_gqa", 3, B=64, Hq=32, Hkv=8, d=128, page_size=64
 C4 = Prefill("chunked_prefill_128k_nvfp4_hadamard_select5", 4, B=1, Hq=32, Hkv=8, Lq=2048, Lk=131072, d=128,
              causal=True, dtype="bf16", qk_fmt="nvfp4", outliers=True, hadamard=True, select=True)
 WORKLOADS = [C0, C1, C2, C3, C4]
+# The decode workload over an MXFP4 cache (E8M0 scale per 32 elements, no tensor scale): the same
+# sequences, lengths, pages and values as C3 (same workload id, hence the same seeds).
+C3_MX = replace(C3, name="decode_paged_mxfp4_gqa", kv_fmt="mxfp4")
 
 
 def _chunk(seed, wl, tensor, b, h, rows, d, outliers, dtype):
