@@ -144,6 +144,137 @@ __device__ __forceinline__ LaneOff lane_offsets(int lane) {
   return o;
 }
 
+// ---- pieces of a tile step (this lane: query qrow, keys 32 kb + 8 (i / 4) + 4 hh + i % 4 of S[kb][i])
+
+// S^T for key block kb (32 keys x the wave's 32 queries) from MXFP4 codes in LDS: D/64 scaled FP4 MFMAs,
+// the E8M0 scales of K (per key and 32-element block) and of Q applied in-instruction.
+template <int D>
+__device__ __forceinline__ v16f qk_mx_block(const LaneOff &lo, int kb, int hh, const v8i *qop4, const int *qsc4,
+                                            const uint8_t *k4, const uint8_t *ksc) {
+  v16f s = (v16f){};
+  const uint32_t scw = D == 128 ? *reinterpret_cast<const uint32_t *>(ksc + lo.ks + 128 * kb)
+                                : *reinterpret_cast<const uint16_t *>(ksc + lo.ks + 64 * kb);
+#pragma unroll
+  for (int st = 0; st < D / 64; st++) {
+    const v4i t = *reinterpret_cast<const v4i *>(k4 + lo.k[st] + 32 * kb * (D / 2));
+    const v8i kop = (v8i){t[0], t[1], t[2], t[3], 0, 0, 0, 0};
+    const int kscl = (int)((scw >> (8 * (2 * st + hh))) & 0xffu);
+    s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop, qop4[st], s, 4, 4, 0, kscl, 0, qsc4[st]);
+  }
+  return s;
+}
+
+// Keys past the query position get -inf (the tile crossing the causal diagonal).
+__device__ __forceinline__ void mask_tile(v16f S[4], int kt, int hh, int qpos) {
+#pragma unroll
+  for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      const int key = kt * 128 + 32 * kb + 8 * (i / 4) + 4 * hh + (i % 4);
+      if (key > qpos) S[kb][i] = -INFINITY;
+    }
+}
+
+// The tile's row reference in log2 units: the smallest integer r >= its largest score, so that
+// P' = 2^(S cs - r) <= 1 (its largest value lies in (1/2, 1]). The maximum runs over independent
+// partial results, so no long dependent chain forms.
+__device__ __forceinline__ float tile_reference(const v16f S[4], float cs) {
+  float mp[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; kb++) {
+    mp[kb] = S[kb][0];
+#pragma unroll
+    for (int i = 1; i < 16; i++) mp[kb] = fmaxf(mp[kb], S[kb][i]);
+  }
+  float mS = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
+  mS = fmaxf(mS, shfl_xor_f(mS, 32));
+  return ceilf(mS * cs);
+}
+
+// Running reference m (log2 units, an integer): raised only when a tile's reference exceeds it by
+// more than ACC_HEADROOM, so the accumulator and the sum (tile weights up to 2^ACC_HEADROOM) stay far
+// from overflow; raising rescales both by an exact power of two. Returns the tile weight exponent kB
+// (2^kB = 2^(r - m)) and the exponent reference rr0: a weight below 2^-127 (the smallest E8M0 scale)
+// adds nothing representable, so those rows take an infinite reference and their probabilities are
+// exactly zero (the clamped scale does not inflate them).
+template <int NDB>
+__device__ __forceinline__ int tile_weight(float r, float &m, float &lsum, v16f *acc, float &rr0) {
+  if (__builtin_amdgcn_ballot_w64(r > m + ACC_HEADROOM) != 0) {   // uniform (always on the first tile)
+    const float m_new = fmaxf(m, r);
+    const float alpha = m == -INFINITY ? 0.0f : __builtin_ldexpf(1.0f, (int)(m - m_new));
+#pragma unroll
+    for (int i = 0; i < NDB; i++) acc[i] *= alpha;
+    lsum *= alpha;
+    m = m_new;
+  }
+  const int kB = (int)fmaxf(r - m, -255.0f);
+  rr0 = kB < -127 ? INFINITY : r;
+  return kB;
+}
+
+// P' = 2^(S cs - r) for key block kb (summed into ts) and P^ = E4M3(P' w_c), w_c = s_v[c] 2^-e
+// (exact), packed straight into the PV B operand, so scores and probabilities are never both held.
+__device__ __forceinline__ void fp8_block(const v16f &Skb, int kb, const float *svs, const LaneOff &lo, float cs,
+                                          float rr0, float &ts, v8i pop[2]) {
+#pragma unroll
+  for (int a4 = 0; a4 < 4; a4++) {
+    const float4 w4 = *reinterpret_cast<const float4 *>(reinterpret_cast<const uint8_t *>(svs) + lo.w +
+                                                        4 * (32 * kb + 8 * a4));
+    const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
+    float pw[4];
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(Skb[4 * a4 + u], cs, -rr0));
+      ts += p;
+      pw[u] = p * wv[u];
+    }
+    // the first conversion keeps the register's high half, which the second one then writes:
+    // starting from the bits of its own (dead) first input avoids materializing a zero
+    int x = __builtin_amdgcn_cvt_pk_fp8_f32(pw[0], pw[1], __float_as_int(pw[0]), false);
+    x = __builtin_amdgcn_cvt_pk_fp8_f32(pw[2], pw[3], x, true);
+    pop[kb >> 1][4 * (kb & 1) + a4] = x;
+  }
+}
+
+// O^T += V^T P^T for an FP8 tile: the tile's power-of-two V scale 2^e rides on V^T's E8M0 operand scale
+// (scA) and the tile weight 2^kBc on P^T's, so the MFMA adds the tile exactly.
+template <int D, int QF>
+__device__ __forceinline__ void pv_fp8(const v8i pop[2], const uint8_t *vq, const LaneOff &lo, int scA, int kBc,
+                                       v16f *acc) {
+  constexpr int NDB = D / 32;
+#pragma unroll
+  for (int t = 0; t < 2; t++) {
+#pragma unroll
+    for (int mb = 0; mb < NDB; mb++) {
+      v8i vop;
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        // source lane (16q + a + 2t'): key 64t + 32(u/2) + 16(u%2) + 8(t'/4) + 4g + t'%4,
+        //                              d 32mb + 16(q%2) + 8a
+        const int krun = 64 * t + 32 * (u >> 1) + 16 * (u & 1);
+        const v2i rr = QF == FA4_MXFP4 ? lds_tr8(vq + lo.v[mb] + krun * D)
+                                       : lds_tr8(vq + lo.v8 + krun * V8_RS + 32 * mb);
+        vop[2 * u] = rr[0];
+        vop[2 * u + 1] = rr[1];
+      }
+      acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, pop[t], acc[mb], 0, 0, 0, scA, 0, kBc + 127);
+    }
+  }
+}
+
+// Wave-uniform reads go through the constant address space, so they become scalar loads (counted
+// apart from the vector loads: waiting for one never waits for the tile loads in flight).
+template <typename T>
+__device__ __forceinline__ T uniform_load(const T *p, int64_t i) {
+  return ((const __attribute__((address_space(4))) T *)p)[i];
+}
+
+// E8M0 code of tile kt's power-of-two V scale 2^e (stored as a float; 2^-127 is the subnormal whose
+// exponent field is 0, matching E8M0 code 0)
+__device__ __forceinline__ int v_tile_scale_code(const float *vfs, int64_t bhk, int nk, int kt) {
+  return (int)((__float_as_uint(uniform_load(vfs, bhk * nk + kt)) >> 23) & 0xffu);
+}
+
 // One 128-key tile for this wave's 32 queries: S^T = K Q^T, softmax step, O^T += V^T P^T.
 // MASK: the tile crosses the causal diagonal (keys past the query position get -inf).
 // sel: a selected tile, computed from the bf16 originals (QK^T and PV on bf16 MFMA).
@@ -169,18 +300,7 @@ __device__ __forceinline__ void tile_step(const AttnArgs &a, const LaneOff &lo, 
     }
   } else if (QF == FA4_MXFP4) {
 #pragma unroll
-    for (int kb = 0; kb < 4; kb++) {
-      S[kb] = (v16f){};
-      const uint32_t scw = D == 128 ? *reinterpret_cast<const uint32_t *>(ksc + lo.ks + 128 * kb)
-                                    : *reinterpret_cast<const uint16_t *>(ksc + lo.ks + 64 * kb);
-#pragma unroll
-      for (int s = 0; s < D / 64; s++) {
-        const v4i t = *reinterpret_cast<const v4i *>(k4 + lo.k[s] + 32 * kb * (D / 2));
-        const v8i kop = (v8i){t[0], t[1], t[2], t[3], 0, 0, 0, 0};
-        const int kscl = (int)((scw >> (8 * (2 * s + hh))) & 0xffu);
-        S[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop, qop4[s], S[kb], 4, 4, 0, kscl, 0, qsc4[s]);
-      }
-    }
+    for (int kb = 0; kb < 4; kb++) S[kb] = qk_mx_block<D>(lo, kb, hh, qop4, qsc4, k4, ksc);
   } else {
 #pragma unroll
     for (int kb = 0; kb < 4; kb++) S[kb] = (v16f){};
@@ -193,51 +313,12 @@ __device__ __forceinline__ void tile_step(const AttnArgs &a, const LaneOff &lo, 
       }
   }
 
-  // ---- softmax step (this lane: query qrow, keys 32kb + 8(i/4) + 4hh + i%4)
   const float cs = sel ? cs_b : cs_q;
-  if (MASK) {
-    const int qpos = qrow + off;
-#pragma unroll
-    for (int kb = 0; kb < 4; kb++)
-#pragma unroll
-      for (int i = 0; i < 16; i++) {
-        const int key = kt * 128 + 32 * kb + 8 * (i / 4) + 4 * hh + (i % 4);
-        if (key > qpos) S[kb][i] = -INFINITY;
-      }
-  }
-  // The tile's row reference in log2 units is the smallest integer r >= its largest score, and
-  // P' = 2^(S cs - r) <= 1 (its largest value lies in (1/2, 1]).
-  // (max and sum run over independent partial results, so no long dependent chain forms)
-  float mp[4];
-#pragma unroll
-  for (int kb = 0; kb < 4; kb++) {
-    mp[kb] = S[kb][0];
-#pragma unroll
-    for (int i = 1; i < 16; i++) mp[kb] = fmaxf(mp[kb], S[kb][i]);
-  }
-  float mS = fmaxf(fmaxf(mp[0], mp[1]), fmaxf(mp[2], mp[3]));
-  mS = fmaxf(mS, shfl_xor_f(mS, 32));
-  const float r = ceilf(mS * cs);
-  // Running reference m (log2 units, an integer): raised only when a tile's reference exceeds it by
-  // more than ACC_HEADROOM, so the accumulator and the sum (tile weights up to 2^ACC_HEADROOM) stay far
-  // from overflow; raising rescales both by an exact power of two.
-  if (__builtin_amdgcn_ballot_w64(r > m + ACC_HEADROOM) != 0) {   // uniform (always on the first tile)
-    const float m_new = fmaxf(m, r);
-    const float alpha = m == -INFINITY ? 0.0f : __builtin_ldexpf(1.0f, (int)(m - m_new));
-#pragma unroll
-    for (int i = 0; i < NDB; i++) acc[i] *= alpha;
-    lsum *= alpha;
-    m = m_new;
-  }
-  int kB = (int)fmaxf(r - m, -255.0f);         // tile weight 2^kB, kB <= ACC_HEADROOM
-  // A weight below 2^-127 (the smallest E8M0 scale) of the reference adds nothing representable:
-  // those rows take an infinite reference, so that their probabilities are exactly zero and the
-  // clamped scale does not inflate them.
-  const float rr0 = kB < -127 ? INFINITY : r;
-  float ts[4] = {0.0f, 0.0f, 0.0f, 0.0f};        // partial sums, one per 16-key group
-
-  // ---- P' = 2^(S cs - r) per element, straight into the operand it feeds (S and P are never both
-  // held whole); then O^T += V^T P^T
+  if (MASK) mask_tile(S, kt, hh, qrow + off);
+  float rr0;
+  const int kB = tile_weight<NDB>(tile_reference(S, cs), m, lsum, acc, rr0);
+  float ts[4] = {0.0f, 0.0f, 0.0f, 0.0f};        // partial sums, one per 32-key block
+  const int kBc = kB < -127 ? -127 : kB;
   if (sel) {
 #pragma unroll
     for (int kb = 0; kb < 4; kb++)
@@ -247,7 +328,6 @@ __device__ __forceinline__ void tile_step(const AttnArgs &a, const LaneOff &lo, 
         ts[kb] += p;
         S[kb][i] = p;
       }
-    const int kBc = kB < -127 ? -127 : kB;
 #pragma unroll
     for (int kb = 0; kb < 4; kb++)
 #pragma unroll
@@ -268,50 +348,10 @@ __device__ __forceinline__ void tile_step(const AttnArgs &a, const LaneOff &lo, 
         }
       }
   } else {
-    // P^ = E4M3(P' w_c) with w_c = s_v[c] 2^-e (exact), packed into the PV B operand
     v8i pop[2];
 #pragma unroll
-    for (int kb = 0; kb < 4; kb++)
-#pragma unroll
-      for (int a4 = 0; a4 < 4; a4++) {
-        const float4 w4 = *reinterpret_cast<const float4 *>(reinterpret_cast<const uint8_t *>(svs) + lo.w +
-                                                            4 * (32 * kb + 8 * a4));
-        const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
-        float pw[4];
-#pragma unroll
-        for (int u = 0; u < 4; u++) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][4 * a4 + u], cs, -rr0));
-          ts[kb] += p;
-          pw[u] = p * wv[u];
-        }
-        // the first conversion keeps the register's high half, which the second one then writes:
-        // starting from the bits of its own (dead) first input avoids materializing a zero
-        int x = __builtin_amdgcn_cvt_pk_fp8_f32(pw[0], pw[1], __float_as_int(pw[0]), false);
-        x = __builtin_amdgcn_cvt_pk_fp8_f32(pw[2], pw[3], x, true);
-        pop[kb >> 1][4 * (kb & 1) + a4] = x;
-      }
-    const int kBc = kB < -127 ? -127 : kB;
-    // E8M0 code of the tile's power-of-two V scale 2^e (stored as a float; 2^-127 is the subnormal
-    // whose exponent field is 0, matching E8M0 code 0)
-    const int scA = (int)((__float_as_uint(a.vfs[bhk * nk + kt]) >> 23) & 0xffu);
-#pragma unroll
-    for (int t = 0; t < 2; t++) {
-#pragma unroll
-      for (int mb = 0; mb < NDB; mb++) {
-        v8i vop;
-#pragma unroll
-        for (int u = 0; u < 4; u++) {
-          // source lane (16q + a + 2t'): key 64t + 32(u/2) + 16(u%2) + 8(t'/4) + 4g + t'%4,
-          //                              d 32mb + 16(q%2) + 8a
-          const int krun = 64 * t + 32 * (u >> 1) + 16 * (u & 1);
-          const v2i rr = QF == FA4_MXFP4 ? lds_tr8(vq + lo.v[mb] + krun * D)
-                                         : lds_tr8(vq + lo.v8 + krun * V8_RS + 32 * mb);
-          vop[2 * u] = rr[0];
-          vop[2 * u + 1] = rr[1];
-        }
-        acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, pop[t], acc[mb], 0, 0, 0, scA, 0, kBc + 127);
-      }
-    }
+    for (int kb = 0; kb < 4; kb++) fp8_block(S[kb], kb, svs, lo, cs, rr0, ts[kb], pop);
+    pv_fp8<D, QF>(pop, vq, lo, v_tile_scale_code(a.vfs, bhk, nk, kt), kBc, acc);
   }
   lsum += __builtin_ldexpf((ts[0] + ts[1]) + (ts[2] + ts[3]), kB);
 }
@@ -388,7 +428,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < NDB; i++) acc[i] = (v16f){};
 
-  auto is_sel = [&](int kt) -> bool { return SEL && a.bitmap[(bhq * nq + qt) * nk + kt] != 0; };
+  auto is_sel = [&](int kt) -> bool { return SEL && uniform_load(a.bitmap, (bhq * nq + qt) * nk + kt) != 0; };
   auto copy_bf16 = [&](int kt) {
     const int64_t krow0 = bhk * a.Lk + (int64_t)kt * 128;
     for (int c = tid; c < 128 * (D / 8); c += ATT_THREADS) {     // 16-byte chunks of bf16 rows
@@ -399,10 +439,8 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
       *reinterpret_cast<v4i *>(v16 + r * H16_RS + 16 * j) = vx;
     }
   };
-// One tile step; MASKV must be a constant. With Lq and Lk multiples of 128 the only tile that crosses
-// the causal diagonal is the last one, so loops run MASKV = false and the diagonal tile is peeled.
 // One tile step; MASKV and SELV must be constants. With Lq and Lk multiples of 128 the only tile that
-// crosses the causal diagonal is the last one.
+// crosses the causal diagonal is the last one, so loops run MASKV = false and the diagonal tile is peeled.
 #define FA4_TILE_STEP(MASKV, SELV, KT, KC, KS, VC, W)                                                         \
   tile_step<D, QF, MASKV, SELV>(a, lo, KT, lane, hh, col, qrow, off, bhq, bhk, nk, cs_q, cs_b, qop4, qsc4, qop16, \
                                 KC, KS, k16, VC, v16, W, m, lsum, acc)
