@@ -283,7 +283,10 @@ def decode(q, kcache, vcache, page_table, ctx_len, Hkv, softmax_scale=None, work
     or MXFP4, from kcache['fmt']) -> paged attention. Returns (o [B, Hq, d] float32, the quantized query)."""
     B, Hq, d = q.shape
     fmt = kcache.get("fmt", FA4_NVFP4)
-    qq = quantize(q.reshape(B, Hq, 1, d), fmt, dual=True)
+    # NVFP4 needs a tensor scale per (sequence, head): one group per row; MXFP4 rows are independent,
+    # so they go as one group of B*Hq rows (same output layout, far fewer workgroups)
+    shape = (B, Hq, 1, d) if fmt == FA4_NVFP4 else (1, 1, B * Hq, d)
+    qq = quantize(q.reshape(shape), fmt, dual=True)
     q1 = {"codes": qq["codes"], "block_scales": qq["block_scales"], "scales": qq["scales"]}
     q2 = {"codes": qq["codes2"], "block_scales": qq["block_scales2"], "scales": qq["scales2"]}
     o = decode_paged(q1, q2, kcache, vcache, page_table, ctx_len, Hq, Hkv, d, softmax_scale=softmax_scale,
@@ -384,7 +387,11 @@ class DecodeRunner:
                    "block_scales": torch.empty(B, Hq, 1, d // (16 if nv else 32), **u8),
                    "scales": torch.empty(B * Hq, **f32) if nv else None}
         self.q2 = {k: (torch.empty_like(t) if t is not None else None) for k, t in self.q1.items()}
-        self._qi = QInput(q.data_ptr(), _dtype_code(q), d, B, Hq, 1, Hq * d, d, d, None, None, 0, 0, 0)
+        if nv:      # one group per (sequence, head): its own tensor scale
+            self._qi = QInput(q.data_ptr(), _dtype_code(q), d, B, Hq, 1, Hq * d, d, d, None, None, 0, 0, 0)
+        else:       # independent rows: one group of B*Hq rows
+            self._qi = QInput(q.data_ptr(), _dtype_code(q), d, 1, 1, B * Hq, B * Hq * d, B * Hq * d, d, None, None,
+                              0, 0, 0)
         self._qo = QOutput(fmt, self.q1["codes"].data_ptr(), self.q1["block_scales"].data_ptr(),
                            _ptr(self.q1["scales"]), None, None)
         self._qr = QOutput(fmt, self.q2["codes"].data_ptr(), self.q2["block_scales"].data_ptr(),

@@ -341,6 +341,84 @@ __global__ void __launch_bounds__(QUANT_THREADS) quantize_kernel(QArgs a) {
   }
 }
 
+// max over the workgroup (every thread calls it; `red` holds QUANT_THREADS / 64 floats)
+__device__ __forceinline__ float block_max(float v, float *red) {
+  for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, shfl_xor_f(v, m));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < QUANT_THREADS / 64; w++) r = fmaxf(r, red[w]);
+  return r;
+}
+
+// NVFP4 of groups small enough for one workgroup (at most QUANT_CHUNK rows, unpaged): the tensor
+// maximum, the codes and, with DUAL, the residual's maximum and codes in one launch (one workgroup per
+// group). Same arithmetic as the multi-pass path: the maxima are the same maxima, reduced in LDS.
+template <int D, int DT, bool DUAL>
+__global__ void __launch_bounds__(QUANT_THREADS) nv_group_kernel(QArgs a) {
+  constexpr int E = Epl<DT>::value;
+  constexpr int LPR = D / E;
+  constexpr int RPW = 64 / LPR;
+  constexpr int RPB = RPW * (QUANT_THREADS / 64);
+  constexpr int NIT = (QUANT_CHUNK + RPB - 1) / RPB;
+  __shared__ float red0[QUANT_THREADS / 64], red1[QUANT_THREADS / 64];
+  const int g = blockIdx.x;
+  const int64_t o = g / a.heads;
+  const int h = g - (int)o * a.heads;
+  int64_t nrows = a.rows;
+  if (a.row_counts) nrows = min<int64_t>(nrows, (int64_t)a.row_counts[o]);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane / LPR, li = lane % LPR;
+  float vin[NIT][E];
+  float gmax = 0.0f;
+#pragma unroll
+  for (int it = 0; it < NIT; it++) {
+    const int64_t rr = it * RPB + wave * RPW + sub;
+#pragma unroll
+    for (int i = 0; i < E; i++) vin[it][i] = 0.0f;
+    if (rr < nrows) load_lane<DT, E>(a.x, o * a.so + h * a.sh + rr * a.sr + li * E, vin[it]);
+    gmax = fmaxf(gmax, lane_amax<E>(vin[it]));            // inactive rows hold zeros
+  }
+  const float st = tensor_scale_from_max(block_max(gmax, red0));
+  if (threadIdx.x == 0) a.scales[g] = st;
+  float rmax = 0.0f;
+#pragma unroll
+  for (int it = 0; it < NIT; it++) {
+    const int64_t rr = it * RPB + wave * RPW + sub;
+    const bool active = rr < nrows;
+    const int64_t orow = (int64_t)g * a.rows + rr;
+    uint32_t sb;
+    double xh[E];
+    const uint32_t c = nv_codes<E>(vin[it], st, &sb, xh);
+    if (active) {
+      store_nibbles<E>(a.codes + orow * (D / 2) + li * (E / 2), c);
+      if ((li % (16 / E)) == 0) a.bscales[orow * (D / 16) + li / (16 / E)] = (uint8_t)sb;
+    }
+    if (DUAL) {
+#pragma unroll
+      for (int i = 0; i < E; i++) vin[it][i] = (float)((double)vin[it][i] - xh[i]);   // the residual
+      rmax = fmaxf(rmax, active ? lane_amax<E>(vin[it]) : 0.0f);
+    }
+  }
+  if (DUAL) {
+    const float rst = tensor_scale_from_max(block_max(rmax, red1));
+    if (threadIdx.x == 0) a.rscales[g] = rst;
+#pragma unroll
+    for (int it = 0; it < NIT; it++) {
+      const int64_t rr = it * RPB + wave * RPW + sub;
+      const int64_t orow = (int64_t)g * a.rows + rr;
+      uint32_t rsb;
+      double rxh[E];
+      const uint32_t rc = nv_codes<E>(vin[it], rst, &rsb, rxh);
+      if (rr < nrows) {
+        store_nibbles<E>(a.rcodes + orow * (D / 2) + li * (E / 2), rc);
+        if ((li % (16 / E)) == 0) a.rbscales[orow * (D / 16) + li / (16 / E)] = (uint8_t)rsb;
+      }
+    }
+  }
+}
+
 // Fold data of FP8 per-token V for the attention kernel: per 128-row tile a power-of-two scale 2^e,
 // e the smallest integer with 448 * 2^e >= sigma (sigma = max of the tile's row scales), clamped to
 // [-127, 127], and per row w = s * 2^-e (exact). With sigma = M 2^E, M in [1, 2): e = E - 8 when
@@ -415,6 +493,12 @@ static hipError_t quantize_dispatch(const QArgs &a, int fmt, bool had, bool dual
       e = hipGetLastError();
     }
     return e;
+  }
+  // NVFP4, groups that fit one workgroup: a single launch
+  if (!had && !norm && !a.page_table && a.rows <= QUANT_CHUNK) {
+    if (dual) hipLaunchKernelGGL((nv_group_kernel<D, DT, true>), dim3((unsigned)groups), dim3(QUANT_THREADS), 0, s, a);
+    else hipLaunchKernelGGL((nv_group_kernel<D, DT, false>), dim3((unsigned)groups), dim3(QUANT_THREADS), 0, s, a);
+    return hipGetLastError();
   }
   // NVFP4: zero the group maxima, reduce them, quantize, turn maxima into tensor scales
   hipLaunchKernelGGL(fill_zero_kernel, dim3(small), dim3(256), 0, s, a.scales, groups);

@@ -117,6 +117,19 @@ def test_nvfp4_special_values_and_empty(fa4):
     assert np.array_equal(_np(out["scales"]), np.ones(3, np.float32))
 
 
+@pytest.mark.parametrize("rows", [40, 100])
+def test_nvfp4_dual_group_sizes(fa4, rows):
+    """Groups of at most 64 rows take the one-launch path, larger ones the multi-pass one: both must
+    give the oracle's codes and tensor scales, for Q1 and the residual Q2, on special values."""
+    x = np.concatenate([_special_rows(rows=rows, seed=3), _special_rows(rows=rows, seed=4)])
+    x = np.ascontiguousarray(x.reshape(1, 2, rows, 128))
+    out = fa4.quantize(torch.from_numpy(x).cuda(), fa4.FA4_NVFP4, dual=True)
+    (c1, s1, t1), (c2, s2, t2) = Q.dual_residual_quantize(x[0].astype(np.float64))
+    assert np.array_equal(_np(out["scales"]), t1) and np.array_equal(_np(out["scales2"]), t2)
+    assert np.array_equal(_np(out["block_scales"])[0], s1) and np.array_equal(_np(out["codes"])[0], c1)
+    assert np.array_equal(_np(out["block_scales2"])[0], s2) and np.array_equal(_np(out["codes2"])[0], c2)
+
+
 def test_dual_residual_query(fa4):
     q = W.decode_query(W.C3)                          # [64, 32, 128] bf16
     out = fa4.quantize(q.reshape(64, 32, 1, 128).cuda(), fa4.FA4_NVFP4, dual=True)
