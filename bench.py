@@ -10,6 +10,8 @@ attention kernel, inputs resident in HBM. `value` is prefill attention TFLOP/s o
   decode        the paged NVFP4 decode step (64 sequences, 32 -> 8 GQA heads, contexts 8K-32K):
                 KV-cache GB/s, and the decode kernels' HBM roofline;
   decode_mxfp4  the same decode step over an MXFP4 cache (same sequences and values);
+  k_quant       (--outlier) quantization of the 128K-token chunked-prefill keys (NVFP4 + Hadamard)
+                plain, with static smoothing, and with smoothing + the per-block scale search;
   cpu_baseline  the CPU oracle (float64 numpy) on a bounded sample of the same workload.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-decode] [--no-cpu-baseline]
                        [--copy-probe] [--summarize-counters DIR]
@@ -172,6 +174,31 @@ def time_decode(fa4, cfg, steps, warmup):
     return step_ms, kern_ms, kv_bytes, int(lay.ctx_len.sum())
 
 
+def time_k_quant(fa4, steps, warmup):
+    """Outlier-aware key quantization on the chunked-prefill workload's keys (B1, 8 key heads, 131072
+    tokens, d128, bf16 with x20 outlier channels): NVFP4 + Hadamard, plain / smoothing / smoothing + search.
+    The smoothing factors come from a 2048-token calibration prefix of Q and K."""
+    cfg = W.C4
+    q, k, _ = W.prefill_inputs(cfg)
+    qc, kc = q.cuda(), k.cuda()
+    del q, k
+    qs, ks = fa4.smoothing_factors(qc, kc[:, :, :2048].contiguous())
+    in_bytes = kc.numel() * 2
+    out_bytes = kc.numel() // 2 + kc.numel() // 16 + 4 * cfg.Hkv
+    res = {"workload": cfg.name + " keys", "rows": cfg.Lk, "heads": cfg.Hkv, "format": "nvfp4+hadamard",
+           "algorithmic_bytes": 2 * in_bytes + out_bytes, "note": "two passes over the input (tensor maximum, codes)"}
+    for name, cs, search in (("plain", None, False), ("smoothing", ks, False), ("smoothing+search", ks, True)):
+        run = fa4.QuantizeRunner(kc, fa4.FA4_NVFP4, hadamard=True, channel_scale=cs, search=search)
+        for _ in range(warmup):
+            run.run()
+        ms = _time_loop(run.run, steps)
+        res[name] = {"ms": ms, "GB/s": (2 * in_bytes + out_bytes) / (ms * 1e-3) / 1e9}
+        print(f"[bench] k_quant {name}: {ms:.4f} ms", file=sys.stderr, flush=True)
+    del qc, kc
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(cfg, heads):
     """The oracle as it stands on `heads` query heads of the workload (quantize + attend every row)."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
@@ -201,6 +228,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=8)
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--outlier", action="store_true", help="also time the outlier-aware key quantization")
     ap.add_argument("--summarize-counters", metavar="DIR")
     args = ap.parse_args()
     if args.summarize_counters:
@@ -255,6 +283,8 @@ def main():
             print(f"[bench] {key} ({dcfg.kv_fmt}): step {d_step:.4f} ms, kernels {d_kern:.4f} ms, {gbs:.0f} GB/s",
                   file=sys.stderr, flush=True)
             torch.cuda.empty_cache()
+    if args.outlier:
+        line["k_quant"] = time_k_quant(fa4, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, min(args.cpu_heads, cfg.Hq))
     print(json.dumps(line), flush=True)

@@ -14,16 +14,16 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfa4.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m fp8_quantized_attention_amd.build` "
+    raise ImportError(f"{LIB_PATH} is not built; run `python fp8_quantized_attention_amd/build.py` "
                       "(or __graft_entry__.build()) first")
 lib = ctypes.CDLL(LIB_PATH)
 
 FA4_OK, FA4_ERR_NULL, FA4_ERR_SHAPE, FA4_ERR_UNSUPPORTED, FA4_ERR_ALIGN, FA4_ERR_WORKSPACE, FA4_ERR_HIP = range(7)
 FA4_F32, FA4_BF16 = 0, 1
 FA4_MXFP4, FA4_NVFP4, FA4_FP8_TOKEN = 0, 1, 2
-FA4_HADAMARD128, FA4_DUAL_RESIDUAL = 1, 2
+FA4_HADAMARD128, FA4_DUAL_RESIDUAL, FA4_SCALE_SEARCH = 1, 2, 4
 
-EXPORTS = ["fa4_quantize_blockscaled", "fa4_select_tiles", "fa4_attn_fwd", "fa4_decode_workspace_bytes",
+EXPORTS = ["fa4_quantize_blockscaled", "fa4_smoothing_factors", "fa4_select_tiles", "fa4_attn_fwd", "fa4_decode_workspace_bytes",
            "fa4_decode_paged", "fa4_status_string", "fa4_last_error"]
 
 _p = ctypes.c_void_p
@@ -34,7 +34,7 @@ class QInput(ctypes.Structure):
     _fields_ = [("x", _p), ("dtype", _i32), ("d", _i32), ("outer", _i64), ("heads", _i32), ("rows", _i64),
                 ("stride_outer", _i64), ("stride_head", _i64), ("stride_row", _i64),
                 ("row_counts", _p), ("page_table", _p), ("page_size", _i32), ("max_pages", _i32),
-                ("num_pages", _i64)]
+                ("num_pages", _i64), ("channel_scale", _p)]
 
 
 class QOutput(ctypes.Structure):
@@ -62,6 +62,8 @@ class DecodeArgs(ctypes.Structure):
 lib.fa4_quantize_blockscaled.argtypes = [ctypes.POINTER(QInput), _u32, ctypes.POINTER(QOutput),
                                          ctypes.POINTER(QOutput), _p, _p]
 lib.fa4_quantize_blockscaled.restype = ctypes.c_int
+lib.fa4_smoothing_factors.argtypes = [ctypes.POINTER(QInput), ctypes.POINTER(QInput), _p, _p, _p]
+lib.fa4_smoothing_factors.restype = ctypes.c_int
 lib.fa4_select_tiles.argtypes = [_p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p]
 lib.fa4_select_tiles.restype = ctypes.c_int
 lib.fa4_attn_fwd.argtypes = [ctypes.POINTER(AttnArgs), _p]
@@ -106,7 +108,7 @@ def _dtype_code(t):
 
 # ---------------------------------------------------------------------------------------------------- quantize
 
-def quantize(x, fmt, hadamard=False, dual=False, row_norms=False, fold=None):
+def quantize(x, fmt, hadamard=False, dual=False, row_norms=False, fold=None, channel_scale=None, search=False):
     """Quantize a [outer, heads, rows, d] tensor (float32 or bf16, contiguous on the GPU).
 
     Returns a dict: codes [outer, heads, rows, d/2 or d] uint8, block_scales (MXFP4: d/32, NVFP4: d/16
@@ -114,6 +116,8 @@ def quantize(x, fmt, hadamard=False, dual=False, row_norms=False, fold=None):
     residual's 'codes2', 'block_scales2', 'scales2'; with row_norms=True 'norm2' [outer, heads, rows];
     FP8 per-token output also carries the attention fold data 'fold_w' [outer, heads, rows] and
     'fold_scale' [outer, heads, rows/128] (default: when rows is a multiple of 128).
+    channel_scale: optional [heads, d] float32 static smoothing factors (see smoothing_factors());
+    search: the per-block scale search (MXFP4 / NVFP4).
     """
     assert x.is_cuda and x.is_contiguous() and x.dim() == 4
     O, H, R, d = x.shape
@@ -128,7 +132,8 @@ def quantize(x, fmt, hadamard=False, dual=False, row_norms=False, fold=None):
         out["codes"] = torch.empty(O, H, R, d // 2, **u8)
         out["block_scales"] = bs = torch.empty(O, H, R, d // (32 if fmt == FA4_MXFP4 else 16), **u8)
         out["scales"] = torch.empty(O * H, dtype=torch.float32, device=dev) if fmt == FA4_NVFP4 else None
-    qin = QInput(x.data_ptr(), _dtype_code(x), d, O, H, R, H * R * d, R * d, d, None, None, 0, 0, 0)
+    qin = QInput(x.data_ptr(), _dtype_code(x), d, O, H, R, H * R * d, R * d, d, None, None, 0, 0, 0,
+                 _ptr(channel_scale))
     if fold is None:
         fold = fmt == FA4_FP8_TOKEN and R % 128 == 0 and R > 0
     if fold:
@@ -145,14 +150,15 @@ def quantize(x, fmt, hadamard=False, dual=False, row_norms=False, fold=None):
                       None, None)
     if row_norms:
         out["norm2"] = torch.empty(O, H, R, dtype=torch.float32, device=dev)
-    flags = (FA4_HADAMARD128 if hadamard else 0) | (FA4_DUAL_RESIDUAL if dual else 0)
+    flags = (FA4_HADAMARD128 if hadamard else 0) | (FA4_DUAL_RESIDUAL if dual else 0) | \
+        (FA4_SCALE_SEARCH if search else 0)
     _check(lib.fa4_quantize_blockscaled(ctypes.byref(qin), flags, ctypes.byref(qout),
                                         ctypes.byref(res) if res is not None else None,
                                         _ptr(out.get("norm2")), _stream()), "fa4_quantize_blockscaled")
     return out
 
 
-def quantize_paged(x, fmt, ctx_len, page_table, num_pages, page_size=64):
+def quantize_paged(x, fmt, ctx_len, page_table, num_pages, page_size=64, channel_scale=None, search=False):
     """Quantize a padded [B, Hkv, Lmax, d] cache tensor (rows r < ctx_len[b] exist) into pages.
 
     fmt FA4_NVFP4 or FA4_MXFP4. Returns a dict with 'fmt', codes [num_pages, Hkv, page_size, d/2],
@@ -171,11 +177,30 @@ def quantize_paged(x, fmt, ctx_len, page_table, num_pages, page_size=64):
         "scales": torch.empty(B * H, dtype=torch.float32, device=dev) if nv else None,
     }
     qin = QInput(x.data_ptr(), _dtype_code(x), d, B, H, R, H * R * d, R * d, d, ctx_len.data_ptr(),
-                 page_table.data_ptr(), page_size, page_table.shape[1], num_pages)
+                 page_table.data_ptr(), page_size, page_table.shape[1], num_pages, _ptr(channel_scale))
     qout = QOutput(fmt, out["codes"].data_ptr(), out["block_scales"].data_ptr(), _ptr(out["scales"]), None, None)
-    _check(lib.fa4_quantize_blockscaled(ctypes.byref(qin), 0, ctypes.byref(qout), None, None, _stream()),
-           "fa4_quantize_blockscaled(paged)")
+    _check(lib.fa4_quantize_blockscaled(ctypes.byref(qin), FA4_SCALE_SEARCH if search else 0, ctypes.byref(qout),
+                                        None, None, _stream()), "fa4_quantize_blockscaled(paged)")
     return out
+
+
+def smoothing_factors(q_calib, k_calib):
+    """Static smoothing factors from calibration tensors q [B, Hq, L, d] and k [B, Hkv, L', d] (contiguous,
+    float32 or bf16): returns (q_scale [Hq, d], k_scale [Hkv, d]) float32 powers of two, to be passed as
+    channel_scale when quantizing Q and K (QK^T unchanged)."""
+    assert q_calib.is_contiguous() and k_calib.is_contiguous()
+    dev = q_calib.device
+    qs = torch.empty(q_calib.shape[1], q_calib.shape[3], dtype=torch.float32, device=dev)
+    ks = torch.empty(k_calib.shape[1], k_calib.shape[3], dtype=torch.float32, device=dev)
+
+    def qin(x):
+        O, H, R, d = x.shape
+        return QInput(x.data_ptr(), _dtype_code(x), d, O, H, R, H * R * d, R * d, d, None, None, 0, 0, 0, None)
+
+    qi, ki = qin(q_calib), qin(k_calib)
+    _check(lib.fa4_smoothing_factors(ctypes.byref(qi), ctypes.byref(ki), qs.data_ptr(), ks.data_ptr(), _stream()),
+           "fa4_smoothing_factors")
+    return qs, ks
 
 
 # ---------------------------------------------------------------------------------------------------- select
@@ -255,7 +280,8 @@ def decode_paged(q1, q2, kcache, vcache, page_table, ctx_len, Hq, Hkv, d=128, pa
 
 # ---------------------------------------------------------------------------------------------------- pipelines
 
-def prefill(q, k, v, causal, fmt=FA4_MXFP4, hadamard=False, select=None, softmax_scale=None, want_lse=True):
+def prefill(q, k, v, causal, fmt=FA4_MXFP4, hadamard=False, select=None, softmax_scale=None, want_lse=True,
+            smooth=None, search=False):
     """Whole prefill path: quantize Q/K (MXFP4 or NVFP4, optional Hadamard), V to FP8 per token,
     optionally select the top num/den tiles for bf16 (select=(num, den)), then fused attention.
 
@@ -266,8 +292,9 @@ def prefill(q, k, v, causal, fmt=FA4_MXFP4, hadamard=False, select=None, softmax
     B, Hq, Lq, d = q.shape
     Hkv, Lk = k.shape[1], k.shape[2]
     sel = select is not None
-    qq = quantize(q, fmt, hadamard=hadamard, row_norms=sel)
-    kq = quantize(k, fmt, hadamard=hadamard, row_norms=sel)
+    qs, ks = smooth if smooth is not None else (None, None)
+    qq = quantize(q, fmt, hadamard=hadamard, row_norms=sel, channel_scale=qs)
+    kq = quantize(k, fmt, hadamard=hadamard, row_norms=sel, channel_scale=ks, search=search)
     vq = quantize(v, FA4_FP8_TOKEN)
     bitmap = counts = None
     if sel:
@@ -296,6 +323,30 @@ def decode(q, kcache, vcache, page_table, ctx_len, Hkv, softmax_scale=None, work
 
 # ---------------------------------------------------------------------------------------------------- runners
 
+class QuantizeRunner:
+    """Preallocated quantization of one [outer, heads, rows, d] tensor (MXFP4 or NVFP4), optionally with a
+    Hadamard rotation, static smoothing factors (channel_scale [heads, d]) and the scale search."""
+
+    def __init__(self, x, fmt, hadamard=False, channel_scale=None, search=False):
+        O, H, R, d = x.shape
+        dev = x.device
+        u8, f32 = dict(dtype=torch.uint8, device=dev), dict(dtype=torch.float32, device=dev)
+        self.x, self.channel_scale = x, channel_scale
+        self.out = {"codes": torch.empty(O, H, R, d // 2, **u8),
+                    "block_scales": torch.empty(O, H, R, d // (32 if fmt == FA4_MXFP4 else 16), **u8),
+                    "scales": torch.empty(O * H, **f32) if fmt == FA4_NVFP4 else None}
+        self._qi = QInput(x.data_ptr(), _dtype_code(x), d, O, H, R, H * R * d, R * d, d, None, None, 0, 0, 0,
+                          _ptr(channel_scale))
+        self._qo = QOutput(fmt, self.out["codes"].data_ptr(), self.out["block_scales"].data_ptr(),
+                           _ptr(self.out["scales"]), None, None)
+        self._fl = (FA4_HADAMARD128 if hadamard else 0) | (FA4_SCALE_SEARCH if search else 0)
+
+    def run(self, stream=None):
+        _check(lib.fa4_quantize_blockscaled(ctypes.byref(self._qi), self._fl, ctypes.byref(self._qo), None, None,
+                                            _stream() if stream is None else stream), "fa4_quantize_blockscaled")
+        return self.out
+
+
 class PrefillRunner:
     """Preallocated prefill path for repeated calls on fixed shapes (benchmarks, serving loops).
 
@@ -304,7 +355,8 @@ class PrefillRunner:
     them in place to change the data.
     """
 
-    def __init__(self, q, k, v, causal, fmt=FA4_MXFP4, hadamard=False, select=None, softmax_scale=None):
+    def __init__(self, q, k, v, causal, fmt=FA4_MXFP4, hadamard=False, select=None, softmax_scale=None,
+                 smooth=None, search=False):
         self.q, self.k, self.v = q, k, v
         B, Hq, Lq, d = q.shape
         Hkv, Lk = k.shape[1], k.shape[2]
@@ -327,18 +379,21 @@ class PrefillRunner:
         self.bitmap = torch.empty(B, Hq, Lq // 128, Lk // 128, **u8) if self.sel else None
         self.counts = torch.empty(B, Hq, dtype=torch.int32, device=dev) if self.sel else None
 
-        def qin(x):
+        def qin(x, cs=None):
             O, H, R, dd = x.shape
-            return QInput(x.data_ptr(), _dtype_code(x), dd, O, H, R, H * R * dd, R * dd, dd, None, None, 0, 0, 0)
+            return QInput(x.data_ptr(), _dtype_code(x), dd, O, H, R, H * R * dd, R * dd, dd, None, None, 0, 0, 0,
+                          _ptr(cs))
 
         def qout(fm, t):
             return QOutput(fm, t["codes"].data_ptr(), _ptr(t.get("block_scales")), _ptr(t.get("scales")),
                            _ptr(t.get("fold_w")), _ptr(t.get("fold_scale")))
 
-        self._qi = [qin(q), qin(k), qin(v)]
+        self.smooth = smooth
+        qs, ks = smooth if smooth is not None else (None, None)
+        self._qi = [qin(q, qs), qin(k, ks), qin(v)]
         self._qo = [qout(fmt, self.qq), qout(fmt, self.kq), qout(FA4_FP8_TOKEN, self.vq)]
         self._norms = [_ptr(self.qq["norm2"]), _ptr(self.kq["norm2"]), None]
-        self._fl = [self.flags, self.flags, 0]
+        self._fl = [self.flags, self.flags | (FA4_SCALE_SEARCH if search else 0), 0]
         if softmax_scale is None:
             softmax_scale = 1.0 / math.sqrt(d)
         self._attn = AttnArgs(fmt, self.qq["codes"].data_ptr(), self.qq["block_scales"].data_ptr(),

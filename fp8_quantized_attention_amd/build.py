@@ -1,6 +1,7 @@
 """Build the HIP library libfa4.so in-tree with hipcc for gfx950.
 
-Usage: python -m fp8_quantized_attention_amd.build   (or call build()).
+Usage: python fp8_quantized_attention_amd/build.py   (or __graft_entry__.build()); run it as a script so
+that the package (which loads the library) is not imported first.
 """
 import os
 import subprocess

@@ -66,8 +66,14 @@ fa4_status fa4_quantize_blockscaled(const fa4_qinput *in, uint32_t flags, const 
   REQUIRE(in->d == 64 || in->d == 128, FA4_ERR_UNSUPPORTED, "quantize: d=%d (64 or 128)", in->d);
   REQUIRE(out->fmt == FA4_MXFP4 || out->fmt == FA4_NVFP4 || out->fmt == FA4_FP8_TOKEN,
           FA4_ERR_UNSUPPORTED, "quantize: format %d", out->fmt);
-  REQUIRE((flags & ~(uint32_t)(FA4_HADAMARD128 | FA4_DUAL_RESIDUAL)) == 0, FA4_ERR_UNSUPPORTED,
+  REQUIRE((flags & ~(uint32_t)(FA4_HADAMARD128 | FA4_DUAL_RESIDUAL | FA4_SCALE_SEARCH)) == 0, FA4_ERR_UNSUPPORTED,
           "quantize: unknown flags 0x%x", flags);
+  if (flags & FA4_SCALE_SEARCH) {
+    REQUIRE(out->fmt == FA4_MXFP4 || out->fmt == FA4_NVFP4, FA4_ERR_UNSUPPORTED,
+            "quantize: scale search needs MXFP4 or NVFP4");
+    REQUIRE(!(flags & FA4_DUAL_RESIDUAL), FA4_ERR_UNSUPPORTED, "quantize: scale search with the dual residual");
+  }
+  REQUIRE(aligned(in->channel_scale, 4), FA4_ERR_ALIGN, "quantize: channel_scale must be 4-byte aligned");
   REQUIRE(in->outer >= 0 && in->heads >= 1 && in->rows >= 0, FA4_ERR_SHAPE,
           "quantize: outer=%lld heads=%d rows=%lld", (long long)in->outer, in->heads, (long long)in->rows);
   const int64_t groups = in->outer * in->heads;
@@ -167,6 +173,31 @@ fa4_status fa4_attn_fwd(const fa4_attn_args *a, void *stream) {
   for (const void *p : ptrs) REQUIRE(aligned(p, 16), FA4_ERR_ALIGN, "attn: every pointer must be 16-byte aligned");
   REQUIRE(a->softmax_scale > 0.0f, FA4_ERR_SHAPE, "attn: softmax_scale must be positive");
   return hip_status(fa4::launch_attn(a, (hipStream_t)stream), "attention launch");
+}
+
+fa4_status fa4_smoothing_factors(const fa4_qinput *q, const fa4_qinput *k, float *q_scale, float *k_scale,
+                                 void *stream) {
+  REQUIRE(q && k && q_scale && k_scale, FA4_ERR_NULL, "smoothing: a required pointer is NULL");
+  for (const fa4_qinput *in : {q, k}) {
+    REQUIRE(in->dtype == FA4_F32 || in->dtype == FA4_BF16, FA4_ERR_UNSUPPORTED, "smoothing: dtype %d", in->dtype);
+    REQUIRE(in->d == 64 || in->d == 128, FA4_ERR_UNSUPPORTED, "smoothing: d=%d (64 or 128)", in->d);
+    REQUIRE(in->outer >= 0 && in->heads >= 1 && in->rows >= 0, FA4_ERR_SHAPE, "smoothing: bad shape");
+    REQUIRE(in->outer * in->heads <= 65535, FA4_ERR_SHAPE, "smoothing: too many groups");
+    REQUIRE(in->rows <= (int64_t)1 << 31, FA4_ERR_SHAPE, "smoothing: rows=%lld", (long long)in->rows);
+    REQUIRE(in->page_table == nullptr, FA4_ERR_UNSUPPORTED, "smoothing: calibration input must be unpaged");
+    REQUIRE(in->rows == 0 || in->outer == 0 || in->x, FA4_ERR_NULL, "smoothing: x is NULL");
+    const int64_t epl = in->dtype == FA4_F32 ? 4 : 8;
+    REQUIRE(aligned(in->x, 16), FA4_ERR_ALIGN, "smoothing: x must be 16-byte aligned");
+    REQUIRE(in->stride_outer % epl == 0 && in->stride_head % epl == 0 && in->stride_row % epl == 0,
+            FA4_ERR_ALIGN, "smoothing: strides must be multiples of 16 bytes");
+    REQUIRE(in->stride_outer >= 0 && in->stride_head >= 0 && in->stride_row >= in->d, FA4_ERR_SHAPE,
+            "smoothing: strides must be non-negative and stride_row >= d");
+  }
+  REQUIRE(q->d == k->d, FA4_ERR_SHAPE, "smoothing: d differs (%d, %d)", q->d, k->d);
+  REQUIRE(q->heads % k->heads == 0, FA4_ERR_SHAPE, "smoothing: Hq=%d is not a multiple of Hkv=%d", q->heads,
+          k->heads);
+  REQUIRE(aligned(q_scale, 4) && aligned(k_scale, 4), FA4_ERR_ALIGN, "smoothing: outputs must be 4-byte aligned");
+  return hip_status(fa4::launch_smoothing(q, k, q_scale, k_scale, (hipStream_t)stream), "smoothing launch");
 }
 
 size_t fa4_decode_workspace_bytes(const fa4_decode_args *a) {

@@ -9,6 +9,8 @@ namespace fa4 {
 // Arguments have been validated by the caller.
 hipError_t launch_quantize(const fa4_qinput *in, uint32_t flags, const fa4_qoutput *out,
                            const fa4_qoutput *residual, float *row_norm2, hipStream_t s);
+hipError_t launch_smoothing(const fa4_qinput *q, const fa4_qinput *k, float *q_scale, float *k_scale,
+                            hipStream_t s);
 hipError_t launch_select(const float *qn, const float *kn, int B, int Hq, int Hkv, int Lq, int Lk,
                          int causal, int num, int den, uint8_t *bitmap, int32_t *counts, hipStream_t s);
 hipError_t launch_attn(const fa4_attn_args *a, hipStream_t s);

@@ -38,6 +38,7 @@ struct QArgs {
   float *rscales;       // residual (dual) tensor maxima / scales
   float *norm2;
   float *fold_w, *fold_scale;
+  const float *cscale;  // optional per-(head, channel) smoothing factors [heads][D]
 };
 
 // Elements per lane: one 16-byte load (8 bf16 or 4 float values).
@@ -171,6 +172,67 @@ __device__ __forceinline__ uint32_t nv_codes(const float v[E], float st, uint32_
   return c;
 }
 
+// Squared reconstruction error of a block, float64: per element (x - x^)^2, summed as a balanced binary
+// tree over the block's elements in index order (in-lane pairs first, then neighbouring lanes of the
+// block; a lane holds E consecutive elements). Contraction into FMAs is off, so every operation rounds
+// as written.
+template <int E>
+__device__ __forceinline__ double block_sse(const float v[E], const double xh[E], int lanes) {
+#pragma clang fp contract(off)
+  double t[E];
+#pragma unroll
+  for (int i = 0; i < E; i++) {
+    const double dlt = (double)v[i] - xh[i];
+    t[i] = dlt * dlt;
+  }
+#pragma unroll
+  for (int w = 1; w < E; w <<= 1)
+#pragma unroll
+    for (int i = 0; i < E; i += 2 * w) t[i] = t[i] + t[i + w];
+  double sum = t[0];
+  for (int m = 1; m < lanes; m <<= 1) sum = sum + shfl_xor_d(sum, m);
+  return sum;
+}
+
+// NVFP4 codes with the per-block scale search: E4M3 block-scale codes c0, c0 - 1, c0 + 1, c0 - 2 (those
+// in [1, 126]; c0 the round-to-nearest code), the first with the smallest squared error wins. A zero c0
+// keeps the zero scale.
+template <int E>
+__device__ __forceinline__ uint32_t nv_codes_search(const float v[E], float st, uint32_t *sb_out, double xh[E]) {
+  uint32_t sb;
+  uint32_t c = nv_codes<E>(v, st, &sb, xh);
+  if (sb == 0u) {
+    *sb_out = sb;
+    return c;
+  }
+  double best = block_sse<E>(v, xh, 16 / E);
+  const int cand[3] = {(int)sb - 1, (int)sb + 1, (int)sb - 2};
+  uint32_t best_sb = sb;
+#pragma unroll
+  for (int k = 0; k < 3; k++) {
+    const int cc = cand[k];
+    if (cc < 1 || cc > 126) continue;                      // uniform over the block's lanes
+    const float sbv = e4m3_value((uint32_t)cc);
+    const float denom = sbv * st;
+    float qv[E];
+    div_lane<E>(v, denom, qv);
+    const uint32_t c2 = e2m1_lane<E>(qv);
+    double xh2[E];
+#pragma unroll
+    for (int i = 0; i < E; i++) xh2[i] = (double)e2m1_value((c2 >> (4 * i)) & 15u) * (double)sbv * (double)st;
+    const double err = block_sse<E>(v, xh2, 16 / E);
+    if (err < best) {
+      best = err;
+      best_sb = (uint32_t)cc;
+      c = c2;
+#pragma unroll
+      for (int i = 0; i < E; i++) xh[i] = xh2[i];
+    }
+  }
+  *sb_out = best_sb;
+  return c;
+}
+
 __device__ __forceinline__ float tensor_scale_from_max(float amax) {
   return amax == 0.0f ? 1.0f : amax / 2688.0f;
 }
@@ -184,7 +246,8 @@ __device__ __forceinline__ void store_nibbles(uint8_t *p, uint32_t c) {
 
 // PASS: 0 = group maxima (NVFP4), 1 = codes (+ residual maxima when DUAL), 2 = residual codes.
 // PAGED: rows go to a paged cache through the page table (then NORM is false).
-template <int D, int DT, int FMT, int PASS, bool HAD, bool DUAL, bool NORM, bool PAGED>
+// SEARCH: the per-block scale search (MXFP4, NVFP4 codes pass; not with DUAL).
+template <int D, int DT, int FMT, int PASS, bool HAD, bool DUAL, bool NORM, bool PAGED, bool SEARCH>
 __global__ void __launch_bounds__(QUANT_THREADS) quantize_kernel(QArgs a) {
   constexpr int E = Epl<DT>::value;       // elements per lane
   constexpr int LPR = D / E;              // lanes per row
@@ -213,6 +276,13 @@ __global__ void __launch_bounds__(QUANT_THREADS) quantize_kernel(QArgs a) {
   // read nothing), so the lane-group shuffles below always see all their lanes.
   constexpr int NIT = QUANT_CHUNK / RPB;
   float vin[NIT][E];
+  // static smoothing: this lane's E channels of head h, multiplied in after the row norms
+  float csm[E];
+  const bool smooth = a.cscale != nullptr;                // uniform
+  if (smooth) {
+#pragma unroll
+    for (int i = 0; i < E; i++) csm[i] = a.cscale[(int64_t)h * D + li * E + i];
+  }
 #pragma unroll
   for (int it = 0; it < NIT; it++) {
     const int64_t rr = r0 + it * RPB + wave * RPW + sub;
@@ -241,6 +311,10 @@ __global__ void __launch_bounds__(QUANT_THREADS) quantize_kernel(QArgs a) {
       for (int m = 1; m < LPR; m <<= 1) s = s + shfl_xor_d(s, m);
       if (active && li == 0) a.norm2[(int64_t)g * a.rows + rr] = (float)s;
     }
+    if (smooth) {
+#pragma unroll
+      for (int i = 0; i < E; i++) v[i] *= csm[i];
+    }
     if (HAD) hadamard128<E>(v);
     int64_t orow = (int64_t)g * a.rows + rr;
     bool store = active;
@@ -252,12 +326,32 @@ __global__ void __launch_bounds__(QUANT_THREADS) quantize_kernel(QArgs a) {
     }
     if (FMT == FA4_MXFP4) {
       const float am = group_max(lane_amax<E>(v), 32 / E);      // 32-element block = 32/E lanes
-      const int e = mx_exponent(am);
+      int e = mx_exponent(am);
       const float mul = pow2_neg(e);
       float sv[E];
 #pragma unroll
       for (int i = 0; i < E; i++) sv[i] = v[i] * mul;          // exact (a power of two)
-      const uint32_t c = e2m1_lane<E>(sv);
+      uint32_t c = e2m1_lane<E>(sv);
+      if (SEARCH && e > -127) {
+        // candidates e (round to nearest) and e - 1 (clips at 6 * 2^(e-1), finer elsewhere)
+        double xh0[E], xh1[E];
+        float sv1[E];
+#pragma unroll
+        for (int i = 0; i < E; i++) sv1[i] = sv[i] * 2.0f;     // exact
+        const uint32_t c1 = e2m1_lane<E>(sv1);
+#pragma unroll
+        for (int i = 0; i < E; i++) {
+          xh0[i] = __builtin_ldexp((double)e2m1_value((c >> (4 * i)) & 15u), e);
+          xh1[i] = __builtin_ldexp((double)e2m1_value((c1 >> (4 * i)) & 15u), e - 1);
+        }
+        const double err0 = block_sse<E>(v, xh0, 32 / E), err1 = block_sse<E>(v, xh1, 32 / E);
+        if (err1 < err0) {                                      // uniform over the block's lanes
+          e -= 1;
+          c = c1;
+#pragma unroll
+          for (int i = 0; i < E; i++) sv[i] = sv1[i];
+        }
+      }
       if (store) {
         store_nibbles<E>(a.codes + orow * (D / 2) + li * (E / 2), c);
         if ((li % (32 / E)) == 0) a.bscales[orow * (D / 32) + li / (32 / E)] = (uint8_t)(e + 127);
@@ -300,7 +394,7 @@ __global__ void __launch_bounds__(QUANT_THREADS) quantize_kernel(QArgs a) {
       } else {
         uint32_t sb;
         double xh[E];
-        const uint32_t c = nv_codes<E>(v, st, &sb, xh);
+        const uint32_t c = SEARCH ? nv_codes_search<E>(v, st, &sb, xh) : nv_codes<E>(v, st, &sb, xh);
         if (PASS == 1) {
           if (store) {
             store_nibbles<E>(a.codes + orow * (D / 2) + li * (E / 2), c);
@@ -355,7 +449,7 @@ __device__ __forceinline__ float block_max(float v, float *red) {
 // NVFP4 of groups small enough for one workgroup (at most QUANT_CHUNK rows, unpaged): the tensor
 // maximum, the codes and, with DUAL, the residual's maximum and codes in one launch (one workgroup per
 // group). Same arithmetic as the multi-pass path: the maxima are the same maxima, reduced in LDS.
-template <int D, int DT, bool DUAL>
+template <int D, int DT, bool DUAL, bool SEARCH>
 __global__ void __launch_bounds__(QUANT_THREADS) nv_group_kernel(QArgs a) {
   constexpr int E = Epl<DT>::value;
   constexpr int LPR = D / E;
@@ -378,6 +472,10 @@ __global__ void __launch_bounds__(QUANT_THREADS) nv_group_kernel(QArgs a) {
 #pragma unroll
     for (int i = 0; i < E; i++) vin[it][i] = 0.0f;
     if (rr < nrows) load_lane<DT, E>(a.x, o * a.so + h * a.sh + rr * a.sr + li * E, vin[it]);
+    if (a.cscale) {                                         // static smoothing (uniform)
+#pragma unroll
+      for (int i = 0; i < E; i++) vin[it][i] *= a.cscale[(int64_t)h * D + li * E + i];
+    }
     gmax = fmaxf(gmax, lane_amax<E>(vin[it]));            // inactive rows hold zeros
   }
   const float st = tensor_scale_from_max(block_max(gmax, red0));
@@ -390,7 +488,7 @@ __global__ void __launch_bounds__(QUANT_THREADS) nv_group_kernel(QArgs a) {
     const int64_t orow = (int64_t)g * a.rows + rr;
     uint32_t sb;
     double xh[E];
-    const uint32_t c = nv_codes<E>(vin[it], st, &sb, xh);
+    const uint32_t c = SEARCH ? nv_codes_search<E>(vin[it], st, &sb, xh) : nv_codes<E>(vin[it], st, &sb, xh);
     if (active) {
       store_nibbles<E>(a.codes + orow * (D / 2) + li * (E / 2), c);
       if ((li % (16 / E)) == 0) a.bscales[orow * (D / 16) + li / (16 / E)] = (uint8_t)sb;
@@ -461,24 +559,30 @@ __global__ void finalize_tensor_scale_kernel(float *p, int64_t n) {
   if (i < n) p[i] = tensor_scale_from_max(p[i]);
 }
 
-template <int D, int DT, int FMT, int PASS, bool HAD, bool DUAL>
+template <int D, int DT, int FMT, int PASS, bool HAD, bool DUAL, bool SEARCH = false>
 static hipError_t launch_q(const QArgs &a, int64_t groups, bool norm, hipStream_t s) {
   if (a.rows == 0 || groups == 0) return hipSuccess;       // nothing to read (NVFP4 scales still finalize)
   dim3 grid((unsigned)((a.rows + QUANT_CHUNK - 1) / QUANT_CHUNK), (unsigned)groups);
   if (a.page_table)                                        // row norms are only written unpaged
-    hipLaunchKernelGGL((quantize_kernel<D, DT, FMT, PASS, HAD, DUAL, false, true>), grid, dim3(QUANT_THREADS), 0, s, a);
+    hipLaunchKernelGGL((quantize_kernel<D, DT, FMT, PASS, HAD, DUAL, false, true, SEARCH>), grid, dim3(QUANT_THREADS),
+                       0, s, a);
   else if (norm)
-    hipLaunchKernelGGL((quantize_kernel<D, DT, FMT, PASS, HAD, DUAL, true, false>), grid, dim3(QUANT_THREADS), 0, s, a);
+    hipLaunchKernelGGL((quantize_kernel<D, DT, FMT, PASS, HAD, DUAL, true, false, SEARCH>), grid, dim3(QUANT_THREADS),
+                       0, s, a);
   else
-    hipLaunchKernelGGL((quantize_kernel<D, DT, FMT, PASS, HAD, DUAL, false, false>), grid, dim3(QUANT_THREADS), 0, s, a);
+    hipLaunchKernelGGL((quantize_kernel<D, DT, FMT, PASS, HAD, DUAL, false, false, SEARCH>), grid, dim3(QUANT_THREADS),
+                       0, s, a);
   return hipGetLastError();
 }
 
 template <int D, int DT>
-static hipError_t quantize_dispatch(const QArgs &a, int fmt, bool had, bool dual, int64_t groups,
+static hipError_t quantize_dispatch(const QArgs &a, int fmt, bool had, bool dual, bool search, int64_t groups,
                                     bool norm, hipStream_t s) {
   hipError_t e = hipSuccess;
   const unsigned small = (unsigned)((groups + 255) / 256);
+  if (fmt == FA4_MXFP4 && search)            // (the scale search is never combined with the dual residual)
+    return had ? launch_q<D, DT, FA4_MXFP4, 1, true, false, true>(a, groups, norm, s)
+               : launch_q<D, DT, FA4_MXFP4, 1, false, false, true>(a, groups, norm, s);
   if (fmt == FA4_MXFP4) {                    // one pass (the residual needs no tensor scale)
     if (dual) return had ? launch_q<D, DT, FA4_MXFP4, 1, true, true>(a, groups, norm, s)
                          : launch_q<D, DT, FA4_MXFP4, 1, false, true>(a, groups, norm, s);
@@ -496,8 +600,9 @@ static hipError_t quantize_dispatch(const QArgs &a, int fmt, bool had, bool dual
   }
   // NVFP4, groups that fit one workgroup: a single launch
   if (!had && !norm && !a.page_table && a.rows <= QUANT_CHUNK) {
-    if (dual) hipLaunchKernelGGL((nv_group_kernel<D, DT, true>), dim3((unsigned)groups), dim3(QUANT_THREADS), 0, s, a);
-    else hipLaunchKernelGGL((nv_group_kernel<D, DT, false>), dim3((unsigned)groups), dim3(QUANT_THREADS), 0, s, a);
+    if (dual) hipLaunchKernelGGL((nv_group_kernel<D, DT, true, false>), dim3((unsigned)groups), dim3(QUANT_THREADS), 0, s, a);
+    else if (search) hipLaunchKernelGGL((nv_group_kernel<D, DT, false, true>), dim3((unsigned)groups), dim3(QUANT_THREADS), 0, s, a);
+    else hipLaunchKernelGGL((nv_group_kernel<D, DT, false, false>), dim3((unsigned)groups), dim3(QUANT_THREADS), 0, s, a);
     return hipGetLastError();
   }
   // NVFP4: zero the group maxima, reduce them, quantize, turn maxima into tensor scales
@@ -509,7 +614,8 @@ static hipError_t quantize_dispatch(const QArgs &a, int fmt, bool had, bool dual
     if (dual) {
       if ((e = launch_q<D, DT, FA4_NVFP4, 1, true, true>(a, groups, false, s)) != hipSuccess) return e;
       if ((e = launch_q<D, DT, FA4_NVFP4, 2, true, true>(a, groups, false, s)) != hipSuccess) return e;
-    } else if ((e = launch_q<D, DT, FA4_NVFP4, 1, true, false>(a, groups, false, s)) != hipSuccess) {
+    } else if ((e = search ? launch_q<D, DT, FA4_NVFP4, 1, true, false, true>(a, groups, false, s)
+                           : launch_q<D, DT, FA4_NVFP4, 1, true, false>(a, groups, false, s)) != hipSuccess) {
       return e;
     }
   } else {
@@ -517,12 +623,114 @@ static hipError_t quantize_dispatch(const QArgs &a, int fmt, bool had, bool dual
     if (dual) {
       if ((e = launch_q<D, DT, FA4_NVFP4, 1, false, true>(a, groups, false, s)) != hipSuccess) return e;
       if ((e = launch_q<D, DT, FA4_NVFP4, 2, false, true>(a, groups, false, s)) != hipSuccess) return e;
-    } else if ((e = launch_q<D, DT, FA4_NVFP4, 1, false, false>(a, groups, false, s)) != hipSuccess) {
+    } else if ((e = search ? launch_q<D, DT, FA4_NVFP4, 1, false, false, true>(a, groups, false, s)
+                           : launch_q<D, DT, FA4_NVFP4, 1, false, false>(a, groups, false, s)) != hipSuccess) {
       return e;
     }
   }
   hipLaunchKernelGGL(finalize_tensor_scale_kernel, dim3(small), dim3(256), 0, s, a.scales, groups);
   if (dual) hipLaunchKernelGGL(finalize_tensor_scale_kernel, dim3(small), dim3(256), 0, s, a.rscales, groups);
+  return hipGetLastError();
+}
+
+// ---- static smoothing factors from calibration tensors
+
+// Per (head, channel) maximum |x| over a tensor's rows, published with atomicMax on the float bits into
+// amax [heads][D] (zeroed beforehand; non-negative floats order like their bit patterns).
+template <int D, int DT>
+__global__ void __launch_bounds__(QUANT_THREADS) channel_amax_kernel(QArgs a, float *amax) {
+  constexpr int E = Epl<DT>::value;
+  constexpr int LPR = D / E;
+  constexpr int RPW = 64 / LPR;
+  constexpr int RPB = RPW * (QUANT_THREADS / 64);
+  constexpr int NIT = QUANT_CHUNK / RPB;
+  const int g = blockIdx.y;
+  const int64_t o = g / a.heads;
+  const int h = g - (int)o * a.heads;
+  int64_t nrows = a.rows;
+  if (a.row_counts) nrows = min<int64_t>(nrows, (int64_t)a.row_counts[o]);
+  const int64_t r0 = (int64_t)blockIdx.x * QUANT_CHUNK;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane / LPR, li = lane % LPR;
+  float m[E];
+#pragma unroll
+  for (int i = 0; i < E; i++) m[i] = 0.0f;
+#pragma unroll
+  for (int it = 0; it < NIT; it++) {
+    const int64_t rr = r0 + it * RPB + wave * RPW + sub;
+    if (rr < nrows) {
+      float v[E];
+      load_lane<DT, E>(a.x, o * a.so + h * a.sh + rr * a.sr + li * E, v);
+#pragma unroll
+      for (int i = 0; i < E; i++) m[i] = fmaxf(m[i], fabsf(v[i]));
+    }
+  }
+  // lanes li, li + LPR, ... of a wave hold the same channels
+#pragma unroll
+  for (int i = 0; i < E; i++)
+    for (int msk = LPR; msk < 64; msk <<= 1) m[i] = fmaxf(m[i], shfl_xor_f(m[i], msk));
+  if (sub == 0) {
+#pragma unroll
+    for (int i = 0; i < E; i++)
+      atomicMax(reinterpret_cast<unsigned int *>(amax + (int64_t)h * D + li * E + i), __float_as_uint(m[i]));
+  }
+}
+
+// Smoothing exponent per (key head, channel): k = floor((e_K - e_Q + 1) / 2) with e = floor(log2 amax)
+// (amax_Q over the query heads of the group), clamped to [-20, 20], 0 when either maximum is zero.
+// Writes k_scale = 2^-k and q_scale = 2^k for every query head of the group, in place of the maxima.
+__global__ void smoothing_kernel(float *q_scale, float *k_scale, int Hkv, int group, int d) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= Hkv * d) return;
+  const int kvh = i / d, c = i - kvh * d;
+  float aq = 0.0f;
+  for (int j = 0; j < group; j++) aq = fmaxf(aq, q_scale[(int64_t)(kvh * group + j) * d + c]);
+  const float ak = k_scale[i];
+  int k = 0;
+  if (aq > 0.0f && ak > 0.0f) {
+    int eq, ek;
+    frexpf(aq, &eq);
+    frexpf(ak, &ek);
+    k = (ek - eq + 1) >> 1;                // floor division by 2 (arithmetic shift)
+    k = k < -20 ? -20 : (k > 20 ? 20 : k);
+  }
+  k_scale[i] = __builtin_ldexpf(1.0f, -k);
+  for (int j = 0; j < group; j++) q_scale[(int64_t)(kvh * group + j) * d + c] = __builtin_ldexpf(1.0f, k);
+}
+
+static QArgs input_args(const fa4_qinput *in) {
+  QArgs a = {};
+  a.x = in->x; a.outer = in->outer; a.rows = in->rows; a.heads = in->heads;
+  a.so = in->stride_outer; a.sh = in->stride_head; a.sr = in->stride_row;
+  a.row_counts = in->row_counts;
+  return a;
+}
+
+template <int D, int DT>
+static hipError_t launch_amax(const fa4_qinput *in, float *amax, hipStream_t s) {
+  const int64_t groups = in->outer * in->heads;
+  const unsigned n = (unsigned)(in->heads * D);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((n + 255) / 256), dim3(256), 0, s, amax, (int64_t)n);
+  if (in->rows > 0 && groups > 0) {
+    dim3 grid((unsigned)((in->rows + QUANT_CHUNK - 1) / QUANT_CHUNK), (unsigned)groups);
+    hipLaunchKernelGGL((channel_amax_kernel<D, DT>), grid, dim3(QUANT_THREADS), 0, s, input_args(in), amax);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_smoothing(const fa4_qinput *q, const fa4_qinput *k, float *q_scale, float *k_scale,
+                            hipStream_t s) {
+  hipError_t e;
+  for (int t = 0; t < 2; t++) {
+    const fa4_qinput *in = t == 0 ? q : k;
+    float *out = t == 0 ? q_scale : k_scale;
+    if (in->d == 128) e = in->dtype == FA4_F32 ? launch_amax<128, 0>(in, out, s) : launch_amax<128, 1>(in, out, s);
+    else e = in->dtype == FA4_F32 ? launch_amax<64, 0>(in, out, s) : launch_amax<64, 1>(in, out, s);
+    if (e != hipSuccess) return e;
+  }
+  const int n = k->heads * k->d;
+  hipLaunchKernelGGL(smoothing_kernel, dim3((n + 255) / 256), dim3(256), 0, s, q_scale, k_scale, k->heads,
+                     q->heads / k->heads, k->d);
   return hipGetLastError();
 }
 
@@ -538,14 +746,16 @@ hipError_t launch_quantize(const fa4_qinput *in, uint32_t flags, const fa4_qoutp
   a.rscales = res ? res->scales : nullptr;
   a.norm2 = norm2;
   a.fold_w = out->fold_w; a.fold_scale = out->fold_scale;
+  a.cscale = in->channel_scale;
   const int64_t groups = in->outer * in->heads;
   const bool had = flags & FA4_HADAMARD128, dual = flags & FA4_DUAL_RESIDUAL, norm = norm2 != nullptr;
+  const bool search = flags & FA4_SCALE_SEARCH;
   if (in->d == 128) {
-    return in->dtype == FA4_F32 ? quantize_dispatch<128, 0>(a, out->fmt, had, dual, groups, norm, s)
-                                : quantize_dispatch<128, 1>(a, out->fmt, had, dual, groups, norm, s);
+    return in->dtype == FA4_F32 ? quantize_dispatch<128, 0>(a, out->fmt, had, dual, search, groups, norm, s)
+                                : quantize_dispatch<128, 1>(a, out->fmt, had, dual, search, groups, norm, s);
   }
-  return in->dtype == FA4_F32 ? quantize_dispatch<64, 0>(a, out->fmt, false, dual, groups, norm, s)
-                              : quantize_dispatch<64, 1>(a, out->fmt, false, dual, groups, norm, s);
+  return in->dtype == FA4_F32 ? quantize_dispatch<64, 0>(a, out->fmt, false, dual, search, groups, norm, s)
+                              : quantize_dispatch<64, 1>(a, out->fmt, false, dual, search, groups, norm, s);
 }
 
 }  // namespace fa4

@@ -43,7 +43,7 @@ typedef enum {
 
 enum { FA4_F32 = 0, FA4_BF16 = 1 };                      /* input element types       */
 enum { FA4_MXFP4 = 0, FA4_NVFP4 = 1, FA4_FP8_TOKEN = 2 }; /* quantized formats         */
-enum { FA4_HADAMARD128 = 1u << 0, FA4_DUAL_RESIDUAL = 1u << 1 }; /* quantizer flags    */
+enum { FA4_HADAMARD128 = 1u << 0, FA4_DUAL_RESIDUAL = 1u << 1, FA4_SCALE_SEARCH = 1u << 2 }; /* quantizer flags */
 
 /* ------------------------------------------------------------------------------------------------
  * Quantization.
@@ -76,6 +76,17 @@ enum { FA4_HADAMARD128 = 1u << 0, FA4_DUAL_RESIDUAL = 1u << 1 }; /* quantizer fl
  *        FA4_DUAL_RESIDUAL (NVFP4 or MXFP4): `out` receives Q1 = F(x) and `residual` receives
  *        Q2 = F(float32(x - dequant(Q1))) in the same format F (`residual->fmt` must equal
  *        `out->fmt`); NVFP4 residuals get their own tensor scales, MXFP4 ones need none.
+ *        FA4_SCALE_SEARCH (MXFP4 or NVFP4, not with FA4_DUAL_RESIDUAL): per-block scale search
+ *        ("BitDecoding-FP4", outlier-aware key quantization). Candidates: MXFP4 exponents e, e - 1;
+ *        NVFP4 E4M3 block-scale codes c, c - 1, c + 1, c - 2 within [1, 126] (e, c: the round-to-
+ *        nearest scales above; the NVFP4 tensor scale is not searched, a zero c is kept). Each is
+ *        scored by the block's squared error sum (x - x^)^2 in float64, summed as a balanced binary
+ *        tree over the block's elements in index order; the first candidate in the listed order with
+ *        the smallest error wins.
+ * channel_scale (optional, [heads][d] float): static smoothing. Element c of a row of head h is
+ *        multiplied by channel_scale[h * d + c] (float32 product) before rotation and quantization
+ *        (row_norm2 still describes the unscaled rows). fa4_smoothing_factors produces power-of-two
+ *        factors, for which the products are exact.
  * fold_w / fold_scale (FP8_TOKEN, optional, unpaged, rows a multiple of 128): the data that folds the
  *        per-token V scale into the attention probabilities. For each 128-row tile j of a group,
  *        fold_scale[j] = 2^e (a float), e = the smallest integer with 448 * 2^e >= max of the tile's
@@ -100,6 +111,7 @@ typedef struct {
   const int32_t *page_table;   /* optional [outer][max_pages]                                     */
   int32_t page_size, max_pages;
   int64_t num_pages;           /* pages in the output cache (paged output only)                   */
+  const float *channel_scale;  /* optional [heads][d] static smoothing factors                    */
 } fa4_qinput;
 
 typedef struct {
@@ -113,6 +125,21 @@ typedef struct {
 
 fa4_status fa4_quantize_blockscaled(const fa4_qinput *in, uint32_t flags, const fa4_qoutput *out,
                                     const fa4_qoutput *residual, float *row_norm2, void *stream);
+
+/* Static smoothing factors for outlier-aware key quantization.
+ *
+ * Source page: "BitDecoding-FP4" (sns.style digest): static smoothing, with the Hadamard rotation and
+ * the scale search, spreads key outliers before FP4 quantization.
+ * From calibration tensors q (heads Hq) and k (heads Hkv, Hq % Hkv == 0, same d; layouts as
+ * fa4_qinput, unpaged; channel_scale ignored): amax_K[kv][c] = max |k| over outer and rows of key
+ * head kv; amax_Q[kv][c] = max |q| over outer, rows and the query heads kv*G .. kv*G+G-1 (G = Hq/Hkv).
+ * With e = floor(log2 amax): k = floor((e_K - e_Q + 1) / 2), clamped to [-20, 20], and k = 0 when either
+ * maximum is zero. Output: k_scale [Hkv][d] = 2^-k, q_scale [Hq][d] = 2^k (the same for the heads of
+ * a group), to be passed as channel_scale when quantizing K and Q: QK^T is unchanged (exact products).
+ * Requirements as fa4_quantize_blockscaled's input (alignment, d in {64, 128}); outputs 4-byte aligned.
+ */
+fa4_status fa4_smoothing_factors(const fa4_qinput *q_calib, const fa4_qinput *k_calib, float *q_scale,
+                                 float *k_scale, void *stream);
 
 /* ------------------------------------------------------------------------------------------------
  * Tile selection.

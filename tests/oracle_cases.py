@@ -9,6 +9,8 @@ import numpy as np
 import workloads as W
 from oracle import attention as A
 from oracle import decode as Dd
+from oracle import formats as F
+from oracle import outlier as OA
 from oracle import quant as Q
 from oracle import selection as S
 
@@ -31,18 +33,23 @@ def assert_parity(got, ref, what=""):
     return rel, mx
 
 
-def quant_head(cfg, x, rotate):
-    """Dequantized Q or K values of one head ([L, d] float64) under the workload's Q/K format."""
+def quant_head(cfg, x, rotate, scale=None, search=False):
+    """Dequantized Q or K values of one head ([L, d] float64) under the workload's Q/K format.
+    scale: optional per-channel smoothing factors [d] (float32 products); search: per-block scale search."""
+    if scale is not None:
+        x = F.fp32(x * np.asarray(scale, np.float64)).astype(np.float64)
     xr = Q.hadamard_rotate(x) if rotate else x
     if cfg.qk_fmt == "mxfp4":
-        return Q.mxfp4_dequantize(*Q.mxfp4_quantize(xr))
-    return Q.nvfp4_dequantize(*Q.nvfp4_quantize(xr[None]))[0]
+        return Q.mxfp4_dequantize(*(OA.mxfp4_quantize_search(xr) if search else Q.mxfp4_quantize(xr)))
+    return Q.nvfp4_dequantize(*(OA.nvfp4_quantize_search(xr[None]) if search else Q.nvfp4_quantize(xr[None])))[0]
 
 
-def prefill_reference(cfg, seed, heads, rows, select=None, q_all=None, k_all=None, v_all=None):
+def prefill_reference(cfg, seed, heads, rows, select=None, q_all=None, k_all=None, v_all=None, smooth=None,
+                      search=False):
     """Oracle O and LSE for the listed (b, h) pairs and query rows.
 
     select = (num, den) enables tile selection (norms, tile maxima and top-k from the oracle).
+    smooth = (q_scale [Hq, d], k_scale [Hkv, d]) static smoothing factors; search: K's scale search.
     q_all/k_all/v_all: optional host tensors already generated (else chunks are regenerated).
     Returns (O [len(heads), R, d], LSE [len(heads), R], bitmaps {(b, h): [nq, nk]}).
     """
@@ -56,12 +63,12 @@ def prefill_reference(cfg, seed, heads, rows, select=None, q_all=None, k_all=Non
         if (b, kvh) not in kv_cache:
             k = (k_all[b, kvh] if k_all is not None else W.prefill_head(cfg, W.T_K, b, kvh, seed)).double().numpy()
             v = (v_all[b, kvh] if v_all is not None else W.prefill_head(cfg, W.T_V, b, kvh, seed)).double().numpy()
-            kd = quant_head(cfg, k, cfg.hadamard)
+            kd = quant_head(cfg, k, cfg.hadamard, None if smooth is None else smooth[1][kvh], search)
             vc, sv = Q.fp8_per_token_quantize(v)
             kn = Q.row_norm2(k)
             kv_cache = {(b, kvh): (k, v, kd, vc, sv, kn)}
         k, v, kd, vc, sv, kn = kv_cache[(b, kvh)]
-        qd = quant_head(cfg, q, cfg.hadamard)
+        qd = quant_head(cfg, q, cfg.hadamard, None if smooth is None else smooth[0][h])
         bm = None
         if select is not None:
             qn = Q.row_norm2(q)

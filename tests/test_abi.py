@@ -57,7 +57,7 @@ def test_status_strings():
 def _q(**kw):
     base = dict(x=16, dtype=fa4.FA4_BF16, d=128, outer=1, heads=2, rows=256, stride_outer=2 * 256 * 128,
                 stride_head=256 * 128, stride_row=128, row_counts=None, page_table=None, page_size=0,
-                max_pages=0, num_pages=0)
+                max_pages=0, num_pages=0, channel_scale=None)
     base.update(kw)
     return fa4.QInput(*[base[f] for f, _ in fa4.QInput._fields_])
 
@@ -89,6 +89,9 @@ def test_quantize_rejects_before_launch():
     res = fa4.QOutput(fa4.FA4_MXFP4, 264, 256, None)                                     # MXFP4: no scales
     assert _call_q(_q(), flags=fa4.FA4_DUAL_RESIDUAL, res=res) == fa4.FA4_ERR_ALIGN
     assert _call_q(_q(), flags=1 << 5) == fa4.FA4_ERR_UNSUPPORTED
+    assert _call_q(_q(), fmt=fa4.FA4_FP8_TOKEN, flags=fa4.FA4_SCALE_SEARCH) == fa4.FA4_ERR_UNSUPPORTED
+    assert _call_q(_q(), flags=fa4.FA4_SCALE_SEARCH | fa4.FA4_DUAL_RESIDUAL) == fa4.FA4_ERR_UNSUPPORTED
+    assert _call_q(_q(channel_scale=258)) == fa4.FA4_ERR_ALIGN
     assert _call_q(_q(outer=70000)) == fa4.FA4_ERR_SHAPE
     assert _call_q(_q(page_table=64, page_size=64, max_pages=2, num_pages=4)) == fa4.FA4_ERR_SHAPE  # rows > 128
     assert b"rows=256" in fa4.lib.fa4_last_error()
@@ -100,6 +103,19 @@ def test_quantize_rejects_before_launch():
         == fa4.FA4_ERR_UNSUPPORTED
     assert _call_q(_q(rows=0)) == fa4.FA4_OK                # nothing to do, no launch
     assert fa4.lib.fa4_last_error() == b""
+
+
+def test_smoothing_rejects_before_launch():
+    f = lambda q, k, qs=256, ks=256: fa4.lib.fa4_smoothing_factors(ctypes.byref(q), ctypes.byref(k), qs, ks, None)
+    q, k = _q(heads=8), _q(heads=2)
+    assert fa4.lib.fa4_smoothing_factors(None, ctypes.byref(k), 256, 256, None) == fa4.FA4_ERR_NULL
+    assert f(q, k, qs=None) == fa4.FA4_ERR_NULL
+    assert f(_q(heads=7), k) == fa4.FA4_ERR_SHAPE                    # Hq not a multiple of Hkv
+    assert f(q, _q(heads=2, d=64, stride_row=64)) == fa4.FA4_ERR_SHAPE   # d differs
+    assert f(q, _q(heads=2, page_table=64, page_size=64, max_pages=4, num_pages=4)) == fa4.FA4_ERR_UNSUPPORTED
+    assert f(q, _q(heads=2, x=24)) == fa4.FA4_ERR_ALIGN
+    assert f(q, k, ks=258) == fa4.FA4_ERR_ALIGN
+    assert f(_q(heads=8, dtype=5), k) == fa4.FA4_ERR_UNSUPPORTED
 
 
 def _attn(**kw):
