@@ -80,6 +80,49 @@ def mxfp4_dequantize(codes, scales):
     return (v * s[..., None]).reshape(c.shape)
 
 
+# ----------------------------------------------------------------------------- MXFP8
+
+def mx8_scale_exponent(amax):
+    """Smallest integer e with 448 * 2^e >= amax, clamped to [-127, 127]; -127 for amax == 0.
+
+    Closed form: with amax = f * 2^E, f in [0.5, 1), 448 * 2^e >= amax holds for
+    e >= E + log2(f / 448); 448 = 0.875 * 2^9, so e = E - 9 when f <= 0.875 and
+    e = E - 8 otherwise. (The tests check it against the definition by search.)
+    """
+    amax = np.asarray(amax, dtype=np.float64)
+    f, E = np.frexp(amax)
+    e = np.where(f <= 0.875, E - 9, E - 8)
+    e = np.where(amax == 0, -127, e)
+    return np.clip(e, -127, 127).astype(np.int64)
+
+
+def mxfp8_quantize(x):
+    """MXFP8 (E4M3 elements) of the last axis of x (length a multiple of 32).
+
+    "MXFP vs NVFP4" (tqpw.cn 81738) section 2.1 (the MX family: 32-element blocks with an E8M0
+    scale, FP8 E4M3 elements) and section 4.2 (Q and K in MXFP8). Reading, as for MXFP4: the scale is
+    the smallest power of two 2^e with 448 * 2^e >= amax (nothing saturates); codes = E4M3(x * 2^-e)
+    (the scaling is exact), round to nearest even.
+    Returns (codes [..., d] uint8, scales [..., d/32] uint8 E8M0).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    assert d % MX_BLOCK == 0
+    blocks = x.reshape(x.shape[:-1] + (d // MX_BLOCK, MX_BLOCK))
+    e = mx8_scale_exponent(np.max(np.abs(blocks), axis=-1))
+    codes = e4m3_encode(blocks * np.ldexp(1.0, -e)[..., None]).reshape(x.shape)
+    return codes.astype(np.uint8), (e + 127).astype(np.uint8)
+
+
+def mxfp8_dequantize(codes, scales):
+    """value = E4M3(code) * 2^(scale-127), float64."""
+    c = np.asarray(codes)
+    d = c.shape[-1]
+    v = e4m3_decode(c).reshape(c.shape[:-1] + (d // MX_BLOCK, MX_BLOCK))
+    s = np.ldexp(1.0, np.asarray(scales, dtype=np.int64) - 127)
+    return (v * s[..., None]).reshape(c.shape)
+
+
 # ----------------------------------------------------------------------------- NVFP4
 
 def nvfp4_quantize(x):

@@ -41,6 +41,8 @@ def quant_head(cfg, x, rotate, scale=None, search=False):
     xr = Q.hadamard_rotate(x) if rotate else x
     if cfg.qk_fmt == "mxfp4":
         return Q.mxfp4_dequantize(*(OA.mxfp4_quantize_search(xr) if search else Q.mxfp4_quantize(xr)))
+    if cfg.qk_fmt == "mxfp8":
+        return Q.mxfp8_dequantize(*Q.mxfp8_quantize(xr))
     return Q.nvfp4_dequantize(*(OA.nvfp4_quantize_search(xr[None]) if search else Q.nvfp4_quantize(xr[None])))[0]
 
 

@@ -188,3 +188,40 @@ def test_zero_and_tiny_blocks_are_defined():
     v = np.full((1, 64), 1e-42, dtype=np.float32)
     c, s = Q.mxfp4_quantize(v)
     assert not np.any(np.isnan(Q.mxfp4_dequantize(c, s)))
+
+
+def test_mx8_exponent_closed_form_vs_definition():
+    """e(amax) == the smallest e with 448 * 2^e >= amax, over every float32 exponent and many mantissas."""
+    rng = np.random.default_rng(1)
+    amax = []
+    for E in range(-149, 128):
+        for m in list(rng.integers(0, 1 << 23, 32)) + [0, 1, 0x600000, 0x5FFFFF, 0x600001, (1 << 23) - 1]:
+            v = np.ldexp(1.0 + m / 2.0 ** 23, E) if E >= -126 else np.ldexp(float(m), -149)
+            if 0 < v < 3.4e38:
+                amax.append(v)
+    amax = np.array(amax, dtype=np.float32).astype(np.float64)
+    got = Q.mx8_scale_exponent(amax)
+    for a, e in zip(amax[::7], got[::7]):
+        want = -127
+        while 448.0 * 2.0 ** want < a and want < 127:
+            want += 1
+        assert e == want, (a, e, want)
+    assert Q.mx8_scale_exponent(np.array([0.0]))[0] == -127
+
+
+def test_mxfp8_codes_are_torch_e4m3_of_the_scaled_block():
+    """Codes equal torch's float8_e4m3fn cast of x * 2^-e (a library routine, RNE), and every block's
+    largest magnitude lands in (224, 448] (the top binade), so nothing saturates."""
+    rng = np.random.default_rng(2)
+    x = (rng.standard_normal((64, 128)) * np.exp2(rng.integers(-40, 40, (64, 4)).repeat(32, 1))).astype(np.float32)
+    x[0, :32] = 0.0
+    codes, scales = Q.mxfp8_quantize(x)
+    e = scales.astype(np.int64) - 127
+    scaled = x.astype(np.float64) * np.ldexp(1.0, -e).repeat(32, axis=1)
+    ref = torch.from_numpy(scaled.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes, ref)
+    am = np.abs(scaled).reshape(64, 4, 32).max(-1)
+    assert np.all((am[am > 0] > 224) & (am[am > 0] <= 448)) and scales[0, 0] == 0
+    back = Q.mxfp8_dequantize(codes, scales)
+    rel = np.abs(back - x) / np.maximum(np.abs(x), 1e-300)
+    assert np.all(rel[np.abs(x) >= np.ldexp(1.0, -6 + e.repeat(32, axis=1))] <= 2.0 ** -4)

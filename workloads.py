@@ -83,6 +83,9 @@ C3 = Decode("decode_paged_nvfp4_gqa", 3, B=64, Hq=32, Hkv=8, d=128, page_size=64
 C4 = Prefill("chunked_prefill_128k_nvfp4_hadamard_select5", 4, B=1, Hq=32, Hkv=8, Lq=2048, Lk=131072, d=128,
              causal=True, dtype="bf16", qk_fmt="nvfp4", outliers=True, hadamard=True, select=True)
 WORKLOADS = [C0, C1, C2, C3, C4]
+# The 4K causal prefill with Q and K in MXFP8 (E4M3 elements, E8M0 scale per 32; "MXFP vs NVFP4"
+# section 4.2's policy for the attention inputs): the same values as C1.
+C1_MX8 = replace(C1, name="prefill_4k_causal_mxfp8", qk_fmt="mxfp8")
 # The decode workload over an MXFP4 cache (E8M0 scale per 32 elements, no tensor scale): the same
 # sequences, lengths, pages and values as C3 (same workload id, hence the same seeds).
 C3_MX = replace(C3, name="decode_paged_mxfp4_gqa", kv_fmt="mxfp4")
