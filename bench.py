@@ -43,6 +43,7 @@ import workloads as W  # noqa: E402
 
 METRIC = "prefill attn TFLOP/s + decode KV GB/s, as % of MXFP4-MFMA / HBM peak"
 MXFP4_PEAK_TFLOPS = 10100.0          # dense MFMA, FP4/FP6
+FP8_PEAK_TFLOPS = 5000.0             # dense MFMA, FP8 (the peak of an MXFP8 QK^T workload)
 HBM_PEAK_GBS = 8000.0
 COPY_BYTES = 1 << 30                 # calibration copy: reads and writes this many bytes
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
@@ -144,7 +145,7 @@ def time_prefill(fa4, cfg, steps, warmup, select):
     """(ms per whole step, ms per attention launch). The step loop has no events inside it; the
     attention kernel is timed on its own loop of back-to-back launches over the same inputs."""
     q, k, v = (t.cuda() for t in W.prefill_inputs(cfg))
-    fmt = fa4.FA4_MXFP4 if cfg.qk_fmt == "mxfp4" else fa4.FA4_NVFP4
+    fmt = {"mxfp4": fa4.FA4_MXFP4, "nvfp4": fa4.FA4_NVFP4, "mxfp8": fa4.FA4_MXFP8}[cfg.qk_fmt]
     run = fa4.PrefillRunner(q, k, v, cfg.causal, fmt=fmt, hadamard=cfg.hadamard, select=select)
     for _ in range(warmup):
         run.run()
@@ -223,7 +224,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=W.C1.name,
-                    choices=[c.name for c in W.WORKLOADS if isinstance(c, W.Prefill)])
+                    choices=[c.name for c in W.WORKLOADS + [W.C1_MX8] if isinstance(c, W.Prefill)])
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=8)
@@ -239,13 +240,14 @@ def main():
         sys.exit(2)
     import fp8_quantized_attention_amd as fa4
 
-    cfg = next(c for c in W.WORKLOADS if c.name == args.workload)
+    cfg = next(c for c in W.WORKLOADS + [W.C1_MX8] if c.name == args.workload)
     select = (5, 100) if cfg.select else None
     if args.copy_probe:
         copy_probe()
     step_ms, attn_ms = time_prefill(fa4, cfg, args.steps, args.warmup, select)
     flops = prefill_flops(cfg)
     achieved = flops / (attn_ms * 1e-3) / 1e12
+    peak = FP8_PEAK_TFLOPS if cfg.qk_fmt == "mxfp8" else MXFP4_PEAK_TFLOPS
     line = {
         "metric": METRIC,
         "value": flops / (step_ms * 1e-3) / 1e12,
@@ -257,13 +259,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4+fp8" if cfg.qk_fmt == "mxfp4" else "nvfp4+fp8",
+        "dtype": cfg.qk_fmt + "+fp8",
         "data": "synthetic",
         "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "Lq": cfg.Lq, "Lk": cfg.Lk,
                    "d": cfg.d, "causal": cfg.causal, "qk_format": cfg.qk_fmt, "hadamard": cfg.hadamard,
                    "bf16_tiles": "5%" if select else "none", "algorithmic_flops": flops},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MXFP4_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / MXFP4_PEAK_TFLOPS, "traffic": recorded_traffic("attn_fwd_kernel")
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": recorded_traffic("attn_fwd_kernel")
                      if cfg.name == W.C1.name else None, "kernel": "attn_fwd_kernel",
                      "kernel_ms": attn_ms},
     }

@@ -20,7 +20,7 @@ lib = ctypes.CDLL(LIB_PATH)
 
 FA4_OK, FA4_ERR_NULL, FA4_ERR_SHAPE, FA4_ERR_UNSUPPORTED, FA4_ERR_ALIGN, FA4_ERR_WORKSPACE, FA4_ERR_HIP = range(7)
 FA4_F32, FA4_BF16 = 0, 1
-FA4_MXFP4, FA4_NVFP4, FA4_FP8_TOKEN = 0, 1, 2
+FA4_MXFP4, FA4_NVFP4, FA4_FP8_TOKEN, FA4_MXFP8 = 0, 1, 2, 3
 FA4_HADAMARD128, FA4_DUAL_RESIDUAL, FA4_SCALE_SEARCH = 1, 2, 4
 
 EXPORTS = ["fa4_quantize_blockscaled", "fa4_smoothing_factors", "fa4_select_tiles", "fa4_attn_fwd", "fa4_decode_workspace_bytes",
@@ -128,6 +128,10 @@ def quantize(x, fmt, hadamard=False, dual=False, row_norms=False, fold=None, cha
         out["codes"] = torch.empty(O, H, R, d, **u8)
         out["scales"] = torch.empty(O, H, R, dtype=torch.float32, device=dev)
         bs = None
+    elif fmt == FA4_MXFP8:
+        out["codes"] = torch.empty(O, H, R, d, **u8)
+        out["block_scales"] = bs = torch.empty(O, H, R, d // 32, **u8)
+        out["scales"] = None
     else:
         out["codes"] = torch.empty(O, H, R, d // 2, **u8)
         out["block_scales"] = bs = torch.empty(O, H, R, d // (32 if fmt == FA4_MXFP4 else 16), **u8)
@@ -222,7 +226,7 @@ def attn_fwd(q, k, v, causal, fmt, Hq, Hkv, Lq, Lk, d, B=1, bitmap=None, q_bf16=
              v_bf16=None, softmax_scale=None, want_lse=True, out=None, lse=None):
     """Prefill attention from quantized operands (dicts as returned by quantize()).
 
-    q/k hold MXFP4 or NVFP4 codes and scales, v holds FP8 per-token codes and scales.
+    q/k hold MXFP4, NVFP4 or MXFP8 codes and scales, v holds FP8 per-token codes and scales.
     Returns (o [B, Hq, Lq, d] float32, lse [B, Hq, Lq] float32 or None).
     """
     dev = q["codes"].device
@@ -365,11 +369,12 @@ class PrefillRunner:
         self.causal, self.fmt, self.select = causal, fmt, select
         self.flags = FA4_HADAMARD128 if hadamard else 0
         u8, f32 = dict(dtype=torch.uint8, device=dev), dict(dtype=torch.float32, device=dev)
-        nb = d // (32 if fmt == FA4_MXFP4 else 16)
-        self.qq = {"codes": torch.empty(B, Hq, Lq, d // 2, **u8), "block_scales": torch.empty(B, Hq, Lq, nb, **u8),
+        nb = d // (16 if fmt == FA4_NVFP4 else 32)
+        cw = d if fmt == FA4_MXFP8 else d // 2                   # code bytes per row
+        self.qq = {"codes": torch.empty(B, Hq, Lq, cw, **u8), "block_scales": torch.empty(B, Hq, Lq, nb, **u8),
                    "scales": torch.empty(B * Hq, **f32) if fmt == FA4_NVFP4 else None,
                    "norm2": torch.empty(B, Hq, Lq, **f32) if self.sel else None}
-        self.kq = {"codes": torch.empty(B, Hkv, Lk, d // 2, **u8), "block_scales": torch.empty(B, Hkv, Lk, nb, **u8),
+        self.kq = {"codes": torch.empty(B, Hkv, Lk, cw, **u8), "block_scales": torch.empty(B, Hkv, Lk, nb, **u8),
                    "scales": torch.empty(B * Hkv, **f32) if fmt == FA4_NVFP4 else None,
                    "norm2": torch.empty(B, Hkv, Lk, **f32) if self.sel else None}
         self.vq = {"codes": torch.empty(B, Hkv, Lk, d, **u8), "scales": torch.empty(B, Hkv, Lk, **f32),

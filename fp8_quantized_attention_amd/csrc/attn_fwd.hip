@@ -64,21 +64,30 @@ __device__ __forceinline__ v4s lds_tr16(const uint8_t *p) {
 // The 16-byte chunks of a K row are XOR-swizzled by kswz(r) and those of a V row by vswz(r), so the
 // QK operand reads (16 rows x one chunk per 16 lanes) and the transposed V reads (16 rows x two
 // chunks per instruction) spread over all LDS banks.
-// bf16 tiles (and the fp16 values of NVFP4 K) use 16-bit rows with stride H16_RS in a separate
+// bf16 tiles (and the fp16 values of NVFP4 K, the bf16 values of MXFP8 K) use 16-bit rows with stride H16_RS in a separate
 // layout [K16 | V] that overlaps the quantized buffers; those tiles are staged synchronously.
+// Q/K formats whose K tiles are expanded to exact 16-bit values in LDS (their block scales are not
+// applied by the MFMA): NVFP4 (fp16) and MXFP8 (bf16).
+template <int QF>
+struct Expanded {
+  static constexpr bool value = QF == FA4_NVFP4 || QF == FA4_MXFP8;
+};
+
 template <int D, int QF, bool SEL>
 struct AttnLds {
   static constexpr int KC = 128 * (D / 2);
   static constexpr int KS = 512;
   static constexpr int VC = 128 * D;
   static constexpr int QBUF = KC + KS + VC + 512;
-  static constexpr int QBYTES = (QF == FA4_MXFP4) ? 2 * QBUF : 0;
+  static constexpr int QBYTES = QF == FA4_MXFP4 ? 2 * QBUF : 0;
   static constexpr int K16 = 128 * H16_RS;
   static constexpr int V8 = 128 * V8_RS;                 // NVFP4 tiles' FP8 V rows
   static constexpr int V16 = 128 * H16_RS;               // selected tiles' bf16 V rows (overlap V8 onwards)
-  // NVFP4 staging of the next tile's raw data: K codes, K scales, V codes, fold factors
-  static constexpr int NVSTAGE = 128 * (D / 2) + 128 * (D / 16) + 128 * D + 512;
-  static constexpr int NBYTES = (QF == FA4_NVFP4) ? K16 + V8 + 512 + NVSTAGE : 0;
+  // staging of the next tile's raw data (NVFP4, MXFP8): K codes, K scales, V codes, fold factors
+  static constexpr int SKC = QF == FA4_MXFP8 ? 128 * D : 128 * (D / 2);
+  static constexpr int SKS = QF == FA4_MXFP8 ? 128 * (D / 32) : 128 * (D / 16);
+  static constexpr int NVSTAGE = SKC + SKS + 128 * D + 512;
+  static constexpr int NBYTES = Expanded<QF>::value ? K16 + V8 + 512 + NVSTAGE : 0;
   static constexpr int SBYTES = SEL ? K16 + V16 : 0;
   static constexpr int HBYTES = NBYTES > SBYTES ? NBYTES : SBYTES;
   static constexpr int BYTES = QBYTES > HBYTES ? QBYTES : HBYTES;
@@ -106,6 +115,22 @@ __device__ __forceinline__ v8h nv_expand8(uint32_t w, _Float16 sb) {
   const v2h t2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
   const v2h t3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
   return (v8h){t0[0], t0[1], t1[0], t1[1], t2[0], t2[1], t3[0], t3[1]};
+}
+
+// MXFP8: an E8M0 scale code as the float 2^(code - 127) for the conversions below (code 0, a block with
+// amax below 448 * 2^-127, is taken as 2^-126 so that the scale stays a normal float).
+__device__ __forceinline__ float mx8_scale_float(uint32_t code) {
+  return __uint_as_float((code > 1u ? code : 1u) << 23);
+}
+// 8 E4M3 codes (w.x bytes 0-3, w.y bytes 4-7) times 2^e as exact bf16 values (at most 4 significant
+// bits; bf16 has the float exponent range), packed two per word in element order.
+__device__ __forceinline__ v4i mx8_expand8(uint2 w, float sc) {
+  v4i r;
+  r[0] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, sc, false));
+  r[1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, sc, true));
+  r[2] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, sc, false));
+  r[3] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, sc, true));
+  return r;
 }
 
 // Per-lane LDS byte offsets of every operand read of a tile step. All the XOR swizzles depend only on
@@ -156,9 +181,9 @@ __device__ __forceinline__ v16f qk_mx_block(const LaneOff &lo, int kb, int hh, c
                                 : *reinterpret_cast<const uint16_t *>(ksc + lo.ks + 64 * kb);
 #pragma unroll
   for (int st = 0; st < D / 64; st++) {
+    const int kscl = (int)((scw >> (8 * (2 * st + hh))) & 0xffu);
     const v4i t = *reinterpret_cast<const v4i *>(k4 + lo.k[st] + 32 * kb * (D / 2));
     const v8i kop = (v8i){t[0], t[1], t[2], t[3], 0, 0, 0, 0};
-    const int kscl = (int)((scw >> (8 * (2 * st + hh))) & 0xffu);
     s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kop, qop4[st], s, 4, 4, 0, kscl, 0, qsc4[st]);
   }
   return s;
@@ -302,6 +327,7 @@ __device__ __forceinline__ void tile_step(const AttnArgs &a, const LaneOff &lo, 
 #pragma unroll
     for (int kb = 0; kb < 4; kb++) S[kb] = qk_mx_block<D>(lo, kb, hh, qop4, qsc4, k4, ksc);
   } else {
+    // expanded K (NVFP4: fp16 values; MXFP8: bf16 values, both exact) and the matching Q registers
 #pragma unroll
     for (int kb = 0; kb < 4; kb++) S[kb] = (v16f){};
 #pragma unroll
@@ -309,7 +335,11 @@ __device__ __forceinline__ void tile_step(const AttnArgs &a, const LaneOff &lo, 
 #pragma unroll
       for (int kb = 0; kb < 4; kb++) {
         const v8h kop = *reinterpret_cast<const v8h *>(k16 + lo.k16 + 32 * kb * H16_RS + 32 * s);
-        S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop, qop16[s], S[kb], 0, 0, 0);
+        if (QF == FA4_MXFP8)
+          S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, kop),
+                                                          __builtin_bit_cast(v8bf, qop16[s]), S[kb], 0, 0, 0);
+        else
+          S[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop, qop16[s], S[kb], 0, 0, 0);
       }
   }
 
@@ -408,6 +438,16 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
       qop4[s] = (v8i){t[0], t[1], t[2], t[3], 0, 0, 0, 0};
       qsc4[s] = a.qs[(bhq * a.Lq + qrow) * (D / 32) + 2 * s + hh];
     }
+  } else if (QF == FA4_MXFP8) {
+    // exact bf16 values code * 2^e (bf16 bits in the fp16-typed registers); lane half hh of step s
+    // holds d = 16 s + 8 hh .. + 7 (one E8M0 block)
+#pragma unroll
+    for (int s = 0; s < 8; s++) {
+      const uint2 w = *reinterpret_cast<const uint2 *>(a.qc + (bhq * a.Lq + qrow) * 128 + 16 * s + 8 * hh);
+      const float sc = mx8_scale_float(a.qs[(bhq * a.Lq + qrow) * 4 + (s >> 1)]);
+      const v4i bf = mx8_expand8(w, sc);
+      qop16[s] = __builtin_bit_cast(v8h, bf);
+    }
   } else {
     // exact NVFP4 values code * s_b in fp16; the tensor scales move into cs_q
 #pragma unroll
@@ -502,28 +542,45 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
                     reinterpret_cast<const float *>(base + L::KC + L::KS + L::VC));
     }
   } else {
-    // ---- NVFP4 tiles: the next tile's raw codes, scales, V and fold factors are brought into a
-    // staging area by direct global->LDS loads while the current tile is computed; at the start of
-    // each tile K is expanded from there to exact fp16 values and V copied next to it.
-    constexpr int SK = 0, SKS = 128 * (D / 2), SV = SKS + 128 * (D / 16), SW = SV + 128 * D;
+    // ---- NVFP4 / MXFP8 tiles: the next tile's raw codes, scales, V and fold factors are brought into
+    // a staging area by direct global->LDS loads while the current tile is computed; at the start of
+    // each tile K is expanded from there to exact 16-bit values (NVFP4: fp16, MXFP8: bf16) and V
+    // copied next to it.
+    constexpr int SK = 0, SKS = L::SKC, SV = SKS + L::SKS, SW = SV + 128 * D;
+    constexpr int KROW = QF == FA4_MXFP8 ? D : D / 2;          // code bytes per K row
     auto issue_nv = [&](int kt) __attribute__((always_inline)) {
       const int64_t krow0 = bhk * a.Lk + (int64_t)kt * 128;
-      // K codes 8 KB, V 16 KB: linear 1 KB chunks spread over the 4 waves
+      // K codes (8 or 16 KB), V 16 KB: linear 1 KB chunks spread over the 4 waves
 #pragma unroll
-      for (int e = 0; e < 2; e++) {
-        const int i = wave * 2 + e;
-        dma16(a.kc + krow0 * (D / 2) + 1024 * i + 16 * lane, nst + SK + 1024 * i);
+      for (int e = 0; e < L::SKC / 4096; e++) {
+        const int i = wave * (L::SKC / 4096) + e;
+        dma16(a.kc + krow0 * KROW + 1024 * i + 16 * lane, nst + SK + 1024 * i);
       }
 #pragma unroll
       for (int e = 0; e < 4; e++) {
         const int i = wave * 4 + e;
         dma16(a.vc + krow0 * D + 1024 * i + 16 * lane, nst + SV + 1024 * i);
       }
-      if (wave == 0) dma16(a.ks + krow0 * (D / 16) + 16 * lane, nst + SKS);
+      if (QF == FA4_MXFP8) {                 // 512 B of E8M0 scales
+        if (wave < 2) dma4(a.ks + krow0 * (D / 32) + 256 * wave + 4 * lane, nst + SKS + 256 * wave);
+      } else if (wave == 0) {
+        dma16(a.ks + krow0 * (D / 16) + 16 * lane, nst + SKS);
+      }
       if (wave >= 2) dma4(a.vw + krow0 + 64 * (wave - 2) + lane, nst + SW + 256 * (wave - 2));
     };
     auto expand_nv = [&]() __attribute__((always_inline)) {
-      {
+      if (QF == FA4_MXFP8) {
+        // thread: row tid / 2, d = 64 (tid % 2) .. + 63 (two E8M0 blocks), 8 values per 16-byte store
+        const int r = tid >> 1, half = tid & 1;
+        const uint8_t *src = nst + SK + r * 128 + 64 * half;
+        const uint32_t scw = *reinterpret_cast<const uint16_t *>(nst + SKS + r * 4 + 2 * half);
+        const float sc0 = mx8_scale_float(scw & 0xffu), sc1 = mx8_scale_float(scw >> 8);
+#pragma unroll
+        for (int g = 0; g < 8; g++) {
+          const uint2 w = *reinterpret_cast<const uint2 *>(src + 8 * g);
+          *reinterpret_cast<v4i *>(k16 + r * H16_RS + 2 * (64 * half + 8 * g)) = mx8_expand8(w, g < 4 ? sc0 : sc1);
+        }
+      } else {
         const int r = tid >> 1, half = tid & 1;
         const v4i c0 = *reinterpret_cast<const v4i *>(nst + SK + r * 64 + 32 * half);
         const v4i c1 = *reinterpret_cast<const v4i *>(nst + SK + r * 64 + 32 * half + 16);
@@ -638,6 +695,7 @@ hipError_t launch_attn(const fa4_attn_args *p, hipStream_t s) {
     if (p->d == 64) return launch_attn_t<64, FA4_MXFP4>(x, causal, false, s);
     return launch_attn_t<128, FA4_MXFP4>(x, causal, sel, s);
   }
+  if (p->fmt == FA4_MXFP8) return launch_attn_t<128, FA4_MXFP8>(x, causal, sel, s);
   return launch_attn_t<128, FA4_NVFP4>(x, causal, sel, s);
 }
 

@@ -64,7 +64,7 @@ fa4_status fa4_quantize_blockscaled(const fa4_qinput *in, uint32_t flags, const 
   REQUIRE(in && out, FA4_ERR_NULL, "quantize: input or output descriptor is NULL");
   REQUIRE(in->dtype == FA4_F32 || in->dtype == FA4_BF16, FA4_ERR_UNSUPPORTED, "quantize: dtype %d", in->dtype);
   REQUIRE(in->d == 64 || in->d == 128, FA4_ERR_UNSUPPORTED, "quantize: d=%d (64 or 128)", in->d);
-  REQUIRE(out->fmt == FA4_MXFP4 || out->fmt == FA4_NVFP4 || out->fmt == FA4_FP8_TOKEN,
+  REQUIRE(out->fmt == FA4_MXFP4 || out->fmt == FA4_NVFP4 || out->fmt == FA4_FP8_TOKEN || out->fmt == FA4_MXFP8,
           FA4_ERR_UNSUPPORTED, "quantize: format %d", out->fmt);
   REQUIRE((flags & ~(uint32_t)(FA4_HADAMARD128 | FA4_DUAL_RESIDUAL | FA4_SCALE_SEARCH)) == 0, FA4_ERR_UNSUPPORTED,
           "quantize: unknown flags 0x%x", flags);
@@ -149,7 +149,8 @@ fa4_status fa4_select_tiles(const float *q_norm2, const float *k_norm2, int32_t 
 
 fa4_status fa4_attn_fwd(const fa4_attn_args *a, void *stream) {
   REQUIRE(a, FA4_ERR_NULL, "attn: args is NULL");
-  REQUIRE(a->fmt == FA4_MXFP4 || a->fmt == FA4_NVFP4, FA4_ERR_UNSUPPORTED, "attn: Q/K format %d", a->fmt);
+  REQUIRE(a->fmt == FA4_MXFP4 || a->fmt == FA4_NVFP4 || a->fmt == FA4_MXFP8, FA4_ERR_UNSUPPORTED,
+          "attn: Q/K format %d", a->fmt);
   REQUIRE(a->B >= 0 && a->Hq >= 1 && a->Hkv >= 1 && a->Hq % a->Hkv == 0, FA4_ERR_SHAPE,
           "attn: B=%d Hq=%d Hkv=%d", a->B, a->Hq, a->Hkv);
   REQUIRE(a->Lq >= 0 && a->Lk > 0 && a->Lq % 128 == 0 && a->Lk % 128 == 0, FA4_ERR_SHAPE,
@@ -160,7 +161,7 @@ fa4_status fa4_attn_fwd(const fa4_attn_args *a, void *stream) {
     REQUIRE(a->d == 128 || (a->d == 64 && !a->bitmap), FA4_ERR_UNSUPPORTED,
             "attn: MXFP4 supports d=128, or d=64 without tile selection (d=%d)", a->d);
   else
-    REQUIRE(a->d == 128, FA4_ERR_UNSUPPORTED, "attn: NVFP4 needs d=128 (d=%d)", a->d);
+    REQUIRE(a->d == 128, FA4_ERR_UNSUPPORTED, "attn: NVFP4 and MXFP8 need d=128 (d=%d)", a->d);
   if (a->B == 0 || a->Lq == 0) return ok();
   REQUIRE(a->q_codes && a->q_scales && a->k_codes && a->k_scales && a->v_codes && a->v_scales && a->o &&
               a->v_fold_w && a->v_fold_scale,

@@ -64,6 +64,16 @@ __device__ __forceinline__ int mx_exponent(float amax) {
   int e = (m <= 0x400000u) ? E - 129 : E - 128;
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
+// MXFP8 (E4M3 elements): smallest e with 448 * 2^e >= amax, clamped, -127 for amax = 0. With f as above
+// and 448 = 0.875 * 2^9: e = E-126-9 if f <= 0.875 (m <= 0x600000) else E-126-8.
+__device__ __forceinline__ int mx8_exponent(float amax) {
+  const uint32_t b = __float_as_uint(amax);
+  const int E = (int)((b >> 23) & 0xffu);
+  const uint32_t m = b & 0x7fffffu;
+  if (E == 0) return -127;
+  int e = (m <= 0x600000u) ? E - 135 : E - 134;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
 // 2^-e as a float for e in [-127, 126] (exact; 2^-126 is the smallest normal).
 __device__ __forceinline__ float pow2_neg(int e) { return __uint_as_float((uint32_t)(127 - e) << 23); }
 

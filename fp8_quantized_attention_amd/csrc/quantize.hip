@@ -374,6 +374,19 @@ __global__ void __launch_bounds__(QUANT_THREADS) quantize_kernel(QArgs a) {
           if ((li % (32 / E)) == 0) a.rbscales[orow * (D / 32) + li / (32 / E)] = (uint8_t)(re + 127);
         }
       }
+    } else if (FMT == FA4_MXFP8) {
+      const int e = mx8_exponent(group_max(lane_amax<E>(v), 32 / E));
+      const float mul = pow2_neg(e);
+      uint32_t c[E / 4];
+#pragma unroll
+      for (int w = 0; w < E / 4; w++)
+        c[w] = e4m3_encode2(v[4 * w] * mul, v[4 * w + 1] * mul) |
+               (e4m3_encode2(v[4 * w + 2] * mul, v[4 * w + 3] * mul) << 16);   // exact scaling, then RNE
+      if (store) {
+        if (E == 8) *reinterpret_cast<uint2 *>(a.codes + orow * D + li * 8) = make_uint2(c[0], c[E / 4 - 1]);
+        else *reinterpret_cast<uint32_t *>(a.codes + orow * D + li * 4) = c[0];
+        if ((li % (32 / E)) == 0) a.bscales[orow * (D / 32) + li / (32 / E)] = (uint8_t)(e + 127);
+      }
     } else if (FMT == FA4_FP8_TOKEN) {
       const float am = group_max(lane_amax<E>(v), LPR);
       const float s = am == 0.0f ? 1.0f : am / 448.0f;
@@ -589,6 +602,9 @@ static hipError_t quantize_dispatch(const QArgs &a, int fmt, bool had, bool dual
     if (had) return launch_q<D, DT, FA4_MXFP4, 1, true, false>(a, groups, norm, s);
     return launch_q<D, DT, FA4_MXFP4, 1, false, false>(a, groups, norm, s);
   }
+  if (fmt == FA4_MXFP8)
+    return had ? launch_q<D, DT, FA4_MXFP8, 1, true, false>(a, groups, norm, s)
+               : launch_q<D, DT, FA4_MXFP8, 1, false, false>(a, groups, norm, s);
   if (fmt == FA4_FP8_TOKEN) {
     if ((e = launch_q<D, DT, FA4_FP8_TOKEN, 1, false, false>(a, groups, norm, s)) != hipSuccess) return e;
     if (a.fold_w && a.rows > 0 && groups > 0) {

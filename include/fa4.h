@@ -42,7 +42,7 @@ typedef enum {
 } fa4_status;
 
 enum { FA4_F32 = 0, FA4_BF16 = 1 };                      /* input element types       */
-enum { FA4_MXFP4 = 0, FA4_NVFP4 = 1, FA4_FP8_TOKEN = 2 }; /* quantized formats         */
+enum { FA4_MXFP4 = 0, FA4_NVFP4 = 1, FA4_FP8_TOKEN = 2, FA4_MXFP8 = 3 }; /* quantized formats */
 enum { FA4_HADAMARD128 = 1u << 0, FA4_DUAL_RESIDUAL = 1u << 1, FA4_SCALE_SEARCH = 1u << 2 }; /* quantizer flags */
 
 /* ------------------------------------------------------------------------------------------------
@@ -69,6 +69,9 @@ enum { FA4_HADAMARD128 = 1u << 0, FA4_DUAL_RESIDUAL = 1u << 1, FA4_SCALE_SEARCH 
  *   FA4_NVFP4: codes [d/2]; block_scales [d/16] E4M3; scales = tensor scale per group [outer*heads]
  *              float: s_t = amax_group / 2688 (1 if zero), s_b = E4M3(amax_block / (6 s_t)),
  *              codes = E2M1(x / (E4M3value(s_b) * s_t)) (float32, IEEE division); value = code*s_b*s_t.
+ *   FA4_MXFP8: codes [d] E4M3; block_scales [d/32] E8M0: per 32 elements, the smallest power of two
+ *              2^e with 448 * 2^e >= amax (e = -127 if amax = 0), codes = E4M3(x * 2^-e) rounded to
+ *              nearest even ("MXFP vs NVFP4" sections 2.1 and 4.2). `scales` unused.
  *   FA4_FP8_TOKEN: codes [d] E4M3; scales = per-row float [out rows]: s = amax_row / 448 (1 if zero),
  *              codes = E4M3(x / s). block_scales unused.
  * flags: FA4_HADAMARD128 rotates each row by the Sylvester Hadamard matrix H_128 / sqrt(128) (float64,
@@ -177,8 +180,8 @@ fa4_status fa4_select_tiles(const float *q_norm2, const float *k_norm2, int32_t 
  *               T = 2^e * sum_c P^ * E4M3value(Vcode_c)     (FP8 x FP8 products);
  *   selected:   T = sum_c bf16(P') * v_c with the bf16 originals;
  *   O = sum_j 2^(r_j - m) T_j / sum_j 2^(r_j - m) sum_c P'   (m = max_j r_j), LSE = m ln 2 + ln(denominator).
- * Layouts: q_codes [B][Hq][Lq][d/2], q_scales [B][Hq][Lq][d/32] (MXFP4) or [d/16] (NVFP4) with
- * q_tscale [B*Hq]; k_* likewise over [B][Hkv][Lk]; v_codes [B][Hkv][Lk][d] E4M3 with v_scales
+ * Layouts: q_codes [B][Hq][Lq][d/2] (MXFP8: [d] E4M3), q_scales [B][Hq][Lq][d/32] (MXFP4, MXFP8: E8M0)
+ * or [d/16] (NVFP4) with q_tscale [B*Hq]; k_* likewise over [B][Hkv][Lk]; v_codes [B][Hkv][Lk][d] E4M3 with v_scales
  * [B][Hkv][Lk], v_fold_w [B][Hkv][Lk] and v_fold_scale [B][Hkv][Lk/128] (the quantizer's fold
  * outputs); q_bf16 [B][Hq][Lq][d], k_bf16 / v_bf16 [B][Hkv][Lk][d] (bf16 bits; required when
  * bitmap is given); bitmap [B][Hq][Lq/128][Lk/128] or NULL; o [B][Hq][Lq][d] float; lse [B][Hq][Lq]
@@ -186,7 +189,7 @@ fa4_status fa4_select_tiles(const float *q_norm2, const float *k_norm2, int32_t 
  * Lq <= Lk when causal; Hq % Hkv == 0; every pointer 16-byte aligned.
  */
 typedef struct {
-  int32_t fmt;                                  /* FA4_MXFP4 or FA4_NVFP4 (format of Q and K) */
+  int32_t fmt;                                  /* FA4_MXFP4, FA4_NVFP4 or FA4_MXFP8 (Q and K) */
   const uint8_t *q_codes, *q_scales; const float *q_tscale;
   const uint8_t *k_codes, *k_scales; const float *k_tscale;
   const uint8_t *v_codes; const float *v_scales;

@@ -23,7 +23,7 @@ def fa4():
 
 def _run(fa4, cfg, seed=0, select=None):
     q, k, v = W.prefill_inputs(cfg, seed)
-    fmt = fa4.FA4_MXFP4 if cfg.qk_fmt == "mxfp4" else fa4.FA4_NVFP4
+    fmt = {"mxfp4": fa4.FA4_MXFP4, "nvfp4": fa4.FA4_NVFP4, "mxfp8": fa4.FA4_MXFP8}[cfg.qk_fmt]
     res = fa4.prefill(q.cuda(), k.cuda(), v.cuda(), cfg.causal, fmt=fmt, hadamard=cfg.hadamard, select=select)
     torch.cuda.synchronize()
     return (q, k, v), res
@@ -94,6 +94,19 @@ def test_deterministic(fa4):
     assert torch.equal(a["o"], b["o"]) and torch.equal(a["lse"], b["lse"]) and torch.equal(a["bitmap"], b["bitmap"])
 
 
+# ---- Q and K in MXFP8 (E4M3 elements, E8M0 per 32): K expanded to exact bf16, QK^T on bf16 MFMAs
+def test_mxfp8_tiny_noncausal_f32(fa4):
+    _check_full(fa4, W.C0.scaled(qk_fmt="mxfp8", d=128))
+
+
+def test_mxfp8_causal_small_gqa_offset(fa4):
+    _check_full(fa4, W.C1_MX8.scaled(Hq=4, Hkv=2, Lq=256, Lk=768))
+
+
+def test_mxfp8_selection_small(fa4):
+    _check_full(fa4, W.C1_MX8.scaled(Hq=2, Hkv=2, Lq=1024, Lk=1024, select=True), select=(5, 100))
+
+
 def _sampled(fa4, cfg, heads, nrows, select=None, seed=0):
     (q, k, v), res = _run(fa4, cfg, seed, select)
     rng = np.random.default_rng(7)
@@ -122,3 +135,7 @@ def test_full_size_prefill_32k_selection(fa4):
 
 def test_full_size_chunked_prefill_128k(fa4):
     _sampled(fa4, W.C4, heads=[(0, 0), (0, 7), (0, 29)], nrows=24, select=(5, 100))
+
+
+def test_full_size_prefill_4k_mxfp8(fa4):
+    _sampled(fa4, W.C1_MX8, heads=[(0, 0), (0, 17)], nrows=96)

@@ -141,6 +141,19 @@ def test_dual_residual_query(fa4):
     assert np.array_equal(_np(out["codes2"]).reshape(2048, 1, -1), c2)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mxfp8_codes_and_scales(fa4, d, dtype):
+    x = np.ascontiguousarray(_special_rows(d=d, rows=96, seed=7).reshape(1, 2, 48, d))
+    t = torch.from_numpy(x)
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    out = fa4.quantize(t.cuda(), fa4.FA4_MXFP8)
+    codes, scales = Q.mxfp8_quantize(t.float().numpy().astype(np.float64))
+    assert out["scales"] is None
+    assert np.array_equal(_np(out["codes"]), codes) and np.array_equal(_np(out["block_scales"]), scales)
+
+
 @pytest.mark.parametrize("special", [False, True])
 def test_dual_residual_query_mxfp4(fa4, special):
     """MXFP4 dual residual: Q1 = MXFP4(q), Q2 = MXFP4(fl32(q - dequant(Q1))), bit for bit."""
