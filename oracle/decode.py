@@ -24,11 +24,22 @@ Formats of the cache (the page reports both): NVFP4 (E4M3 scale per 16
 elements along d and an FP32 tensor scale per (sequence, key head)) or MXFP4
 (E8M0 scale per 32 elements along d, no tensor scale). The query residuals take
 the cache's format. The probability steps are the same for both.
+
+Probability format (p_fmt): "fp8" is the default above. "nvfp4" quantizes the
+probabilities to FP4 with E4M3 block scales, the case in which the digest says
+a block scale can round to zero for long contexts. The underflow-aware reading
+used here: each tile row of P' is normalized to its own maximum (so that
+maximum is exactly 1) and taken as one NVFP4 group, blocks of 16 consecutive
+keys from the tile start. The group's tensor scale is then fl32(1/2688), which
+puts a block whose maximum is amax_b at the E4M3 scale E4M3(~448 amax_b); a
+block scale reaches zero only when amax_b < 2^-10 / 448, a block that carries
+under 2.2e-6 of the tile's largest probability. P^ = the NVFP4 values
+(code * s_b * s_t, approximately P') and T = sum_c P^_c v^_c.
 """
 import numpy as np
 
 from .formats import E4M3_MAX, e4m3_decode, e4m3_encode, fp32
-from .quant import mxfp4_dequantize, nvfp4_dequantize
+from .quant import mxfp4_dequantize, nvfp4_dequantize, nvfp4_quantize
 
 TILE = 128
 
@@ -40,9 +51,21 @@ def gather_pages(pages, page_table_b, L, page_size, kvh):
     return pages[phys, kvh, c % page_size]
 
 
-def decode_one(q_hat, k_hat, v_hat, scale, chunk=None, round_p=True):
+def quantize_p_nvfp4(p):
+    """P^ of one tile row p (float64, largest element exactly 1, at most 128 keys) in NVFP4: the
+    row is one group (tensor scale from its amax 1), E4M3 scales per 16 keys from the row start; a
+    ragged row is padded with zeros, which leaves every block maximum unchanged. Returns the
+    dequantized values (float64, same length as p)."""
+    n = len(p)
+    x = np.concatenate([np.asarray(p, np.float64), np.zeros((-n) % 16)])[None, None, :]
+    codes, sb, st = nvfp4_quantize(x)
+    return nvfp4_dequantize(codes, sb, st)[0, 0, :n]
+
+
+def decode_one(q_hat, k_hat, v_hat, scale, chunk=None, round_p=True, p_fmt="fp8"):
     """O for one query row against L keys. chunk: optional split length (multiple of 128) whose
-    partial results (m, l, O) are merged afterwards; the merged result equals the single pass."""
+    partial results (m, l, O) are merged afterwards; the merged result equals the single pass.
+    p_fmt: "fp8" (P^ = E4M3(448 P')) or "nvfp4" (quantize_p_nvfp4)."""
     L = k_hat.shape[0]
     if chunk is None:
         chunk = max(L, 1)
@@ -55,8 +78,13 @@ def decode_one(q_hat, k_hat, v_hat, scale, chunk=None, round_p=True):
             S = scale * (k_hat[cs] @ q_hat)
             m = S.max()
             P = np.exp(S - m)
-            Ph = e4m3_decode(e4m3_encode(E4M3_MAX * P)) if round_p else E4M3_MAX * P
-            ms.append(m); ls.append(P.sum()); Ts.append((Ph @ v_hat[cs]) / E4M3_MAX)
+            if not round_p:
+                T = P @ v_hat[cs]
+            elif p_fmt == "nvfp4":
+                T = quantize_p_nvfp4(P) @ v_hat[cs]
+            else:
+                T = (e4m3_decode(e4m3_encode(E4M3_MAX * P)) @ v_hat[cs]) / E4M3_MAX
+            ms.append(m); ls.append(P.sum()); Ts.append(T)
         M = np.array(ms)
         mm = M.max()
         f = np.exp(M - mm)
@@ -74,7 +102,8 @@ def dequant_query(q1, q2, fmt="nvfp4"):
 
 
 def decode_paged(q1, q2, k_pages, v_pages, k_tscale, v_tscale, page_table, ctx_len,
-                 Hq, Hkv, page_size=64, scale=None, pairs=None, chunk=None, round_p=True, fmt="nvfp4"):
+                 Hq, Hkv, page_size=64, scale=None, pairs=None, chunk=None, round_p=True, fmt="nvfp4",
+                 p_fmt="fp8"):
     """O9 through the page table.
 
     fmt "nvfp4": q1, q2 = (codes [B*Hq, 1, d/2], block scales [B*Hq, 1, d/16], tensor scales
@@ -82,6 +111,7 @@ def decode_paged(q1, q2, k_pages, v_pages, k_tscale, v_tscale, page_table, ctx_l
     page_size, d/16]); k_tscale / v_tscale [B, Hkv] float32.
     fmt "mxfp4": q1, q2 = (codes, E8M0 scales [B*Hq, 1, d/32]); pages hold E8M0 scales
     [P, Hkv, page_size, d/32]; the tensor-scale arguments are unused.
+    p_fmt: probability format, "fp8" or "nvfp4" (decode_one).
     Returns O float32 [B, Hq, d]; pairs (optional) restricts the computed (b, h) pairs, the rest
     stay zero.
     """
@@ -110,5 +140,5 @@ def decode_paged(q1, q2, k_pages, v_pages, k_tscale, v_tscale, page_table, ctx_l
                 v_hat = mxfp4_dequantize(vc, vs)
             cache = {(b, kv): (k_hat, v_hat)}
         k_hat, v_hat = cache[(b, kv)]
-        O[b, h] = fp32(decode_one(qhat[b, h], k_hat, v_hat, scale, chunk=chunk, round_p=round_p))
+        O[b, h] = fp32(decode_one(qhat[b, h], k_hat, v_hat, scale, chunk=chunk, round_p=round_p, p_fmt=p_fmt))
     return O

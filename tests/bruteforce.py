@@ -185,8 +185,9 @@ def attention_rows(rows, Q, K, Vc, sv, Qo, Ko, Vo, sel, Lq, Lk, causal, scale, r
     return out
 
 
-def decode_row(q, K, V, scale, round_p=True):
-    """O9 by loops for one query row over len(K) keys, tiles of 128 from 0."""
+def decode_row(q, K, V, scale, round_p=True, p_fmt="fp8"):
+    """O9 by loops for one query row over len(K) keys, tiles of 128 from 0. p_fmt "nvfp4": each
+    tile's probabilities (largest exactly 1) form one NVFP4 group, P^ its values, T = sum P^ v."""
     d = len(q)
     terms = []
     for t0 in range(0, len(K), 128):
@@ -195,10 +196,17 @@ def decode_row(q, K, V, scale, round_p=True):
         m = max(S.values())
         P = {c: math.exp(S[c] - m) for c in cols}
         T = [0.0] * d
-        for c in cols:
-            p = e4m3_value(e4m3_encode(448.0 * P[c])) if round_p else 448.0 * P[c]
-            for t in range(d):
-                T[t] += p * V[c][t]
+        if round_p and p_fmt == "nvfp4":
+            codes, sbs, st = nvfp4_group([[f32(P[c]) for c in cols]])
+            ph = dict(zip(cols, nvfp4_values(codes, sbs, st)[0]))
+            for c in cols:
+                for t in range(d):
+                    T[t] += 448.0 * ph[c] * V[c][t]
+        else:
+            for c in cols:
+                p = e4m3_value(e4m3_encode(448.0 * P[c])) if round_p else 448.0 * P[c]
+                for t in range(d):
+                    T[t] += p * V[c][t]
         terms.append((m, sum(P.values()), [v / 448.0 for v in T]))
     mm = max(t[0] for t in terms)
     D = sum(math.exp(t[0] - mm) * t[1] for t in terms)

@@ -136,5 +136,5 @@ def decode_reference(cfg, seed, layout, pairs, logical, q1, q2):
     for (b, h) in pairs:
         kh = logical[(W.T_K, b, h // group)]
         vh = logical[(W.T_V, b, h // group)]
-        out.append(Dd.decode_one(qhat[b, h], kh, vh, 1.0 / np.sqrt(cfg.d)).astype(np.float32))
+        out.append(Dd.decode_one(qhat[b, h], kh, vh, 1.0 / np.sqrt(cfg.d), p_fmt=cfg.p_fmt).astype(np.float32))
     return np.stack(out)

@@ -142,3 +142,78 @@ def test_dual_residual_query_cuts_logit_error(fmt):
     e1 = np.linalg.norm(kh @ x1[0, 0] - l0) / np.linalg.norm(l0)
     e2 = np.linalg.norm(kh @ x12[0, 0] - l0) / np.linalg.norm(l0)
     assert e2 < 0.25 * e1
+
+
+# ---- probabilities in NVFP4 (E2M1 codes, E4M3 scales per 16 keys), the underflow case
+
+def _p_rows(seed=0):
+    """Tile rows of probabilities in (0, 1] with the largest exactly 1: full, ragged, one block, one
+    key, and blocks whose maxima fall by 2^-3 each down past the block-scale underflow point."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for n in [128, 77, 16, 1, 128]:
+        p = np.exp(-rng.exponential(6.0, n))
+        p[rng.integers(n)] = 1.0
+        rows.append(p)
+    steps = np.concatenate([2.0 ** (-3 * k) * (0.5 + 0.5 * rng.random(16)) for k in range(8)])
+    steps[0] = 1.0
+    rows.append(steps)
+    return rows
+
+
+def test_p_nvfp4_equals_bruteforce():
+    for p in _p_rows():
+        got = Dd.quantize_p_nvfp4(p)
+        codes, sbs, st = bf.nvfp4_group([[bf.f32(float(v)) for v in p]])
+        assert st == bf.f32(1.0 / 2688.0)
+        assert got.tolist() == bf.nvfp4_values(codes, sbs, st)[0]
+
+
+def test_p_nvfp4_block_scales_do_not_underflow():
+    """Normalizing each tile row to its maximum keeps E4M3 block scales off zero down to block maxima
+    of 2^-10/448; a block scale taken straight from amax_b / 6 (no tensor scale) is zero below
+    6 * 2^-10, which is the underflow the digest describes."""
+    from oracle.formats import e4m3_decode, e4m3_encode
+    p = _p_rows()[-1]
+    ph = Dd.quantize_p_nvfp4(p).reshape(8, 16)
+    for k, blk in enumerate(p.reshape(8, 16)):
+        amax = blk.max()
+        j = int(blk.argmax())
+        assert (ph[k].max() == 0) == (amax < 2.0 ** -10 / 448)
+        if amax >= 2.0 ** -6 / 448:               # E4M3-normal block scale: the block max keeps 2^-4
+            assert abs(ph[k, j] - amax) <= (2.0 ** -4 + 1e-6) * amax
+        naive = float(e4m3_decode(e4m3_encode(np.array([amax / 6.0])))[0])
+        assert (naive == 0) == (amax < 6 * 2.0 ** -10)
+    assert (ph.max(axis=1) > 0).sum() == 7 and ph[7].max() == 0   # 2^-21 < 2^-10/448 < 2^-18
+
+
+def test_bruteforce_decode_p_nvfp4():
+    cfg = SMALL.scaled(B=1, ctx_lo=300, ctx_hi=300)
+    lay, kp, vp, kt, vt, q, q1, q2, logical = build_cache(cfg)
+    O = Dd.decode_paged(q1, q2, kp, vp, kt, vt, lay.page_table.numpy(), lay.ctx_len.numpy(), cfg.Hq, cfg.Hkv,
+                        pairs=[(0, 3)], p_fmt="nvfp4")
+    qhat = Dd.dequant_query(q1, q2).reshape(cfg.B, cfg.Hq, cfg.d)
+    K = logical[(W.T_K, 0, 0)][1].tolist()
+    V = logical[(W.T_V, 0, 0)][1].tolist()
+    ref = bf.decode_row(qhat[0, 3].tolist(), K, V, 1 / np.sqrt(cfg.d), p_fmt="nvfp4")
+    assert np.abs(O[0, 3] - np.array(ref)).max() <= 1e-6 * np.abs(ref).max()
+    fp8 = Dd.decode_paged(q1, q2, kp, vp, kt, vt, lay.page_table.numpy(), lay.ctx_len.numpy(), cfg.Hq, cfg.Hkv,
+                          pairs=[(0, 3)])
+    assert np.abs(O[0, 3] - fp8[0, 3]).max() > 1e-4 * np.abs(ref).max()   # the format is really used
+
+
+@FMTS
+def test_p_nvfp4_split_merge_and_error(fmt):
+    cfg = SMALL
+    lay, kp, vp, kt, vt, q, q1, q2, logical = build_cache(cfg, fmt=fmt)
+    qhat = Dd.dequant_query(q1, q2, fmt).reshape(cfg.B, cfg.Hq, cfg.d)
+    kh = logical[(W.T_K, 2, 1)][1]; vh = logical[(W.T_V, 2, 1)][1]
+    one = Dd.decode_one(qhat[2, 5], kh, vh, 1 / np.sqrt(cfg.d), p_fmt="nvfp4")
+    for chunk in [128, 256]:
+        sp = Dd.decode_one(qhat[2, 5], kh, vh, 1 / np.sqrt(cfg.d), chunk=chunk, p_fmt="nvfp4")
+        assert np.abs(sp - one).max() <= 1e-12 * np.abs(one).max()
+    exact = Dd.decode_one(qhat[2, 5], kh, vh, 1 / np.sqrt(cfg.d), round_p=False)
+    fp8 = Dd.decode_one(qhat[2, 5], kh, vh, 1 / np.sqrt(cfg.d))
+    e4 = np.linalg.norm(one - exact) / np.linalg.norm(exact)
+    e8 = np.linalg.norm(fp8 - exact) / np.linalg.norm(exact)
+    assert e8 < e4 < 0.15          # FP4 probabilities: about 9% here, FP8 about 2%

@@ -67,6 +67,7 @@ class Decode:
     ctx_lo: int
     ctx_hi: int
     kv_fmt: str = "nvfp4"        # format of the paged K/V cache and of the query residuals
+    p_fmt: str = "fp8"           # format of the probabilities before PV: "fp8" or "nvfp4"
 
     def scaled(self, **kw):
         return replace(self, **kw)
@@ -89,6 +90,7 @@ C1_MX8 = replace(C1, name="prefill_4k_causal_mxfp8", qk_fmt="mxfp8")
 # The decode workload over an MXFP4 cache (E8M0 scale per 32 elements, no tensor scale): the same
 # sequences, lengths, pages and values as C3 (same workload id, hence the same seeds).
 C3_MX = replace(C3, name="decode_paged_mxfp4_gqa", kv_fmt="mxfp4")
+C3_P4 = replace(C3, name="decode_paged_nvfp4_gqa_p4", p_fmt="nvfp4")
 
 
 def _chunk(seed, wl, tensor, b, h, rows, d, outliers, dtype):
