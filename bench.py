@@ -10,6 +10,9 @@ attention kernel, inputs resident in HBM. `value` is prefill attention TFLOP/s o
   decode        the paged NVFP4 decode step (64 sequences, 32 -> 8 GQA heads, contexts 8K-32K):
                 KV-cache GB/s, and the decode kernels' HBM roofline;
   decode_mxfp4  the same decode step over an MXFP4 cache (same sequences and values);
+  decode_p4, decode_mxfp4_p4
+                the two decode steps with the probabilities in NVFP4 (E4M3 scales per 16 keys)
+                instead of FP8;
   k_quant       (--outlier) quantization of the 128K-token chunked-prefill keys (NVFP4 + Hadamard)
                 plain, with static smoothing, and with smoothing + the per-block scale search;
   cpu_baseline  the CPU oracle (float64 numpy) on a bounded sample of the same workload.
@@ -49,11 +52,14 @@ COPY_BYTES = 1 << 30                 # calibration copy: reads and writes this m
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "fp8_quantized_attention_amd", "csrc")
 # sources whose change invalidates a kernel's recorded counters
-# (template argument of the decode kernel: 1 = NVFP4 cache, 0 = MXFP4 cache)
+# (template arguments of the decode kernel: cache format 1 = NVFP4, 0 = MXFP4; probability format
+# 0 = FP8, 1 = NVFP4)
 KERNEL_SOURCES = {
     "attn_fwd_kernel": ["attn_fwd.hip", "fa4_device.h"],
-    "decode_split_kernel<1>": ["decode.hip", "fa4_device.h"],
-    "decode_split_kernel<0>": ["decode.hip", "fa4_device.h"],
+    "decode_split_kernel<1, 0>": ["decode.hip", "fa4_device.h"],
+    "decode_split_kernel<0, 0>": ["decode.hip", "fa4_device.h"],
+    "decode_split_kernel<1, 1>": ["decode.hip", "fa4_device.h"],
+    "decode_split_kernel<0, 1>": ["decode.hip", "fa4_device.h"],
 }
 
 
@@ -165,7 +171,8 @@ def time_decode(fa4, cfg, steps, warmup):
         del x
     torch.cuda.empty_cache()
     q = W.decode_query(cfg).cuda()
-    run = fa4.DecodeRunner(q, caches[0], caches[1], pt, ctx, cfg.Hkv)
+    run = fa4.DecodeRunner(q, caches[0], caches[1], pt, ctx, cfg.Hkv,
+                           p_fmt=fa4.FA4_P_NVFP4 if cfg.p_fmt == "nvfp4" else fa4.FA4_P_FP8)
     for _ in range(warmup):
         run.run()
     step_ms = _time_loop(run.run, steps)
@@ -226,6 +233,7 @@ def main():
     ap.add_argument("--workload", default=W.C1.name,
                     choices=[c.name for c in W.WORKLOADS + [W.C1_MX8] if isinstance(c, W.Prefill)])
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-p4", action="store_true", help="skip the decode steps with NVFP4 probabilities")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=8)
     ap.add_argument("--copy-probe", action="store_true")
@@ -272,17 +280,20 @@ def main():
     print(f"[bench] prefill {cfg.name}: step {step_ms:.4f} ms, attention {attn_ms:.4f} ms", file=sys.stderr,
           flush=True)
     if not args.no_decode:
-        for key, dcfg in (("decode", W.C3), ("decode_mxfp4", W.C3_MX)):
+        dec = [("decode", W.C3), ("decode_mxfp4", W.C3_MX)]
+        if not args.no_p4:
+            dec += [("decode_p4", W.C3_P4), ("decode_mxfp4_p4", W.C3_MX_P4)]
+        for key, dcfg in dec:
             d_step, d_kern, kv_bytes, tokens = time_decode(fa4, dcfg, args.steps, args.warmup)
             gbs = kv_bytes / (d_kern * 1e-3) / 1e9
-            kname = "decode_split_kernel<1>" if dcfg.kv_fmt == "nvfp4" else "decode_split_kernel<0>"
+            kname = "decode_split_kernel<%d, %d>" % (dcfg.kv_fmt == "nvfp4", dcfg.p_fmt == "nvfp4")
             line[key] = {
                 "metric": "decode KV GB/s", "workload": dcfg.name, "value": kv_bytes / (d_step * 1e-3) / 1e9,
                 "unit": "GB/s", "ms_per_step": d_step, "kv_bytes": kv_bytes, "context_tokens": tokens,
                 "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": gbs / HBM_PEAK_GBS, "traffic": recorded_traffic(kname),
                              "traffic_kernel": kname, "kernel": "decode_split+combine", "kernel_ms": d_kern}}
-            print(f"[bench] {key} ({dcfg.kv_fmt}): step {d_step:.4f} ms, kernels {d_kern:.4f} ms, {gbs:.0f} GB/s",
+            print(f"[bench] {key} ({dcfg.kv_fmt}, P {dcfg.p_fmt}): step {d_step:.4f} ms, kernels {d_kern:.4f} ms, {gbs:.0f} GB/s",
                   file=sys.stderr, flush=True)
             torch.cuda.empty_cache()
     if args.outlier:

@@ -22,6 +22,7 @@ FA4_OK, FA4_ERR_NULL, FA4_ERR_SHAPE, FA4_ERR_UNSUPPORTED, FA4_ERR_ALIGN, FA4_ERR
 FA4_F32, FA4_BF16 = 0, 1
 FA4_MXFP4, FA4_NVFP4, FA4_FP8_TOKEN, FA4_MXFP8 = 0, 1, 2, 3
 FA4_HADAMARD128, FA4_DUAL_RESIDUAL, FA4_SCALE_SEARCH = 1, 2, 4
+FA4_P_FP8, FA4_P_NVFP4 = 0, 1                      # decode probability formats
 
 EXPORTS = ["fa4_quantize_blockscaled", "fa4_smoothing_factors", "fa4_select_tiles", "fa4_attn_fwd", "fa4_decode_workspace_bytes",
            "fa4_decode_paged", "fa4_status_string", "fa4_last_error"]
@@ -56,7 +57,7 @@ class DecodeArgs(ctypes.Structure):
                 ("k_codes", _p), ("k_scales", _p), ("v_codes", _p), ("v_scales", _p),
                 ("k_tscale", _p), ("v_tscale", _p), ("page_table", _p), ("ctx_len", _p),
                 ("B", _i32), ("Hq", _i32), ("Hkv", _i32), ("d", _i32), ("page_size", _i32), ("max_pages", _i32),
-                ("num_pages", _i64), ("softmax_scale", _f32), ("o", _p)]
+                ("num_pages", _i64), ("softmax_scale", _f32), ("o", _p), ("p_fmt", _i32)]
 
 
 lib.fa4_quantize_blockscaled.argtypes = [ctypes.POINTER(QInput), _u32, ctypes.POINTER(QOutput),
@@ -248,7 +249,7 @@ def attn_fwd(q, k, v, causal, fmt, Hq, Hkv, Lq, Lk, d, B=1, bitmap=None, q_bf16=
 # ---------------------------------------------------------------------------------------------------- decode
 
 def decode_args(q1, q2, kcache, vcache, page_table, ctx_len, Hq, Hkv, d=128, page_size=64, softmax_scale=None,
-                out=None, fmt=FA4_NVFP4):
+                out=None, fmt=FA4_NVFP4, p_fmt=FA4_P_FP8):
     B = ctx_len.shape[0]
     if out is None:
         out = torch.empty(B, Hq, d, dtype=torch.float32, device=ctx_len.device)
@@ -260,7 +261,7 @@ def decode_args(q1, q2, kcache, vcache, page_table, ctx_len, Hq, Hkv, d=128, pag
                    vcache["codes"].data_ptr(), vcache["block_scales"].data_ptr(),
                    _ptr(kcache.get("scales")), _ptr(vcache.get("scales")),
                    page_table.data_ptr(), ctx_len.data_ptr(), B, Hq, Hkv, d, page_size, page_table.shape[1],
-                   kcache["codes"].shape[0], softmax_scale, out.data_ptr())
+                   kcache["codes"].shape[0], softmax_scale, out.data_ptr(), p_fmt)
     return a, out
 
 
@@ -270,11 +271,12 @@ def decode_workspace(a, device):
 
 
 def decode_paged(q1, q2, kcache, vcache, page_table, ctx_len, Hq, Hkv, d=128, page_size=64, softmax_scale=None,
-                 workspace=None, out=None, fmt=FA4_NVFP4):
+                 workspace=None, out=None, fmt=FA4_NVFP4, p_fmt=FA4_P_FP8):
     """Decode attention for one query token per sequence. q1/q2: dicts of the dual-residual query
-    ([B, Hq, 1, d] rows); kcache / vcache: paged dicts from quantize_paged(); all in format fmt."""
+    ([B, Hq, 1, d] rows); kcache / vcache: paged dicts from quantize_paged(); all in format fmt.
+    p_fmt: probability format, FA4_P_FP8 (0) or FA4_P_NVFP4."""
     a, out = decode_args(q1, q2, kcache, vcache, page_table, ctx_len, Hq, Hkv, d, page_size, softmax_scale, out,
-                         fmt)
+                         fmt, p_fmt)
     if workspace is None:
         workspace = decode_workspace(a, ctx_len.device)
     _check(lib.fa4_decode_paged(ctypes.byref(a), workspace.data_ptr(), workspace.numel(), _stream()),
@@ -309,9 +311,10 @@ def prefill(q, k, v, causal, fmt=FA4_MXFP4, hadamard=False, select=None, softmax
     return {"o": o, "lse": lse, "bitmap": bitmap, "counts": counts, "q": qq, "k": kq, "v": vq}
 
 
-def decode(q, kcache, vcache, page_table, ctx_len, Hkv, softmax_scale=None, workspace=None, out=None):
+def decode(q, kcache, vcache, page_table, ctx_len, Hkv, softmax_scale=None, workspace=None, out=None, p_fmt=FA4_P_FP8):
     """One decode step: q [B, Hq, d] (bf16 or float32) -> dual-residual query in the cache's format (NVFP4
-    or MXFP4, from kcache['fmt']) -> paged attention. Returns (o [B, Hq, d] float32, the quantized query)."""
+    or MXFP4, from kcache['fmt']) -> paged attention with probabilities in p_fmt (FA4_P_FP8 or
+    FA4_P_NVFP4). Returns (o [B, Hq, d] float32, the quantized query)."""
     B, Hq, d = q.shape
     fmt = kcache.get("fmt", FA4_NVFP4)
     # NVFP4 needs a tensor scale per (sequence, head): one group per row; MXFP4 rows are independent,
@@ -321,7 +324,7 @@ def decode(q, kcache, vcache, page_table, ctx_len, Hkv, softmax_scale=None, work
     q1 = {"codes": qq["codes"], "block_scales": qq["block_scales"], "scales": qq["scales"]}
     q2 = {"codes": qq["codes2"], "block_scales": qq["block_scales2"], "scales": qq["scales2"]}
     o = decode_paged(q1, q2, kcache, vcache, page_table, ctx_len, Hq, Hkv, d, softmax_scale=softmax_scale,
-                     workspace=workspace, out=out, fmt=fmt)
+                     workspace=workspace, out=out, fmt=fmt, p_fmt=p_fmt)
     return o, qq
 
 
@@ -436,7 +439,7 @@ class DecodeRunner:
     """Preallocated decode step: dual-residual query quantization (in the cache's format, NVFP4 or MXFP4)
     plus paged attention."""
 
-    def __init__(self, q, kcache, vcache, page_table, ctx_len, Hkv, softmax_scale=None):
+    def __init__(self, q, kcache, vcache, page_table, ctx_len, Hkv, softmax_scale=None, p_fmt=FA4_P_FP8):
         B, Hq, d = q.shape
         dev = q.device
         self.q = q
@@ -457,7 +460,7 @@ class DecodeRunner:
         self._qr = QOutput(fmt, self.q2["codes"].data_ptr(), self.q2["block_scales"].data_ptr(),
                            _ptr(self.q2["scales"]), None, None)
         self.args, self.o = decode_args(self.q1, self.q2, kcache, vcache, page_table, ctx_len, Hq, Hkv, d,
-                                        softmax_scale=softmax_scale, fmt=fmt)
+                                        softmax_scale=softmax_scale, fmt=fmt, p_fmt=p_fmt)
         self.ws = decode_workspace(self.args, dev)
         self._keep = (kcache, vcache, page_table, ctx_len)
 

@@ -47,8 +47,14 @@ struct DecArgs {
   int B, Hq, Hkv, max_pages, nsplit;
   int64_t num_pages;
   float scale;
+  float pscale;                                   // final factor of P^: 1/448 (FP8) or s_t (NVFP4)
   float *ws, *o;
 };
+
+// NVFP4 probabilities: a tile row of P' (largest element exactly 1) is one group, so its tensor scale
+// is fl32(1/2688) and the block scales are E4M3(amax_b / fl32(6 s_t)).
+constexpr float P4_ST = 1.0f / 2688.0f;
+constexpr float P4_SIX_ST = 6.0f * P4_ST;
 
 // 8 E2M1 codes (4 bytes) times an fp16 block scale, as exact fp16 values.
 __device__ __forceinline__ v8h expand8(uint32_t w, _Float16 sb) {
@@ -222,7 +228,7 @@ __device__ __forceinline__ v8h row_shl_v8h(v8h v) {
   return __builtin_bit_cast(v8h, x);
 }
 
-template <int FMT>
+template <int FMT, int PF>
 __global__ void __launch_bounds__(DEC_THREADS) decode_split_kernel(DecArgs a) {
   __shared__ float part[DEC_SLOTS][4][DEC_PART];
   // Workgroup order: (sequence, key head) fastest, split slowest. Workgroups are handed to the 8 XCDs
@@ -350,26 +356,66 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_split_kernel(DecArgs a) {
       mt = fmaxf(mt, shfl_xor_f(mt, 8));
       mt = fmaxf(mt, shfl_xor_f(mt, 16));
       mt = fmaxf(mt, shfl_xor_f(mt, 32));
-      // ---- P' = 2^(x - m~), P^ = E4M3(448 P') (exact in fp16), in the B layout of quarter
-      // 2 rep + kq: element 4 (kk & 1) + i for kk = 2 kq + (kk & 1)
+      // ---- P' = 2^(x - m~) and P^ in the B layout of quarter 2 rep + kq: element 4 (kk & 1) + i for
+      // kk = 2 kq + (kk & 1)
       v8h popl[2];
+      if constexpr (PF == FA4_P_NVFP4) {
+        // P^ in NVFP4: key block 4 rep + kk (16 keys: i = 0..3 here, the rest in lane groups g ^ 1,
+        // g ^ 2, g ^ 3) gets s_b = E4M3(amax_b / (6 s_t)) and codes E2M1(P' / (s_b s_t)) (hardware
+        // conversion: nearest even, saturating, sign kept); E2M1 * s_b (at most 6 significant bits,
+        // exact in fp16 and bf16) enters the MFMA and s_t is applied with the final normalization.
+        v2h pr[2][4];
 #pragma unroll
-      for (int kq = 0; kq < 2; kq++) {
-        v2h pr[4];
+        for (int kk = 0; kk < 4; kk++) {
+          float p[4];
 #pragma unroll
-        for (int u = 0; u < 4; u++) {
-          const int kk = 2 * kq + (u >> 1), i0 = 2 * (u & 1);
-          const float p0 = __builtin_amdgcn_exp2f(x[kk][i0] - mt);
-          const float p1 = __builtin_amdgcn_exp2f(x[kk][i0 + 1] - mt);
-          lsum += p0 + p1;
-          const uint32_t pc = e4m3_encode2(448.0f * p0, 448.0f * p1);
+          for (int i = 0; i < 4; i++) p[i] = __builtin_amdgcn_exp2f(x[kk][i] - mt);
+          lsum += (p[0] + p[1]) + (p[2] + p[3]);
+          float bm = fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3]));
+          bm = fmaxf(bm, shfl_xor_f(bm, 16));
+          bm = fmaxf(bm, shfl_xor_f(bm, 32));
+          const float sbv = e4m3_value(e4m3_encode(bm / P4_SIX_ST));
+          const float rq = sbv > 0.0f ? 1.0f / (sbv * P4_ST) : 0.0f;
+          uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, p[0] * rq, p[1] * rq, 1.0f, 0);
+          w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, p[2] * rq, p[3] * rq, 1.0f, 1);
+          v2h r0, r1;
           if constexpr (FMT == FA4_NVFP4) {
-            pr[u] = e4m3x2_f16(pc);
-          } else {                                            // bf16 bits in the same registers
-            pr[u] = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pc, 1.0f, false));
+            const _Float16 sbh = (_Float16)sbv;
+            r0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * (v2h){sbh, sbh};
+            r1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * (v2h){sbh, sbh};
+          } else {                                            // bf16 bits: the values are exact in bf16
+            const auto f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+            const auto f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+            r0 = __builtin_bit_cast(v2h, (__float_as_uint(f0[0] * sbv) >> 16) | (__float_as_uint(f0[1] * sbv) & 0xffff0000u));
+            r1 = __builtin_bit_cast(v2h, (__float_as_uint(f1[0] * sbv) >> 16) | (__float_as_uint(f1[1] * sbv) & 0xffff0000u));
           }
+          pr[kk >> 1][2 * (kk & 1)] = r0;
+          pr[kk >> 1][2 * (kk & 1) + 1] = r1;
         }
-        popl[kq] = (v8h){pr[0][0], pr[0][1], pr[1][0], pr[1][1], pr[2][0], pr[2][1], pr[3][0], pr[3][1]};
+#pragma unroll
+        for (int kq = 0; kq < 2; kq++)
+          popl[kq] = (v8h){pr[kq][0][0], pr[kq][0][1], pr[kq][1][0], pr[kq][1][1],
+                           pr[kq][2][0], pr[kq][2][1], pr[kq][3][0], pr[kq][3][1]};
+      } else {
+        // P^ = E4M3(448 P'), exact in fp16 (bf16 for MXFP4 caches)
+#pragma unroll
+        for (int kq = 0; kq < 2; kq++) {
+          v2h pr[4];
+#pragma unroll
+          for (int u = 0; u < 4; u++) {
+            const int kk = 2 * kq + (u >> 1), i0 = 2 * (u & 1);
+            const float p0 = __builtin_amdgcn_exp2f(x[kk][i0] - mt);
+            const float p1 = __builtin_amdgcn_exp2f(x[kk][i0 + 1] - mt);
+            lsum += p0 + p1;
+            const uint32_t pc = e4m3_encode2(448.0f * p0, 448.0f * p1);
+            if constexpr (FMT == FA4_NVFP4) {
+              pr[u] = e4m3x2_f16(pc);
+            } else {                                            // bf16 bits in the same registers
+              pr[u] = __builtin_bit_cast(v2h, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pc, 1.0f, false));
+            }
+          }
+          popl[kq] = (v8h){pr[0][0], pr[0][1], pr[1][0], pr[1][1], pr[2][0], pr[2][1], pr[3][0], pr[3][1]};
+        }
       }
       lsum += shfl_xor_f(lsum, 8);
       lsum += shfl_xor_f(lsum, 16);
@@ -455,7 +501,7 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_split_kernel(DecArgs a) {
 }
 
 // Merge the splits of each (sequence, head): O = sum e^(m_s - m) O_s / sum e^(m_s - m) l_s, times
-// the V tensor scale / 448 (P^ carried a factor 448). A split's (m, l) are read by all threads of
+// the V tensor scale and P^'s factor (1/448 for FP8 probabilities, s_t for NVFP4 ones). A split's (m, l) are read by all threads of
 // the block alike; the loop is unrolled so that the loads of several splits are in flight at once.
 __global__ void __launch_bounds__(128) decode_combine_kernel(DecArgs a) {
   __shared__ float red[2];
@@ -478,7 +524,7 @@ __global__ void __launch_bounds__(128) decode_combine_kernel(DecArgs a) {
     l += f * p[1];
     o += f * p[2 + d];
   }
-  const float vts = (a.vt ? a.vt[(int64_t)b * a.Hkv + kvh] : 1.0f) * (1.0f / 448.0f);
+  const float vts = (a.vt ? a.vt[(int64_t)b * a.Hkv + kvh] : 1.0f) * a.pscale;
   a.o[((int64_t)b * a.Hq + h) * 128 + d] = o / l * vts;
 }
 
@@ -495,6 +541,7 @@ static DecArgs make_dec(const fa4_decode_args *p, void *ws) {
   x.nsplit = (p->max_pages * 64 + DEC_SPLIT - 1) / DEC_SPLIT;
   x.num_pages = p->num_pages;
   x.scale = p->softmax_scale;
+  x.pscale = p->p_fmt == FA4_P_NVFP4 ? P4_ST : 1.0f / 448.0f;
   x.ws = static_cast<float *>(ws); x.o = p->o;
   return x;
 }
@@ -508,8 +555,14 @@ hipError_t launch_decode(const fa4_decode_args *p, void *ws, hipStream_t s) {
   if (p->B == 0) return hipSuccess;
   const DecArgs x = make_dec(p, ws);
   const dim3 grid((unsigned)((int64_t)x.nsplit * x.B * x.Hkv));
-  if (p->fmt == FA4_MXFP4) hipLaunchKernelGGL(decode_split_kernel<FA4_MXFP4>, grid, dim3(DEC_THREADS), 0, s, x);
-  else hipLaunchKernelGGL(decode_split_kernel<FA4_NVFP4>, grid, dim3(DEC_THREADS), 0, s, x);
+  const bool p4 = p->p_fmt == FA4_P_NVFP4;
+  if (p->fmt == FA4_MXFP4) {
+    if (p4) hipLaunchKernelGGL((decode_split_kernel<FA4_MXFP4, FA4_P_NVFP4>), grid, dim3(DEC_THREADS), 0, s, x);
+    else hipLaunchKernelGGL((decode_split_kernel<FA4_MXFP4, FA4_P_FP8>), grid, dim3(DEC_THREADS), 0, s, x);
+  } else {
+    if (p4) hipLaunchKernelGGL((decode_split_kernel<FA4_NVFP4, FA4_P_NVFP4>), grid, dim3(DEC_THREADS), 0, s, x);
+    else hipLaunchKernelGGL((decode_split_kernel<FA4_NVFP4, FA4_P_FP8>), grid, dim3(DEC_THREADS), 0, s, x);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(x.Hq, x.B), dim3(128), 0, s, x);

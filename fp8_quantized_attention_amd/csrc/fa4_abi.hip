@@ -209,6 +209,8 @@ size_t fa4_decode_workspace_bytes(const fa4_decode_args *a) {
 fa4_status fa4_decode_paged(const fa4_decode_args *a, void *ws, size_t ws_bytes, void *stream) {
   REQUIRE(a, FA4_ERR_NULL, "decode: args is NULL");
   REQUIRE(a->fmt == FA4_NVFP4 || a->fmt == FA4_MXFP4, FA4_ERR_UNSUPPORTED, "decode: format %d", a->fmt);
+  REQUIRE(a->p_fmt == FA4_P_FP8 || a->p_fmt == FA4_P_NVFP4, FA4_ERR_UNSUPPORTED, "decode: probability format %d",
+          a->p_fmt);
   REQUIRE(a->d == 128, FA4_ERR_UNSUPPORTED, "decode: d=%d (128)", a->d);
   REQUIRE(a->page_size == 64, FA4_ERR_UNSUPPORTED, "decode: page_size=%d (64)", a->page_size);
   REQUIRE(a->B >= 0 && a->Hkv >= 1 && a->Hq == 4 * a->Hkv, FA4_ERR_UNSUPPORTED,

@@ -43,6 +43,7 @@ typedef enum {
 
 enum { FA4_F32 = 0, FA4_BF16 = 1 };                      /* input element types       */
 enum { FA4_MXFP4 = 0, FA4_NVFP4 = 1, FA4_FP8_TOKEN = 2, FA4_MXFP8 = 3 }; /* quantized formats */
+enum { FA4_P_FP8 = 0, FA4_P_NVFP4 = 1 };                   /* decode probability formats */
 enum { FA4_HADAMARD128 = 1u << 0, FA4_DUAL_RESIDUAL = 1u << 1, FA4_SCALE_SEARCH = 1u << 2 }; /* quantizer flags */
 
 /* ------------------------------------------------------------------------------------------------
@@ -222,6 +223,13 @@ fa4_status fa4_attn_fwd(const fa4_attn_args *a, void *stream);
  *              [d/32] E8M0; the four tensor-scale pointers are not read (may be NULL).
  * Other layouts: q1_codes/q2_codes [B][Hq][d/2]; k_codes/v_codes [num_pages][Hkv][page_size][d/2];
  * page_table [B][max_pages] (entries past ceil(ctx_len[b]/page_size) are not read); o [B][Hq][d] float.
+ * p_fmt selects the format of the probabilities before PV:
+ *   FA4_P_FP8 (0, the default): P^ = E4M3(448 P') as above.
+ *   FA4_P_NVFP4: FP4 with E4M3 scales per 16 keys (the case in which a block scale can round to zero).
+ *              Each tile row of P' (its largest element exactly 1) is one NVFP4 group: tensor scale
+ *              s_t = fl32(1/2688), block scale s_b = E4M3(amax_b / fl32(6 s_t)) per 16 keys from the
+ *              tile start, P^ = E2M1(P' / (s_b s_t)) * s_b * s_t, T = sum_c P^ v^_c. A block scale is
+ *              zero only when the block's largest probability is under 2^-10/448 of the tile's.
  * The work is split over key ranges; partial results go to a caller-provided workspace of
  * fa4_decode_workspace_bytes(a) bytes (256-byte aligned) and are merged by a second kernel.
  * Requirements: d = 128; page_size = 64; Hq / Hkv = 4; 1 <= ctx_len[b] <= max_pages * page_size.
@@ -237,6 +245,7 @@ typedef struct {
   int64_t num_pages;
   float softmax_scale;
   float *o;
+  int32_t p_fmt;                                /* FA4_P_FP8 (0) or FA4_P_NVFP4                 */
 } fa4_decode_args;
 
 size_t fa4_decode_workspace_bytes(const fa4_decode_args *a);

@@ -128,13 +128,15 @@ def decode_query_quant(cfg, seed):
     return q, (Q.dual_residual_quantize(rows) if cfg.kv_fmt == "nvfp4" else Q.dual_residual_quantize_mx(rows))
 
 
-def decode_reference(cfg, seed, layout, pairs, logical, q1, q2):
-    """Oracle O for the listed (b, h) pairs from contiguous dequantized rows."""
+def decode_reference(cfg, seed, layout, pairs, logical, q1, q2, scale=None):
+    """Oracle O for the listed (b, h) pairs from contiguous dequantized rows (softmax scale 1/sqrt(d)
+    unless given)."""
+    scale = 1.0 / np.sqrt(cfg.d) if scale is None else scale
     qhat = Dd.dequant_query(q1, q2, cfg.kv_fmt).reshape(cfg.B, cfg.Hq, cfg.d)
     group = cfg.Hq // cfg.Hkv
     out = []
     for (b, h) in pairs:
         kh = logical[(W.T_K, b, h // group)]
         vh = logical[(W.T_V, b, h // group)]
-        out.append(Dd.decode_one(qhat[b, h], kh, vh, 1.0 / np.sqrt(cfg.d), p_fmt=cfg.p_fmt).astype(np.float32))
+        out.append(Dd.decode_one(qhat[b, h], kh, vh, scale, p_fmt=cfg.p_fmt).astype(np.float32))
     return np.stack(out)

@@ -160,7 +160,7 @@ def _dec(**kw):
                 q2_tscale=256,
                 k_codes=256, k_scales=256, v_codes=256, v_scales=256, k_tscale=256, v_tscale=256,
                 page_table=256, ctx_len=256, B=4, Hq=32, Hkv=8, d=128, page_size=64, max_pages=8, num_pages=32,
-                softmax_scale=0.088, o=256)
+                softmax_scale=0.088, o=256, p_fmt=fa4.FA4_P_FP8)
     base.update(kw)
     return fa4.DecodeArgs(*[base[f] for f, _ in fa4.DecodeArgs._fields_])
 
@@ -180,6 +180,8 @@ def test_decode_rejects_before_launch():
     assert call(a, ws=520, n=need) == fa4.FA4_ERR_ALIGN
     assert call(_dec(B=0)) == fa4.FA4_OK
     assert call(_dec(fmt=fa4.FA4_FP8_TOKEN)) == fa4.FA4_ERR_UNSUPPORTED
+    assert call(_dec(p_fmt=2)) == fa4.FA4_ERR_UNSUPPORTED
+    assert call(_dec(p_fmt=fa4.FA4_P_NVFP4), ws=512, n=need - 1) == fa4.FA4_ERR_WORKSPACE
     # NVFP4 needs its tensor scales; MXFP4 has none (the pointers are not read) and 4-byte scale rows
     assert call(_dec(v_tscale=None)) == fa4.FA4_ERR_NULL
     mx = dict(fmt=fa4.FA4_MXFP4, q1_tscale=None, q2_tscale=None, k_tscale=None, v_tscale=None)

@@ -15,7 +15,7 @@ def fa4():
     return m
 
 
-def _gpu_decode(fa4, cfg, lay, seed=0):
+def _gpu_decode(fa4, cfg, lay, seed=0, scale=None):
     ctx = lay.ctx_len.cuda()
     pt = lay.page_table.cuda()
     caches = []
@@ -25,12 +25,14 @@ def _gpu_decode(fa4, cfg, lay, seed=0):
         caches.append(fa4.quantize_paged(x, fmt, ctx, pt, lay.num_pages))
         del x
     q = W.decode_query(cfg, seed).cuda()
-    o, _ = fa4.decode(q, caches[0], caches[1], pt, ctx, cfg.Hkv)
+    pf = fa4.FA4_P_NVFP4 if cfg.p_fmt == "nvfp4" else fa4.FA4_P_FP8
+    o, _ = fa4.decode(q, caches[0], caches[1], pt, ctx, cfg.Hkv, softmax_scale=scale, p_fmt=pf)
     torch.cuda.synchronize()
     return o.cpu().numpy(), caches
 
 
-FMTS = pytest.mark.parametrize("base", [W.C3, W.C3_MX], ids=["nvfp4", "mxfp4"])
+FMTS = pytest.mark.parametrize("base", [W.C3, W.C3_MX, W.C3_P4, W.C3_MX_P4],
+                               ids=["nvfp4", "mxfp4", "nvfp4_p4", "mxfp4_p4"])
 
 
 @FMTS
@@ -68,3 +70,27 @@ def test_full_size_decode_sampled(fa4, base):
     q, (q1, q2) = decode_query_quant(cfg, 0)
     ref = decode_reference(cfg, 0, lay, pairs, logical, q1, q2)
     assert_parity(np.stack([o[b, h] for b, h in pairs]), ref, "decode full size")
+
+
+@pytest.mark.parametrize("base", [W.C3_P4, W.C3_MX_P4], ids=["nvfp4_p4", "mxfp4_p4"])
+def test_decode_p4_peaked_softmax(fa4, base):
+    """A softmax scale 8x the usual makes many 16-key blocks of P' small against their tile maximum
+    (under 6 * 2^-10, where a block scale taken from amax/6 alone would round to zero): the per-tile
+    normalization must keep them, as the oracle does."""
+    cfg = base.scaled(B=3, Hq=8, Hkv=2, ctx_lo=300, ctx_hi=1500)
+    lay = W.decode_layout(cfg)
+    scale = 8.0 / np.sqrt(cfg.d)
+    o, _ = _gpu_decode(fa4, cfg, lay, scale=scale)
+    _, _, _, _, logical = decode_cache(cfg, lay, 0)
+    q, (q1, q2) = decode_query_quant(cfg, 0)
+    pairs = [(b, h) for b in range(cfg.B) for h in range(cfg.Hq)]
+    ref = decode_reference(cfg, 0, lay, pairs, logical, q1, q2, scale=scale)
+    assert_parity(np.stack([o[b, h] for b, h in pairs]), ref, "decode p4 peaked")
+    # the regime: in the first sequence's first head a third or more of the 16-key blocks lie under
+    # 6 * 2^-10
+    from oracle import decode as Dd
+    qhat = Dd.dequant_query(q1, q2, cfg.kv_fmt).reshape(cfg.B, cfg.Hq, cfg.d)
+    S = scale * (logical[(W.T_K, 0, 0)] @ qhat[0, 0])
+    L = len(S) - len(S) % 128
+    P = np.exp(S[:L].reshape(-1, 128) - S[:L].reshape(-1, 128).max(axis=1, keepdims=True))
+    assert (P.reshape(-1, 16).max(axis=1) < 6 * 2.0 ** -10).mean() > 0.3

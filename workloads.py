@@ -91,6 +91,7 @@ C1_MX8 = replace(C1, name="prefill_4k_causal_mxfp8", qk_fmt="mxfp8")
 # sequences, lengths, pages and values as C3 (same workload id, hence the same seeds).
 C3_MX = replace(C3, name="decode_paged_mxfp4_gqa", kv_fmt="mxfp4")
 C3_P4 = replace(C3, name="decode_paged_nvfp4_gqa_p4", p_fmt="nvfp4")
+C3_MX_P4 = replace(C3_MX, name="decode_paged_mxfp4_gqa_p4", p_fmt="nvfp4")
 
 
 def _chunk(seed, wl, tensor, b, h, rows, d, outliers, dtype):
