@@ -62,19 +62,20 @@ def quantize_p_nvfp4(p):
     return nvfp4_dequantize(codes, sb, st)[0, 0, :n]
 
 
-def decode_one(q_hat, k_hat, v_hat, scale, chunk=None, round_p=True, p_fmt="fp8"):
-    """O for one query row against L keys. chunk: optional split length (multiple of 128) whose
-    partial results (m, l, O) are merged afterwards; the merged result equals the single pass.
-    p_fmt: "fp8" (P^ = E4M3(448 P')) or "nvfp4" (quantize_p_nvfp4)."""
+def decode_one(q_hat, k_hat, v_hat, scale, chunk=None, round_p=True, p_fmt="fp8", tile=TILE):
+    """O for one query row against L keys (v_hat may be narrower than k_hat). chunk: optional split
+    length (multiple of the tile) whose partial results (m, l, O) are merged afterwards; the merged
+    result equals the single pass. p_fmt: "fp8" (P^ = E4M3(448 P')) or "nvfp4" (quantize_p_nvfp4).
+    tile: keys per probability tile (128; one 64-key page for the MLA geometry)."""
     L = k_hat.shape[0]
     if chunk is None:
         chunk = max(L, 1)
-    assert chunk % TILE == 0 or chunk >= L
+    assert chunk % tile == 0 or chunk >= L
     parts = []
     for s0 in range(0, L, chunk):
         ms, ls, Ts = [], [], []
-        for t0 in range(s0, min(s0 + chunk, L), TILE):
-            cs = np.arange(t0, min(t0 + TILE, L, s0 + chunk))
+        for t0 in range(s0, min(s0 + chunk, L), tile):
+            cs = np.arange(t0, min(t0 + tile, L, s0 + chunk))
             S = scale * (k_hat[cs] @ q_hat)
             m = S.max()
             P = np.exp(S - m)
@@ -141,4 +142,45 @@ def decode_paged(q1, q2, k_pages, v_pages, k_tscale, v_tscale, page_table, ctx_l
             cache = {(b, kv): (k_hat, v_hat)}
         k_hat, v_hat = cache[(b, kv)]
         O[b, h] = fp32(decode_one(qhat[b, h], k_hat, v_hat, scale, chunk=chunk, round_p=round_p, p_fmt=p_fmt))
+    return O
+
+
+# ----------------------------------------------------------------------------------------------- MLA
+
+MLA_SLICE = 64          # columns per slice of the latent cache's pages
+
+
+def gather_mla_rows(codes, scales, page_table_b, L, page_size=64):
+    """MXFP4 codes [L, d/2] and E8M0 scales [L, d/32] of one sequence's latent rows, read through its
+    page table from column-sliced pages: codes [P][d/64][page_size][32], scales [P][d/64][page_size][2]
+    (slice j holds columns 64 j .. 64 j + 63 of every row of the page)."""
+    c = np.arange(L)
+    phys = np.asarray(page_table_b)[c // page_size]
+    rc = codes[phys, :, c % page_size]
+    rs = scales[phys, :, c % page_size]
+    return rc.reshape(L, -1), rs.reshape(L, -1)
+
+
+def decode_mla(q1, q2, codes, scales, page_table, ctx_len, Hq, d_v, scale, page_size=64, pairs=None,
+               chunk=None, round_p=True):
+    """Decode in the MLA geometry ("BitDecoding-FP4" covers GQA and MLA attention; the geometry is
+    not spelled out there): every query head of a sequence attends to one shared latent row per
+    token, which is the key (all d values, the latent part and the rotary part) and whose first d_v
+    values are the value. The cache is MXFP4 (E8M0 per 32 along the row); the query of each head is
+    the dual residual pair (q1, q2 = (codes [B*Hq, d/2], E8M0 [B*Hq, d/32])) of its absorbed form.
+    Probability tiles are one 64-key page. Returns O float32 [B, Hq, d_v] (pairs: optional subset of
+    (b, h) to compute; the rest stay zero)."""
+    B = len(ctx_len)
+    d = 2 * q1[0].shape[-1]
+    qhat = (mxfp4_dequantize(*q1) + mxfp4_dequantize(*q2)).reshape(B, Hq, d)
+    O = np.zeros((B, Hq, d_v), dtype=np.float32)
+    pairs = [(b, h) for b in range(B) for h in range(Hq)] if pairs is None else pairs
+    rows = {}
+    for (b, h) in pairs:
+        if b not in rows:
+            k_hat = mxfp4_dequantize(*gather_mla_rows(codes, scales, page_table[b], int(ctx_len[b]), page_size))
+            rows = {b: k_hat}
+        k_hat = rows[b]
+        O[b, h] = fp32(decode_one(qhat[b, h], k_hat, k_hat[:, :d_v], scale, chunk=chunk, round_p=round_p,
+                                  tile=page_size))
     return O

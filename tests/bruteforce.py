@@ -185,14 +185,15 @@ def attention_rows(rows, Q, K, Vc, sv, Qo, Ko, Vo, sel, Lq, Lk, causal, scale, r
     return out
 
 
-def decode_row(q, K, V, scale, round_p=True, p_fmt="fp8"):
-    """O9 by loops for one query row over len(K) keys, tiles of 128 from 0. p_fmt "nvfp4": each
-    tile's probabilities (largest exactly 1) form one NVFP4 group, P^ its values, T = sum P^ v."""
-    d = len(q)
+def decode_row(q, K, V, scale, round_p=True, p_fmt="fp8", tile=128):
+    """O9 by loops for one query row over len(K) keys, tiles of `tile` keys from 0 (V rows may be
+    shorter than K rows). p_fmt "nvfp4": each tile's probabilities (largest exactly 1) form one NVFP4
+    group, P^ its values, T = sum P^ v."""
+    d = len(V[0])
     terms = []
-    for t0 in range(0, len(K), 128):
-        cols = range(t0, min(t0 + 128, len(K)))
-        S = {c: scale * sum(q[t] * K[c][t] for t in range(d)) for c in cols}
+    for t0 in range(0, len(K), tile):
+        cols = range(t0, min(t0 + tile, len(K)))
+        S = {c: scale * sum(q[t] * K[c][t] for t in range(len(q))) for c in cols}
         m = max(S.values())
         P = {c: math.exp(S[c] - m) for c in cols}
         T = [0.0] * d

@@ -68,6 +68,8 @@ class Decode:
     ctx_hi: int
     kv_fmt: str = "nvfp4"        # format of the paged K/V cache and of the query residuals
     p_fmt: str = "fp8"           # format of the probabilities before PV: "fp8" or "nvfp4"
+    d_v: int = 0                 # MLA geometry: value width (the first d_v of each latent row); 0 = GQA
+    softmax_scale: float = 0.0   # 0: 1/sqrt(d)
 
     def scaled(self, **kw):
         return replace(self, **kw)
@@ -92,6 +94,11 @@ C1_MX8 = replace(C1, name="prefill_4k_causal_mxfp8", qk_fmt="mxfp8")
 C3_MX = replace(C3, name="decode_paged_mxfp4_gqa", kv_fmt="mxfp4")
 C3_P4 = replace(C3, name="decode_paged_nvfp4_gqa_p4", p_fmt="nvfp4")
 C3_MX_P4 = replace(C3_MX, name="decode_paged_mxfp4_gqa_p4", p_fmt="nvfp4")
+# MLA-shaped decode: 16 query heads (one tensor-parallel shard of a 128-head model) over one shared
+# latent row per token, 512 latent + 64 rotary values (the key); the value is the latent part. The
+# softmax scale is that of the un-absorbed 128 + 64 query-key width. Contexts and pages as C3.
+C5_MLA = Decode("decode_paged_mla_mxfp4", 5, B=64, Hq=16, Hkv=1, d=576, page_size=64, ctx_lo=8192,
+                ctx_hi=32768, kv_fmt="mxfp4", d_v=512, softmax_scale=192 ** -0.5)
 
 
 def _chunk(seed, wl, tensor, b, h, rows, d, outliers, dtype):
