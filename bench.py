@@ -13,6 +13,8 @@ attention kernel, inputs resident in HBM. `value` is prefill attention TFLOP/s o
   decode_p4, decode_mxfp4_p4
                 the two decode steps with the probabilities in NVFP4 (E4M3 scales per 16 keys)
                 instead of FP8;
+  decode_mla    decode in the MLA geometry (64 sequences, 16 heads over one shared 576-wide MXFP4
+                latent row per token, value = its first 512 values, contexts 8K-32K): KV GB/s;
   k_quant       (--outlier) quantization of the 128K-token chunked-prefill keys (NVFP4 + Hadamard)
                 plain, with static smoothing, and with smoothing + the per-block scale search;
   cpu_baseline  the CPU oracle (float64 numpy) on a bounded sample of the same workload.
@@ -60,6 +62,7 @@ KERNEL_SOURCES = {
     "decode_split_kernel<0, 0>": ["decode.hip", "fa4_device.h"],
     "decode_split_kernel<1, 1>": ["decode.hip", "fa4_device.h"],
     "decode_split_kernel<0, 1>": ["decode.hip", "fa4_device.h"],
+    "decode_mla_kernel": ["decode_mla.hip", "fa4_device.h"],
 }
 
 
@@ -182,6 +185,24 @@ def time_decode(fa4, cfg, steps, warmup):
     return step_ms, kern_ms, kv_bytes, int(lay.ctx_len.sum())
 
 
+def time_decode_mla(fa4, cfg, steps, warmup):
+    lay = W.decode_layout(cfg)
+    ctx, pt = lay.ctx_len.cuda(), lay.page_table.cuda()
+    x = W.decode_kv_padded(cfg, lay, W.T_K, device="cuda")[:, 0].contiguous()
+    cache = fa4.quantize_paged_mla(x, ctx, pt, lay.num_pages)
+    del x
+    torch.cuda.empty_cache()
+    q = W.decode_query(cfg).cuda()
+    run = fa4.DecodeMlaRunner(q, cache, pt, ctx, cfg.softmax_scale)
+    for _ in range(warmup):
+        run.run()
+    step_ms = _time_loop(run.run, steps)
+    kern_ms = _time_loop(run.attention, steps)
+    # one latent row per token: d/2 code bytes + d/32 E8M0 bytes
+    kv_bytes = float(lay.ctx_len.double().sum()) * (cfg.d // 2 + cfg.d // 32)
+    return step_ms, kern_ms, kv_bytes, int(lay.ctx_len.sum())
+
+
 def time_k_quant(fa4, steps, warmup):
     """Outlier-aware key quantization on the chunked-prefill workload's keys (B1, 8 key heads, 131072
     tokens, d128, bf16 with x20 outlier channels): NVFP4 + Hadamard, plain / smoothing / smoothing + search.
@@ -296,6 +317,18 @@ def main():
             print(f"[bench] {key} ({dcfg.kv_fmt}, P {dcfg.p_fmt}): step {d_step:.4f} ms, kernels {d_kern:.4f} ms, {gbs:.0f} GB/s",
                   file=sys.stderr, flush=True)
             torch.cuda.empty_cache()
+        dcfg = W.C5_MLA
+        d_step, d_kern, kv_bytes, tokens = time_decode_mla(fa4, dcfg, args.steps, args.warmup)
+        gbs = kv_bytes / (d_kern * 1e-3) / 1e9
+        line["decode_mla"] = {
+            "metric": "decode KV GB/s", "workload": dcfg.name, "value": kv_bytes / (d_step * 1e-3) / 1e9,
+            "unit": "GB/s", "ms_per_step": d_step, "kv_bytes": kv_bytes, "context_tokens": tokens,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": recorded_traffic("decode_mla_kernel"),
+                         "traffic_kernel": "decode_mla_kernel", "kernel": "decode_mla+combine", "kernel_ms": d_kern}}
+        print(f"[bench] decode_mla (mxfp4): step {d_step:.4f} ms, kernels {d_kern:.4f} ms, {gbs:.0f} GB/s",
+              file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
     if args.outlier:
         line["k_quant"] = time_k_quant(fa4, args.steps, args.warmup)
     if not args.no_cpu_baseline:

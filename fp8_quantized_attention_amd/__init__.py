@@ -57,7 +57,7 @@ class DecodeArgs(ctypes.Structure):
                 ("k_codes", _p), ("k_scales", _p), ("v_codes", _p), ("v_scales", _p),
                 ("k_tscale", _p), ("v_tscale", _p), ("page_table", _p), ("ctx_len", _p),
                 ("B", _i32), ("Hq", _i32), ("Hkv", _i32), ("d", _i32), ("page_size", _i32), ("max_pages", _i32),
-                ("num_pages", _i64), ("softmax_scale", _f32), ("o", _p), ("p_fmt", _i32)]
+                ("num_pages", _i64), ("softmax_scale", _f32), ("o", _p), ("p_fmt", _i32), ("d_v", _i32)]
 
 
 lib.fa4_quantize_blockscaled.argtypes = [ctypes.POINTER(QInput), _u32, ctypes.POINTER(QOutput),
@@ -261,7 +261,7 @@ def decode_args(q1, q2, kcache, vcache, page_table, ctx_len, Hq, Hkv, d=128, pag
                    vcache["codes"].data_ptr(), vcache["block_scales"].data_ptr(),
                    _ptr(kcache.get("scales")), _ptr(vcache.get("scales")),
                    page_table.data_ptr(), ctx_len.data_ptr(), B, Hq, Hkv, d, page_size, page_table.shape[1],
-                   kcache["codes"].shape[0], softmax_scale, out.data_ptr(), p_fmt)
+                   kcache["codes"].shape[0], softmax_scale, out.data_ptr(), p_fmt, 0)
     return a, out
 
 
@@ -282,6 +282,94 @@ def decode_paged(q1, q2, kcache, vcache, page_table, ctx_len, Hq, Hkv, d=128, pa
     _check(lib.fa4_decode_paged(ctypes.byref(a), workspace.data_ptr(), workspace.numel(), _stream()),
            "fa4_decode_paged")
     return out
+
+
+# ---------------------------------------------------------------------------------------------------- MLA decode
+
+MLA_D, MLA_DV, MLA_H = 576, 512, 16
+
+
+def quantize_paged_mla(x, ctx_len, page_table, num_pages, page_size=64):
+    """MXFP4 latent cache from a padded [B, Lmax, 576] tensor (rows r < ctx_len[b] exist): column-sliced
+    pages, codes [num_pages, 9, page_size, 32] and E8M0 scales [num_pages, 9, page_size, 2] (the rows
+    quantized as nine 64-wide heads)."""
+    assert x.is_cuda and x.is_contiguous() and x.shape[-1] == MLA_D
+    B, R, d = x.shape
+    ns = d // 64
+    dev = x.device
+    out = {"fmt": FA4_MXFP4,
+           "codes": torch.zeros(num_pages, ns, page_size, 32, dtype=torch.uint8, device=dev),
+           "block_scales": torch.zeros(num_pages, ns, page_size, 2, dtype=torch.uint8, device=dev)}
+    qin = QInput(x.data_ptr(), _dtype_code(x), 64, B, ns, R, R * d, 64, d, ctx_len.data_ptr(), page_table.data_ptr(),
+                 page_size, page_table.shape[1], num_pages, None)
+    qout = QOutput(FA4_MXFP4, out["codes"].data_ptr(), out["block_scales"].data_ptr(), None, None, None)
+    _check(lib.fa4_quantize_blockscaled(ctypes.byref(qin), 0, ctypes.byref(qout), None, None, _stream()),
+           "fa4_quantize_blockscaled(paged MLA)")
+    return out
+
+
+def mla_decode_args(q1, q2, cache, page_table, ctx_len, softmax_scale, out=None):
+    B = ctx_len.shape[0]
+    if out is None:
+        out = torch.empty(B, MLA_H, MLA_DV, dtype=torch.float32, device=ctx_len.device)
+    a = DecodeArgs(FA4_MXFP4, q1["codes"].data_ptr(), q1["block_scales"].data_ptr(), None,
+                   q2["codes"].data_ptr(), q2["block_scales"].data_ptr(), None,
+                   cache["codes"].data_ptr(), cache["block_scales"].data_ptr(), None, None, None, None,
+                   page_table.data_ptr(), ctx_len.data_ptr(), B, MLA_H, 1, MLA_D, cache["codes"].shape[2],
+                   page_table.shape[1], cache["codes"].shape[0], softmax_scale, out.data_ptr(), FA4_P_FP8, MLA_DV)
+    return a, out
+
+
+def decode_mla(q, cache, page_table, ctx_len, softmax_scale, workspace=None, out=None):
+    """One decode step in the MLA geometry: q [B, 16, 576] absorbed queries (bf16 or float32) -> MXFP4
+    dual residual -> attention over the shared latent rows (key: all 576 values, value: the first 512).
+    Returns (o [B, 16, 512] float32, the quantized query)."""
+    B, H, d = q.shape
+    assert H == MLA_H and d == MLA_D
+    qq = quantize(q.reshape(1, 1, B * H * (d // 64), 64), FA4_MXFP4, dual=True)
+    q1 = {"codes": qq["codes"], "block_scales": qq["block_scales"]}
+    q2 = {"codes": qq["codes2"], "block_scales": qq["block_scales2"]}
+    a, out = mla_decode_args(q1, q2, cache, page_table, ctx_len, softmax_scale, out)
+    if workspace is None:
+        workspace = decode_workspace(a, ctx_len.device)
+    _check(lib.fa4_decode_paged(ctypes.byref(a), workspace.data_ptr(), workspace.numel(), _stream()),
+           "fa4_decode_paged(MLA)")
+    return out, qq
+
+
+class DecodeMlaRunner:
+    """Preallocated MLA decode step: MXFP4 dual-residual query quantization plus paged attention."""
+
+    def __init__(self, q, cache, page_table, ctx_len, softmax_scale):
+        B, H, d = q.shape
+        assert H == MLA_H and d == MLA_D and q.is_contiguous()
+        dev = q.device
+        rows = B * H * (d // 64)
+        u8 = dict(dtype=torch.uint8, device=dev)
+        self.q = q
+        self.q1 = {"codes": torch.empty(B, H, d // 2, **u8), "block_scales": torch.empty(B, H, d // 32, **u8)}
+        self.q2 = {k: torch.empty_like(t) for k, t in self.q1.items()}
+        self._qi = QInput(q.data_ptr(), _dtype_code(q), 64, 1, 1, rows, rows * 64, rows * 64, 64, None, None, 0, 0, 0,
+                          None)
+        self._qo = QOutput(FA4_MXFP4, self.q1["codes"].data_ptr(), self.q1["block_scales"].data_ptr(), None, None, None)
+        self._qr = QOutput(FA4_MXFP4, self.q2["codes"].data_ptr(), self.q2["block_scales"].data_ptr(), None, None, None)
+        self.args, self.o = mla_decode_args(self.q1, self.q2, cache, page_table, ctx_len, softmax_scale)
+        self.ws = decode_workspace(self.args, dev)
+        self._keep = (cache, page_table, ctx_len)
+
+    def quantize(self, stream=None):
+        _check(lib.fa4_quantize_blockscaled(ctypes.byref(self._qi), FA4_DUAL_RESIDUAL, ctypes.byref(self._qo),
+                                            ctypes.byref(self._qr), None, _stream() if stream is None else stream),
+               "fa4_quantize_blockscaled")
+
+    def attention(self, stream=None):
+        _check(lib.fa4_decode_paged(ctypes.byref(self.args), self.ws.data_ptr(), self.ws.numel(),
+                                    _stream() if stream is None else stream), "fa4_decode_paged(MLA)")
+
+    def run(self):
+        self.quantize()
+        self.attention()
+        return self.o
 
 
 # ---------------------------------------------------------------------------------------------------- pipelines

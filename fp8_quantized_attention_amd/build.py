@@ -10,7 +10,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfa4.so")
-SOURCES = ["fa4_abi.hip", "quantize.hip", "select.hip", "attn_fwd.hip", "decode.hip"]
+SOURCES = ["fa4_abi.hip", "quantize.hip", "select.hip", "attn_fwd.hip", "decode.hip", "decode_mla.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

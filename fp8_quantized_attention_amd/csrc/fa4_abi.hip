@@ -203,11 +203,37 @@ fa4_status fa4_smoothing_factors(const fa4_qinput *q, const fa4_qinput *k, float
 
 size_t fa4_decode_workspace_bytes(const fa4_decode_args *a) {
   if (!a || a->B <= 0 || a->Hkv <= 0 || a->max_pages <= 0) return 0;
-  return fa4::decode_workspace_bytes(a);
+  return a->d_v != 0 ? fa4::decode_mla_workspace_bytes(a) : fa4::decode_workspace_bytes(a);
+}
+
+static fa4_status decode_mla(const fa4_decode_args *a, void *ws, size_t ws_bytes, void *stream) {
+  REQUIRE(a->d_v == fa4::MLA_DV && a->d == fa4::MLA_D, FA4_ERR_UNSUPPORTED, "decode (MLA): d=%d d_v=%d (576, 512)",
+          a->d, a->d_v);
+  REQUIRE(a->fmt == FA4_MXFP4 && a->p_fmt == FA4_P_FP8, FA4_ERR_UNSUPPORTED,
+          "decode (MLA): needs an MXFP4 cache and FP8 probabilities (fmt=%d p_fmt=%d)", a->fmt, a->p_fmt);
+  REQUIRE(a->Hq == fa4::MLA_H && a->Hkv == 1, FA4_ERR_UNSUPPORTED, "decode (MLA): needs Hq=16, Hkv=1 (Hq=%d Hkv=%d)",
+          a->Hq, a->Hkv);
+  REQUIRE(a->page_size == 64, FA4_ERR_UNSUPPORTED, "decode (MLA): page_size=%d (64)", a->page_size);
+  REQUIRE(a->B >= 0 && a->B <= 65535, FA4_ERR_SHAPE, "decode (MLA): B=%d", a->B);
+  REQUIRE(a->max_pages >= 1 && a->num_pages >= 1, FA4_ERR_SHAPE, "decode (MLA): max_pages and num_pages >= 1");
+  REQUIRE((int64_t)a->max_pages * 64 <= ((int64_t)1 << 30), FA4_ERR_SHAPE, "decode (MLA): context too long");
+  REQUIRE(((int64_t)a->max_pages + 31) / 32 * a->B < ((int64_t)1 << 31), FA4_ERR_SHAPE, "decode (MLA): grid too large");
+  if (a->B == 0) return ok();
+  REQUIRE(a->q1_codes && a->q1_scales && a->q2_codes && a->q2_scales && a->k_codes && a->k_scales &&
+              a->page_table && a->ctx_len && a->o,
+          FA4_ERR_NULL, "decode (MLA): a required pointer is NULL");
+  const void *ptrs16[] = {a->q1_codes, a->q2_codes, a->k_codes, a->k_scales};
+  for (const void *p : ptrs16)
+    REQUIRE(aligned(p, 16), FA4_ERR_ALIGN, "decode (MLA): code and cache scale arrays must be 16-byte aligned");
+  const size_t need = fa4::decode_mla_workspace_bytes(a);
+  REQUIRE(ws && ws_bytes >= need, FA4_ERR_WORKSPACE, "decode (MLA): workspace %zu bytes, %zu needed", ws_bytes, need);
+  REQUIRE(aligned(ws, 256), FA4_ERR_ALIGN, "decode (MLA): workspace must be 256-byte aligned");
+  return hip_status(fa4::launch_decode_mla(a, ws, (hipStream_t)stream), "decode (MLA) launch");
 }
 
 fa4_status fa4_decode_paged(const fa4_decode_args *a, void *ws, size_t ws_bytes, void *stream) {
   REQUIRE(a, FA4_ERR_NULL, "decode: args is NULL");
+  if (a->d_v != 0) return decode_mla(a, ws, ws_bytes, stream);
   REQUIRE(a->fmt == FA4_NVFP4 || a->fmt == FA4_MXFP4, FA4_ERR_UNSUPPORTED, "decode: format %d", a->fmt);
   REQUIRE(a->p_fmt == FA4_P_FP8 || a->p_fmt == FA4_P_NVFP4, FA4_ERR_UNSUPPORTED, "decode: probability format %d",
           a->p_fmt);

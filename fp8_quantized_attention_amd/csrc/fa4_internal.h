@@ -17,4 +17,9 @@ hipError_t launch_attn(const fa4_attn_args *a, hipStream_t s);
 size_t decode_workspace_bytes(const fa4_decode_args *a);
 hipError_t launch_decode(const fa4_decode_args *a, void *ws, hipStream_t s);
 
+// MLA geometry of fa4_decode_paged: latent row width (key), value width, query heads.
+constexpr int MLA_D = 576, MLA_DV = 512, MLA_H = 16;
+size_t decode_mla_workspace_bytes(const fa4_decode_args *a);
+hipError_t launch_decode_mla(const fa4_decode_args *a, void *ws, hipStream_t s);
+
 }  // namespace fa4

@@ -233,6 +233,17 @@ fa4_status fa4_attn_fwd(const fa4_attn_args *a, void *stream);
  * The work is split over key ranges; partial results go to a caller-provided workspace of
  * fa4_decode_workspace_bytes(a) bytes (256-byte aligned) and are merged by a second kernel.
  * Requirements: d = 128; page_size = 64; Hq / Hkv = 4; 1 <= ctx_len[b] <= max_pages * page_size.
+ *
+ * MLA geometry (d_v = 512; "BitDecoding-FP4" reports the method on MLA attention as well): every query
+ * head of sequence b attends to one shared latent row per token, whose d = 576 values (512 latent, 64
+ * rotary) are the key and whose first d_v = 512 values are the value; q1/q2 hold each head's absorbed
+ * query. Probability tiles are one 64-key page (otherwise as above, P^ = E4M3(448 P')).
+ *   fmt = FA4_MXFP4, p_fmt = FA4_P_FP8, Hq = 16, Hkv = 1, d = 576, page_size = 64.
+ *   q1_codes/q2_codes [B][Hq][288], q1_scales/q2_scales [B][Hq][18] E8M0.
+ *   k_codes [num_pages][9][64][32] and k_scales [num_pages][9][64][2] E8M0: slice j of a page holds
+ *   columns 64 j .. 64 j + 63 of its 64 rows (fa4_quantize_blockscaled's paged output for the rows
+ *   taken as nine 64-wide heads). v_codes, v_scales and the tensor scales are not read (may be NULL).
+ *   o [B][Hq][512] float. Workspace: fa4_decode_workspace_bytes(a).
  */
 typedef struct {
   int32_t fmt;                                  /* FA4_NVFP4 or FA4_MXFP4 (Q1, Q2, K and V)     */
@@ -246,6 +257,7 @@ typedef struct {
   float softmax_scale;
   float *o;
   int32_t p_fmt;                                /* FA4_P_FP8 (0) or FA4_P_NVFP4                 */
+  int32_t d_v;                                  /* 0: GQA geometry; 512: MLA geometry (below)   */
 } fa4_decode_args;
 
 size_t fa4_decode_workspace_bytes(const fa4_decode_args *a);

@@ -140,3 +140,28 @@ def decode_reference(cfg, seed, layout, pairs, logical, q1, q2, scale=None):
         vh = logical[(W.T_V, b, h // group)]
         out.append(Dd.decode_one(qhat[b, h], kh, vh, scale, p_fmt=cfg.p_fmt).astype(np.float32))
     return np.stack(out)
+
+
+def mla_cache(cfg, layout, seed, seqs=None):
+    """Oracle MLA latent cache: each sequence's rows (576 wide) MXFP4-quantized per token and laid out
+    in column-sliced pages [P][9][64][32] / [P][9][64][2]; seqs: optional subset of sequences to build
+    (the rest stay zero). Returns (codes, scales, {b: (rows float64, codes [L, 288], scales [L, 18])})."""
+    ns = cfg.d // 64
+    codes = np.zeros((layout.num_pages, ns, cfg.page_size, 32), np.uint8)
+    scales = np.zeros((layout.num_pages, ns, cfg.page_size, 2), np.uint8)
+    rows = {}
+    for b in (range(cfg.B) if seqs is None else seqs):
+        L = int(layout.ctx_len[b])
+        x = W.decode_kv_head(cfg, W.T_K, b, 0, L, seed).double().numpy()
+        qc, qs = Q.mxfp4_quantize(x)
+        c = np.arange(L)
+        phys = layout.page_table[b].numpy()[c // cfg.page_size]
+        codes[phys, :, c % cfg.page_size] = qc.reshape(L, ns, 32)
+        scales[phys, :, c % cfg.page_size] = qs.reshape(L, ns, 2)
+        rows[b] = (x, qc, qs)
+    return codes, scales, rows
+
+
+def mla_query_quant(cfg, seed):
+    q = W.decode_query(cfg, seed).double().numpy()
+    return q, Q.dual_residual_quantize_mx(q.reshape(cfg.B * cfg.Hq, cfg.d))

@@ -160,7 +160,7 @@ def _dec(**kw):
                 q2_tscale=256,
                 k_codes=256, k_scales=256, v_codes=256, v_scales=256, k_tscale=256, v_tscale=256,
                 page_table=256, ctx_len=256, B=4, Hq=32, Hkv=8, d=128, page_size=64, max_pages=8, num_pages=32,
-                softmax_scale=0.088, o=256, p_fmt=fa4.FA4_P_FP8)
+                softmax_scale=0.088, o=256, p_fmt=fa4.FA4_P_FP8, d_v=0)
     base.update(kw)
     return fa4.DecodeArgs(*[base[f] for f, _ in fa4.DecodeArgs._fields_])
 
@@ -189,3 +189,22 @@ def test_decode_rejects_before_launch():
     assert call(_dec(k_scales=260)) == fa4.FA4_ERR_ALIGN
     assert call(_dec(k_scales=260, **mx), ws=None, n=need) == fa4.FA4_ERR_WORKSPACE
     assert call(_dec(k_scales=258, **mx)) == fa4.FA4_ERR_ALIGN
+
+
+def test_mla_decode_rejects_before_launch():
+    call = lambda a, ws=512, n=1 << 30: fa4.lib.fa4_decode_paged(ctypes.byref(a), ws, n, None)
+    mla = dict(fmt=fa4.FA4_MXFP4, d=576, d_v=512, Hq=16, Hkv=1, max_pages=40, q1_tscale=None, q2_tscale=None,
+               k_tscale=None, v_tscale=None, v_codes=None, v_scales=None)
+    a = _dec(**mla)
+    need = fa4.lib.fa4_decode_workspace_bytes(ctypes.byref(a))
+    assert need == 4 * 2 * 16 * 514 * 4                     # B x ceil(40 / 32) splits x heads x (m, l, O)
+    assert call(a, ws=512, n=need - 1) == fa4.FA4_ERR_WORKSPACE
+    assert call(a, ws=520, n=need) == fa4.FA4_ERR_ALIGN
+    assert call(_dec(**{**mla, "fmt": fa4.FA4_NVFP4})) == fa4.FA4_ERR_UNSUPPORTED
+    assert call(_dec(**{**mla, "p_fmt": fa4.FA4_P_NVFP4})) == fa4.FA4_ERR_UNSUPPORTED
+    assert call(_dec(**{**mla, "Hq": 32})) == fa4.FA4_ERR_UNSUPPORTED
+    assert call(_dec(**{**mla, "d": 128})) == fa4.FA4_ERR_UNSUPPORTED
+    assert call(_dec(**{**mla, "d_v": 256})) == fa4.FA4_ERR_UNSUPPORTED
+    assert call(_dec(**{**mla, "k_scales": 264})) == fa4.FA4_ERR_ALIGN
+    assert call(_dec(**{**mla, "k_codes": None})) == fa4.FA4_ERR_NULL
+    assert call(_dec(**{**mla, "B": 0})) == fa4.FA4_OK

@@ -7,29 +7,16 @@ import bruteforce as bf
 import workloads as W
 from oracle import decode as Dd
 from oracle import quant as Q
+from oracle_cases import mla_cache, mla_query_quant
 
 SMALL = W.C5_MLA.scaled(B=2, ctx_lo=150, ctx_hi=330)
 
 
 def build_mla(cfg, seed=0):
-    """Latent rows quantized to MXFP4 per token (576 wide), laid out in column-sliced pages
-    [P][9][64][32] / [P][9][64][2]; the dual-residual query per head."""
+    """Column-sliced MXFP4 latent pages and the dual-residual query per head (oracle_cases)."""
     lay = W.decode_layout(cfg, seed)
-    ns = cfg.d // 64
-    codes = np.zeros((lay.num_pages, ns, cfg.page_size, 32), np.uint8)
-    scales = np.zeros((lay.num_pages, ns, cfg.page_size, 2), np.uint8)
-    rows = {}
-    for b in range(cfg.B):
-        L = int(lay.ctx_len[b])
-        x = W.decode_kv_head(cfg, W.T_K, b, 0, L, seed).double().numpy()
-        qc, qs = Q.mxfp4_quantize(x)                     # [L, 288], [L, 18]
-        c = np.arange(L)
-        phys = lay.page_table[b].numpy()[c // cfg.page_size]
-        codes[phys, :, c % cfg.page_size] = qc.reshape(L, ns, 32)
-        scales[phys, :, c % cfg.page_size] = qs.reshape(L, ns, 2)
-        rows[b] = (x, qc, qs)
-    q = W.decode_query(cfg, seed).double().numpy()
-    q1, q2 = Q.dual_residual_quantize_mx(q.reshape(cfg.B * cfg.Hq, cfg.d))
+    codes, scales, rows = mla_cache(cfg, lay, seed)
+    q, (q1, q2) = mla_query_quant(cfg, seed)
     return lay, codes, scales, rows, q, q1, q2
 
 
