@@ -62,11 +62,14 @@ def quantize_p_nvfp4(p):
     return nvfp4_dequantize(codes, sb, st)[0, 0, :n]
 
 
-def decode_one(q_hat, k_hat, v_hat, scale, chunk=None, round_p=True, p_fmt="fp8", tile=TILE):
+def decode_one(q_hat, k_hat, v_hat, scale, chunk=None, round_p=True, p_fmt="fp8", tile=TILE, pow2_ref=False):
     """O for one query row against L keys (v_hat may be narrower than k_hat). chunk: optional split
     length (multiple of the tile) whose partial results (m, l, O) are merged afterwards; the merged
     result equals the single pass. p_fmt: "fp8" (P^ = E4M3(448 P')) or "nvfp4" (quantize_p_nvfp4).
-    tile: keys per probability tile (128; one 64-key page for the MLA geometry)."""
+    tile: keys per probability tile (128; one 64-key page for the MLA geometry).
+    pow2_ref: the tile reference is a power of two instead of the tile maximum (the prefill's rule,
+    "MpFA QK4V8" section 3.3 per-tile P scaling): with x = S log2(e), r = ceil(max x), P' = 2^(x - r)
+    (largest value in (1/2, 1]) and the tiles merge with exact weights 2^(r_j - max_j r_j)."""
     L = k_hat.shape[0]
     if chunk is None:
         chunk = max(L, 1)
@@ -77,8 +80,14 @@ def decode_one(q_hat, k_hat, v_hat, scale, chunk=None, round_p=True, p_fmt="fp8"
         for t0 in range(s0, min(s0 + chunk, L), tile):
             cs = np.arange(t0, min(t0 + tile, L, s0 + chunk))
             S = scale * (k_hat[cs] @ q_hat)
-            m = S.max()
-            P = np.exp(S - m)
+            if pow2_ref:
+                X = S * np.log2(np.e)
+                r = np.ceil(X.max())
+                P = np.exp2(X - r)
+                m = r * np.log(2.0)              # merged below through exp(m_j - max m) = 2^(r_j - max r)
+            else:
+                m = S.max()
+                P = np.exp(S - m)
             if not round_p:
                 T = P @ v_hat[cs]
             elif p_fmt == "nvfp4":
@@ -168,8 +177,9 @@ def decode_mla(q1, q2, codes, scales, page_table, ctx_len, Hq, d_v, scale, page_
     token, which is the key (all d values, the latent part and the rotary part) and whose first d_v
     values are the value. The cache is MXFP4 (E8M0 per 32 along the row); the query of each head is
     the dual residual pair (q1, q2 = (codes [B*Hq, d/2], E8M0 [B*Hq, d/32])) of its absorbed form.
-    Probability tiles are one 64-key page. Returns O float32 [B, Hq, d_v] (pairs: optional subset of
-    (b, h) to compute; the rest stay zero)."""
+    Probability tiles are one 64-key page, each with a power-of-two reference (decode_one's
+    pow2_ref). Returns O float32 [B, Hq, d_v] (pairs: optional subset of (b, h) to compute; the rest
+    stay zero)."""
     B = len(ctx_len)
     d = 2 * q1[0].shape[-1]
     qhat = (mxfp4_dequantize(*q1) + mxfp4_dequantize(*q2)).reshape(B, Hq, d)
@@ -182,5 +192,5 @@ def decode_mla(q1, q2, codes, scales, page_table, ctx_len, Hq, d_v, scale, page_
             rows = {b: k_hat}
         k_hat = rows[b]
         O[b, h] = fp32(decode_one(qhat[b, h], k_hat, k_hat[:, :d_v], scale, chunk=chunk, round_p=round_p,
-                                  tile=page_size))
+                                  tile=page_size, pow2_ref=True))
     return O

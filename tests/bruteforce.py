@@ -185,17 +185,23 @@ def attention_rows(rows, Q, K, Vc, sv, Qo, Ko, Vo, sel, Lq, Lk, causal, scale, r
     return out
 
 
-def decode_row(q, K, V, scale, round_p=True, p_fmt="fp8", tile=128):
+def decode_row(q, K, V, scale, round_p=True, p_fmt="fp8", tile=128, pow2_ref=False):
     """O9 by loops for one query row over len(K) keys, tiles of `tile` keys from 0 (V rows may be
     shorter than K rows). p_fmt "nvfp4": each tile's probabilities (largest exactly 1) form one NVFP4
-    group, P^ its values, T = sum P^ v."""
+    group, P^ its values, T = sum P^ v. pow2_ref: each tile's reference is 2^r, r the smallest
+    integer >= the largest score in log2 units (P = 2^(S log2 e - r)), merged with weights 2^(r - max r)."""
     d = len(V[0])
     terms = []
     for t0 in range(0, len(K), tile):
         cols = range(t0, min(t0 + tile, len(K)))
         S = {c: scale * sum(q[t] * K[c][t] for t in range(len(q))) for c in cols}
-        m = max(S.values())
-        P = {c: math.exp(S[c] - m) for c in cols}
+        if pow2_ref:
+            r = math.ceil(max(S[c] / math.log(2.0) for c in cols))
+            P = {c: 2.0 ** (S[c] / math.log(2.0) - r) for c in cols}
+            m = r * math.log(2.0)
+        else:
+            m = max(S.values())
+            P = {c: math.exp(S[c] - m) for c in cols}
         T = [0.0] * d
         if round_p and p_fmt == "nvfp4":
             codes, sbs, st = nvfp4_group([[f32(P[c]) for c in cols]])
