@@ -14,12 +14,14 @@
 // direct global->LDS loads one page ahead. Wave w scores keys 16 w .. 16 w + 15 of the page against
 // the 16 heads with 16x16x128 scaled FP4 MFMAs: the key codes and their scale bytes are the A operand,
 // the head's [Q1 | Q2] codes (1152 values, so the dual-residual sum forms in the accumulator) the B
-// operand. The page maximum and sum of each head are exchanged through LDS and P^ = E4M3(448 P')
-// (exact in bf16) is written to LDS as [head][key]. For PV wave w owns the values d = 128 w ..
-// 128 w + 127: each key's 4-byte run of 8 values is converted to bf16 with the key's block scale (code
-// * 2^e has at most 2 significant bits), an 8x8 transpose of 16-bit values gives the key-contiguous A
-// operand of O^T = V^T P^T, and a 16x16x32 bf16 MFMA adds a 32-key quarter. Each wave keeps the
-// running maximum, sum and its part of O; a second kernel merges the workgroups of a sequence.
+// operand. The page maximum and sum of each head are exchanged through LDS. The page's reference is a
+// power of two 2^r (r the smallest integer >= its largest score in log2 units, the prefill's rule), so
+// P' = 2^(x - r) and the page's weight against the running reference, 2^(r - R), is exact: it rides
+// on P^ = E4M3(448 P') * 2^(r - R) (exact in bf16), written to LDS as [head][key]. For PV wave w owns
+// the values d = 128 w .. 128 w + 127: each key's 4-byte run of 8 values is converted to bf16 with the
+// key's block scale (code * 2^e has at most 2 significant bits), an 8x8 transpose of 16-bit values
+// gives the key-contiguous A operand of O^T = V^T P^T, and a 16x16x32 bf16 MFMA adds a 32-key quarter
+// straight into the accumulator. A second kernel merges the workgroups of a sequence.
 #include "fa4_device.h"
 #include "fa4_internal.h"
 
@@ -44,13 +46,47 @@ struct MlaArgs {
   float *ws, *o;
 };
 
-typedef __attribute__((address_space(3))) void mla_lds_t;
+constexpr int MLA_NB = 2;                         // LDS page buffers: pages are loaded MLA_NB - 1 ahead
+constexpr float MLA_HEADROOM = 32.0f;             // largest page weight 2^k before the reference is raised
+constexpr int MLA_DMA = 5;                        // direct loads per wave per page (each wave alike)
+
+// Direct global->LDS load of 16 bytes per lane to l + 16 * lane (l wave-uniform). Written as inline asm
+// so that the compiler, which cannot tell which LDS bytes such a load writes, does not wait for it
+// before every later LDS read; the kernel waits for these loads itself (vmcnt) before the barrier
+// that publishes a page. M0 takes the LDS address and needs one wait state before the load; no other
+// instruction of these kernels reads M0 (the compiler warns that it does not preserve a clobbered M0).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void mla_dma16(const void *g, uint8_t *l) {
-  __builtin_amdgcn_global_load_lds(g, (mla_lds_t *)l, 16, 0, 0);
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t *)l);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+// Wait until at most n of this wave's direct loads are in flight (n: 0, MLA_DMA or 2 MLA_DMA).
+__device__ __forceinline__ void mla_wait(int n) {
+  if (n >= 2 * MLA_DMA) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+  else if (n >= MLA_DMA) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-__global__ void __launch_bounds__(MLA_THREADS) decode_mla_kernel(MlaArgs a) {
-  __shared__ __align__(16) uint8_t tile[2][MLA_TC + MLA_TS];
+// max / sum over the four lanes n, n + 16, n + 32, n + 48 (lane swaps on the VALU, no LDS)
+__device__ __forceinline__ float quad_max(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float quad_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Three workgroups per CU (LDS 50 KB each): at most 168 VGPRs.
+__global__ void __launch_bounds__(MLA_THREADS) __attribute__((amdgpu_waves_per_eu(3))) decode_mla_kernel(MlaArgs a) {
+  __shared__ __align__(16) uint8_t tile[MLA_NB][MLA_TC + MLA_TS];
+  __shared__ __align__(16) uint8_t qlds[2][MLA_H][MLA_D / 2];     // Q1, Q2 codes of the 16 heads
   __shared__ __align__(16) uint16_t pT[MLA_H * MLA_PP];
   __shared__ float red_m[4][MLA_H], red_l[4][MLA_H];
   // Workgroup order: sequence fastest, split slowest (every XCD gets the same mix of sequences and
@@ -66,9 +102,15 @@ __global__ void __launch_bounds__(MLA_THREADS) decode_mla_kernel(MlaArgs a) {
   const int32_t *pt = a.pt + (int64_t)b * a.max_pages;
 
   // ---- B operand of QK: head n; chunk s, lane group g holds values 128 s + 32 g .. + 31 of the
-  // concatenated [Q1 | Q2] (a 32-block never straddles the two) with its E8M0 scale
-  v8i qop[9];
-  int qsc[9];
+  // concatenated [Q1 | Q2] (a 32-block never straddles the two). The codes go to LDS (read once per
+  // page); the E8M0 scales stay in registers, four per register, picked by the MFMA's byte select.
+  for (int idx = tid; idx < 2 * MLA_H * (MLA_D / 32); idx += MLA_THREADS) {
+    const int r = idx / (MLA_H * (MLA_D / 32)), hc = idx - r * (MLA_H * (MLA_D / 32));
+    const int h = hc / (MLA_D / 32), c16 = hc - h * (MLA_D / 32);
+    *reinterpret_cast<v4i *>(&qlds[r][h][16 * c16]) =
+        *reinterpret_cast<const v4i *>((r ? a.q2c : a.q1c) + ((int64_t)b * MLA_H + h) * (MLA_D / 2) + 16 * c16);
+  }
+  uint32_t qsc[3] = {0u, 0u, 0u};
   {
     const int64_t bh = (int64_t)b * MLA_H + n;
 #pragma unroll
@@ -76,10 +118,11 @@ __global__ void __launch_bounds__(MLA_THREADS) decode_mla_kernel(MlaArgs a) {
       const int c = 128 * s + 32 * g;
       const bool r2 = c >= MLA_D;
       const int d0 = r2 ? c - MLA_D : c;
-      const v4i w = *reinterpret_cast<const v4i *>((r2 ? a.q2c : a.q1c) + bh * (MLA_D / 2) + d0 / 2);
-      qop[s] = (v8i){w[0], w[1], w[2], w[3], 0, 0, 0, 0};
-      qsc[s] = (r2 ? a.q2s : a.q1s)[bh * (MLA_D / 32) + d0 / 32];
+      qsc[s >> 2] |= (uint32_t)(r2 ? a.q2s : a.q1s)[bh * (MLA_D / 32) + d0 / 32] << (8 * (s & 3));
     }
+    // use the scales here, so that the compiler waits for their loads before the page loop
+    // (inside it the count would also cover page loads in flight)
+    asm volatile("" ::"v"(qsc[0]), "v"(qsc[1]), "v"(qsc[2]));
   }
 
   // physical page of the split's page i (wave-uniform); an id outside the cache reads page 0 and
@@ -99,20 +142,25 @@ __global__ void __launch_bounds__(MLA_THREADS) decode_mla_kernel(MlaArgs a) {
     if (wave == 3 && lane < (MLA_TS - 1024) / 16) mla_dma16(gs + 1024 + 16 * lane, lc + MLA_TC + 1024);
   };
 
+  // Running state of head n: the reference R (an integer, log2 units), the sum and this wave's part
+  // of O, both relative to 2^R. A page with reference r enters with the exact weight 2^(r - R), carried
+  // by P^ into the MFMA; R is raised only when a page's r exceeds it by more than MLA_HEADROOM.
   const float cs = a.scale * MLA_LOG2E;
-  float m_run = -INFINITY, l_run = 0.0f;
+  float R = -INFINITY, l_run = 0.0f;
   v4f acc[8];
 #pragma unroll
   for (int e = 0; e < 8; e++) acc[e] = (v4f){0.f, 0.f, 0.f, 0.f};
-  issue(0, 0);
+  for (int i = 0; i < MLA_NB - 1 && i < np; i++) issue(i, i);
+  int buf = 0;
   for (int i = 0; i < np; i++) {
-    const int buf = i & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    mla_wait(MLA_DMA * min(MLA_NB - 2, np - 1 - i));           // this wave's loads of page i are done
     __syncthreads();                                           // page i landed; page i - 1 consumed
-    if (i + 1 < np) issue(i + 1, buf ^ 1);                      // in flight during this page's work
+    if (i + MLA_NB - 1 < np) issue(i + MLA_NB - 1, buf == 0 ? MLA_NB - 1 : buf - 1);   // page i - 1's buffer
+    const int cur = buf;
+    buf = buf + 1 == MLA_NB ? 0 : buf + 1;
     const int kval = page_ok(page_id(i)) ? min(64, L - 64 * (p0 + i)) : 0;   // valid keys (uniform)
     if (kval == 0) continue;
-    const uint8_t *lc = tile[buf];
+    const uint8_t *lc = tile[cur];
 
     // ---- S^T = K Q^T for keys 16 wave .. + 15 (rows) and the 16 heads (columns)
     v4f S = (v4f){0.f, 0.f, 0.f, 0.f};
@@ -121,57 +169,65 @@ __global__ void __launch_bounds__(MLA_THREADS) decode_mla_kernel(MlaArgs a) {
 #pragma unroll
       for (int s = 0; s < 9; s++) {
         const int c = 128 * s + 32 * g;
-        const int d0 = c >= MLA_D ? c - MLA_D : c;
+        const bool r2 = c >= MLA_D;
+        const int d0 = r2 ? c - MLA_D : c;
         const int sl = d0 >> 6, hf = (d0 >> 5) & 1;
         const v4i t = *reinterpret_cast<const v4i *>(lc + sl * 2048 + krow * 32 + hf * 16);
         const int ksc = lc[MLA_TC + sl * 128 + krow * 2 + hf];
-        S = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4((v8i){t[0], t[1], t[2], t[3], 0, 0, 0, 0}, qop[s],
-                                                             S, 4, 4, 0, ksc, 0, qsc[s]);
+        const v4i qw = *reinterpret_cast<const v4i *>(&qlds[r2][n][d0 / 2]);
+        const v8i ka = (v8i){t[0], t[1], t[2], t[3], 0, 0, 0, 0}, qb = (v8i){qw[0], qw[1], qw[2], qw[3], 0, 0, 0, 0};
+        switch (s & 3) {                                       // the byte select must be a constant
+          case 0: S = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qb, S, 4, 4, 0, ksc, 0, (int)qsc[s >> 2]); break;
+          case 1: S = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qb, S, 4, 4, 0, ksc, 1, (int)qsc[s >> 2]); break;
+          case 2: S = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qb, S, 4, 4, 0, ksc, 2, (int)qsc[s >> 2]); break;
+          default: S = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qb, S, 4, 4, 0, ksc, 3, (int)qsc[s >> 2]); break;
+        }
       }
     }
-    // ---- this lane: head n, keys 16 wave + 4 g + t
+    // ---- this lane: head n, keys 16 wave + 4 g + t; scores in log2 units
     float x[4], mw = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 4; t++) {
       x[t] = 16 * wave + 4 * g + t < kval ? S[t] * cs : -INFINITY;
       mw = fmaxf(mw, x[t]);
     }
-    mw = fmaxf(mw, shfl_xor_f(mw, 16));
-    mw = fmaxf(mw, shfl_xor_f(mw, 32));
+    mw = quad_max(mw);
     if (g == 0) red_m[wave][n] = mw;
     __syncthreads();
-    const float mt = fmaxf(fmaxf(red_m[0][n], red_m[1][n]), fmaxf(red_m[2][n], red_m[3][n]));
+    // the page's reference: the smallest integer r >= its largest score (P' = 2^(x - r) <= 1)
+    const float r = ceilf(fmaxf(fmaxf(red_m[0][n], red_m[1][n]), fmaxf(red_m[2][n], red_m[3][n])));
+    if (__builtin_amdgcn_ballot_w64(r > R + MLA_HEADROOM) != 0) {  // uniform (always on the first page)
+      const float R_new = fmaxf(R, r);
+      const float alpha = R == -INFINITY ? 0.0f : __builtin_ldexpf(1.0f, (int)(R - R_new));
+#pragma unroll
+      for (int e = 0; e < 8; e++) acc[e] *= alpha;
+      l_run *= alpha;
+      R = R_new;
+    }
+    const int k = (int)fmaxf(r - R, -255.0f);                  // page weight 2^k, k <= MLA_HEADROOM
     float ls = 0.0f;
     {
       float p[4];
 #pragma unroll
       for (int t = 0; t < 4; t++) {
-        p[t] = __builtin_amdgcn_exp2f(x[t] - mt);
+        p[t] = __builtin_amdgcn_exp2f(x[t] - r);
         ls += p[t];
       }
-      // P^ = E4M3(448 P'), as bf16 (exact)
+      // P^ = E4M3(448 P') times 2^k, as bf16 (exact; a weight under 2^-126 adds nothing representable)
       const uint32_t c01 = e4m3_encode2(448.0f * p[0], 448.0f * p[1]);
       const uint32_t c23 = e4m3_encode2(448.0f * p[2], 448.0f * p[3]);
-      const uint32_t u0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c01, 1.0f, false));
-      const uint32_t u1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c23, 1.0f, false));
+      const float w = __uint_as_float((uint32_t)(k + 127) << 23);
+      uint32_t u0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c01, w, false));
+      uint32_t u1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c23, w, false));
+      if (k < -126) u0 = u1 = 0u;
       *reinterpret_cast<uint2 *>(&pT[n * MLA_PP + 16 * wave + 4 * g]) = make_uint2(u0, u1);
     }
-    ls += shfl_xor_f(ls, 16);
-    ls += shfl_xor_f(ls, 32);
+    ls = quad_sum(ls);
     if (g == 0) red_l[wave][n] = ls;
     __syncthreads();
-    const float lt = (red_l[0][n] + red_l[1][n]) + (red_l[2][n] + red_l[3][n]);
-    // running merge: O and l stay relative to the running maximum
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);    // 0 on the first tile
-    const float f = __builtin_amdgcn_exp2f(mt - m_new);
-    l_run = l_run * alpha + lt * f;
-    m_run = m_new;
+    l_run += ((red_l[0][n] + red_l[1][n]) + (red_l[2][n] + red_l[3][n])) * __builtin_ldexpf(1.0f, k);
 
     // ---- O^T += V^T P^T for values d = 128 wave + 8 n + e (A row n of accumulator e), two quarters
-    v4f tmp[8];
-#pragma unroll
-    for (int e = 0; e < 8; e++) tmp[e] = (v4f){0.f, 0.f, 0.f, 0.f};
     const int sl = 2 * wave + (n >> 3);                        // slice of this lane's 8 values
 #pragma unroll
     for (int q = 0; q < 2; q++) {
@@ -200,16 +256,15 @@ __global__ void __launch_bounds__(MLA_THREADS) decode_mla_kernel(MlaArgs a) {
 #pragma unroll
         for (int jp = 0; jp < 4; jp++)
           av[jp] = (int)__builtin_amdgcn_perm(kw[2 * jp + 1][e >> 1], kw[2 * jp][e >> 1], sel);
-        tmp[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, av), pb, tmp[e], 0, 0, 0);
+        acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, av), pb, acc[e], 0, 0, 0);
       }
     }
-#pragma unroll
-    for (int e = 0; e < 8; e++) acc[e] = acc[e] * alpha + tmp[e] * f;
   }
-  // ---- partial of this split: lane (head n, group g) holds d = 128 wave + 32 g + 8 t + e in acc[e][t]
+  // ---- partial of this split, relative to 2^R: lane (head n, group g) holds d = 128 wave + 32 g + 8 t
+  // + e in acc[e][t]
   float *dst = a.ws + (((int64_t)b * a.nsplit + split) * MLA_H + n) * MLA_PART;
   if (wave == 0 && g == 0) {
-    dst[0] = m_run;
+    dst[0] = R;
     dst[1] = l_run;
   }
 #pragma unroll
