@@ -281,13 +281,16 @@ __global__ void __launch_bounds__(256) decode_mla_combine_kernel(MlaArgs a) {
   const int ns = ((L + 63) / 64 + MLA_PAGES - 1) / MLA_PAGES;
   const float *base = a.ws + ((int64_t)b * a.nsplit * MLA_H + h) * MLA_PART;
   constexpr int SS = MLA_H * MLA_PART;                       // floats between splits
+  // every split below ns wrote its partial (R = -inf and zeros when none of its pages was valid); the
+  // loops are unrolled so that several splits' loads are in flight at once
   float mm = -INFINITY;
+#pragma unroll 8
   for (int s = 0; s < ns; s++) mm = fmaxf(mm, base[(int64_t)s * SS]);
   float l = 0.f, o0 = 0.f, o1 = 0.f;
+#pragma unroll 8
   for (int s = 0; s < ns; s++) {
     const float *p = base + (int64_t)s * SS;
-    if (p[0] == -INFINITY) continue;
-    const float f = __builtin_amdgcn_exp2f(p[0] - mm);
+    const float f = p[0] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(p[0] - mm);
     l += f * p[1];
     o0 += f * p[2 + tid];
     o1 += f * p[2 + 256 + tid];
