@@ -36,6 +36,11 @@ tiles of 128 keys; column c of tile j is unmasked when not causal or c <= r + of
   4. m_r = max_j r_rj, D_r = sum_j 2^(r_rj - m_r) sum_c P'_rc (unquantized P'),
      N_r = sum_j 2^(r_rj - m_r) T_rj; O_r = N_r / D_r (returned as float32),
      LSE_r = m_r ln 2 + ln D_r.
+  4-bit V (v_deq given): V is MXFP4 with its 32-element blocks along the keys
+     ("MpFA QK4V8" section 6 names 4-bit V as an extension without a format; blocks
+     along the contraction axis of PV are the ones a block-scaled product can apply),
+     v_deq its dequantized values. Unselected tile: P^_rc = E4M3(448 P'_rc),
+     T_rj = (1/448) sum_c P^_rc v_deq_c.
 Without rounding of P, every choice of the per-tile powers of two cancels and
 O is exactly softmax(S) V. Because P' and P^ depend only on their own tile, the
 result does not depend on the order in which tiles are visited;
@@ -59,9 +64,9 @@ def fold_exponent(sigma):
     return min(max(e, -127), 127)
 
 
-def _tile_terms(S, unmasked, sel, vq_vals, s_v, v_orig, round_p=True):
+def _tile_terms(S, unmasked, sel, vq_vals, s_v, v_orig, round_p=True, v_deq=None):
     """Per-row (r, sum P', T) of one key tile, r the tile's power-of-two row reference in log2 units.
-    S: [R, n] float64 scores (already scaled)."""
+    S: [R, n] float64 scores (already scaled). v_deq: the tile's dequantized 4-bit V (else FP8 V)."""
     X = np.where(unmasked, S * np.log2(np.e), -np.inf)
     has = unmasked.any(axis=1)
     r = np.where(has, np.ceil(X.max(axis=1, initial=-np.inf)), 0.0)
@@ -70,6 +75,9 @@ def _tile_terms(S, unmasked, sel, vq_vals, s_v, v_orig, round_p=True):
     if sel:
         Pt = bf16_round(P) if round_p else P
         T = Pt @ v_orig
+    elif v_deq is not None:
+        Ph = e4m3_decode(e4m3_encode(E4M3_MAX * P)) if round_p else E4M3_MAX * P
+        T = (Ph @ v_deq) / E4M3_MAX
     else:
         e = fold_exponent(float(np.max(s_v)))
         w = s_v.astype(np.float64) * 2.0 ** -e
@@ -91,16 +99,17 @@ def _row_tiles(rows, Lq, Lk, causal, tile=TILE):
 
 def attend_rows(rows, q_rows, k_deq, v_codes, s_v, scale, Lq, Lk, causal,
                 q_orig_rows=None, k_orig=None, v_orig=None, sel_row=None, round_p=True,
-                tile_order=None):
+                tile_order=None, v_deq=None):
     """Two-pass O8 for a group of query rows that all lie in one 128-row q-tile.
 
     rows: [R] query indices; q_rows: [R, d] dequantized Q; k_deq: [Lk, d];
     v_codes: [Lk, d] E4M3 codes; s_v: [Lk] float32; sel_row: [nk] bool for
-    this q-tile (None = nothing selected). Returns (O [R, d] float64, LSE [R]).
+    this q-tile (None = nothing selected); v_deq: [Lk, d] dequantized 4-bit V (then
+    v_codes and s_v are not used). Returns (O [R, d] float64, LSE [R]).
     """
     rows = np.asarray(rows)
     off = Lk - Lq
-    vq_vals = e4m3_decode(v_codes)
+    vq_vals = e4m3_decode(v_codes) if v_deq is None else None
     tiles = _row_tiles(rows, Lq, Lk, causal)
     if tile_order is not None:
         tiles = [tiles[t] for t in tile_order]
@@ -113,8 +122,9 @@ def attend_rows(rows, q_rows, k_deq, v_codes, s_v, scale, Lq, Lk, causal,
             S = scale * (q_orig_rows @ k_orig[cs].T)
         else:
             S = scale * (q_rows @ k_deq[cs].T)
-        m, l, T = _tile_terms(S, unmasked, sel, vq_vals[cs], s_v[cs],
-                              v_orig[cs] if sel else None, round_p)
+        m, l, T = _tile_terms(S, unmasked, sel, None if vq_vals is None else vq_vals[cs],
+                              None if s_v is None else s_v[cs], v_orig[cs] if sel else None, round_p,
+                              None if v_deq is None else v_deq[cs])
         ms.append(m); ls.append(l); Ts.append(T)
     M = np.stack(ms, axis=0)                       # [J, R] log2 units
     mrow = M.max(axis=0)
@@ -126,7 +136,7 @@ def attend_rows(rows, q_rows, k_deq, v_codes, s_v, scale, Lq, Lk, causal,
 
 def attend_rows_online(rows, q_rows, k_deq, v_codes, s_v, scale, Lq, Lk, causal,
                        q_orig_rows=None, k_orig=None, v_orig=None, sel_row=None, round_p=True,
-                       tile_order=None):
+                       tile_order=None, v_deq=None):
     """The same computation as attend_rows with a running max m, sum l and accumulator acc.
 
     For each tile (log2 units): m_new = max(m, r); acc = acc 2^(m - m_new) + T 2^(r - m_new);
@@ -134,11 +144,11 @@ def attend_rows_online(rows, q_rows, k_deq, v_codes, s_v, scale, Lq, Lk, causal,
     """
     rows = np.asarray(rows)
     off = Lk - Lq
-    vq_vals = e4m3_decode(v_codes)
+    vq_vals = e4m3_decode(v_codes) if v_deq is None else None
     tiles = _row_tiles(rows, Lq, Lk, causal)
     if tile_order is not None:
         tiles = [tiles[t] for t in tile_order]
-    R, d = len(rows), v_codes.shape[1]
+    R, d = len(rows), (v_codes if v_deq is None else v_deq).shape[1]
     m = np.full(R, -np.inf)
     l = np.zeros(R)
     acc = np.zeros((R, d))
@@ -147,8 +157,9 @@ def attend_rows_online(rows, q_rows, k_deq, v_codes, s_v, scale, Lq, Lk, causal,
         unmasked = np.ones((R, TILE), dtype=bool) if not causal else (cs[None, :] <= rows[:, None] + off)
         sel = bool(sel_row[j]) if sel_row is not None else False
         S = scale * ((q_orig_rows @ k_orig[cs].T) if sel else (q_rows @ k_deq[cs].T))
-        mt, lt, T = _tile_terms(S, unmasked, sel, vq_vals[cs], s_v[cs],
-                                v_orig[cs] if sel else None, round_p)
+        mt, lt, T = _tile_terms(S, unmasked, sel, None if vq_vals is None else vq_vals[cs],
+                                None if s_v is None else s_v[cs], v_orig[cs] if sel else None, round_p,
+                                None if v_deq is None else v_deq[cs])
         m_new = np.maximum(m, mt)
         a_old = np.where(np.isfinite(m), np.exp2(m - m_new), 0.0)
         a_new = np.where(np.isfinite(mt), np.exp2(mt - m_new), 0.0)
@@ -160,10 +171,10 @@ def attend_rows_online(rows, q_rows, k_deq, v_codes, s_v, scale, Lq, Lk, causal,
 
 def attention_prefill(q_deq, k_deq, v_codes, s_v, causal, scale=None,
                       q_orig=None, k_orig=None, v_orig=None, bitmap=None,
-                      rows=None, heads=None, round_p=True):
+                      rows=None, heads=None, round_p=True, v_deq=None):
     """O8 over a batch: q_deq [B, Hq, Lq, d]; k_deq [B, Hkv, Lk, d]; v_codes [B, Hkv, Lk, d]
     (E4M3 codes, token-major); s_v [B, Hkv, Lk]; optional originals (bf16 values as float64)
-    and bitmap [B, Hq, nq, nk].
+    and bitmap [B, Hq, nq, nk]; v_deq [B, Hkv, Lk, d]: dequantized 4-bit V instead of v_codes, s_v.
 
     rows: optional array of query rows to compute (default all); heads: optional
     list of (b, h) pairs (default all). Returns (O float32 [B, Hq, R, d],
@@ -186,11 +197,12 @@ def attention_prefill(q_deq, k_deq, v_codes, s_v, causal, scale=None,
             rr = rows[sel_idx]
             sel_row = bitmap[b, h, i] if bitmap is not None else None
             o, lse = attend_rows(
-                rr, q_deq[b, h, rr], k_deq[b, kv], v_codes[b, kv], s_v[b, kv], scale, Lq, Lk, causal,
+                rr, q_deq[b, h, rr], k_deq[b, kv], None if v_codes is None else v_codes[b, kv],
+                None if s_v is None else s_v[b, kv], scale, Lq, Lk, causal,
                 q_orig_rows=None if q_orig is None else q_orig[b, h, rr],
                 k_orig=None if k_orig is None else k_orig[b, kv],
                 v_orig=None if v_orig is None else v_orig[b, kv],
-                sel_row=sel_row, round_p=round_p)
+                sel_row=sel_row, round_p=round_p, v_deq=None if v_deq is None else v_deq[b, kv])
             O[b, h, sel_idx] = fp32(o)
             LSE[b, h, sel_idx] = fp32(lse)
     return O, LSE

@@ -123,6 +123,18 @@ def mxfp8_dequantize(codes, scales):
     return (v * s[..., None]).reshape(c.shape)
 
 
+def mxfp4_keys_quantize(v):
+    """4-bit V for prefill: MXFP4 of v [..., L, d] with its 32-element blocks along L (the key axis),
+    i.e. MXFP4 of the transposed rows v^T [..., d, L]. Returns (codes [..., d, L/2], E8M0 scales
+    [..., d, L/32]); element 2i of a code row in the low nibble, as for any MXFP4 row."""
+    return mxfp4_quantize(np.swapaxes(np.asarray(v, dtype=np.float64), -1, -2))
+
+
+def mxfp4_keys_dequantize(codes, scales):
+    """Values [..., L, d] of mxfp4_keys_quantize's output (exact)."""
+    return np.swapaxes(mxfp4_dequantize(codes, scales), -1, -2)
+
+
 # ----------------------------------------------------------------------------- NVFP4
 
 def nvfp4_quantize(x):

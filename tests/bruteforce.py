@@ -139,11 +139,12 @@ def bf16(x):
     return math.copysign(r, x)
 
 
-def attention_rows(rows, Q, K, Vc, sv, Qo, Ko, Vo, sel, Lq, Lk, causal, scale, round_p=True):
+def attention_rows(rows, Q, K, Vc, sv, Qo, Ko, Vo, sel, Lq, Lk, causal, scale, round_p=True, Vd=None):
     """O8 by loops. Q/K: dequantized rows (lists); Vc: E4M3 codes; sv: per-key scales;
-    Qo/Ko/Vo: original values for selected tiles; sel(i, j) -> bool. Returns list of output rows."""
+    Qo/Ko/Vo: original values for selected tiles; sel(i, j) -> bool. Vd: dequantized 4-bit V rows
+    (then P^ = E4M3(448 P), T = sum P^ v / 448, and Vc, sv are not used). Returns output rows."""
     off = Lk - Lq
-    d = len(Vc[0])
+    d = len((Vc if Vd is None else Vd)[0])
     out = []
     for r in rows:
         i = r // 128
@@ -167,6 +168,12 @@ def attention_rows(rows, Q, K, Vc, sv, Qo, Ko, Vo, sel, Lq, Lk, causal, scale, r
                     p = bf16(P[c]) if round_p else P[c]
                     for t in range(d):
                         T[t] += p * Vo[c][t]
+            elif Vd is not None:
+                for c in cols:
+                    p = e4m3_value(e4m3_encode(448.0 * P[c])) if round_p else 448.0 * P[c]
+                    for t in range(d):
+                        T[t] += p * Vd[c][t]
+                T = [v / 448.0 for v in T]
             else:
                 sigma = max(sv[128 * j:128 * j + 128])
                 e = -127                              # smallest e with 448 * 2^e >= sigma

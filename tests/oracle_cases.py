@@ -66,10 +66,13 @@ def prefill_reference(cfg, seed, heads, rows, select=None, q_all=None, k_all=Non
             k = (k_all[b, kvh] if k_all is not None else W.prefill_head(cfg, W.T_K, b, kvh, seed)).double().numpy()
             v = (v_all[b, kvh] if v_all is not None else W.prefill_head(cfg, W.T_V, b, kvh, seed)).double().numpy()
             kd = quant_head(cfg, k, cfg.hadamard, None if smooth is None else smooth[1][kvh], search)
-            vc, sv = Q.fp8_per_token_quantize(v)
+            if cfg.v_fmt == "mxfp4k":
+                vc, sv, vd = None, None, Q.mxfp4_keys_dequantize(*Q.mxfp4_keys_quantize(v))
+            else:
+                (vc, sv), vd = Q.fp8_per_token_quantize(v), None
             kn = Q.row_norm2(k)
-            kv_cache = {(b, kvh): (k, v, kd, vc, sv, kn)}
-        k, v, kd, vc, sv, kn = kv_cache[(b, kvh)]
+            kv_cache = {(b, kvh): (k, v, kd, vc, sv, vd, kn)}
+        k, v, kd, vc, sv, vd, kn = kv_cache[(b, kvh)]
         qd = quant_head(cfg, q, cfg.hadamard, None if smooth is None else smooth[0][h])
         bm = None
         if select is not None:
@@ -77,9 +80,11 @@ def prefill_reference(cfg, seed, heads, rows, select=None, q_all=None, k_all=Non
             bm, _ = S.select_tiles(qn[None, None], kn[None, None], cfg.Lq, cfg.Lk, cfg.causal, select[0], select[1])
             bm = bm[0, 0]
             bitmaps[(b, h)] = bm
-        O, L = A.attention_prefill(qd[None, None], kd[None, None], vc[None, None], sv[None, None], cfg.causal,
+        O, L = A.attention_prefill(qd[None, None], kd[None, None], None if vc is None else vc[None, None],
+                                   None if sv is None else sv[None, None], cfg.causal,
                                    q_orig=q[None, None], k_orig=k[None, None], v_orig=v[None, None],
-                                   bitmap=None if bm is None else bm[None, None], rows=rows)
+                                   bitmap=None if bm is None else bm[None, None], rows=rows,
+                                   v_deq=None if vd is None else vd[None, None])
         outs.append(O[0, 0]); lses.append(L[0, 0])
     return np.stack(outs), np.stack(lses), bitmaps
 

@@ -164,3 +164,50 @@ def test_tile_reference_is_a_power_of_two_bound():
     pmax = np.exp2(X.max(axis=1) - r)
     assert np.all((pmax > 0.5) & (pmax <= 1.0))
     assert np.allclose(l, np.where(unmasked, np.exp2(X - r[:, None]), 0.0).sum(axis=1), rtol=0, atol=0)
+
+
+# ---- 4-bit V: MXFP4 with 32-element blocks along the keys
+
+def test_mxfp4_keys_quantize_is_columnwise_mxfp4_by_loops():
+    v = W.prefill_inputs(W.C0.scaled(Hq=1, Hkv=1, Lq=128, Lk=128))[2][0, 0].double().numpy()   # [128, 64]
+    codes, scales = Q.mxfp4_keys_quantize(v)
+    assert codes.shape == (64, 64) and scales.shape == (64, 4)
+    for dcol in (0, 17, 63):
+        c, sc = bf.mxfp4_row([float(x) for x in v[:, dcol]])
+        assert c == [int(x) for b in codes[dcol] for x in (b & 15, b >> 4)] and sc == scales[dcol].tolist()
+    vd = Q.mxfp4_keys_dequantize(codes, scales)
+    assert np.array_equal(vd[:, 17], np.array(bf.mxfp4_row_values(*bf.mxfp4_row([float(x) for x in v[:, 17]]))))
+
+
+def _v4(v):
+    return Q.mxfp4_keys_dequantize(*Q.mxfp4_keys_quantize(v))
+
+
+@pytest.mark.parametrize("cfg", [W.C0, SMALL], ids=lambda c: c.name)
+def test_v4_without_p_rounding_is_sdpa_on_dequantized(cfg):
+    q, k, v, qd, kd, vc, sv = _prepare(cfg)
+    vd = _v4(v)
+    O, _ = A.attention_prefill(qd, kd, None, None, cfg.causal, round_p=False, v_deq=vd)
+    ref = _sdpa(qd, kd, vd, cfg.causal, 1 / np.sqrt(q.shape[-1]))
+    assert np.abs(O - ref).max() <= 1e-6 * np.abs(ref).max()
+    Or, _ = A.attention_prefill(qd, kd, None, None, cfg.causal, v_deq=vd)
+    assert 0 < np.abs(Or - O).max() <= 0.05 * np.abs(O).max()
+
+
+def test_v4_bruteforce_and_online_causal_offset_with_selection():
+    cfg = SMALL_GQA_OFF.scaled(Hq=2, Hkv=1, Lq=128, Lk=384, qk_fmt="mxfp4", hadamard=False)
+    q, k, v, qd, kd, vc, sv = _prepare(cfg)
+    vd = _v4(v)
+    bitmap = np.zeros((1, 2, 1, 3), np.uint8); bitmap[0, 1, 0, 1] = 1
+    rows = np.array([0, 3, 64, 127])
+    O, _ = A.attention_prefill(qd, kd, None, None, True, q_orig=q, k_orig=k, v_orig=v, bitmap=bitmap, rows=rows,
+                               v_deq=vd)
+    for h in range(2):
+        ref = bf.attention_rows(rows.tolist(), qd[0, h].tolist(), kd[0, 0].tolist(), None, None, q[0, h].tolist(),
+                                k[0, 0].tolist(), v[0, 0].tolist(), lambda i, j, h=h: bool(bitmap[0, h, i, j]), 128,
+                                384, True, 1 / np.sqrt(128), Vd=vd[0, 0].tolist())
+        assert np.abs(O[0, h] - np.array(ref)).max() <= 1e-6 * np.abs(ref).max()
+        on, _ = A.attend_rows_online(rows, qd[0, h, rows], kd[0, 0], None, None, 1 / np.sqrt(128), 128, 384, True,
+                                     q_orig_rows=q[0, h, rows], k_orig=k[0, 0], v_orig=v[0, 0],
+                                     sel_row=bitmap[0, h, 0], tile_order=[2, 0, 1], v_deq=vd[0, 0])
+        assert np.abs(on - O[0, h]).max() <= 1e-6 * np.abs(O[0, h]).max()     # O is float32
