@@ -155,7 +155,8 @@ def time_prefill(fa4, cfg, steps, warmup, select):
     attention kernel is timed on its own loop of back-to-back launches over the same inputs."""
     q, k, v = (t.cuda() for t in W.prefill_inputs(cfg))
     fmt = {"mxfp4": fa4.FA4_MXFP4, "nvfp4": fa4.FA4_NVFP4, "mxfp8": fa4.FA4_MXFP8}[cfg.qk_fmt]
-    run = fa4.PrefillRunner(q, k, v, cfg.causal, fmt=fmt, hadamard=cfg.hadamard, select=select)
+    vf = fa4.FA4_MXFP4_KEYS if cfg.v_fmt == "mxfp4k" else fa4.FA4_FP8_TOKEN
+    run = fa4.PrefillRunner(q, k, v, cfg.causal, fmt=fmt, hadamard=cfg.hadamard, select=select, v_fmt=vf)
     for _ in range(warmup):
         run.run()
     step_ms = _time_loop(run.run, steps)
@@ -163,16 +164,25 @@ def time_prefill(fa4, cfg, steps, warmup, select):
     return step_ms, attn_ms
 
 
+_KV_CACHE = {}
+
+
+def decode_kv_inputs(cfg):
+    """Padded K and V of a decode workload on the GPU, generated once per (workload id, shape): the
+    cache- and probability-format variants of one workload share their sequences and values."""
+    key = (cfg.workload, cfg.B, cfg.Hkv, cfg.d, cfg.ctx_lo, cfg.ctx_hi)
+    if key not in _KV_CACHE:
+        _KV_CACHE.clear()
+        lay = W.decode_layout(cfg)
+        _KV_CACHE[key] = (lay, [W.decode_kv_padded(cfg, lay, t, device="cuda") for t in (W.T_K, W.T_V)])
+    return _KV_CACHE[key]
+
+
 def time_decode(fa4, cfg, steps, warmup):
-    lay = W.decode_layout(cfg)
+    lay, xs = decode_kv_inputs(cfg)
     ctx, pt = lay.ctx_len.cuda(), lay.page_table.cuda()
     nv = cfg.kv_fmt == "nvfp4"
-    caches = []
-    for tensor in (W.T_K, W.T_V):
-        x = W.decode_kv_padded(cfg, lay, tensor, device="cuda")
-        caches.append(fa4.quantize_paged(x, fa4.FA4_NVFP4 if nv else fa4.FA4_MXFP4, ctx, pt, lay.num_pages))
-        del x
-    torch.cuda.empty_cache()
+    caches = [fa4.quantize_paged(x, fa4.FA4_NVFP4 if nv else fa4.FA4_MXFP4, ctx, pt, lay.num_pages) for x in xs]
     q = W.decode_query(cfg).cuda()
     run = fa4.DecodeRunner(q, caches[0], caches[1], pt, ctx, cfg.Hkv,
                            p_fmt=fa4.FA4_P_NVFP4 if cfg.p_fmt == "nvfp4" else fa4.FA4_P_FP8)
@@ -186,6 +196,8 @@ def time_decode(fa4, cfg, steps, warmup):
 
 
 def time_decode_mla(fa4, cfg, steps, warmup):
+    _KV_CACHE.clear()
+    torch.cuda.empty_cache()
     lay = W.decode_layout(cfg)
     ctx, pt = lay.ctx_len.cuda(), lay.page_table.cuda()
     x = W.decode_kv_padded(cfg, lay, W.T_K, device="cuda")[:, 0].contiguous()
@@ -252,7 +264,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=W.C1.name,
-                    choices=[c.name for c in W.WORKLOADS + [W.C1_MX8] if isinstance(c, W.Prefill)])
+                    choices=[c.name for c in W.WORKLOADS + [W.C1_MX8, W.C1_V4] if isinstance(c, W.Prefill)])
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-p4", action="store_true", help="skip the decode steps with NVFP4 probabilities")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -269,7 +281,7 @@ def main():
         sys.exit(2)
     import fp8_quantized_attention_amd as fa4
 
-    cfg = next(c for c in W.WORKLOADS + [W.C1_MX8] if c.name == args.workload)
+    cfg = next(c for c in W.WORKLOADS + [W.C1_MX8, W.C1_V4] if c.name == args.workload)
     select = (5, 100) if cfg.select else None
     if args.copy_probe:
         copy_probe()
@@ -288,7 +300,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": cfg.qk_fmt + "+fp8",
+        "dtype": cfg.qk_fmt + ("+fp4v" if cfg.v_fmt == "mxfp4k" else "+fp8"),
         "data": "synthetic",
         "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "Lq": cfg.Lq, "Lk": cfg.Lk,
                    "d": cfg.d, "causal": cfg.causal, "qk_format": cfg.qk_fmt, "hadamard": cfg.hadamard,

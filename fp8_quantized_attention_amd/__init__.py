@@ -20,7 +20,7 @@ lib = ctypes.CDLL(LIB_PATH)
 
 FA4_OK, FA4_ERR_NULL, FA4_ERR_SHAPE, FA4_ERR_UNSUPPORTED, FA4_ERR_ALIGN, FA4_ERR_WORKSPACE, FA4_ERR_HIP = range(7)
 FA4_F32, FA4_BF16 = 0, 1
-FA4_MXFP4, FA4_NVFP4, FA4_FP8_TOKEN, FA4_MXFP8 = 0, 1, 2, 3
+FA4_MXFP4, FA4_NVFP4, FA4_FP8_TOKEN, FA4_MXFP8, FA4_MXFP4_KEYS = 0, 1, 2, 3, 4
 FA4_HADAMARD128, FA4_DUAL_RESIDUAL, FA4_SCALE_SEARCH = 1, 2, 4
 FA4_P_FP8, FA4_P_NVFP4 = 0, 1                      # decode probability formats
 
@@ -48,7 +48,8 @@ class AttnArgs(ctypes.Structure):
                 ("k_codes", _p), ("k_scales", _p), ("k_tscale", _p), ("v_codes", _p), ("v_scales", _p),
                 ("v_fold_w", _p), ("v_fold_scale", _p), ("q_bf16", _p), ("k_bf16", _p), ("v_bf16", _p), ("bitmap", _p),
                 ("B", _i32), ("Hq", _i32), ("Hkv", _i32), ("Lq", _i32), ("Lk", _i32), ("d", _i32),
-                ("causal", _i32), ("softmax_scale", _f32), ("o", _p), ("lse", _p)]
+                ("causal", _i32), ("softmax_scale", _f32), ("o", _p), ("lse", _p), ("v_fmt", _i32),
+                ("v_block_scales", _p)]
 
 
 class DecodeArgs(ctypes.Structure):
@@ -129,6 +130,10 @@ def quantize(x, fmt, hadamard=False, dual=False, row_norms=False, fold=None, cha
         out["codes"] = torch.empty(O, H, R, d, **u8)
         out["scales"] = torch.empty(O, H, R, dtype=torch.float32, device=dev)
         bs = None
+    elif fmt == FA4_MXFP4_KEYS:          # 4-bit V: blocks of 32 along the rows, codes per column
+        out["codes"] = torch.empty(O, H, d, R // 2, **u8)
+        out["block_scales"] = bs = torch.empty(O, H, d, R // 32, **u8)
+        out["scales"] = None
     elif fmt == FA4_MXFP8:
         out["codes"] = torch.empty(O, H, R, d, **u8)
         out["block_scales"] = bs = torch.empty(O, H, R, d // 32, **u8)
@@ -224,12 +229,14 @@ def select_tiles(q_norm2, k_norm2, causal, num=5, den=100):
 # ---------------------------------------------------------------------------------------------------- attention
 
 def attn_fwd(q, k, v, causal, fmt, Hq, Hkv, Lq, Lk, d, B=1, bitmap=None, q_bf16=None, k_bf16=None,
-             v_bf16=None, softmax_scale=None, want_lse=True, out=None, lse=None):
+             v_bf16=None, softmax_scale=None, want_lse=True, out=None, lse=None, v_fmt=FA4_FP8_TOKEN):
     """Prefill attention from quantized operands (dicts as returned by quantize()).
 
-    q/k hold MXFP4, NVFP4 or MXFP8 codes and scales, v holds FP8 per-token codes and scales.
+    q/k hold MXFP4, NVFP4 or MXFP8 codes and scales; v holds FP8 per-token codes and scales
+    (v_fmt FA4_FP8_TOKEN) or 4-bit V (v_fmt FA4_MXFP4_KEYS, MXFP4 Q/K only, no bitmap).
     Returns (o [B, Hq, Lq, d] float32, lse [B, Hq, Lq] float32 or None).
     """
+    v4 = v_fmt == FA4_MXFP4_KEYS
     dev = q["codes"].device
     if out is None:
         out = torch.empty(B, Hq, Lq, d, dtype=torch.float32, device=dev)
@@ -239,9 +246,10 @@ def attn_fwd(q, k, v, causal, fmt, Hq, Hkv, Lq, Lk, d, B=1, bitmap=None, q_bf16=
         softmax_scale = 1.0 / math.sqrt(d)
     a = AttnArgs(fmt, q["codes"].data_ptr(), q["block_scales"].data_ptr(), _ptr(q.get("scales")),
                  k["codes"].data_ptr(), k["block_scales"].data_ptr(), _ptr(k.get("scales")),
-                 v["codes"].data_ptr(), v["scales"].data_ptr(), v["fold_w"].data_ptr(), v["fold_scale"].data_ptr(),
+                 v["codes"].data_ptr(), _ptr(v.get("scales")), _ptr(v.get("fold_w")), _ptr(v.get("fold_scale")),
                  _ptr(q_bf16), _ptr(k_bf16), _ptr(v_bf16), _ptr(bitmap),
-                 B, Hq, Hkv, Lq, Lk, d, int(causal), softmax_scale, out.data_ptr(), _ptr(lse if want_lse else None))
+                 B, Hq, Hkv, Lq, Lk, d, int(causal), softmax_scale, out.data_ptr(), _ptr(lse if want_lse else None),
+                 v_fmt if v4 else 0, _ptr(v.get("block_scales")) if v4 else None)
     _check(lib.fa4_attn_fwd(ctypes.byref(a), _stream()), "fa4_attn_fwd")
     return out, (lse if want_lse else None)
 
@@ -375,7 +383,7 @@ class DecodeMlaRunner:
 # ---------------------------------------------------------------------------------------------------- pipelines
 
 def prefill(q, k, v, causal, fmt=FA4_MXFP4, hadamard=False, select=None, softmax_scale=None, want_lse=True,
-            smooth=None, search=False):
+            smooth=None, search=False, v_fmt=FA4_FP8_TOKEN):
     """Whole prefill path: quantize Q/K (MXFP4 or NVFP4, optional Hadamard), V to FP8 per token,
     optionally select the top num/den tiles for bf16 (select=(num, den)), then fused attention.
 
@@ -389,13 +397,13 @@ def prefill(q, k, v, causal, fmt=FA4_MXFP4, hadamard=False, select=None, softmax
     qs, ks = smooth if smooth is not None else (None, None)
     qq = quantize(q, fmt, hadamard=hadamard, row_norms=sel, channel_scale=qs)
     kq = quantize(k, fmt, hadamard=hadamard, row_norms=sel, channel_scale=ks, search=search)
-    vq = quantize(v, FA4_FP8_TOKEN)
+    vq = quantize(v, v_fmt)
     bitmap = counts = None
     if sel:
         bitmap, counts = select_tiles(qq["norm2"], kq["norm2"], causal, select[0], select[1])
     o, lse = attn_fwd(qq, kq, vq, causal, fmt, Hq, Hkv, Lq, Lk, d, B=B, bitmap=bitmap,
                       q_bf16=q if sel else None, k_bf16=k if sel else None, v_bf16=v if sel else None,
-                      softmax_scale=softmax_scale, want_lse=want_lse)
+                      softmax_scale=softmax_scale, want_lse=want_lse, v_fmt=v_fmt)
     return {"o": o, "lse": lse, "bitmap": bitmap, "counts": counts, "q": qq, "k": kq, "v": vq}
 
 
@@ -451,7 +459,7 @@ class PrefillRunner:
     """
 
     def __init__(self, q, k, v, causal, fmt=FA4_MXFP4, hadamard=False, select=None, softmax_scale=None,
-                 smooth=None, search=False):
+                 smooth=None, search=False, v_fmt=FA4_FP8_TOKEN):
         self.q, self.k, self.v = q, k, v
         B, Hq, Lq, d = q.shape
         Hkv, Lk = k.shape[1], k.shape[2]
@@ -468,8 +476,12 @@ class PrefillRunner:
         self.kq = {"codes": torch.empty(B, Hkv, Lk, cw, **u8), "block_scales": torch.empty(B, Hkv, Lk, nb, **u8),
                    "scales": torch.empty(B * Hkv, **f32) if fmt == FA4_NVFP4 else None,
                    "norm2": torch.empty(B, Hkv, Lk, **f32) if self.sel else None}
-        self.vq = {"codes": torch.empty(B, Hkv, Lk, d, **u8), "scales": torch.empty(B, Hkv, Lk, **f32),
-                   "fold_w": torch.empty(B, Hkv, Lk, **f32), "fold_scale": torch.empty(B, Hkv, Lk // 128, **f32)}
+        v4 = v_fmt == FA4_MXFP4_KEYS
+        if v4:
+            self.vq = {"codes": torch.empty(B, Hkv, d, Lk // 2, **u8), "block_scales": torch.empty(B, Hkv, d, Lk // 32, **u8)}
+        else:
+            self.vq = {"codes": torch.empty(B, Hkv, Lk, d, **u8), "scales": torch.empty(B, Hkv, Lk, **f32),
+                       "fold_w": torch.empty(B, Hkv, Lk, **f32), "fold_scale": torch.empty(B, Hkv, Lk // 128, **f32)}
         self.o = torch.empty(B, Hq, Lq, d, **f32)
         self.lse = torch.empty(B, Hq, Lq, **f32)
         self.bitmap = torch.empty(B, Hq, Lq // 128, Lk // 128, **u8) if self.sel else None
@@ -487,7 +499,7 @@ class PrefillRunner:
         self.smooth = smooth
         qs, ks = smooth if smooth is not None else (None, None)
         self._qi = [qin(q, qs), qin(k, ks), qin(v)]
-        self._qo = [qout(fmt, self.qq), qout(fmt, self.kq), qout(FA4_FP8_TOKEN, self.vq)]
+        self._qo = [qout(fmt, self.qq), qout(fmt, self.kq), qout(FA4_MXFP4_KEYS if v4 else FA4_FP8_TOKEN, self.vq)]
         self._norms = [_ptr(self.qq["norm2"]), _ptr(self.kq["norm2"]), None]
         self._fl = [self.flags, self.flags | (FA4_SCALE_SEARCH if search else 0), 0]
         if softmax_scale is None:
@@ -495,12 +507,13 @@ class PrefillRunner:
         self._attn = AttnArgs(fmt, self.qq["codes"].data_ptr(), self.qq["block_scales"].data_ptr(),
                               _ptr(self.qq["scales"]), self.kq["codes"].data_ptr(),
                               self.kq["block_scales"].data_ptr(), _ptr(self.kq["scales"]),
-                              self.vq["codes"].data_ptr(), self.vq["scales"].data_ptr(),
-                              self.vq["fold_w"].data_ptr(), self.vq["fold_scale"].data_ptr(),
+                              self.vq["codes"].data_ptr(), _ptr(self.vq.get("scales")),
+                              _ptr(self.vq.get("fold_w")), _ptr(self.vq.get("fold_scale")),
                               q.data_ptr() if self.sel else None, k.data_ptr() if self.sel else None,
                               v.data_ptr() if self.sel else None, _ptr(self.bitmap),
                               B, Hq, Hkv, Lq, Lk, d, int(causal), softmax_scale, self.o.data_ptr(),
-                              self.lse.data_ptr())
+                              self.lse.data_ptr(), FA4_MXFP4_KEYS if v4 else 0,
+                              _ptr(self.vq.get("block_scales")) if v4 else None)
         self.shape = (B, Hq, Hkv, Lq, Lk, d)
 
     def quantize(self, stream=None):

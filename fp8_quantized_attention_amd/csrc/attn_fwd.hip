@@ -39,6 +39,7 @@ struct AttnArgs {
   const uint8_t *kc, *ks; const float *kt;
   const uint8_t *vc; const float *vs;
   const float *vw, *vfs;
+  const uint8_t *vbs;                 // 4-bit V: E8M0 scales [B][Hkv][d][Lk/32] (codes in vc: [B][Hkv][d][Lk/2])
   const uint16_t *qb, *kb, *vb;
   const uint8_t *bitmap;
   int B, Hq, Hkv, Lq, Lk, causal;
@@ -239,12 +240,15 @@ __device__ __forceinline__ int tile_weight(float r, float &m, float &lsum, v16f 
 
 // P' = 2^(S cs - r) for key block kb (summed into ts) and P^ = E4M3(P' w_c), w_c = s_v[c] 2^-e
 // (exact), packed straight into the PV B operand, so scores and probabilities are never both held.
+template <bool V4>
 __device__ __forceinline__ void fp8_block(const v16f &Skb, int kb, const float *svs, const LaneOff &lo, float cs,
                                           float rr0, float &ts, v8i pop[2]) {
 #pragma unroll
   for (int a4 = 0; a4 < 4; a4++) {
-    const float4 w4 = *reinterpret_cast<const float4 *>(reinterpret_cast<const uint8_t *>(svs) + lo.w +
-                                                        4 * (32 * kb + 8 * a4));
+    // 4-bit V has no per-token scale to fold: P^ = E4M3(448 P'), the 448 leaves with the final division
+    const float4 w4 = V4 ? make_float4(448.0f, 448.0f, 448.0f, 448.0f)
+                         : *reinterpret_cast<const float4 *>(reinterpret_cast<const uint8_t *>(svs) + lo.w +
+                                                             4 * (32 * kb + 8 * a4));
     const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
     float pw[4];
 #pragma unroll
@@ -287,6 +291,31 @@ __device__ __forceinline__ void pv_fp8(const v8i pop[2], const uint8_t *vq, cons
   }
 }
 
+// O^T += V^T P^T for a tile of 4-bit V (MXFP4, E8M0 scales along the keys): V^T rows (one value of d,
+// 128 keys) sit in LDS as 64 code bytes each, 16-byte pieces XOR-swizzled as K's. The A operand of MFMA t
+// (keys 64 t .. 64 t + 63) for row 32 mb + (lane % 32) is the piece 2 t + lane / 32, with that
+// 32-key block's scale byte: FP4 V^T times FP8 P^T in one scaled MFMA, both scales applied inside.
+// Within each 32-key block the codes are stored in the key order of the FP8 operand (P^T's bytes 4 a + u
+// of lane half h are keys 8 a + 4 h + u), so no reordering is needed here.
+template <int D>
+__device__ __forceinline__ void pv_fp4v(const v8i pop[2], const uint8_t *vt, const uint8_t *vts, int lane, int kBc,
+                                        v16f *acc) {
+  constexpr int NDB = D / 32;
+  const int h = lane >> 5;
+#pragma unroll
+  for (int mb = 0; mb < NDB; mb++) {
+    const int row = 32 * mb + (lane & 31);
+    const uint32_t sw = *reinterpret_cast<const uint32_t *>(vts + 4 * row);     // the row's 4 block scales
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+      const v4i c = *reinterpret_cast<const v4i *>(vt + row * 64 + 16 * ((2 * t + h) ^ kswz<128>(row)));
+      const int sa = (int)((sw >> (8 * (2 * t + h))) & 0xffu);
+      acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4((v8i){c[0], c[1], c[2], c[3], 0, 0, 0, 0}, pop[t],
+                                                                acc[mb], 4, 0, 0, sa, 0, kBc + 127);
+    }
+  }
+}
+
 // Wave-uniform reads go through the constant address space, so they become scalar loads (counted
 // apart from the vector loads: waiting for one never waits for the tile loads in flight).
 template <typename T>
@@ -303,7 +332,7 @@ __device__ __forceinline__ int v_tile_scale_code(const float *vfs, int64_t bhk, 
 // One 128-key tile for this wave's 32 queries: S^T = K Q^T, softmax step, O^T += V^T P^T.
 // MASK: the tile crosses the causal diagonal (keys past the query position get -inf).
 // sel: a selected tile, computed from the bf16 originals (QK^T and PV on bf16 MFMA).
-template <int D, int QF, bool MASK, bool sel>
+template <int D, int QF, bool MASK, bool sel, bool V4 = false>
 __device__ __forceinline__ void tile_step(const AttnArgs &a, const LaneOff &lo, int kt, int lane, int hh, int col, int qrow,
                                           int off, int64_t bhq, int64_t bhk, int nk, float cs_q, float cs_b,
                                           const v8i *qop4, const int *qsc4, const v8h *qop16, const uint8_t *k4,
@@ -380,13 +409,16 @@ __device__ __forceinline__ void tile_step(const AttnArgs &a, const LaneOff &lo, 
   } else {
     v8i pop[2];
 #pragma unroll
-    for (int kb = 0; kb < 4; kb++) fp8_block(S[kb], kb, svs, lo, cs, rr0, ts[kb], pop);
-    pv_fp8<D, QF>(pop, vq, lo, v_tile_scale_code(a.vfs, bhk, nk, kt), kBc, acc);
+    for (int kb = 0; kb < 4; kb++) fp8_block<V4>(S[kb], kb, svs, lo, cs, rr0, ts[kb], pop);
+    if constexpr (V4)   // vq: V^T codes; svs: V^T block scales (the fold-factor slot of the tile buffer)
+      pv_fp4v<D>(pop, vq, reinterpret_cast<const uint8_t *>(svs), lane, kBc, acc);
+    else
+      pv_fp8<D, QF>(pop, vq, lo, v_tile_scale_code(a.vfs, bhk, nk, kt), kBc, acc);
   }
   lsum += __builtin_ldexpf((ts[0] + ts[1]) + (ts[2] + ts[3]), kB);
 }
 
-template <int D, int QF, bool CAUSAL, bool SEL>
+template <int D, int QF, bool CAUSAL, bool SEL, bool V4 = false>
 __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
   constexpr int NDB = D / 32;        // 32-row blocks of d in O^T
   typedef AttnLds<D, QF, SEL> L;
@@ -482,7 +514,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
 // One tile step; MASKV and SELV must be constants. With Lq and Lk multiples of 128 the only tile that
 // crosses the causal diagonal is the last one, so loops run MASKV = false and the diagonal tile is peeled.
 #define FA4_TILE_STEP(MASKV, SELV, KT, KC, KS, VC, W)                                                         \
-  tile_step<D, QF, MASKV, SELV>(a, lo, KT, lane, hh, col, qrow, off, bhq, bhk, nk, cs_q, cs_b, qop4, qsc4, qop16, \
+  tile_step<D, QF, MASKV, SELV, V4>(a, lo, KT, lane, hh, col, qrow, off, bhq, bhk, nk, cs_q, cs_b, qop4, qsc4, qop16, \
                                 KC, KS, k16, VC, v16, W, m, lsum, acc)
 
   // Tiles are visited in two passes: first every tile computed from the quantized operands, then the
@@ -506,18 +538,35 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
         const int r = i * (1024 / (D / 2)) + lane / (D / 32), p = lane % (D / 32);
         dma16(a.kc + (krow0 + r) * (D / 2) + 16 * (p ^ kswz<D>(r)), base + 1024 * i);
       }
+      if constexpr (V4) {
+        // V^T rows (d = 0 .. 127) of the tile: 64 bytes each at key offset 64 kt, laid out as K's rows
 #pragma unroll
-      for (int e = 0; e < VI; e++) {
-        const int i = wave * VI + e;
-        const int r = i * (1024 / D) + lane / (D / 16), p = lane % (D / 16);
-        dma16(a.vc + (krow0 + r) * D + 16 * (p ^ vswz<D>(r)), base + L::KC + L::KS + 1024 * i);
+        for (int e = 0; e < KI; e++) {
+          const int i = wave * KI + e;
+          const int r = i * 16 + lane / 4, p = lane % 4;
+          dma16(a.vc + (bhk * D + r) * (a.Lk / 2) + (int64_t)kt * 64 + 16 * (p ^ kswz<128>(r)),
+                base + L::KC + L::KS + 1024 * i);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < VI; e++) {
+          const int i = wave * VI + e;
+          const int r = i * (1024 / D) + lane / (D / 16), p = lane % (D / 16);
+          dma16(a.vc + (krow0 + r) * D + 16 * (p ^ vswz<D>(r)), base + L::KC + L::KS + 1024 * i);
+        }
       }
       if (D == 128) {
         if (wave < 2) dma4(a.ks + (krow0 + 64 * wave + lane) * 4, base + L::KC + 256 * wave);
       } else if (wave == 0) {
         dma4(a.ks + krow0 * 2 + 4 * lane, base + L::KC);
       }
-      if (wave >= 2) dma4(a.vw + krow0 + 64 * (wave - 2) + lane, base + L::KC + L::KS + L::VC + 256 * (wave - 2));
+      if (V4) {           // the 4 scale bytes of each V^T row into the fold-factor slot
+        if (wave >= 2)
+          dma4(a.vbs + (bhk * D + 64 * (wave - 2) + lane) * (a.Lk / 32) + (int64_t)kt * 4,
+               base + L::KC + L::KS + L::VC + 256 * (wave - 2));
+      } else if (wave >= 2) {
+        dma4(a.vw + krow0 + 64 * (wave - 2) + lane, base + L::KC + L::KS + L::VC + 256 * (wave - 2));
+      }
     };
     int b = 0;
     int kt = next_quant(0);
@@ -641,7 +690,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
 #undef FA4_TILE_STEP
   // ---------------- epilogue: O = O_acc / l, LSE = m ln2 + ln l
   const float l = lsum + shfl_xor_f(lsum, 32);
-  const float fin = 1.0f / l;
+  const float fin = (V4 ? 1.0f / 448.0f : 1.0f) / l;     // 4-bit V: P^ carried a factor 448
   float *orow = a.o + (bhq * a.Lq + qrow) * D;
 #pragma unroll
   for (int mb = 0; mb < NDB; mb++)
@@ -655,10 +704,21 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
 }
 
 // Kernels whose LDS exceeds the default dynamic limit are opted in (idempotent, cheap).
-template <int D, int QF, bool CAUSAL, bool SEL>
+template <int D, int QF, bool CAUSAL, bool SEL, bool V4 = false>
 static hipError_t allow_lds() {
-  return hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_fwd_kernel<D, QF, CAUSAL, SEL>),
+  return hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_fwd_kernel<D, QF, CAUSAL, SEL, V4>),
                              hipFuncAttributeMaxDynamicSharedMemorySize, AttnLds<D, QF, SEL>::BYTES);
+}
+
+// MXFP4 Q/K with 4-bit V (d = 128, no bitmap)
+static hipError_t launch_attn_v4(const AttnArgs &x, bool causal, hipStream_t s) {
+  dim3 grid((unsigned)((int64_t)(x.Lq / 128) * x.Hq * x.B));
+  hipError_t e = causal ? allow_lds<128, FA4_MXFP4, true, false, true>() : allow_lds<128, FA4_MXFP4, false, false, true>();
+  if (e != hipSuccess) return e;
+  const size_t l0 = AttnLds<128, FA4_MXFP4, false>::BYTES;
+  if (causal) hipLaunchKernelGGL((attn_fwd_kernel<128, FA4_MXFP4, true, false, true>), grid, dim3(ATT_THREADS), l0, s, x);
+  else hipLaunchKernelGGL((attn_fwd_kernel<128, FA4_MXFP4, false, false, true>), grid, dim3(ATT_THREADS), l0, s, x);
+  return hipGetLastError();
 }
 
 template <int D, int QF>
@@ -684,6 +744,7 @@ hipError_t launch_attn(const fa4_attn_args *p, hipStream_t s) {
   x.kc = p->k_codes; x.ks = p->k_scales; x.kt = p->k_tscale;
   x.vc = p->v_codes; x.vs = p->v_scales;
   x.vw = p->v_fold_w; x.vfs = p->v_fold_scale;
+  x.vbs = p->v_block_scales;
   x.qb = p->q_bf16; x.kb = p->k_bf16; x.vb = p->v_bf16;
   x.bitmap = p->bitmap;
   x.B = p->B; x.Hq = p->Hq; x.Hkv = p->Hkv; x.Lq = p->Lq; x.Lk = p->Lk; x.causal = p->causal;
@@ -691,6 +752,7 @@ hipError_t launch_attn(const fa4_attn_args *p, hipStream_t s) {
   x.o = p->o; x.lse = p->lse;
   if (x.B == 0 || x.Hq == 0 || x.Lq == 0) return hipSuccess;
   const bool causal = p->causal != 0, sel = p->bitmap != nullptr;
+  if (p->v_fmt == FA4_MXFP4_KEYS) return launch_attn_v4(x, causal, s);
   if (p->fmt == FA4_MXFP4) {
     if (p->d == 64) return launch_attn_t<64, FA4_MXFP4>(x, causal, false, s);
     return launch_attn_t<128, FA4_MXFP4>(x, causal, sel, s);

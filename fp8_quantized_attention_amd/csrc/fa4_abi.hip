@@ -64,8 +64,18 @@ fa4_status fa4_quantize_blockscaled(const fa4_qinput *in, uint32_t flags, const 
   REQUIRE(in && out, FA4_ERR_NULL, "quantize: input or output descriptor is NULL");
   REQUIRE(in->dtype == FA4_F32 || in->dtype == FA4_BF16, FA4_ERR_UNSUPPORTED, "quantize: dtype %d", in->dtype);
   REQUIRE(in->d == 64 || in->d == 128, FA4_ERR_UNSUPPORTED, "quantize: d=%d (64 or 128)", in->d);
-  REQUIRE(out->fmt == FA4_MXFP4 || out->fmt == FA4_NVFP4 || out->fmt == FA4_FP8_TOKEN || out->fmt == FA4_MXFP8,
+  REQUIRE(out->fmt == FA4_MXFP4 || out->fmt == FA4_NVFP4 || out->fmt == FA4_FP8_TOKEN || out->fmt == FA4_MXFP8 ||
+              out->fmt == FA4_MXFP4_KEYS,
           FA4_ERR_UNSUPPORTED, "quantize: format %d", out->fmt);
+  if (out->fmt == FA4_MXFP4_KEYS) {
+    REQUIRE(flags == 0 && !residual && !row_norm2 && !in->page_table && !in->row_counts && !in->channel_scale &&
+                !out->fold_w && !out->fold_scale,
+            FA4_ERR_UNSUPPORTED, "quantize: MXFP4_KEYS takes no flags, residual, row norms, paging, ragged rows, "
+                                 "smoothing or fold outputs");
+    REQUIRE(in->rows % 32 == 0, FA4_ERR_SHAPE, "quantize: MXFP4_KEYS needs rows in multiples of 32 (rows=%lld)",
+            (long long)in->rows);
+    REQUIRE(in->rows / 32 <= 0x7fffffff, FA4_ERR_SHAPE, "quantize: MXFP4_KEYS grid too large");
+  }
   REQUIRE((flags & ~(uint32_t)(FA4_HADAMARD128 | FA4_DUAL_RESIDUAL | FA4_SCALE_SEARCH)) == 0, FA4_ERR_UNSUPPORTED,
           "quantize: unknown flags 0x%x", flags);
   if (flags & FA4_SCALE_SEARCH) {
@@ -162,10 +172,20 @@ fa4_status fa4_attn_fwd(const fa4_attn_args *a, void *stream) {
             "attn: MXFP4 supports d=128, or d=64 without tile selection (d=%d)", a->d);
   else
     REQUIRE(a->d == 128, FA4_ERR_UNSUPPORTED, "attn: NVFP4 and MXFP8 need d=128 (d=%d)", a->d);
+  const bool v4 = a->v_fmt == FA4_MXFP4_KEYS;
+  REQUIRE(v4 || a->v_fmt == 0 || a->v_fmt == FA4_FP8_TOKEN, FA4_ERR_UNSUPPORTED, "attn: V format %d", a->v_fmt);
+  if (v4)
+    REQUIRE(a->fmt == FA4_MXFP4 && a->d == 128 && !a->bitmap, FA4_ERR_UNSUPPORTED,
+            "attn: 4-bit V needs MXFP4 Q/K, d=128 and no tile selection");
   if (a->B == 0 || a->Lq == 0) return ok();
-  REQUIRE(a->q_codes && a->q_scales && a->k_codes && a->k_scales && a->v_codes && a->v_scales && a->o &&
-              a->v_fold_w && a->v_fold_scale,
-          FA4_ERR_NULL, "attn: a required pointer is NULL");
+  if (v4)
+    REQUIRE(a->q_codes && a->q_scales && a->k_codes && a->k_scales && a->v_codes && a->v_block_scales && a->o,
+            FA4_ERR_NULL, "attn: a required pointer is NULL");
+  else
+    REQUIRE(a->q_codes && a->q_scales && a->k_codes && a->k_scales && a->v_codes && a->v_scales && a->o &&
+                a->v_fold_w && a->v_fold_scale,
+            FA4_ERR_NULL, "attn: a required pointer is NULL");
+  REQUIRE(aligned(a->v_block_scales, 16), FA4_ERR_ALIGN, "attn: every pointer must be 16-byte aligned");
   if (a->fmt == FA4_NVFP4) REQUIRE(a->q_tscale && a->k_tscale, FA4_ERR_NULL, "attn: NVFP4 tensor scales NULL");
   if (a->bitmap) REQUIRE(a->q_bf16 && a->k_bf16 && a->v_bf16, FA4_ERR_NULL, "attn: bf16 originals needed with a bitmap");
   const void *ptrs[] = {a->q_codes, a->q_scales, a->k_codes, a->k_scales, a->v_codes, a->v_scales, a->o,

@@ -750,6 +750,39 @@ hipError_t launch_smoothing(const fa4_qinput *q, const fa4_qinput *k, float *q_s
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------------- MXFP4 along rows
+// 4-bit V for prefill: MXFP4 with 32-element blocks along the rows (the keys) of each column. Thread =
+// (group, column c, block of 32 rows); the loads of a block's rows are coalesced over the columns. Codes
+// of column c: [group][d][rows/2], two per byte, low nibble first; within a block, code position j holds
+// row 8 ((j >> 2) & 3) + 4 (j >> 4) + (j & 3) of the block (the key order of the attention's FP8
+// probability operand). Scales: [group][d][rows/32] E8M0, the MXFP4 rule of the row quantizer.
+template <int DT>
+__global__ void __launch_bounds__(128) mx_keys_kernel(QArgs a, int d) {
+  const int c = threadIdx.x, g = blockIdx.y, r0 = 32 * blockIdx.x;
+  if (c >= d) return;
+  const int64_t o = g / a.heads, h = g - o * a.heads;
+  const int64_t base = o * a.so + h * a.sh + (int64_t)r0 * a.sr + c;
+  float v[32];
+#pragma unroll
+  for (int j = 0; j < 32; j++)
+    v[j] = DT == 0 ? static_cast<const float *>(a.x)[base + j * a.sr]
+                   : bf16_bits_to_float(static_cast<const uint16_t *>(a.x)[base + j * a.sr]);
+  float am = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 32; j++) am = fmaxf(am, fabsf(v[j]));
+  const int e = mx_exponent(am);
+  const float mul = pow2_neg(e);                              // exact scaling (a power of two)
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int jp = 0; jp < 32; jp += 2) {                        // positions jp, jp + 1: rows k0, k0 + 1
+    const int k0 = 8 * ((jp >> 2) & 3) + 4 * (jp >> 4) + (jp & 3);
+    w[jp >> 3] |= e2m1_pair(v[k0] * mul, v[k0 + 1] * mul) << (4 * (jp & 7));
+  }
+  const int64_t row = (int64_t)g * d + c;
+  *reinterpret_cast<uint4 *>(a.codes + row * (a.rows / 2) + r0 / 2) = make_uint4(w[0], w[1], w[2], w[3]);
+  a.bscales[row * (a.rows / 32) + r0 / 32] = (uint8_t)(e + 127);
+}
+
 hipError_t launch_quantize(const fa4_qinput *in, uint32_t flags, const fa4_qoutput *out,
                            const fa4_qoutput *res, float *norm2, hipStream_t s) {
   QArgs a;
@@ -766,6 +799,12 @@ hipError_t launch_quantize(const fa4_qinput *in, uint32_t flags, const fa4_qoutp
   const int64_t groups = in->outer * in->heads;
   const bool had = flags & FA4_HADAMARD128, dual = flags & FA4_DUAL_RESIDUAL, norm = norm2 != nullptr;
   const bool search = flags & FA4_SCALE_SEARCH;
+  if (out->fmt == FA4_MXFP4_KEYS) {
+    const dim3 grid((unsigned)(in->rows / 32), (unsigned)groups);
+    if (in->dtype == FA4_F32) hipLaunchKernelGGL(mx_keys_kernel<0>, grid, dim3(128), 0, s, a, in->d);
+    else hipLaunchKernelGGL(mx_keys_kernel<1>, grid, dim3(128), 0, s, a, in->d);
+    return hipGetLastError();
+  }
   if (in->d == 128) {
     return in->dtype == FA4_F32 ? quantize_dispatch<128, 0>(a, out->fmt, had, dual, search, groups, norm, s)
                                 : quantize_dispatch<128, 1>(a, out->fmt, had, dual, search, groups, norm, s);

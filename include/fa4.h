@@ -42,7 +42,7 @@ typedef enum {
 } fa4_status;
 
 enum { FA4_F32 = 0, FA4_BF16 = 1 };                      /* input element types       */
-enum { FA4_MXFP4 = 0, FA4_NVFP4 = 1, FA4_FP8_TOKEN = 2, FA4_MXFP8 = 3 }; /* quantized formats */
+enum { FA4_MXFP4 = 0, FA4_NVFP4 = 1, FA4_FP8_TOKEN = 2, FA4_MXFP8 = 3, FA4_MXFP4_KEYS = 4 }; /* quantized formats */
 enum { FA4_P_FP8 = 0, FA4_P_NVFP4 = 1 };                   /* decode probability formats */
 enum { FA4_HADAMARD128 = 1u << 0, FA4_DUAL_RESIDUAL = 1u << 1, FA4_SCALE_SEARCH = 1u << 2 }; /* quantizer flags */
 
@@ -75,6 +75,13 @@ enum { FA4_HADAMARD128 = 1u << 0, FA4_DUAL_RESIDUAL = 1u << 1, FA4_SCALE_SEARCH 
  *              nearest even ("MXFP vs NVFP4" sections 2.1 and 4.2). `scales` unused.
  *   FA4_FP8_TOKEN: codes [d] E4M3; scales = per-row float [out rows]: s = amax_row / 448 (1 if zero),
  *              codes = E4M3(x / s). block_scales unused.
+ *   FA4_MXFP4_KEYS (4-bit V for fa4_attn_fwd; "MpFA QK4V8" section 6 names 4-bit V): MXFP4 with the
+ *              32-element blocks along the rows (the keys) of each column, i.e. the MXFP4 rule above
+ *              applied to the columns. codes [groups][d][rows/2]: column c's values along the rows, two
+ *              per byte, low nibble first, and within each block of 32 rows code position j holds row
+ *              8 ((j >> 2) & 3) + 4 (j >> 4) + (j & 3) of the block (the key order of the attention's FP8
+ *              probability operand); block_scales [groups][d][rows/32] E8M0. rows % 32 == 0; no flags,
+ *              residual, row norms, paging, ragged rows, smoothing or fold outputs.
  * flags: FA4_HADAMARD128 rotates each row by the Sylvester Hadamard matrix H_128 / sqrt(128) (float64,
  *        rounded to float32) before quantizing (d must be 128; NVFP4 or MXFP4 only).
  *        FA4_DUAL_RESIDUAL (NVFP4 or MXFP4): `out` receives Q1 = F(x) and `residual` receives
@@ -188,6 +195,10 @@ fa4_status fa4_select_tiles(const float *q_norm2, const float *k_norm2, int32_t 
  * bitmap is given); bitmap [B][Hq][Lq/128][Lk/128] or NULL; o [B][Hq][Lq][d] float; lse [B][Hq][Lq]
  * float or NULL. Requirements: d = 128 (or 64 for MXFP4 without a bitmap); Lq, Lk multiples of 128;
  * Lq <= Lk when causal; Hq % Hkv == 0; every pointer 16-byte aligned.
+ * 4-bit V (v_fmt = FA4_MXFP4_KEYS; MXFP4 Q/K, d = 128, no bitmap): v_codes [B][Hkv][d][Lk/2] and
+ * v_block_scales as fa4_quantize_blockscaled's FA4_MXFP4_KEYS output; v_scales and v_fold_* are not read.
+ * Quantized tiles then take P^ = E4M3(448 P') and T = (1/448) sum_c P^ v^_c with the dequantized 4-bit
+ * values v^ (FP4 V^T times FP8 P^T in one block-scaled MFMA).
  */
 typedef struct {
   int32_t fmt;                                  /* FA4_MXFP4, FA4_NVFP4 or FA4_MXFP8 (Q and K) */
@@ -201,6 +212,9 @@ typedef struct {
   float softmax_scale;
   float *o;
   float *lse;
+  int32_t v_fmt;                               /* 0 or FA4_FP8_TOKEN: v_codes/v_scales/v_fold_* as above;
+                                                  FA4_MXFP4_KEYS: 4-bit V (see below)                  */
+  const uint8_t *v_block_scales;               /* FA4_MXFP4_KEYS: E8M0 [B][Hkv][d][Lk/32]             */
 } fa4_attn_args;
 
 fa4_status fa4_attn_fwd(const fa4_attn_args *a, void *stream);

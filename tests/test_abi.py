@@ -73,6 +73,14 @@ def test_quantize_rejects_before_launch():
     assert _call_q(_q(d=96)) == fa4.FA4_ERR_UNSUPPORTED
     assert _call_q(_q(dtype=7)) == fa4.FA4_ERR_UNSUPPORTED
     assert _call_q(_q(), fmt=9) == fa4.FA4_ERR_UNSUPPORTED
+    # MXFP4_KEYS (4-bit V): no flags, paging or row norms; rows in multiples of 32
+    assert _call_q(_q(), fmt=fa4.FA4_MXFP4_KEYS, flags=fa4.FA4_HADAMARD128) == fa4.FA4_ERR_UNSUPPORTED
+    assert _call_q(_q(rows=40, stride_head=40 * 128, stride_outer=2 * 40 * 128), fmt=fa4.FA4_MXFP4_KEYS) == \
+        fa4.FA4_ERR_SHAPE
+    assert _call_q(_q(), fmt=fa4.FA4_MXFP4_KEYS, norm=256) == fa4.FA4_ERR_UNSUPPORTED
+    assert _call_q(_q(page_table=256, page_size=64, max_pages=4, num_pages=8), fmt=fa4.FA4_MXFP4_KEYS) == \
+        fa4.FA4_ERR_UNSUPPORTED
+    assert _call_q(_q(), fmt=fa4.FA4_MXFP4_KEYS, bs=None) == fa4.FA4_ERR_NULL
     assert _call_q(_q(x=None)) == fa4.FA4_ERR_NULL
     assert _call_q(_q(x=18)) == fa4.FA4_ERR_ALIGN
     assert _call_q(_q(x=24)) == fa4.FA4_ERR_ALIGN                     # 8-byte aligned is not enough
@@ -121,7 +129,8 @@ def test_smoothing_rejects_before_launch():
 def _attn(**kw):
     base = dict(fmt=fa4.FA4_MXFP4, q_codes=256, q_scales=256, q_tscale=None, k_codes=256, k_scales=256,
                 k_tscale=None, v_codes=256, v_scales=256, v_fold_w=256, v_fold_scale=256, q_bf16=None, k_bf16=None, v_bf16=None, bitmap=None,
-                B=1, Hq=4, Hkv=2, Lq=256, Lk=512, d=128, causal=1, softmax_scale=0.088, o=256, lse=None)
+                B=1, Hq=4, Hkv=2, Lq=256, Lk=512, d=128, causal=1, softmax_scale=0.088, o=256, lse=None,
+                v_fmt=0, v_block_scales=None)
     base.update(kw)
     return fa4.AttnArgs(*[base[f] for f, _ in fa4.AttnArgs._fields_])
 
@@ -143,6 +152,14 @@ def test_attention_rejects_before_launch():
     assert call(_attn(v_codes=264)) == fa4.FA4_ERR_ALIGN
     assert call(_attn(softmax_scale=0.0)) == fa4.FA4_ERR_SHAPE
     assert call(_attn(Lq=0)) == fa4.FA4_OK
+    # 4-bit V: MXFP4 Q/K, d = 128, no bitmap; its E8M0 scales replace v_scales and the fold data
+    v4 = dict(v_fmt=fa4.FA4_MXFP4_KEYS, v_scales=None, v_fold_w=None, v_fold_scale=None, v_block_scales=256)
+    assert call(_attn(v_fmt=7)) == fa4.FA4_ERR_UNSUPPORTED
+    assert call(_attn(**v4, bitmap=256, q_bf16=256, k_bf16=256, v_bf16=256)) == fa4.FA4_ERR_UNSUPPORTED
+    assert call(_attn(**v4, fmt=fa4.FA4_NVFP4, q_tscale=256, k_tscale=256)) == fa4.FA4_ERR_UNSUPPORTED
+    assert call(_attn(**{**v4, "v_block_scales": None})) == fa4.FA4_ERR_NULL
+    assert call(_attn(**{**v4, "v_block_scales": 260})) == fa4.FA4_ERR_ALIGN
+    assert call(_attn(**v4, Lq=0)) == fa4.FA4_OK
 
 
 def test_select_rejects_before_launch():

@@ -24,7 +24,9 @@ def fa4():
 def _run(fa4, cfg, seed=0, select=None):
     q, k, v = W.prefill_inputs(cfg, seed)
     fmt = {"mxfp4": fa4.FA4_MXFP4, "nvfp4": fa4.FA4_NVFP4, "mxfp8": fa4.FA4_MXFP8}[cfg.qk_fmt]
-    res = fa4.prefill(q.cuda(), k.cuda(), v.cuda(), cfg.causal, fmt=fmt, hadamard=cfg.hadamard, select=select)
+    vf = fa4.FA4_MXFP4_KEYS if cfg.v_fmt == "mxfp4k" else fa4.FA4_FP8_TOKEN
+    res = fa4.prefill(q.cuda(), k.cuda(), v.cuda(), cfg.causal, fmt=fmt, hadamard=cfg.hadamard, select=select,
+                      v_fmt=vf)
     torch.cuda.synchronize()
     return (q, k, v), res
 
@@ -139,3 +141,19 @@ def test_full_size_chunked_prefill_128k(fa4):
 
 def test_full_size_prefill_4k_mxfp8(fa4):
     _sampled(fa4, W.C1_MX8, heads=[(0, 0), (0, 17)], nrows=96)
+
+
+
+# ---- 4-bit V (MXFP4 along the keys; FP4 V^T x FP8 P^T in one block-scaled MFMA)
+
+def test_v4_causal_small(fa4):
+    _check_full(fa4, W.C1_V4.scaled(Hq=2, Hkv=2, Lq=512, Lk=512))
+
+
+def test_v4_noncausal_gqa_offset(fa4):
+    _check_full(fa4, W.C1_V4.scaled(Hq=4, Hkv=2, Lq=256, Lk=768, causal=False))
+    _check_full(fa4, W.C1_V4.scaled(Hq=4, Hkv=2, Lq=256, Lk=768), seed=1)
+
+
+def test_full_size_prefill_4k_v4(fa4):
+    _sampled(fa4, W.C1_V4, heads=[(0, 0), (0, 21)], nrows=96)

@@ -192,3 +192,31 @@ def test_paged_kv_cache(fa4, base):
             phys = lay.page_table[b].numpy()[c // 64]
             assert np.array_equal(_np(out["codes"])[phys, :, c % 64], rc[phys, :, c % 64])
             assert np.array_equal(_np(out["block_scales"])[phys, :, c % 64], rs[phys, :, c % 64])
+
+
+
+def _keys_layout(codes):
+    """The attention's storage order of MXFP4_KEYS codes: within each 32-value block, position j holds
+    value 8 ((j >> 2) & 3) + 4 (j >> 4) + (j & 3) (nibbles repacked two per byte, low first)."""
+    c = np.stack([codes & 15, codes >> 4], axis=-1).reshape(codes.shape[:-1] + (-1, 32))
+    j = np.arange(32)
+    perm = 8 * ((j >> 2) & 3) + 4 * (j >> 4) + (j & 3)
+    c = c[..., perm].reshape(codes.shape[:-1] + (-1, 2))
+    return (c[..., 0] | (c[..., 1] << 4)).astype(np.uint8)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mxfp4_keys_codes_and_scales(fa4, d, dtype):
+    """4-bit V: MXFP4 blocks along the rows of each column, bit for bit, in the attention's key order."""
+    x = np.concatenate([_special_rows(d=d, rows=64, seed=8), _special_rows(d=d, rows=64, seed=9),
+                        np.random.default_rng(3).standard_normal((128, d)).astype(np.float32)])
+    x = np.ascontiguousarray(x.reshape(1, 2, 128, d))
+    t = torch.from_numpy(x)
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    out = fa4.quantize(t.cuda(), fa4.FA4_MXFP4_KEYS)
+    codes, scales = Q.mxfp4_keys_quantize(t.float().numpy().astype(np.float64))
+    assert out["codes"].shape == (1, 2, d, 64) and out["block_scales"].shape == (1, 2, d, 4)
+    assert np.array_equal(_np(out["block_scales"]), scales)
+    assert np.array_equal(_np(out["codes"]), _keys_layout(codes))
