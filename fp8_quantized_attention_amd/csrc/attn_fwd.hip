@@ -32,6 +32,7 @@ constexpr int K4_RS = 80;     // LDS row stride (bytes) of 4-bit K codes (64 B +
 constexpr int V8_RS = 144;    // LDS row stride of FP8 V rows (128 B + pad)
 constexpr int H16_RS = 272;   // LDS row stride of 16-bit rows (256 B + pad)
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LOG2_448 = 8.807354922057604f;   // 4-bit V: 448 P' = 2^(x - r + log2 448)
 constexpr float ACC_HEADROOM = 32.0f;   // largest tile weight 2^k allowed before the reference is raised
 
 struct AttnArgs {
@@ -253,9 +254,15 @@ __device__ __forceinline__ void fp8_block(const v16f &Skb, int kb, const float *
     float pw[4];
 #pragma unroll
     for (int u = 0; u < 4; u++) {
-      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(Skb[4 * a4 + u], cs, -rr0));
-      ts += p;
-      pw[u] = p * wv[u];
+      if (V4) {   // 448 P' straight from the exponent (log2 448 folded into the reference); ts sums 448 P'
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(Skb[4 * a4 + u], cs, -rr0 + LOG2_448));
+        ts += p;
+        pw[u] = p;
+      } else {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(Skb[4 * a4 + u], cs, -rr0));
+        ts += p;
+        pw[u] = p * wv[u];
+      }
     }
     // the first conversion keeps the register's high half, which the second one then writes:
     // starting from the bits of its own (dead) first input avoids materializing a zero
@@ -415,7 +422,8 @@ __device__ __forceinline__ void tile_step(const AttnArgs &a, const LaneOff &lo, 
     else
       pv_fp8<D, QF>(pop, vq, lo, v_tile_scale_code(a.vfs, bhk, nk, kt), kBc, acc);
   }
-  lsum += __builtin_ldexpf((ts[0] + ts[1]) + (ts[2] + ts[3]), kB);
+  const float tsum = (ts[0] + ts[1]) + (ts[2] + ts[3]);
+  lsum += __builtin_ldexpf(V4 && !sel ? tsum * (1.0f / 448.0f) : tsum, kB);   // 4-bit V: ts summed 448 P'
 }
 
 template <int D, int QF, bool CAUSAL, bool SEL, bool V4 = false>
