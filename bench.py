@@ -268,7 +268,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-p4", action="store_true", help="skip the decode steps with NVFP4 probabilities")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=8)
+    ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--outlier", action="store_true", help="also time the outlier-aware key quantization")
     ap.add_argument("--summarize-counters", metavar="DIR")
