@@ -10,4 +10,4 @@ invariants and a pure-Python brute force.
 Parity status: every function here has at least one independent pin (see
 tests/test_*_oracle.py); no function is parity-unpinned.
 """
-from . import attention, decode, formats, quant, selection  # noqa: F401
+from . import attention, decode, formats, outlier, quant, selection  # noqa: F401
