@@ -501,7 +501,8 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_split_kernel(DecArgs a) {
 }
 
 // Merge the splits of each (sequence, head): O = sum e^(m_s - m) O_s / sum e^(m_s - m) l_s, times
-// the V tensor scale and P^'s factor (1/448 for FP8 probabilities, s_t for NVFP4 ones). A split's (m, l) are read by all threads of
+// the V tensor scale and P^'s factor (1/448 for FP8 probabilities, s_t for NVFP4 ones); a sequence
+// with no key (ctx_len <= 0) gets O = 0. A split's (m, l) are read by all threads of
 // the block alike; the loop is unrolled so that the loads of several splits are in flight at once.
 __global__ void __launch_bounds__(128) decode_combine_kernel(DecArgs a) {
   __shared__ float red[2];
@@ -525,7 +526,7 @@ __global__ void __launch_bounds__(128) decode_combine_kernel(DecArgs a) {
     o += f * p[2 + d];
   }
   const float vts = (a.vt ? a.vt[(int64_t)b * a.Hkv + kvh] : 1.0f) * a.pscale;
-  a.o[((int64_t)b * a.Hq + h) * 128 + d] = o / l * vts;
+  a.o[((int64_t)b * a.Hq + h) * 128 + d] = ns > 0 ? o / l * vts : 0.0f;   // an empty context gives zeros
 }
 
 static DecArgs make_dec(const fa4_decode_args *p, void *ws) {

@@ -296,7 +296,7 @@ __global__ void __launch_bounds__(256) decode_mla_combine_kernel(MlaArgs a) {
     o1 += f * p[2 + 256 + tid];
   }
   float *o = a.o + ((int64_t)b * MLA_H + h) * MLA_DV;
-  const float r = 1.0f / (448.0f * l);
+  const float r = ns > 0 ? 1.0f / (448.0f * l) : 0.0f;      // an empty context (ctx_len <= 0) gives zeros
   o[tid] = o0 * r;
   o[tid + 256] = o1 * r;
 }

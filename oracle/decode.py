@@ -67,10 +67,13 @@ def decode_one(q_hat, k_hat, v_hat, scale, chunk=None, round_p=True, p_fmt="fp8"
     length (multiple of the tile) whose partial results (m, l, O) are merged afterwards; the merged
     result equals the single pass. p_fmt: "fp8" (P^ = E4M3(448 P')) or "nvfp4" (quantize_p_nvfp4).
     tile: keys per probability tile (128; one 64-key page for the MLA geometry).
+    An empty context (L = 0) has no softmax; its output is defined as zero (the pages do not cover it).
     pow2_ref: the tile reference is a power of two instead of the tile maximum (the prefill's rule,
     "MpFA QK4V8" section 3.3 per-tile P scaling): with x = S log2(e), r = ceil(max x), P' = 2^(x - r)
     (largest value in (1/2, 1]) and the tiles merge with exact weights 2^(r_j - max_j r_j)."""
     L = k_hat.shape[0]
+    if L == 0:
+        return np.zeros(v_hat.shape[1])   # no cached token: the softmax is empty and O is defined as 0
     if chunk is None:
         chunk = max(L, 1)
     assert chunk % tile == 0 or chunk >= L
@@ -137,6 +140,8 @@ def decode_paged(q1, q2, k_pages, v_pages, k_tscale, v_tscale, page_table, ctx_l
     for (b, h) in pairs:
         kv = h // group
         L = int(ctx_len[b])
+        if L <= 0:
+            continue                                  # empty context: O stays zero (decode_one)
         if (b, kv) not in cache:
             kc = gather_pages(k_pages[0], page_table[b], L, page_size, kv)
             ks = gather_pages(k_pages[1], page_table[b], L, page_size, kv)
@@ -187,6 +192,8 @@ def decode_mla(q1, q2, codes, scales, page_table, ctx_len, Hq, d_v, scale, page_
     pairs = [(b, h) for b in range(B) for h in range(Hq)] if pairs is None else pairs
     rows = {}
     for (b, h) in pairs:
+        if int(ctx_len[b]) <= 0:
+            continue                                  # empty context: O stays zero (decode_one)
         if b not in rows:
             k_hat = mxfp4_dequantize(*gather_mla_rows(codes, scales, page_table[b], int(ctx_len[b]), page_size))
             rows = {b: k_hat}

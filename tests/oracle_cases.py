@@ -106,6 +106,8 @@ def decode_cache(cfg, layout, seed, pairs_only=None):
     logical = {}
     for b in range(cfg.B):
         L = int(layout.ctx_len[b])
+        if L <= 0:
+            continue
         c = np.arange(L)
         phys = layout.page_table[b].numpy()[c // ps]
         for h in range(cfg.Hkv):
@@ -141,6 +143,9 @@ def decode_reference(cfg, seed, layout, pairs, logical, q1, q2, scale=None):
     group = cfg.Hq // cfg.Hkv
     out = []
     for (b, h) in pairs:
+        if int(layout.ctx_len[b]) <= 0:
+            out.append(np.zeros(cfg.d, np.float32))      # empty context (decode_one)
+            continue
         kh = logical[(W.T_K, b, h // group)]
         vh = logical[(W.T_V, b, h // group)]
         out.append(Dd.decode_one(qhat[b, h], kh, vh, scale, p_fmt=cfg.p_fmt).astype(np.float32))
@@ -157,6 +162,8 @@ def mla_cache(cfg, layout, seed, seqs=None):
     rows = {}
     for b in (range(cfg.B) if seqs is None else seqs):
         L = int(layout.ctx_len[b])
+        if L <= 0:
+            continue
         x = W.decode_kv_head(cfg, W.T_K, b, 0, L, seed).double().numpy()
         qc, qs = Q.mxfp4_quantize(x)
         c = np.arange(L)

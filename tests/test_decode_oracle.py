@@ -217,3 +217,19 @@ def test_p_nvfp4_split_merge_and_error(fmt):
     e4 = np.linalg.norm(one - exact) / np.linalg.norm(exact)
     e8 = np.linalg.norm(fp8 - exact) / np.linalg.norm(exact)
     assert e8 < e4 < 0.15          # FP4 probabilities: about 9% here, FP8 about 2%
+
+
+@FMTS
+def test_empty_context_is_zero_and_leaves_others(fmt):
+    """A sequence with no cached token has an empty softmax; its output is defined as zero, and the
+    other sequences' outputs do not change (their pages and query rows are untouched)."""
+    cfg = SMALL
+    lay, kp, vp, kt, vt, q, q1, q2, logical = build_cache(cfg, fmt=fmt)
+    pt, ctx = lay.page_table.numpy(), lay.ctx_len.numpy()
+    full = Dd.decode_paged(q1, q2, kp, vp, kt, vt, pt, ctx, cfg.Hq, cfg.Hkv, fmt=fmt)
+    ctx0 = ctx.copy(); ctx0[1] = 0
+    pt0 = pt.copy(); pt0[1] = -1
+    some = Dd.decode_paged(q1, q2, kp, vp, kt, vt, pt0, ctx0, cfg.Hq, cfg.Hkv, fmt=fmt)
+    assert not some[1].any()
+    assert np.array_equal(some[[0, 2]], full[[0, 2]])
+    assert not Dd.decode_one(np.ones(cfg.d), np.zeros((0, cfg.d)), np.zeros((0, cfg.d)), 0.1).any()

@@ -48,6 +48,28 @@ def test_decode_small_all_pairs(fa4, ctx, base):
     assert_parity(np.stack([o[b, h] for b, h in pairs]), ref, f"decode ctx {ctx}")
 
 
+def with_empty(lay, seqs):
+    """The layout with the listed sequences emptied (context 0, no pages)."""
+    ctx, pt = lay.ctx_len.clone(), lay.page_table.clone()
+    ctx[list(seqs)] = 0
+    pt[list(seqs)] = -1
+    return W.DecodeLayout(ctx, pt, lay.num_pages, lay.max_pages)
+
+
+@FMTS
+def test_decode_empty_sequences(fa4, base):
+    """Sequences with no cached token get O = 0; the others are unaffected."""
+    cfg = base.scaled(B=5, Hq=8, Hkv=2, ctx_lo=100, ctx_hi=900)
+    lay = with_empty(W.decode_layout(cfg), [0, 3])
+    o, _ = _gpu_decode(fa4, cfg, lay)
+    assert not o[[0, 3]].any()
+    _, _, _, _, logical = decode_cache(cfg, lay, 0)
+    q, (q1, q2) = decode_query_quant(cfg, 0)
+    pairs = [(b, h) for b in (1, 2, 4) for h in range(cfg.Hq)]
+    ref = decode_reference(cfg, 0, lay, pairs, logical, q1, q2)
+    assert_parity(np.stack([o[b, h] for b, h in pairs]), ref, "decode with empty sequences")
+
+
 @FMTS
 def test_decode_deterministic(fa4, base):
     cfg = base.scaled(B=4, Hq=8, Hkv=2, ctx_lo=1000, ctx_hi=3000)

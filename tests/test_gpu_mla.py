@@ -34,8 +34,13 @@ def _gpu(fa4, cfg, lay, seed=0):
     return o.cpu().numpy(), cache, qq
 
 
-def _check(fa4, cfg, pairs=None, seed=0):
+def _check(fa4, cfg, pairs=None, seed=0, empty=()):
     lay = W.decode_layout(cfg, seed)
+    if empty:                                            # emptied sequences: context 0, no pages
+        ctx, pt = lay.ctx_len.clone(), lay.page_table.clone()
+        ctx[list(empty)] = 0
+        pt[list(empty)] = -1
+        lay = W.DecodeLayout(ctx, pt, lay.num_pages, lay.max_pages)
     print(f"[mla] B={cfg.B} ctx={lay.ctx_len.tolist()[:8]}", flush=True)
     o, cache, qq = _gpu(fa4, cfg, lay, seed)
     seqs = sorted({b for b, _ in pairs}) if pairs else None
@@ -59,12 +64,19 @@ def _check(fa4, cfg, pairs=None, seed=0):
                         cfg.softmax_scale, pairs=pairs)
     assert_parity(np.stack([o[b, h] for b, h in pairs]), np.stack([ref[b, h] for b, h in pairs]),
                   f"mla B={cfg.B}")
+    for b in empty:
+        assert not o[b].any()
 
 
 @pytest.mark.parametrize("ctx", [(150, 700), (1, 70), (64, 64), (2047, 2113)])
 def test_mla_small_all_pairs(fa4, ctx):
     """Ragged last pages, one-key and one-page contexts, and contexts across the 32-page split."""
     _check(fa4, W.C5_MLA.scaled(B=4, ctx_lo=ctx[0], ctx_hi=ctx[1]))
+
+
+def test_mla_empty_sequences(fa4):
+    """Sequences with no cached token get O = 0; the others are unaffected."""
+    _check(fa4, W.C5_MLA.scaled(B=4, ctx_lo=100, ctx_hi=2200), empty=(1, 2))
 
 
 def test_mla_deterministic(fa4):

@@ -96,3 +96,15 @@ def test_bruteforce_mla_row():
     V = [k[:cfg.d_v] for k in K]
     ref = bf.decode_row(qv, K, V, cfg.softmax_scale, tile=64, pow2_ref=True)
     assert np.abs(O[0, 3] - np.array(ref)).max() <= 1e-6 * np.abs(ref).max()
+
+
+def test_empty_context_is_zero_and_leaves_others():
+    cfg = SMALL
+    lay, codes, scales, rows, q, q1, q2 = build_mla(cfg)
+    pt, ctx = lay.page_table.numpy(), lay.ctx_len.numpy()
+    full = Dd.decode_mla(q1, q2, codes, scales, pt, ctx, cfg.Hq, cfg.d_v, cfg.softmax_scale)
+    ctx0 = ctx.copy(); ctx0[0] = 0
+    pt0 = pt.copy(); pt0[0] = -1
+    some = Dd.decode_mla(q1, q2, codes, scales, pt0, ctx0, cfg.Hq, cfg.d_v, cfg.softmax_scale)
+    assert not some[0].any()
+    assert np.array_equal(some[1], full[1])
