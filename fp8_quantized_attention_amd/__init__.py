@@ -24,7 +24,7 @@ FA4_MXFP4, FA4_NVFP4, FA4_FP8_TOKEN, FA4_MXFP8, FA4_MXFP4_KEYS = 0, 1, 2, 3, 4
 FA4_HADAMARD128, FA4_DUAL_RESIDUAL, FA4_SCALE_SEARCH = 1, 2, 4
 FA4_P_FP8, FA4_P_NVFP4 = 0, 1                      # decode probability formats
 
-EXPORTS = ["fa4_quantize_blockscaled", "fa4_smoothing_factors", "fa4_select_tiles", "fa4_attn_fwd", "fa4_decode_workspace_bytes",
+EXPORTS = ["fa4_quantize_blockscaled", "fa4_quantize_prefill", "fa4_smoothing_factors", "fa4_select_tiles", "fa4_attn_fwd", "fa4_decode_workspace_bytes",
            "fa4_decode_paged", "fa4_status_string", "fa4_last_error"]
 
 _p = ctypes.c_void_p
@@ -64,6 +64,8 @@ class DecodeArgs(ctypes.Structure):
 lib.fa4_quantize_blockscaled.argtypes = [ctypes.POINTER(QInput), _u32, ctypes.POINTER(QOutput),
                                          ctypes.POINTER(QOutput), _p, _p]
 lib.fa4_quantize_blockscaled.restype = ctypes.c_int
+lib.fa4_quantize_prefill.argtypes = [ctypes.POINTER(QInput)] * 3 + [ctypes.POINTER(QOutput)] * 3 + [_p, _p, _p]
+lib.fa4_quantize_prefill.restype = ctypes.c_int
 lib.fa4_smoothing_factors.argtypes = [ctypes.POINTER(QInput), ctypes.POINTER(QInput), _p, _p, _p]
 lib.fa4_smoothing_factors.restype = ctypes.c_int
 lib.fa4_select_tiles.argtypes = [_p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p]
@@ -110,17 +112,8 @@ def _dtype_code(t):
 
 # ---------------------------------------------------------------------------------------------------- quantize
 
-def quantize(x, fmt, hadamard=False, dual=False, row_norms=False, fold=None, channel_scale=None, search=False):
-    """Quantize a [outer, heads, rows, d] tensor (float32 or bf16, contiguous on the GPU).
-
-    Returns a dict: codes [outer, heads, rows, d/2 or d] uint8, block_scales (MXFP4: d/32, NVFP4: d/16
-    per row), scales (NVFP4: [outer*heads] tensor scales; FP8: per-row), and with dual=True the
-    residual's 'codes2', 'block_scales2', 'scales2'; with row_norms=True 'norm2' [outer, heads, rows];
-    FP8 per-token output also carries the attention fold data 'fold_w' [outer, heads, rows] and
-    'fold_scale' [outer, heads, rows/128] (default: when rows is a multiple of 128).
-    channel_scale: optional [heads, d] float32 static smoothing factors (see smoothing_factors());
-    search: the per-block scale search (MXFP4 / NVFP4).
-    """
+def _quant_buffers(x, fmt, dual=False, row_norms=False, fold=None, channel_scale=None):
+    """Output tensors and the (input, output, residual) ABI descriptors of one quantization."""
     assert x.is_cuda and x.is_contiguous() and x.dim() == 4
     O, H, R, d = x.shape
     dev = x.device
@@ -160,12 +153,40 @@ def quantize(x, fmt, hadamard=False, dual=False, row_norms=False, fold=None, cha
                       None, None)
     if row_norms:
         out["norm2"] = torch.empty(O, H, R, dtype=torch.float32, device=dev)
+    return out, qin, qout, res
+
+
+def quantize(x, fmt, hadamard=False, dual=False, row_norms=False, fold=None, channel_scale=None, search=False):
+    """Quantize a [outer, heads, rows, d] tensor (float32 or bf16, contiguous on the GPU).
+
+    Returns a dict: codes [outer, heads, rows, d/2 or d] uint8, block_scales (MXFP4: d/32, NVFP4: d/16
+    per row), scales (NVFP4: [outer*heads] tensor scales; FP8: per-row), and with dual=True the
+    residual's 'codes2', 'block_scales2', 'scales2'; with row_norms=True 'norm2' [outer, heads, rows];
+    FP8 per-token output also carries the attention fold data 'fold_w' [outer, heads, rows] and
+    'fold_scale' [outer, heads, rows/128] (default: when rows is a multiple of 128).
+    channel_scale: optional [heads, d] float32 static smoothing factors (see smoothing_factors());
+    search: the per-block scale search (MXFP4 / NVFP4).
+    """
+    out, qin, qout, res = _quant_buffers(x, fmt, dual, row_norms, fold, channel_scale)
     flags = (FA4_HADAMARD128 if hadamard else 0) | (FA4_DUAL_RESIDUAL if dual else 0) | \
         (FA4_SCALE_SEARCH if search else 0)
     _check(lib.fa4_quantize_blockscaled(ctypes.byref(qin), flags, ctypes.byref(qout),
                                         ctypes.byref(res) if res is not None else None,
                                         _ptr(out.get("norm2")), _stream()), "fa4_quantize_blockscaled")
     return out
+
+
+def quantize_prefill(q, k, v, fmt=FA4_MXFP4, row_norms=False):
+    """Q and K (MXFP4 or MXFP8, optional row norms) and V (FP8 per token with its fold data) of a
+    prefill in one launch (fa4_quantize_prefill). Returns three dicts laid out as quantize() returns
+    them; the values are the same bit for bit."""
+    bufs = [_quant_buffers(q, fmt, row_norms=row_norms), _quant_buffers(k, fmt, row_norms=row_norms),
+            _quant_buffers(v, FA4_FP8_TOKEN, fold=True)]
+    (qo, qi, qd, _), (ko, ki, kd, _), (vo, vi, vd, _) = bufs
+    _check(lib.fa4_quantize_prefill(ctypes.byref(qi), ctypes.byref(ki), ctypes.byref(vi), ctypes.byref(qd),
+                                    ctypes.byref(kd), ctypes.byref(vd), _ptr(qo.get("norm2")), _ptr(ko.get("norm2")),
+                                    _stream()), "fa4_quantize_prefill")
+    return qo, ko, vo
 
 
 def quantize_paged(x, fmt, ctx_len, page_table, num_pages, page_size=64, channel_scale=None, search=False):
@@ -395,9 +416,12 @@ def prefill(q, k, v, causal, fmt=FA4_MXFP4, hadamard=False, select=None, softmax
     Hkv, Lk = k.shape[1], k.shape[2]
     sel = select is not None
     qs, ks = smooth if smooth is not None else (None, None)
-    qq = quantize(q, fmt, hadamard=hadamard, row_norms=sel, channel_scale=qs)
-    kq = quantize(k, fmt, hadamard=hadamard, row_norms=sel, channel_scale=ks, search=search)
-    vq = quantize(v, v_fmt)
+    if fmt in (FA4_MXFP4, FA4_MXFP8) and not hadamard and smooth is None and not search and v_fmt == FA4_FP8_TOKEN:
+        qq, kq, vq = quantize_prefill(q, k, v, fmt, row_norms=sel)        # one launch for all three
+    else:
+        qq = quantize(q, fmt, hadamard=hadamard, row_norms=sel, channel_scale=qs)
+        kq = quantize(k, fmt, hadamard=hadamard, row_norms=sel, channel_scale=ks, search=search)
+        vq = quantize(v, v_fmt)
     bitmap = counts = None
     if sel:
         bitmap, counts = select_tiles(qq["norm2"], kq["norm2"], causal, select[0], select[1])
@@ -502,6 +526,8 @@ class PrefillRunner:
         self._qo = [qout(fmt, self.qq), qout(fmt, self.kq), qout(FA4_MXFP4_KEYS if v4 else FA4_FP8_TOKEN, self.vq)]
         self._norms = [_ptr(self.qq["norm2"]), _ptr(self.kq["norm2"]), None]
         self._fl = [self.flags, self.flags | (FA4_SCALE_SEARCH if search else 0), 0]
+        # MXFP4 / MXFP8 Q and K with FP8 V and no rotation or search: one launch for all three
+        self.fused = fmt in (FA4_MXFP4, FA4_MXFP8) and self.flags == 0 and not search and not v4
         if softmax_scale is None:
             softmax_scale = 1.0 / math.sqrt(d)
         self._attn = AttnArgs(fmt, self.qq["codes"].data_ptr(), self.qq["block_scales"].data_ptr(),
@@ -518,9 +544,16 @@ class PrefillRunner:
 
     def quantize(self, stream=None):
         s = _stream() if stream is None else stream
-        for i in range(3):
-            _check(lib.fa4_quantize_blockscaled(ctypes.byref(self._qi[i]), self._fl[i], ctypes.byref(self._qo[i]),
-                                                None, self._norms[i], s), "fa4_quantize_blockscaled")
+        if self.fused:
+            qi, qo = self._qi, self._qo
+            _check(lib.fa4_quantize_prefill(ctypes.byref(qi[0]), ctypes.byref(qi[1]), ctypes.byref(qi[2]),
+                                            ctypes.byref(qo[0]), ctypes.byref(qo[1]), ctypes.byref(qo[2]),
+                                            self._norms[0], self._norms[1], s), "fa4_quantize_prefill")
+        else:
+            for i in range(3):
+                _check(lib.fa4_quantize_blockscaled(ctypes.byref(self._qi[i]), self._fl[i],
+                                                    ctypes.byref(self._qo[i]), None, self._norms[i], s),
+                       "fa4_quantize_blockscaled")
         if self.sel:
             B, Hq, Hkv, Lq, Lk, d = self.shape
             _check(lib.fa4_select_tiles(self.qq["norm2"].data_ptr(), self.kq["norm2"].data_ptr(), B, Hq, Hkv, Lq, Lk,

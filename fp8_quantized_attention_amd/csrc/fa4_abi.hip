@@ -59,8 +59,14 @@ const char *fa4_status_string(int s) {
 
 const char *fa4_last_error(void) { return g_last_error.c_str(); }
 
-fa4_status fa4_quantize_blockscaled(const fa4_qinput *in, uint32_t flags, const fa4_qoutput *out,
-                                    const fa4_qoutput *residual, float *row_norm2, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// The checks of one quantization; *empty is set when there is nothing to enqueue.
+fa4_status check_quantize(const fa4_qinput *in, uint32_t flags, const fa4_qoutput *out, const fa4_qoutput *residual,
+                          float *row_norm2, bool *empty) {
+  *empty = false;
   REQUIRE(in && out, FA4_ERR_NULL, "quantize: input or output descriptor is NULL");
   REQUIRE(in->dtype == FA4_F32 || in->dtype == FA4_BF16, FA4_ERR_UNSUPPORTED, "quantize: dtype %d", in->dtype);
   REQUIRE(in->d == 64 || in->d == 128, FA4_ERR_UNSUPPORTED, "quantize: d=%d (64 or 128)", in->d);
@@ -89,7 +95,10 @@ fa4_status fa4_quantize_blockscaled(const fa4_qinput *in, uint32_t flags, const 
   const int64_t groups = in->outer * in->heads;
   REQUIRE(groups <= 65535, FA4_ERR_SHAPE, "quantize: %lld groups (at most 65535)", (long long)groups);
   REQUIRE(in->rows <= (int64_t)1 << 31, FA4_ERR_SHAPE, "quantize: rows=%lld", (long long)in->rows);
-  if (groups == 0 || (in->rows == 0 && out->fmt != FA4_NVFP4)) return ok();
+  if (groups == 0 || (in->rows == 0 && out->fmt != FA4_NVFP4)) {
+    *empty = true;
+    return ok();
+  }
   REQUIRE(in->rows == 0 || in->x, FA4_ERR_NULL, "quantize: x is NULL");
   REQUIRE(out->codes || in->rows == 0, FA4_ERR_NULL, "quantize: codes is NULL");
   if (out->fmt != FA4_FP8_TOKEN && in->rows > 0)
@@ -134,8 +143,45 @@ fa4_status fa4_quantize_blockscaled(const fa4_qinput *in, uint32_t flags, const 
             "quantize: fold outputs need unpaged, non-ragged rows in multiples of 128");
     REQUIRE(aligned(out->fold_w, 4) && aligned(out->fold_scale, 4), FA4_ERR_ALIGN, "quantize: fold alignment");
   }
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+fa4_status fa4_quantize_blockscaled(const fa4_qinput *in, uint32_t flags, const fa4_qoutput *out,
+                                    const fa4_qoutput *residual, float *row_norm2, void *stream) {
+  bool empty;
+  const fa4_status st = check_quantize(in, flags, out, residual, row_norm2, &empty);
+  if (st != FA4_OK || empty) return st;
   return hip_status(fa4::launch_quantize(in, flags, out, residual, row_norm2, (hipStream_t)stream),
                     "quantize launch");
+}
+
+fa4_status fa4_quantize_prefill(const fa4_qinput *q, const fa4_qinput *k, const fa4_qinput *v,
+                                const fa4_qoutput *q_out, const fa4_qoutput *k_out, const fa4_qoutput *v_out,
+                                float *q_norm2, float *k_norm2, void *stream) {
+  REQUIRE(q && k && v && q_out && k_out && v_out, FA4_ERR_NULL, "quantize_prefill: a descriptor is NULL");
+  REQUIRE((q_out->fmt == FA4_MXFP4 || q_out->fmt == FA4_MXFP8) && k_out->fmt == q_out->fmt, FA4_ERR_UNSUPPORTED,
+          "quantize_prefill: Q and K must both be MXFP4 or both MXFP8 (formats %d, %d)", q_out->fmt, k_out->fmt);
+  REQUIRE(v_out->fmt == FA4_FP8_TOKEN && v_out->fold_w && v_out->fold_scale, FA4_ERR_UNSUPPORTED,
+          "quantize_prefill: V must be FP8 per token with its fold outputs");
+  REQUIRE(q->dtype == k->dtype && k->dtype == v->dtype && q->d == k->d && k->d == v->d, FA4_ERR_UNSUPPORTED,
+          "quantize_prefill: Q, K and V must share dtype and d");
+  REQUIRE(!q->page_table && !k->page_table && !v->page_table && !q->row_counts && !k->row_counts && !v->row_counts,
+          FA4_ERR_UNSUPPORTED, "quantize_prefill: paged or ragged rows need fa4_quantize_blockscaled");
+  REQUIRE((q_norm2 == nullptr) == (k_norm2 == nullptr), FA4_ERR_UNSUPPORTED,
+          "quantize_prefill: row norms of both Q and K, or of neither");
+  bool eq, ek, ev;
+  fa4_status st;
+  if ((st = check_quantize(q, 0, q_out, nullptr, q_norm2, &eq)) != FA4_OK) return st;
+  if ((st = check_quantize(k, 0, k_out, nullptr, k_norm2, &ek)) != FA4_OK) return st;
+  if ((st = check_quantize(v, 0, v_out, nullptr, nullptr, &ev)) != FA4_OK) return st;
+  REQUIRE(fa4::prefill_quant_blocks(q, k, v) < ((int64_t)1 << 31), FA4_ERR_SHAPE, "quantize_prefill: grid too large");
+  if (eq && ek && ev) return ok();
+  return hip_status(fa4::launch_quantize_prefill(q, k, v, q_out, k_out, v_out, q_norm2, k_norm2, (hipStream_t)stream),
+                    "quantize_prefill launch");
 }
 
 fa4_status fa4_select_tiles(const float *q_norm2, const float *k_norm2, int32_t B, int32_t Hq, int32_t Hkv,

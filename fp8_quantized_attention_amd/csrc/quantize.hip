@@ -19,6 +19,7 @@ namespace fa4 {
 
 constexpr int QUANT_THREADS = 256;
 constexpr int QUANT_CHUNK = 64;      // rows per workgroup (one group; NVFP4 maxima reduce per workgroup)
+constexpr int PREFILL_QK_CHUNK = 64; // rows per workgroup of Q and K in the one-launch prefill quantization
 
 // 1/sqrt(128) as the float64 nearest to 1/fl64(sqrt(128)).
 #define FA4_RSQRT128 0x1.6a09e667f3bccp-4
@@ -55,6 +56,27 @@ __device__ __forceinline__ void load_lane(const void *x, int64_t off, float v[E]
   } else {
     const uint4 t = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + off);
     const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      v[2 * i] = bf16_bits_to_float(w[i] & 0xffffu);
+      v[2 * i + 1] = bf16_bits_to_float(w[i] >> 16);
+    }
+  }
+}
+
+// One lane's 16-byte run of a row, as loaded, and its E values widened to float.
+template <int DT>
+__device__ __forceinline__ uint4 load_raw(const void *x, int64_t off) {
+  return DT == 0 ? *reinterpret_cast<const uint4 *>(static_cast<const float *>(x) + off)
+                 : *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(x) + off);
+}
+template <int DT, int E>
+__device__ __forceinline__ void widen_lane(const uint4 t, float v[E]) {
+  const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+  if (DT == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) v[i] = __uint_as_float(w[i]);
+  } else {
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       v[2 * i] = bf16_bits_to_float(w[i] & 0xffffu);
@@ -247,20 +269,41 @@ __device__ __forceinline__ void store_nibbles(uint8_t *p, uint32_t c) {
 // PASS: 0 = group maxima (NVFP4), 1 = codes (+ residual maxima when DUAL), 2 = residual codes.
 // PAGED: rows go to a paged cache through the page table (then NORM is false).
 // SEARCH: the per-block scale search (MXFP4, NVFP4 codes pass; not with DUAL).
-template <int D, int DT, int FMT, int PASS, bool HAD, bool DUAL, bool NORM, bool PAGED, bool SEARCH>
-__global__ void __launch_bounds__(QUANT_THREADS) quantize_kernel(QArgs a) {
+// Fold data of FP8 per-token V for the attention kernel: per 128-row tile a power-of-two scale 2^e,
+// e the smallest integer with 448 * 2^e >= sigma (sigma = max of the tile's row scales), clamped to
+// [-127, 127], and per row w = s * 2^-e (exact). With sigma = M 2^E, M in [1, 2): e = E - 8 when
+// M <= 1.75 (448 * 2^(E-8) = 1.75 * 2^E) and E - 7 otherwise; a subnormal sigma gives -127.
+__device__ __forceinline__ int fold_exponent(float sigma) {
+  const uint32_t b = __float_as_uint(sigma);
+  const int E = (int)((b >> 23) & 0xffu);
+  if (E == 0) return -127;
+  const int e = E - 127 - 8 + ((b & 0x7fffffu) > 0x600000u ? 1 : 0);
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+// 2^e as a float for e in [-127, 127] (2^-127 is the subnormal 0x00400000).
+__device__ __forceinline__ float pow2_float(int e) {
+  return __uint_as_float(e == -127 ? 0x00400000u : (uint32_t)(e + 127) << 23);
+}
+
+// One workgroup's share of a quantization: chunk bx (CHUNK rows) of group g (= o * heads + h).
+// FOLD (FP8_TOKEN, CHUNK = 128, rows in whole 128-row tiles): the chunk is one key tile, and its fold
+// data are formed here from the per-token scales just computed: e = fold_exponent(max of the tile's
+// scales), w_c = s_c 2^-e and the tile scale 2^e.
+template <int D, int DT, int FMT, int PASS, bool HAD, bool DUAL, bool NORM, bool PAGED, bool SEARCH,
+          int CHUNK = QUANT_CHUNK, bool FOLD = false>
+__device__ __forceinline__ void quantize_rows(const QArgs &a, int64_t bx, int g) {
+  static_assert(!FOLD || (FMT == FA4_FP8_TOKEN && CHUNK == 128), "fold data need FP8 per token, 128-row chunks");
   constexpr int E = Epl<DT>::value;       // elements per lane
   constexpr int LPR = D / E;              // lanes per row
   constexpr int RPW = 64 / LPR;           // rows per wave
   constexpr int RPB = RPW * (QUANT_THREADS / 64);
   __shared__ float red[QUANT_THREADS / 64];
 
-  const int g = blockIdx.y;               // group = o * heads + h
   const int64_t o = g / a.heads;
   const int h = g - (int)o * a.heads;
   int64_t nrows = a.rows;
   if (a.row_counts) nrows = min<int64_t>(nrows, (int64_t)a.row_counts[o]);
-  const int64_t r0 = (int64_t)blockIdx.x * QUANT_CHUNK;
+  const int64_t r0 = bx * CHUNK;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane / LPR, li = lane % LPR;
 
@@ -272,10 +315,12 @@ __global__ void __launch_bounds__(QUANT_THREADS) quantize_kernel(QArgs a) {
   float gmax = 0.0f;
 
   // All rows of the chunk are loaded before any is processed, so a wave has its whole share of the
-  // chunk in flight at once. Every lane runs every iteration (rows past the end are inactive and
-  // read nothing), so the lane-group shuffles below always see all their lanes.
-  constexpr int NIT = QUANT_CHUNK / RPB;
-  float vin[NIT][E];
+  // chunk in flight at once; they are held as loaded (16 bytes per row and lane, bf16 still packed)
+  // and widened to float when processed. Every lane runs every iteration (rows past the end are
+  // inactive and read nothing), so the lane-group shuffles below always see all their lanes.
+  constexpr int NIT = CHUNK / RPB;
+  uint4 vin[NIT];
+  float skeep[FOLD ? NIT : 1];            // FOLD: this lane's rows' per-token scales
   // static smoothing: this lane's E channels of head h, multiplied in after the row norms
   float csm[E];
   const bool smooth = a.cscale != nullptr;                // uniform
@@ -286,17 +331,15 @@ __global__ void __launch_bounds__(QUANT_THREADS) quantize_kernel(QArgs a) {
 #pragma unroll
   for (int it = 0; it < NIT; it++) {
     const int64_t rr = r0 + it * RPB + wave * RPW + sub;
-#pragma unroll
-    for (int i = 0; i < E; i++) vin[it][i] = 0.0f;
-    if (rr < nrows) load_lane<DT, E>(a.x, o * a.so + h * a.sh + rr * a.sr + li * E, vin[it]);
+    vin[it] = make_uint4(0u, 0u, 0u, 0u);                 // widens to zeros
+    if (rr < nrows) vin[it] = load_raw<DT>(a.x, o * a.so + h * a.sh + rr * a.sr + li * E);
   }
 #pragma unroll
   for (int it = 0; it < NIT; it++) {
     const int64_t rr = r0 + it * RPB + wave * RPW + sub;
     const bool active = rr < nrows;
     float v[E];
-#pragma unroll
-    for (int i = 0; i < E; i++) v[i] = vin[it][i];
+    widen_lane<DT, E>(vin[it], v);
     // rows are processed by whole lane groups, so inactive lanes only feed zeros to the shuffles
     if (NORM && PASS <= 1) {
       // balanced pairwise tree over the row: in-lane pairs first, then neighbouring lanes
@@ -390,6 +433,7 @@ __global__ void __launch_bounds__(QUANT_THREADS) quantize_kernel(QArgs a) {
     } else if (FMT == FA4_FP8_TOKEN) {
       const float am = group_max(lane_amax<E>(v), LPR);
       const float s = am == 0.0f ? 1.0f : am / 448.0f;
+      if (FOLD) skeep[FOLD ? it : 0] = s;
       float qv[E];
       div_lane<E>(v, s, qv);
       uint32_t c[E / 4];
@@ -445,6 +489,52 @@ __global__ void __launch_bounds__(QUANT_THREADS) quantize_kernel(QArgs a) {
       // non-negative floats order like their bit patterns
       atomicMax(reinterpret_cast<unsigned int *>(dst + g), __float_as_uint(m));
     }
+  }
+  if constexpr (FOLD) {
+    // every lane of a row's lane group holds that row's scale; the tile maximum over all 128 rows
+    float m = skeep[0];
+#pragma unroll
+    for (int i = 1; i < NIT; i++) m = fmaxf(m, skeep[i]);
+    for (int k = 1; k < 64; k <<= 1) m = fmaxf(m, shfl_xor_f(m, k));
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < QUANT_THREADS / 64; w++) m = fmaxf(m, red[w]);
+    const int e = fold_exponent(m);
+#pragma unroll
+    for (int i = 0; i < NIT; i++) {
+      const int64_t rr = r0 + i * RPB + wave * RPW + sub;
+      if (li == 0 && rr < nrows) a.fold_w[(int64_t)g * a.rows + rr] = __builtin_ldexpf(skeep[i], -e);
+    }
+    if (threadIdx.x == 0) a.fold_scale[(int64_t)g * (a.rows / 128) + bx] = pow2_float(e);
+  }
+}
+
+template <int D, int DT, int FMT, int PASS, bool HAD, bool DUAL, bool NORM, bool PAGED, bool SEARCH,
+          int CHUNK = QUANT_CHUNK, bool FOLD = false>
+__global__ void __launch_bounds__(QUANT_THREADS) quantize_kernel(QArgs a) {
+  quantize_rows<D, DT, FMT, PASS, HAD, DUAL, NORM, PAGED, SEARCH, CHUNK, FOLD>(a, blockIdx.x, (int)blockIdx.y);
+}
+
+// The three operands of a prefill in one launch, so that their ramps and tails overlap: workgroups
+// [0, nq) take Q's chunks (MXFP4 or MXFP8), [nq, nq + nk) K's, the rest V's (FP8 per token with the
+// fold data, 128-row chunks). Each block's work is exactly that of the separate calls.
+template <int D, int DT, int QKF, bool NORM>
+__global__ void __launch_bounds__(QUANT_THREADS) prefill_quant_kernel(QArgs q, QArgs k, QArgs v, int64_t qchunks,
+                                                                      int64_t kchunks, int64_t vchunks, int64_t nq,
+                                                                      int64_t nk) {
+  const int64_t blk = blockIdx.x;
+  if (blk < nq) {
+    quantize_rows<D, DT, QKF, 1, false, false, NORM, false, false, PREFILL_QK_CHUNK>(q, blk % qchunks,
+                                                                                     (int)(blk / qchunks));
+  } else if (blk < nq + nk) {
+    const int64_t b = blk - nq;
+    quantize_rows<D, DT, QKF, 1, false, false, NORM, false, false, PREFILL_QK_CHUNK>(k, b % kchunks,
+                                                                                     (int)(b / kchunks));
+  } else {
+    const int64_t b = blk - nq - nk;
+    quantize_rows<D, DT, FA4_FP8_TOKEN, 1, false, false, false, false, false, 128, true>(v, b % vchunks,
+                                                                                       (int)(b / vchunks));
   }
 }
 
@@ -530,38 +620,6 @@ __global__ void __launch_bounds__(QUANT_THREADS) nv_group_kernel(QArgs a) {
   }
 }
 
-// Fold data of FP8 per-token V for the attention kernel: per 128-row tile a power-of-two scale 2^e,
-// e the smallest integer with 448 * 2^e >= sigma (sigma = max of the tile's row scales), clamped to
-// [-127, 127], and per row w = s * 2^-e (exact). With sigma = M 2^E, M in [1, 2): e = E - 8 when
-// M <= 1.75 (448 * 2^(E-8) = 1.75 * 2^E) and E - 7 otherwise; a subnormal sigma gives -127.
-__device__ __forceinline__ int fold_exponent(float sigma) {
-  const uint32_t b = __float_as_uint(sigma);
-  const int E = (int)((b >> 23) & 0xffu);
-  if (E == 0) return -127;
-  const int e = E - 127 - 8 + ((b & 0x7fffffu) > 0x600000u ? 1 : 0);
-  return e < -127 ? -127 : (e > 127 ? 127 : e);
-}
-// 2^e as a float for e in [-127, 127] (2^-127 is the subnormal 0x00400000).
-__device__ __forceinline__ float pow2_float(int e) {
-  return __uint_as_float(e == -127 ? 0x00400000u : (uint32_t)(e + 127) << 23);
-}
-
-__global__ void __launch_bounds__(128) fold_kernel(const float *scales, float *fold_w, float *fold_scale,
-                                                   int64_t rows) {
-  __shared__ float red[2];
-  const int64_t g = blockIdx.y, tile = blockIdx.x;
-  const int t = threadIdx.x;
-  const int64_t row = g * rows + tile * 128 + t;
-  const float sv = scales[row];
-  float m = sv;
-  for (int k = 1; k < 64; k <<= 1) m = fmaxf(m, shfl_xor_f(m, k));
-  if ((t & 63) == 0) red[t >> 6] = m;
-  __syncthreads();
-  const int e = fold_exponent(fmaxf(red[0], red[1]));
-  fold_w[row] = __builtin_ldexpf(sv, -e);
-  if (t == 0) fold_scale[g * (rows / 128) + tile] = pow2_float(e);
-}
-
 __global__ void fill_zero_kernel(float *p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0.0f;
@@ -606,13 +664,17 @@ static hipError_t quantize_dispatch(const QArgs &a, int fmt, bool had, bool dual
     return had ? launch_q<D, DT, FA4_MXFP8, 1, true, false>(a, groups, norm, s)
                : launch_q<D, DT, FA4_MXFP8, 1, false, false>(a, groups, norm, s);
   if (fmt == FA4_FP8_TOKEN) {
-    if ((e = launch_q<D, DT, FA4_FP8_TOKEN, 1, false, false>(a, groups, norm, s)) != hipSuccess) return e;
-    if (a.fold_w && a.rows > 0 && groups > 0) {
-      hipLaunchKernelGGL(fold_kernel, dim3((unsigned)(a.rows / 128), (unsigned)groups), dim3(128), 0, s,
-                         a.scales, a.fold_w, a.fold_scale, a.rows);
-      e = hipGetLastError();
-    }
-    return e;
+    if (!a.fold_w) return launch_q<D, DT, FA4_FP8_TOKEN, 1, false, false>(a, groups, norm, s);
+    if (a.rows == 0 || groups == 0) return hipSuccess;
+    // with fold data: one workgroup per 128-row key tile (rows are whole tiles, unpaged, not ragged)
+    const dim3 grid((unsigned)(a.rows / 128), (unsigned)groups);
+    if (norm)
+      hipLaunchKernelGGL((quantize_kernel<D, DT, FA4_FP8_TOKEN, 1, false, false, true, false, false, 128, true>), grid,
+                         dim3(QUANT_THREADS), 0, s, a);
+    else
+      hipLaunchKernelGGL((quantize_kernel<D, DT, FA4_FP8_TOKEN, 1, false, false, false, false, false, 128, true>), grid,
+                         dim3(QUANT_THREADS), 0, s, a);
+    return hipGetLastError();
   }
   // NVFP4, groups that fit one workgroup: a single launch
   if (!had && !norm && !a.page_table && a.rows <= QUANT_CHUNK) {
@@ -783,8 +845,7 @@ __global__ void __launch_bounds__(128) mx_keys_kernel(QArgs a, int d) {
   a.bscales[row * (a.rows / 32) + r0 / 32] = (uint8_t)(e + 127);
 }
 
-hipError_t launch_quantize(const fa4_qinput *in, uint32_t flags, const fa4_qoutput *out,
-                           const fa4_qoutput *res, float *norm2, hipStream_t s) {
+static QArgs quant_args(const fa4_qinput *in, const fa4_qoutput *out, const fa4_qoutput *res, float *norm2) {
   QArgs a;
   a.x = in->x; a.outer = in->outer; a.rows = in->rows; a.heads = in->heads;
   a.so = in->stride_outer; a.sh = in->stride_head; a.sr = in->stride_row;
@@ -796,6 +857,56 @@ hipError_t launch_quantize(const fa4_qinput *in, uint32_t flags, const fa4_qoutp
   a.norm2 = norm2;
   a.fold_w = out->fold_w; a.fold_scale = out->fold_scale;
   a.cscale = in->channel_scale;
+  return a;
+}
+
+template <int D, int DT>
+static hipError_t launch_prefill_quant(const QArgs &q, const QArgs &k, const QArgs &v, int qkf, bool norm,
+                                       int64_t qch, int64_t kch, int64_t vch, int64_t nq, int64_t nk, int64_t nv,
+                                       hipStream_t s) {
+  const dim3 grid((unsigned)(nq + nk + nv));
+  // chunk counts divide block indices only inside the branch of a tensor that has blocks
+  qch = qch > 0 ? qch : 1; kch = kch > 0 ? kch : 1; vch = vch > 0 ? vch : 1;
+  if (qkf == FA4_MXFP4) {
+    if (norm) hipLaunchKernelGGL((prefill_quant_kernel<D, DT, FA4_MXFP4, true>), grid, dim3(QUANT_THREADS), 0, s, q, k,
+                                 v, qch, kch, vch, nq, nk);
+    else hipLaunchKernelGGL((prefill_quant_kernel<D, DT, FA4_MXFP4, false>), grid, dim3(QUANT_THREADS), 0, s, q, k, v,
+                            qch, kch, vch, nq, nk);
+  } else {
+    if (norm) hipLaunchKernelGGL((prefill_quant_kernel<D, DT, FA4_MXFP8, true>), grid, dim3(QUANT_THREADS), 0, s, q, k,
+                                 v, qch, kch, vch, nq, nk);
+    else hipLaunchKernelGGL((prefill_quant_kernel<D, DT, FA4_MXFP8, false>), grid, dim3(QUANT_THREADS), 0, s, q, k, v,
+                            qch, kch, vch, nq, nk);
+  }
+  return hipGetLastError();
+}
+
+int64_t prefill_quant_blocks(const fa4_qinput *q, const fa4_qinput *k, const fa4_qinput *v) {
+  return (q->rows + PREFILL_QK_CHUNK - 1) / PREFILL_QK_CHUNK * (q->outer * q->heads) +
+         (k->rows + PREFILL_QK_CHUNK - 1) / PREFILL_QK_CHUNK * (k->outer * k->heads) +
+         v->rows / 128 * (v->outer * v->heads);
+}
+
+hipError_t launch_quantize_prefill(const fa4_qinput *q, const fa4_qinput *k, const fa4_qinput *v,
+                                   const fa4_qoutput *qo, const fa4_qoutput *ko, const fa4_qoutput *vo,
+                                   float *q_norm2, float *k_norm2, hipStream_t s) {
+  const QArgs qa = quant_args(q, qo, nullptr, q_norm2), ka = quant_args(k, ko, nullptr, k_norm2),
+              va = quant_args(v, vo, nullptr, nullptr);
+  const int64_t qch = (q->rows + PREFILL_QK_CHUNK - 1) / PREFILL_QK_CHUNK,
+                kch = (k->rows + PREFILL_QK_CHUNK - 1) / PREFILL_QK_CHUNK, vch = v->rows / 128;
+  const int64_t nq = qch * (q->outer * q->heads), nk = kch * (k->outer * k->heads), nv = vch * (v->outer * v->heads);
+  if (nq + nk + nv == 0) return hipSuccess;
+  const bool norm = q_norm2 != nullptr;
+  if (q->d == 128)
+    return q->dtype == FA4_F32 ? launch_prefill_quant<128, 0>(qa, ka, va, qo->fmt, norm, qch, kch, vch, nq, nk, nv, s)
+                               : launch_prefill_quant<128, 1>(qa, ka, va, qo->fmt, norm, qch, kch, vch, nq, nk, nv, s);
+  return q->dtype == FA4_F32 ? launch_prefill_quant<64, 0>(qa, ka, va, qo->fmt, norm, qch, kch, vch, nq, nk, nv, s)
+                             : launch_prefill_quant<64, 1>(qa, ka, va, qo->fmt, norm, qch, kch, vch, nq, nk, nv, s);
+}
+
+hipError_t launch_quantize(const fa4_qinput *in, uint32_t flags, const fa4_qoutput *out,
+                           const fa4_qoutput *res, float *norm2, hipStream_t s) {
+  const QArgs a = quant_args(in, out, res, norm2);
   const int64_t groups = in->outer * in->heads;
   const bool had = flags & FA4_HADAMARD128, dual = flags & FA4_DUAL_RESIDUAL, norm = norm2 != nullptr;
   const bool search = flags & FA4_SCALE_SEARCH;

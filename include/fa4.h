@@ -3,6 +3,7 @@
  *
  * Four entry points make up the path:
  *   fa4_quantize_blockscaled  Q/K -> 4-bit E2M1 with block scales (MXFP4 or NVFP4), V -> FP8 E4M3
+ *                             (fa4_quantize_prefill: Q, K and V of a prefill in one launch)
  *   fa4_select_tiles          ThriftAttention-style choice of the 128x128 tiles computed in bf16
  *   fa4_attn_fwd              fused prefill attention (scaled-MFMA QK^T and PV, FP32 online softmax)
  *   fa4_decode_paged          decode attention over a paged FP4 (NVFP4 or MXFP4) KV cache
@@ -136,6 +137,23 @@ typedef struct {
 
 fa4_status fa4_quantize_blockscaled(const fa4_qinput *in, uint32_t flags, const fa4_qoutput *out,
                                     const fa4_qoutput *residual, float *row_norm2, void *stream);
+
+/* The three quantizations of a prefill in one launch.
+ *
+ * Source pages: "MpFA QK4V8" sections 2.1-2.2 (Q and K in 4 bits, V in 8 bits, quantized before the
+ * attention kernel); "MXFP vs NVFP4" (tqpw.cn 81738) section 3.1 (fused quantization kernels with
+ * coalesced global-memory access).
+ * Writes exactly what three fa4_quantize_blockscaled calls with flags = 0 would write: q and k into
+ * q_out and k_out (both FA4_MXFP4 or both FA4_MXFP8, with row norms into q_norm2 / k_norm2 when both
+ * are given), v into v_out (FA4_FP8_TOKEN with fold_w and fold_scale). Inputs as for
+ * fa4_quantize_blockscaled; q, k and v share dtype and d, are unpaged and not ragged (row_counts NULL),
+ * and v's rows are a multiple of 128. Rotation, the dual residual, the scale search, NVFP4 and 4-bit V
+ * are not offered here (use the separate calls). One launch lets the three streams' start-up and
+ * drain overlap, which matters at a few tens of MB per tensor.
+ */
+fa4_status fa4_quantize_prefill(const fa4_qinput *q, const fa4_qinput *k, const fa4_qinput *v,
+                                const fa4_qoutput *q_out, const fa4_qoutput *k_out, const fa4_qoutput *v_out,
+                                float *q_norm2, float *k_norm2, void *stream);
 
 /* Static smoothing factors for outlier-aware key quantization.
  *

@@ -113,6 +113,32 @@ def test_quantize_rejects_before_launch():
     assert fa4.lib.fa4_last_error() == b""
 
 
+def _call_qp(q=None, k=None, v=None, qf=fa4.FA4_MXFP4, kf=None, vout=None, qn=None, kn=None):
+    q, k, v = q or _q(), k or _q(), v or _q()
+    qo = fa4.QOutput(qf, 256, 256, None)
+    ko = fa4.QOutput(qf if kf is None else kf, 256, 256, None)
+    vo = vout or fa4.QOutput(fa4.FA4_FP8_TOKEN, 256, None, 256, 256, 256)
+    return fa4.lib.fa4_quantize_prefill(*[ctypes.byref(t) for t in (q, k, v, qo, ko, vo)], qn, kn, None)
+
+
+def test_quantize_prefill_rejects_before_launch():
+    assert fa4.lib.fa4_quantize_prefill(None, None, None, None, None, None, None, None, None) == fa4.FA4_ERR_NULL
+    assert _call_qp(qf=fa4.FA4_NVFP4) == fa4.FA4_ERR_UNSUPPORTED                 # Q/K: MXFP4 or MXFP8 only
+    assert _call_qp(kf=fa4.FA4_MXFP8) == fa4.FA4_ERR_UNSUPPORTED                 # Q and K alike
+    assert _call_qp(vout=fa4.QOutput(fa4.FA4_FP8_TOKEN, 256, None, 256)) == fa4.FA4_ERR_UNSUPPORTED   # no fold
+    assert _call_qp(vout=fa4.QOutput(fa4.FA4_MXFP4, 256, 256, None, 256, 256)) == fa4.FA4_ERR_UNSUPPORTED
+    assert _call_qp(k=_q(dtype=fa4.FA4_F32)) == fa4.FA4_ERR_UNSUPPORTED
+    assert _call_qp(v=_q(d=64, stride_row=64)) == fa4.FA4_ERR_UNSUPPORTED
+    assert _call_qp(k=_q(page_table=256, page_size=64, max_pages=4, num_pages=8)) == fa4.FA4_ERR_UNSUPPORTED
+    assert _call_qp(v=_q(row_counts=256)) == fa4.FA4_ERR_UNSUPPORTED
+    assert _call_qp(qn=256) == fa4.FA4_ERR_UNSUPPORTED                           # norms of both or neither
+    assert _call_qp(v=_q(rows=200)) == fa4.FA4_ERR_UNSUPPORTED                   # V rows in whole 128-row tiles
+    assert _call_qp(q=_q(x=None)) == fa4.FA4_ERR_NULL
+    assert _call_qp(k=_q(x=24)) == fa4.FA4_ERR_ALIGN
+    assert _call_qp(q=_q(rows=0), k=_q(rows=0), v=_q(rows=0)) == fa4.FA4_OK      # nothing to do, no launch
+    assert fa4.lib.fa4_last_error() == b""
+
+
 def test_smoothing_rejects_before_launch():
     f = lambda q, k, qs=256, ks=256: fa4.lib.fa4_smoothing_factors(ctypes.byref(q), ctypes.byref(k), qs, ks, None)
     q, k = _q(heads=8), _q(heads=2)

@@ -220,3 +220,43 @@ def test_mxfp4_keys_codes_and_scales(fa4, d, dtype):
     assert out["codes"].shape == (1, 2, d, 64) and out["block_scales"].shape == (1, 2, d, 4)
     assert np.array_equal(_np(out["block_scales"]), scales)
     assert np.array_equal(_np(out["codes"]), _keys_layout(codes))
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("f32", 128), ("bf16", 128)])
+@pytest.mark.parametrize("norms", [False, True])
+def test_prefill_quantize_one_launch(fa4, fmt, dtype, d, norms):
+    """fa4_quantize_prefill: Q and K (a ragged last 64-row chunk in Q) and V with its fold data, all
+    against the oracle bit for bit, and equal to the three separate calls."""
+    g = torch.Generator().manual_seed(21)
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    B, Hq, Hkv, Lq, Lk = 2, 4, 2, 200, 384
+    q = (torch.randn(B, Hq, Lq, d, generator=g) * 2).to(dt)
+    k = torch.randn(B, Hkv, Lk, d, generator=g)
+    k[..., 3] *= 20.0                                   # an outlier channel
+    k = k.to(dt)
+    v = (torch.randn(B, Hkv, Lk, d, generator=g) * torch.rand(B, Hkv, Lk, 1, generator=g) * 8).to(dt)
+    v[0, 1, 130] = 0.0                                  # an all-zero token (scale 1)
+    F = fa4.FA4_MXFP4 if fmt == "mxfp4" else fa4.FA4_MXFP8
+    qq, kq, vq = fa4.quantize_prefill(q.cuda(), k.cuda(), v.cuda(), F, row_norms=norms)
+    torch.cuda.synchronize()
+    quant = Q.mxfp4_quantize if fmt == "mxfp4" else Q.mxfp8_quantize
+    for x, out in ((q, qq), (k, kq)):
+        xf = x.float().numpy().astype(np.float64)
+        codes, sc = quant(xf)
+        assert np.array_equal(_np(out["codes"]), codes)
+        assert np.array_equal(_np(out["block_scales"]), sc)
+        if norms:
+            assert np.array_equal(_np(out["norm2"]), Q.row_norm2(xf))
+    codes, sv = Q.fp8_per_token_quantize(v.float().numpy())
+    assert np.array_equal(_np(vq["codes"]), codes)
+    assert np.array_equal(_np(vq["scales"]), sv)
+    tiles = sv.reshape(B, Hkv, -1, 128).astype(np.float64)
+    e = np.vectorize(_fold_exponent)(tiles.max(axis=-1))
+    assert np.array_equal(_np(vq["fold_scale"]).astype(np.float64), 2.0 ** e)
+    assert np.array_equal(_np(vq["fold_w"]).astype(np.float64), (tiles * 2.0 ** -e[..., None]).reshape(B, Hkv, -1))
+    sep = [fa4.quantize(x.cuda(), F, row_norms=norms) for x in (q, k)] + [fa4.quantize(v.cuda(), fa4.FA4_FP8_TOKEN)]
+    for a, b in zip((qq, kq, vq), sep):
+        for key, t in b.items():
+            if t is not None:
+                assert torch.equal(a[key], t), key
