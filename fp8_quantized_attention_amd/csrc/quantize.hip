@@ -256,7 +256,8 @@ __device__ __forceinline__ uint32_t nv_codes_search(const float v[E], float st, 
 }
 
 __device__ __forceinline__ float tensor_scale_from_max(float amax) {
-  return amax == 0.0f ? 1.0f : amax / 2688.0f;
+  const float t = amax / 2688.0f;          // zero also when the quotient underflows (amax < ~2.7e-42)
+  return t == 0.0f ? 1.0f : t;
 }
 
 // store E/2 bytes of packed 4-bit codes (E = 4: 2 bytes, E = 8: 4 bytes)
@@ -620,6 +621,56 @@ __global__ void __launch_bounds__(QUANT_THREADS) nv_group_kernel(QArgs a) {
   }
 }
 
+// NVFP4 of one-row groups (the decode query: one row per (sequence, head)), unpaged: each row is
+// quantized by its own lane group (D/E lanes), so the tensor maximum and, with DUAL, the residual's
+// maximum are lane-group shuffles with no workgroup barrier. Same arithmetic as nv_group_kernel: the
+// maxima are the same maxima, the codes the same nv_codes.
+template <int D, int DT, bool DUAL, bool SEARCH>
+__global__ void __launch_bounds__(QUANT_THREADS) nv_row_kernel(QArgs a, int64_t groups) {
+  constexpr int E = Epl<DT>::value;
+  constexpr int LPR = D / E;
+  constexpr int RPW = 64 / LPR;
+  constexpr int RPB = RPW * (QUANT_THREADS / 64);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane / LPR, li = lane % LPR;
+  const int64_t g = (int64_t)blockIdx.x * RPB + wave * RPW + sub;
+  const bool live = g < groups;                             // every lane runs the shuffles below
+  const int64_t o = live ? g / a.heads : 0;
+  const int h = live ? (int)(g - o * a.heads) : 0;
+  bool active = live;
+  if (live && a.row_counts) active = a.row_counts[o] >= 1;
+  float v[E];
+  const uint4 raw = active ? load_raw<DT>(a.x, o * a.so + h * a.sh + li * E) : make_uint4(0u, 0u, 0u, 0u);
+  widen_lane<DT, E>(raw, v);
+  if (a.cscale && live) {                                   // static smoothing
+#pragma unroll
+    for (int i = 0; i < E; i++) v[i] *= a.cscale[(int64_t)h * D + li * E + i];
+  }
+  const float st = tensor_scale_from_max(group_max(lane_amax<E>(v), LPR));
+  if (live && li == 0) a.scales[g] = st;
+  uint32_t sb;
+  double xh[E];
+  const uint32_t c = SEARCH ? nv_codes_search<E>(v, st, &sb, xh) : nv_codes<E>(v, st, &sb, xh);
+  if (active) {
+    store_nibbles<E>(a.codes + g * (D / 2) + li * (E / 2), c);
+    if ((li % (16 / E)) == 0) a.bscales[g * (D / 16) + li / (16 / E)] = (uint8_t)sb;
+  }
+  if (DUAL) {
+    float rv[E];
+#pragma unroll
+    for (int i = 0; i < E; i++) rv[i] = (float)((double)v[i] - xh[i]);                // the residual
+    const float rst = tensor_scale_from_max(group_max(active ? lane_amax<E>(rv) : 0.0f, LPR));
+    if (live && li == 0) a.rscales[g] = rst;
+    uint32_t rsb;
+    double rxh[E];
+    const uint32_t rc = nv_codes<E>(rv, rst, &rsb, rxh);
+    if (active) {
+      store_nibbles<E>(a.rcodes + g * (D / 2) + li * (E / 2), rc);
+      if ((li % (16 / E)) == 0) a.rbscales[g * (D / 16) + li / (16 / E)] = (uint8_t)rsb;
+    }
+  }
+}
+
 __global__ void fill_zero_kernel(float *p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0.0f;
@@ -674,6 +725,15 @@ static hipError_t quantize_dispatch(const QArgs &a, int fmt, bool had, bool dual
     else
       hipLaunchKernelGGL((quantize_kernel<D, DT, FA4_FP8_TOKEN, 1, false, false, false, false, false, 128, true>), grid,
                          dim3(QUANT_THREADS), 0, s, a);
+    return hipGetLastError();
+  }
+  // NVFP4, one-row groups: a lane group per row
+  if (!had && !norm && !a.page_table && a.rows == 1) {
+    constexpr int RPB = (64 / (D / Epl<DT>::value)) * (QUANT_THREADS / 64);
+    const dim3 grid((unsigned)((groups + RPB - 1) / RPB));
+    if (dual) hipLaunchKernelGGL((nv_row_kernel<D, DT, true, false>), grid, dim3(QUANT_THREADS), 0, s, a, groups);
+    else if (search) hipLaunchKernelGGL((nv_row_kernel<D, DT, false, true>), grid, dim3(QUANT_THREADS), 0, s, a, groups);
+    else hipLaunchKernelGGL((nv_row_kernel<D, DT, false, false>), grid, dim3(QUANT_THREADS), 0, s, a, groups);
     return hipGetLastError();
   }
   // NVFP4, groups that fit one workgroup: a single launch

@@ -69,7 +69,8 @@ enum { FA4_HADAMARD128 = 1u << 0, FA4_DUAL_RESIDUAL = 1u << 1, FA4_SCALE_SEARCH 
  *              the smallest power of two 2^e with 6 * 2^e >= amax (e = -127 if amax = 0), codes =
  *              E2M1(x * 2^-e) rounded to nearest even. `scales` unused (may be NULL).
  *   FA4_NVFP4: codes [d/2]; block_scales [d/16] E4M3; scales = tensor scale per group [outer*heads]
- *              float: s_t = amax_group / 2688 (1 if zero), s_b = E4M3(amax_block / (6 s_t)),
+ *              float: s_t = amax_group / 2688 (1 if that float32 quotient is zero, i.e. amax = 0 or
+ *              below ~2.7e-42; all block scales are then 0), s_b = E4M3(amax_block / (6 s_t)),
  *              codes = E2M1(x / (E4M3value(s_b) * s_t)) (float32, IEEE division); value = code*s_b*s_t.
  *   FA4_MXFP8: codes [d] E4M3; block_scales [d/32] E8M0: per 32 elements, the smallest power of two
  *              2^e with 448 * 2^e >= amax (e = -127 if amax = 0), codes = E4M3(x * 2^-e) rounded to

@@ -142,7 +142,8 @@ def nvfp4_quantize(x):
 
     Steps (float32 rounding points marked fl32):
       1. amax_t = max |x| over the group; s_t = fl32(amax_t / 2688), 2688 = 6*448;
-         s_t = 1 when amax_t == 0.
+         s_t = 1 when that is zero (amax_t == 0, or so small that the quotient underflows: the
+         tensor then quantizes like an all-zero one, every block scale rounding to zero).
       2. per block of 16 along d: r = fl32(amax_b / fl32(6 * s_t)); block scale
          s_b = E4M3(r) (nearest-even, saturating at 448).
       3. denom = fl32(E4M3value(s_b) * s_t); element code = E2M1(fl32(x / denom)),
@@ -155,7 +156,8 @@ def nvfp4_quantize(x):
     assert d % NV_BLOCK == 0
     x32 = fp32(x)
     amax_t = np.max(np.abs(x32).reshape(G, -1), axis=1).astype(np.float32) if R > 0 else np.zeros(G, np.float32)
-    s_t = np.where(amax_t == 0, np.float32(1.0), amax_t / np.float32(6.0 * E4M3_MAX)).astype(np.float32)
+    s_t = (amax_t / np.float32(6.0 * E4M3_MAX)).astype(np.float32)
+    s_t = np.where(s_t == 0, np.float32(1.0), s_t).astype(np.float32)
     blocks = x32.reshape(G, R, d // NV_BLOCK, NV_BLOCK)
     amax_b = np.max(np.abs(blocks), axis=-1).astype(np.float32)
     six_st = (np.float32(6.0) * s_t).astype(np.float32)

@@ -260,3 +260,28 @@ def test_prefill_quantize_one_launch(fa4, fmt, dtype, d, norms):
         for key, t in b.items():
             if t is not None:
                 assert torch.equal(a[key], t), key
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dual", [False, True])
+def test_nvfp4_one_row_groups(fa4, d, dtype, dual):
+    """NVFP4 of one-row groups (one row per (outer, head), the decode query's shape), with zero, signed-zero,
+    subnormal, huge and tie-laden rows, and a group count that leaves part of the last workgroup idle:
+    tensor scales, block scales and codes of Q1 (and Q2) bit for bit."""
+    rows = _special_rows(d=d, rows=70, seed=5)
+    t = torch.from_numpy(np.ascontiguousarray(rows.reshape(7, 10, 1, d)))
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    out = fa4.quantize(t.cuda(), fa4.FA4_NVFP4, dual=dual)
+    x = t.float().numpy().astype(np.float64).reshape(70, 1, d)
+    if dual:
+        (c1, s1, t1), (c2, s2, t2) = Q.dual_residual_quantize(x)
+        assert np.array_equal(_np(out["scales2"]), t2)
+        assert np.array_equal(_np(out["block_scales2"]).reshape(70, 1, -1), s2)
+        assert np.array_equal(_np(out["codes2"]).reshape(70, 1, -1), c2)
+    else:
+        c1, s1, t1 = Q.nvfp4_quantize(x)
+    assert np.array_equal(_np(out["scales"]), t1)
+    assert np.array_equal(_np(out["block_scales"]).reshape(70, 1, -1), s1)
+    assert np.array_equal(_np(out["codes"]).reshape(70, 1, -1), c1)

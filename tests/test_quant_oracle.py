@@ -190,6 +190,26 @@ def test_zero_and_tiny_blocks_are_defined():
     assert not np.any(np.isnan(Q.mxfp4_dequantize(c, s)))
 
 
+def test_nvfp4_tensor_scale_underflow_is_a_zero_tensor():
+    """When fl32(amax/2688) underflows to zero the tensor quantizes as an all-zero one: s_t = 1, every
+    block scale 0, signed-zero codes. Across tiny magnitudes no block scale is ever an E4M3 NaN code
+    (0x7F / 0xFF) and every dequantized value is finite."""
+    x = np.zeros((1, 1, 32), dtype=np.float32)
+    x[0, 0, :16] = np.float32(1e-42)
+    x[0, 0, 16:] = np.float32(-1e-42)
+    assert np.float32(1e-42) / np.float32(2688) == 0                 # the quotient underflows
+    c, sb, st = Q.nvfp4_quantize(x)
+    assert st[0] == 1.0 and np.all(sb == 0)
+    u = F.unpack_nibbles(c)[0, 0]
+    assert np.all(u[:16] == 0) and np.all(u[16:] == 8)
+    rng = np.random.default_rng(3)
+    for e in range(-160, -118, 2):
+        t = (rng.standard_normal((4, 3, 32)) * 2.0 ** e).astype(np.float32)
+        c, sb, st = Q.nvfp4_quantize(t)
+        assert np.all(st > 0) and not np.any((sb & 0x7F) == 0x7F)
+        assert np.all(np.isfinite(Q.nvfp4_dequantize(c, sb, st)))
+
+
 def test_mx8_exponent_closed_form_vs_definition():
     """e(amax) == the smallest e with 448 * 2^e >= amax, over every float32 exponent and many mantissas."""
     rng = np.random.default_rng(1)
