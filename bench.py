@@ -2,8 +2,9 @@
 """Benchmark of block-scaled low-bit fused attention on one MI355X.
 
 One step = the whole prefill path on the 4K causal workload (B=1, H=32, L=4096, d=128): MXFP4
-quantization of Q and K, FP8 per-token quantization of V (with its P-fold data) and the fused
-attention kernel, inputs resident in HBM. `value` is prefill attention TFLOP/s over the step
+quantization of Q and K and FP8 per-token quantization of V (with its P-fold data), in one launch,
+then the fused attention kernel, inputs resident in HBM. Each timed loop follows W untimed steps and
+at least 0.1 s of untimed back-to-back steps. `value` is prefill attention TFLOP/s over the step
 (algorithmic flops: 4 d per unmasked query-key pair). The same line carries:
   roofline      the attention kernel alone: its algorithmic flops / its average launch time (HIP
                 events on the launch stream) against the dense MXFP4 MFMA peak;
@@ -138,6 +139,22 @@ def prefill_flops(cfg):
     return 4.0 * cfg.d * causal_pairs(cfg.Lq, cfg.Lk, cfg.causal) * cfg.B * cfg.Hq
 
 
+WARM_S = 0.1
+
+
+def _warm(fn, n):
+    """n untimed calls, continued until at least WARM_S seconds of back-to-back work have run, so that
+    the timed loop does not start on clocks still ramping up after the host-side input generation."""
+    for _ in range(n):
+        fn()
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    while time.perf_counter() - t < WARM_S:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+
+
 def _time_loop(fn, n):
     """Average ms of n back-to-back calls of fn, HIP events on the current (launch) stream."""
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -157,8 +174,7 @@ def time_prefill(fa4, cfg, steps, warmup, select):
     fmt = {"mxfp4": fa4.FA4_MXFP4, "nvfp4": fa4.FA4_NVFP4, "mxfp8": fa4.FA4_MXFP8}[cfg.qk_fmt]
     vf = fa4.FA4_MXFP4_KEYS if cfg.v_fmt == "mxfp4k" else fa4.FA4_FP8_TOKEN
     run = fa4.PrefillRunner(q, k, v, cfg.causal, fmt=fmt, hadamard=cfg.hadamard, select=select, v_fmt=vf)
-    for _ in range(warmup):
-        run.run()
+    _warm(run.run, warmup)
     step_ms = _time_loop(run.run, steps)
     attn_ms = _time_loop(run.attention, steps)
     return step_ms, attn_ms
@@ -186,8 +202,7 @@ def time_decode(fa4, cfg, steps, warmup):
     q = W.decode_query(cfg).cuda()
     run = fa4.DecodeRunner(q, caches[0], caches[1], pt, ctx, cfg.Hkv,
                            p_fmt=fa4.FA4_P_NVFP4 if cfg.p_fmt == "nvfp4" else fa4.FA4_P_FP8)
-    for _ in range(warmup):
-        run.run()
+    _warm(run.run, warmup)
     step_ms = _time_loop(run.run, steps)
     kern_ms = _time_loop(run.attention, steps)
     # K and V codes plus block scales (d/16 E4M3 or d/32 E8M0 bytes) per (token, key head)
@@ -206,8 +221,7 @@ def time_decode_mla(fa4, cfg, steps, warmup):
     torch.cuda.empty_cache()
     q = W.decode_query(cfg).cuda()
     run = fa4.DecodeMlaRunner(q, cache, pt, ctx, cfg.softmax_scale)
-    for _ in range(warmup):
-        run.run()
+    _warm(run.run, warmup)
     step_ms = _time_loop(run.run, steps)
     kern_ms = _time_loop(run.attention, steps)
     # one latent row per token: d/2 code bytes + d/32 E8M0 bytes
@@ -230,8 +244,7 @@ def time_k_quant(fa4, steps, warmup):
            "algorithmic_bytes": 2 * in_bytes + out_bytes, "note": "two passes over the input (tensor maximum, codes)"}
     for name, cs, search in (("plain", None, False), ("smoothing", ks, False), ("smoothing+search", ks, True)):
         run = fa4.QuantizeRunner(kc, fa4.FA4_NVFP4, hadamard=True, channel_scale=cs, search=search)
-        for _ in range(warmup):
-            run.run()
+        _warm(run.run, warmup)
         ms = _time_loop(run.run, steps)
         res[name] = {"ms": ms, "GB/s": (2 * in_bytes + out_bytes) / (ms * 1e-3) / 1e9}
         print(f"[bench] k_quant {name}: {ms:.4f} ms", file=sys.stderr, flush=True)
