@@ -35,6 +35,7 @@ constexpr int DEC_THREADS = 256;
 constexpr int DEC_TPW = 4;                        // tiles per wave
 constexpr int DEC_SLOTS = 4 * DEC_TPW;            // tiles per workgroup
 constexpr int DEC_SPLIT = 128 * DEC_SLOTS;        // keys per workgroup
+static_assert(DEC_SPLIT == DEC_SPLIT_KEYS, "the ABI's grid check uses DEC_SPLIT_KEYS");
 constexpr int DEC_PART = 130;                     // floats per (split, head) partial: m, l, O[128]
 constexpr float DEC_LOG2E = 1.4426950408889634f;
 

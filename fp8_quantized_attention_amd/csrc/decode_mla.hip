@@ -28,7 +28,6 @@
 namespace fa4 {
 
 constexpr int MLA_THREADS = 256;
-constexpr int MLA_PAGES = 32;                     // pages (64-key tiles) per workgroup
 constexpr int MLA_NS = MLA_D / 64;                // column slices per page
 constexpr int MLA_TC = MLA_NS * 64 * 32;          // code bytes per page
 constexpr int MLA_TS = MLA_NS * 64 * 2;           // scale bytes per page

@@ -283,7 +283,7 @@ static fa4_status decode_mla(const fa4_decode_args *a, void *ws, size_t ws_bytes
   REQUIRE(a->B >= 0 && a->B <= 65535, FA4_ERR_SHAPE, "decode (MLA): B=%d", a->B);
   REQUIRE(a->max_pages >= 1 && a->num_pages >= 1, FA4_ERR_SHAPE, "decode (MLA): max_pages and num_pages >= 1");
   REQUIRE((int64_t)a->max_pages * 64 <= ((int64_t)1 << 30), FA4_ERR_SHAPE, "decode (MLA): context too long");
-  REQUIRE(((int64_t)a->max_pages + 31) / 32 * a->B < ((int64_t)1 << 31), FA4_ERR_SHAPE, "decode (MLA): grid too large");
+  REQUIRE(((int64_t)a->max_pages + fa4::MLA_PAGES - 1) / fa4::MLA_PAGES * a->B < ((int64_t)1 << 31), FA4_ERR_SHAPE, "decode (MLA): grid too large");
   if (a->B == 0) return ok();
   REQUIRE(a->q1_codes && a->q1_scales && a->q2_codes && a->q2_scales && a->k_codes && a->k_scales &&
               a->page_table && a->ctx_len && a->o,
@@ -309,7 +309,9 @@ fa4_status fa4_decode_paged(const fa4_decode_args *a, void *ws, size_t ws_bytes,
           "decode: needs Hq = 4 Hkv (Hq=%d Hkv=%d)", a->Hq, a->Hkv);
   REQUIRE(a->max_pages >= 1 && a->num_pages >= 1, FA4_ERR_SHAPE, "decode: max_pages and num_pages >= 1");
   REQUIRE(a->B <= 65535 && a->Hkv <= 65535 && a->Hq <= 65535, FA4_ERR_SHAPE, "decode: grid too large");
-  REQUIRE(((int64_t)a->max_pages * 64 + 2047) / 2048 * a->B * a->Hkv < ((int64_t)1 << 31), FA4_ERR_SHAPE,
+  REQUIRE(((int64_t)a->max_pages * 64 + fa4::DEC_SPLIT_KEYS - 1) / fa4::DEC_SPLIT_KEYS * a->B * a->Hkv <
+              ((int64_t)1 << 31),
+          FA4_ERR_SHAPE,
           "decode: grid too large");
   REQUIRE((int64_t)a->max_pages * 64 <= ((int64_t)1 << 30), FA4_ERR_SHAPE, "decode: context too long");
   if (a->B == 0) return ok();
