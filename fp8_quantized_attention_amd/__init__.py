@@ -176,12 +176,12 @@ def quantize(x, fmt, hadamard=False, dual=False, row_norms=False, fold=None, cha
     return out
 
 
-def quantize_prefill(q, k, v, fmt=FA4_MXFP4, row_norms=False):
-    """Q and K (MXFP4 or MXFP8, optional row norms) and V (FP8 per token with its fold data) of a
-    prefill in one launch (fa4_quantize_prefill). Returns three dicts laid out as quantize() returns
-    them; the values are the same bit for bit."""
+def quantize_prefill(q, k, v, fmt=FA4_MXFP4, row_norms=False, v_fmt=FA4_FP8_TOKEN):
+    """Q and K (MXFP4 or MXFP8, optional row norms) and V (FP8 per token with its fold data, or 4-bit V
+    with v_fmt=FA4_MXFP4_KEYS and MXFP4 Q/K) of a prefill in one launch (fa4_quantize_prefill). Returns
+    three dicts laid out as quantize() returns them; the values are the same bit for bit."""
     bufs = [_quant_buffers(q, fmt, row_norms=row_norms), _quant_buffers(k, fmt, row_norms=row_norms),
-            _quant_buffers(v, FA4_FP8_TOKEN, fold=True)]
+            _quant_buffers(v, v_fmt, fold=True if v_fmt == FA4_FP8_TOKEN else None)]
     (qo, qi, qd, _), (ko, ki, kd, _), (vo, vi, vd, _) = bufs
     _check(lib.fa4_quantize_prefill(ctypes.byref(qi), ctypes.byref(ki), ctypes.byref(vi), ctypes.byref(qd),
                                     ctypes.byref(kd), ctypes.byref(vd), _ptr(qo.get("norm2")), _ptr(ko.get("norm2")),
@@ -416,8 +416,9 @@ def prefill(q, k, v, causal, fmt=FA4_MXFP4, hadamard=False, select=None, softmax
     Hkv, Lk = k.shape[1], k.shape[2]
     sel = select is not None
     qs, ks = smooth if smooth is not None else (None, None)
-    if fmt in (FA4_MXFP4, FA4_MXFP8) and not hadamard and smooth is None and not search and v_fmt == FA4_FP8_TOKEN:
-        qq, kq, vq = quantize_prefill(q, k, v, fmt, row_norms=sel)        # one launch for all three
+    if fmt in (FA4_MXFP4, FA4_MXFP8) and not hadamard and smooth is None and not search and \
+            (v_fmt == FA4_FP8_TOKEN or (fmt == FA4_MXFP4 and d == 128)):
+        qq, kq, vq = quantize_prefill(q, k, v, fmt, row_norms=sel, v_fmt=v_fmt)     # one launch for all three
     else:
         qq = quantize(q, fmt, hadamard=hadamard, row_norms=sel, channel_scale=qs)
         kq = quantize(k, fmt, hadamard=hadamard, row_norms=sel, channel_scale=ks, search=search)
@@ -527,7 +528,8 @@ class PrefillRunner:
         self._norms = [_ptr(self.qq["norm2"]), _ptr(self.kq["norm2"]), None]
         self._fl = [self.flags, self.flags | (FA4_SCALE_SEARCH if search else 0), 0]
         # MXFP4 / MXFP8 Q and K with FP8 V and no rotation or search: one launch for all three
-        self.fused = fmt in (FA4_MXFP4, FA4_MXFP8) and self.flags == 0 and not search and not v4
+        self.fused = fmt in (FA4_MXFP4, FA4_MXFP8) and self.flags == 0 and not search and \
+            (not v4 or (fmt == FA4_MXFP4 and d == 128))
         if softmax_scale is None:
             softmax_scale = 1.0 / math.sqrt(d)
         self._attn = AttnArgs(fmt, self.qq["codes"].data_ptr(), self.qq["block_scales"].data_ptr(),

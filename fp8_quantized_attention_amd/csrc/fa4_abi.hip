@@ -165,8 +165,12 @@ fa4_status fa4_quantize_prefill(const fa4_qinput *q, const fa4_qinput *k, const 
   REQUIRE(q && k && v && q_out && k_out && v_out, FA4_ERR_NULL, "quantize_prefill: a descriptor is NULL");
   REQUIRE((q_out->fmt == FA4_MXFP4 || q_out->fmt == FA4_MXFP8) && k_out->fmt == q_out->fmt, FA4_ERR_UNSUPPORTED,
           "quantize_prefill: Q and K must both be MXFP4 or both MXFP8 (formats %d, %d)", q_out->fmt, k_out->fmt);
-  REQUIRE(v_out->fmt == FA4_FP8_TOKEN && v_out->fold_w && v_out->fold_scale, FA4_ERR_UNSUPPORTED,
-          "quantize_prefill: V must be FP8 per token with its fold outputs");
+  const bool v4 = v_out->fmt == FA4_MXFP4_KEYS;
+  REQUIRE((v_out->fmt == FA4_FP8_TOKEN && v_out->fold_w && v_out->fold_scale) ||
+              (v4 && q_out->fmt == FA4_MXFP4 && q->d == 128),
+          FA4_ERR_UNSUPPORTED,
+          "quantize_prefill: V must be FP8 per token with its fold outputs, or 4-bit V (MXFP4_KEYS) with MXFP4 Q/K "
+          "and d = 128");
   REQUIRE(q->dtype == k->dtype && k->dtype == v->dtype && q->d == k->d && k->d == v->d, FA4_ERR_UNSUPPORTED,
           "quantize_prefill: Q, K and V must share dtype and d");
   REQUIRE(!q->page_table && !k->page_table && !v->page_table && !q->row_counts && !k->row_counts && !v->row_counts,
@@ -178,7 +182,7 @@ fa4_status fa4_quantize_prefill(const fa4_qinput *q, const fa4_qinput *k, const 
   if ((st = check_quantize(q, 0, q_out, nullptr, q_norm2, &eq)) != FA4_OK) return st;
   if ((st = check_quantize(k, 0, k_out, nullptr, k_norm2, &ek)) != FA4_OK) return st;
   if ((st = check_quantize(v, 0, v_out, nullptr, nullptr, &ev)) != FA4_OK) return st;
-  REQUIRE(fa4::prefill_quant_blocks(q, k, v) < ((int64_t)1 << 31), FA4_ERR_SHAPE, "quantize_prefill: grid too large");
+  REQUIRE(fa4::prefill_quant_blocks(q, k, v, v4) < ((int64_t)1 << 31), FA4_ERR_SHAPE, "quantize_prefill: grid too large");
   if (eq && ek && ev) return ok();
   return hip_status(fa4::launch_quantize_prefill(q, k, v, q_out, k_out, v_out, q_norm2, k_norm2, (hipStream_t)stream),
                     "quantize_prefill launch");

@@ -12,7 +12,7 @@ hipError_t launch_quantize(const fa4_qinput *in, uint32_t flags, const fa4_qoutp
 hipError_t launch_quantize_prefill(const fa4_qinput *q, const fa4_qinput *k, const fa4_qinput *v,
                                    const fa4_qoutput *qo, const fa4_qoutput *ko, const fa4_qoutput *vo,
                                    float *q_norm2, float *k_norm2, hipStream_t s);
-int64_t prefill_quant_blocks(const fa4_qinput *q, const fa4_qinput *k, const fa4_qinput *v);
+int64_t prefill_quant_blocks(const fa4_qinput *q, const fa4_qinput *k, const fa4_qinput *v, bool v4);
 hipError_t launch_smoothing(const fa4_qinput *q, const fa4_qinput *k, float *q_scale, float *k_scale,
                             hipStream_t s);
 hipError_t launch_select(const float *qn, const float *kn, int B, int Hq, int Hkv, int Lq, int Lk,

@@ -520,7 +520,12 @@ __global__ void __launch_bounds__(QUANT_THREADS) quantize_kernel(QArgs a) {
 // The three operands of a prefill in one launch, so that their ramps and tails overlap: workgroups
 // [0, nq) take Q's chunks (MXFP4 or MXFP8), [nq, nq + nk) K's, the rest V's (FP8 per token with the
 // fold data, 128-row chunks). Each block's work is exactly that of the separate calls.
-template <int D, int DT, int QKF, bool NORM>
+template <int DT>
+__device__ __forceinline__ void mx_keys_unit(const QArgs &a, int d, int c, int64_t rb, int64_t g);
+
+// VF: FA4_FP8_TOKEN (V per token with its fold data, 128-row chunks) or FA4_MXFP4_KEYS (4-bit V: each
+// workgroup takes two 32-key units, a column per thread, as mx_keys_kernel; vchunks = rows / 32).
+template <int D, int DT, int QKF, bool NORM, int VF = FA4_FP8_TOKEN>
 __global__ void __launch_bounds__(QUANT_THREADS) prefill_quant_kernel(QArgs q, QArgs k, QArgs v, int64_t qchunks,
                                                                       int64_t kchunks, int64_t vchunks, int64_t nq,
                                                                       int64_t nk) {
@@ -532,6 +537,9 @@ __global__ void __launch_bounds__(QUANT_THREADS) prefill_quant_kernel(QArgs q, Q
     const int64_t b = blk - nq;
     quantize_rows<D, DT, QKF, 1, false, false, NORM, false, false, PREFILL_QK_CHUNK>(k, b % kchunks,
                                                                                      (int)(b / kchunks));
+  } else if constexpr (VF == FA4_MXFP4_KEYS) {
+    const int64_t u = 2 * (blk - nq - nk) + (threadIdx.x >> 7), c = threadIdx.x & 127;   // no barrier follows
+    if (u < vchunks * v.outer * v.heads && c < D) mx_keys_unit<DT>(v, D, (int)c, u % vchunks, u / vchunks);
   } else {
     const int64_t b = blk - nq - nk;
     quantize_rows<D, DT, FA4_FP8_TOKEN, 1, false, false, false, false, false, 128, true>(v, b % vchunks,
@@ -879,9 +887,8 @@ hipError_t launch_smoothing(const fa4_qinput *q, const fa4_qinput *k, float *q_s
 // row 8 ((j >> 2) & 3) + 4 (j >> 4) + (j & 3) of the block (the key order of the attention's FP8
 // probability operand). Scales: [group][d][rows/32] E8M0, the MXFP4 rule of the row quantizer.
 template <int DT>
-__global__ void __launch_bounds__(128) mx_keys_kernel(QArgs a, int d) {
-  const int c = threadIdx.x, g = blockIdx.y, r0 = 32 * blockIdx.x;
-  if (c >= d) return;
+__device__ __forceinline__ void mx_keys_unit(const QArgs &a, int d, int c, int64_t rb, int64_t g) {
+  const int64_t r0 = 32 * rb;
   const int64_t o = g / a.heads, h = g - o * a.heads;
   const int64_t base = o * a.so + h * a.sh + (int64_t)r0 * a.sr + c;
   float v[32];
@@ -900,9 +907,14 @@ __global__ void __launch_bounds__(128) mx_keys_kernel(QArgs a, int d) {
     const int k0 = 8 * ((jp >> 2) & 3) + 4 * (jp >> 4) + (jp & 3);
     w[jp >> 3] |= e2m1_pair(v[k0] * mul, v[k0 + 1] * mul) << (4 * (jp & 7));
   }
-  const int64_t row = (int64_t)g * d + c;
+  const int64_t row = g * d + c;
   *reinterpret_cast<uint4 *>(a.codes + row * (a.rows / 2) + r0 / 2) = make_uint4(w[0], w[1], w[2], w[3]);
   a.bscales[row * (a.rows / 32) + r0 / 32] = (uint8_t)(e + 127);
+}
+
+template <int DT>
+__global__ void __launch_bounds__(128) mx_keys_kernel(QArgs a, int d) {
+  if ((int)threadIdx.x < d) mx_keys_unit<DT>(a, d, threadIdx.x, blockIdx.x, blockIdx.y);
 }
 
 static QArgs quant_args(const fa4_qinput *in, const fa4_qoutput *out, const fa4_qoutput *res, float *norm2) {
@@ -921,12 +933,19 @@ static QArgs quant_args(const fa4_qinput *in, const fa4_qoutput *out, const fa4_
 }
 
 template <int D, int DT>
-static hipError_t launch_prefill_quant(const QArgs &q, const QArgs &k, const QArgs &v, int qkf, bool norm,
+static hipError_t launch_prefill_quant(const QArgs &q, const QArgs &k, const QArgs &v, int qkf, bool norm, bool v4,
                                        int64_t qch, int64_t kch, int64_t vch, int64_t nq, int64_t nk, int64_t nv,
                                        hipStream_t s) {
   const dim3 grid((unsigned)(nq + nk + nv));
   // chunk counts divide block indices only inside the branch of a tensor that has blocks
   qch = qch > 0 ? qch : 1; kch = kch > 0 ? kch : 1; vch = vch > 0 ? vch : 1;
+  if (v4) {                                      // 4-bit V goes with MXFP4 Q and K
+    if (norm) hipLaunchKernelGGL((prefill_quant_kernel<D, DT, FA4_MXFP4, true, FA4_MXFP4_KEYS>), grid,
+                                 dim3(QUANT_THREADS), 0, s, q, k, v, qch, kch, vch, nq, nk);
+    else hipLaunchKernelGGL((prefill_quant_kernel<D, DT, FA4_MXFP4, false, FA4_MXFP4_KEYS>), grid, dim3(QUANT_THREADS),
+                            0, s, q, k, v, qch, kch, vch, nq, nk);
+    return hipGetLastError();
+  }
   if (qkf == FA4_MXFP4) {
     if (norm) hipLaunchKernelGGL((prefill_quant_kernel<D, DT, FA4_MXFP4, true>), grid, dim3(QUANT_THREADS), 0, s, q, k,
                                  v, qch, kch, vch, nq, nk);
@@ -941,10 +960,14 @@ static hipError_t launch_prefill_quant(const QArgs &q, const QArgs &k, const QAr
   return hipGetLastError();
 }
 
-int64_t prefill_quant_blocks(const fa4_qinput *q, const fa4_qinput *k, const fa4_qinput *v) {
+// workgroups of V in the one-launch quantization: 128-row tiles (FP8 per token) or pairs of 32-key units
+static int64_t v_blocks(const fa4_qinput *v, bool v4) {
+  return v4 ? (v->rows / 32 * (v->outer * v->heads) + 1) / 2 : v->rows / 128 * (v->outer * v->heads);
+}
+
+int64_t prefill_quant_blocks(const fa4_qinput *q, const fa4_qinput *k, const fa4_qinput *v, bool v4) {
   return (q->rows + PREFILL_QK_CHUNK - 1) / PREFILL_QK_CHUNK * (q->outer * q->heads) +
-         (k->rows + PREFILL_QK_CHUNK - 1) / PREFILL_QK_CHUNK * (k->outer * k->heads) +
-         v->rows / 128 * (v->outer * v->heads);
+         (k->rows + PREFILL_QK_CHUNK - 1) / PREFILL_QK_CHUNK * (k->outer * k->heads) + v_blocks(v, v4);
 }
 
 hipError_t launch_quantize_prefill(const fa4_qinput *q, const fa4_qinput *k, const fa4_qinput *v,
@@ -952,16 +975,19 @@ hipError_t launch_quantize_prefill(const fa4_qinput *q, const fa4_qinput *k, con
                                    float *q_norm2, float *k_norm2, hipStream_t s) {
   const QArgs qa = quant_args(q, qo, nullptr, q_norm2), ka = quant_args(k, ko, nullptr, k_norm2),
               va = quant_args(v, vo, nullptr, nullptr);
+  const bool v4 = vo->fmt == FA4_MXFP4_KEYS;
   const int64_t qch = (q->rows + PREFILL_QK_CHUNK - 1) / PREFILL_QK_CHUNK,
-                kch = (k->rows + PREFILL_QK_CHUNK - 1) / PREFILL_QK_CHUNK, vch = v->rows / 128;
-  const int64_t nq = qch * (q->outer * q->heads), nk = kch * (k->outer * k->heads), nv = vch * (v->outer * v->heads);
+                kch = (k->rows + PREFILL_QK_CHUNK - 1) / PREFILL_QK_CHUNK, vch = v->rows / (v4 ? 32 : 128);
+  const int64_t nq = qch * (q->outer * q->heads), nk = kch * (k->outer * k->heads), nv = v_blocks(v, v4);
   if (nq + nk + nv == 0) return hipSuccess;
   const bool norm = q_norm2 != nullptr;
   if (q->d == 128)
-    return q->dtype == FA4_F32 ? launch_prefill_quant<128, 0>(qa, ka, va, qo->fmt, norm, qch, kch, vch, nq, nk, nv, s)
-                               : launch_prefill_quant<128, 1>(qa, ka, va, qo->fmt, norm, qch, kch, vch, nq, nk, nv, s);
-  return q->dtype == FA4_F32 ? launch_prefill_quant<64, 0>(qa, ka, va, qo->fmt, norm, qch, kch, vch, nq, nk, nv, s)
-                             : launch_prefill_quant<64, 1>(qa, ka, va, qo->fmt, norm, qch, kch, vch, nq, nk, nv, s);
+    return q->dtype == FA4_F32
+               ? launch_prefill_quant<128, 0>(qa, ka, va, qo->fmt, norm, v4, qch, kch, vch, nq, nk, nv, s)
+               : launch_prefill_quant<128, 1>(qa, ka, va, qo->fmt, norm, v4, qch, kch, vch, nq, nk, nv, s);
+  if (v4) return hipErrorInvalidValue;           // the ABI admits 4-bit V here only with d = 128
+  return q->dtype == FA4_F32 ? launch_prefill_quant<64, 0>(qa, ka, va, qo->fmt, norm, false, qch, kch, vch, nq, nk, nv, s)
+                             : launch_prefill_quant<64, 1>(qa, ka, va, qo->fmt, norm, false, qch, kch, vch, nq, nk, nv, s);
 }
 
 hipError_t launch_quantize(const fa4_qinput *in, uint32_t flags, const fa4_qoutput *out,

@@ -146,10 +146,11 @@ fa4_status fa4_quantize_blockscaled(const fa4_qinput *in, uint32_t flags, const 
  * coalesced global-memory access).
  * Writes exactly what three fa4_quantize_blockscaled calls with flags = 0 would write: q and k into
  * q_out and k_out (both FA4_MXFP4 or both FA4_MXFP8, with row norms into q_norm2 / k_norm2 when both
- * are given), v into v_out (FA4_FP8_TOKEN with fold_w and fold_scale). Inputs as for
+ * are given), v into v_out (FA4_FP8_TOKEN with fold_w and fold_scale, or FA4_MXFP4_KEYS, 4-bit V, when
+ * Q and K are MXFP4 and d = 128). Inputs as for
  * fa4_quantize_blockscaled; q, k and v share dtype and d, are unpaged and not ragged (row_counts NULL),
- * and v's rows are a multiple of 128. Rotation, the dual residual, the scale search, NVFP4 and 4-bit V
- * are not offered here (use the separate calls). One launch lets the three streams' start-up and
+ * and v's rows are a multiple of 128 (FP8) or 32 (4-bit V). Rotation, the dual residual, the scale
+ * search and NVFP4 are not offered here (use the separate calls). One launch lets the three streams' start-up and
  * drain overlap, which matters at a few tens of MB per tensor.
  */
 fa4_status fa4_quantize_prefill(const fa4_qinput *q, const fa4_qinput *k, const fa4_qinput *v,

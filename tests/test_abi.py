@@ -127,6 +127,11 @@ def test_quantize_prefill_rejects_before_launch():
     assert _call_qp(kf=fa4.FA4_MXFP8) == fa4.FA4_ERR_UNSUPPORTED                 # Q and K alike
     assert _call_qp(vout=fa4.QOutput(fa4.FA4_FP8_TOKEN, 256, None, 256)) == fa4.FA4_ERR_UNSUPPORTED   # no fold
     assert _call_qp(vout=fa4.QOutput(fa4.FA4_MXFP4, 256, 256, None, 256, 256)) == fa4.FA4_ERR_UNSUPPORTED
+    v4 = fa4.QOutput(fa4.FA4_MXFP4_KEYS, 256, 256, None)                      # 4-bit V: MXFP4 Q/K, d = 128
+    assert _call_qp(qf=fa4.FA4_MXFP8, vout=v4) == fa4.FA4_ERR_UNSUPPORTED
+    assert _call_qp(q=_q(d=64, stride_row=64), k=_q(d=64, stride_row=64), v=_q(d=64, stride_row=64), vout=v4) == \
+        fa4.FA4_ERR_UNSUPPORTED
+    assert _call_qp(v=_q(rows=40, stride_head=40 * 128, stride_outer=2 * 40 * 128), vout=v4) == fa4.FA4_ERR_SHAPE
     assert _call_qp(k=_q(dtype=fa4.FA4_F32)) == fa4.FA4_ERR_UNSUPPORTED
     assert _call_qp(v=_q(d=64, stride_row=64)) == fa4.FA4_ERR_UNSUPPORTED
     assert _call_qp(k=_q(page_table=256, page_size=64, max_pages=4, num_pages=8)) == fa4.FA4_ERR_UNSUPPORTED

@@ -285,3 +285,30 @@ def test_nvfp4_one_row_groups(fa4, d, dtype, dual):
     assert np.array_equal(_np(out["scales"]), t1)
     assert np.array_equal(_np(out["block_scales"]).reshape(70, 1, -1), s1)
     assert np.array_equal(_np(out["codes"]).reshape(70, 1, -1), c1)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_quantize_one_launch_v4(fa4, dtype):
+    """fa4_quantize_prefill with 4-bit V: MXFP4 Q and K and V's MXFP4 blocks along the keys (in the
+    attention's key order), against the oracle and the separate calls, bit for bit; an odd number of
+    32-key units leaves the last workgroup half idle."""
+    g = torch.Generator().manual_seed(23)
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    B, Hq, Hkv, Lq, Lk = 1, 4, 3, 192, 96
+    q = torch.randn(B, Hq, Lq, 128, generator=g).to(dt)
+    k = torch.randn(B, Hkv, Lk, 128, generator=g).to(dt)
+    v = (torch.randn(B, Hkv, Lk, 128, generator=g) * torch.rand(B, Hkv, Lk, 1, generator=g) * 8).to(dt)
+    v[0, 2, 40:72] = 0.0                                # an all-zero block of keys
+    qq, kq, vq = fa4.quantize_prefill(q.cuda(), k.cuda(), v.cuda(), fa4.FA4_MXFP4, v_fmt=fa4.FA4_MXFP4_KEYS)
+    torch.cuda.synchronize()
+    for x, out in ((q, qq), (k, kq)):
+        codes, sc = Q.mxfp4_quantize(x.float().numpy().astype(np.float64))
+        assert np.array_equal(_np(out["codes"]), codes) and np.array_equal(_np(out["block_scales"]), sc)
+    codes, scales = Q.mxfp4_keys_quantize(v.float().numpy().astype(np.float64))
+    assert np.array_equal(_np(vq["block_scales"]), scales)
+    assert np.array_equal(_np(vq["codes"]), _keys_layout(codes))
+    sep = [fa4.quantize(x.cuda(), fa4.FA4_MXFP4) for x in (q, k)] + [fa4.quantize(v.cuda(), fa4.FA4_MXFP4_KEYS)]
+    for a, b in zip((qq, kq, vq), sep):
+        for key, t in b.items():
+            if t is not None:
+                assert torch.equal(a[key], t), key
