@@ -20,6 +20,7 @@ namespace fa4 {
 constexpr int QUANT_THREADS = 256;
 constexpr int QUANT_CHUNK = 64;      // rows per workgroup (one group; NVFP4 maxima reduce per workgroup)
 constexpr int PREFILL_QK_CHUNK = 64; // rows per workgroup of Q and K in the one-launch prefill quantization
+constexpr int NV_MAX_CHUNK = 256;    // rows per workgroup of NVFP4's tensor-maximum pass
 
 // 1/sqrt(128) as the float64 nearest to 1/fl64(sqrt(128)).
 #define FA4_RSQRT128 0x1.6a09e667f3bccp-4
@@ -692,16 +693,19 @@ __global__ void finalize_tensor_scale_kernel(float *p, int64_t n) {
 template <int D, int DT, int FMT, int PASS, bool HAD, bool DUAL, bool SEARCH = false>
 static hipError_t launch_q(const QArgs &a, int64_t groups, bool norm, hipStream_t s) {
   if (a.rows == 0 || groups == 0) return hipSuccess;       // nothing to read (NVFP4 scales still finalize)
-  dim3 grid((unsigned)((a.rows + QUANT_CHUNK - 1) / QUANT_CHUNK), (unsigned)groups);
+  // NVFP4's maximum passes end every workgroup with an atomicMax on its group's maximum; larger chunks
+  // there keep the number of atomics on one address down (2048 per head of 128K rows at 64 rows)
+  constexpr int CH = (FMT == FA4_NVFP4 && PASS == 0) ? NV_MAX_CHUNK : QUANT_CHUNK;
+  dim3 grid((unsigned)((a.rows + CH - 1) / CH), (unsigned)groups);
   if (a.page_table)                                        // row norms are only written unpaged
-    hipLaunchKernelGGL((quantize_kernel<D, DT, FMT, PASS, HAD, DUAL, false, true, SEARCH>), grid, dim3(QUANT_THREADS),
-                       0, s, a);
+    hipLaunchKernelGGL((quantize_kernel<D, DT, FMT, PASS, HAD, DUAL, false, true, SEARCH, CH>), grid,
+                       dim3(QUANT_THREADS), 0, s, a);
   else if (norm)
-    hipLaunchKernelGGL((quantize_kernel<D, DT, FMT, PASS, HAD, DUAL, true, false, SEARCH>), grid, dim3(QUANT_THREADS),
-                       0, s, a);
+    hipLaunchKernelGGL((quantize_kernel<D, DT, FMT, PASS, HAD, DUAL, true, false, SEARCH, CH>), grid,
+                       dim3(QUANT_THREADS), 0, s, a);
   else
-    hipLaunchKernelGGL((quantize_kernel<D, DT, FMT, PASS, HAD, DUAL, false, false, SEARCH>), grid, dim3(QUANT_THREADS),
-                       0, s, a);
+    hipLaunchKernelGGL((quantize_kernel<D, DT, FMT, PASS, HAD, DUAL, false, false, SEARCH, CH>), grid,
+                       dim3(QUANT_THREADS), 0, s, a);
   return hipGetLastError();
 }
 
