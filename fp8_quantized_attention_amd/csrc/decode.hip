@@ -38,6 +38,8 @@ constexpr int DEC_SPLIT = 128 * DEC_SLOTS;        // keys per workgroup
 static_assert(DEC_SPLIT == DEC_SPLIT_KEYS, "the ABI's grid check uses DEC_SPLIT_KEYS");
 constexpr int DEC_PART = 130;                     // floats per (split, head) partial: m, l, O[128]
 constexpr float DEC_LOG2E = 1.4426950408889634f;
+// cache policy of the KV-cache loads: non-temporal (each cache byte is read once per decode step)
+constexpr int DEC_NT = 2;
 
 struct DecArgs {
   const uint8_t *q1c, *q1s, *q2c, *q2s;
@@ -144,8 +146,8 @@ __device__ __forceinline__ void load_k(const TilePages &tp, int n, int g, v4i kc
 #pragma unroll
   for (int kb = 0; kb < 8; kb++) {
     const int p = kb >> 2, r0 = 16 * (kb & 3);
-    kc[kb] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(tp.kc[p], vo_c, r0 * 64, 0));
-    ks[kb] = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(tp.ks[p], vo_s, r0 * 8, 0);
+    kc[kb] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(tp.kc[p], vo_c, r0 * 64, DEC_NT));
+    ks[kb] = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(tp.ks[p], vo_s, r0 * 8, DEC_NT);
   }
 }
 
@@ -162,9 +164,9 @@ __device__ __forceinline__ void load_v(const TilePages &tp, int lane, int n, int
 #pragma unroll
     for (int j = 0; j < 8; j++) {
       const int r0 = 32 * (q & 1) + 16 * (j >> 2) + (j & 3);
-      vc[q][j] = __builtin_amdgcn_raw_buffer_load_b32(tp.vc[p], vo_c, r0 * 64, 0);
+      vc[q][j] = __builtin_amdgcn_raw_buffer_load_b32(tp.vc[p], vo_c, r0 * 64, DEC_NT);
     }
-    vs[q] = __builtin_amdgcn_raw_buffer_load_b32(tp.vs[p], 4 * lane, 256 * (q & 1), 0);
+    vs[q] = __builtin_amdgcn_raw_buffer_load_b32(tp.vs[p], 4 * lane, 256 * (q & 1), DEC_NT);
   }
 }
 
@@ -174,8 +176,8 @@ __device__ __forceinline__ void load_k_mx(const TilePages &tp, int n, int g, v4i
 #pragma unroll
   for (int kb = 0; kb < 8; kb++) {
     const int p = kb >> 2, r0 = 16 * (kb & 3);
-    kc[kb] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(tp.kc[p], vo_c, r0 * 64, 0));
-    ks[kb] = __builtin_amdgcn_raw_buffer_load_b8(tp.ks[p], vo_s, r0 * 4, 0);
+    kc[kb] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(tp.kc[p], vo_c, r0 * 64, DEC_NT));
+    ks[kb] = __builtin_amdgcn_raw_buffer_load_b8(tp.ks[p], vo_s, r0 * 4, DEC_NT);
   }
 }
 
@@ -190,9 +192,9 @@ __device__ __forceinline__ void load_v_mx(const TilePages &tp, int lane, int n, 
 #pragma unroll
     for (int j = 0; j < 8; j++) {
       const int r0 = 32 * (q & 1) + 16 * (j >> 2) + (j & 3);
-      vc[q][j] = __builtin_amdgcn_raw_buffer_load_b32(tp.vc[p], vo_c, r0 * 64, 0);
+      vc[q][j] = __builtin_amdgcn_raw_buffer_load_b32(tp.vc[p], vo_c, r0 * 64, DEC_NT);
     }
-    vs[q] = __builtin_amdgcn_raw_buffer_load_b32(tp.vs[p], 4 * (lane & 31), 128 * (q & 1), 0);
+    vs[q] = __builtin_amdgcn_raw_buffer_load_b32(tp.vs[p], 4 * (lane & 31), 128 * (q & 1), DEC_NT);
   }
 }
 
