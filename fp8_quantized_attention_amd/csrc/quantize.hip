@@ -695,7 +695,11 @@ static hipError_t launch_q(const QArgs &a, int64_t groups, bool norm, hipStream_
   if (a.rows == 0 || groups == 0) return hipSuccess;       // nothing to read (NVFP4 scales still finalize)
   // NVFP4's maximum passes end every workgroup with an atomicMax on its group's maximum; larger chunks
   // there keep the number of atomics on one address down (2048 per head of 128K rows at 64 rows)
-  constexpr int CH = (FMT == FA4_NVFP4 && PASS == 0) ? NV_MAX_CHUNK : QUANT_CHUNK;
+  // MXFP4 dual residual (the decode query: a few thousand rows, two quantizations per row) in chunks of
+  // one row per lane group, so that many small workgroups each finish after one row
+  constexpr int CH = (FMT == FA4_NVFP4 && PASS == 0) ? NV_MAX_CHUNK
+                     : (FMT == FA4_MXFP4 && DUAL)     ? (64 / (D / Epl<DT>::value)) * (QUANT_THREADS / 64)
+                                                      : QUANT_CHUNK;
   dim3 grid((unsigned)((a.rows + CH - 1) / CH), (unsigned)groups);
   if (a.page_table)                                        // row norms are only written unpaged
     hipLaunchKernelGGL((quantize_kernel<D, DT, FMT, PASS, HAD, DUAL, false, true, SEARCH, CH>), grid,
