@@ -102,12 +102,17 @@ def mxfp4_quantize_search(x):
 
 def nvfp4_quantize_search(x):
     """NVFP4 with the per-block scale search. x [G, R, d]. The tensor scale is the round-to-nearest
-    one (amax / 2688). Returns (codes, block scales, tensor scales) as nvfp4_quantize."""
+    one, fl32(amax / 2688), or 1 when that quotient is zero (an all-zero group, or one whose maximum
+    is so small that the quotient underflows: every block scale is then zero). Returns (codes, block
+    scales, tensor scales) as nvfp4_quantize."""
     x = np.asarray(x, dtype=np.float64)
     G, R, d = x.shape
     x32 = fp32(x)
     amax_t = np.max(np.abs(x32).reshape(G, -1), axis=1).astype(np.float32) if R > 0 else np.zeros(G, np.float32)
-    s_t = np.where(amax_t == 0, np.float32(1.0), amax_t / np.float32(6.0 * 448.0)).astype(np.float32)
+    # the round-to-nearest tensor scale, with its zero rule: 1 when fl32(amax / 2688) is zero (amax == 0,
+    # or a maximum so small that the quotient underflows), as in quant.nvfp4_quantize
+    s_t = (amax_t / np.float32(6.0 * 448.0)).astype(np.float32)
+    s_t = np.where(s_t == 0, np.float32(1.0), s_t).astype(np.float32)
     blocks = x32.reshape(G, R, d // NV_BLOCK, NV_BLOCK)
     amax_b = np.max(np.abs(blocks), axis=-1).astype(np.float32)
     six_st = (np.float32(6.0) * s_t).astype(np.float32)

@@ -90,7 +90,9 @@ def mxfp4_row_values(codes, scales):
 def nvfp4_group(rows):
     """rows: list of rows (floats, already float32 values) -> (codes, block scales, tensor scale)."""
     amax_t = max((abs(v) for r in rows for v in r), default=0.0)
-    st = 1.0 if amax_t == 0 else f32(amax_t / 2688.0)
+    st = f32(amax_t / 2688.0)
+    if st == 0:                      # amax_t == 0, or a quotient that underflows float32
+        st = 1.0
     six_st = f32(6.0 * st)
     codes, sbs = [], []
     for r in rows:

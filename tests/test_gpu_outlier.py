@@ -117,3 +117,24 @@ def test_prefill_with_smoothing_and_search(fa4, base):
     ref, lse, _ = prefill_reference(cfg, 0, heads, rows, select=sel, q_all=q, k_all=k, v_all=v,
                                     smooth=(_np(qs), _np(ks)), search=True)
     assert_parity(_np(res["o"])[0], ref, f"prefill {base} smoothing + search")
+
+
+@pytest.mark.parametrize("rows", [6, 100])
+@pytest.mark.parametrize("search", [False, True])
+def test_nvfp4_subnormal_tensor_maximum(fa4, rows, search):
+    """Groups whose maximum is subnormal (1e-42: fl32(amax / 2688) underflows, so s_t = 1 and the group
+    quantizes as all zeros; 1e-39 and 3e-40: a subnormal tensor scale) and one normal group, plain and
+    with the scale search, on the one-launch (<= 64 rows) and multi-pass paths: bit for bit."""
+    rng = np.random.default_rng(11)
+    g = []
+    for amax in (1e-42, 1e-39, 3e-40, 1e-30):
+        x = rng.standard_normal((rows, 128))
+        g.append((x / np.abs(x).max() * amax).astype(np.float32))
+    x = np.stack(g)[None]                                             # [1, 4, rows, 128]
+    out = fa4.quantize(torch.from_numpy(np.ascontiguousarray(x)).cuda(), fa4.FA4_NVFP4, search=search)
+    xf = x[0].astype(np.float64)
+    c, s, st = OA.nvfp4_quantize_search(xf) if search else Q.nvfp4_quantize(xf)
+    assert st[0] == 1.0
+    assert np.array_equal(_np(out["scales"]), st)
+    assert np.array_equal(_np(out["block_scales"])[0], s)
+    assert np.array_equal(_np(out["codes"])[0], c)

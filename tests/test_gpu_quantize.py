@@ -155,14 +155,22 @@ def test_mxfp8_codes_and_scales(fa4, d, dtype):
 
 
 @pytest.mark.parametrize("special", [False, True])
-def test_dual_residual_query_mxfp4(fa4, special):
-    """MXFP4 dual residual: Q1 = MXFP4(q), Q2 = MXFP4(fl32(q - dequant(Q1))), bit for bit."""
+@pytest.mark.parametrize("layout", ["row_groups", "one_group"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_dual_residual_query_mxfp4(fa4, special, layout, dtype):
+    """MXFP4 dual residual: Q1 = MXFP4(q), Q2 = MXFP4(fl32(q - dequant(Q1))), bit for bit. Layouts: n
+    groups of one row, and one group of n rows (the decode query's layout, chunked by rows per workgroup);
+    n = 2048 for the decode query and 67 (not a multiple of the chunk) for the special rows."""
     if special:
-        q = torch.from_numpy(_special_rows(rows=64)).reshape(64, 1, 128)
+        q = torch.from_numpy(np.concatenate([_special_rows(rows=64), _special_rows(rows=8, seed=9)[5:]]))
     else:
-        q = W.decode_query(W.C3).float().reshape(64 * 32, 1, 128)
+        q = W.decode_query(W.C3).float().reshape(64 * 32, 128)
+    if dtype == "bf16":
+        q = q.to(torch.bfloat16)
     n = q.shape[0]
-    out = fa4.quantize(q.reshape(1, n, 1, 128).contiguous().cuda(), fa4.FA4_MXFP4, dual=True)
+    shape = (1, n, 1, 128) if layout == "row_groups" else (1, 1, n, 128)
+    out = fa4.quantize(q.reshape(shape).contiguous().cuda(), fa4.FA4_MXFP4, dual=True)
+    q = q.float().reshape(n, 1, 128)
     (c1, s1), (c2, s2) = Q.dual_residual_quantize_mx(q.numpy().reshape(n, 1, 128))
     assert out["scales"] is None and out["scales2"] is None
     assert np.array_equal(_np(out["block_scales"]).reshape(n, 1, -1), s1)

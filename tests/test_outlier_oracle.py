@@ -150,3 +150,39 @@ def test_smoothing_keeps_qk_exact_and_cuts_logit_error():
     e_smooth = logit_err(q2, k2, Q.nvfp4_quantize)
     e_both = logit_err(q2, k2, O.nvfp4_quantize_search)
     assert e_smooth < 0.9 * e_rtn and e_both < e_smooth
+
+
+def _tiny_groups():
+    """Groups whose tensor maximum is subnormal: 1e-42 (fl32(amax / 2688) underflows to zero) and
+    1e-39, 3e-40 (the quotient is a representable subnormal), plus one normal group."""
+    rng = np.random.default_rng(11)
+    g = []
+    for amax in (1e-42, 1e-39, 3e-40, 1e-30):
+        x = rng.standard_normal((6, 128))
+        x = x / np.abs(x).max() * amax
+        g.append(x.astype(np.float32))
+    return np.stack(g).astype(np.float64)
+
+
+def test_nv_search_tensor_scale_zero_rule():
+    """The search path takes the tensor scale of nvfp4_quantize: 1 when fl32(amax / 2688) is zero.
+    With a maximum of 1e-42 the quotient underflows, so the group quantizes as an all-zero one (zero
+    block scales, signed-zero codes) instead of dividing by a zero scale; the other groups keep
+    their round-to-nearest tensor scale and match the exact brute force block by block."""
+    x = _tiny_groups()
+    assert np.float32(1e-42) / np.float32(2688) == 0 and np.float32(1e-39) / np.float32(2688) > 0
+    codes, sb, st = O.nvfp4_quantize_search(x)
+    _, _, st0 = Q.nvfp4_quantize(x)
+    assert np.array_equal(st, st0) and st[0] == 1.0 and np.all(st[1:] < 1e-30)
+    assert np.all(sb[0] == 0)
+    u = F.unpack_nibbles(codes)[0]
+    assert np.array_equal(u, np.signbit(x[0]).astype(np.int64) << 3)
+    for g in range(x.shape[0]):
+        _, _, bst = bf.nvfp4_group([[float(v) for v in r] for r in x[g]])
+        assert bf.f32(bst) == float(st[g])
+        for r in range(x.shape[1]):
+            for b in range(8):
+                vals = [float(v) for v in x[g, r, 16 * b:16 * b + 16]]
+                assert sb[g, r, b] == _bf_nv_block(vals, float(st[g])), (g, r, b)
+    assert not np.any((sb & 0x7F) == 0x7F)
+    assert np.all(np.isfinite(Q.nvfp4_dequantize(codes, sb, st)))

@@ -245,3 +245,27 @@ def test_mxfp8_codes_are_torch_e4m3_of_the_scaled_block():
     back = Q.mxfp8_dequantize(codes, scales)
     rel = np.abs(back - x) / np.maximum(np.abs(x), 1e-300)
     assert np.all(rel[np.abs(x) >= np.ldexp(1.0, -6 + e.repeat(32, axis=1))] <= 2.0 ** -4)
+
+
+def test_dual_residual_vs_bruteforce():
+    """NVFP4 dual residual re-derived by the brute-force loops: Q1 = the group's NVFP4 by search over
+    every code, x1 its exact value (Python doubles), r = fl32(q - x1) rounded once, Q2 = NVFP4(r) with
+    its own tensor scale. Codes, block scales and tensor scales must equal the oracle's. Groups of
+    several rows and of one row, bf16-valued and float32 inputs, and a row of special values."""
+    rng = np.random.default_rng(21)
+    q = rng.standard_normal((3, 4, 64)).astype(np.float32)
+    q[1] = q[1].astype(np.float32) * np.float32(2.0 ** -20)
+    q[2, 0, :16] = np.float32([0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -6.0, 0.25, 0.75, 1.25, -1.75, 2.5, 3.5, 5.0, 0.0])
+    q[2, 1] = 0.0
+    q[0] = torch.from_numpy(q[0]).to(torch.bfloat16).float().numpy()
+    for groups in (q, q.reshape(12, 1, 64)):
+        (c1, s1, t1), (c2, s2, t2) = Q.dual_residual_quantize(groups.astype(np.float64))
+        u1, u2 = F.unpack_nibbles(c1), F.unpack_nibbles(c2)
+        for g in range(groups.shape[0]):
+            rows = [[float(v) for v in r] for r in groups[g]]
+            bc1, bs1, bt1 = bf.nvfp4_group(rows)
+            assert bf.f32(bt1) == float(t1[g]) and bs1 == s1[g].tolist() and bc1 == u1[g].tolist()
+            x1 = bf.nvfp4_values(bc1, bs1, bt1)
+            res = [[bf.f32(a - b) for a, b in zip(r, xr)] for r, xr in zip(rows, x1)]
+            bc2, bs2, bt2 = bf.nvfp4_group(res)
+            assert bf.f32(bt2) == float(t2[g]) and bs2 == s2[g].tolist() and bc2 == u2[g].tolist()
