@@ -1,34 +1,41 @@
 #!/usr/bin/env python3
 """Benchmark of block-scaled low-bit fused attention on one MI355X.
 
-One step = the whole prefill path on the 4K causal workload (B=1, H=32, L=4096, d=128): MXFP4
-quantization of Q and K and FP8 per-token quantization of V (with its P-fold data), in one launch,
-then the fused attention kernel, inputs resident in HBM. Each timed loop follows W untimed steps and
-at least 0.1 s of untimed back-to-back steps. `value` is prefill attention TFLOP/s over the step
-(algorithmic flops: 4 d per unmasked query-key pair). The same line carries:
+One step = the whole prefill path on the 32K causal workload with tile selection (B=1, H=32,
+L=32768, d=128; the largest single-GPU prefill workload): MXFP4 quantization of Q and K with their
+row norms and FP8 per-token quantization of V (with its P-fold data) in one launch, the top-5% tile
+selection, then the fused attention kernel (MXFP4/FP8 tiles and bf16 selected tiles merged through
+one online softmax), inputs resident in HBM. Each timed loop follows W untimed steps and at least
+0.1 s of untimed back-to-back steps. `value` is prefill TFLOP/s over the step (algorithmic flops:
+4 d per unmasked query-key pair). The line also carries:
   roofline      the attention kernel alone: its algorithmic flops / its average launch time (HIP
-                events on the launch stream) against the dense MXFP4 MFMA peak;
+                events on the launch stream) against the dense MXFP4 MFMA peak, plus the kernel's
+                HBM traffic per launch from the recorded FETCH_SIZE / WRITE_SIZE counters;
+  error         the GPU output on sampled heads and rows against unquantized attention (float64
+                softmax(q k^T / sqrt(d)) v of the bf16 originals): relative L2 and max-abs / max|O|;
+                with tile selection also the error of the same kernel without selected tiles and the
+                share of that error the selected tiles remove;
+  legs          the other prefill workloads (4K causal MXFP4; 128K chunked prefill with NVFP4 +
+                Hadamard and tile selection), each with its own roofline and error;
   decode        the paged NVFP4 decode step (64 sequences, 32 -> 8 GQA heads, contexts 8K-32K):
-                KV-cache GB/s, and the decode kernels' HBM roofline;
-  decode_mxfp4  the same decode step over an MXFP4 cache (same sequences and values);
-  decode_p4, decode_mxfp4_p4
-                the two decode steps with the probabilities in NVFP4 (E4M3 scales per 16 keys)
-                instead of FP8;
+                KV-cache GB/s, the decode kernels' HBM roofline and the error;
+  decode_mxfp4, decode_p4, decode_mxfp4_p4
+                the same decode over an MXFP4 cache and / or with NVFP4 probabilities;
   decode_mla    decode in the MLA geometry (64 sequences, 16 heads over one shared 576-wide MXFP4
-                latent row per token, value = its first 512 values, contexts 8K-32K): KV GB/s;
+                latent row per token, value = its first 512 values, contexts 8K-32K);
   k_quant       (--outlier) quantization of the 128K-token chunked-prefill keys (NVFP4 + Hadamard)
                 plain, with static smoothing, and with smoothing + the per-block scale search;
-  cpu_baseline  the CPU oracle (float64 numpy) on a bounded sample of the same workload.
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-decode] [--no-cpu-baseline]
-                       [--copy-probe] [--summarize-counters DIR]
+  cpu_baseline  the CPU oracle (float64 numpy) on a bounded sample of the headline workload.
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-legs] [--no-decode]
+                       [--no-error] [--no-cpu-baseline] [--quick] [--copy-probe] [--summarize-counters DIR]
 
 HBM traffic: `--copy-probe` adds one untimed plain device copy of COPY_BYTES, so that a
 `rocprofv3 --pmc FETCH_SIZE` (then `WRITE_SIZE`) run of this script records the counters of the
 measured kernels and of a copy of known size together. `--summarize-counters DIR` turns the
-counter CSVs under DIR into profiles/traffic.json: per kernel, the counter reads per dispatch, each
-scaled by (known copy bytes / what the counter read for the copy), with a hash of the kernel's
-sources. The benchmark reports that traffic only while the sources still hash the same (the
-counters describe the kernel they were taken on), and null otherwise.
+counter CSVs under DIR into profiles/traffic.json: per kernel instantiation, the counter reads per
+dispatch, each scaled by (known copy bytes / what the counter read for the copy), with a hash of the
+kernel's sources. The benchmark reports that traffic only while the sources still hash the same
+(the counters describe the kernel they were taken on), and null otherwise.
 """
 import argparse
 import csv
@@ -54,17 +61,30 @@ HBM_PEAK_GBS = 8000.0
 COPY_BYTES = 1 << 30                 # calibration copy: reads and writes this many bytes
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "fp8_quantized_attention_amd", "csrc")
-# sources whose change invalidates a kernel's recorded counters
-# (template arguments of the decode kernel: cache format 1 = NVFP4, 0 = MXFP4; probability format
-# 0 = FP8, 1 = NVFP4)
+# Kernel instantiations whose counters are recorded, with the sources whose change invalidates them.
+# Attention template arguments: <d, Q/K format (0 MXFP4, 1 NVFP4), causal, selection, 4-bit V>; each
+# instantiation is run by one workload here (no selection: 4K causal; MXFP4 with selection: 32K;
+# NVFP4 with selection: the 128K chunked prefill). Decode: <cache format (1 NVFP4, 0 MXFP4),
+# probability format (0 FP8, 1 NVFP4)>.
+ATTN_SRC = ["attn_fwd.hip", "fa4_device.h"]
+DEC_SRC = ["decode.hip", "fa4_device.h"]
 KERNEL_SOURCES = {
-    "attn_fwd_kernel": ["attn_fwd.hip", "fa4_device.h"],
-    "decode_split_kernel<1, 0>": ["decode.hip", "fa4_device.h"],
-    "decode_split_kernel<0, 0>": ["decode.hip", "fa4_device.h"],
-    "decode_split_kernel<1, 1>": ["decode.hip", "fa4_device.h"],
-    "decode_split_kernel<0, 1>": ["decode.hip", "fa4_device.h"],
+    "attn_fwd_kernel<128, 0, true, false, false>": ATTN_SRC,
+    "attn_fwd_kernel<128, 0, true, true, false>": ATTN_SRC,
+    "attn_fwd_kernel<128, 1, true, true, false>": ATTN_SRC,
+    "decode_split_kernel<1, 0>": DEC_SRC,
+    "decode_split_kernel<0, 0>": DEC_SRC,
+    "decode_split_kernel<1, 1>": DEC_SRC,
+    "decode_split_kernel<0, 1>": DEC_SRC,
     "decode_mla_kernel": ["decode_mla.hip", "fa4_device.h"],
 }
+PREFILL = [W.C1, W.C2, W.C4, W.C1_MX8, W.C1_V4]
+
+
+def attn_kernel_name(cfg, select):
+    fmt = {"mxfp4": 0, "nvfp4": 1, "mxfp8": 3}[cfg.qk_fmt]
+    b = lambda x: "true" if x else "false"   # noqa: E731
+    return f"attn_fwd_kernel<{cfg.d}, {fmt}, {b(cfg.causal)}, {b(select)}, {b(cfg.v_fmt == 'mxfp4k')}>"
 
 
 def sources_sha(kernel):
@@ -105,6 +125,11 @@ def summarize_counters(root):
     fac = {c: COPY_BYTES / (per[("copy", c)] * 1024.0) for c in ("FETCH_SIZE", "WRITE_SIZE") if ("copy", c) in per}
     out = {"copy_bytes": COPY_BYTES, "copy_kib_raw": {c: per[("copy", c)] for c in fac}, "scale": fac,
            "kernels": {}}
+    try:                                                 # keep kernels this run did not cover
+        with open(TRAFFIC_JSON) as fh:
+            out["kernels"] = {k: v for k, v in json.load(fh).get("kernels", {}).items() if k in KERNEL_SOURCES}
+    except (OSError, ValueError):
+        pass
     for k in KERNEL_SOURCES:
         if (k, "FETCH_SIZE") in per and (k, "WRITE_SIZE") in per and len(fac) == 2:
             fb = per[(k, "FETCH_SIZE")] * 1024.0 * fac["FETCH_SIZE"]
@@ -142,12 +167,14 @@ def prefill_flops(cfg):
 WARM_S = 0.1
 
 
-def _warm(fn, n):
+def _warm(fn, n, quick=False):
     """n untimed calls, continued until at least WARM_S seconds of back-to-back work have run, so that
     the timed loop does not start on clocks still ramping up after the host-side input generation."""
     for _ in range(n):
         fn()
     torch.cuda.synchronize()
+    if quick:
+        return
     t = time.perf_counter()
     while time.perf_counter() - t < WARM_S:
         for _ in range(8):
@@ -167,18 +194,108 @@ def _time_loop(fn, n):
     return t0.elapsed_time(t1) / n
 
 
-def time_prefill(fa4, cfg, steps, warmup, select):
-    """(ms per whole step, ms per attention launch). The step loop has no events inside it; the
-    attention kernel is timed on its own loop of back-to-back launches over the same inputs."""
+# ---------------------------------------------------------------------------------------------- errors
+
+def _rel(got, ref):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    return (float(np.linalg.norm(got - ref) / np.linalg.norm(ref)),
+            float(np.abs(got - ref).max() / np.abs(ref).max()))
+
+
+def exact_attention_rows(q, k, v, rows, off, causal, scale):
+    """float64 softmax(q k^T * scale) v for query rows `rows` of one head (q [Lq, d], k/v [Lk, d],
+    float64), query i at key position off + i when causal. Unquantized: the reference for the error."""
+    s = (q[rows] @ k.T) * scale
+    if causal:
+        s = np.where(np.arange(k.shape[0])[None, :] > (off + rows)[:, None], -np.inf, s)
+    s -= s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    return (p @ v) / p.sum(axis=1, keepdims=True)
+
+
+def sample_heads_rows(cfg):
+    heads = [(0, 0), (0, cfg.Hq // 2 + 1)]
+    rows = np.unique(np.concatenate([np.linspace(0, cfg.Lq - 1, 96).astype(np.int64),
+                                     np.arange(cfg.Lq - 32, cfg.Lq)]))
+    return heads, rows
+
+
+def prefill_error(cfg, q, k, v, outs):
+    """Error of each GPU output in `outs` ({name: o [B, Hq, Lq, d] tensor}) against unquantized
+    attention on the sampled heads and rows."""
+    heads, rows = sample_heads_rows(cfg)
+    group = cfg.Hq // cfg.Hkv
+    ref, got = [], {n: [] for n in outs}
+    for (b, h) in heads:
+        qh = q[b, h].double().cpu().numpy()
+        kh = k[b, h // group].double().cpu().numpy()
+        vh = v[b, h // group].double().cpu().numpy()
+        ref.append(exact_attention_rows(qh, kh, vh, rows, cfg.Lk - cfg.Lq, cfg.causal, cfg.d ** -0.5))
+        for n, o in outs.items():
+            got[n].append(o[b, h][torch.from_numpy(rows).to(o.device)].cpu().numpy())
+    res = {"sample": f"heads {heads}, {len(rows)} query rows (96 spread + the last 32)", "reference":
+           "unquantized float64 attention of the bf16 inputs"}
+    for n in outs:
+        rel, mx = _rel(np.stack(got[n]), np.stack(ref))
+        res[n] = {"rel_l2": rel, "max_abs_over_max": mx}
+    return res
+
+
+# ---------------------------------------------------------------------------------------------- prefill
+
+def time_prefill(fa4, cfg, steps, warmup, quick=False, error=True):
+    """Times one prefill workload: (ms per whole step, ms per attention launch, error dict or None).
+    The step loop has no events inside it; the attention kernel is timed on its own loop of
+    back-to-back launches over the same inputs."""
     q, k, v = (t.cuda() for t in W.prefill_inputs(cfg))
     fmt = {"mxfp4": fa4.FA4_MXFP4, "nvfp4": fa4.FA4_NVFP4, "mxfp8": fa4.FA4_MXFP8}[cfg.qk_fmt]
     vf = fa4.FA4_MXFP4_KEYS if cfg.v_fmt == "mxfp4k" else fa4.FA4_FP8_TOKEN
+    select = (5, 100) if cfg.select else None
     run = fa4.PrefillRunner(q, k, v, cfg.causal, fmt=fmt, hadamard=cfg.hadamard, select=select, v_fmt=vf)
-    _warm(run.run, warmup)
+    _warm(run.run, warmup, quick)
     step_ms = _time_loop(run.run, steps)
     attn_ms = _time_loop(run.attention, steps)
-    return step_ms, attn_ms
+    err = None
+    if error:
+        run.run()
+        outs = {"gpu": run.o}
+        if select is not None:          # the same quantized operands without selected tiles
+            o_ns, _ = fa4.attn_fwd(run.qq, run.kq, run.vq, cfg.causal, fmt, cfg.Hq, cfg.Hkv, cfg.Lq, cfg.Lk, cfg.d,
+                                   B=cfg.B, want_lse=False, v_fmt=vf)
+            outs["gpu_no_selection"] = o_ns
+        torch.cuda.synchronize()
+        err = prefill_error(cfg, q, k, v, outs)
+        if select is not None:
+            e1, e0 = err["gpu"]["rel_l2"], err["gpu_no_selection"]["rel_l2"]
+            err["selection_gap_recovered"] = 1.0 - e1 / e0
+    del run, q, k, v
+    torch.cuda.empty_cache()
+    return step_ms, attn_ms, err
 
+
+def prefill_record(fa4, cfg, args, headline=False):
+    step_ms, attn_ms, err = time_prefill(fa4, cfg, args.steps, args.warmup, args.quick, not args.no_error)
+    flops = prefill_flops(cfg)
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    peak = FP8_PEAK_TFLOPS if cfg.qk_fmt == "mxfp8" else MXFP4_PEAK_TFLOPS
+    kname = attn_kernel_name(cfg, cfg.select)
+    rec = {
+        "workload": cfg.name, "value": flops / (step_ms * 1e-3) / 1e12, "unit": "TFLOP/s", "ms_per_step": step_ms,
+        "dtype": cfg.qk_fmt + ("+fp4v" if cfg.v_fmt == "mxfp4k" else "+fp8") + ("+bf16tiles" if cfg.select else ""),
+        "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "Lq": cfg.Lq, "Lk": cfg.Lk,
+                   "d": cfg.d, "causal": cfg.causal, "qk_format": cfg.qk_fmt, "hadamard": cfg.hadamard,
+                   "bf16_tiles": "5%" if cfg.select else "none", "algorithmic_flops": flops},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": recorded_traffic(kname) if kname in KERNEL_SOURCES else None,
+                     "kernel": kname, "kernel_ms": attn_ms},
+        "error_vs_unquantized": err,
+    }
+    print(f"[bench] prefill {cfg.name}: step {step_ms:.4f} ms, attention {attn_ms:.4f} ms "
+          f"({achieved:.0f} TFLOP/s, {100 * achieved / peak:.1f}% of peak)", file=sys.stderr, flush=True)
+    return rec
+
+
+# ---------------------------------------------------------------------------------------------- decode
 
 _KV_CACHE = {}
 
@@ -194,7 +311,27 @@ def decode_kv_inputs(cfg):
     return _KV_CACHE[key]
 
 
-def time_decode(fa4, cfg, steps, warmup):
+DEC_PAIRS = [(0, 0), (7, 5), (21, 13), (33, 30), (50, 18), (63, 31)]
+
+
+def decode_error(q, k, v, ctx, o, pairs, group, scale, d_v=None):
+    """GPU decode output vs unquantized float64 attention of the bf16 query and cache rows."""
+    ref, got = [], []
+    for (b, h) in pairs:
+        L = int(ctx[b])
+        kh = k[b, h // group, :L].double().cpu().numpy()
+        vh = (v[b, h // group, :L] if v is not None else k[b, h // group, :L, :d_v]).double().cpu().numpy()
+        qh = q[b, h].double().cpu().numpy()
+        s = (kh @ qh) * scale
+        p = np.exp(s - s.max())
+        ref.append((p @ vh) / p.sum())
+        got.append(o[b, h].cpu().numpy())
+    rel, mx = _rel(np.stack(got), np.stack(ref))
+    return {"sample": f"(sequence, head) pairs {pairs}", "reference": "unquantized float64 attention of the bf16 "
+            "query and cache rows", "gpu": {"rel_l2": rel, "max_abs_over_max": mx}}
+
+
+def time_decode(fa4, cfg, steps, warmup, quick=False, error=True):
     lay, xs = decode_kv_inputs(cfg)
     ctx, pt = lay.ctx_len.cuda(), lay.page_table.cuda()
     nv = cfg.kv_fmt == "nvfp4"
@@ -202,31 +339,54 @@ def time_decode(fa4, cfg, steps, warmup):
     q = W.decode_query(cfg).cuda()
     run = fa4.DecodeRunner(q, caches[0], caches[1], pt, ctx, cfg.Hkv,
                            p_fmt=fa4.FA4_P_NVFP4 if cfg.p_fmt == "nvfp4" else fa4.FA4_P_FP8)
-    _warm(run.run, warmup)
+    _warm(run.run, warmup, quick)
     step_ms = _time_loop(run.run, steps)
     kern_ms = _time_loop(run.attention, steps)
+    err = None
+    if error:
+        run.run()
+        torch.cuda.synchronize()
+        err = decode_error(q, xs[0], xs[1], lay.ctx_len, run.o, DEC_PAIRS, cfg.Hq // cfg.Hkv, cfg.d ** -0.5)
     # K and V codes plus block scales (d/16 E4M3 or d/32 E8M0 bytes) per (token, key head)
     kv_bytes = float(lay.ctx_len.double().sum()) * cfg.Hkv * 2 * (cfg.d // 2 + cfg.d // (16 if nv else 32))
-    return step_ms, kern_ms, kv_bytes, int(lay.ctx_len.sum())
+    return step_ms, kern_ms, kv_bytes, int(lay.ctx_len.sum()), err
 
 
-def time_decode_mla(fa4, cfg, steps, warmup):
+def time_decode_mla(fa4, cfg, steps, warmup, quick=False, error=True):
     _KV_CACHE.clear()
     torch.cuda.empty_cache()
     lay = W.decode_layout(cfg)
     ctx, pt = lay.ctx_len.cuda(), lay.page_table.cuda()
-    x = W.decode_kv_padded(cfg, lay, W.T_K, device="cuda")[:, 0].contiguous()
-    cache = fa4.quantize_paged_mla(x, ctx, pt, lay.num_pages)
-    del x
-    torch.cuda.empty_cache()
+    x = W.decode_kv_padded(cfg, lay, W.T_K, device="cuda")
+    cache = fa4.quantize_paged_mla(x[:, 0].contiguous(), ctx, pt, lay.num_pages)
     q = W.decode_query(cfg).cuda()
     run = fa4.DecodeMlaRunner(q, cache, pt, ctx, cfg.softmax_scale)
-    _warm(run.run, warmup)
+    _warm(run.run, warmup, quick)
     step_ms = _time_loop(run.run, steps)
     kern_ms = _time_loop(run.attention, steps)
+    err = None
+    if error:
+        run.run()
+        torch.cuda.synchronize()
+        err = decode_error(q, x, None, lay.ctx_len, run.o, [(b, h % 16) for b, h in DEC_PAIRS], cfg.Hq,
+                           cfg.softmax_scale, d_v=cfg.d_v)
+    del x
+    torch.cuda.empty_cache()
     # one latent row per token: d/2 code bytes + d/32 E8M0 bytes
     kv_bytes = float(lay.ctx_len.double().sum()) * (cfg.d // 2 + cfg.d // 32)
-    return step_ms, kern_ms, kv_bytes, int(lay.ctx_len.sum())
+    return step_ms, kern_ms, kv_bytes, int(lay.ctx_len.sum()), err
+
+
+def decode_record(key, dcfg, step_ms, kern_ms, kv_bytes, tokens, err, kname, kernel):
+    gbs = kv_bytes / (kern_ms * 1e-3) / 1e9
+    print(f"[bench] {key} ({dcfg.kv_fmt}, P {dcfg.p_fmt}): step {step_ms:.4f} ms, kernels {kern_ms:.4f} ms, "
+          f"{gbs:.0f} GB/s", file=sys.stderr, flush=True)
+    return {"metric": "decode KV GB/s", "workload": dcfg.name, "value": kv_bytes / (step_ms * 1e-3) / 1e9,
+            "unit": "GB/s", "ms_per_step": step_ms, "kv_bytes": kv_bytes, "context_tokens": tokens,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": recorded_traffic(kname),
+                         "traffic_kernel": kname, "kernel": kernel, "kernel_ms": kern_ms},
+            "error_vs_unquantized": err}
 
 
 def time_k_quant(fa4, steps, warmup):
@@ -253,22 +413,31 @@ def time_k_quant(fa4, steps, warmup):
     return res
 
 
-def cpu_baseline(cfg, heads):
-    """The oracle as it stands on `heads` query heads of the workload (quantize + attend every row)."""
+# ---------------------------------------------------------------------------------------------- CPU oracle
+
+def cpu_baseline(cfg, rows_n):
+    """The oracle as it stands on one query head of the workload: quantize that head's Q, K and V
+    (whole sequence), select its tiles, attend `rows_n` query rows spread over the sequence."""
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from oracle_cases import prefill_reference
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
-        cores = os.cpu_count()
+        threads = 1
+    rows = np.unique(np.linspace(0, cfg.Lq - 1, rows_n).astype(np.int64))
     t = time.time()
-    prefill_reference(cfg, 0, [(0, h) for h in range(heads)], np.arange(cfg.Lq))
+    prefill_reference(cfg, 0, [(0, 0)], rows, (5, 100) if cfg.select else None)
     secs = time.time() - t
-    flops = prefill_flops(cfg) * heads / (cfg.B * cfg.Hq)
-    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{heads} of {cfg.Hq} heads, all {cfg.Lq} query rows (quantize Q/K/V + attention), "
-                      f"{secs:.1f} s"}
+    off = cfg.Lk - cfg.Lq
+    pairs = float(np.minimum(cfg.Lk, off + rows + 1).sum()) if cfg.causal else float(len(rows) * cfg.Lk)
+    flops = 4.0 * cfg.d * pairs
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "host_cpu_count": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "sample": f"head (0, 0) of {cfg.name}: quantize its Q, K, V ({cfg.Lk} rows each)"
+                      f"{', select its tiles' if cfg.select else ''}, attend {len(rows)} query rows spread over "
+                      f"the sequence ({pairs:.3g} query-key pairs); {secs:.1f} s; cores = the numpy BLAS threads "
+                      f"(element-wise numpy runs on one)"}
 
 
 def main():
@@ -276,12 +445,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=W.C1.name,
-                    choices=[c.name for c in W.WORKLOADS + [W.C1_MX8, W.C1_V4] if isinstance(c, W.Prefill)])
+    ap.add_argument("--workload", default=W.C2.name, choices=[c.name for c in PREFILL])
+    ap.add_argument("--no-legs", action="store_true", help="skip the other prefill workloads")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-p4", action="store_true", help="skip the decode steps with NVFP4 probabilities")
+    ap.add_argument("--no-error", action="store_true", help="skip the errors against unquantized attention")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=32)
+    ap.add_argument("--cpu-rows", type=int, default=160, help="query rows of the CPU oracle's sample")
+    ap.add_argument("--quick", action="store_true", help="no 0.1 s warm loop (profiler runs)")
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--outlier", action="store_true", help="also time the outlier-aware key quantization")
     ap.add_argument("--summarize-counters", metavar="DIR")
@@ -294,70 +465,49 @@ def main():
         sys.exit(2)
     import fp8_quantized_attention_amd as fa4
 
-    cfg = next(c for c in W.WORKLOADS + [W.C1_MX8, W.C1_V4] if c.name == args.workload)
-    select = (5, 100) if cfg.select else None
+    cfg = next(c for c in PREFILL if c.name == args.workload)
     if args.copy_probe:
         copy_probe()
-    step_ms, attn_ms = time_prefill(fa4, cfg, args.steps, args.warmup, select)
-    flops = prefill_flops(cfg)
-    achieved = flops / (attn_ms * 1e-3) / 1e12
-    peak = FP8_PEAK_TFLOPS if cfg.qk_fmt == "mxfp8" else MXFP4_PEAK_TFLOPS
+    head = prefill_record(fa4, cfg, args, headline=True)
     line = {
         "metric": METRIC,
-        "value": flops / (step_ms * 1e-3) / 1e12,
+        "value": head["value"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": step_ms,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": cfg.qk_fmt + ("+fp4v" if cfg.v_fmt == "mxfp4k" else "+fp8"),
+        "dtype": head["dtype"],
         "data": "synthetic",
-        "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "Lq": cfg.Lq, "Lk": cfg.Lk,
-                   "d": cfg.d, "causal": cfg.causal, "qk_format": cfg.qk_fmt, "hadamard": cfg.hadamard,
-                   "bf16_tiles": "5%" if select else "none", "algorithmic_flops": flops},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": recorded_traffic("attn_fwd_kernel")
-                     if cfg.name == W.C1.name else None, "kernel": "attn_fwd_kernel",
-                     "kernel_ms": attn_ms},
+        "config": head["config"],
+        "roofline": head["roofline"],
+        "error_vs_unquantized": head["error_vs_unquantized"],
     }
-    print(f"[bench] prefill {cfg.name}: step {step_ms:.4f} ms, attention {attn_ms:.4f} ms", file=sys.stderr,
-          flush=True)
+    if not args.no_legs:
+        line["legs"] = {}
+        for lcfg in (W.C1, W.C2, W.C4):
+            if lcfg.name != cfg.name:
+                line["legs"][lcfg.name] = prefill_record(fa4, lcfg, args)
     if not args.no_decode:
         dec = [("decode", W.C3), ("decode_mxfp4", W.C3_MX)]
         if not args.no_p4:
             dec += [("decode_p4", W.C3_P4), ("decode_mxfp4_p4", W.C3_MX_P4)]
         for key, dcfg in dec:
-            d_step, d_kern, kv_bytes, tokens = time_decode(fa4, dcfg, args.steps, args.warmup)
-            gbs = kv_bytes / (d_kern * 1e-3) / 1e9
+            res = time_decode(fa4, dcfg, args.steps, args.warmup, args.quick, not args.no_error)
             kname = "decode_split_kernel<%d, %d>" % (dcfg.kv_fmt == "nvfp4", dcfg.p_fmt == "nvfp4")
-            line[key] = {
-                "metric": "decode KV GB/s", "workload": dcfg.name, "value": kv_bytes / (d_step * 1e-3) / 1e9,
-                "unit": "GB/s", "ms_per_step": d_step, "kv_bytes": kv_bytes, "context_tokens": tokens,
-                "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                             "frac": gbs / HBM_PEAK_GBS, "traffic": recorded_traffic(kname),
-                             "traffic_kernel": kname, "kernel": "decode_split+combine", "kernel_ms": d_kern}}
-            print(f"[bench] {key} ({dcfg.kv_fmt}, P {dcfg.p_fmt}): step {d_step:.4f} ms, kernels {d_kern:.4f} ms, {gbs:.0f} GB/s",
-                  file=sys.stderr, flush=True)
+            line[key] = decode_record(key, dcfg, *res, kname, "decode_split+combine")
             torch.cuda.empty_cache()
-        dcfg = W.C5_MLA
-        d_step, d_kern, kv_bytes, tokens = time_decode_mla(fa4, dcfg, args.steps, args.warmup)
-        gbs = kv_bytes / (d_kern * 1e-3) / 1e9
-        line["decode_mla"] = {
-            "metric": "decode KV GB/s", "workload": dcfg.name, "value": kv_bytes / (d_step * 1e-3) / 1e9,
-            "unit": "GB/s", "ms_per_step": d_step, "kv_bytes": kv_bytes, "context_tokens": tokens,
-            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "traffic": recorded_traffic("decode_mla_kernel"),
-                         "traffic_kernel": "decode_mla_kernel", "kernel": "decode_mla+combine", "kernel_ms": d_kern}}
-        print(f"[bench] decode_mla (mxfp4): step {d_step:.4f} ms, kernels {d_kern:.4f} ms, {gbs:.0f} GB/s",
-              file=sys.stderr, flush=True)
+        _KV_CACHE.clear()
+        res = time_decode_mla(fa4, W.C5_MLA, args.steps, args.warmup, args.quick, not args.no_error)
+        line["decode_mla"] = decode_record("decode_mla", W.C5_MLA, *res, "decode_mla_kernel", "decode_mla+combine")
         torch.cuda.empty_cache()
     if args.outlier:
         line["k_quant"] = time_k_quant(fa4, args.steps, args.warmup)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, min(args.cpu_heads, cfg.Hq))
+        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_rows)
     print(json.dumps(line), flush=True)
 
 
