@@ -81,7 +81,10 @@ struct AttnLds {
   static constexpr int KS = 512;
   static constexpr int VC = 128 * D;
   static constexpr int QBUF = KC + KS + VC + 512;
-  static constexpr int QBYTES = QF == FA4_MXFP4 ? 2 * QBUF : 0;
+  // the pipelined d = 128 path: K buffers (codes + E8M0) and V buffers (codes + w_c + the tile's V scale)
+  static constexpr int PKBUF = 128 * 64 + 512;
+  static constexpr int PVBUF = 128 * 128 + 512 + 16;
+  static constexpr int QBYTES = QF != FA4_MXFP4 ? 0 : D == 128 ? 2 * PKBUF + 2 * PVBUF : 2 * QBUF;
   static constexpr int K16 = 128 * H16_RS;
   static constexpr int V8 = 128 * V8_RS;                 // NVFP4 tiles' FP8 V rows
   static constexpr int V16 = 128 * H16_RS;               // selected tiles' bf16 V rows (overlap V8 onwards)
@@ -107,6 +110,28 @@ __device__ __forceinline__ void dma4(const void *g, uint8_t *l) {
   __builtin_amdgcn_global_load_lds(g, (lds_void_t *)l, 4, 0, 0);
 }
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// The same direct global->LDS loads written as inline asm, for the pipelined MXFP4 loop: the compiler
+// cannot tell which LDS bytes such a load writes, so after the builtin it waits for the load before every
+// later LDS read, which would put the next tiles' load latency in front of this tile's softmax. These
+// loads are waited for explicitly (wait_vmem) before the barrier that publishes their buffers. M0 takes
+// the wave-uniform LDS address and needs one wait state before the load; no other code of this kernel
+// reads M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// Addressing: a wave-uniform 64-bit base (SGPRs) plus a 32-bit per-lane byte offset; the LDS address is
+// passed as an integer (the dynamic LDS base taken once from the array, plus an offset).
+__device__ __forceinline__ void dma16_nw(const void *sbase, uint32_t voff, uint32_t l) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(l);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_nw(const void *sbase, uint32_t voff, uint32_t l) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(l);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 // 8 E2M1 codes (4 bytes, low nibble first) times an E4M3 block scale as exact fp16 values (code * s_b
 // has at most 6 significant bits): hardware fp4 -> fp16 conversion, then one packed multiply.
@@ -191,6 +216,20 @@ __device__ __forceinline__ v16f qk_mx_block(const LaneOff &lo, int kb, int hh, c
   return s;
 }
 
+// The same product for d = 128 with the key's scale word read once and shifted by 8 hh, so that the E8M0
+// byte of block 2 st + hh is byte 2 st of the operand, picked by the MFMA's scale byte select (no per-MFMA
+// extraction).
+__device__ __forceinline__ v16f qk_mx128(const LaneOff &lo, int kb, int hh, const v8i *qop4, const int *qsc4,
+                                         const uint8_t *k4, const uint8_t *ksc) {
+  const int scw = (int)(*reinterpret_cast<const uint32_t *>(ksc + lo.ks + 128 * kb) >> (8 * hh));
+  const v4i t0 = *reinterpret_cast<const v4i *>(k4 + lo.k[0] + 32 * kb * 64);
+  const v4i t1 = *reinterpret_cast<const v4i *>(k4 + lo.k[1] + 32 * kb * 64);
+  v16f s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4((v8i){t0[0], t0[1], t0[2], t0[3], 0, 0, 0, 0}, qop4[0],
+                                                          (v16f){}, 4, 4, 0, scw, 0, qsc4[0]);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4((v8i){t1[0], t1[1], t1[2], t1[3], 0, 0, 0, 0}, qop4[1], s,
+                                                         4, 4, 2, scw, 0, qsc4[1]);
+}
+
 // Keys past the query position get -inf (the tile crossing the causal diagonal).
 __device__ __forceinline__ void mask_tile(v16f S[4], int kt, int hh, int qpos) {
 #pragma unroll
@@ -200,6 +239,83 @@ __device__ __forceinline__ void mask_tile(v16f S[4], int kt, int hh, int qpos) {
       const int key = kt * 128 + 32 * kb + 8 * (i / 4) + 4 * hh + (i % 4);
       if (key > qpos) S[kb][i] = -INFINITY;
     }
+}
+
+// The same mask for the pipelined loop, where the diagonal tile is met inside the loop. It is written as
+// bit arithmetic on an opaque value so that the compiler neither hoists the 64 key comparisons out of the
+// loop nor forms them as 64 lane masks in scalar registers: m = -1 exactly when the key lies past the
+// query (index > lim), and the score's bits are then replaced by those of -inf.
+__device__ __forceinline__ void mask_tile_rt(v16f S[4], int kt, int hh, int qpos) {
+  int lim = qpos - kt * 128 - 4 * hh;             // largest unmasked key index within the tile, less 4 hh
+  asm volatile("" : "+v"(lim));
+#pragma unroll
+  for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      int m = lim - (32 * kb + 8 * (i / 4) + (i % 4));
+      asm volatile("" : "+v"(m));
+      m >>= 31;
+      S[kb][i] = __uint_as_float((__float_as_uint(S[kb][i]) & ~(uint32_t)m) | (0xff800000u & (uint32_t)m));
+    }
+}
+
+// max(a, b, c) as one v_max3_f32. Written as asm because the compiler, which cannot know that MFMA results
+// are canonical floats, otherwise canonicalizes the first operands of every maximum chain with extra VALU
+// instructions (the inputs here are finite or -inf).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// max of this lane's value and lane l ^ 32's, by one lane swap on the VALU (no LDS crossbar round trip)
+__device__ __forceinline__ float max_lane32(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+}
+
+// Block kb of mask_tile_rt, for a limit already made opaque by the caller.
+__device__ __forceinline__ void mask_block_rt(v16f &Skb, int kb, int lim) {
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    int m = lim - (32 * kb + 8 * (i / 4) + (i % 4));
+    asm volatile("" : "+v"(m));
+    m >>= 31;
+    Skb[i] = __uint_as_float((__float_as_uint(Skb[i]) & ~(uint32_t)m) | (0xff800000u & (uint32_t)m));
+  }
+}
+__device__ __forceinline__ float block_max(const v16f &Skb) {
+  // a balanced tree of 3-input maxima (5 + 2 instructions, depth 3)
+  const float a = max3f(Skb[0], Skb[1], Skb[2]), b = max3f(Skb[3], Skb[4], Skb[5]);
+  const float c = max3f(Skb[6], Skb[7], Skb[8]), d = max3f(Skb[9], Skb[10], Skb[11]);
+  const float e = max3f(Skb[12], Skb[13], Skb[14]);
+  return max3f(max3f(a, b, c), d, max3f(e, Skb[15], Skb[15]));
+}
+
+// fp8_block with the block's fold factors already in registers (w4[a4] = w_c of keys 32 kb + 8 a4 + 4 hh + u).
+template <bool V4>
+__device__ __forceinline__ void fp8_block_w(const v16f &Skb, const float4 *w4, float cs, float rr0, float &ts,
+                                            int &x0, int &x1, int &x2, int &x3) {
+  int *xs[4] = {&x0, &x1, &x2, &x3};
+#pragma unroll
+  for (int a4 = 0; a4 < 4; a4++) {
+    const float wv[4] = {w4[a4].x, w4[a4].y, w4[a4].z, w4[a4].w};
+    float pw[4];
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      if (V4) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(Skb[4 * a4 + u], cs, -rr0 + LOG2_448));
+        ts = (a4 == 0 && u == 0) ? p : ts + p;
+        pw[u] = p;
+      } else {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(Skb[4 * a4 + u], cs, -rr0));
+        ts = (a4 == 0 && u == 0) ? p : ts + p;
+        pw[u] = p * wv[u];
+      }
+    }
+    int x = __builtin_amdgcn_cvt_pk_fp8_f32(pw[0], pw[1], __float_as_int(pw[0]), false);
+    *xs[a4] = __builtin_amdgcn_cvt_pk_fp8_f32(pw[2], pw[3], x, true);
+  }
 }
 
 // The tile's row reference in log2 units: the smallest integer r >= its largest score, so that
@@ -295,6 +411,37 @@ __device__ __forceinline__ void pv_fp8(const v8i pop[2], const uint8_t *vq, cons
       }
       acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, pop[t], acc[mb], 0, 0, 0, scA, 0, kBc + 127);
     }
+  }
+}
+
+// Half t of pv_fp8 for d = 128 (keys 64 t .. 64 t + 63 of an MXFP4-path tile): the pipelined loop issues
+// the two halves as soon as their probabilities are packed.
+__device__ __forceinline__ void pv_fp8_half(const v8i &pop, int t, const uint8_t *vq, const LaneOff &lo, int scA,
+                                            int kBc, v16f *acc) {
+#pragma unroll
+  for (int mb = 0; mb < 4; mb++) {
+    v8i vop;
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const v2i rr = lds_tr8(vq + lo.v[mb] + (64 * t + 32 * (u >> 1) + 16 * (u & 1)) * 128);
+      vop[2 * u] = rr[0];
+      vop[2 * u + 1] = rr[1];
+    }
+    acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, pop, acc[mb], 0, 0, 0, scA, 0, kBc + 127);
+  }
+}
+// Half t of pv_fp4v (4-bit V^T, keys 64 t .. 64 t + 63).
+__device__ __forceinline__ void pv_fp4v_half(const v8i &pop, int t, const uint8_t *vt, const uint8_t *vts, int lane,
+                                             int kBc, v16f *acc) {
+  const int h = lane >> 5;
+#pragma unroll
+  for (int mb = 0; mb < 4; mb++) {
+    const int row = 32 * mb + (lane & 31);
+    const int sw = (int)(*reinterpret_cast<const uint32_t *>(vts + 4 * row) >> (8 * h));
+    const v4i c = *reinterpret_cast<const v4i *>(vt + row * 64 + 16 * ((2 * t + h) ^ kswz<128>(row)));
+    const v8i va = (v8i){c[0], c[1], c[2], c[3], 0, 0, 0, 0};
+    acc[mb] = t == 0 ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pop, acc[mb], 4, 0, 0, sw, 0, kBc + 127)
+                     : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pop, acc[mb], 4, 0, 2, sw, 0, kBc + 127);
   }
 }
 
@@ -459,7 +606,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
   }
   const int kvh = h / (a.Hq / a.Hkv);
   const int off = a.Lk - a.Lq;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5, col = lane & 31;
   const int qrow = qt * 128 + wave * 32 + col;      // this lane's query (B-operand column)
   const LaneOff lo = lane_offsets<D>(lane);
@@ -534,8 +681,266 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
       while (kt < kt_end && is_sel(kt)) kt++;
     return kt;
   };
-  if (QF == FA4_MXFP4) {
-    // ---- quantized tiles: direct global->LDS loads into a double buffer, one tile ahead
+  if constexpr (QF == FA4_MXFP4 && D == 128) {
+    // ---- quantized tiles, software-pipelined. K and V have double buffers of their own and K runs one tile
+    // ahead of V: iteration i (tile t_i, whose scores S are already in registers with their reference)
+    // converts S block by block to FP8 probabilities and, as each block's registers free up, issues the
+    // next tile's QK^T MFMAs into them (K(t_{i+1}) in LDS); the two halves of this tile's PV MFMAs go out as
+    // soon as their probabilities are packed. The matrix core then works on QK^T(t_{i+1}) and PV(t_i) while
+    // the VALU computes the softmax of t_i, and the row maximum of t_{i+1} follows. Loads for K(t_{i+2}) and
+    // V(t_{i+1}) are issued at the top of iteration i into the buffers that K(t_i) and V(t_{i-1}) left.
+    constexpr int KBUF = L::PKBUF;          // codes (XOR-swizzled rows) + E8M0
+    constexpr int VBUF = L::PVBUF;          // V codes + w_c + the tile's V scale (4-bit V: V^T codes + E8M0)
+    uint8_t *const vbase = lds + 2 * KBUF;
+    const uint32_t lds_addr =
+        __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t *)lds);
+    // per-lane byte offsets of the loads (loop-invariant; the tile's position goes into the uniform base)
+    uint32_t ko[2], vo[4];
+#pragma unroll
+    for (int e = 0; e < 2; e++) {          // K codes: 16 rows x 64 B per wave-load, two per wave
+      const int r = (wave * 2 + e) * 16 + (lane >> 2), p = lane & 3;
+      ko[e] = (uint32_t)(r * 64 + 16 * (p ^ kswz<128>(r)));
+    }
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      if constexpr (V4) {                  // V^T rows (d): 16 rows x 64 B per wave-load, two per wave
+        const int r = (wave * 2 + (e & 1)) * 16 + (lane >> 2), p = lane & 3;
+        vo[e] = (uint32_t)(r * (a.Lk / 2) + 16 * (p ^ kswz<128>(r)));
+      } else {                             // V rows: 8 rows x 128 B per wave-load, four per wave
+        const int r = (wave * 4 + e) * 8 + (lane >> 3), p = lane & 7;
+        vo[e] = (uint32_t)(r * 128 + 16 * (p ^ vswz<128>(r)));
+      }
+    }
+    const uint32_t so = (uint32_t)(((wave & 1) * 64 + lane) * 4);       // one 4-byte item per row
+    const uint32_t vso = V4 ? (uint32_t)(((wave & 1) * 64 + lane) * (a.Lk / 32)) : 0u;   // 4-bit V^T scale rows
+    auto issue_k = [&](int kt, int buf) __attribute__((always_inline)) {
+      const uint32_t base = lds_addr + buf * KBUF;
+      const uint8_t *g = a.kc + (bhk * a.Lk + (int64_t)kt * 128) * 64;
+#pragma unroll
+      for (int e = 0; e < 2; e++) dma16_nw(g, ko[e], base + 1024 * (wave * 2 + e));
+      if (wave < 2) dma4_nw(a.ks + (bhk * a.Lk + (int64_t)kt * 128) * 4, so, base + 8192 + 256 * wave);
+    };
+    auto issue_v = [&](int kt, int buf) __attribute__((always_inline)) {
+      const uint32_t base = lds_addr + 2 * KBUF + buf * VBUF;
+      if constexpr (V4) {
+        // V^T rows (d = 0 .. 127) of the tile: 64 bytes each at key offset 64 kt, laid out as K's rows
+        const uint8_t *g = a.vc + bhk * 128 * (int64_t)(a.Lk / 2) + (int64_t)kt * 64;
+#pragma unroll
+        for (int e = 0; e < 2; e++) dma16_nw(g, vo[e], base + 1024 * (wave * 2 + e));
+        if (wave >= 2) dma4_nw(a.vbs + bhk * 128 * (int64_t)(a.Lk / 32) + (int64_t)kt * 4, vso, base + 8192 + 256 * (wave - 2));
+      } else {
+        const uint8_t *g = a.vc + (bhk * a.Lk + (int64_t)kt * 128) * 128;
+#pragma unroll
+        for (int e = 0; e < 4; e++) dma16_nw(g, vo[e], base + 1024 * (wave * 4 + e));
+        if (wave >= 2) dma4_nw(a.vw + bhk * a.Lk + (int64_t)kt * 128, so, base + 16384 + 256 * (wave - 2));
+        // the tile's power-of-two V scale (4 bytes, one lane): read from LDS in the loop, so that no scalar
+        // load (whose wait would also drain the LDS reads in flight) sits on the loop's path
+        if (wave == 1 && lane == 0) dma4_nw(a.vfs + bhk * nk + kt, 0u, base + 16384 + 512);
+      }
+    };
+    const float cs = cs_q;
+    int tc = next_quant(0);
+    if (tc < kt_end) {
+      int tn = next_quant(tc + 1);
+      issue_k(tc, 0);
+      issue_v(tc, 0);
+      if (tn < kt_end) issue_k(tn, 1);
+      wait_vmem();
+      __syncthreads();
+      v16f S[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; kb++) S[kb] = qk_mx128(lo, kb, hh, qop4, qsc4, lds, lds + 8192);
+      if (CAUSAL && tc == last) mask_tile_rt(S, tc, hh, qrow + off);
+      float rr0;
+      int kB = tile_weight<NDB>(tile_reference(S, cs), m, lsum, acc, rr0);
+      // The second PV half of each tile is issued in the next iteration's first region (its V operands are
+      // read into registers before the barrier that frees the V buffer). Before the first tile the pending
+      // half is all zero operands, which add exact zeros.
+      v8i vpend[4], ppend = (v8i){};
+      int vspend[4];
+#pragma unroll
+      for (int mb = 0; mb < 4; mb++) {
+        vpend[mb] = (v8i){};
+        vspend[mb] = 0x7f7f7f7f;                   // E8M0 1.0 in every byte
+      }
+      int kpend = 0, spend = 127;                  // pending half's P^T weight exponent and V^T scale code
+      int ib = 0;                                  // iteration parity: K(t_i) in buffer ib, V(t_i) in buffer ib
+      while (true) {
+        const bool has_next = tn < kt_end;
+        const int tnn = has_next ? next_quant(tn + 1) : kt_end;
+        wait_vmem();
+        __syncthreads();      // K(t_{i+1}) and V(t_i) landed; every wave is done with K(t_i) and V(t_{i-1})
+        if (tnn < kt_end) issue_k(tnn, ib);
+        if (has_next) issue_v(tn, ib ^ 1);
+        const uint8_t *kq = lds + (ib ^ 1) * KBUF;            // K(t_{i+1})
+        const uint8_t *vq = vbase + ib * VBUF;                // V(t_i)
+        const float *svs = reinterpret_cast<const float *>(vq + (V4 ? 8192 : 16384));
+        const int kBc = kB < -127 ? -127 : kB;
+        const int scA = V4 ? 0 : (int)((*reinterpret_cast<const uint32_t *>(vq + 16384 + 512) >> 23) & 0xffu);
+        // Five regions, separated by scheduling barriers. Region r < 4 converts block r of this tile to FP8
+        // probabilities (VALU) while the matrix core runs: in region 0 the previous tile's second PV half; in
+        // region r >= 1 the next tile's QK^T for key block r - 1 (into the registers that block's softmax has
+        // just read) and in region 2 this tile's first PV half. Region 4 runs the next tile's QK^T for block 3
+        // beside its row maximum over blocks 0-2, and reads this tile's V for the second half. Each region
+        // issues its LDS reads first, then spreads its MFMAs through its VALU work. On the last tile the
+        // next-tile QK^T reads the other K buffer's stale (in-bounds) bytes and its scores are never used:
+        // issuing it unconditionally keeps the score registers in place.
+        const bool diag_next = CAUSAL && tn == last;
+        float ts[4], mp[3];
+        v8i pop[2];                  // packed FP8 probabilities: the P^T operand of each PV half (keys 64 t ..)
+        v8i vop[4];
+        int vsw[4];
+#pragma unroll
+        for (int r = 0; r < 5; r++) {
+          // ---- LDS reads
+          float4 w4[4];
+          if (r < 4 && !V4) {
+#pragma unroll
+            for (int a4 = 0; a4 < 4; a4++)
+              w4[a4] = *reinterpret_cast<const float4 *>(reinterpret_cast<const uint8_t *>(svs) + lo.w + 4 * (32 * r + 8 * a4));
+          }
+          v4i k0, k1;
+          int scw = 0;
+          const int qb = r - 1;                            // key block of the next tile's QK^T in this region
+          if (r >= 1) {
+            k0 = *reinterpret_cast<const v4i *>(kq + lo.k[0] + 2048 * qb);
+            k1 = *reinterpret_cast<const v4i *>(kq + lo.k[1] + 2048 * qb);
+            scw = (int)(*reinterpret_cast<const uint32_t *>(kq + 8192 + lo.ks + 128 * qb) >> (8 * hh));
+          }
+          if (r == 2 || r == 4) {                          // V^T operands of half t
+            const int t = r == 2 ? 0 : 1;
+#pragma unroll
+            for (int mb = 0; mb < 4; mb++) {
+              if constexpr (V4) {
+                const int row = 32 * mb + (lane & 31);
+                vsw[mb] = (int)(*reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint8_t *>(svs) + 4 * row) >>
+                                (8 * hh));
+                const v4i c = *reinterpret_cast<const v4i *>(vq + row * 64 + 16 * ((2 * t + hh) ^ kswz<128>(row)));
+                vop[mb] = (v8i){c[0], c[1], c[2], c[3], 0, 0, 0, 0};
+              } else {
+#pragma unroll
+                for (int u = 0; u < 4; u++) {
+                  const v2i rr = lds_tr8(vq + lo.v[mb] + (64 * t + 32 * (u >> 1) + 16 * (u & 1)) * 128);
+                  vop[mb][2 * u] = rr[0];
+                  vop[mb][2 * u + 1] = rr[1];
+                }
+              }
+            }
+          }
+          // ---- VALU
+          if (r < 4) {
+            int x0, x1, x2, x3;
+            fp8_block_w<V4>(S[r], w4, cs, rr0, ts[r], x0, x1, x2, x3);
+            pop[r >> 1][4 * (r & 1) + 0] = x0;
+            pop[r >> 1][4 * (r & 1) + 1] = x1;
+            pop[r >> 1][4 * (r & 1) + 2] = x2;
+            pop[r >> 1][4 * (r & 1) + 3] = x3;
+          } else {
+#pragma unroll
+            for (int b = 0; b < 3; b++) {
+              mp[b] = block_max(S[b]);                     // (recomputed after masking the diagonal tile)
+              asm volatile("" : "+v"(mp[b]));              // computed here, beside block 3's MFMAs
+            }
+          }
+          // ---- MFMA
+          if (r == 0) {
+#pragma unroll
+            for (int mb = 0; mb < 4; mb++) {
+              if constexpr (V4)
+                acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vpend[mb], ppend, acc[mb], 4, 0, 2, vspend[mb], 0,
+                                                                          kpend + 127);
+              else
+                acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vpend[mb], ppend, acc[mb], 0, 0, 0, spend, 0,
+                                                                          kpend + 127);
+            }
+          } else {
+            S[qb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4((v8i){k0[0], k0[1], k0[2], k0[3], 0, 0, 0, 0}, qop4[0],
+                                                                   (v16f){}, 4, 4, 0, scw, 0, qsc4[0]);
+            if (r == 2) {
+#pragma unroll
+              for (int mb = 0; mb < 4; mb++) {
+                if constexpr (V4)
+                  acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[mb], pop[0], acc[mb], 4, 0, 0, vsw[mb], 0,
+                                                                            kBc + 127);
+                else
+                  acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[mb], pop[0], acc[mb], 0, 0, 0, scA, 0,
+                                                                            kBc + 127);
+              }
+            }
+            S[qb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4((v8i){k1[0], k1[1], k1[2], k1[3], 0, 0, 0, 0}, qop4[1],
+                                                                   S[qb], 4, 4, 2, scw, 0, qsc4[1]);
+          }
+          // ---- schedule: LDS reads first, then the MFMAs spread through the VALU work
+          __builtin_amdgcn_sched_group_barrier(0x100, 32, 0);
+          if (r == 0) {
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+              __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
+          } else if (r == 2) {
+#pragma unroll
+            for (int g = 0; g < 6; g++) {
+              __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
+          } else if (r < 4) {
+            __builtin_amdgcn_sched_group_barrier(0x002, 20, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 30, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          } else {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // this tile's second PV half goes out in the next region 0
+#pragma unroll
+        for (int mb = 0; mb < 4; mb++) {
+          vpend[mb] = vop[mb];
+          vspend[mb] = vsw[mb];
+        }
+        ppend = pop[1];
+        kpend = kBc;
+        spend = scA;
+        const float tsum = (ts[0] + ts[1]) + (ts[2] + ts[3]);
+        lsum += __builtin_ldexpf(V4 ? tsum * (1.0f / 448.0f) : tsum, kB);
+        if (!has_next) break;
+        float mS;
+        if (diag_next) {
+          mask_tile_rt(S, tn, hh, qrow + off);
+          mS = max3f(max3f(block_max(S[0]), block_max(S[1]), block_max(S[2])), block_max(S[3]), block_max(S[3]));
+        } else {
+          mS = max3f(max3f(mp[0], mp[1], mp[2]), block_max(S[3]), block_max(S[3]));
+        }
+        mS = max_lane32(mS);
+        const float m_old = m;
+        kB = tile_weight<NDB>(ceilf(mS * cs), m, lsum, acc, rr0);
+        if (m != m_old) {            // the reference was raised: the pending half's weight follows it
+          kpend -= (int)(m - m_old);
+          if (kpend < -127) {        // below the smallest E8M0 weight: that half adds nothing representable
+            kpend = -127;
+            ppend = (v8i){};
+          }
+        }
+        tc = tn;
+        tn = tnn;
+        ib ^= 1;
+      }
+      // the last tile's second PV half
+#pragma unroll
+      for (int mb = 0; mb < 4; mb++) {
+        if constexpr (V4)
+          acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vpend[mb], ppend, acc[mb], 4, 0, 2, vspend[mb], 0,
+                                                                    kpend + 127);
+        else
+          acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vpend[mb], ppend, acc[mb], 0, 0, 0, spend, 0, kpend + 127);
+      }
+    }
+  } else if (QF == FA4_MXFP4) {
+    // ---- quantized tiles (d = 64): direct global->LDS loads into a double buffer, one tile ahead
     auto issue = [&](int kt, int b) {
       uint8_t *base = lds + b * L::QBUF;
       const int64_t krow0 = bhk * a.Lk + (int64_t)kt * 128;
