@@ -157,3 +157,72 @@ def test_v4_noncausal_gqa_offset(fa4):
 
 def test_full_size_prefill_4k_v4(fa4):
     _sampled(fa4, W.C1_V4, heads=[(0, 0), (0, 21)], nrows=96)
+
+
+# ---- 4K causal at the other two seeds (small shape in full, full size on sampled rows)
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_causal_small_mxfp4_seeds(fa4, seed):
+    _check_full(fa4, W.C1.scaled(Hq=2, Hkv=2, Lq=512, Lk=512), seed)
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_full_size_prefill_4k_seeds(fa4, seed):
+    _sampled(fa4, W.C1, heads=[(0, 3), (0, 26)], nrows=64, seed=seed)
+
+
+# ---- the online softmax's reference jumps: keys of some tiles scaled so that a tile's row maximum rises
+# far above the running reference (the accumulator and the pending half-tile are rescaled), and so far that
+# earlier tiles fall below the smallest representable weight
+
+def _jump_inputs(causal, factors, seed=31):
+    g = torch.Generator().manual_seed(seed)
+    L, d = 128 * len(factors), 128
+    q = torch.randn(1, 2, L, d, generator=g).to(torch.bfloat16)
+    k = torch.randn(1, 2, L, d, generator=g)
+    for j, f in enumerate(factors):
+        k[:, :, 128 * j:128 * (j + 1)] *= f
+    k = k.to(torch.bfloat16)
+    v = torch.randn(1, 2, L, d, generator=g).to(torch.bfloat16)
+    return q, k, v
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("factors", [(1, 1, 1, 8, 1, 1, 1, 1), (1, 2, 40, 1, 1, 1, 160, 1)],
+                         ids=["raise_once", "raise_past_smallest_weight"])
+@pytest.mark.parametrize("select", [None, (25, 100)])
+def test_reference_jumps(fa4, causal, factors, select):
+    from oracle import quant as Q
+    from oracle import selection as S
+    q, k, v = _jump_inputs(causal, factors)
+    L = q.shape[2]
+    res = fa4.prefill(q.cuda(), k.cuda(), v.cuda(), causal, fmt=fa4.FA4_MXFP4, select=select)
+    torch.cuda.synchronize()
+    qd, kd, vd = (t.double().numpy() for t in (q, k, v))
+    qq = Q.mxfp4_dequantize(*Q.mxfp4_quantize(qd))
+    kk = Q.mxfp4_dequantize(*Q.mxfp4_quantize(kd))
+    vc, sv = Q.fp8_per_token_quantize(vd)
+    bm = None
+    if select is not None:
+        bm, _ = S.select_tiles(Q.row_norm2(qd), Q.row_norm2(kd), L, L, causal, *select)
+        assert np.array_equal(res["bitmap"].cpu().numpy(), bm)
+    O, lse = A.attention_prefill(qq, kk, vc, sv, causal, q_orig=qd, k_orig=kd, v_orig=vd, bitmap=bm)
+    # Conditioning of this input: scores reach ~230 in log2 units, where the float32 rounding of the
+    # exponent's argument (2^-24 relative) already flips bf16 and E4M3 probability codes of rows that one
+    # key dominates. The oracle itself, with its softmax scale moved by one float32 ulp, differs by
+    # delta; the max-abs bound is max(2e-3, 2 delta), the relative-L2 bound stays 1e-3.
+    O1, _ = A.attention_prefill(qq, kk, vc, sv, causal, scale=(1.0 + 2.0 ** -23) / np.sqrt(128), q_orig=qd,
+                                k_orig=kd, v_orig=vd, bitmap=bm)
+    _, delta = rel_errors(O1, O)
+    rel, mx = rel_errors(res["o"].cpu().numpy(), O)
+    what = f"jumps {factors} causal={causal} select={select}"
+    assert rel <= 1e-3 and mx <= max(2e-3, 2 * delta), f"{what}: rel-L2 {rel:.3e} max-abs/max {mx:.3e} (delta {delta:.2e})"
+    # LSE: the scores themselves are float32 sums of 128 products here reaching ~1e4, so their rounding
+    # (about 2^-23 of sum |q_i k_i| per score, in units of the softmax scale) bounds the LSE agreement
+    eps_s = 2.0 ** -23 * (np.abs(qq) @ np.abs(np.swapaxes(kk, -1, -2))).max() / np.sqrt(128)
+    assert np.abs(res["lse"].cpu().numpy() - lse).max() < 1e-4 + 4 * eps_s
+
+
+def test_few_quantized_tiles_between_selected(fa4):
+    """90% of the tiles in bf16: the quantized pipeline runs over one or two tiles per row of tiles."""
+    _check_full(fa4, W.C2.scaled(Hq=2, Hkv=2, Lq=1024, Lk=1024), select=(90, 100))
