@@ -25,7 +25,8 @@ FA4_HADAMARD128, FA4_DUAL_RESIDUAL, FA4_SCALE_SEARCH = 1, 2, 4
 FA4_P_FP8, FA4_P_NVFP4 = 0, 1                      # decode probability formats
 
 EXPORTS = ["fa4_quantize_blockscaled", "fa4_quantize_prefill", "fa4_smoothing_factors", "fa4_select_tiles", "fa4_attn_fwd", "fa4_decode_workspace_bytes",
-           "fa4_decode_paged", "fa4_status_string", "fa4_last_error"]
+           "fa4_decode_paged", "fa4_decode_paged_noalloc", "fa4_status_string", "fa4_last_error"]
+DECODE_SCRATCH_BYTES = 40 << 20                    # FA4_DECODE_SCRATCH_BYTES
 
 _p = ctypes.c_void_p
 _i32, _i64, _u32, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_float
@@ -76,6 +77,8 @@ lib.fa4_decode_workspace_bytes.argtypes = [ctypes.POINTER(DecodeArgs)]
 lib.fa4_decode_workspace_bytes.restype = ctypes.c_size_t
 lib.fa4_decode_paged.argtypes = [ctypes.POINTER(DecodeArgs), _p, ctypes.c_size_t, _p]
 lib.fa4_decode_paged.restype = ctypes.c_int
+lib.fa4_decode_paged_noalloc.argtypes = [ctypes.POINTER(DecodeArgs), _p]
+lib.fa4_decode_paged_noalloc.restype = ctypes.c_int
 lib.fa4_status_string.argtypes = [ctypes.c_int]
 lib.fa4_status_string.restype = ctypes.c_char_p
 lib.fa4_last_error.argtypes = []
@@ -311,6 +314,13 @@ def decode_paged(q1, q2, kcache, vcache, page_table, ctx_len, Hq, Hkv, d=128, pa
     _check(lib.fa4_decode_paged(ctypes.byref(a), workspace.data_ptr(), workspace.numel(), _stream()),
            "fa4_decode_paged")
     return out
+
+
+def decode_paged_noalloc(args, stream=None):
+    """fa4_decode_paged_noalloc on a DecodeArgs struct (from decode_args or mla_decode_args): the decode
+    attention with the library's own scratch, no workspace allocated."""
+    _check(lib.fa4_decode_paged_noalloc(ctypes.byref(args), _stream() if stream is None else stream),
+           "fa4_decode_paged_noalloc")
 
 
 # ---------------------------------------------------------------------------------------------------- MLA decode

@@ -3,6 +3,7 @@
 // thread-local message for fa4_last_error().
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "fa4_internal.h"
@@ -269,6 +270,45 @@ fa4_status fa4_smoothing_factors(const fa4_qinput *q, const fa4_qinput *k, float
           k->heads);
   REQUIRE(aligned(q_scale, 4) && aligned(k_scale, 4), FA4_ERR_ALIGN, "smoothing: outputs must be 4-byte aligned");
   return hip_status(fa4::launch_smoothing(q, k, q_scale, k_scale, (hipStream_t)stream), "smoothing launch");
+}
+
+// ---- decode without a caller workspace. The split partials live in `scratch`, a device global of
+// FA4_DECODE_SCRATCH_BYTES per GPU. In host code `scratch` names a host-side stand-in, not device memory:
+// its device address on each GPU comes from hipGetSymbolAddress, called once per device with that device
+// current, and only that address is handed to the kernels.
+}  // extern "C"
+namespace {
+__device__ __align__(256) uint8_t scratch[FA4_DECODE_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];          // device address of `scratch` per device, once looked up
+}  // namespace
+extern "C" {
+
+fa4_status fa4_decode_paged_noalloc(const fa4_decode_args *a, void *stream) {
+  REQUIRE(a, FA4_ERR_NULL, "decode (no allocation): args is NULL");
+  const size_t need = fa4_decode_workspace_bytes(a);
+  REQUIRE(need <= FA4_DECODE_SCRATCH_BYTES, FA4_ERR_WORKSPACE,
+          "decode (no allocation): these shapes need %zu bytes of scratch, more than the %zu the library holds; "
+          "use fa4_decode_paged with a workspace",
+          need, (size_t)FA4_DECODE_SCRATCH_BYTES);
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "decode (no allocation): hipGetDevice");
+  REQUIRE(dev >= 0 && dev < kMaxDevices, FA4_ERR_UNSUPPORTED, "decode (no allocation): device %d", dev);
+  void *ptr = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+      void *p = nullptr;
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_status(e, "decode (no allocation): hipGetSymbolAddress(scratch)");
+      REQUIRE(p != nullptr, FA4_ERR_HIP, "decode (no allocation): no device address for the scratch array");
+      g_scratch_ptr[dev] = p;
+    }
+    ptr = g_scratch_ptr[dev];
+  }
+  return fa4_decode_paged(a, ptr, FA4_DECODE_SCRATCH_BYTES, stream);
 }
 
 size_t fa4_decode_workspace_bytes(const fa4_decode_args *a) {

@@ -7,6 +7,7 @@
  *   fa4_select_tiles          ThriftAttention-style choice of the 128x128 tiles computed in bf16
  *   fa4_attn_fwd              fused prefill attention (scaled-MFMA QK^T and PV, FP32 online softmax)
  *   fa4_decode_paged          decode attention over a paged FP4 (NVFP4 or MXFP4) KV cache
+ *                             (fa4_decode_paged_noalloc: the same without a caller workspace)
  *
  * Conventions shared by every call:
  *   - Every pointer in an argument struct is a DEVICE pointer owned by the caller and must stay valid
@@ -298,6 +299,24 @@ typedef struct {
 size_t fa4_decode_workspace_bytes(const fa4_decode_args *a);
 fa4_status fa4_decode_paged(const fa4_decode_args *a, void *workspace, size_t workspace_bytes,
                             void *stream);
+
+/*
+ * fa4_decode_paged without a workspace argument, for callers that cannot allocate device memory (code
+ * recorded into a HIP graph, tight serving loops, harnesses that forbid allocation). It computes exactly
+ * what fa4_decode_paged computes, with the same kernels and the same validation, and allocates nothing:
+ * the split partials go to a scratch array of FA4_DECODE_SCRATCH_BYTES that the library holds as a
+ * device global on every GPU it runs on, for the life of the process. Its address on the current device
+ * is looked up once per device, on that device's first call.
+ *   - Returns FA4_ERR_WORKSPACE, enqueuing nothing, when fa4_decode_workspace_bytes(a) exceeds
+ *     FA4_DECODE_SCRATCH_BYTES (for example 64 sequences of 32K tokens need 17 MB in the GQA geometry and
+ *     34 MB in the MLA geometry).
+ *   - Every call on one GPU uses that GPU's one array, and nothing in it needs to start at any value (each
+ *     call writes every partial it reads). Calls that overlap on one GPU (on different streams, or from
+ *     different threads without ordering) race on it: order them, or use fa4_decode_paged with
+ *     workspaces of their own.
+ */
+#define FA4_DECODE_SCRATCH_BYTES ((size_t)40 << 20)
+fa4_status fa4_decode_paged_noalloc(const fa4_decode_args *a, void *stream);
 
 /* ------------------------------------------------------------------------------------------------ */
 const char *fa4_status_string(int status);   /* static text of a status code                        */

@@ -256,3 +256,20 @@ def test_mla_decode_rejects_before_launch():
     assert call(_dec(**{**mla, "k_scales": 264})) == fa4.FA4_ERR_ALIGN
     assert call(_dec(**{**mla, "k_codes": None})) == fa4.FA4_ERR_NULL
     assert call(_dec(**{**mla, "B": 0})) == fa4.FA4_OK
+
+
+def test_decode_noalloc_rejects_before_any_gpu_call():
+    """fa4_decode_paged_noalloc checks its scratch need against the fixed size before it touches a device:
+    NULL args, and shapes whose split partials exceed FA4_DECODE_SCRATCH_BYTES, are refused with nothing
+    enqueued (no GPU here)."""
+    assert fa4.lib.fa4_decode_paged_noalloc(None, None) == fa4.FA4_ERR_NULL
+    text = open(HEADER).read()
+    m = re.search(r"#define FA4_DECODE_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == fa4.DECODE_SCRATCH_BYTES
+    # 64 sequences of up to 128K tokens, 8 key heads: 64 splits of 2048 keys each
+    a = fa4.DecodeArgs(fa4.FA4_NVFP4, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16, 16,
+                       64, 32, 8, 128, 64, 2048, 131072, 0.088, 16, fa4.FA4_P_FP8, 0)
+    need = fa4.lib.fa4_decode_workspace_bytes(ctypes.byref(a))
+    assert need > fa4.DECODE_SCRATCH_BYTES
+    assert fa4.lib.fa4_decode_paged_noalloc(ctypes.byref(a), None) == fa4.FA4_ERR_WORKSPACE
+    assert b"scratch" in fa4.lib.fa4_last_error()
