@@ -11,7 +11,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libfa4.so")
+# FA4_LIBRARY may name another build of the same library (the sanitizer build of the host code)
+LIB_PATH = os.environ.get("FA4_LIBRARY") or os.path.join(_HERE, "libfa4.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python fp8_quantized_attention_amd/build.py` "

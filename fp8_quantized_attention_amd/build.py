@@ -1,7 +1,8 @@
 """Build the HIP library libfa4.so in-tree with hipcc for gfx950.
 
-Usage: python fp8_quantized_attention_amd/build.py   (or __graft_entry__.build()); run it as a script so
-that the package (which loads the library) is not imported first.
+Usage: python fp8_quantized_attention_amd/build.py [--sanitize]   (or __graft_entry__.build()); run it as
+a script so that the package (which loads the library) is not imported first. --sanitize builds the
+host-sanitized copy under _build/sanitize/ instead.
 """
 import os
 import subprocess
@@ -25,10 +26,36 @@ FLAGS = [
 ]
 
 
-def build(verbose=False, extra_flags=()):
+# The host code (argument validation, dispatch) with AddressSanitizer and UndefinedBehaviorSanitizer, for
+# tests of the C ABI on the CPU: the sanitizers apply to host code only, device code is built at -O1.
+SAN_LIB = os.path.join(HERE, "_build", "sanitize", "libfa4.so")
+SAN_FLAGS = [
+    "--offload-arch=gfx950", "-std=c++17", "-fPIC", "-shared",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+    "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math",
+    "-Xarch_host", "-O1", "-Xarch_host", "-g", "-Xarch_host", "-fno-omit-frame-pointer",
+    # each sanitizer flag right after -Xarch_host: host code only
+    "-Xarch_host", "-fsanitize=" + "address", "-Xarch_host", "-fsanitize=" + "undefined",
+    "-Xarch_device", "-O1",
+]
+
+
+def sanitizer_runtime():
+    """The clang AddressSanitizer runtime that a process loading SAN_LIB must preload."""
+    import glob
+    libs = sorted(glob.glob(os.path.join(os.path.dirname(os.path.dirname(HIPCC)), "llvm", "lib", "clang", "*", "lib",
+                                         "linux", "libclang_rt.asan-x86_64.so")))
+    return libs[-1] if libs else None
+
+
+def build(verbose=False, extra_flags=(), sanitize=False):
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *extra_flags, "-I", os.path.join(HERE, "..", "include"), "-o", tmp, *srcs]
+    dst = SAN_LIB if sanitize else LIB
+    os.makedirs(os.path.dirname(dst), exist_ok=True)
+    tmp = dst + ".tmp"
+    flags = SAN_FLAGS if sanitize else FLAGS
+    cmd = [HIPCC, *flags, *extra_flags, "-I", os.path.join(HERE, "..", "include"), "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -37,10 +64,9 @@ def build(verbose=False, extra_flags=()):
         raise RuntimeError("hipcc failed:\n" + out)
     if verbose and out.strip():
         print(out)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, dst)
+    return dst
 
 
 if __name__ == "__main__":
-    build(verbose="-v" in sys.argv)
-    print(LIB)
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))
