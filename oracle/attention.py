@@ -169,6 +169,95 @@ def attend_rows_online(rows, q_rows, k_deq, v_codes, s_v, scale, Lq, Lk, causal,
     return acc / l[:, None], m * np.log(2.0) + np.log(l)
 
 
+def rounding_slack(rows, q_rows, k_deq, v_codes, s_v, scale, Lq, Lk, causal,
+                   q_orig_rows=None, k_orig=None, v_orig=None, sel_row=None, v_deq=None):
+    """Per-row, per-column bound [R, d] on how far O moves when probability roundings that lie within the
+    FP32 evaluation error of a rounding midpoint go to the other neighbour.
+
+    The pages keep the softmax in FP32 ("MpFA QK4V8" section 3.3); `attend_rows` evaluates it in float64.
+    A computation in FP32 reaches the rounded value (E4M3 of P' w_c, E4M3 of 448 P', bf16 of P') from an
+    argument that differs from the float64 one by a relative amount of at most
+        eps_rc = ln 2 * dX_rc + 2^-22 + 2^-24,   u = 2^-24,
+        dX_rc = log2(e) * scale * (d / 8) u sum_i |q_ri| |k_ci| + 4 u |X_rc| + u |X_rc - r_rj|.
+    The rounding model: the d products are exact in FP32 (4-, 8- and 16-bit operands) and are summed by
+    matrix-core steps of 16 products that round at most twice each (d / 8 roundings along any path); the
+    score-to-log2 factor carries up to 3 roundings (scale, log2(e), tensor scales) and the shifted argument
+    one more; then two units in the last place for the exponential and one for the fold factor. Where the rounding of the argument times (1 - eps) or (1 + eps) differs from the
+    float64 rounding, both neighbours are correct results. Each such element adds its larger rounding
+    difference, times the absolute values of its V row as the tile's T uses them, weighted as in step 4:
+        slack_r = (1 / D_r) sum_j 2^(r_rj - m_r) sum_c delta_rc |V_c|.
+    The denominator D uses the unrounded P' and moves only by the evaluation error itself.
+    """
+    rows = np.asarray(rows)
+    off = Lk - Lq
+    u = 2.0 ** -24
+    d = (v_codes if v_deq is None else v_deq).shape[1]
+    vq_vals = e4m3_decode(v_codes) if v_deq is None else None
+    ms, ls, Ss = [], [], []
+    for j in _row_tiles(rows, Lq, Lk, causal):
+        cs = np.arange(j * TILE, (j + 1) * TILE)
+        unmasked = np.ones((len(rows), TILE), dtype=bool) if not causal else (cs[None, :] <= rows[:, None] + off)
+        sel = bool(sel_row[j]) if sel_row is not None else False
+        qq, kk = (q_orig_rows, k_orig[cs]) if sel else (q_rows, k_deq[cs])
+        S = scale * (qq @ kk.T)
+        A = np.abs(qq) @ np.abs(kk).T
+        X = np.where(unmasked, S * np.log2(np.e), -np.inf)
+        has = unmasked.any(axis=1)
+        r = np.where(has, np.ceil(X.max(axis=1, initial=-np.inf)), 0.0)
+        P = np.where(unmasked, np.exp2(X - r[:, None]), 0.0)
+        Xf = np.where(unmasked, X, 0.0)
+        dX = np.log2(np.e) * scale * (d / 8) * u * A + 4 * u * np.abs(Xf) + u * np.abs(Xf - r[:, None])
+        eps = np.log(2.0) * dX + 2.0 ** -22 + 2.0 ** -24
+        if sel:
+            rnd, arg, vabs, unit = bf16_round, P, np.abs(v_orig[cs]), 1.0
+        elif v_deq is not None:
+            rnd, arg, vabs, unit = (lambda x: e4m3_decode(e4m3_encode(x))), E4M3_MAX * P, np.abs(v_deq[cs]), 1.0 / E4M3_MAX
+        else:
+            e = fold_exponent(float(np.max(s_v[cs])))
+            w = s_v[cs].astype(np.float64) * 2.0 ** -e
+            rnd, arg, vabs, unit = (lambda x: e4m3_decode(e4m3_encode(x))), P * w[None, :], np.abs(vq_vals[cs]), 2.0 ** e
+        mid = rnd(arg)
+        delta = np.maximum(np.abs(rnd(arg * (1 - eps)) - mid), np.abs(rnd(arg * (1 + eps)) - mid))
+        delta = np.where(unmasked, delta, 0.0)
+        ms.append(np.where(has, r, -np.inf))
+        ls.append(P.sum(axis=1))
+        Ss.append(unit * (delta @ vabs))
+    M = np.stack(ms, axis=0)
+    mrow = M.max(axis=0)
+    f = np.exp2(M - mrow[None, :])
+    D = (f * np.stack(ls, axis=0)).sum(axis=0)
+    return (f[:, :, None] * np.stack(Ss, axis=0)).sum(axis=0) / D[:, None]
+
+
+def prefill_rounding_slack(q_deq, k_deq, v_codes, s_v, causal, scale=None, q_orig=None, k_orig=None, v_orig=None,
+                           bitmap=None, rows=None, heads=None, v_deq=None):
+    """`rounding_slack` over a batch, with the arguments and layout of `attention_prefill`; returns
+    float64 [B, Hq, R, d]."""
+    B, Hq, Lq, d = q_deq.shape
+    Hkv, Lk = k_deq.shape[1], k_deq.shape[2]
+    group = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    rows = np.arange(Lq) if rows is None else np.asarray(rows)
+    heads = [(b, h) for b in range(B) for h in range(Hq)] if heads is None else heads
+    out = np.zeros((B, Hq, len(rows), d))
+    qtile = rows // TILE
+    for (b, h) in heads:
+        kv = h // group
+        for i in np.unique(qtile):
+            sel_idx = np.nonzero(qtile == i)[0]
+            rr = rows[sel_idx]
+            out[b, h, sel_idx] = rounding_slack(
+                rr, q_deq[b, h, rr], k_deq[b, kv], None if v_codes is None else v_codes[b, kv],
+                None if s_v is None else s_v[b, kv], scale, Lq, Lk, causal,
+                q_orig_rows=None if q_orig is None else q_orig[b, h, rr],
+                k_orig=None if k_orig is None else k_orig[b, kv],
+                v_orig=None if v_orig is None else v_orig[b, kv],
+                sel_row=bitmap[b, h, i] if bitmap is not None else None,
+                v_deq=None if v_deq is None else v_deq[b, kv])
+    return out
+
+
 def attention_prefill(q_deq, k_deq, v_codes, s_v, causal, scale=None,
                       q_orig=None, k_orig=None, v_orig=None, bitmap=None,
                       rows=None, heads=None, round_p=True, v_deq=None):

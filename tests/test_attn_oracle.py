@@ -211,3 +211,135 @@ def test_v4_bruteforce_and_online_causal_offset_with_selection():
                                      q_orig_rows=q[0, h, rows], k_orig=k[0, 0], v_orig=v[0, 0],
                                      sel_row=bitmap[0, h, 0], tile_order=[2, 0, 1], v_deq=vd[0, 0])
         assert np.abs(on - O[0, h]).max() <= 1e-6 * np.abs(O[0, h]).max()     # O is float32
+
+
+# ---- rounding slack: the allowance for probability roundings that are ties within FP32 evaluation error
+
+def _one_row_case(sv_vals, x=None, d=16, seed=3):
+    """One query row and one 128-key tile (not causal, scale 1): S_c = x_c / log2(e), so X_c = x_c."""
+    rng = np.random.default_rng(seed)
+    x = np.zeros(128) if x is None else np.asarray(x, np.float64)
+    q = np.zeros((1, d)); q[0, 0] = 1.0
+    k = np.zeros((128, d)); k[:, 0] = x / np.log2(np.e)
+    codes = rng.integers(0, 0x7e, size=(128, d)).astype(np.uint8)     # finite E4M3 codes, both signs below
+    codes |= (rng.integers(0, 2, size=(128, d)) * 0x80).astype(np.uint8)
+    sv = np.ones(128, np.float32)
+    sv[:len(sv_vals)] = sv_vals
+    return q, k, codes, sv
+
+
+def test_rounding_slack_is_zero_away_from_ties():
+    # P' = 1 for every key and w = s_v (e = 0): 448, 176 and 1 are E4M3 values, nothing is near a midpoint
+    q, k, codes, sv = _one_row_case([448.0, 176.0])
+    sl = A.rounding_slack(np.array([0]), q, k, codes, sv, 1.0, 1, 128, False)
+    assert sl.shape == (1, 16) and np.all(sl == 0.0)
+
+
+def test_rounding_slack_single_fp8_tie_equals_the_flip():
+    # Two tiles. Tile 0: X = 0 (P' = 1), V scales 1792, 736 and 1 give e = 2 and w = 448, 184, 0.25, where
+    # 184 is the midpoint of the E4M3 neighbours 176 and 192 (ties to even: 192). Tile 1: X = 3 everywhere,
+    # so the row reference is 3 and tile 0 weighs 2^-3. The slack must be exactly the change of O when that
+    # one probability takes the other neighbour, by the plain formula.
+    d = 16
+    rng = np.random.default_rng(3)
+    q = np.zeros((1, d)); q[0, 0] = 1.0
+    k = np.zeros((256, d)); k[128:, 0] = 3.0 / np.log2(np.e)
+    codes = rng.integers(0, 0x7e, size=(256, d)).astype(np.uint8) | (rng.integers(0, 2, size=(256, d)) * 0x80).astype(np.uint8)
+    sv = np.ones(256, np.float32); sv[0] = 1792.0; sv[1] = 736.0
+    O, _ = A.attend_rows(np.array([0]), q, k, codes, sv, 1.0, 1, 256, False)
+    vals = np.vectorize(bf.e4m3_value)(codes).astype(np.float64)      # E4M3 values from the table
+    ph0 = np.full(128, 0.25); ph0[0] = 448.0; ph0[1] = 192.0           # E4M3(P' w), tile 0 (times 2^2)
+    ph1 = np.ones(128)                                                 # tile 1: P' = 1, w = 1 (e = 0)
+    D = 2.0 ** -3 * 128 + 128
+    num = 2.0 ** -3 * 4.0 * (ph0 @ vals[:128]) + ph1 @ vals[128:]
+    assert np.allclose(O[0], num / D, rtol=0, atol=1e-12)
+    flip = 2.0 ** -3 * 4.0 * 16.0 * np.abs(vals[1]) / D
+    sl = A.rounding_slack(np.array([0]), q, k, codes, sv, 1.0, 1, 256, False)
+    assert np.allclose(sl[0], flip, rtol=1e-12, atol=0) and flip.max() > 0
+
+
+def test_rounding_slack_bf16_and_4bit_v_ties():
+    # selected tile: P'_1 = 0.75 + 2^-9 (midpoint of the bf16 neighbours 0.75 and 0.75 + 2^-8), reached
+    # through 2^(X - r) to within a float64 rounding; 4-bit V: 448 P'_1 = 184 (an E4M3 midpoint)
+    for kind, target, lo, hi in (("bf16", 0.75 + 2.0 ** -9, 0.75, 0.75 + 2.0 ** -8),
+                                 ("v4", 184.0 / 448.0, 176.0 / 448.0, 192.0 / 448.0)):
+        x = np.zeros(128); x[1] = np.log2(target)                      # r = 0 (key 0 has X = 0)
+        q, k, codes, sv = _one_row_case([], x=x)
+        rng = np.random.default_rng(5)
+        vrow = rng.standard_normal((128, 16))
+        P = np.exp2(x)
+        if kind == "bf16":
+            sl = A.rounding_slack(np.array([0]), q * 0, k * 0, codes, sv, 1.0, 1, 128, False, q_orig_rows=q,
+                                  k_orig=k, v_orig=vrow, sel_row=np.array([True]))
+            flip = np.abs(hi - lo) * np.abs(vrow[1]) / P.sum()
+        else:
+            sl = A.rounding_slack(np.array([0]), q, k, None, None, 1.0, 1, 128, False, v_deq=vrow)
+            flip = (hi - lo) * np.abs(vrow[1]) / P.sum()
+        assert np.allclose(sl[0], flip, rtol=1e-9, atol=0), kind
+
+
+def _fp32_prefill_rows(rows, qd, kd, vc, sv, scale, Lq, Lk, causal):
+    """The quantized-tile computation of O evaluated in float32 (scores, the log2 factor, exponentials and
+    fold products), merged exactly; also returns how many E4M3 probability codes differ from float64's."""
+    f32 = np.float32
+    vals = np.vectorize(bf.e4m3_value)(vc).astype(np.float64)
+    enc = np.vectorize(bf.e4m3_encode)
+    dec = np.vectorize(bf.e4m3_value)
+    off = Lk - Lq
+    terms, flips = [], 0
+    for j in range(Lk // 128):
+        cs = np.arange(128 * j, 128 * j + 128)
+        un = np.ones((len(rows), 128), bool) if not causal else cs[None, :] <= rows[:, None] + off
+        if not un.any():
+            continue
+        S = (qd[rows].astype(f32) @ kd[cs].astype(f32).T) * f32(scale * np.log2(np.e))
+        X = np.where(un, S.astype(np.float64), -np.inf)
+        r = np.ceil(X.max(axis=1))
+        P = np.where(un, np.exp2((X - r[:, None]).astype(f32)).astype(f32), f32(0)).astype(np.float64)
+        e = A.fold_exponent(float(sv[cs].max()))
+        w = sv[cs].astype(np.float64) * 2.0 ** -e
+        Ph = dec(enc((P * w[None, :]).astype(f32).astype(np.float64)))
+        X64 = np.where(un, scale * (qd[rows] @ kd[cs].T) * np.log2(np.e), -np.inf)
+        r64 = np.ceil(X64.max(axis=1))
+        Ph64 = dec(enc(np.where(un, np.exp2(X64 - r64[:, None]), 0.0) * w[None, :]))
+        flips += int(np.sum(Ph * 2.0 ** r[:, None] != Ph64 * 2.0 ** r64[:, None]))
+        terms.append((r, P.sum(axis=1), 2.0 ** e * (Ph @ vals[cs])))
+    m = np.max([t[0] for t in terms], axis=0)
+    num, den = 0.0, 0.0
+    for r, l, T in terms:
+        f = np.exp2(r - m)
+        num, den = num + f[:, None] * T, den + f * l
+    return num / den[:, None], flips
+
+
+def test_rounding_slack_covers_an_fp32_evaluation():
+    # Ties planted where they matter: for 32 rows, the per-token V scale of the row's largest-probability
+    # key in tile 0 is set so that P' w lands on an E4M3 midpoint (to within the float32 rounding of the
+    # scale). A float32 evaluation then rounds some of them the other way; the oracle's O plus its slack
+    # must still cover the result, and the test must have seen such flips.
+    cfg = W.C1.scaled(Hq=1, Hkv=1, Lq=128, Lk=256, causal=False)
+    _, _, _, qd, kd, vc, sv = _prepare(cfg)
+    qd, kd, vc, sv = qd[0, 0], kd[0, 0], vc[0, 0], sv[0, 0].copy()
+    scale, rows = 1 / np.sqrt(128), np.arange(128)
+    X = scale * (qd @ kd[:128].T) * np.log2(np.e)
+    P = np.exp2(X - np.ceil(X.max(axis=1))[:, None])
+    e = A.fold_exponent(float(sv[:128].max()))
+    table = np.array(sorted({bf.e4m3_value(c) for c in range(0x7f)}))
+    mids = (table[1:] + table[:-1]) / 2
+    planted = set()
+    for row in range(0, 128, 4):
+        c = int(np.argmax(P[row]))
+        pw = P[row, c] * float(sv[c]) * 2.0 ** -e
+        mid = mids[np.argmin(np.abs(mids - pw))]
+        s_new = np.float32(mid / P[row, c] * 2.0 ** e)
+        if c in planted or s_new > sv[:128].max():
+            continue
+        sv[c] = s_new
+        planted.add(c)
+    assert A.fold_exponent(float(sv[:128].max())) == e and len(planted) >= 16
+    O, _ = A.attend_rows(rows, qd, kd, vc, sv, scale, 128, 256, False)
+    sl = A.rounding_slack(rows, qd, kd, vc, sv, scale, 128, 256, False)
+    O32, flips = _fp32_prefill_rows(rows, qd, kd, vc, sv, scale, 128, 256, False)
+    dif = np.abs(O32 - O)
+    assert flips >= 1 and dif.max() > 1e-3 * np.abs(O).max()        # the flips move O well past noise
+    assert np.all(dif <= sl + 1e-5 * np.abs(O).max())
