@@ -258,7 +258,7 @@ def attn_fwd(q, k, v, causal, fmt, Hq, Hkv, Lq, Lk, d, B=1, bitmap=None, q_bf16=
     """Prefill attention from quantized operands (dicts as returned by quantize()).
 
     q/k hold MXFP4, NVFP4 or MXFP8 codes and scales; v holds FP8 per-token codes and scales
-    (v_fmt FA4_FP8_TOKEN) or 4-bit V (v_fmt FA4_MXFP4_KEYS, MXFP4 Q/K only, no bitmap).
+    (v_fmt FA4_FP8_TOKEN) or 4-bit V (v_fmt FA4_MXFP4_KEYS, MXFP4 Q/K only; selected tiles read v_bf16).
     Returns (o [B, Hq, Lq, d] float32, lse [B, Hq, Lq] float32 or None).
     """
     v4 = v_fmt == FA4_MXFP4_KEYS

@@ -1100,6 +1100,11 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
       FA4_TILE_STEP(true, false, kt, nullptr, nullptr, v16, hsv);
     }
   }
+  if constexpr (V4) {
+    // 4-bit V: the quantized tiles' P^ carried a factor 448 (their sums did not); bf16 tiles carry none
+#pragma unroll
+    for (int i = 0; i < NDB; i++) acc[i] *= 1.0f / 448.0f;
+  }
   if (SEL) {
     // ---- selected tiles from the bf16 originals
     for (int kt = 0; kt < (CAUSAL ? last : kt_end); kt++) {
@@ -1119,7 +1124,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
 #undef FA4_TILE_STEP
   // ---------------- epilogue: O = O_acc / l, LSE = m ln2 + ln l
   const float l = lsum + shfl_xor_f(lsum, 32);
-  const float fin = (V4 ? 1.0f / 448.0f : 1.0f) / l;     // 4-bit V: P^ carried a factor 448
+  const float fin = 1.0f / l;
   float *orow = a.o + (bhq * a.Lq + qrow) * D;
 #pragma unroll
   for (int mb = 0; mb < NDB; mb++)
@@ -1630,15 +1635,19 @@ static hipError_t allow_lds() {
                              hipFuncAttributeMaxDynamicSharedMemorySize, AttnLds<D, QF, SEL>::BYTES);
 }
 
-// MXFP4 Q/K with 4-bit V (d = 128, no bitmap)
-static hipError_t launch_attn_v4(const AttnArgs &x, bool causal, hipStream_t s) {
+// MXFP4 Q/K with 4-bit V (d = 128)
+template <bool CAUSAL, bool SEL>
+static hipError_t launch_attn_v4_t(const AttnArgs &x, hipStream_t s) {
   dim3 grid((unsigned)((int64_t)(x.Lq / 128) * x.Hq * x.B));
-  hipError_t e = causal ? allow_lds<128, FA4_MXFP4, true, false, true>() : allow_lds<128, FA4_MXFP4, false, false, true>();
+  hipError_t e = allow_lds<128, FA4_MXFP4, CAUSAL, SEL, true>();
   if (e != hipSuccess) return e;
-  const size_t l0 = AttnLds<128, FA4_MXFP4, false>::BYTES;
-  if (causal) hipLaunchKernelGGL((attn_fwd_kernel<128, FA4_MXFP4, true, false, true>), grid, dim3(ATT_THREADS), l0, s, x);
-  else hipLaunchKernelGGL((attn_fwd_kernel<128, FA4_MXFP4, false, false, true>), grid, dim3(ATT_THREADS), l0, s, x);
+  constexpr size_t lds_bytes = AttnLds<128, FA4_MXFP4, SEL>::BYTES;
+  hipLaunchKernelGGL((attn_fwd_kernel<128, FA4_MXFP4, CAUSAL, SEL, true>), grid, dim3(ATT_THREADS), lds_bytes, s, x);
   return hipGetLastError();
+}
+static hipError_t launch_attn_v4(const AttnArgs &x, bool causal, bool sel, hipStream_t s) {
+  if (causal) return sel ? launch_attn_v4_t<true, true>(x, s) : launch_attn_v4_t<true, false>(x, s);
+  return sel ? launch_attn_v4_t<false, true>(x, s) : launch_attn_v4_t<false, false>(x, s);
 }
 
 template <int D, int QF>
@@ -1672,7 +1681,7 @@ hipError_t launch_attn(const fa4_attn_args *p, hipStream_t s) {
   x.o = p->o; x.lse = p->lse;
   if (x.B == 0 || x.Hq == 0 || x.Lq == 0) return hipSuccess;
   const bool causal = p->causal != 0, sel = p->bitmap != nullptr;
-  if (p->v_fmt == FA4_MXFP4_KEYS) return launch_attn_v4(x, causal, s);
+  if (p->v_fmt == FA4_MXFP4_KEYS) return launch_attn_v4(x, causal, sel, s);
   if (p->fmt == FA4_MXFP4) {
     if (p->d == 64) return launch_attn_t<64, FA4_MXFP4>(x, causal, false, s);
     return launch_attn_t<128, FA4_MXFP4>(x, causal, sel, s);

@@ -226,8 +226,7 @@ fa4_status fa4_attn_fwd(const fa4_attn_args *a, void *stream) {
   const bool v4 = a->v_fmt == FA4_MXFP4_KEYS;
   REQUIRE(v4 || a->v_fmt == 0 || a->v_fmt == FA4_FP8_TOKEN, FA4_ERR_UNSUPPORTED, "attn: V format %d", a->v_fmt);
   if (v4)
-    REQUIRE(a->fmt == FA4_MXFP4 && a->d == 128 && !a->bitmap, FA4_ERR_UNSUPPORTED,
-            "attn: 4-bit V needs MXFP4 Q/K, d=128 and no tile selection");
+    REQUIRE(a->fmt == FA4_MXFP4 && a->d == 128, FA4_ERR_UNSUPPORTED, "attn: 4-bit V needs MXFP4 Q/K and d=128");
   if (a->B == 0 || a->Lq == 0) return ok();
   if (v4)
     REQUIRE(a->q_codes && a->q_scales && a->k_codes && a->k_scales && a->v_codes && a->v_block_scales && a->o,

@@ -216,10 +216,10 @@ fa4_status fa4_select_tiles(const float *q_norm2, const float *k_norm2, int32_t 
  * bitmap is given); bitmap [B][Hq][Lq/128][Lk/128] or NULL; o [B][Hq][Lq][d] float; lse [B][Hq][Lq]
  * float or NULL. Requirements: d = 128 (or 64 for MXFP4 without a bitmap); Lq, Lk multiples of 128;
  * Lq <= Lk when causal; Hq % Hkv == 0; every pointer 16-byte aligned.
- * 4-bit V (v_fmt = FA4_MXFP4_KEYS; MXFP4 Q/K, d = 128, no bitmap): v_codes [B][Hkv][d][Lk/2] and
- * v_block_scales as fa4_quantize_blockscaled's FA4_MXFP4_KEYS output; v_scales and v_fold_* are not read.
- * Quantized tiles then take P^ = E4M3(448 P') and T = (1/448) sum_c P^ v^_c with the dequantized 4-bit
- * values v^ (FP4 V^T times FP8 P^T in one block-scaled MFMA).
+ * 4-bit V (v_fmt = FA4_MXFP4_KEYS; MXFP4 Q/K, d = 128): v_codes [B][Hkv][d][Lk/2] and v_block_scales as
+ * fa4_quantize_blockscaled's FA4_MXFP4_KEYS output; v_scales and v_fold_* are not read. Quantized tiles
+ * then take P^ = E4M3(448 P') and T = (1/448) sum_c P^ v^_c with the dequantized 4-bit values v^ (FP4
+ * V^T times FP8 P^T in one block-scaled MFMA); selected tiles (with a bitmap) read v_bf16 as usual.
  */
 typedef struct {
   int32_t fmt;                                  /* FA4_MXFP4, FA4_NVFP4 or FA4_MXFP8 (Q and K) */

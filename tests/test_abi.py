@@ -183,10 +183,11 @@ def test_attention_rejects_before_launch():
     assert call(_attn(v_codes=264)) == fa4.FA4_ERR_ALIGN
     assert call(_attn(softmax_scale=0.0)) == fa4.FA4_ERR_SHAPE
     assert call(_attn(Lq=0)) == fa4.FA4_OK
-    # 4-bit V: MXFP4 Q/K, d = 128, no bitmap; its E8M0 scales replace v_scales and the fold data
+    # 4-bit V: MXFP4 Q/K, d = 128; its E8M0 scales replace v_scales and the fold data
     v4 = dict(v_fmt=fa4.FA4_MXFP4_KEYS, v_scales=None, v_fold_w=None, v_fold_scale=None, v_block_scales=256)
     assert call(_attn(v_fmt=7)) == fa4.FA4_ERR_UNSUPPORTED
-    assert call(_attn(**v4, bitmap=256, q_bf16=256, k_bf16=256, v_bf16=256)) == fa4.FA4_ERR_UNSUPPORTED
+    assert call(_attn(**v4, bitmap=256)) == fa4.FA4_ERR_NULL            # selection needs the bf16 originals
+    assert call(_attn(**v4, bitmap=256, q_bf16=256, k_bf16=256, v_bf16=256, Lq=0)) == fa4.FA4_OK
     assert call(_attn(**v4, fmt=fa4.FA4_NVFP4, q_tscale=256, k_tscale=256)) == fa4.FA4_ERR_UNSUPPORTED
     assert call(_attn(**{**v4, "v_block_scales": None})) == fa4.FA4_ERR_NULL
     assert call(_attn(**{**v4, "v_block_scales": 260})) == fa4.FA4_ERR_ALIGN

@@ -185,6 +185,21 @@ def test_v4_noncausal_gqa_offset(fa4):
     _check_full(fa4, W.C1_V4.scaled(Hq=4, Hkv=2, Lq=256, Lk=768), seed=1)
 
 
+@pytest.mark.parametrize("select", [(5, 100), (25, 100), (100, 100)], ids=["sel5", "sel25", "all"])
+def test_v4_with_selection(fa4, select):
+    # quantized tiles through 4-bit V (their P^ carries 448), selected tiles through bf16 V (no 448)
+    _check_full(fa4, W.C1_V4.scaled(Hq=2, Hkv=2, Lq=512, Lk=512), select=select)
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "noncausal"])
+def test_v4_with_selection_gqa_offset(fa4, causal):
+    _check_full(fa4, W.C1_V4.scaled(Hq=4, Hkv=2, Lq=256, Lk=768, causal=causal), select=(10, 100))
+
+
+def test_full_size_prefill_4k_v4_selection(fa4):
+    _sampled(fa4, W.C1_V4, heads=[(0, 3), (0, 30)], nrows=64, select=(5, 100))
+
+
 def test_full_size_prefill_4k_v4(fa4):
     _sampled(fa4, W.C1_V4, heads=[(0, 0), (0, 21)], nrows=96)
 
