@@ -231,8 +231,10 @@ __device__ __forceinline__ v8h row_shl_v8h(v8h v) {
   return __builtin_bit_cast(v8h, x);
 }
 
+// NVFP4 caches: three waves per SIMD (at most 168 VGPRs; the few values that do not fit spill); the
+// MXFP4 path keeps two, where the spills it would need cost more than the extra wave brings.
 template <int FMT, int PF>
-__global__ void __launch_bounds__(DEC_THREADS) decode_split_kernel(DecArgs a) {
+__global__ void __launch_bounds__(DEC_THREADS, FMT == FA4_NVFP4 ? 3 : 2) decode_split_kernel(DecArgs a) {
   __shared__ float part[DEC_SLOTS][4][DEC_PART];
   // Workgroup order: (sequence, key head) fastest, split slowest. Workgroups are handed to the 8 XCDs
   // round-robin, so every XCD gets the same mix of sequences (with 8 key heads, one key head each,

@@ -24,7 +24,7 @@ hipError_t launch_decode(const fa4_decode_args *a, void *ws, hipStream_t s);
 // MLA geometry of fa4_decode_paged: latent row width (key), value width, query heads.
 constexpr int MLA_D = 576, MLA_DV = 512, MLA_H = 16;
 constexpr int DEC_SPLIT_KEYS = 2048;   // keys per workgroup of the GQA decode (one split)
-constexpr int MLA_PAGES = 32;          // pages (64-key tiles) per workgroup of the MLA decode
+constexpr int MLA_PAGES = 40;          // pages (64-key tiles) per workgroup of the MLA decode
 size_t decode_mla_workspace_bytes(const fa4_decode_args *a);
 hipError_t launch_decode_mla(const fa4_decode_args *a, void *ws, hipStream_t s);
 

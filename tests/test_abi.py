@@ -242,11 +242,11 @@ def test_decode_rejects_before_launch():
 
 def test_mla_decode_rejects_before_launch():
     call = lambda a, ws=512, n=1 << 30: fa4.lib.fa4_decode_paged(ctypes.byref(a), ws, n, None)
-    mla = dict(fmt=fa4.FA4_MXFP4, d=576, d_v=512, Hq=16, Hkv=1, max_pages=40, q1_tscale=None, q2_tscale=None,
+    mla = dict(fmt=fa4.FA4_MXFP4, d=576, d_v=512, Hq=16, Hkv=1, max_pages=60, q1_tscale=None, q2_tscale=None,
                k_tscale=None, v_tscale=None, v_codes=None, v_scales=None)
     a = _dec(**mla)
     need = fa4.lib.fa4_decode_workspace_bytes(ctypes.byref(a))
-    assert need == 4 * 2 * 16 * 514 * 4                     # B x ceil(40 / 32) splits x heads x (m, l, O)
+    assert need == 4 * 2 * 16 * 514 * 4                     # B x ceil(60 / 40) splits x heads x (m, l, O)
     assert call(a, ws=512, n=need - 1) == fa4.FA4_ERR_WORKSPACE
     assert call(a, ws=520, n=need) == fa4.FA4_ERR_ALIGN
     assert call(_dec(**{**mla, "fmt": fa4.FA4_NVFP4})) == fa4.FA4_ERR_UNSUPPORTED
