@@ -130,6 +130,12 @@ def test_nvfp4_head_pairs_xcd_order(fa4):
     _check_full(fa4, W.C4.scaled(Hq=32, Hkv=8, Lq=256, Lk=512), select=(5, 100))
 
 
+@pytest.mark.parametrize("hkv", [2, 4], ids=["fallback_order", "xcd_order"])
+def test_nvfp4_head_pairs_two_batches(fa4, hkv):
+    # B = 2: batch and key head ordered without (2 x 2 key heads) and with (2 x 4 = 8) the XCD grouping
+    _check_full(fa4, W.C4.scaled(B=2, Hq=2 * hkv, Hkv=hkv, Lq=256, Lk=512), select=(10, 100))
+
+
 @pytest.mark.parametrize("hq", [2, 6], ids=["mha", "group3"])
 def test_nvfp4_odd_groups(fa4, hq):
     _check_full(fa4, W.C4.scaled(Hq=hq, Hkv=2, Lq=256, Lk=768), select=(5, 100))
