@@ -479,14 +479,11 @@ __device__ __forceinline__ int v_tile_scale_code(const float *vfs, int64_t bhk, 
   return (int)((__float_as_uint(uniform_load(vfs, bhk * nk + kt)) >> 23) & 0xffu);
 }
 
-// A selected tile from the bf16 originals for this wave's 32 queries: S^T = K Q^T and O^T += V^T P^T on
-// bf16 MFMAs with the same online softmax (P' = 2^(S cs - r) in fp32, the tile weight 2^kB applied to P
-// before its rounding to bf16). qb: this lane's bf16 Q operand (d = 16 s + 8 hh .. + 7 for step s); K and
-// V rows in LDS as 16-bit rows of stride H16_RS.
-template <bool MASK>
-__device__ __forceinline__ void bf16_tile(const v8bf *qb, const uint8_t *k16, const uint8_t *v16, const LaneOff &lo,
-                                          int kt, int hh, int qpos, float cs, float &m, float &lsum, v16f *acc) {
-  v16f S[4];
+// A selected tile from the bf16 originals for this wave's 32 queries, in three steps: S^T = K Q^T on the
+// bf16 MFMA (bf16_qk), the online-softmax step with P' = 2^(S cs - r) in fp32 and its rounding to bf16
+// after the tile weight 2^kB (bf16_probs), and O^T += V^T P^T on the bf16 MFMA (bf16_pv). qb: this lane's
+// bf16 Q operand (d = 16 s + 8 hh .. + 7 for step s); K and V rows in LDS as 16-bit rows of stride H16_RS.
+__device__ __forceinline__ void bf16_qk(const v8bf *qb, const uint8_t *k16, const LaneOff &lo, v16f S[4]) {
   // one key block at a time (the scheduling barrier keeps the compiler from holding all 32 K operands)
 #pragma unroll
   for (int kb = 0; kb < 4; kb++) {
@@ -499,27 +496,35 @@ __device__ __forceinline__ void bf16_tile(const v8bf *qb, const uint8_t *k16, co
     S[kb] = sx;
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (MASK) mask_tile(S, kt, hh, qpos);
+}
+// The tile weight 2^kB goes into the exponent (2^(S cs - r + kB) = P' 2^kB, the sum then already carries
+// it); P' 2^kB is rounded to bf16 by the hardware conversion (nearest even), two values per instruction.
+// pb[kb][p]: keys 32 kb + 16 p .. (the PV operand order).
+__device__ __forceinline__ void bf16_probs(v16f S[4], float cs, float &m, float &lsum, v16f *acc, v8bf pb[4][2]) {
   float rr0;
   const int kB = tile_weight<4>(tile_reference(S, cs), m, lsum, acc, rr0);
-  const int kBc = kB < -127 ? -127 : kB;
+  const float sh = kB < -127 ? -INFINITY : (float)kB - rr0;     // below 2^-127 the tile adds nothing
   float ts[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int kb = 0; kb < 4; kb++)
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][i], cs, -rr0));
-      ts[kb] += p;
-      S[kb][i] = p;
+    for (int p = 0; p < 2; p++) {
+      float pv[8];
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        pv[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kb][8 * p + j], cs, sh));
+        ts[kb] += pv[j];
+      }
+      pb[kb][p] = (v8bf){(__bf16)pv[0], (__bf16)pv[1], (__bf16)pv[2], (__bf16)pv[3],
+                         (__bf16)pv[4], (__bf16)pv[5], (__bf16)pv[6], (__bf16)pv[7]};
     }
+  lsum += (ts[0] + ts[1]) + (ts[2] + ts[3]);
+}
+__device__ __forceinline__ void bf16_pv(const v8bf pb[4][2], const uint8_t *v16, const LaneOff &lo, v16f *acc) {
 #pragma unroll
   for (int kb = 0; kb < 4; kb++)
 #pragma unroll
-    for (int p = 0; p < 2; p++) {
-      v8s pbs;
-#pragma unroll
-      for (int j = 0; j < 8; j++) pbs[j] = (short)float_to_bf16_bits(__builtin_ldexpf(S[kb][8 * p + j], kBc));
-      const v8bf pb = __builtin_bit_cast(v8bf, pbs);
+    for (int p = 0; p < 2; p++)
 #pragma unroll
       for (int mb = 0; mb < 4; mb++) {
         v4s rr[2];
@@ -528,10 +533,18 @@ __device__ __forceinline__ void bf16_tile(const v8bf *qb, const uint8_t *k16, co
           rr[v] = lds_tr16(v16 + lo.v16 + (32 * kb + 16 * p + 8 * v) * H16_RS + 64 * mb);
         // whole-vector reinterpretation (inserting bit-cast elements one at a time miscompiles)
         const v8bf vop = __builtin_bit_cast(v8bf, (v8s)__builtin_shufflevector(rr[0], rr[1], 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb, acc[mb], 0, 0, 0);
+        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[kb][p], acc[mb], 0, 0, 0);
       }
-    }
-  lsum += __builtin_ldexpf((ts[0] + ts[1]) + (ts[2] + ts[3]), kB);
+}
+template <bool MASK>
+__device__ __forceinline__ void bf16_tile(const v8bf *qb, const uint8_t *k16, const uint8_t *v16, const LaneOff &lo,
+                                          int kt, int hh, int qpos, float cs, float &m, float &lsum, v16f *acc) {
+  v16f S[4];
+  bf16_qk(qb, k16, lo, S);
+  if (MASK) mask_tile(S, kt, hh, qpos);
+  v8bf pb[4][2];
+  bf16_probs(S, cs, m, lsum, acc, pb);
+  bf16_pv(pb, v16, lo, acc);
 }
 
 // One 128-key tile for this wave's 32 queries: S^T = K Q^T, softmax step, O^T += V^T P^T.
@@ -544,13 +557,7 @@ __device__ __forceinline__ void tile_step(const AttnArgs &a, const LaneOff &lo, 
                                           const uint8_t *ksc, const uint8_t *k16, const uint8_t *vq,
                                           const uint8_t *v16, const float *svs, float &m, float &lsum, v16f *acc) {
   constexpr int NDB = D / 32;
-  if (sel) {
-    v8bf qb[8];
-#pragma unroll
-    for (int s = 0; s < 8; s++) qb[s] = *reinterpret_cast<const v8bf *>(a.qb + (bhq * a.Lq + qrow) * D + 16 * s + 8 * hh);
-    bf16_tile<MASK>(qb, k16, v16, lo, kt, hh, qrow + off, cs_b, m, lsum, acc);
-    return;
-  }
+  static_assert(!sel, "selected tiles take their own pass");
   v16f S[4];
   if (QF == FA4_MXFP4) {
 #pragma unroll
@@ -672,16 +679,6 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
   for (int i = 0; i < NDB; i++) acc[i] = (v16f){};
 
   auto is_sel = [&](int kt) -> bool { return SEL && uniform_load(a.bitmap, (bhq * nq + qt) * nk + kt) != 0; };
-  auto copy_bf16 = [&](int kt) {
-    const int64_t krow0 = bhk * a.Lk + (int64_t)kt * 128;
-    for (int c = tid; c < 128 * (D / 8); c += ATT_THREADS) {     // 16-byte chunks of bf16 rows
-      const int r = c / (D / 8), j = c % (D / 8);
-      const v4i kx = *reinterpret_cast<const v4i *>(a.kb + (krow0 + r) * D + 8 * j);
-      const v4i vx = *reinterpret_cast<const v4i *>(a.vb + (krow0 + r) * D + 8 * j);
-      *reinterpret_cast<v4i *>(k16 + r * H16_RS + 16 * j) = kx;
-      *reinterpret_cast<v4i *>(v16 + r * H16_RS + 16 * j) = vx;
-    }
-  };
 // One tile step; MASKV and SELV must be constants. With Lq and Lk multiples of 128 the only tile that
 // crosses the causal diagonal is the last one, so loops run MASKV = false and the diagonal tile is peeled.
 #define FA4_TILE_STEP(MASKV, SELV, KT, KC, KS, VC, W)                                                         \
@@ -1105,20 +1102,68 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < NDB; i++) acc[i] *= 1.0f / 448.0f;
   }
-  if (SEL) {
-    // ---- selected tiles from the bf16 originals
-    for (int kt = 0; kt < (CAUSAL ? last : kt_end); kt++) {
-      if (!is_sel(kt)) continue;          // uniform per workgroup
-      __syncthreads();
-      copy_bf16(kt);
-      __syncthreads();
-      FA4_TILE_STEP(false, true, kt, nullptr, nullptr, nullptr, nullptr);
+  if constexpr (SEL && D == 128) {
+    // ---- selected tiles from the bf16 originals. Their K and V rows come by direct global->LDS loads into
+    // padded 16-bit rows (a lane whose 16 bytes fall on a row's padding loads the row's first chunk again):
+    // the next selected tile's K while this tile's softmax and PV run, its V while the next tile's QK^T
+    // runs. The bf16 Q operand is read once (and waited for before the first tile load is issued).
+    v8bf qb[8];
+#pragma unroll
+    for (int s = 0; s < 8; s++) qb[s] = *reinterpret_cast<const v8bf *>(a.qb + (bhq * a.Lq + qrow) * D + 16 * s + 8 * hh);
+#pragma unroll
+    for (int s = 0; s < 8; s++) {
+      v4i t = __builtin_bit_cast(v4i, qb[s]);
+      asm volatile("" : "+v"(t));
+      qb[s] = __builtin_bit_cast(v8bf, t);
     }
-    if (CAUSAL && is_sel(last)) {
+    const uint32_t lds_a =
+        __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t *)lds);
+    constexpr int NL = L::K16 / 1024;          // 34 wave-loads of 1 KB per tensor: 9 for waves 0, 1, 8 for 2, 3
+    auto issue16 = [&](const uint16_t *src, int kt, uint32_t dst) __attribute__((always_inline)) {
+      const uint8_t *g = reinterpret_cast<const uint8_t *>(src + (bhk * a.Lk + (int64_t)kt * 128) * 128);
+      for (int e = wave; e < NL; e += 4) {
+        const uint32_t o = 1024u * e + 16u * lane;
+        const uint32_t row = o / H16_RS, c = (o - row * H16_RS) >> 4;
+        dma16_nw(g, row * 256 + 16 * (c < 16 ? c : 0), dst + 1024 * e);
+      }
+    };
+    auto wait_all_but_one_tensor = [&]() __attribute__((always_inline)) {   // this wave's older loads
+      if (wave < 2)
+        asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    };
+    auto next_sel = [&](int t) -> int {
+      while (t < kt_end && !is_sel(t)) t++;
+      return t;
+    };
+    const uint32_t k_lds = lds_a, v_lds = lds_a + L::K16;
+    __syncthreads();                           // the quantized tiles' buffers are free
+    int u = next_sel(0);
+    if (u < kt_end) {
+      issue16(a.kb, u, k_lds);
+      issue16(a.vb, u, v_lds);
+    }
+    while (u < kt_end) {
+      const int un = next_sel(u + 1);
+      wait_all_but_one_tensor();               // K(u) landed (V(u) may be in flight)
       __syncthreads();
-      copy_bf16(last);
+      v16f S[4];
+      bf16_qk(qb, k16, lo, S);
+      __syncthreads();                         // every wave is done with K(u)
+      if (un < kt_end) issue16(a.kb, un, k_lds);
+      if (CAUSAL && u == last) mask_tile_rt(S, u, hh, qrow + off);
+      v8bf pb[4][2];
+      bf16_probs(S, cs_b, m, lsum, acc, pb);
+      if (un < kt_end)
+        wait_all_but_one_tensor();             // V(u) landed (K(un) may be in flight)
+      else
+        wait_vmem();
       __syncthreads();
-      FA4_TILE_STEP(true, true, last, nullptr, nullptr, nullptr, nullptr);
+      bf16_pv(pb, v16, lo, acc);
+      __syncthreads();                         // every wave is done with V(u)
+      if (un < kt_end) issue16(a.vb, un, v_lds);
+      u = un;
     }
   }
 #undef FA4_TILE_STEP
