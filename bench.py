@@ -57,6 +57,7 @@ import workloads as W  # noqa: E402
 METRIC = "prefill attn TFLOP/s + decode KV GB/s, as % of MXFP4-MFMA / HBM peak"
 MXFP4_PEAK_TFLOPS = 10100.0          # dense MFMA, FP4/FP6
 FP8_PEAK_TFLOPS = 5000.0             # dense MFMA, FP8 (the peak of an MXFP8 QK^T workload)
+BF16_PEAK_TFLOPS = 2500.0            # dense MFMA, bf16 / fp16
 HBM_PEAK_GBS = 8000.0
 COPY_BYTES = 1 << 30                 # calibration copy: reads and writes this many bytes
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
@@ -247,8 +248,29 @@ def prefill_error(cfg, q, k, v, outs):
 
 # ---------------------------------------------------------------------------------------------- prefill
 
+def visited_tiles(cfg):
+    """128 x 128 (query, key) tiles the attention visits (those holding an unmasked pair)."""
+    nq, nk, off = cfg.Lq // 128, cfg.Lk // 128, cfg.Lk - cfg.Lq
+    per_head = sum(min(nk, (off + 128 * i + 127) // 128 + 1) if cfg.causal else nk for i in range(nq))
+    return per_head * cfg.B * cfg.Hq
+
+
+def mixed_ceiling_tflops(cfg, bf16_frac):
+    """The dense-MFMA ceiling of the workload's mix of products: half of the flops are QK^T at the Q/K
+    format's rate (MXFP4 10.1 PF and MXFP8 5.0 PF, both with native block scales; NVFP4, whose E4M3
+    scales on 16 elements the matrix cores do not take, at the fp16 rate 2.5 PF), half PV at the V/P
+    rate (FP8 5.0 PF; 4-bit V times FP8 P also runs at the FP8 rate), and the selected tiles' share of
+    both at the bf16 rate (2.5 PF)."""
+    qk = {"mxfp4": MXFP4_PEAK_TFLOPS, "nvfp4": BF16_PEAK_TFLOPS, "mxfp8": FP8_PEAK_TFLOPS}[cfg.qk_fmt]
+    pv = FP8_PEAK_TFLOPS
+    f = bf16_frac
+    per_tflop = 0.5 * ((1 - f) / qk + f / BF16_PEAK_TFLOPS) + 0.5 * ((1 - f) / pv + f / BF16_PEAK_TFLOPS)
+    return 1.0 / per_tflop
+
+
 def time_prefill(fa4, cfg, steps, warmup, quick=False, error=True):
-    """Times one prefill workload: (ms per whole step, ms per attention launch, error dict or None).
+    """Times one prefill workload: (ms per whole step, ms per attention launch, error dict or None,
+    fraction of visited tiles computed in bf16).
     The step loop has no events inside it; the attention kernel is timed on its own loop of
     back-to-back launches over the same inputs."""
     q, k, v = (t.cuda() for t in W.prefill_inputs(cfg))
@@ -259,6 +281,7 @@ def time_prefill(fa4, cfg, steps, warmup, quick=False, error=True):
     _warm(run.run, warmup, quick)
     step_ms = _time_loop(run.run, steps)
     attn_ms = _time_loop(run.attention, steps)
+    bf16_frac = float(run.counts.sum().item()) / visited_tiles(cfg) if select is not None else 0.0
     err = None
     if error:
         run.run()
@@ -274,11 +297,12 @@ def time_prefill(fa4, cfg, steps, warmup, quick=False, error=True):
             err["selection_gap_recovered"] = 1.0 - e1 / e0
     del run, q, k, v
     torch.cuda.empty_cache()
-    return step_ms, attn_ms, err
+    return step_ms, attn_ms, err, bf16_frac
 
 
 def prefill_record(fa4, cfg, args, headline=False):
-    step_ms, attn_ms, err = time_prefill(fa4, cfg, args.steps, args.warmup, args.quick, not args.no_error)
+    step_ms, attn_ms, err, bf16_frac = time_prefill(fa4, cfg, args.steps, args.warmup, args.quick, not args.no_error)
+    mixed = mixed_ceiling_tflops(cfg, bf16_frac)
     flops = prefill_flops(cfg)
     achieved = flops / (attn_ms * 1e-3) / 1e12
     peak = FP8_PEAK_TFLOPS if cfg.qk_fmt == "mxfp8" else MXFP4_PEAK_TFLOPS
@@ -291,7 +315,10 @@ def prefill_record(fa4, cfg, args, headline=False):
                    "bf16_tiles": "5%" if cfg.select else "none", "algorithmic_flops": flops},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": recorded_traffic(kname) if kname in KERNEL_SOURCES else None,
-                     "kernel": kname, "kernel_ms": attn_ms},
+                     "kernel": kname, "kernel_ms": attn_ms,
+                     "mixed_ceiling": {"peak": mixed, "frac": achieved / mixed, "bf16_tile_fraction": bf16_frac,
+                                       "note": "QK^T and PV each at their operand formats' dense MFMA rate"}},
+        "other_kernels_ms": step_ms - attn_ms,
         "error_vs_unquantized": err,
     }
     print(f"[bench] prefill {cfg.name}: step {step_ms:.4f} ms, attention {attn_ms:.4f} ms "
