@@ -231,10 +231,21 @@ __device__ __forceinline__ v8h row_shl_v8h(v8h v) {
   return __builtin_bit_cast(v8h, x);
 }
 
-// NVFP4 caches: three waves per SIMD (at most 168 VGPRs; the few values that do not fit spill); the
-// MXFP4 path keeps two, where the spills it would need cost more than the extra wave brings.
+// the 2 values of nibble pair i (constant after unrolling) of w as bf16 with scale sc
+__device__ __forceinline__ uint32_t cvt_bf16_fp4_sel(uint32_t w, float sc, int i) {
+  switch (i) {
+    case 0: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0));
+    case 1: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1));
+    case 2: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2));
+    default: return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3));
+  }
+}
+
+// Three waves per SIMD (at most 168 VGPRs), with no spills: the V scale shuffles share one address
+// register and the MXFP4 path expands V one pair of d values at a time. (A spill in the tile loop
+// costs more than the third wave brings.)
 template <int FMT, int PF>
-__global__ void __launch_bounds__(DEC_THREADS, FMT == FA4_NVFP4 ? 3 : 2) decode_split_kernel(DecArgs a) {
+__global__ void __launch_bounds__(DEC_THREADS, 3) decode_split_kernel(DecArgs a) {
   __shared__ float part[DEC_SLOTS][4][DEC_PART];
   // Workgroup order: (sequence, key head) fastest, split slowest. Workgroups are handed to the 8 XCDs
   // round-robin, so every XCD gets the same mix of sequences (with 8 key heads, one key head each,
@@ -284,13 +295,14 @@ __global__ void __launch_bounds__(DEC_THREADS, FMT == FA4_NVFP4 ? 3 : 2) decode_
     c2 = ck * a.q2t[bq];
   }
   // V scale redistribution: (key j of this lane, block n / 2) sits in lane 2 kk_j + n / 8, byte
-  // (n / 2) % 4, kk_j the key's row within its quarter
-  // (MXFP4: the key's 4-byte scale row sits in lane kk_j, byte n / 4)
-  int vs_addr[8];
-#pragma unroll
-  for (int j = 0; j < 8; j++)
-    vs_addr[j] = FMT == FA4_NVFP4 ? 4 * (2 * (16 * (j >> 2) + 4 * g + (j & 3)) + (n >> 3))
-                                  : 4 * (16 * (j >> 2) + 4 * g + (j & 3));
+  // (n / 2) % 4, kk_j = 16 (j / 4) + 4 g + j % 4 the key's row within its quarter (MXFP4: the key's
+  // 4-byte scale row sits in lane kk_j, byte n / 4). The lane shuffle's byte address is one per-lane
+  // base plus a constant per j, which goes into the instruction's offset field, so the eight
+  // addresses take one register (keeping the NVFP4 kernel within three waves per SIMD without spills).
+  const int vs_base = FMT == FA4_NVFP4 ? 4 * (8 * g + (n >> 3)) : 16 * g;
+  auto vs_addr = [&](int j) -> int {
+    return vs_base + (FMT == FA4_NVFP4 ? 8 * (16 * (j >> 2) + (j & 3)) : 4 * (16 * (j >> 2) + (j & 3)));
+  };
   const int vs_sh = FMT == FA4_NVFP4 ? 8 * ((n >> 1) & 3) : 8 * (n >> 2);
 
   // Software pipeline over the wave's tiles: the next tile's K is requested as soon as this tile's
@@ -437,8 +449,8 @@ __global__ void __launch_bounds__(DEC_THREADS, FMT == FA4_NVFP4 ? 3 : 2) decode_
           v2h sp[4];
 #pragma unroll
           for (int jp = 0; jp < 4; jp++) {
-            const uint32_t s0 = (uint32_t)__builtin_amdgcn_ds_bpermute(vs_addr[2 * jp], (int)vs[q]);
-            const uint32_t s1 = (uint32_t)__builtin_amdgcn_ds_bpermute(vs_addr[2 * jp + 1], (int)vs[q]);
+            const uint32_t s0 = (uint32_t)__builtin_amdgcn_ds_bpermute(vs_addr(2 * jp), (int)vs[q]);
+            const uint32_t s1 = (uint32_t)__builtin_amdgcn_ds_bpermute(vs_addr(2 * jp + 1), (int)vs[q]);
             sp[jp] = e4m3x2_f16(((s0 >> vs_sh) & 0xffu) | (((s1 >> vs_sh) & 0xffu) << 8));
           }
 #pragma unroll
@@ -446,28 +458,33 @@ __global__ void __launch_bounds__(DEC_THREADS, FMT == FA4_NVFP4 ? 3 : 2) decode_
             acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(expand8s(w[e], sp), pb, acc[e], 0, 0, 0);
         } else {
           // key j's run of 8 d values -> bf16 with its own scale 2^(code - 127); scale code 0 (blocks
-          // below 6 * 2^-127) is taken as 2^-126 so that the conversion's scale stays a normal float
-          uint32_t kw[8][4];
+          // below 6 * 2^-127) is taken as 2^-126 so that the conversion's scale stays a normal float.
+          // Converted one pair of d values (i) at a time, right before the two MFMAs (d = 8 n + 2 i,
+          // 8 n + 2 i + 1) that take them, so that only 8 converted words are live.
+          float sc[8];
 #pragma unroll
           for (int j = 0; j < 8; j++) {
-            const uint32_t sw = (uint32_t)__builtin_amdgcn_ds_bpermute(vs_addr[j], (int)vs[q]);
+            const uint32_t sw = (uint32_t)__builtin_amdgcn_ds_bpermute(vs_addr(j), (int)vs[q]);
             const uint32_t code = (sw >> vs_sh) & 0xffu;
-            const float sc = __uint_as_float((code > 1u ? code : 1u) << 23);
-            kw[j][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(vc[q][j], sc, 0));
-            kw[j][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(vc[q][j], sc, 1));
-            kw[j][2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(vc[q][j], sc, 2));
-            kw[j][3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(vc[q][j], sc, 3));
+            sc[j] = __uint_as_float((code > 1u ? code : 1u) << 23);
           }
-          // 8x8 transpose of 16-bit values: A operand of d = 8 n + e holds keys j = 0..7
 #pragma unroll
-          for (int e = 0; e < 8; e++) {
-            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-            v4i av;
+          for (int i = 0; i < 4; i++) {
+            uint32_t kw[8];
 #pragma unroll
-            for (int jp = 0; jp < 4; jp++)
-              av[jp] = (int)__builtin_amdgcn_perm(kw[2 * jp + 1][e >> 1], kw[2 * jp][e >> 1], sel);
-            acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, av),
-                                                             __builtin_bit_cast(v8bf, pb), acc[e], 0, 0, 0);
+            for (int j = 0; j < 8; j++)
+              kw[j] = cvt_bf16_fp4_sel(vc[q][j], sc[j], i);
+            // 8x8 transpose of 16-bit values: A operand of d = 8 n + e holds keys j = 0..7
+#pragma unroll
+            for (int e = 2 * i; e < 2 * i + 2; e++) {
+              const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+              v4i av;
+#pragma unroll
+              for (int jp = 0; jp < 4; jp++) av[jp] = (int)__builtin_amdgcn_perm(kw[2 * jp + 1], kw[2 * jp], sel);
+              acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, av),
+                                                               __builtin_bit_cast(v8bf, pb), acc[e], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
       }
