@@ -515,6 +515,7 @@ def main():
         "data": "synthetic",
         "config": head["config"],
         "roofline": head["roofline"],
+        "other_kernels_ms": head["other_kernels_ms"],
         "error_vs_unquantized": head["error_vs_unquantized"],
     }
     if not args.no_legs:
