@@ -63,17 +63,15 @@ COPY_BYTES = 1 << 30                 # calibration copy: reads and writes this m
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "fp8_quantized_attention_amd", "csrc")
 # Kernel instantiations whose counters are recorded, with the sources whose change invalidates them.
-# One-head attention kernel: <d, Q/K format (0 MXFP4, 1 NVFP4, 3 MXFP8), causal, selection, 4-bit V>
-# (no selection: 4K causal; MXFP4 with selection: 32K). Two-head kernel of the expanded-K formats
-# (NVFP4, MXFP8 with an even number of query heads per key head): <Q/K format, causal, selection>
-# (the 128K chunked prefill). Decode: <cache format (1 NVFP4, 0 MXFP4), probability format (0 FP8,
-# 1 NVFP4)>.
+# Attention kernel: <d, Q/K format (0 MXFP4, 1 NVFP4, 3 MXFP8), causal, selection, 4-bit V>
+# (MXFP4 without selection: 4K causal; MXFP4 with selection: 32K; NVFP4 with selection: the 128K
+# chunked prefill). Decode: <cache format (1 NVFP4, 0 MXFP4), probability format (0 FP8, 1 NVFP4)>.
 ATTN_SRC = ["attn_fwd.hip", "fa4_device.h"]
 DEC_SRC = ["decode.hip", "fa4_device.h"]
 KERNEL_SOURCES = {
     "attn_fwd_kernel<128, 0, true, false, false>": ATTN_SRC,
     "attn_fwd_kernel<128, 0, true, true, false>": ATTN_SRC,
-    "attn_x8_kernel<1, true, true>": ATTN_SRC,
+    "attn_fwd_kernel<128, 1, true, true, false>": ATTN_SRC,
     "decode_split_kernel<1, 0>": DEC_SRC,
     "decode_split_kernel<0, 0>": DEC_SRC,
     "decode_split_kernel<1, 1>": DEC_SRC,
@@ -87,8 +85,6 @@ def attn_kernel_name(cfg, select):
     """The attention kernel instantiation fa4_attn_fwd launches for this workload."""
     fmt = {"mxfp4": 0, "nvfp4": 1, "mxfp8": 3}[cfg.qk_fmt]
     b = lambda x: "true" if x else "false"   # noqa: E731
-    if cfg.qk_fmt in ("nvfp4", "mxfp8") and cfg.v_fmt != "mxfp4k" and (cfg.Hq // cfg.Hkv) % 2 == 0:
-        return f"attn_x8_kernel<{fmt}, {b(cfg.causal)}, {b(select)}>"
     return f"attn_fwd_kernel<{cfg.d}, {fmt}, {b(cfg.causal)}, {b(select)}, {b(cfg.v_fmt == 'mxfp4k')}>"
 
 

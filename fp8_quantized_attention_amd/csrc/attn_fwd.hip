@@ -28,7 +28,6 @@
 namespace fa4 {
 
 constexpr int ATT_THREADS = 256;
-constexpr int K4_RS = 80;     // LDS row stride (bytes) of 4-bit K codes (64 B + pad, conflict-free b128 reads)
 constexpr int V8_RS = 144;    // LDS row stride of FP8 V rows (128 B + pad)
 constexpr int H16_RS = 272;   // LDS row stride of 16-bit rows (256 B + pad)
 constexpr float LOG2E = 1.4426950408889634f;
@@ -270,16 +269,6 @@ __device__ __forceinline__ float max_lane32(float v) {
   return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
 }
 
-// Block kb of mask_tile_rt, for a limit already made opaque by the caller.
-__device__ __forceinline__ void mask_block_rt(v16f &Skb, int kb, int lim) {
-#pragma unroll
-  for (int i = 0; i < 16; i++) {
-    int m = lim - (32 * kb + 8 * (i / 4) + (i % 4));
-    asm volatile("" : "+v"(m));
-    m >>= 31;
-    Skb[i] = __uint_as_float((__float_as_uint(Skb[i]) & ~(uint32_t)m) | (0xff800000u & (uint32_t)m));
-  }
-}
 __device__ __forceinline__ float block_max(const v16f &Skb) {
   // a balanced tree of 3-input maxima (5 + 2 instructions, depth 3)
   const float a = max3f(Skb[0], Skb[1], Skb[2]), b = max3f(Skb[3], Skb[4], Skb[5]);
@@ -410,36 +399,6 @@ __device__ __forceinline__ void pv_fp8(const v8i pop[2], const uint8_t *vq, cons
   }
 }
 
-// Half t of pv_fp8 for d = 128 (keys 64 t .. 64 t + 63 of an MXFP4-path tile): the pipelined loop issues
-// the two halves as soon as their probabilities are packed.
-__device__ __forceinline__ void pv_fp8_half(const v8i &pop, int t, const uint8_t *vq, const LaneOff &lo, int scA,
-                                            int kBc, v16f *acc) {
-#pragma unroll
-  for (int mb = 0; mb < 4; mb++) {
-    v8i vop;
-#pragma unroll
-    for (int u = 0; u < 4; u++) {
-      const v2i rr = lds_tr8(vq + lo.v[mb] + (64 * t + 32 * (u >> 1) + 16 * (u & 1)) * 128);
-      vop[2 * u] = rr[0];
-      vop[2 * u + 1] = rr[1];
-    }
-    acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, pop, acc[mb], 0, 0, 0, scA, 0, kBc + 127);
-  }
-}
-// Half t of pv_fp4v (4-bit V^T, keys 64 t .. 64 t + 63).
-__device__ __forceinline__ void pv_fp4v_half(const v8i &pop, int t, const uint8_t *vt, const uint8_t *vts, int lane,
-                                             int kBc, v16f *acc) {
-  const int h = lane >> 5;
-#pragma unroll
-  for (int mb = 0; mb < 4; mb++) {
-    const int row = 32 * mb + (lane & 31);
-    const int sw = (int)(*reinterpret_cast<const uint32_t *>(vts + 4 * row) >> (8 * h));
-    const v4i c = *reinterpret_cast<const v4i *>(vt + row * 64 + 16 * ((2 * t + h) ^ kswz<128>(row)));
-    const v8i va = (v8i){c[0], c[1], c[2], c[3], 0, 0, 0, 0};
-    acc[mb] = t == 0 ? __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pop, acc[mb], 4, 0, 0, sw, 0, kBc + 127)
-                     : __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, pop, acc[mb], 4, 0, 2, sw, 0, kBc + 127);
-  }
-}
 
 // O^T += V^T P^T for a tile of 4-bit V (MXFP4, E8M0 scales along the keys): V^T rows (one value of d,
 // 128 keys) sit in LDS as 64 code bytes each, 16-byte pieces XOR-swizzled as K's. The A operand of MFMA t
@@ -536,20 +495,9 @@ __device__ __forceinline__ void bf16_pv(const v8bf pb[4][2], const uint8_t *v16,
         acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pb[kb][p], acc[mb], 0, 0, 0);
       }
 }
-template <bool MASK>
-__device__ __forceinline__ void bf16_tile(const v8bf *qb, const uint8_t *k16, const uint8_t *v16, const LaneOff &lo,
-                                          int kt, int hh, int qpos, float cs, float &m, float &lsum, v16f *acc) {
-  v16f S[4];
-  bf16_qk(qb, k16, lo, S);
-  if (MASK) mask_tile(S, kt, hh, qpos);
-  v8bf pb[4][2];
-  bf16_probs(S, cs, m, lsum, acc, pb);
-  bf16_pv(pb, v16, lo, acc);
-}
-
-// One 128-key tile for this wave's 32 queries: S^T = K Q^T, softmax step, O^T += V^T P^T.
-// MASK: the tile crosses the causal diagonal (keys past the query position get -inf).
-// sel: a selected tile, computed from the bf16 originals (QK^T and PV on bf16 MFMA).
+// One quantized 128-key tile for this wave's 32 queries: S^T = K Q^T, softmax step, O^T += V^T P^T.
+// MASK: the tile crosses the causal diagonal (keys past the query position get -inf). sel must be
+// false (selected tiles run in a pass of their own, from the bf16 originals).
 template <int D, int QF, bool MASK, bool sel, bool V4 = false>
 __device__ __forceinline__ void tile_step(const AttnArgs &a, const LaneOff &lo, int kt, int lane, int hh, int col, int qrow,
                                           int off, int64_t bhq, int64_t bhk, int nk, float cs_q, float cs_b,
@@ -1182,497 +1130,6 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
   if (a.lse && hh == 0) a.lse[bhq * a.Lq + qrow] = m * 0.6931471805599453f + logf(l);
 }
 
-// ======================================================================================================
-// Q/K formats whose K tiles are expanded to exact 16-bit values (NVFP4: fp16, MXFP8: bf16), d = 128, for
-// grouped-query attention with an even number of query heads per key head: one workgroup of 8 waves takes
-// the same 128-query tile of two query heads that share a key head (waves 0-3 the first head, waves 4-7 the
-// second), so every K/V tile brought into LDS and every K expansion serves 256 queries.
-//
-// Quantized tiles run software-pipelined with one barrier per tile. Iteration i (tile T_i, whose scores are
-// in registers with their reference) converts T_i's scores to FP8 probabilities block by block while the
-// matrix core computes QK^T of T_{i+1} (its K already expanded) and the two PV halves (the second one goes
-// out at the start of the next iteration); in its last region it expands the raw K of T_{i+2} into the fp16
-// buffer that T_i's K left. Raw K has two staging slots and V three buffers, so the pending PV half reads
-// V(T_{i-1}) from LDS while V(T_{i+1}) is loaded. The tile sequence is the union of both heads' quantized
-// tiles: a wave whose head selected a tile computes its scores and gives it reference -inf, so its
-// probabilities, sum and PV contributions are exact zeros. The selected tiles follow in a second pass, their
-// bf16 K and V double-buffered and prefetched one tile ahead by direct global->LDS loads.
-constexpr int X8_THREADS = 512;
-
-template <int QF>
-struct X8Lds {
-  static constexpr int K16B = 128 * H16_RS;                                   // one expanded K tile
-  static constexpr int RAWC = QF == FA4_MXFP8 ? 128 * 128 : 128 * 64;         // raw K codes of a tile
-  static constexpr int RAWB = RAWC + (QF == FA4_MXFP8 ? 128 * 4 : 128 * 8);   // + block scales
-  static constexpr int VBUF = 128 * 128 + 512 + 16;     // FP8 V rows (XOR-swizzled), w_c, the tile's V scale
-  static constexpr int OFF_RAW = 2 * K16B;
-  static constexpr int OFF_V = OFF_RAW + 2 * RAWB;
-  static constexpr int QBYTES = OFF_V + 3 * VBUF;
-  static constexpr int SBUF = 2 * K16B;                 // a selected tile: bf16 K rows, then bf16 V rows
-  static constexpr int SBYTES = 2 * SBUF;
-  static constexpr int BYTES = QBYTES > SBYTES ? QBYTES : SBYTES;
-};
-
-// One quarter of one K row (item i of 512: row i / 4, 32 values of d from 32 (i % 4)): raw codes and block
-// scales (staging layout: rows of codes, then rows of scales) to exact 16-bit values in the padded row
-// layout.
-template <int QF>
-__device__ __forceinline__ void x8_expand(const uint8_t *raw, uint8_t *k16, int tid) {
-  const int r = tid >> 2, j = tid & 3;
-  uint8_t *dst = k16 + r * H16_RS + 64 * j;
-  if constexpr (QF == FA4_MXFP8) {
-    const v4i c0 = *reinterpret_cast<const v4i *>(raw + r * 128 + 32 * j);
-    const v4i c1 = *reinterpret_cast<const v4i *>(raw + r * 128 + 32 * j + 16);
-    const float sc = mx8_scale_float(raw[X8Lds<QF>::RAWC + r * 4 + j]);      // one E8M0 block of 32
-    *reinterpret_cast<v4i *>(dst) = mx8_expand8(make_uint2((uint32_t)c0[0], (uint32_t)c0[1]), sc);
-    *reinterpret_cast<v4i *>(dst + 16) = mx8_expand8(make_uint2((uint32_t)c0[2], (uint32_t)c0[3]), sc);
-    *reinterpret_cast<v4i *>(dst + 32) = mx8_expand8(make_uint2((uint32_t)c1[0], (uint32_t)c1[1]), sc);
-    *reinterpret_cast<v4i *>(dst + 48) = mx8_expand8(make_uint2((uint32_t)c1[2], (uint32_t)c1[3]), sc);
-  } else {
-    const v4i c = *reinterpret_cast<const v4i *>(raw + r * 64 + 16 * j);
-    const uint32_t sw = *reinterpret_cast<const uint16_t *>(raw + X8Lds<QF>::RAWC + r * 8 + 2 * j);   // two blocks of 16
-    const _Float16 s0 = (_Float16)e4m3_value(sw & 0xffu), s1 = (_Float16)e4m3_value(sw >> 8);
-    *reinterpret_cast<v8h *>(dst) = nv_expand8((uint32_t)c[0], s0);
-    *reinterpret_cast<v8h *>(dst + 16) = nv_expand8((uint32_t)c[1], s0);
-    *reinterpret_cast<v8h *>(dst + 32) = nv_expand8((uint32_t)c[2], s1);
-    *reinterpret_cast<v8h *>(dst + 48) = nv_expand8((uint32_t)c[3], s1);
-  }
-}
-
-// S^T for key block kb of an expanded tile: 8 MFMAs over d (fp16 for NVFP4, bf16 for MXFP8).
-template <int QF>
-__device__ __forceinline__ v16f x8_qk_block(const uint8_t *k16, const LaneOff &lo, int kb, const v8h *qop) {
-  v16f s = (v16f){};
-#pragma unroll
-  for (int st = 0; st < 8; st++) {
-    const v8h kop = *reinterpret_cast<const v8h *>(k16 + lo.k16 + 32 * kb * H16_RS + 32 * st);
-    if constexpr (QF == FA4_MXFP8)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, kop), __builtin_bit_cast(v8bf, qop[st]), s, 0,
-                                                  0, 0);
-    else
-      s = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop, qop[st], s, 0, 0, 0);
-  }
-  return s;
-}
-
-template <int QF, bool CAUSAL, bool SEL>
-__global__ void __launch_bounds__(X8_THREADS, 1) attn_x8_kernel(AttnArgs a) {
-  constexpr int NW = X8_THREADS / 64, NT = X8_THREADS, HP = 2, ER = 1;    // waves, threads, heads, items/thread
-  constexpr int NDB = 4;
-  typedef X8Lds<QF> L;
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const int nq = a.Lq / 128, nk = a.Lk / 128;
-  const int gq = a.Hq / a.Hkv, gp = gq / HP;              // query heads per key head, head groups per key head
-  // Work order as in the 4-wave kernel, over (q-tile, batch, head pair): longest causal rows first, and
-  // all the pairs of one key head on one XCD when the key heads split evenly over the 8 XCDs.
-  int qt, h0, b;
-  {
-    const int Lb = blockIdx.x, nb = a.B * a.Hkv;
-    if (nb % 8 == 0) {
-      const int x = Lb & 7, r = Lb >> 3, per = (nb / 8) * gp;
-      const int level = r / per, rem = r - level * per;
-      const int bhk = x + 8 * (rem / gp);
-      b = bhk / a.Hkv;
-      h0 = (bhk - b * a.Hkv) * gq + HP * (rem % gp);
-      qt = nq - 1 - level;
-    } else {
-      const int np = a.B * (a.Hq / HP);
-      const int level = Lb / np, rem = Lb - level * np;
-      b = rem / (a.Hq / HP);
-      h0 = HP * (rem - b * (a.Hq / HP));
-      qt = nq - 1 - level;
-    }
-  }
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int half = wave >> 2;                              // which head of the pair
-  const int h = h0 + half, kvh = h0 / gq;
-  const int hh = lane >> 5, col = lane & 31;
-  const int qrow = qt * 128 + (wave & 3) * 32 + col;
-  const LaneOff lo = lane_offsets<128>(lane);
-  const int64_t bhq = (int64_t)b * a.Hq + h, bhk = (int64_t)b * a.Hkv + kvh;
-  const int64_t qg = bhq * a.Lq + qrow;
-  const int off = a.Lk - a.Lq;
-
-  // ---- query operand (exact 16-bit values), in registers for the whole quantized pass
-  v8h qop[8];
-  float cs = a.scale * LOG2E;
-  if constexpr (QF == FA4_MXFP8) {
-#pragma unroll
-    for (int s = 0; s < 8; s++) {
-      const uint2 w = *reinterpret_cast<const uint2 *>(a.qc + qg * 128 + 16 * s + 8 * hh);
-      qop[s] = __builtin_bit_cast(v8h, mx8_expand8(w, mx8_scale_float(a.qs[qg * 4 + (s >> 1)])));
-    }
-  } else {
-#pragma unroll
-    for (int s = 0; s < 8; s++) {
-      const uint32_t w = *reinterpret_cast<const uint32_t *>(a.qc + qg * 64 + 8 * s + 4 * hh);
-      qop[s] = nv_expand8(w, (_Float16)e4m3_value(a.qs[qg * 8 + s]));
-    }
-    cs *= a.qt[bhq] * a.kt[bhk];            // the two tensor scales
-  }
-
-  int kt_end = nk;
-  if (CAUSAL) kt_end = min(nk, (off + qt * 128 + 127) / 128 + 1);
-  const int last = kt_end - 1;
-  float m = -INFINITY, lsum = 0.0f;
-  v16f acc[NDB];
-#pragma unroll
-  for (int i = 0; i < NDB; i++) acc[i] = (v16f){};
-
-  // selection bitmaps of the two heads ([B][Hq][nq][nk] bytes)
-  const uint8_t *bm = SEL ? a.bitmap + (((int64_t)b * a.Hq + h0) * nq + qt) * nk : nullptr;
-  const int64_t bm_next = (int64_t)nq * nk;
-  auto sel_of = [&](int t, int hf) -> bool { return SEL && uniform_load(bm, hf * bm_next + t) != 0; };
-  auto next_quant = [&](int t) -> int {       // first tile >= t that one of the heads computes quantized
-    if (SEL)
-      while (t < kt_end && sel_of(t, 0) && sel_of(t, 1)) t++;
-    return t;
-  };
-
-  const uint32_t lds_addr =
-      __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t *)lds);
-  // per-lane byte offsets of the V loads: 8 rows x 128 B per wave-load, 16 / NW per wave, chunks XOR-swizzled
-  constexpr int VL = 16 / NW;
-  uint32_t vo[VL];
-#pragma unroll
-  for (int e = 0; e < VL; e++) {
-    const int r = (wave * VL + e) * 8 + (lane >> 3), p = lane & 7;
-    vo[e] = (uint32_t)(r * 128 + 16 * (p ^ vswz<128>(r)));
-  }
-  const uint32_t so = (uint32_t)(((wave & 1) * 64 + lane) * 4);
-  auto issue_raw = [&](int kt, int slot) __attribute__((always_inline)) {
-    const uint32_t base = lds_addr + L::OFF_RAW + slot * L::RAWB;
-    const int64_t krow0 = bhk * a.Lk + (int64_t)kt * 128;
-    constexpr int KL = L::RAWC / 1024 / NW;            // wave-loads of codes per wave
-    const uint8_t *g = a.kc + krow0 * (QF == FA4_MXFP8 ? 128 : 64);
-#pragma unroll
-    for (int e = 0; e < KL; e++)
-      dma16_nw(g, 1024u * (wave * KL + e) + 16 * lane, base + 1024 * (wave * KL + e));
-    if constexpr (QF == FA4_MXFP8) {      // 512 B of E8M0 scales
-      if (wave >= NW - 2) dma4_nw(a.ks + krow0 * 4, so, base + L::RAWC + 256 * (wave - (NW - 2)));
-    } else {                              // 1 KB of E4M3 scales
-      if (wave == NW - 1) dma16_nw(a.ks + krow0 * 8, 16u * lane, base + L::RAWC);
-    }
-  };
-  auto issue_v = [&](int kt, int buf) __attribute__((always_inline)) {
-    const uint32_t base = lds_addr + L::OFF_V + buf * L::VBUF;
-    const uint8_t *g = a.vc + (bhk * a.Lk + (int64_t)kt * 128) * 128;
-#pragma unroll
-    for (int e = 0; e < VL; e++) dma16_nw(g, vo[e], base + 1024 * (wave * VL + e));
-    if (wave == 2 || wave == 3) dma4_nw(a.vw + bhk * a.Lk + (int64_t)kt * 128, so, base + 16384 + 256 * (wave - 2));
-    if (wave == 1 && lane == 0) dma4_nw(a.vfs + bhk * nk + kt, 0u, base + 16384 + 512);
-  };
-
-  // V buffer 2 starts as zeros: before the first tile the pending PV half multiplies it by zero
-  // probabilities, and zero codes keep that product an exact zero (stale bytes could hold FP8 NaNs).
-  for (int i = tid; i < L::VBUF / 16; i += NT)
-    *reinterpret_cast<v4i *>(lds + L::OFF_V + 2 * L::VBUF + 16 * i) = (v4i){0, 0, 0, 0};
-
-  int t0 = next_quant(0);
-  if (t0 < kt_end) {
-    int t1 = next_quant(t0 + 1);
-    int t2 = t1 < kt_end ? next_quant(t1 + 1) : kt_end;
-    issue_raw(t0, 0);
-    issue_v(t0, 0);
-    if (t1 < kt_end) issue_raw(t1, 1);
-    wait_vmem();
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < ER; e++) x8_expand<QF>(lds + L::OFF_RAW, lds, tid + NT * e);          // K(T_0) into buffer 0
-    __syncthreads();
-    if (t2 < kt_end) issue_raw(t2, 0);
-#pragma unroll
-    for (int e = 0; e < ER; e++) x8_expand<QF>(lds + L::OFF_RAW + L::RAWB, lds + L::K16B, tid + NT * e);   // K(T_1)
-    v16f S[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; kb++) S[kb] = x8_qk_block<QF>(lds, lo, kb, qop);
-    if (CAUSAL && t0 == last) mask_tile_rt(S, t0, hh, qrow + off);
-    float mS = max3f(max3f(block_max(S[0]), block_max(S[1]), block_max(S[2])), block_max(S[3]), block_max(S[3]));
-    mS = max_lane32(mS);
-    if (sel_of(t0, half)) mS = -INFINITY;     // this head computes the tile from bf16
-    float rr0;
-    int kB = tile_weight<NDB>(ceilf(mS * cs), m, lsum, acc, rr0);
-
-    v8i ppend = (v8i){};                      // pending PV half: P^T operand, weight exponent, V scale, V buffer
-    int kpend = 0, spend = 127, vpb = 2;
-    int vb = 0;                               // V buffer of T_i
-    int it = 0;                               // iteration parity: K(T_{i+1}) in buffer (it + 1) & 1
-    int tn = t1, tnn = t2;
-    while (true) {
-      const bool has_next = tn < kt_end;
-      const int t3 = tnn < kt_end ? next_quant(tnn + 1) : kt_end;
-      const int vbn = vb == 2 ? 0 : vb + 1;
-      wait_vmem();
-      __syncthreads();   // K(T_{i+1}) expanded, raw K(T_{i+2}) and V(T_i) landed; K(T_i), raw K(T_{i+1}) and
-                         // V(T_{i-2}) are no longer read
-      if (t3 < kt_end) issue_raw(t3, (it + 1) & 1);
-      if (has_next) issue_v(tn, vbn);
-      const uint8_t *kq = lds + ((it + 1) & 1) * L::K16B;             // K(T_{i+1})
-      const uint8_t *vq = lds + L::OFF_V + vb * L::VBUF;              // V(T_i)
-      const uint8_t *vp = lds + L::OFF_V + vpb * L::VBUF;             // V(T_{i-1}): the pending half
-      const float *svs = reinterpret_cast<const float *>(vq + 16384);
-      const int kBc = kB < -127 ? -127 : kB;
-      const int scA = (int)((*reinterpret_cast<const uint32_t *>(vq + 16384 + 512) >> 23) & 0xffu);
-      const bool diag_next = CAUSAL && tn == last;
-      float ts[4], mp[3];
-      v8i pop[2];
-      // Regions (separated by scheduling barriers): r < 4 converts block r of T_i (VALU); the matrix core runs
-      // the pending PV half (r = 0), QK^T of T_{i+1} for key block r - 1 into the registers block r - 1 has
-      // just freed (r >= 1), and T_i's first PV half split over r = 2, 3. Region 4 takes the row maxima of
-      // T_{i+1}'s blocks 0-2 and expands raw K(T_{i+2}) beside the QK^T of block 3. Each region runs as two
-      // halves (half p: elements 8 p .. 8 p + 7 of the block, d steps 4 p .. 4 p + 3 of the QK^T, half the PV
-      // MFMAs) so that only half of the operands are held at a time. On the last tile the next-tile QK^T and
-      // the expansion read stale (in-bounds) bytes whose results are never used.
-      const uint8_t *rawp = lds + L::OFF_RAW + (it & 1) * L::RAWB;     // raw K(T_{i+2})
-      uint8_t *kdst0 = lds + (it & 1) * L::K16B + (tid >> 2) * H16_RS + 64 * (tid & 3);
-#pragma unroll
-      for (int hr = 0; hr < 10; hr++) {
-        const int r = hr >> 1, p = hr & 1, qb = r - 1;
-        // ---- LDS reads
-        float4 w2[2];
-        if (r < 4) {
-#pragma unroll
-          for (int k = 0; k < 2; k++)
-            w2[k] = *reinterpret_cast<const float4 *>(reinterpret_cast<const uint8_t *>(svs) + lo.w +
-                                                      4 * (32 * r + 8 * (2 * p + k)));
-        }
-        v8h kop[4];
-        if (r >= 1) {
-#pragma unroll
-          for (int k = 0; k < 4; k++)
-            kop[k] = *reinterpret_cast<const v8h *>(kq + lo.k16 + 32 * qb * H16_RS + 32 * (4 * p + k));
-        }
-        const int nv = r == 0 ? 2 : (r == 2 || r == 3) ? 1 : 0;    // PV MFMAs in this half
-        const int mb0 = r == 0 ? 2 * p : r == 2 ? p : 2 + p;
-        const uint8_t *vsrc = r == 0 ? vp : vq;
-        const int t = r == 0 ? 1 : 0;
-        v8i vop[2];
-#pragma unroll
-        for (int j = 0; j < 2; j++) {
-          if (j < nv) {
-#pragma unroll
-            for (int u = 0; u < 4; u++) {
-              const v2i rr = lds_tr8(vsrc + lo.v[mb0 + j] + (64 * t + 32 * (u >> 1) + 16 * (u & 1)) * 128);
-              vop[j][2 * u] = rr[0];
-              vop[j][2 * u + 1] = rr[1];
-            }
-          }
-        }
-        v4i raw_c[ER];
-        uint32_t raw_s[ER];
-        if (r == 4) {
-#pragma unroll
-          for (int e = 0; e < ER; e++) {
-            const int ti = tid + NT * e;                                 // expansion item (row ti / 4)
-            if constexpr (QF == FA4_MXFP8) {
-              raw_c[e] = *reinterpret_cast<const v4i *>(rawp + (ti >> 2) * 128 + 32 * (ti & 3) + 16 * p);
-              raw_s[e] = rawp[L::RAWC + (ti >> 2) * 4 + (ti & 3)];
-            } else {
-              raw_c[e] = *reinterpret_cast<const v4i *>(rawp + (ti >> 2) * 64 + 16 * (ti & 3));
-              raw_s[e] = *reinterpret_cast<const uint16_t *>(rawp + L::RAWC + (ti >> 2) * 8 + 2 * (ti & 3));
-            }
-          }
-        }
-        // ---- VALU
-        if (r < 4) {
-#pragma unroll
-          for (int k = 0; k < 2; k++) {
-            const int a4 = 2 * p + k;
-            const float wv[4] = {w2[k].x, w2[k].y, w2[k].z, w2[k].w};
-            float pw[4];
-#pragma unroll
-            for (int uu = 0; uu < 4; uu++) {
-              const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r][4 * a4 + uu], cs, -rr0));
-              ts[r] = (a4 == 0 && uu == 0) ? pr : ts[r] + pr;
-              pw[uu] = pr * wv[uu];
-            }
-            int x = __builtin_amdgcn_cvt_pk_fp8_f32(pw[0], pw[1], __float_as_int(pw[0]), false);
-            pop[r >> 1][4 * (r & 1) + a4] = __builtin_amdgcn_cvt_pk_fp8_f32(pw[2], pw[3], x, true);
-          }
-        } else if (p == 0) {
-#pragma unroll
-          for (int bb = 0; bb < 3; bb++) {
-            mp[bb] = block_max(S[bb]);
-            asm volatile("" : "+v"(mp[bb]));
-          }
-        }
-        // ---- MFMA
-        if (r == 0) {
-#pragma unroll
-          for (int j = 0; j < 2; j++)
-            acc[mb0 + j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[j], ppend, acc[mb0 + j], 0, 0, 0, spend, 0,
-                                                                           kpend + 127);
-        } else {
-          v16f sx = p == 0 ? (v16f){} : S[qb];
-#pragma unroll
-          for (int k = 0; k < 4; k++) {
-            if constexpr (QF == FA4_MXFP8)
-              sx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, kop[k]),
-                                                           __builtin_bit_cast(v8bf, qop[4 * p + k]), sx, 0, 0, 0);
-            else
-              sx = __builtin_amdgcn_mfma_f32_32x32x16_f16(kop[k], qop[4 * p + k], sx, 0, 0, 0);
-            if (nv == 1 && k == 1)
-              acc[mb0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[0], pop[0], acc[mb0], 0, 0, 0, scA, 0, kBc + 127);
-          }
-          S[qb] = sx;
-        }
-        // ---- expansion of raw K(T_{i+2}) into the buffer K(T_i) left (half p: 16 of this thread's 32 values)
-        if (r == 4) {
-#pragma unroll
-          for (int e = 0; e < ER; e++) {
-            uint8_t *kdst = kdst0 + (NT / 4) * e * H16_RS;               // item tid + NT e: NT / 4 rows further
-            if constexpr (QF == FA4_MXFP8) {
-              const float sc = mx8_scale_float(raw_s[e]);
-              *reinterpret_cast<v4i *>(kdst + 32 * p) = mx8_expand8(make_uint2((uint32_t)raw_c[e][0], (uint32_t)raw_c[e][1]), sc);
-              *reinterpret_cast<v4i *>(kdst + 32 * p + 16) =
-                  mx8_expand8(make_uint2((uint32_t)raw_c[e][2], (uint32_t)raw_c[e][3]), sc);
-            } else {
-              const _Float16 sb = (_Float16)e4m3_value((raw_s[e] >> (8 * p)) & 0xffu);
-              *reinterpret_cast<v8h *>(kdst + 32 * p) = nv_expand8((uint32_t)raw_c[e][2 * p], sb);
-              *reinterpret_cast<v8h *>(kdst + 32 * p + 16) = nv_expand8((uint32_t)raw_c[e][2 * p + 1], sb);
-            }
-          }
-        }
-        // ---- schedule: LDS reads first, then the MFMAs spread through the VALU work
-        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-        if (r == 0) {
-#pragma unroll
-          for (int g = 0; g < 2; g++) {
-            __builtin_amdgcn_sched_group_barrier(0x002, 18, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          }
-        } else if (r == 2 || r == 3) {
-#pragma unroll
-          for (int g = 0; g < 5; g++) {
-            __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          }
-        } else {
-#pragma unroll
-          for (int g = 0; g < 4; g++) {
-            __builtin_amdgcn_sched_group_barrier(0x002, 9, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      ppend = pop[1];
-      kpend = kBc;
-      spend = scA;
-      vpb = vb;
-      lsum += __builtin_ldexpf((ts[0] + ts[1]) + (ts[2] + ts[3]), kB);
-      if (!has_next) break;
-      if (diag_next) {
-        mask_tile_rt(S, tn, hh, qrow + off);
-        mS = max3f(max3f(block_max(S[0]), block_max(S[1]), block_max(S[2])), block_max(S[3]), block_max(S[3]));
-      } else {
-        mS = max3f(max3f(mp[0], mp[1], mp[2]), block_max(S[3]), block_max(S[3]));
-      }
-      mS = max_lane32(mS);
-      if (sel_of(tn, half)) mS = -INFINITY;
-      const float m_old = m;
-      kB = tile_weight<NDB>(ceilf(mS * cs), m, lsum, acc, rr0);
-      if (m != m_old) {            // the reference was raised: the pending half's weight follows it
-        kpend -= (int)(m - m_old);
-        if (kpend < -127) {
-          kpend = -127;
-          ppend = (v8i){};
-        }
-      }
-      tn = tnn;
-      tnn = t3;
-      vb = vbn;
-      it ^= 1;
-    }
-    // the last tile's second PV half
-#pragma unroll
-    for (int mb = 0; mb < 4; mb++) {
-      v8i vop;
-#pragma unroll
-      for (int u = 0; u < 4; u++) {
-        const v2i rr = lds_tr8(lds + L::OFF_V + vpb * L::VBUF + lo.v[mb] + (64 + 32 * (u >> 1) + 16 * (u & 1)) * 128);
-        vop[2 * u] = rr[0];
-        vop[2 * u + 1] = rr[1];
-      }
-      acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop, ppend, acc[mb], 0, 0, 0, spend, 0, kpend + 127);
-    }
-  }
-
-  if constexpr (SEL) {
-    // ---- selected tiles from the bf16 originals: both heads' selections, each wave computing its own head's
-    // tiles; K and V rows arrive by direct loads into padded 16-bit rows (a lane whose 16 bytes fall on a
-    // row's padding loads the row's first chunk again), one tile ahead
-    v8bf qb[8];
-#pragma unroll
-    for (int s = 0; s < 8; s++) qb[s] = *reinterpret_cast<const v8bf *>(a.qb + qg * 128 + 16 * s + 8 * hh);
-    const float cs_b = a.scale * LOG2E;
-    auto next_sel = [&](int t) -> int {
-      while (t < kt_end && !sel_of(t, 0) && !sel_of(t, 1)) t++;
-      return t;
-    };
-    auto issue_bf = [&](int kt, int buf) __attribute__((always_inline)) {
-      const int64_t krow0 = bhk * a.Lk + (int64_t)kt * 128;
-      const uint8_t *gk = reinterpret_cast<const uint8_t *>(a.kb + krow0 * 128);
-      const uint8_t *gv = reinterpret_cast<const uint8_t *>(a.vb + krow0 * 128);
-      const uint32_t base = lds_addr + buf * L::SBUF;
-      constexpr int NL = L::K16B / 1024;                 // 34 wave-loads per tensor
-      for (int e = wave; e < 2 * NL; e += NW) {
-        const int ii = e < NL ? e : e - NL;
-        const uint32_t o = 1024u * ii + 16u * lane;
-        const uint32_t row = o / H16_RS, c = (o - row * H16_RS) >> 4;
-        dma16_nw(e < NL ? gk : gv, row * 256 + 16 * (c < 16 ? c : 0), base + (e < NL ? 0 : L::K16B) + 1024 * ii);
-      }
-    };
-    __syncthreads();                     // every wave is done with the quantized pass's buffers
-    int u = next_sel(0), sb = 0;
-    if (u < kt_end) issue_bf(u, 0);
-    while (u < kt_end) {
-      const int un = next_sel(u + 1);
-      wait_vmem();
-      __syncthreads();                   // tile u landed; the other buffer's tile is consumed
-      if (un < kt_end) issue_bf(un, sb ^ 1);
-      if (sel_of(u, half)) {
-        const uint8_t *k16 = lds + sb * L::SBUF;
-        if (CAUSAL && u == last)
-          bf16_tile<true>(qb, k16, k16 + L::K16B, lo, u, hh, qrow + off, cs_b, m, lsum, acc);
-        else
-          bf16_tile<false>(qb, k16, k16 + L::K16B, lo, u, hh, qrow + off, cs_b, m, lsum, acc);
-      }
-      sb ^= 1;
-      u = un;
-    }
-  }
-
-  // ---------------- epilogue: O = O_acc / l, LSE = m ln2 + ln l
-  const float l = lsum + shfl_xor_f(lsum, 32);
-  const float fin = 1.0f / l;
-  float *orow = a.o + qg * 128;
-#pragma unroll
-  for (int mb = 0; mb < NDB; mb++)
-#pragma unroll
-    for (int a4 = 0; a4 < 4; a4++) {
-      const float4 v = make_float4(acc[mb][4 * a4] * fin, acc[mb][4 * a4 + 1] * fin, acc[mb][4 * a4 + 2] * fin,
-                                   acc[mb][4 * a4 + 3] * fin);
-      *reinterpret_cast<float4 *>(orow + 32 * mb + 8 * a4 + 4 * hh) = v;
-    }
-  if (a.lse && hh == 0) a.lse[qg] = m * 0.6931471805599453f + logf(l);
-}
-
-template <int QF, bool CAUSAL, bool SEL>
-static hipError_t launch_x8_t(const AttnArgs &x, hipStream_t s) {
-  const void *fn = reinterpret_cast<const void *>(&attn_x8_kernel<QF, CAUSAL, SEL>);
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, X8Lds<QF>::BYTES);
-  if (e != hipSuccess) return e;
-  dim3 grid((unsigned)((int64_t)(x.Lq / 128) * x.B * (x.Hq / 2)));
-  hipLaunchKernelGGL((attn_x8_kernel<QF, CAUSAL, SEL>), grid, dim3(X8_THREADS), X8Lds<QF>::BYTES, s, x);
-  return hipGetLastError();
-}
-template <int QF>
-static hipError_t launch_x8(const AttnArgs &x, bool causal, bool sel, hipStream_t s) {
-  if (causal) return sel ? launch_x8_t<QF, true, true>(x, s) : launch_x8_t<QF, true, false>(x, s);
-  return sel ? launch_x8_t<QF, false, true>(x, s) : launch_x8_t<QF, false, false>(x, s);
-}
-
 // Kernels whose LDS exceeds the default dynamic limit are opted in (idempotent, cheap).
 template <int D, int QF, bool CAUSAL, bool SEL, bool V4 = false>
 static hipError_t allow_lds() {
@@ -1731,10 +1188,9 @@ hipError_t launch_attn(const fa4_attn_args *p, hipStream_t s) {
     if (p->d == 64) return launch_attn_t<64, FA4_MXFP4>(x, causal, false, s);
     return launch_attn_t<128, FA4_MXFP4>(x, causal, sel, s);
   }
-  // expanded-K formats: two query heads per workgroup when the heads of each key head pair up
-  const bool pairs = (x.Hq / x.Hkv) % 2 == 0;
-  if (p->fmt == FA4_MXFP8) return pairs ? launch_x8<FA4_MXFP8>(x, causal, sel, s) : launch_attn_t<128, FA4_MXFP8>(x, causal, sel, s);
-  return pairs ? launch_x8<FA4_NVFP4>(x, causal, sel, s) : launch_attn_t<128, FA4_NVFP4>(x, causal, sel, s);
+  // expanded-K formats (NVFP4 -> fp16, MXFP8 -> bf16)
+  if (p->fmt == FA4_MXFP8) return launch_attn_t<128, FA4_MXFP8>(x, causal, sel, s);
+  return launch_attn_t<128, FA4_NVFP4>(x, causal, sel, s);
 }
 
 }  // namespace fa4

@@ -109,29 +109,29 @@ def test_mxfp8_selection_small(fa4):
     _check_full(fa4, W.C1_MX8.scaled(Hq=2, Hkv=2, Lq=1024, Lk=1024, select=True), select=(5, 100))
 
 
-# ---- NVFP4 / MXFP8 with two query heads of one key head per workgroup (an even number of query heads
-# per key head); odd groups take the one-head kernel. The two heads' selections differ, so each head's
-# waves skip the tiles the other head computes in the other precision.
+# ---- NVFP4 / MXFP8 over grouped key heads (one to four query heads per key head), with and without
+# selection (the heads of a group select different tiles), in both work orders (key heads split evenly
+# over the 8 XCDs, and not).
 
 @pytest.mark.parametrize("causal", [True, False], ids=["causal", "noncausal"])
 @pytest.mark.parametrize("select", [None, (5, 100), (25, 100)], ids=["nosel", "sel5", "sel25"])
-def test_nvfp4_head_pairs(fa4, causal, select):
+def test_nvfp4_gqa(fa4, causal, select):
     _check_full(fa4, W.C4.scaled(Hq=4, Hkv=2, Lq=256, Lk=768, causal=causal), select=select)
 
 
 @pytest.mark.parametrize("frac", [0, 90, 100])
-def test_nvfp4_head_pairs_selection_extremes(fa4, frac):
+def test_nvfp4_gqa_selection_extremes(fa4, frac):
     # 100%: no quantized tile at all; 90%: runs of one or two quantized tiles between selected ones
     _check_full(fa4, W.C4.scaled(Hq=4, Hkv=2, Lq=512, Lk=1024), select=(frac, 100))
 
 
-def test_nvfp4_head_pairs_xcd_order(fa4):
-    # 8 key heads (the work order that keeps each key head's pairs on one XCD), two pairs per key head
+def test_nvfp4_gqa_xcd_order(fa4):
+    # 8 key heads (the work order that keeps all query heads of a key head on one XCD), 4 per key head
     _check_full(fa4, W.C4.scaled(Hq=32, Hkv=8, Lq=256, Lk=512), select=(5, 100))
 
 
 @pytest.mark.parametrize("hkv", [2, 4], ids=["fallback_order", "xcd_order"])
-def test_nvfp4_head_pairs_two_batches(fa4, hkv):
+def test_nvfp4_gqa_two_batches(fa4, hkv):
     # B = 2: batch and key head ordered without (2 x 2 key heads) and with (2 x 4 = 8) the XCD grouping
     _check_full(fa4, W.C4.scaled(B=2, Hq=2 * hkv, Hkv=hkv, Lq=256, Lk=512), select=(10, 100))
 
@@ -141,7 +141,7 @@ def test_nvfp4_odd_groups(fa4, hq):
     _check_full(fa4, W.C4.scaled(Hq=hq, Hkv=2, Lq=256, Lk=768), select=(5, 100))
 
 
-def test_mxfp8_head_pairs_selection(fa4):
+def test_mxfp8_gqa_selection(fa4):
     _check_full(fa4, W.C1_MX8.scaled(Hq=4, Hkv=2, Lq=512, Lk=512, select=True), select=(10, 100))
 
 
