@@ -66,7 +66,7 @@ __device__ __forceinline__ v4s lds_tr16(const uint8_t *p) {
 // QK operand reads (16 rows x one chunk per 16 lanes) and the transposed V reads (16 rows x two
 // chunks per instruction) spread over all LDS banks.
 // bf16 tiles (and the fp16 values of NVFP4 K, the bf16 values of MXFP8 K) use 16-bit rows with stride H16_RS in a separate
-// layout [K16 | V] that overlaps the quantized buffers; those tiles are staged synchronously.
+// layout [K16 | V] that overlaps the quantized buffers (the selected tiles' pass runs after the quantized tiles).
 // Q/K formats whose K tiles are expanded to exact 16-bit values in LDS (their block scales are not
 // applied by the MFMA): NVFP4 (fp16) and MXFP8 (bf16).
 template <int QF>
@@ -85,13 +85,19 @@ struct AttnLds {
   static constexpr int PVBUF = 128 * 128 + 512 + 16;
   static constexpr int QBYTES = QF != FA4_MXFP4 ? 0 : D == 128 ? 2 * PKBUF + 2 * PVBUF : 2 * QBUF;
   static constexpr int K16 = 128 * H16_RS;
-  static constexpr int V8 = 128 * V8_RS;                 // NVFP4 tiles' FP8 V rows
+  static constexpr int V8 = 128 * V8_RS;                 // MXFP8 tiles' FP8 V rows
   static constexpr int V16 = 128 * H16_RS;               // selected tiles' bf16 V rows (overlap V8 onwards)
   // staging of the next tile's raw data (NVFP4, MXFP8): K codes, K scales, V codes, fold factors
   static constexpr int SKC = QF == FA4_MXFP8 ? 128 * D : 128 * (D / 2);
   static constexpr int SKS = QF == FA4_MXFP8 ? 128 * (D / 32) : 128 * (D / 16);
   static constexpr int NVSTAGE = SKC + SKS + 128 * D + 512;
-  static constexpr int NBYTES = Expanded<QF>::value ? K16 + V8 + 512 + NVSTAGE : 0;
+  // NVFP4: [K16 | raw K codes and scales of the next tile | two V buffers (FP8 rows, XOR-swizzled as the
+  // MXFP4 path's, then 128 fold factors)], V and fold factors loaded straight into their buffer.
+  // MXFP8: [K16 | V8 | fold factors | staging of the next tile's K codes, K scales, V and fold factors].
+  static constexpr int NVVBUF = 128 * D + 512;
+  static constexpr int NBYTES = QF == FA4_NVFP4   ? K16 + SKC + SKS + 2 * NVVBUF
+                                : QF == FA4_MXFP8 ? K16 + V8 + 512 + NVSTAGE
+                                                  : 0;
   static constexpr int SBYTES = SEL ? K16 + V16 : 0;
   static constexpr int HBYTES = NBYTES > SBYTES ? NBYTES : SBYTES;
   static constexpr int BYTES = QBYTES > HBYTES ? QBYTES : HBYTES;
@@ -169,7 +175,7 @@ struct LaneOff {
   int w;         // fold factors
   int k16;       // 16-bit K rows
   int v16;       // bf16 V rows (transposed 16-bit reads)
-  int v8;        // NVFP4 tiles' FP8 V rows (stride V8_RS)
+  int v8;        // MXFP8 tiles' FP8 V rows (stride V8_RS)
 };
 
 template <int D>
@@ -389,7 +395,7 @@ __device__ __forceinline__ void pv_fp8(const v8i pop[2], const uint8_t *vq, cons
         // source lane (16q + a + 2t'): key 64t + 32(u/2) + 16(u%2) + 8(t'/4) + 4g + t'%4,
         //                              d 32mb + 16(q%2) + 8a
         const int krun = 64 * t + 32 * (u >> 1) + 16 * (u & 1);
-        const v2i rr = QF == FA4_MXFP4 ? lds_tr8(vq + lo.v[mb] + krun * D)
+        const v2i rr = QF != FA4_MXFP8 ? lds_tr8(vq + lo.v[mb] + krun * D)
                                        : lds_tr8(vq + lo.v8 + krun * V8_RS + 32 * mb);
         vop[2 * u] = rr[0];
         vop[2 * u + 1] = rr[1];
@@ -550,9 +556,9 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
   typedef AttnLds<D, QF, SEL> L;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   uint8_t *const k16 = lds;                              // 16-bit K rows, stride H16_RS
-  uint8_t *const v16 = lds + L::K16;                     // bf16 V rows (stride H16_RS) / NVFP4 tiles' FP8 V
-  float *const hsv = reinterpret_cast<float *>(lds + L::K16 + L::V8);    // w_c of NVFP4 tiles
-  uint8_t *const nst = lds + L::K16 + L::V8 + 512;       // NVFP4 staging: [K codes | K scales | V | w]
+  uint8_t *const v16 = lds + L::K16;                     // bf16 V rows (stride H16_RS) / MXFP8 tiles' FP8 V
+  float *const hsv = reinterpret_cast<float *>(lds + L::K16 + L::V8);    // w_c of MXFP8 tiles
+  uint8_t *const nst = lds + L::K16 + L::V8 + 512;       // MXFP8 staging: [K codes | K scales | V | w]
 
   const int nq = a.Lq / 128, nk = a.Lk / 128;
   // Work order: one block per (q-tile, batch, head), dispatched longest causal rows first. Blocks are
@@ -964,35 +970,88 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
       FA4_TILE_STEP(true, false, kt, base, base + L::KC, base + L::KC + L::KS,
                     reinterpret_cast<const float *>(base + L::KC + L::KS + L::VC));
     }
+  } else if constexpr (QF == FA4_NVFP4) {
+    // ---- NVFP4 tiles: the next tile's raw K codes and E4M3 scales come into a staging area, its V and
+    // fold factors straight into the V buffer the previous tile left, by direct global->LDS loads while
+    // the current tile is computed; between two barriers at the start of each tile K is expanded from
+    // the staging area to exact fp16 values (code * s_b).
+    constexpr int RAWK = L::K16, RAWS = RAWK + L::SKC, VBUF0 = RAWS + L::SKS;
+    auto issue_nv4 = [&](int kt, int vb) __attribute__((always_inline)) {
+      const int64_t krow0 = bhk * a.Lk + (int64_t)kt * 128;
+#pragma unroll
+      for (int e = 0; e < 2; e++) {        // K codes: 8 KB, linear 1 KB chunks
+        const int i = wave * 2 + e;
+        dma16(a.kc + krow0 * (D / 2) + 1024 * i + 16 * lane, lds + RAWK + 1024 * i);
+      }
+      if (wave == 0) dma16(a.ks + krow0 * (D / 16) + 16 * lane, lds + RAWS);
+      uint8_t *const vbuf = lds + VBUF0 + vb * L::NVVBUF;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {        // V rows: 8 rows x 128 B per wave-load, chunks XOR-swizzled
+        const int r = (wave * 4 + e) * 8 + (lane >> 3), p = lane & 7;
+        dma16(a.vc + (krow0 + r) * D + 16 * (p ^ vswz<D>(r)), vbuf + 1024 * (wave * 4 + e));
+      }
+      if (wave >= 2) dma4(a.vw + krow0 + 64 * (wave - 2) + lane, vbuf + 128 * D + 256 * (wave - 2));
+    };
+    auto expand_k = [&]() __attribute__((always_inline)) {
+      const int r = tid >> 1, half = tid & 1;
+      const v4i c0 = *reinterpret_cast<const v4i *>(lds + RAWK + r * 64 + 32 * half);
+      const v4i c1 = *reinterpret_cast<const v4i *>(lds + RAWK + r * 64 + 32 * half + 16);
+      const uint32_t sbw = *reinterpret_cast<const uint32_t *>(lds + RAWS + r * 8 + 4 * half);
+#pragma unroll
+      for (int blk = 0; blk < 4; blk++) {
+        const v4i &cc = blk < 2 ? c0 : c1;
+        const uint32_t w0 = (uint32_t)cc[2 * (blk & 1)], w1 = (uint32_t)cc[2 * (blk & 1) + 1];
+        const _Float16 sb = (_Float16)e4m3_value((sbw >> (8 * blk)) & 0xffu);
+        *reinterpret_cast<v8h *>(k16 + r * H16_RS + 2 * (64 * half + 16 * blk)) = nv_expand8(w0, sb);
+        *reinterpret_cast<v8h *>(k16 + r * H16_RS + 2 * (64 * half + 16 * blk + 8)) = nv_expand8(w1, sb);
+      }
+    };
+    auto vbuf_of = [&](int vb) -> uint8_t * { return lds + VBUF0 + vb * L::NVVBUF; };
+    int kt = next_quant(0), vb = 0;
+    if (kt < kt_end) issue_nv4(kt, 0);
+    const int stop = CAUSAL ? last : kt_end;   // the diagonal tile is peeled below
+    while (kt < stop) {
+      const int nxt = next_quant(kt + 1);
+      wait_vmem();
+      __syncthreads();                   // raw K and V of tile kt landed; the previous tile is consumed
+      expand_k();
+      __syncthreads();                   // K of tile kt ready; the staging area is free
+      if (nxt < kt_end) issue_nv4(nxt, vb ^ 1);   // in flight during this tile's compute
+      FA4_TILE_STEP(false, false, kt, nullptr, nullptr, vbuf_of(vb),
+                    reinterpret_cast<const float *>(vbuf_of(vb) + 128 * D));
+      kt = nxt;
+      vb ^= 1;
+    }
+    if (CAUSAL && kt == last) {
+      wait_vmem();
+      __syncthreads();
+      expand_k();
+      __syncthreads();
+      FA4_TILE_STEP(true, false, kt, nullptr, nullptr, vbuf_of(vb), reinterpret_cast<const float *>(vbuf_of(vb) + 128 * D));
+    }
   } else {
-    // ---- NVFP4 / MXFP8 tiles: the next tile's raw codes, scales, V and fold factors are brought into
-    // a staging area by direct global->LDS loads while the current tile is computed; at the start of
-    // each tile K is expanded from there to exact 16-bit values (NVFP4: fp16, MXFP8: bf16) and V
-    // copied next to it.
+    // ---- MXFP8 tiles: the next tile's raw codes, scales, V and fold factors are brought into a staging
+    // area by direct global->LDS loads while the current tile is computed; at the start of each tile K
+    // is expanded from there to exact bf16 values and V copied next to it.
     constexpr int SK = 0, SKS = L::SKC, SV = SKS + L::SKS, SW = SV + 128 * D;
-    constexpr int KROW = QF == FA4_MXFP8 ? D : D / 2;          // code bytes per K row
     auto issue_nv = [&](int kt) __attribute__((always_inline)) {
       const int64_t krow0 = bhk * a.Lk + (int64_t)kt * 128;
-      // K codes (8 or 16 KB), V 16 KB: linear 1 KB chunks spread over the 4 waves
+      // K codes 16 KB, V 16 KB: linear 1 KB chunks spread over the 4 waves
 #pragma unroll
       for (int e = 0; e < L::SKC / 4096; e++) {
         const int i = wave * (L::SKC / 4096) + e;
-        dma16(a.kc + krow0 * KROW + 1024 * i + 16 * lane, nst + SK + 1024 * i);
+        dma16(a.kc + krow0 * D + 1024 * i + 16 * lane, nst + SK + 1024 * i);
       }
 #pragma unroll
       for (int e = 0; e < 4; e++) {
         const int i = wave * 4 + e;
         dma16(a.vc + krow0 * D + 1024 * i + 16 * lane, nst + SV + 1024 * i);
       }
-      if (QF == FA4_MXFP8) {                 // 512 B of E8M0 scales
-        if (wave < 2) dma4(a.ks + krow0 * (D / 32) + 256 * wave + 4 * lane, nst + SKS + 256 * wave);
-      } else if (wave == 0) {
-        dma16(a.ks + krow0 * (D / 16) + 16 * lane, nst + SKS);
-      }
+      if (wave < 2) dma4(a.ks + krow0 * (D / 32) + 256 * wave + 4 * lane, nst + SKS + 256 * wave);   // E8M0
       if (wave >= 2) dma4(a.vw + krow0 + 64 * (wave - 2) + lane, nst + SW + 256 * (wave - 2));
     };
     auto expand_nv = [&]() __attribute__((always_inline)) {
-      if (QF == FA4_MXFP8) {
+      {
         // thread: row tid / 2, d = 64 (tid % 2) .. + 63 (two E8M0 blocks), 8 values per 16-byte store
         const int r = tid >> 1, half = tid & 1;
         const uint8_t *src = nst + SK + r * 128 + 64 * half;
@@ -1002,19 +1061,6 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
         for (int g = 0; g < 8; g++) {
           const uint2 w = *reinterpret_cast<const uint2 *>(src + 8 * g);
           *reinterpret_cast<v4i *>(k16 + r * H16_RS + 2 * (64 * half + 8 * g)) = mx8_expand8(w, g < 4 ? sc0 : sc1);
-        }
-      } else {
-        const int r = tid >> 1, half = tid & 1;
-        const v4i c0 = *reinterpret_cast<const v4i *>(nst + SK + r * 64 + 32 * half);
-        const v4i c1 = *reinterpret_cast<const v4i *>(nst + SK + r * 64 + 32 * half + 16);
-        const uint32_t sbw = *reinterpret_cast<const uint32_t *>(nst + SKS + r * 8 + 4 * half);
-#pragma unroll
-        for (int blk = 0; blk < 4; blk++) {
-          const v4i &cc = blk < 2 ? c0 : c1;
-          const uint32_t w0 = (uint32_t)cc[2 * (blk & 1)], w1 = (uint32_t)cc[2 * (blk & 1) + 1];
-          const _Float16 sb = (_Float16)e4m3_value((sbw >> (8 * blk)) & 0xffu);
-          *reinterpret_cast<v8h *>(k16 + r * H16_RS + 2 * (64 * half + 16 * blk)) = nv_expand8(w0, sb);
-          *reinterpret_cast<v8h *>(k16 + r * H16_RS + 2 * (64 * half + 16 * blk + 8)) = nv_expand8(w1, sb);
         }
       }
 #pragma unroll
