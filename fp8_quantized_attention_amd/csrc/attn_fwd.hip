@@ -28,7 +28,6 @@
 namespace fa4 {
 
 constexpr int ATT_THREADS = 256;
-constexpr int V8_RS = 144;    // LDS row stride of FP8 V rows (128 B + pad)
 constexpr int H16_RS = 272;   // LDS row stride of 16-bit rows (256 B + pad)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LOG2_448 = 8.807354922057604f;   // 4-bit V: 448 P' = 2^(x - r + log2 448)
@@ -85,19 +84,13 @@ struct AttnLds {
   static constexpr int PVBUF = 128 * 128 + 512 + 16;
   static constexpr int QBYTES = QF != FA4_MXFP4 ? 0 : D == 128 ? 2 * PKBUF + 2 * PVBUF : 2 * QBUF;
   static constexpr int K16 = 128 * H16_RS;
-  static constexpr int V8 = 128 * V8_RS;                 // MXFP8 tiles' FP8 V rows
-  static constexpr int V16 = 128 * H16_RS;               // selected tiles' bf16 V rows (overlap V8 onwards)
-  // staging of the next tile's raw data (NVFP4, MXFP8): K codes, K scales, V codes, fold factors
+  static constexpr int V16 = 128 * H16_RS;               // selected tiles' bf16 V rows
+  // expanded-K formats (NVFP4, MXFP8): [K16 | raw K codes and block scales of the next tile | two V
+  // buffers (FP8 rows, XOR-swizzled as the MXFP4 path's, then 128 fold factors)]
   static constexpr int SKC = QF == FA4_MXFP8 ? 128 * D : 128 * (D / 2);
   static constexpr int SKS = QF == FA4_MXFP8 ? 128 * (D / 32) : 128 * (D / 16);
-  static constexpr int NVSTAGE = SKC + SKS + 128 * D + 512;
-  // NVFP4: [K16 | raw K codes and scales of the next tile | two V buffers (FP8 rows, XOR-swizzled as the
-  // MXFP4 path's, then 128 fold factors)], V and fold factors loaded straight into their buffer.
-  // MXFP8: [K16 | V8 | fold factors | staging of the next tile's K codes, K scales, V and fold factors].
-  static constexpr int NVVBUF = 128 * D + 512;
-  static constexpr int NBYTES = QF == FA4_NVFP4   ? K16 + SKC + SKS + 2 * NVVBUF
-                                : QF == FA4_MXFP8 ? K16 + V8 + 512 + NVSTAGE
-                                                  : 0;
+  static constexpr int XVBUF = 128 * D + 512;
+  static constexpr int NBYTES = Expanded<QF>::value ? K16 + SKC + SKS + 2 * XVBUF : 0;
   static constexpr int SBYTES = SEL ? K16 + V16 : 0;
   static constexpr int HBYTES = NBYTES > SBYTES ? NBYTES : SBYTES;
   static constexpr int BYTES = QBYTES > HBYTES ? QBYTES : HBYTES;
@@ -175,7 +168,6 @@ struct LaneOff {
   int w;         // fold factors
   int k16;       // 16-bit K rows
   int v16;       // bf16 V rows (transposed 16-bit reads)
-  int v8;        // MXFP8 tiles' FP8 V rows (stride V8_RS)
 };
 
 template <int D>
@@ -190,7 +182,6 @@ __device__ __forceinline__ LaneOff lane_offsets(int lane) {
     const int kl = 8 * (tp >> 2) + 4 * (q4 >> 1) + (tp & 3);       // key within its 16-key run
 #pragma unroll
     for (int mb = 0; mb < 4; mb++) o.v[mb] = kl * D + 16 * ((2 * mb + (q4 & 1)) ^ vswz<D>(kl)) + 8 * aa;
-    o.v8 = kl * V8_RS + 16 * (q4 & 1) + 8 * aa;
   }
   o.w = 16 * hh;
   o.k16 = col * H16_RS + 16 * hh;
@@ -395,8 +386,7 @@ __device__ __forceinline__ void pv_fp8(const v8i pop[2], const uint8_t *vq, cons
         // source lane (16q + a + 2t'): key 64t + 32(u/2) + 16(u%2) + 8(t'/4) + 4g + t'%4,
         //                              d 32mb + 16(q%2) + 8a
         const int krun = 64 * t + 32 * (u >> 1) + 16 * (u & 1);
-        const v2i rr = QF != FA4_MXFP8 ? lds_tr8(vq + lo.v[mb] + krun * D)
-                                       : lds_tr8(vq + lo.v8 + krun * V8_RS + 32 * mb);
+        const v2i rr = lds_tr8(vq + lo.v[mb] + krun * D);
         vop[2 * u] = rr[0];
         vop[2 * u + 1] = rr[1];
       }
@@ -556,9 +546,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
   typedef AttnLds<D, QF, SEL> L;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   uint8_t *const k16 = lds;                              // 16-bit K rows, stride H16_RS
-  uint8_t *const v16 = lds + L::K16;                     // bf16 V rows (stride H16_RS) / MXFP8 tiles' FP8 V
-  float *const hsv = reinterpret_cast<float *>(lds + L::K16 + L::V8);    // w_c of MXFP8 tiles
-  uint8_t *const nst = lds + L::K16 + L::V8 + 512;       // MXFP8 staging: [K codes | K scales | V | w]
+  uint8_t *const v16 = lds + L::K16;                     // bf16 V rows of the selected tiles (stride H16_RS)
 
   const int nq = a.Lq / 128, nk = a.Lk / 128;
   // Work order: one block per (q-tile, batch, head), dispatched longest causal rows first. Blocks are
@@ -970,45 +958,63 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
       FA4_TILE_STEP(true, false, kt, base, base + L::KC, base + L::KC + L::KS,
                     reinterpret_cast<const float *>(base + L::KC + L::KS + L::VC));
     }
-  } else if constexpr (QF == FA4_NVFP4) {
-    // ---- NVFP4 tiles: the next tile's raw K codes and E4M3 scales come into a staging area, its V and
-    // fold factors straight into the V buffer the previous tile left, by direct global->LDS loads while
-    // the current tile is computed; between two barriers at the start of each tile K is expanded from
-    // the staging area to exact fp16 values (code * s_b).
+  } else {
+    // ---- NVFP4 / MXFP8 tiles: the next tile's raw K codes and block scales come into a staging area, its
+    // V and fold factors straight into the V buffer the previous tile left, by direct global->LDS loads
+    // while the current tile is computed; between two barriers at the start of each tile K is expanded
+    // from the staging area to exact 16-bit values (NVFP4: fp16 code * s_b, MXFP8: bf16 code * 2^e).
     constexpr int RAWK = L::K16, RAWS = RAWK + L::SKC, VBUF0 = RAWS + L::SKS;
-    auto issue_nv4 = [&](int kt, int vb) __attribute__((always_inline)) {
+    auto issue_x = [&](int kt, int vb) __attribute__((always_inline)) {
       const int64_t krow0 = bhk * a.Lk + (int64_t)kt * 128;
 #pragma unroll
-      for (int e = 0; e < 2; e++) {        // K codes: 8 KB, linear 1 KB chunks
-        const int i = wave * 2 + e;
-        dma16(a.kc + krow0 * (D / 2) + 1024 * i + 16 * lane, lds + RAWK + 1024 * i);
+      for (int e = 0; e < L::SKC / 4096; e++) {   // K codes (8 or 16 KB): linear 1 KB chunks
+        const int i = wave * (L::SKC / 4096) + e;
+        dma16(a.kc + krow0 * (L::SKC / 128) + 1024 * i + 16 * lane, lds + RAWK + 1024 * i);
       }
-      if (wave == 0) dma16(a.ks + krow0 * (D / 16) + 16 * lane, lds + RAWS);
-      uint8_t *const vbuf = lds + VBUF0 + vb * L::NVVBUF;
+      if (QF == FA4_MXFP8) {                     // 512 B of E8M0 scales
+        if (wave < 2) dma4(a.ks + krow0 * (D / 32) + 256 * wave + 4 * lane, lds + RAWS + 256 * wave);
+      } else if (wave == 0) {                    // 1 KB of E4M3 scales
+        dma16(a.ks + krow0 * (D / 16) + 16 * lane, lds + RAWS);
+      }
+      uint8_t *const vbuf = lds + VBUF0 + vb * L::XVBUF;
 #pragma unroll
-      for (int e = 0; e < 4; e++) {        // V rows: 8 rows x 128 B per wave-load, chunks XOR-swizzled
+      for (int e = 0; e < 4; e++) {              // V rows: 8 rows x 128 B per wave-load, chunks XOR-swizzled
         const int r = (wave * 4 + e) * 8 + (lane >> 3), p = lane & 7;
         dma16(a.vc + (krow0 + r) * D + 16 * (p ^ vswz<D>(r)), vbuf + 1024 * (wave * 4 + e));
       }
       if (wave >= 2) dma4(a.vw + krow0 + 64 * (wave - 2) + lane, vbuf + 128 * D + 256 * (wave - 2));
     };
     auto expand_k = [&]() __attribute__((always_inline)) {
-      const int r = tid >> 1, half = tid & 1;
-      const v4i c0 = *reinterpret_cast<const v4i *>(lds + RAWK + r * 64 + 32 * half);
-      const v4i c1 = *reinterpret_cast<const v4i *>(lds + RAWK + r * 64 + 32 * half + 16);
-      const uint32_t sbw = *reinterpret_cast<const uint32_t *>(lds + RAWS + r * 8 + 4 * half);
+      const int r = tid >> 1, half = tid & 1;    // thread: row r, d = 64 half .. 64 half + 63
+      if (QF == FA4_MXFP8) {
+        // two E8M0 blocks, 8 values per 16-byte store
+        const uint8_t *src = lds + RAWK + r * 128 + 64 * half;
+        const uint32_t scw = *reinterpret_cast<const uint16_t *>(lds + RAWS + r * 4 + 2 * half);
+        const float sc0 = mx8_scale_float(scw & 0xffu), sc1 = mx8_scale_float(scw >> 8);
 #pragma unroll
-      for (int blk = 0; blk < 4; blk++) {
-        const v4i &cc = blk < 2 ? c0 : c1;
-        const uint32_t w0 = (uint32_t)cc[2 * (blk & 1)], w1 = (uint32_t)cc[2 * (blk & 1) + 1];
-        const _Float16 sb = (_Float16)e4m3_value((sbw >> (8 * blk)) & 0xffu);
-        *reinterpret_cast<v8h *>(k16 + r * H16_RS + 2 * (64 * half + 16 * blk)) = nv_expand8(w0, sb);
-        *reinterpret_cast<v8h *>(k16 + r * H16_RS + 2 * (64 * half + 16 * blk + 8)) = nv_expand8(w1, sb);
+        for (int g = 0; g < 8; g++) {
+          const uint2 w = *reinterpret_cast<const uint2 *>(src + 8 * g);
+          *reinterpret_cast<v4i *>(k16 + r * H16_RS + 2 * (64 * half + 8 * g)) = mx8_expand8(w, g < 4 ? sc0 : sc1);
+        }
+      } else {
+        // four E4M3 blocks of 16 values
+        const v4i c0 = *reinterpret_cast<const v4i *>(lds + RAWK + r * 64 + 32 * half);
+        const v4i c1 = *reinterpret_cast<const v4i *>(lds + RAWK + r * 64 + 32 * half + 16);
+        const uint32_t sbw = *reinterpret_cast<const uint32_t *>(lds + RAWS + r * 8 + 4 * half);
+#pragma unroll
+        for (int blk = 0; blk < 4; blk++) {
+          const v4i &cc = blk < 2 ? c0 : c1;
+          const uint32_t w0 = (uint32_t)cc[2 * (blk & 1)], w1 = (uint32_t)cc[2 * (blk & 1) + 1];
+          const _Float16 sb = (_Float16)e4m3_value((sbw >> (8 * blk)) & 0xffu);
+          *reinterpret_cast<v8h *>(k16 + r * H16_RS + 2 * (64 * half + 16 * blk)) = nv_expand8(w0, sb);
+          *reinterpret_cast<v8h *>(k16 + r * H16_RS + 2 * (64 * half + 16 * blk + 8)) = nv_expand8(w1, sb);
+        }
       }
     };
-    auto vbuf_of = [&](int vb) -> uint8_t * { return lds + VBUF0 + vb * L::NVVBUF; };
+    auto vbuf_of = [&](int vb) -> uint8_t * { return lds + VBUF0 + vb * L::XVBUF; };
+    auto w_of = [&](int vb) -> const float * { return reinterpret_cast<const float *>(vbuf_of(vb) + 128 * D); };
     int kt = next_quant(0), vb = 0;
-    if (kt < kt_end) issue_nv4(kt, 0);
+    if (kt < kt_end) issue_x(kt, 0);
     const int stop = CAUSAL ? last : kt_end;   // the diagonal tile is peeled below
     while (kt < stop) {
       const int nxt = next_quant(kt + 1);
@@ -1016,9 +1022,8 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
       __syncthreads();                   // raw K and V of tile kt landed; the previous tile is consumed
       expand_k();
       __syncthreads();                   // K of tile kt ready; the staging area is free
-      if (nxt < kt_end) issue_nv4(nxt, vb ^ 1);   // in flight during this tile's compute
-      FA4_TILE_STEP(false, false, kt, nullptr, nullptr, vbuf_of(vb),
-                    reinterpret_cast<const float *>(vbuf_of(vb) + 128 * D));
+      if (nxt < kt_end) issue_x(nxt, vb ^ 1);   // in flight during this tile's compute
+      FA4_TILE_STEP(false, false, kt, nullptr, nullptr, vbuf_of(vb), w_of(vb));
       kt = nxt;
       vb ^= 1;
     }
@@ -1027,68 +1032,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
       __syncthreads();
       expand_k();
       __syncthreads();
-      FA4_TILE_STEP(true, false, kt, nullptr, nullptr, vbuf_of(vb), reinterpret_cast<const float *>(vbuf_of(vb) + 128 * D));
-    }
-  } else {
-    // ---- MXFP8 tiles: the next tile's raw codes, scales, V and fold factors are brought into a staging
-    // area by direct global->LDS loads while the current tile is computed; at the start of each tile K
-    // is expanded from there to exact bf16 values and V copied next to it.
-    constexpr int SK = 0, SKS = L::SKC, SV = SKS + L::SKS, SW = SV + 128 * D;
-    auto issue_nv = [&](int kt) __attribute__((always_inline)) {
-      const int64_t krow0 = bhk * a.Lk + (int64_t)kt * 128;
-      // K codes 16 KB, V 16 KB: linear 1 KB chunks spread over the 4 waves
-#pragma unroll
-      for (int e = 0; e < L::SKC / 4096; e++) {
-        const int i = wave * (L::SKC / 4096) + e;
-        dma16(a.kc + krow0 * D + 1024 * i + 16 * lane, nst + SK + 1024 * i);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; e++) {
-        const int i = wave * 4 + e;
-        dma16(a.vc + krow0 * D + 1024 * i + 16 * lane, nst + SV + 1024 * i);
-      }
-      if (wave < 2) dma4(a.ks + krow0 * (D / 32) + 256 * wave + 4 * lane, nst + SKS + 256 * wave);   // E8M0
-      if (wave >= 2) dma4(a.vw + krow0 + 64 * (wave - 2) + lane, nst + SW + 256 * (wave - 2));
-    };
-    auto expand_nv = [&]() __attribute__((always_inline)) {
-      {
-        // thread: row tid / 2, d = 64 (tid % 2) .. + 63 (two E8M0 blocks), 8 values per 16-byte store
-        const int r = tid >> 1, half = tid & 1;
-        const uint8_t *src = nst + SK + r * 128 + 64 * half;
-        const uint32_t scw = *reinterpret_cast<const uint16_t *>(nst + SKS + r * 4 + 2 * half);
-        const float sc0 = mx8_scale_float(scw & 0xffu), sc1 = mx8_scale_float(scw >> 8);
-#pragma unroll
-        for (int g = 0; g < 8; g++) {
-          const uint2 w = *reinterpret_cast<const uint2 *>(src + 8 * g);
-          *reinterpret_cast<v4i *>(k16 + r * H16_RS + 2 * (64 * half + 8 * g)) = mx8_expand8(w, g < 4 ? sc0 : sc1);
-        }
-      }
-#pragma unroll
-      for (int c = tid; c < 128 * (D / 16); c += ATT_THREADS) {
-        const int rr = c / (D / 16), j = c % (D / 16);
-        *reinterpret_cast<v4i *>(v16 + rr * V8_RS + 16 * j) = *reinterpret_cast<const v4i *>(nst + SV + rr * D + 16 * j);
-      }
-      if (tid < 128) hsv[tid] = reinterpret_cast<const float *>(nst + SW)[tid];
-    };
-    int kt = next_quant(0);
-    if (kt < kt_end) issue_nv(kt);
-    const int stop = CAUSAL ? last : kt_end;   // the diagonal tile is peeled below
-    while (kt < stop) {
-      const int nxt = next_quant(kt + 1);
-      wait_vmem();
-      __syncthreads();                   // staging holds tile kt; the previous tile's K/V are consumed
-      expand_nv();
-      __syncthreads();                   // K/V of tile kt ready; the staging area is free
-      if (nxt < kt_end) issue_nv(nxt);   // in flight during this tile's compute
-      FA4_TILE_STEP(false, false, kt, nullptr, nullptr, v16, hsv);
-      kt = nxt;
-    }
-    if (CAUSAL && kt == last) {
-      wait_vmem();
-      __syncthreads();
-      expand_nv();
-      __syncthreads();
-      FA4_TILE_STEP(true, false, kt, nullptr, nullptr, v16, hsv);
+      FA4_TILE_STEP(true, false, kt, nullptr, nullptr, vbuf_of(vb), w_of(vb));
     }
   }
   if constexpr (V4) {
