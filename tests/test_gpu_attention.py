@@ -97,6 +97,29 @@ def test_deterministic(fa4):
 
 
 # ---- Q and K in MXFP8 (E4M3 elements, E8M0 per 32): K expanded to exact bf16, QK^T on bf16 MFMAs
+def test_fp8_pv_one_large_many_small(fa4):
+    """PV with one dominant probability per row in every 128-key tile and 127 others about 2^-8 of it, so
+    that each 64-key FP8 MFMA step adds one large product next to many small ones, the case where the
+    FP8 MFMA's accumulation is inexact: the result must stay within the parity bar."""
+    cfg = W.C1.scaled(B=1, Hq=1, Hkv=1, Lq=128, Lk=512, causal=False)
+    d = cfg.d
+    q = torch.zeros(1, 1, cfg.Lq, d)
+    k = torch.zeros(1, 1, cfg.Lk, d)
+    rows = torch.arange(cfg.Lq)
+    q[0, 0, rows, rows % d] = 64.0                       # exact in MXFP4 (code 4, scale 2^4)
+    keys = torch.arange(cfg.Lk)
+    k[0, 0, keys, keys % d] = 1.0                        # score 64 / sqrt(128) for keys r, r + 128, ..., else 0
+    g = torch.Generator().manual_seed(11)
+    v = torch.randn(1, 1, cfg.Lk, d, generator=g) * (1.0 + 4.0 * torch.rand(1, 1, cfg.Lk, 1, generator=g))
+    q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    res = fa4.prefill(q.cuda(), k.cuda(), v.cuda(), cfg.causal, fmt=fa4.FA4_MXFP4)
+    torch.cuda.synchronize()
+    O, L, _, slack = prefill_reference(cfg, 0, [(0, 0)], np.arange(cfg.Lq), None, q, k, v, slack=True)
+    got = res["o"].cpu().numpy().reshape(-1, cfg.Lq, d)
+    assert_parity(got, O, "one large product next to many small ones", slack)
+    assert np.abs(res["lse"].cpu().numpy().reshape(-1, cfg.Lq) - L).max() < 1e-4
+
+
 def test_mxfp8_tiny_noncausal_f32(fa4):
     _check_full(fa4, W.C0.scaled(qk_fmt="mxfp8", d=128))
 
