@@ -48,6 +48,7 @@ struct DecArgs {
   const float *kt, *vt;
   const int32_t *pt, *ctx;
   int B, Hq, Hkv, max_pages, nsplit;
+  int G, VG;                                      // query heads per key head; groups of up to 4 of them
   int64_t num_pages;
   float scale;
   float pscale;                                   // final factor of P^: 1/448 (FP8) or s_t (NVFP4)
@@ -247,12 +248,18 @@ __device__ __forceinline__ uint32_t cvt_bf16_fp4_sel(uint32_t w, float sc, int i
 template <int FMT, int PF>
 __global__ void __launch_bounds__(DEC_THREADS, 3) decode_split_kernel(DecArgs a) {
   __shared__ float part[DEC_SLOTS][4][DEC_PART];
-  // Workgroup order: (sequence, key head) fastest, split slowest. Workgroups are handed to the 8 XCDs
-  // round-robin, so every XCD gets the same mix of sequences (with 8 key heads, one key head each,
-  // whose pages then stay in that XCD's L2), and the mostly empty trailing splits come last.
-  const int nbk = a.B * a.Hkv;
+  // A workgroup serves one group of up to 4 query heads of a key head (a key head with G query heads
+  // has VG = ceil(G / 4) groups; group sub holds heads 4 sub .. min(G, 4 sub + 4) - 1 of it).
+  // Workgroup order: (sequence, key head, group) fastest, split slowest. Workgroups are handed to the
+  // 8 XCDs round-robin, so every XCD gets the same mix of sequences (with 8 key heads of one group,
+  // one key head each, whose pages then stay in that XCD's L2), and the mostly empty trailing splits
+  // come last.
+  const int nvk = a.Hkv * a.VG, nbk = a.B * nvk;
   const int split = (int)(blockIdx.x / (unsigned)nbk), bk = (int)(blockIdx.x - (unsigned)split * nbk);
-  const int b = bk / a.Hkv, kvh = bk - b * a.Hkv;
+  const int b = bk / nvk, vkh = bk - b * nvk;
+  const int kvh = vkh / a.VG, sub = vkh - kvh * a.VG;
+  const int nh = min(4, a.G - 4 * sub);                   // heads in this group
+  const int h0 = kvh * a.G + 4 * sub;                      // its first query head
   const int L = min(a.ctx[b], a.max_pages * 64);
   if (split * DEC_SPLIT >= L) return;                      // uniform per workgroup
   const int tid = threadIdx.x, lane = tid & 63;
@@ -263,7 +270,8 @@ __global__ void __launch_bounds__(DEC_THREADS, 3) decode_split_kernel(DecArgs a)
   // this wave's tiles: split * DEC_SPLIT + 128 (4 it + wave), it = 0 .. DEC_TPW - 1
   const int tbase = split * DEC_SPLIT + 128 * wave;
 
-  // ---- query operand: column n = residual (n >> 2) & 1 of head 4 kvh + (n & 3); columns 8..15
+  // ---- query operand: column n = residual (n >> 2) & 1 of head h0 + (n & 3) (a group of fewer than 4
+  // heads repeats its last head in the spare columns, whose results are not kept); columns 8..15
   // repeat columns 0..7, so that both halves of each row hold every score and split the softmax.
   // NVFP4: physical d of (lane group g, step s, element j) = 32 g + 8 s + j. MXFP4: lane group g holds
   // d = 32 g .. 32 g + 31 (one E8M0 block) as FP4 codes with its scale byte.
@@ -271,7 +279,7 @@ __global__ void __launch_bounds__(DEC_THREADS, 3) decode_split_kernel(DecArgs a)
   v8i qmx = {};
   int qsc = 0;
   {
-    const int hq = kvh * 4 + (n & 3);
+    const int hq = h0 + min(n & 3, nh - 1);
     const bool r2 = n & 4;
     const uint8_t *qc = (r2 ? a.q2c : a.q1c) + ((int64_t)b * a.Hq + hq) * 64 + 16 * g;
     const v4i w = *reinterpret_cast<const v4i *>(qc);
@@ -287,7 +295,7 @@ __global__ void __launch_bounds__(DEC_THREADS, 3) decode_split_kernel(DecArgs a)
   }
   // scores of head n & 3: x = log2e * scale * s_tK * (s_t1 D[Q1 column] + s_t2 D[Q2 column]) (the
   // tensor scales are 1 for MXFP4)
-  const int64_t bq = (int64_t)b * a.Hq + kvh * 4 + (n & 3);
+  const int64_t bq = (int64_t)b * a.Hq + h0 + min(n & 3, nh - 1);
   float c1 = DEC_LOG2E * a.scale, c2 = c1;
   if constexpr (FMT == FA4_NVFP4) {
     const float ck = c1 * a.kt[(int64_t)b * a.Hkv + kvh];
@@ -515,7 +523,7 @@ __global__ void __launch_bounds__(DEC_THREADS, 3) decode_split_kernel(DecArgs a)
       o0 += f * part[w][hd][2 + d0];
       o1 += f * part[w][hd][3 + d0];
     }
-    float *dst = a.ws + ((((int64_t)b * a.Hkv + kvh) * a.nsplit + split) * 4 + hd) * DEC_PART;
+    float *dst = a.ws + ((((int64_t)b * nvk + vkh) * a.nsplit + split) * 4 + hd) * DEC_PART;
     if (d0 == 0) { dst[0] = mm; dst[1] = l; }
     dst[2 + d0] = o0;
     dst[3 + d0] = o1;
@@ -529,10 +537,11 @@ __global__ void __launch_bounds__(DEC_THREADS, 3) decode_split_kernel(DecArgs a)
 __global__ void __launch_bounds__(128) decode_combine_kernel(DecArgs a) {
   __shared__ float red[2];
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
-  const int kvh = h / 4, hd = h & 3;
+  const int kvh = h / a.G, c = h - kvh * a.G, hd = c & 3;
+  const int vkh = kvh * a.VG + (c >> 2);                  // the workgroups of head h's group
   const int L = min(a.ctx[b], a.max_pages * 64);
   const int ns = (L + DEC_SPLIT - 1) / DEC_SPLIT;
-  const float *base = a.ws + (((int64_t)b * a.Hkv + kvh) * a.nsplit * 4 + hd) * DEC_PART;
+  const float *base = a.ws + (((int64_t)b * a.Hkv * a.VG + vkh) * a.nsplit * 4 + hd) * DEC_PART;
   float mm = -INFINITY;
   for (int s = d; s < ns; s += 128) mm = fmaxf(mm, base[(int64_t)s * 4 * DEC_PART]);
   for (int m = 1; m < 64; m <<= 1) mm = fmaxf(mm, shfl_xor_f(mm, m));
@@ -561,6 +570,8 @@ static DecArgs make_dec(const fa4_decode_args *p, void *ws) {
   x.kt = nv ? p->k_tscale : nullptr; x.vt = nv ? p->v_tscale : nullptr;
   x.pt = p->page_table; x.ctx = p->ctx_len;
   x.B = p->B; x.Hq = p->Hq; x.Hkv = p->Hkv; x.max_pages = p->max_pages;
+  x.G = p->Hq / p->Hkv;
+  x.VG = (x.G + 3) / 4;
   x.nsplit = (p->max_pages * 64 + DEC_SPLIT - 1) / DEC_SPLIT;
   x.num_pages = p->num_pages;
   x.scale = p->softmax_scale;
@@ -571,13 +582,13 @@ static DecArgs make_dec(const fa4_decode_args *p, void *ws) {
 
 size_t decode_workspace_bytes(const fa4_decode_args *p) {
   const int64_t nsplit = ((int64_t)p->max_pages * 64 + DEC_SPLIT - 1) / DEC_SPLIT;
-  return (size_t)p->B * p->Hkv * nsplit * 4 * DEC_PART * sizeof(float);
+  return (size_t)p->B * p->Hkv * ((p->Hq / p->Hkv + 3) / 4) * nsplit * 4 * DEC_PART * sizeof(float);
 }
 
 hipError_t launch_decode(const fa4_decode_args *p, void *ws, hipStream_t s) {
   if (p->B == 0) return hipSuccess;
   const DecArgs x = make_dec(p, ws);
-  const dim3 grid((unsigned)((int64_t)x.nsplit * x.B * x.Hkv));
+  const dim3 grid((unsigned)((int64_t)x.nsplit * x.B * x.Hkv * x.VG));
   const bool p4 = p->p_fmt == FA4_P_NVFP4;
   if (p->fmt == FA4_MXFP4) {
     if (p4) hipLaunchKernelGGL((decode_split_kernel<FA4_MXFP4, FA4_P_NVFP4>), grid, dim3(DEC_THREADS), 0, s, x);

@@ -348,11 +348,12 @@ fa4_status fa4_decode_paged(const fa4_decode_args *a, void *ws, size_t ws_bytes,
           a->p_fmt);
   REQUIRE(a->d == 128, FA4_ERR_UNSUPPORTED, "decode: d=%d (128)", a->d);
   REQUIRE(a->page_size == 64, FA4_ERR_UNSUPPORTED, "decode: page_size=%d (64)", a->page_size);
-  REQUIRE(a->B >= 0 && a->Hkv >= 1 && a->Hq == 4 * a->Hkv, FA4_ERR_UNSUPPORTED,
-          "decode: needs Hq = 4 Hkv (Hq=%d Hkv=%d)", a->Hq, a->Hkv);
+  REQUIRE(a->B >= 0 && a->Hkv >= 1 && a->Hq >= a->Hkv && a->Hq % a->Hkv == 0 && a->Hq / a->Hkv <= 64,
+          FA4_ERR_UNSUPPORTED, "decode: needs Hq a multiple of Hkv, at most 64 Hkv (Hq=%d Hkv=%d)", a->Hq, a->Hkv);
   REQUIRE(a->max_pages >= 1 && a->num_pages >= 1, FA4_ERR_SHAPE, "decode: max_pages and num_pages >= 1");
   REQUIRE(a->B <= 65535 && a->Hkv <= 65535 && a->Hq <= 65535, FA4_ERR_SHAPE, "decode: grid too large");
-  REQUIRE(((int64_t)a->max_pages * 64 + fa4::DEC_SPLIT_KEYS - 1) / fa4::DEC_SPLIT_KEYS * a->B * a->Hkv <
+  REQUIRE(((int64_t)a->max_pages * 64 + fa4::DEC_SPLIT_KEYS - 1) / fa4::DEC_SPLIT_KEYS * a->B * a->Hkv *
+                  ((a->Hq / a->Hkv + 3) / 4) <
               ((int64_t)1 << 31),
           FA4_ERR_SHAPE,
           "decode: grid too large");

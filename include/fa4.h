@@ -267,8 +267,10 @@ fa4_status fa4_attn_fwd(const fa4_attn_args *a, void *stream);
  *              zero only when the block's largest probability is under 2^-10/448 of the tile's.
  * The work is split over key ranges; partial results go to a caller-provided workspace of
  * fa4_decode_workspace_bytes(a) bytes (256-byte aligned) and are merged by a second kernel.
- * Requirements: d = 128; page_size = 64; Hq / Hkv = 4; 0 <= ctx_len[b] <= max_pages * page_size (a
- * sequence with ctx_len[b] = 0 reads no page and gets O = 0, in both geometries).
+ * Requirements: d = 128; page_size = 64; Hq a multiple of Hkv with at most 64 query heads per key head
+ * (groups of up to 4 of them share one pass over the key head's pages, so 4 per key head reads the
+ * cache once and 8 reads it twice); 0 <= ctx_len[b] <= max_pages * page_size (a sequence with
+ * ctx_len[b] = 0 reads no page and gets O = 0, in both geometries).
  *
  * MLA geometry (d_v = 512; "BitDecoding-FP4" reports the method on MLA attention as well): every query
  * head of sequence b attends to one shared latent row per token, whose d = 576 values (512 latent, 64

@@ -221,7 +221,12 @@ def test_decode_rejects_before_launch():
     assert need == 4 * 8 * 1 * 4 * 130 * 4
     assert call(_dec(d=64)) == fa4.FA4_ERR_UNSUPPORTED
     assert call(_dec(page_size=32)) == fa4.FA4_ERR_UNSUPPORTED
-    assert call(_dec(Hq=16)) == fa4.FA4_ERR_UNSUPPORTED
+    assert call(_dec(Hq=12)) == fa4.FA4_ERR_UNSUPPORTED               # not a multiple of Hkv = 8
+    assert call(_dec(Hq=8 * 65)) == fa4.FA4_ERR_UNSUPPORTED           # more than 64 query heads per key head
+    # groups of up to 4 query heads per workgroup: 8 per key head take two groups' partials
+    assert fa4.lib.fa4_decode_workspace_bytes(ctypes.byref(_dec(Hq=64))) == 2 * need
+    assert fa4.lib.fa4_decode_workspace_bytes(ctypes.byref(_dec(Hq=16))) == need
+    assert fa4.lib.fa4_decode_workspace_bytes(ctypes.byref(_dec(Hq=8))) == need
     assert call(_dec(k_codes=None)) == fa4.FA4_ERR_NULL
     assert call(_dec(k_codes=264)) == fa4.FA4_ERR_ALIGN
     assert call(a, ws=512, n=need - 1) == fa4.FA4_ERR_WORKSPACE

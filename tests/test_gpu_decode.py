@@ -48,6 +48,22 @@ def test_decode_small_all_pairs(fa4, ctx, base):
     assert_parity(np.stack([o[b, h] for b, h in pairs]), ref, f"decode ctx {ctx}")
 
 
+@FMTS
+@pytest.mark.parametrize("hq", [2, 4, 6, 16, 24], ids=["g1", "g2", "g3", "g8", "g12"])
+def test_decode_query_groups(fa4, hq, base):
+    """Query heads per key head other than 4: a workgroup serves a group of up to 4 of them (a smaller
+    group repeats its last head in the spare matrix columns; more than 4 take several groups, each a
+    pass over the key head's pages)."""
+    cfg = base.scaled(B=3, Hq=hq, Hkv=2, ctx_lo=300, ctx_hi=2500)
+    lay = W.decode_layout(cfg)
+    o, _ = _gpu_decode(fa4, cfg, lay)
+    _, _, _, _, logical = decode_cache(cfg, lay, 0)
+    q, (q1, q2) = decode_query_quant(cfg, 0)
+    pairs = [(b, h) for b in range(cfg.B) for h in range(cfg.Hq)]
+    ref = decode_reference(cfg, 0, lay, pairs, logical, q1, q2)
+    assert_parity(np.stack([o[b, h] for b, h in pairs]), ref, f"decode with {hq // 2} query heads per key head")
+
+
 def with_empty(lay, seqs):
     """The layout with the listed sequences emptied (context 0, no pages)."""
     ctx, pt = lay.ctx_len.clone(), lay.page_table.clone()
