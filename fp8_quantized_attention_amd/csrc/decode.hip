@@ -13,8 +13,9 @@
 // 8 values of its d-run before the 8x8 transpose of 16-bit values) and P^ enters as bf16.
 //
 // Work decomposition: the keys of each (sequence, key head) are cut into splits of DEC_SPLIT keys; a
-// workgroup owns one split and its 4 waves take the split's 128-key tiles (the probability tiles) in
-// turn. The 8 query rows of a GQA group (4 heads x {Q1, Q2}) form the columns of a 16x16x32 fp16
+// workgroup owns one split for one group of up to 4 of the key head's query heads, and its 4 waves
+// take the split's 128-key tiles (the probability tiles) in turn. The 8 query rows of the group
+// (4 heads x {Q1, Q2}; a smaller group repeats its last head) form the columns of a 16x16x32 fp16
 // MFMA whose rows are 16 keys: NVFP4 values code * s_b are exact in fp16 (at most 5 significant
 // bits), so K and Q codes are expanded in registers (hardware fp4->fp16 conversion, then one packed
 // multiply by the block scales) and the tensor scales are applied to the fp32 scores. The d axis of
