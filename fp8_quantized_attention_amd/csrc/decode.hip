@@ -84,12 +84,14 @@ __device__ __forceinline__ _Float16 e4m3_f16(uint32_t code) { return (_Float16)e
 
 // Transpose of an 8x8 matrix of nibbles held as 8 words (word j, nibble e) -> (word e, nibble j):
 // swap the off-diagonal 4x4 blocks (16-bit halves), then the 2x2 blocks inside them (bytes), then
-// the single nibbles.
+// the single nibbles. The first two steps are one byte permute per output word (v_perm_b32: byte k
+// of the result is byte sel_k of the pair {hi word: bytes 4..7, lo word: bytes 0..3}); the last one
+// is a shift and a bit-field merge per output word: 32 instructions in all.
 __device__ __forceinline__ void transpose8x8_nibbles(uint32_t w[8]) {
 #pragma unroll
   for (int j = 0; j < 4; j++) {
-    const uint32_t lo = (w[j] & 0xffffu) | (w[j + 4] << 16);
-    const uint32_t hi = (w[j] >> 16) | (w[j + 4] & 0xffff0000u);
+    const uint32_t lo = __builtin_amdgcn_perm(w[j + 4], w[j], 0x05040100u);   // halves 0 of j, j + 4
+    const uint32_t hi = __builtin_amdgcn_perm(w[j + 4], w[j], 0x07060302u);   // halves 1 of j, j + 4
     w[j] = lo;
     w[j + 4] = hi;
   }
@@ -97,14 +99,14 @@ __device__ __forceinline__ void transpose8x8_nibbles(uint32_t w[8]) {
   for (int k = 0; k < 4; k++) {
     const int r = (k & 1) + 4 * (k >> 1);                   // 0, 1, 4, 5
     const uint32_t x = w[r], y = w[r + 2];
-    w[r] = (x & 0x00ff00ffu) | ((y & 0x00ff00ffu) << 8);
-    w[r + 2] = ((x >> 8) & 0x00ff00ffu) | (y & 0xff00ff00u);
+    w[r] = __builtin_amdgcn_perm(y, x, 0x06020400u);        // bytes x0 y0 x2 y2
+    w[r + 2] = __builtin_amdgcn_perm(y, x, 0x07030501u);    // bytes x1 y1 x3 y3
   }
 #pragma unroll
   for (int r = 0; r < 8; r += 2) {
-    const uint32_t t = ((w[r] >> 4) ^ w[r + 1]) & 0x0f0f0f0fu;
-    w[r + 1] ^= t;
-    w[r] ^= t << 4;
+    const uint32_t x = w[r], y = w[r + 1];
+    w[r] = (x & 0x0f0f0f0fu) | ((y << 4) & 0xf0f0f0f0u);   // low nibbles of x and y
+    w[r + 1] = ((x >> 4) & 0x0f0f0f0fu) | (y & 0xf0f0f0f0u);  // high nibbles of x and y
   }
 }
 
@@ -313,6 +315,9 @@ __global__ void __launch_bounds__(DEC_THREADS, 3) decode_split_kernel(DecArgs a)
     return vs_base + (FMT == FA4_NVFP4 ? 8 * (16 * (j >> 2) + (j & 3)) : 4 * (16 * (j >> 2) + (j & 3)));
   };
   const int vs_sh = FMT == FA4_NVFP4 ? 8 * ((n >> 1) & 3) : 8 * (n >> 2);
+  // NVFP4: one byte permute gathers the two keys' scale bytes (byte vs_sh / 8 of each shuffled word)
+  // into bits 15:0 (selector 0x0c gives a zero byte)
+  const uint32_t vs_sel = 0x0c0c0000u | ((uint32_t)(4 + (vs_sh >> 3)) << 8) | (uint32_t)(vs_sh >> 3);
 
   // Software pipeline over the wave's tiles: the next tile's K is requested as soon as this tile's
   // QK has consumed the K registers, and its V as soon as this tile's PV has consumed V, so each
@@ -460,7 +465,7 @@ __global__ void __launch_bounds__(DEC_THREADS, 3) decode_split_kernel(DecArgs a)
           for (int jp = 0; jp < 4; jp++) {
             const uint32_t s0 = (uint32_t)__builtin_amdgcn_ds_bpermute(vs_addr(2 * jp), (int)vs[q]);
             const uint32_t s1 = (uint32_t)__builtin_amdgcn_ds_bpermute(vs_addr(2 * jp + 1), (int)vs[q]);
-            sp[jp] = e4m3x2_f16(((s0 >> vs_sh) & 0xffu) | (((s1 >> vs_sh) & 0xffu) << 8));
+            sp[jp] = e4m3x2_f16(__builtin_amdgcn_perm(s1, s0, vs_sel));
           }
 #pragma unroll
           for (int e = 0; e < 8; e++)
