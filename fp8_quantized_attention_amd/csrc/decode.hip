@@ -471,16 +471,16 @@ __global__ void __launch_bounds__(DEC_THREADS, 3) decode_split_kernel(DecArgs a)
           for (int e = 0; e < 8; e++)
             acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(expand8s(w[e], sp), pb, acc[e], 0, 0, 0);
         } else {
-          // key j's run of 8 d values -> bf16 with its own scale 2^(code - 127); scale code 0 (blocks
-          // below 6 * 2^-127) is taken as 2^-126 so that the conversion's scale stays a normal float.
+          // key j's run of 8 d values -> bf16 with its own scale 2^(code - 127). The conversion reads
+          // only the exponent field of its float scale, as an E8M0 code, so the code's bits go there
+          // directly (code 0 acts as 2^-127: E2M1 * 2^-127 >= 2^-128 is a bf16 subnormal, exact).
           // Converted one pair of d values (i) at a time, right before the two MFMAs (d = 8 n + 2 i,
           // 8 n + 2 i + 1) that take them, so that only 8 converted words are live.
           float sc[8];
 #pragma unroll
           for (int j = 0; j < 8; j++) {
             const uint32_t sw = (uint32_t)__builtin_amdgcn_ds_bpermute(vs_addr(j), (int)vs[q]);
-            const uint32_t code = (sw >> vs_sh) & 0xffu;
-            sc[j] = __uint_as_float((code > 1u ? code : 1u) << 23);
+            sc[j] = __uint_as_float(__builtin_amdgcn_ubfe(sw, vs_sh, 8) << 23);
           }
 #pragma unroll
           for (int i = 0; i < 4; i++) {

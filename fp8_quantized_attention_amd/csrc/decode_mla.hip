@@ -232,9 +232,9 @@ __global__ void __launch_bounds__(MLA_THREADS) __attribute__((amdgpu_waves_per_e
     for (int q = 0; q < 2; q++) {
       // B: head n, keys 32 q + 8 g .. + 7
       const v8bf pb = *reinterpret_cast<const v8bf *>(&pT[n * MLA_PP + 32 * q + 8 * g]);
-      // A: key 32 q + 8 g + j's run of 8 values -> bf16 with its block scale 2^(code - 127); scale code 0
-      // (blocks below 6 * 2^-127) is taken as 2^-126 so that the conversion's scale stays a normal
-      // float; keys past the context take 2^0 (their P^ is 0)
+      // A: key 32 q + 8 g + j's run of 8 values -> bf16 with its block scale 2^(code - 127) (the
+      // conversion reads the exponent field of its float scale as an E8M0 code, so code 0 acts as
+      // 2^-127, exact in bf16); keys past the context take 2^0 (their P^ is 0)
       uint32_t kw[8][4];
 #pragma unroll
       for (int j = 0; j < 8; j++) {
@@ -242,7 +242,7 @@ __global__ void __launch_bounds__(MLA_THREADS) __attribute__((amdgpu_waves_per_e
         const uint32_t wd = *reinterpret_cast<const uint32_t *>(lc + sl * 2048 + key * 32 + 4 * (n & 7));
         uint32_t code = lc[MLA_TC + sl * 128 + key * 2 + ((n & 7) >> 2)];
         code = key < kval ? code : 127u;
-        const float sc = __uint_as_float((code > 1u ? code : 1u) << 23);
+        const float sc = __uint_as_float(code << 23);
         kw[j][0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 0));
         kw[j][1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 1));
         kw[j][2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wd, sc, 2));

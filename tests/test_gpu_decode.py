@@ -132,3 +132,38 @@ def test_decode_p4_peaked_softmax(fa4, base):
     L = len(S) - len(S) % 128
     P = np.exp(S[:L].reshape(-1, 128) - S[:L].reshape(-1, 128).max(axis=1, keepdims=True))
     assert (P.reshape(-1, 16).max(axis=1) < 6 * 2.0 ** -10).mean() > 0.3
+
+
+@pytest.mark.parametrize("base", [W.C3_MX, W.C3_MX_P4], ids=["mxfp4", "mxfp4_p4"])
+def test_decode_mxfp4_smallest_v_scale(fa4, base):
+    """V at 2^-127 of the usual size: every MXFP4 block of V gets the E8M0 code 0 (scale 2^-127), whose
+    values code * 2^-127 (down to 2^-128) the kernel must take exactly, as the oracle does."""
+    from oracle import quant as Q
+    cfg = base.scaled(B=3, Hq=8, Hkv=2, ctx_lo=100, ctx_hi=900)
+    lay = W.decode_layout(cfg)
+    ctx, pt = lay.ctx_len.cuda(), lay.page_table.cuda()
+    xk = W.decode_kv_padded(cfg, lay, W.T_K, 0)
+    xv = W.decode_kv_padded(cfg, lay, W.T_V, 0) * 2.0 ** -127          # bf16 values, used by both sides
+    kc = fa4.quantize_paged(xk.cuda(), fa4.FA4_MXFP4, ctx, pt, lay.num_pages)
+    vc = fa4.quantize_paged(xv.cuda(), fa4.FA4_MXFP4, ctx, pt, lay.num_pages)
+    q = W.decode_query(cfg, 0).cuda()
+    pf = fa4.FA4_P_NVFP4 if cfg.p_fmt == "nvfp4" else fa4.FA4_P_FP8
+    o, _ = fa4.decode(q, kc, vc, pt, ctx, cfg.Hkv, p_fmt=pf)
+    o = o.cpu().numpy()
+    _, _, _, _, logical = decode_cache(cfg, lay, 0)
+    vs = vc["block_scales"].cpu().numpy()
+    for b in range(cfg.B):
+        L = int(lay.ctx_len[b])
+        c = np.arange(L)
+        phys = lay.page_table[b].numpy()[c // cfg.page_size]
+        for h in range(cfg.Hkv):
+            codes, scales = Q.mxfp4_quantize(xv[b, h, :L].double().numpy())
+            assert not scales.any()                                         # the regime: code 0 throughout
+            assert np.array_equal(vc["codes"].cpu().numpy()[phys, h, c % cfg.page_size], codes)
+            assert np.array_equal(vs[phys, h, c % cfg.page_size], scales)
+            logical[(W.T_V, b, h)] = Q.mxfp4_dequantize(codes, scales)
+    q_, (q1, q2) = decode_query_quant(cfg, 0)
+    pairs = [(b, h) for b in range(cfg.B) for h in range(cfg.Hq)]
+    ref = decode_reference(cfg, 0, lay, pairs, logical, q1, q2)
+    assert np.abs(ref).max() < 2.0 ** -120
+    assert_parity(np.stack([o[b, h] for b, h in pairs]), ref, "decode with V at the smallest E8M0 scale")
