@@ -142,11 +142,10 @@ __device__ __forceinline__ v8h nv_expand8(uint32_t w, _Float16 sb) {
   return (v8h){t0[0], t0[1], t1[0], t1[1], t2[0], t2[1], t3[0], t3[1]};
 }
 
-// MXFP8: an E8M0 scale code as the float 2^(code - 127) for the conversions below (code 0, a block with
-// amax below 448 * 2^-127, is taken as 2^-126 so that the scale stays a normal float).
-__device__ __forceinline__ float mx8_scale_float(uint32_t code) {
-  return __uint_as_float((code > 1u ? code : 1u) << 23);
-}
+// MXFP8: an E8M0 scale code as the scale operand of the conversions below, which read the exponent
+// field of their float scale as an E8M0 code: the code's bits go there unchanged (code 0, a block with
+// amax below 448 * 2^-127, acts as 2^-127; its values under bf16's smallest subnormal 2^-133 round).
+__device__ __forceinline__ float mx8_scale_float(uint32_t code) { return __uint_as_float(code << 23); }
 // 8 E4M3 codes (w.x bytes 0-3, w.y bytes 4-7) times 2^e as exact bf16 values (at most 4 significant
 // bits; bf16 has the float exponent range), packed two per word in element order.
 __device__ __forceinline__ v4i mx8_expand8(uint2 w, float sc) {
