@@ -20,9 +20,10 @@
 // bits), so K and Q codes are expanded in registers (hardware fp4->fp16 conversion, then one packed
 // multiply by the block scales) and the tensor scales are applied to the fp32 scores. The d axis of
 // the QK product is permuted so that each lane's operand is one 16-byte run of a key's codes.
-// PV is O^T = V^T P^T, whose A operand needs 8 keys of one d in a lane: each lane loads one 4-byte
-// word (8 d values) of 8 key rows and an 8x8 nibble transpose in registers turns them into 8 words
-// of 8 keys each, one per d value, so V never goes through LDS. P^ = E4M3(448 P') is exact in fp16.
+// PV is O^T = V^T P^T, whose A operand needs 8 keys of one d in a lane: each lane gets one 4-byte
+// word (8 d values) of 8 key rows (loaded as 8-byte runs, one word of each swapped with the
+// neighbour lane) and an 8x8 nibble transpose in registers turns them into 8 words of 8 keys each,
+// one per d value, so V never goes through LDS. P^ = E4M3(448 P') is exact in fp16.
 // Both pages of a tile are resolved with wave-uniform page-table reads; the next tile's K and V
 // loads are issued as soon as the registers holding the current tile's codes are consumed, so every
 // wave keeps a tile in flight while it computes. Each tile's (max, sum, P^V) goes to LDS, the tiles
@@ -155,23 +156,48 @@ __device__ __forceinline__ void load_k(const TilePages &tp, int n, int g, v4i kc
   }
 }
 
-// V of a tile for the PV A operand: quarter q (32 keys), element j of lane (g, n) is the key
-// 32 q + 16 (j / 4) + 4 g + j % 4, whose codes word n (d = 8 n .. 8 n + 7) the lane loads. The
-// quarter's 32 scale rows (256 contiguous bytes) are loaded one word per lane (lane L: key L / 2,
-// blocks 4 (L % 2) .. 4 (L % 2) + 3) and redistributed with lane shuffles when the quarter is used.
-__device__ __forceinline__ void load_v(const TilePages &tp, int lane, int n, int g, uint32_t vc[4][8],
-                                       uint32_t vs[4]) {
-  const int vo_c = 4 * g * 64 + 4 * n;                    // per-lane offsets; the rest is scalar
+// V codes of a tile for the PV A operand: quarter q (32 keys), element j of lane (g, n) is the key
+// 32 q + 16 (j / 4) + 4 g + j % 4, of whose codes the lane needs word n (d = 8 n .. 8 n + 7). The
+// words arrive as 8-byte runs: lane (g, 2 m + t) loads words 2 m, 2 m + 1 of the keys of elements
+// 2 i + t (i = 0..3), and pair_transpose2 (when the quarter is used) swaps one word of each pair
+// with the neighbour lane, so that lane 2 m + t' ends with word 2 m + t' of both keys. Measured
+// against one 4-byte word per key (NVFP4 cache 5.22 against 5.08-5.13 TB/s, MXFP4 5.52-5.56 against
+// 5.28-5.29, same runs); 16-byte runs with a 4x4 word transpose across each quad of lanes ran at
+// 5.12 and 5.47-5.50: their exchange costs twice the instructions per word.
+__device__ __forceinline__ void load_v_codes(const TilePages &tp, int n, int g, uint32_t vc[4][8]) {
+  const int vo_c = (4 * g + (n & 1)) * 64 + 8 * (n >> 1);   // per-lane offsets; the rest is scalar
 #pragma unroll
   for (int q = 0; q < 4; q++) {
     const int p = q >> 1;
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-      const int r0 = 32 * (q & 1) + 16 * (j >> 2) + (j & 3);
-      vc[q][j] = __builtin_amdgcn_raw_buffer_load_b32(tp.vc[p], vo_c, r0 * 64, DEC_NT);
+    for (int i = 0; i < 4; i++) {
+      const int r0 = 32 * (q & 1) + 16 * (i >> 1) + 2 * (i & 1);
+      const v2i w = __builtin_bit_cast(v2i, __builtin_amdgcn_raw_buffer_load_b64(tp.vc[p], vo_c, r0 * 64, DEC_NT));
+      vc[q][2 * i] = (uint32_t)w[0];
+      vc[q][2 * i + 1] = (uint32_t)w[1];
     }
-    vs[q] = __builtin_amdgcn_raw_buffer_load_b32(tp.vs[p], 4 * lane, 256 * (q & 1), DEC_NT);
   }
+}
+
+// 2x2 transpose of words across a lane pair: lane t holds row t in x[0..1]; afterwards it holds
+// column t (x[s] = row s's word t): a neighbour exchange (quad permute 1,0,3,2) and a select per word.
+__device__ __forceinline__ void pair_transpose2(uint32_t *x, bool odd) {
+  const uint32_t a0 = x[0], a1 = x[1];
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)a0, 0xb1, 0xf, 0xf, true);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)a1, 0xb1, 0xf, 0xf, true);
+  x[0] = !odd ? a0 : r1;
+  x[1] = odd ? a1 : r0;
+}
+
+// V of a tile: codes as load_v_codes; the quarter's 32 scale rows (256 contiguous bytes) are loaded
+// one word per lane (lane L: key L / 2, blocks 4 (L % 2) .. 4 (L % 2) + 3) and redistributed with
+// lane shuffles when the quarter is used.
+__device__ __forceinline__ void load_v(const TilePages &tp, int lane, int n, int g, uint32_t vc[4][8],
+                                       uint32_t vs[4]) {
+  load_v_codes(tp, n, g, vc);
+#pragma unroll
+  for (int q = 0; q < 4; q++)
+    vs[q] = __builtin_amdgcn_raw_buffer_load_b32(tp.vs[q >> 1], 4 * lane, 256 * (q & 1), DEC_NT);
 }
 
 // MXFP4 K: as load_k, with the one E8M0 scale of the lane's 32 values (block g of key 16 kb + n).
@@ -185,21 +211,15 @@ __device__ __forceinline__ void load_k_mx(const TilePages &tp, int n, int g, v4i
   }
 }
 
-// MXFP4 V: codes as load_v; the quarter's 32 scale rows (4 bytes each, 128 contiguous bytes) are
-// loaded one row per lane (lane L: key L % 32) and fetched by lane shuffles when the quarter is used.
+// MXFP4 V: codes as load_v_codes; the quarter's 32 scale rows (4 bytes each, 128 contiguous bytes)
+// are loaded one row per lane (lane L: key L % 32) and fetched by lane shuffles when the quarter is
+// used.
 __device__ __forceinline__ void load_v_mx(const TilePages &tp, int lane, int n, int g, uint32_t vc[4][8],
                                           uint32_t vs[4]) {
-  const int vo_c = 4 * g * 64 + 4 * n;
+  load_v_codes(tp, n, g, vc);
 #pragma unroll
-  for (int q = 0; q < 4; q++) {
-    const int p = q >> 1;
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-      const int r0 = 32 * (q & 1) + 16 * (j >> 2) + (j & 3);
-      vc[q][j] = __builtin_amdgcn_raw_buffer_load_b32(tp.vc[p], vo_c, r0 * 64, DEC_NT);
-    }
-    vs[q] = __builtin_amdgcn_raw_buffer_load_b32(tp.vs[p], 4 * (lane & 31), 128 * (q & 1), DEC_NT);
-  }
+  for (int q = 0; q < 4; q++)
+    vs[q] = __builtin_amdgcn_raw_buffer_load_b32(tp.vs[q >> 1], 4 * (lane & 31), 128 * (q & 1), DEC_NT);
 }
 
 template <int FMT>
@@ -269,6 +289,7 @@ __global__ void __launch_bounds__(DEC_THREADS, 3) decode_split_kernel(DecArgs a)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;                  // MFMA column / lane group
   const int rep = n >> 3;                                  // softmax half: key blocks 4 rep .. 4 rep + 3
+  const bool qodd = lane & 1;                              // position in the lane's pair
   const int32_t *pt = a.pt + (int64_t)b * a.max_pages;
   // this wave's tiles: split * DEC_SPLIT + 128 (4 it + wave), it = 0 .. DEC_TPW - 1
   const int tbase = split * DEC_SPLIT + 128 * wave;
@@ -455,6 +476,8 @@ __global__ void __launch_bounds__(DEC_THREADS, 3) decode_split_kernel(DecArgs a)
 #pragma unroll
       for (int q = 0; q < 4; q++) {
         const v8h pb = q < 2 ? popl[q] : row_shl_v8h<8>(popl[q - 2]);
+#pragma unroll
+        for (int i = 0; i < 4; i++) pair_transpose2(&vc[q][2 * i], qodd);   // vc[q][j]: word n of key j
         if constexpr (FMT == FA4_NVFP4) {
           uint32_t w[8];
 #pragma unroll
