@@ -36,6 +36,13 @@ tiles of 128 keys; column c of tile j is unmasked when not causal or c <= r + of
   4. m_r = max_j r_rj, D_r = sum_j 2^(r_rj - m_r) sum_c P'_rc (unquantized P'),
      N_r = sum_j 2^(r_rj - m_r) T_rj; O_r = N_r / D_r (returned as float32),
      LSE_r = m_r ln 2 + ln D_r.
+  MXFP4 probabilities (p_fmt = "mxfp4", FP8 V, unselected tiles): in step 3 P^ is the MXFP4
+     quantization of the row of P'_rc w_c over 32 consecutive keys of the tile (keys 128 j + 32 b ..
+     + 31): per block the MX scale 2^e_b (the smallest power of two with 6 * 2^e_b >= the block's
+     largest P' w), codes E2M1(P' w 2^-e_b), P^ = code * 2^e_b; T_rj = 2^e_j sum_c P^_rc E4M3value(Vcode_c).
+     ("BitDecoding-FP4": probabilities in FP4 under a scale that cannot underflow; "MXFP vs NVFP4"
+     section 2.1: the MX block of 32 with an E8M0 scale. Blocks run along the keys, the contraction
+     axis of PV, so a block-scaled product applies each block's scale.)
   4-bit V (v_deq given): V is MXFP4 with its 32-element blocks along the keys
      ("MpFA QK4V8" section 6 names 4-bit V as an extension without a format; blocks
      along the contraction axis of PV are the ones a block-scaled product can apply),
@@ -48,7 +55,8 @@ result does not depend on the order in which tiles are visited;
 """
 import numpy as np
 
-from .formats import E4M3_MAX, bf16_round, e4m3_decode, e4m3_encode, fp32
+from .formats import E4M3_MAX, bf16_round, e2m1_decode, e2m1_encode, e4m3_decode, e4m3_encode, fp32
+from .quant import MX_BLOCK, mx_scale_exponent, mxfp4_dequantize, mxfp4_quantize
 
 TILE = 128
 
@@ -64,9 +72,37 @@ def fold_exponent(sigma):
     return min(max(e, -127), 127)
 
 
-def _tile_terms(S, unmasked, sel, vq_vals, s_v, v_orig, round_p=True, v_deq=None):
+def mxfp4_rows(x):
+    """MXFP4 quantization of each row of x ([R, n], n a multiple of 32, values >= 0) over consecutive
+    32-element blocks, returned dequantized (float64): the block-scaled quantizer of the inputs
+    applied to the probabilities."""
+    return mxfp4_dequantize(*mxfp4_quantize(x))
+
+
+def mxfp4_tie_delta(arg, eps):
+    """Per element of arg ([R, n] >= 0, 32-blocks along the last axis), the largest change of its MXFP4
+    value when every element may be evaluated with a relative error up to its eps ([R, n]): each
+    element may round to either neighbour of its perturbed argument, and the block scale may follow
+    either end of the block maximum's range (a maximum within that error of 6 * 2^e). Returns [R, n]."""
+    R, n = arg.shape
+    a = arg.reshape(R, n // MX_BLOCK, MX_BLOCK)
+    ep = eps.reshape(a.shape)
+    amax = a.max(axis=-1)
+    em = ep.max(axis=-1)
+    e0 = mx_scale_exponent(amax)
+    mid = e2m1_decode(e2m1_encode(a * np.ldexp(1.0, -e0)[..., None])) * np.ldexp(1.0, e0)[..., None]
+    delta = np.zeros_like(a)
+    for e in (mx_scale_exponent(amax * (1 - em)), e0, mx_scale_exponent(amax * (1 + em))):
+        s = np.ldexp(1.0, e)[..., None]
+        for f in (1 - ep, 1.0, 1 + ep):
+            delta = np.maximum(delta, np.abs(e2m1_decode(e2m1_encode(a * f / s)) * s - mid))
+    return delta.reshape(R, n)
+
+
+def _tile_terms(S, unmasked, sel, vq_vals, s_v, v_orig, round_p=True, v_deq=None, p_fmt="fp8"):
     """Per-row (r, sum P', T) of one key tile, r the tile's power-of-two row reference in log2 units.
-    S: [R, n] float64 scores (already scaled). v_deq: the tile's dequantized 4-bit V (else FP8 V)."""
+    S: [R, n] float64 scores (already scaled). v_deq: the tile's dequantized 4-bit V (else FP8 V).
+    p_fmt: "fp8" (P^ in E4M3) or "mxfp4" (P^ in MXFP4 over 32-key blocks; FP8 V only)."""
     X = np.where(unmasked, S * np.log2(np.e), -np.inf)
     has = unmasked.any(axis=1)
     r = np.where(has, np.ceil(X.max(axis=1, initial=-np.inf)), 0.0)
@@ -82,7 +118,12 @@ def _tile_terms(S, unmasked, sel, vq_vals, s_v, v_orig, round_p=True, v_deq=None
         e = fold_exponent(float(np.max(s_v)))
         w = s_v.astype(np.float64) * 2.0 ** -e
         Pw = P * w[None, :]
-        Ph = e4m3_decode(e4m3_encode(Pw)) if round_p else Pw
+        if not round_p:
+            Ph = Pw
+        elif p_fmt == "mxfp4":
+            Ph = mxfp4_rows(Pw)
+        else:
+            Ph = e4m3_decode(e4m3_encode(Pw))
         T = 2.0 ** e * (Ph @ vq_vals)
     return np.where(has, r, -np.inf), l, T
 
@@ -99,7 +140,7 @@ def _row_tiles(rows, Lq, Lk, causal, tile=TILE):
 
 def attend_rows(rows, q_rows, k_deq, v_codes, s_v, scale, Lq, Lk, causal,
                 q_orig_rows=None, k_orig=None, v_orig=None, sel_row=None, round_p=True,
-                tile_order=None, v_deq=None):
+                tile_order=None, v_deq=None, p_fmt="fp8"):
     """Two-pass O8 for a group of query rows that all lie in one 128-row q-tile.
 
     rows: [R] query indices; q_rows: [R, d] dequantized Q; k_deq: [Lk, d];
@@ -124,7 +165,7 @@ def attend_rows(rows, q_rows, k_deq, v_codes, s_v, scale, Lq, Lk, causal,
             S = scale * (q_rows @ k_deq[cs].T)
         m, l, T = _tile_terms(S, unmasked, sel, None if vq_vals is None else vq_vals[cs],
                               None if s_v is None else s_v[cs], v_orig[cs] if sel else None, round_p,
-                              None if v_deq is None else v_deq[cs])
+                              None if v_deq is None else v_deq[cs], p_fmt)
         ms.append(m); ls.append(l); Ts.append(T)
     M = np.stack(ms, axis=0)                       # [J, R] log2 units
     mrow = M.max(axis=0)
@@ -136,7 +177,7 @@ def attend_rows(rows, q_rows, k_deq, v_codes, s_v, scale, Lq, Lk, causal,
 
 def attend_rows_online(rows, q_rows, k_deq, v_codes, s_v, scale, Lq, Lk, causal,
                        q_orig_rows=None, k_orig=None, v_orig=None, sel_row=None, round_p=True,
-                       tile_order=None, v_deq=None):
+                       tile_order=None, v_deq=None, p_fmt="fp8"):
     """The same computation as attend_rows with a running max m, sum l and accumulator acc.
 
     For each tile (log2 units): m_new = max(m, r); acc = acc 2^(m - m_new) + T 2^(r - m_new);
@@ -159,7 +200,7 @@ def attend_rows_online(rows, q_rows, k_deq, v_codes, s_v, scale, Lq, Lk, causal,
         S = scale * ((q_orig_rows @ k_orig[cs].T) if sel else (q_rows @ k_deq[cs].T))
         mt, lt, T = _tile_terms(S, unmasked, sel, None if vq_vals is None else vq_vals[cs],
                                 None if s_v is None else s_v[cs], v_orig[cs] if sel else None, round_p,
-                                None if v_deq is None else v_deq[cs])
+                                None if v_deq is None else v_deq[cs], p_fmt)
         m_new = np.maximum(m, mt)
         a_old = np.where(np.isfinite(m), np.exp2(m - m_new), 0.0)
         a_new = np.where(np.isfinite(mt), np.exp2(mt - m_new), 0.0)
@@ -170,7 +211,7 @@ def attend_rows_online(rows, q_rows, k_deq, v_codes, s_v, scale, Lq, Lk, causal,
 
 
 def rounding_slack(rows, q_rows, k_deq, v_codes, s_v, scale, Lq, Lk, causal,
-                   q_orig_rows=None, k_orig=None, v_orig=None, sel_row=None, v_deq=None):
+                   q_orig_rows=None, k_orig=None, v_orig=None, sel_row=None, v_deq=None, p_fmt="fp8"):
     """Per-row, per-column bound [R, d] on how far O moves when probability roundings that lie within the
     FP32 evaluation error of a rounding midpoint go to the other neighbour.
 
@@ -187,6 +228,9 @@ def rounding_slack(rows, q_rows, k_deq, v_codes, s_v, scale, Lq, Lk, causal,
     difference, times the absolute values of its V row as the tile's T uses them, weighted as in step 4:
         slack_r = (1 / D_r) sum_j 2^(r_rj - m_r) sum_c delta_rc |V_c|.
     The denominator D uses the unrounded P' and moves only by the evaluation error itself.
+    MXFP4 probabilities (p_fmt = "mxfp4"): an element's FP4 rounding may go either way as above, and the
+    block's scale either way when the block maximum lies within its error of a scale boundary
+    (`mxfp4_tie_delta`).
     """
     rows = np.asarray(rows)
     off = Lk - Lq
@@ -216,8 +260,11 @@ def rounding_slack(rows, q_rows, k_deq, v_codes, s_v, scale, Lq, Lk, causal,
             e = fold_exponent(float(np.max(s_v[cs])))
             w = s_v[cs].astype(np.float64) * 2.0 ** -e
             rnd, arg, vabs, unit = (lambda x: e4m3_decode(e4m3_encode(x))), P * w[None, :], np.abs(vq_vals[cs]), 2.0 ** e
-        mid = rnd(arg)
-        delta = np.maximum(np.abs(rnd(arg * (1 - eps)) - mid), np.abs(rnd(arg * (1 + eps)) - mid))
+        if p_fmt == "mxfp4" and not sel and v_deq is None:
+            delta = mxfp4_tie_delta(arg, np.where(unmasked, eps, 0.0))
+        else:
+            mid = rnd(arg)
+            delta = np.maximum(np.abs(rnd(arg * (1 - eps)) - mid), np.abs(rnd(arg * (1 + eps)) - mid))
         delta = np.where(unmasked, delta, 0.0)
         ms.append(np.where(has, r, -np.inf))
         ls.append(P.sum(axis=1))
@@ -230,7 +277,7 @@ def rounding_slack(rows, q_rows, k_deq, v_codes, s_v, scale, Lq, Lk, causal,
 
 
 def prefill_rounding_slack(q_deq, k_deq, v_codes, s_v, causal, scale=None, q_orig=None, k_orig=None, v_orig=None,
-                           bitmap=None, rows=None, heads=None, v_deq=None):
+                           bitmap=None, rows=None, heads=None, v_deq=None, p_fmt="fp8"):
     """`rounding_slack` over a batch, with the arguments and layout of `attention_prefill`; returns
     float64 [B, Hq, R, d]."""
     B, Hq, Lq, d = q_deq.shape
@@ -254,16 +301,17 @@ def prefill_rounding_slack(q_deq, k_deq, v_codes, s_v, causal, scale=None, q_ori
                 k_orig=None if k_orig is None else k_orig[b, kv],
                 v_orig=None if v_orig is None else v_orig[b, kv],
                 sel_row=bitmap[b, h, i] if bitmap is not None else None,
-                v_deq=None if v_deq is None else v_deq[b, kv])
+                v_deq=None if v_deq is None else v_deq[b, kv], p_fmt=p_fmt)
     return out
 
 
 def attention_prefill(q_deq, k_deq, v_codes, s_v, causal, scale=None,
                       q_orig=None, k_orig=None, v_orig=None, bitmap=None,
-                      rows=None, heads=None, round_p=True, v_deq=None):
+                      rows=None, heads=None, round_p=True, v_deq=None, p_fmt="fp8"):
     """O8 over a batch: q_deq [B, Hq, Lq, d]; k_deq [B, Hkv, Lk, d]; v_codes [B, Hkv, Lk, d]
     (E4M3 codes, token-major); s_v [B, Hkv, Lk]; optional originals (bf16 values as float64)
-    and bitmap [B, Hq, nq, nk]; v_deq [B, Hkv, Lk, d]: dequantized 4-bit V instead of v_codes, s_v.
+    and bitmap [B, Hq, nq, nk]; v_deq [B, Hkv, Lk, d]: dequantized 4-bit V instead of v_codes, s_v;
+    p_fmt: "fp8" or "mxfp4" (the probabilities of the unselected tiles; FP8 V).
 
     rows: optional array of query rows to compute (default all); heads: optional
     list of (b, h) pairs (default all). Returns (O float32 [B, Hq, R, d],
@@ -291,7 +339,7 @@ def attention_prefill(q_deq, k_deq, v_codes, s_v, causal, scale=None,
                 q_orig_rows=None if q_orig is None else q_orig[b, h, rr],
                 k_orig=None if k_orig is None else k_orig[b, kv],
                 v_orig=None if v_orig is None else v_orig[b, kv],
-                sel_row=sel_row, round_p=round_p, v_deq=None if v_deq is None else v_deq[b, kv])
+                sel_row=sel_row, round_p=round_p, v_deq=None if v_deq is None else v_deq[b, kv], p_fmt=p_fmt)
             O[b, h, sel_idx] = fp32(o)
             LSE[b, h, sel_idx] = fp32(lse)
     return O, LSE

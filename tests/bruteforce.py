@@ -141,10 +141,13 @@ def bf16(x):
     return math.copysign(r, x)
 
 
-def attention_rows(rows, Q, K, Vc, sv, Qo, Ko, Vo, sel, Lq, Lk, causal, scale, round_p=True, Vd=None):
+def attention_rows(rows, Q, K, Vc, sv, Qo, Ko, Vo, sel, Lq, Lk, causal, scale, round_p=True, Vd=None,
+                   p_fmt="fp8"):
     """O8 by loops. Q/K: dequantized rows (lists); Vc: E4M3 codes; sv: per-key scales;
     Qo/Ko/Vo: original values for selected tiles; sel(i, j) -> bool. Vd: dequantized 4-bit V rows
-    (then P^ = E4M3(448 P), T = sum P^ v / 448, and Vc, sv are not used). Returns output rows."""
+    (then P^ = E4M3(448 P), T = sum P^ v / 448, and Vc, sv are not used). p_fmt "mxfp4" (FP8 V): the
+    tile's P' w (masked keys 0) is MXFP4-quantized over blocks of 32 consecutive keys by mxfp4_row.
+    Returns output rows."""
     off = Lk - Lq
     d = len((Vc if Vd is None else Vd)[0])
     out = []
@@ -181,11 +184,18 @@ def attention_rows(rows, Q, K, Vc, sv, Qo, Ko, Vo, sel, Lq, Lk, causal, scale, r
                 e = -127                              # smallest e with 448 * 2^e >= sigma
                 while 448.0 * 2.0 ** e < sigma:
                     e += 1
+                pw = {c: P[c] * sv[c] * 2.0 ** -e for c in cols}
+                if round_p and p_fmt == "mxfp4":
+                    row = [pw.get(c, 0.0) for c in range(128 * j, 128 * j + 128)]
+                    vals = mxfp4_row_values(*mxfp4_row(row))
+                    ph = {c: vals[c - 128 * j] for c in cols}
+                elif round_p:
+                    ph = {c: e4m3_value(e4m3_encode(pw[c])) for c in cols}
+                else:
+                    ph = pw
                 for c in cols:
-                    w = sv[c] * 2.0 ** -e
-                    p = e4m3_value(e4m3_encode(P[c] * w)) if round_p else P[c] * w
                     for t in range(d):
-                        T[t] += p * e4m3_value(Vc[c][t])
+                        T[t] += ph[c] * e4m3_value(Vc[c][t])
                 T = [2.0 ** e * v for v in T]
             terms.append((m, sum(P.values()), T))
         mm = max(t[0] for t in terms)

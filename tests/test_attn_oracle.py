@@ -343,3 +343,115 @@ def test_rounding_slack_covers_an_fp32_evaluation():
     dif = np.abs(O32 - O)
     assert flips >= 1 and dif.max() > 1e-3 * np.abs(O).max()        # the flips move O well past noise
     assert np.all(dif <= sl + 1e-5 * np.abs(O).max())
+
+
+# ---- MXFP4 probabilities (FP8 V): P' w quantized to MXFP4 over 32 consecutive keys of each tile
+
+def test_p_mxfp4_bruteforce_noncausal_tiny():
+    cfg = W.C0.scaled(Hq=1, Hkv=1)
+    q, k, v, qd, kd, vc, sv = _prepare(cfg)
+    rows = [0, 5, 127, 128, 200, 255]
+    O, _ = A.attention_prefill(qd, kd, vc, sv, False, rows=np.array(rows), p_fmt="mxfp4")
+    ref = bf.attention_rows(rows, qd[0, 0].tolist(), kd[0, 0].tolist(), vc[0, 0].tolist(), sv[0, 0].tolist(),
+                            None, None, None, lambda i, j: False, 256, 256, False, 1 / np.sqrt(64), p_fmt="mxfp4")
+    assert np.abs(O[0, 0] - np.array(ref)).max() <= 1e-6 * np.abs(ref).max()
+    O8, _ = A.attention_prefill(qd, kd, vc, sv, False, rows=np.array(rows))
+    assert np.abs(O8 - O).max() > 1e-3 * np.abs(O).max()          # the FP4 rounding is applied
+
+
+def test_p_mxfp4_bruteforce_causal_offset_with_selection():
+    # causal with an offset: the diagonal tile's masked keys enter their blocks as zeros; selected tiles
+    # keep bf16 probabilities
+    cfg = SMALL_GQA_OFF.scaled(Hq=2, Hkv=1, Lq=128, Lk=384, qk_fmt="mxfp4", hadamard=False)
+    q, k, v, qd, kd, vc, sv = _prepare(cfg)
+    bitmap = np.zeros((1, 2, 1, 3), np.uint8); bitmap[0, 1, 0, 1] = 1; bitmap[0, 0, 0, 2] = 1
+    rows = np.array([0, 1, 40, 64, 127])
+    O, _ = A.attention_prefill(qd, kd, vc, sv, True, q_orig=q, k_orig=k, v_orig=v, bitmap=bitmap, rows=rows,
+                               p_fmt="mxfp4")
+    Oo, _ = A.attention_prefill(qd, kd, vc, sv, True, q_orig=q, k_orig=k, v_orig=v, bitmap=bitmap, rows=rows,
+                                p_fmt="mxfp4", heads=[(0, 0), (0, 1)])
+    for h in range(2):
+        ref = bf.attention_rows(rows.tolist(), qd[0, h].tolist(), kd[0, 0].tolist(), vc[0, 0].tolist(),
+                                sv[0, 0].tolist(), q[0, h].tolist(), k[0, 0].tolist(), v[0, 0].tolist(),
+                                lambda i, j, h=h: bool(bitmap[0, h, i, j]), 128, 384, True, 1 / np.sqrt(128),
+                                p_fmt="mxfp4")
+        assert np.abs(O[0, h] - np.array(ref)).max() <= 1e-6 * np.abs(ref).max()
+        assert np.array_equal(O[0, h], Oo[0, h])
+
+
+def test_p_mxfp4_online_equals_two_pass():
+    cfg = SMALL
+    q, k, v, qd, kd, vc, sv = _prepare(cfg)
+    rows = np.arange(256, 384)
+    kw = dict(q_orig_rows=None, k_orig=None, v_orig=None, sel_row=None, p_fmt="mxfp4")
+    o1, l1 = A.attend_rows(rows, qd[0, 0, rows], kd[0, 0], vc[0, 0], sv[0, 0], 1 / np.sqrt(128), 512, 512, True, **kw)
+    o2, l2 = A.attend_rows_online(rows, qd[0, 0, rows], kd[0, 0], vc[0, 0], sv[0, 0], 1 / np.sqrt(128), 512, 512,
+                                  True, tile_order=[2, 0, 1], **kw)
+    assert np.abs(o1 - o2).max() <= 1e-12 * np.abs(o1).max() and np.abs(l1 - l2).max() <= 1e-12
+
+
+def _representable_row_case(block_vals, d=16, seed=5):
+    """One query row against one 128-key tile with X = 0 for every key (q = 0), so P' = 1 and
+    P' w = s_v 2^-e: with s_v = block_vals (a multiple of 32 values, then 1/64 for the rest), sigma = max s_v."""
+    rng = np.random.default_rng(seed)
+    q = np.zeros((1, d))
+    k = rng.standard_normal((128, d))
+    codes = rng.integers(0, 0x7e, size=(128, d)).astype(np.uint8) | (rng.integers(0, 2, size=(128, d)) * 0x80).astype(np.uint8)
+    sv = np.full(128, 1.0 / 64, np.float32)
+    sv[:len(block_vals)] = block_vals
+    return q, k, codes, sv
+
+
+def test_p_mxfp4_is_exact_when_every_block_is_representable():
+    # every block's largest P' w is 6 * 2^e_b and the rest are E2M1 values times 2^e_b: the MXFP4
+    # rounding is the identity, so O equals the unrounded-probability result
+    base = np.array([6, 4, 3, 2, 1.5, 1, 0.5, 0] * 4, np.float32)
+    vals = np.concatenate([base * 2.0 ** -4, base * 2.0 ** -9, base * 2.0 ** 3, base])
+    q, k, codes, sv = _representable_row_case(vals)
+    o4, _ = A.attend_rows(np.array([0]), q, k, codes, sv, 1.0, 1, 128, False, p_fmt="mxfp4")
+    o0, _ = A.attend_rows(np.array([0]), q, k, codes, sv, 1.0, 1, 128, False, round_p=False)
+    assert np.array_equal(o4, o0)
+    # away from ties (block maxima 4 * 2^k, between the scale boundaries 3 * 2^k and 6 * 2^k; every value
+    # on the grid, none at a midpoint) the slack is zero
+    base4 = np.array([4, 3, 2, 1.5, 1, 0.5, 0, 4] * 4, np.float32)
+    qz, kz, cz, svz = _representable_row_case(np.concatenate([base4 * 2.0 ** -4, base4, base4 * 2.0 ** -7]))
+    oz, _ = A.attend_rows(np.array([0]), qz, kz, cz, svz, 1.0, 1, 128, False, p_fmt="mxfp4")
+    oz0, _ = A.attend_rows(np.array([0]), qz, kz, cz, svz, 1.0, 1, 128, False, round_p=False)
+    assert np.array_equal(oz, oz0)
+    assert np.all(A.rounding_slack(np.array([0]), qz, kz, cz, svz, 1.0, 1, 128, False, p_fmt="mxfp4") == 0.0)
+    # one value off the grid (1.25 * 2^3 between 1 and 1.5): that element moves to a neighbour, the rest stay
+    sv2 = sv.copy(); sv2[64 + 5] = np.float32(1.25 * 2.0 ** 3)
+    o4b, _ = A.attend_rows(np.array([0]), q, k, codes, sv2, 1.0, 1, 128, False, p_fmt="mxfp4")
+    e = A.fold_exponent(float(sv2.max()))
+    vals8 = np.vectorize(bf.e4m3_value)(codes).astype(np.float64)
+    # the changed element's MXFP4 value by the brute-force quantizer, at its block's scale
+    blk = sv2[64:96].astype(np.float64) * 2.0 ** -e
+    eb = Q.mx_scale_exponent(blk.max())
+    q69 = bf.e2m1_value(bf.e2m1_encode(blk[5] * 2.0 ** -eb)) * 2.0 ** eb
+    o0b, _ = A.attend_rows(np.array([0]), q, k, codes, sv2, 1.0, 1, 128, False, round_p=False)
+    want = o0b[0] + 2.0 ** e * (q69 - blk[5]) * vals8[69] / 128.0
+    assert np.allclose(o4b[0], want, rtol=0, atol=1e-12 * np.abs(want).max())
+    assert q69 != blk[5]
+
+
+def test_rounding_slack_mxfp4_block_scale_tie():
+    # block 1's largest P' w is exactly 6 * 2^e_b: under any evaluation error the block may take the next
+    # scale 2^(e_b + 1), where 1.5 * 2^e_b (the midpoint of the coarser grid's 1 and 2) rounds to 2 * 2^e_b
+    # (ties to the even code); the slack must hold exactly that change, and nothing for the other blocks
+    base = np.array([6, 4, 3, 2, 1.5, 1, 0.5, 0] * 4, np.float32)
+    vals = np.concatenate([base * 2.0 ** -4, base * 2.0 ** -2])
+    q, k, codes, sv = _representable_row_case(vals)
+    e = A.fold_exponent(float(sv.max()))
+    sl = A.rounding_slack(np.array([0]), q, k, codes, sv, 1.0, 1, 128, False, p_fmt="mxfp4")
+    pw = sv.astype(np.float64) * 2.0 ** -e
+    vals8 = np.abs(np.vectorize(bf.e4m3_value)(codes).astype(np.float64))
+    delta = np.zeros(128)
+    for b in range(4):
+        blk = pw[32 * b:32 * b + 32]
+        eb = Q.mx_scale_exponent(blk.max())
+        fine = np.array([bf.e2m1_value(bf.e2m1_encode(x * 2.0 ** -eb)) * 2.0 ** eb for x in blk])
+        if b < 2:        # at a scale boundary: also the coarser grid
+            coarse = np.array([bf.e2m1_value(bf.e2m1_encode(x * 2.0 ** -(eb + 1))) * 2.0 ** (eb + 1) for x in blk])
+            delta[32 * b:32 * b + 32] = np.abs(coarse - fine)
+    want = 2.0 ** e * (delta @ vals8) / 128.0
+    assert delta.max() > 0 and np.allclose(sl[0], want, rtol=1e-12, atol=0)
