@@ -23,7 +23,7 @@ FA4_OK, FA4_ERR_NULL, FA4_ERR_SHAPE, FA4_ERR_UNSUPPORTED, FA4_ERR_ALIGN, FA4_ERR
 FA4_F32, FA4_BF16 = 0, 1
 FA4_MXFP4, FA4_NVFP4, FA4_FP8_TOKEN, FA4_MXFP8, FA4_MXFP4_KEYS = 0, 1, 2, 3, 4
 FA4_HADAMARD128, FA4_DUAL_RESIDUAL, FA4_SCALE_SEARCH = 1, 2, 4
-FA4_P_FP8, FA4_P_NVFP4 = 0, 1                      # decode probability formats
+FA4_P_FP8, FA4_P_NVFP4, FA4_P_MXFP4 = 0, 1, 2         # probability formats (decode: FP8, NVFP4; prefill: FP8, MXFP4)
 
 EXPORTS = ["fa4_quantize_blockscaled", "fa4_quantize_prefill", "fa4_smoothing_factors", "fa4_select_tiles", "fa4_attn_fwd", "fa4_decode_workspace_bytes",
            "fa4_decode_paged", "fa4_decode_paged_noalloc", "fa4_status_string", "fa4_last_error"]
@@ -51,7 +51,7 @@ class AttnArgs(ctypes.Structure):
                 ("v_fold_w", _p), ("v_fold_scale", _p), ("q_bf16", _p), ("k_bf16", _p), ("v_bf16", _p), ("bitmap", _p),
                 ("B", _i32), ("Hq", _i32), ("Hkv", _i32), ("Lq", _i32), ("Lk", _i32), ("d", _i32),
                 ("causal", _i32), ("softmax_scale", _f32), ("o", _p), ("lse", _p), ("v_fmt", _i32),
-                ("v_block_scales", _p)]
+                ("v_block_scales", _p), ("p_fmt", _i32)]
 
 
 class DecodeArgs(ctypes.Structure):
@@ -254,11 +254,13 @@ def select_tiles(q_norm2, k_norm2, causal, num=5, den=100):
 # ---------------------------------------------------------------------------------------------------- attention
 
 def attn_fwd(q, k, v, causal, fmt, Hq, Hkv, Lq, Lk, d, B=1, bitmap=None, q_bf16=None, k_bf16=None,
-             v_bf16=None, softmax_scale=None, want_lse=True, out=None, lse=None, v_fmt=FA4_FP8_TOKEN):
+             v_bf16=None, softmax_scale=None, want_lse=True, out=None, lse=None, v_fmt=FA4_FP8_TOKEN,
+             p_fmt=FA4_P_FP8):
     """Prefill attention from quantized operands (dicts as returned by quantize()).
 
     q/k hold MXFP4, NVFP4 or MXFP8 codes and scales; v holds FP8 per-token codes and scales
     (v_fmt FA4_FP8_TOKEN) or 4-bit V (v_fmt FA4_MXFP4_KEYS, MXFP4 Q/K only; selected tiles read v_bf16).
+    p_fmt: probabilities of the quantized tiles, FA4_P_FP8 or FA4_P_MXFP4 (MXFP4 Q/K, FP8 V, d = 128).
     Returns (o [B, Hq, Lq, d] float32, lse [B, Hq, Lq] float32 or None).
     """
     v4 = v_fmt == FA4_MXFP4_KEYS
@@ -274,7 +276,7 @@ def attn_fwd(q, k, v, causal, fmt, Hq, Hkv, Lq, Lk, d, B=1, bitmap=None, q_bf16=
                  v["codes"].data_ptr(), _ptr(v.get("scales")), _ptr(v.get("fold_w")), _ptr(v.get("fold_scale")),
                  _ptr(q_bf16), _ptr(k_bf16), _ptr(v_bf16), _ptr(bitmap),
                  B, Hq, Hkv, Lq, Lk, d, int(causal), softmax_scale, out.data_ptr(), _ptr(lse if want_lse else None),
-                 v_fmt if v4 else 0, _ptr(v.get("block_scales")) if v4 else None)
+                 v_fmt if v4 else 0, _ptr(v.get("block_scales")) if v4 else None, p_fmt)
     _check(lib.fa4_attn_fwd(ctypes.byref(a), _stream()), "fa4_attn_fwd")
     return out, (lse if want_lse else None)
 
@@ -415,9 +417,10 @@ class DecodeMlaRunner:
 # ---------------------------------------------------------------------------------------------------- pipelines
 
 def prefill(q, k, v, causal, fmt=FA4_MXFP4, hadamard=False, select=None, softmax_scale=None, want_lse=True,
-            smooth=None, search=False, v_fmt=FA4_FP8_TOKEN):
+            smooth=None, search=False, v_fmt=FA4_FP8_TOKEN, p_fmt=FA4_P_FP8):
     """Whole prefill path: quantize Q/K (MXFP4 or NVFP4, optional Hadamard), V to FP8 per token,
-    optionally select the top num/den tiles for bf16 (select=(num, den)), then fused attention.
+    optionally select the top num/den tiles for bf16 (select=(num, den)), then fused attention with the
+    probabilities in p_fmt (FA4_P_FP8 or FA4_P_MXFP4).
 
     q [B, Hq, Lq, d], k / v [B, Hkv, Lk, d]: contiguous float32 or bf16 CUDA tensors (bf16 needed for
     selection, whose tiles read the originals). Returns a dict with 'o', 'lse', 'bitmap', 'counts',
@@ -439,7 +442,7 @@ def prefill(q, k, v, causal, fmt=FA4_MXFP4, hadamard=False, select=None, softmax
         bitmap, counts = select_tiles(qq["norm2"], kq["norm2"], causal, select[0], select[1])
     o, lse = attn_fwd(qq, kq, vq, causal, fmt, Hq, Hkv, Lq, Lk, d, B=B, bitmap=bitmap,
                       q_bf16=q if sel else None, k_bf16=k if sel else None, v_bf16=v if sel else None,
-                      softmax_scale=softmax_scale, want_lse=want_lse, v_fmt=v_fmt)
+                      softmax_scale=softmax_scale, want_lse=want_lse, v_fmt=v_fmt, p_fmt=p_fmt)
     return {"o": o, "lse": lse, "bitmap": bitmap, "counts": counts, "q": qq, "k": kq, "v": vq}
 
 
@@ -495,7 +498,7 @@ class PrefillRunner:
     """
 
     def __init__(self, q, k, v, causal, fmt=FA4_MXFP4, hadamard=False, select=None, softmax_scale=None,
-                 smooth=None, search=False, v_fmt=FA4_FP8_TOKEN):
+                 smooth=None, search=False, v_fmt=FA4_FP8_TOKEN, p_fmt=FA4_P_FP8):
         self.q, self.k, self.v = q, k, v
         B, Hq, Lq, d = q.shape
         Hkv, Lk = k.shape[1], k.shape[2]
@@ -552,7 +555,7 @@ class PrefillRunner:
                               v.data_ptr() if self.sel else None, _ptr(self.bitmap),
                               B, Hq, Hkv, Lq, Lk, d, int(causal), softmax_scale, self.o.data_ptr(),
                               self.lse.data_ptr(), FA4_MXFP4_KEYS if v4 else 0,
-                              _ptr(self.vq.get("block_scales")) if v4 else None)
+                              _ptr(self.vq.get("block_scales")) if v4 else None, p_fmt)
         self.shape = (B, Hq, Hkv, Lq, Lk, d)
 
     def quantize(self, stream=None):

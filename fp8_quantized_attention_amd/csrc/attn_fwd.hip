@@ -299,6 +299,74 @@ __device__ __forceinline__ void fp8_block_w(const v16f &Skb, const float4 *w4, f
   }
 }
 
+// MXFP4 probabilities: this lane's half of one 32-key block (keys 32 kb + 8 a4 + 4 hh + u, element
+// 4 a4 + u of Skb) becomes P' w_c in place; ts sums P' and am takes the largest P' w_c.
+__device__ __forceinline__ void p4_block_w(v16f &Skb, const float4 *w4, float cs, float rr0, float &ts, float &am) {
+#pragma unroll
+  for (int a4 = 0; a4 < 4; a4++) {
+    const float wv[4] = {w4[a4].x, w4[a4].y, w4[a4].z, w4[a4].w};
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(Skb[4 * a4 + u], cs, -rr0));
+      ts = (a4 == 0 && u == 0) ? p : ts + p;
+      Skb[4 * a4 + u] = p * wv[u];
+    }
+  }
+  am = block_max(Skb);
+}
+
+// Biased E8M0 code of the MX scale of a block maximum a >= 0: the smallest power of two 2^e with
+// 6 * 2^e >= a. With a = 1.f * 2^E, 6 * 2^e >= a holds from e = E - 2 when f <= 0.5 and from e = E - 1
+// otherwise; adding 0x3fffff to the bits carries into the exponent field exactly when f > 0.5. Zero and
+// subnormal maxima give code 0 (2^-127).
+__device__ __forceinline__ int mx_p_code(float a) {
+  const int c = (int)((__float_as_uint(a) + 0x3fffffu) >> 23) - 2;
+  return c < 0 ? 0 : c;
+}
+
+// 16 values (x[8 w + j] into nibble j of word w) as E2M1 codes of x / sc, sc a power of two
+// (round to nearest even; the hardware conversion divides by its power-of-two scale).
+__device__ __forceinline__ void pack_fp4x16(const v16f &x, float sc, uint32_t &w0, uint32_t &w1) {
+  uint32_t a = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x[0], x[1], sc, 0);
+  a = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a, x[2], x[3], sc, 1);
+  a = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a, x[4], x[5], sc, 2);
+  w0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(a, x[6], x[7], sc, 3);
+  uint32_t b = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x[8], x[9], sc, 0);
+  b = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(b, x[10], x[11], sc, 1);
+  b = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(b, x[12], x[13], sc, 2);
+  w1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(b, x[14], x[15], sc, 3);
+}
+
+// The FP4 P^T operand of one PV half from the P' w of key blocks 2t (S0) and 2t + 1 (S1). Lane half hh's
+// operand holds the 32 keys of block 2t + hh: nibbles 0..15 the keys 8 a + u of that block (held by lane
+// half 0), nibbles 16..31 the keys 8 a + 4 + u (held by lane half 1); the FP8 V^T operand pairs its
+// k positions with these keys. Each lane quantizes its own halves of both blocks under the block
+// scales (block maxima over both lane halves), then swaps one block's words with lane l ^ 32
+// (v_permlane32_swap exchanges the upper lanes of its first register with the lower lanes of its second).
+// Returns the operand and, in sb, the biased E8M0 B-operand scale: block scale times the tile weight
+// 2^kBc; a block below 2^-127 adds nothing representable and is zeroed.
+__device__ __forceinline__ v8i p4_operand(const v16f &S0, const v16f &S1, float am0, float am1, int hh, int kBc,
+                                          int &sb) {
+  const int c0 = mx_p_code(max_lane32(am0)), c1 = mx_p_code(max_lane32(am1));
+  uint32_t o0[2], o1[2];
+  pack_fp4x16(S0, __uint_as_float((uint32_t)c0 << 23), o0[0], o0[1]);
+  pack_fp4x16(S1, __uint_as_float((uint32_t)c1 << 23), o1[0], o1[1]);
+  int wv[4];
+#pragma unroll
+  for (int k = 0; k < 2; k++) {
+    const auto x = __builtin_amdgcn_permlane32_swap(o0[k], o1[k], false, false);
+    wv[k] = (int)x[0];
+    wv[k + 2] = (int)x[1];
+  }
+  sb = (hh ? c1 : c0) + kBc;
+  if (sb < 0) {
+    sb = 0;
+#pragma unroll
+    for (int k = 0; k < 4; k++) wv[k] = 0;
+  }
+  return (v8i){wv[0], wv[1], wv[2], wv[3], 0, 0, 0, 0};
+}
+
 // The tile's row reference in log2 units: the smallest integer r >= its largest score, so that
 // P' = 2^(S cs - r) <= 1 (its largest value lies in (1/2, 1]). The maximum runs over independent
 // partial results, so no long dependent chain forms.
@@ -539,7 +607,7 @@ __device__ __forceinline__ void tile_step(const AttnArgs &a, const LaneOff &lo, 
   lsum += __builtin_ldexpf(V4 ? tsum * (1.0f / 448.0f) : tsum, kB);   // 4-bit V: ts summed 448 P'
 }
 
-template <int D, int QF, bool CAUSAL, bool SEL, bool V4 = false>
+template <int D, int QF, bool CAUSAL, bool SEL, bool V4 = false, bool P4 = false>
 __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
   constexpr int NDB = D / 32;        // 32-row blocks of d in O^T
   typedef AttnLds<D, QF, SEL> L;
@@ -740,7 +808,8 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
         // next-tile QK^T reads the other K buffer's stale (in-bounds) bytes and its scores are never used:
         // issuing it unconditionally keeps the score registers in place.
         const bool diag_next = CAUSAL && tn == last;
-        float ts[4], mp[3];
+        float ts[4], mp[3], am[2];
+        int psb[2];                  // MXFP4 P: biased E8M0 B-operand scale of each PV half (per lane)
         v8i pop[2];                  // packed FP8 probabilities: the P^T operand of each PV half (keys 64 t ..)
         v8i vop[4];
         int vsw[4];
@@ -783,12 +852,19 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
           }
           // ---- VALU
           if (r < 4) {
-            int x0, x1, x2, x3;
-            fp8_block_w<V4>(S[r], w4, cs, rr0, ts[r], x0, x1, x2, x3);
-            pop[r >> 1][4 * (r & 1) + 0] = x0;
-            pop[r >> 1][4 * (r & 1) + 1] = x1;
-            pop[r >> 1][4 * (r & 1) + 2] = x2;
-            pop[r >> 1][4 * (r & 1) + 3] = x3;
+            if constexpr (P4) {
+              // MXFP4 P: P' w in place; after each pair of blocks, their FP4 operand (the next tile's QK^T
+              // into those registers waits for it)
+              p4_block_w(S[r], w4, cs, rr0, ts[r], am[r & 1]);
+              if (r & 1) pop[r >> 1] = p4_operand(S[r - 1], S[r], am[0], am[1], hh, kBc, psb[r >> 1]);
+            } else {
+              int x0, x1, x2, x3;
+              fp8_block_w<V4>(S[r], w4, cs, rr0, ts[r], x0, x1, x2, x3);
+              pop[r >> 1][4 * (r & 1) + 0] = x0;
+              pop[r >> 1][4 * (r & 1) + 1] = x1;
+              pop[r >> 1][4 * (r & 1) + 2] = x2;
+              pop[r >> 1][4 * (r & 1) + 3] = x3;
+            }
           } else {
 #pragma unroll
             for (int b = 0; b < 3; b++) {
@@ -804,8 +880,8 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
                 acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vpend[mb], ppend, acc[mb], 4, 0, 2, vspend[mb], 0,
                                                                           kpend + 127);
               else
-                acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vpend[mb], ppend, acc[mb], 0, 0, 0, spend, 0,
-                                                                          kpend + 127);
+                acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vpend[mb], ppend, acc[mb], 0, P4 ? 4 : 0, 0, spend,
+                                                                          0, kpend + 127);
             }
           } else {
             S[qb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4((v8i){k0[0], k0[1], k0[2], k0[3], 0, 0, 0, 0}, qop4[0],
@@ -816,6 +892,9 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
                 if constexpr (V4)
                   acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[mb], pop[0], acc[mb], 4, 0, 0, vsw[mb], 0,
                                                                             kBc + 127);
+                else if constexpr (P4)
+                  acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[mb], pop[0], acc[mb], 0, 4, 0, scA, 0,
+                                                                            psb[0]);
                 else
                   acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[mb], pop[0], acc[mb], 0, 0, 0, scA, 0,
                                                                             kBc + 127);
@@ -857,7 +936,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
           vspend[mb] = vsw[mb];
         }
         ppend = pop[1];
-        kpend = kBc;
+        kpend = P4 ? psb[1] - 127 : kBc;
         spend = scA;
         const float tsum = (ts[0] + ts[1]) + (ts[2] + ts[3]);
         lsum += __builtin_ldexpf(V4 ? tsum * (1.0f / 448.0f) : tsum, kB);
@@ -890,7 +969,8 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
           acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vpend[mb], ppend, acc[mb], 4, 0, 2, vspend[mb], 0,
                                                                     kpend + 127);
         else
-          acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vpend[mb], ppend, acc[mb], 0, 0, 0, spend, 0, kpend + 127);
+          acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vpend[mb], ppend, acc[mb], 0, P4 ? 4 : 0, 0, spend, 0,
+                                                                    kpend + 127);
       }
     }
   } else if (QF == FA4_MXFP4) {
@@ -1120,9 +1200,9 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
 }
 
 // Kernels whose LDS exceeds the default dynamic limit are opted in (idempotent, cheap).
-template <int D, int QF, bool CAUSAL, bool SEL, bool V4 = false>
+template <int D, int QF, bool CAUSAL, bool SEL, bool V4 = false, bool P4 = false>
 static hipError_t allow_lds() {
-  return hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_fwd_kernel<D, QF, CAUSAL, SEL, V4>),
+  return hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_fwd_kernel<D, QF, CAUSAL, SEL, V4, P4>),
                              hipFuncAttributeMaxDynamicSharedMemorySize, AttnLds<D, QF, SEL>::BYTES);
 }
 
@@ -1139,6 +1219,22 @@ static hipError_t launch_attn_v4_t(const AttnArgs &x, hipStream_t s) {
 static hipError_t launch_attn_v4(const AttnArgs &x, bool causal, bool sel, hipStream_t s) {
   if (causal) return sel ? launch_attn_v4_t<true, true>(x, s) : launch_attn_v4_t<true, false>(x, s);
   return sel ? launch_attn_v4_t<false, true>(x, s) : launch_attn_v4_t<false, false>(x, s);
+}
+
+// MXFP4 Q/K, FP8 V, MXFP4 probabilities (d = 128)
+template <bool CAUSAL, bool SEL>
+static hipError_t launch_attn_p4_t(const AttnArgs &x, hipStream_t s) {
+  dim3 grid((unsigned)((int64_t)(x.Lq / 128) * x.Hq * x.B));
+  hipError_t e = allow_lds<128, FA4_MXFP4, CAUSAL, SEL, false, true>();
+  if (e != hipSuccess) return e;
+  constexpr size_t lds_bytes = AttnLds<128, FA4_MXFP4, SEL>::BYTES;
+  hipLaunchKernelGGL((attn_fwd_kernel<128, FA4_MXFP4, CAUSAL, SEL, false, true>), grid, dim3(ATT_THREADS), lds_bytes,
+                     s, x);
+  return hipGetLastError();
+}
+static hipError_t launch_attn_p4(const AttnArgs &x, bool causal, bool sel, hipStream_t s) {
+  if (causal) return sel ? launch_attn_p4_t<true, true>(x, s) : launch_attn_p4_t<true, false>(x, s);
+  return sel ? launch_attn_p4_t<false, true>(x, s) : launch_attn_p4_t<false, false>(x, s);
 }
 
 template <int D, int QF>
@@ -1173,6 +1269,7 @@ hipError_t launch_attn(const fa4_attn_args *p, hipStream_t s) {
   if (x.B == 0 || x.Hq == 0 || x.Lq == 0) return hipSuccess;
   const bool causal = p->causal != 0, sel = p->bitmap != nullptr;
   if (p->v_fmt == FA4_MXFP4_KEYS) return launch_attn_v4(x, causal, sel, s);
+  if (p->p_fmt == FA4_P_MXFP4) return launch_attn_p4(x, causal, sel, s);
   if (p->fmt == FA4_MXFP4) {
     if (p->d == 64) return launch_attn_t<64, FA4_MXFP4>(x, causal, false, s);
     return launch_attn_t<128, FA4_MXFP4>(x, causal, sel, s);

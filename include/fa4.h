@@ -45,7 +45,8 @@ typedef enum {
 
 enum { FA4_F32 = 0, FA4_BF16 = 1 };                      /* input element types       */
 enum { FA4_MXFP4 = 0, FA4_NVFP4 = 1, FA4_FP8_TOKEN = 2, FA4_MXFP8 = 3, FA4_MXFP4_KEYS = 4 }; /* quantized formats */
-enum { FA4_P_FP8 = 0, FA4_P_NVFP4 = 1 };                   /* decode probability formats */
+enum { FA4_P_FP8 = 0, FA4_P_NVFP4 = 1, FA4_P_MXFP4 = 2 };  /* probability formats (decode: FP8, NVFP4;
+                                                               prefill: FP8, MXFP4)        */
 enum { FA4_HADAMARD128 = 1u << 0, FA4_DUAL_RESIDUAL = 1u << 1, FA4_SCALE_SEARCH = 1u << 2 }; /* quantizer flags */
 
 /* ------------------------------------------------------------------------------------------------
@@ -220,6 +221,12 @@ fa4_status fa4_select_tiles(const float *q_norm2, const float *k_norm2, int32_t 
  * fa4_quantize_blockscaled's FA4_MXFP4_KEYS output; v_scales and v_fold_* are not read. Quantized tiles
  * then take P^ = E4M3(448 P') and T = (1/448) sum_c P^ v^_c with the dequantized 4-bit values v^ (FP4
  * V^T times FP8 P^T in one block-scaled MFMA); selected tiles (with a bitmap) read v_bf16 as usual.
+ * FP4 probabilities (p_fmt = FA4_P_MXFP4; MXFP4 Q/K, FP8 V, d = 128; "BitDecoding-FP4": probabilities
+ * in FP4 under a scale that cannot underflow, "MXFP vs NVFP4" section 2.1: the MX block): in each
+ * unselected tile row, P' w_c over 32 consecutive keys (keys 128 j + 32 b .. + 31) is one MXFP4 block:
+ * 2^e_b = the smallest power of two with 6 * 2^e_b >= its largest P' w, P^ = E2M1(P' w 2^-e_b) 2^e_b,
+ * T = 2^e * sum_c P^ * E4M3value(Vcode_c) (FP8 V^T times FP4 P^T in one block-scaled MFMA, e_b and the
+ * tile weight as P^T's E8M0 operand scale). p_fmt = 0 (FA4_P_FP8) keeps the FP8 probabilities above.
  */
 typedef struct {
   int32_t fmt;                                  /* FA4_MXFP4, FA4_NVFP4 or FA4_MXFP8 (Q and K) */
@@ -236,6 +243,7 @@ typedef struct {
   int32_t v_fmt;                               /* 0 or FA4_FP8_TOKEN: v_codes/v_scales/v_fold_* as above;
                                                   FA4_MXFP4_KEYS: 4-bit V (see below)                  */
   const uint8_t *v_block_scales;               /* FA4_MXFP4_KEYS: E8M0 [B][Hkv][d][Lk/32]             */
+  int32_t p_fmt;                               /* FA4_P_FP8 (0) or FA4_P_MXFP4 (see above)            */
 } fa4_attn_args;
 
 fa4_status fa4_attn_fwd(const fa4_attn_args *a, void *stream);

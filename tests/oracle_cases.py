@@ -90,14 +90,14 @@ def prefill_reference(cfg, seed, heads, rows, select=None, q_all=None, k_all=Non
                                    None if sv is None else sv[None, None], cfg.causal,
                                    q_orig=q[None, None], k_orig=k[None, None], v_orig=v[None, None],
                                    bitmap=None if bm is None else bm[None, None], rows=rows,
-                                   v_deq=None if vd is None else vd[None, None])
+                                   v_deq=None if vd is None else vd[None, None], p_fmt=cfg.p_fmt)
         outs.append(O[0, 0]); lses.append(L[0, 0])
         if slack:
             slacks.append(A.prefill_rounding_slack(
                 qd[None, None], kd[None, None], None if vc is None else vc[None, None],
                 None if sv is None else sv[None, None], cfg.causal, q_orig=q[None, None], k_orig=k[None, None],
                 v_orig=v[None, None], bitmap=None if bm is None else bm[None, None], rows=rows,
-                v_deq=None if vd is None else vd[None, None])[0, 0])
+                v_deq=None if vd is None else vd[None, None], p_fmt=cfg.p_fmt)[0, 0])
     if slack:
         return np.stack(outs), np.stack(lses), bitmaps, np.stack(slacks)
     return np.stack(outs), np.stack(lses), bitmaps

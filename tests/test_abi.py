@@ -161,7 +161,7 @@ def _attn(**kw):
     base = dict(fmt=fa4.FA4_MXFP4, q_codes=256, q_scales=256, q_tscale=None, k_codes=256, k_scales=256,
                 k_tscale=None, v_codes=256, v_scales=256, v_fold_w=256, v_fold_scale=256, q_bf16=None, k_bf16=None, v_bf16=None, bitmap=None,
                 B=1, Hq=4, Hkv=2, Lq=256, Lk=512, d=128, causal=1, softmax_scale=0.088, o=256, lse=None,
-                v_fmt=0, v_block_scales=None)
+                v_fmt=0, v_block_scales=None, p_fmt=fa4.FA4_P_FP8)
     base.update(kw)
     return fa4.AttnArgs(*[base[f] for f, _ in fa4.AttnArgs._fields_])
 
@@ -192,6 +192,15 @@ def test_attention_rejects_before_launch():
     assert call(_attn(**{**v4, "v_block_scales": None})) == fa4.FA4_ERR_NULL
     assert call(_attn(**{**v4, "v_block_scales": 260})) == fa4.FA4_ERR_ALIGN
     assert call(_attn(**v4, Lq=0)) == fa4.FA4_OK
+    # MXFP4 probabilities: MXFP4 Q/K, FP8 V, d = 128 (validated before the empty-shape early return)
+    assert call(_attn(p_fmt=fa4.FA4_P_NVFP4)) == fa4.FA4_ERR_UNSUPPORTED
+    assert call(_attn(p_fmt=9)) == fa4.FA4_ERR_UNSUPPORTED
+    assert call(_attn(p_fmt=fa4.FA4_P_MXFP4, **v4)) == fa4.FA4_ERR_UNSUPPORTED
+    assert call(_attn(p_fmt=fa4.FA4_P_MXFP4, fmt=fa4.FA4_NVFP4, q_tscale=256, k_tscale=256)) == fa4.FA4_ERR_UNSUPPORTED
+    assert call(_attn(p_fmt=fa4.FA4_P_MXFP4, fmt=fa4.FA4_MXFP8)) == fa4.FA4_ERR_UNSUPPORTED
+    assert call(_attn(p_fmt=fa4.FA4_P_MXFP4, d=64)) == fa4.FA4_ERR_UNSUPPORTED
+    assert call(_attn(p_fmt=fa4.FA4_P_MXFP4, v_fold_w=None)) == fa4.FA4_ERR_NULL
+    assert call(_attn(p_fmt=fa4.FA4_P_MXFP4, Lq=0)) == fa4.FA4_OK
 
 
 def test_select_rejects_before_launch():

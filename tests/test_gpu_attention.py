@@ -25,8 +25,9 @@ def _run(fa4, cfg, seed=0, select=None):
     q, k, v = W.prefill_inputs(cfg, seed)
     fmt = {"mxfp4": fa4.FA4_MXFP4, "nvfp4": fa4.FA4_NVFP4, "mxfp8": fa4.FA4_MXFP8}[cfg.qk_fmt]
     vf = fa4.FA4_MXFP4_KEYS if cfg.v_fmt == "mxfp4k" else fa4.FA4_FP8_TOKEN
+    pf = fa4.FA4_P_MXFP4 if cfg.p_fmt == "mxfp4" else fa4.FA4_P_FP8
     res = fa4.prefill(q.cuda(), k.cuda(), v.cuda(), cfg.causal, fmt=fmt, hadamard=cfg.hadamard, select=select,
-                      v_fmt=vf)
+                      v_fmt=vf, p_fmt=pf)
     torch.cuda.synchronize()
     return (q, k, v), res
 
@@ -265,12 +266,17 @@ def _jump_inputs(causal, factors, seed=31):
 @pytest.mark.parametrize("factors", [(1, 1, 1, 8, 1, 1, 1, 1), (1, 2, 40, 1, 1, 1, 160, 1)],
                          ids=["raise_once", "raise_past_smallest_weight"])
 @pytest.mark.parametrize("select", [None, (25, 100)])
-def test_reference_jumps(fa4, causal, factors, select):
+@pytest.mark.parametrize("p4", [False, True], ids=["p8", "p4"])
+def test_reference_jumps(fa4, causal, factors, select, p4):
+    # p4: MXFP4 probabilities, whose per-block E8M0 scale carries the tile weight (and the pending half's
+    # weight follows a raised reference)
     from oracle import quant as Q
     from oracle import selection as S
     q, k, v = _jump_inputs(causal, factors)
     L = q.shape[2]
-    res = fa4.prefill(q.cuda(), k.cuda(), v.cuda(), causal, fmt=fa4.FA4_MXFP4, select=select)
+    pf = "mxfp4" if p4 else "fp8"
+    res = fa4.prefill(q.cuda(), k.cuda(), v.cuda(), causal, fmt=fa4.FA4_MXFP4, select=select,
+                      p_fmt=fa4.FA4_P_MXFP4 if p4 else fa4.FA4_P_FP8)
     torch.cuda.synchronize()
     qd, kd, vd = (t.double().numpy() for t in (q, k, v))
     qq = Q.mxfp4_dequantize(*Q.mxfp4_quantize(qd))
@@ -280,16 +286,16 @@ def test_reference_jumps(fa4, causal, factors, select):
     if select is not None:
         bm, _ = S.select_tiles(Q.row_norm2(qd), Q.row_norm2(kd), L, L, causal, *select)
         assert np.array_equal(res["bitmap"].cpu().numpy(), bm)
-    O, lse = A.attention_prefill(qq, kk, vc, sv, causal, q_orig=qd, k_orig=kd, v_orig=vd, bitmap=bm)
+    O, lse = A.attention_prefill(qq, kk, vc, sv, causal, q_orig=qd, k_orig=kd, v_orig=vd, bitmap=bm, p_fmt=pf)
     # Conditioning of this input: scores reach ~230 in log2 units, where the float32 rounding of the
     # exponent's argument (2^-24 relative) already flips bf16 and E4M3 probability codes of rows that one
     # key dominates. The oracle itself, with its softmax scale moved by one float32 ulp, differs by
     # delta; the max-abs bound is max(2e-3, 2 delta), the relative-L2 bound stays 1e-3.
     O1, _ = A.attention_prefill(qq, kk, vc, sv, causal, scale=(1.0 + 2.0 ** -23) / np.sqrt(128), q_orig=qd,
-                                k_orig=kd, v_orig=vd, bitmap=bm)
+                                k_orig=kd, v_orig=vd, bitmap=bm, p_fmt=pf)
     _, delta = rel_errors(O1, O)
     rel, mx = rel_errors(res["o"].cpu().numpy(), O)
-    what = f"jumps {factors} causal={causal} select={select}"
+    what = f"jumps {factors} causal={causal} select={select} p={pf}"
     assert rel <= 1e-3 and mx <= max(2e-3, 2 * delta), f"{what}: rel-L2 {rel:.3e} max-abs/max {mx:.3e} (delta {delta:.2e})"
     # LSE: the scores themselves are float32 sums of 128 products here reaching ~1e4, so their rounding
     # (about 2^-23 of sum |q_i k_i| per score, in units of the softmax scale) bounds the LSE agreement
@@ -300,3 +306,31 @@ def test_reference_jumps(fa4, causal, factors, select):
 def test_few_quantized_tiles_between_selected(fa4):
     """90% of the tiles in bf16: the quantized pipeline runs over one or two tiles per row of tiles."""
     _check_full(fa4, W.C2.scaled(Hq=2, Hkv=2, Lq=1024, Lk=1024), select=(90, 100))
+
+
+# ---- MXFP4 probabilities (FP8 V^T x FP4 P^T, the block scale and the tile weight as P^T's E8M0 scale)
+
+def test_p4_causal_small(fa4):
+    rel, mx, res, _ = _check_full(fa4, W.C1_P4.scaled(Hq=2, Hkv=2, Lq=512, Lk=512))
+    # the probabilities are rounded to FP4 (the result differs from the FP8-probability path)
+    (q, k, v), r8 = _run(fa4, W.C1.scaled(Hq=2, Hkv=2, Lq=512, Lk=512))
+    assert rel_errors(res["o"].cpu().numpy(), r8["o"].cpu().numpy())[0] > 1e-3
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "noncausal"])
+def test_p4_gqa_offset(fa4, causal):
+    _check_full(fa4, W.C1_P4.scaled(Hq=4, Hkv=2, Lq=256, Lk=768, causal=causal))
+    _check_full(fa4, W.C1_P4.scaled(Hq=4, Hkv=2, Lq=256, Lk=768, causal=causal), seed=1)
+
+
+@pytest.mark.parametrize("select", [(5, 100), (25, 100), (100, 100)], ids=["sel5", "sel25", "all"])
+def test_p4_with_selection(fa4, select):
+    _check_full(fa4, W.C1_P4.scaled(Hq=2, Hkv=2, Lq=512, Lk=512), select=select)
+
+
+def test_full_size_prefill_4k_p4(fa4):
+    _sampled(fa4, W.C1_P4, heads=[(0, 2), (0, 27)], nrows=96)
+
+
+def test_full_size_prefill_32k_p4_selection(fa4):
+    _sampled(fa4, W.C2.scaled(p_fmt="mxfp4"), heads=[(0, 9)], nrows=16, select=(5, 100))

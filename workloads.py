@@ -51,6 +51,7 @@ class Prefill:
     hadamard: bool = False
     select: bool = False
     v_fmt: str = "fp8"      # "fp8" (E4M3 per token) or "mxfp4k" (MXFP4, 32-blocks along the keys)
+    p_fmt: str = "fp8"      # probabilities of the quantized tiles: "fp8" (E4M3) or "mxfp4" (32-key MX blocks)
 
     def scaled(self, **kw):
         return replace(self, **kw)
@@ -92,6 +93,8 @@ WORKLOADS = [C0, C1, C2, C3, C4]
 C1_MX8 = replace(C1, name="prefill_4k_causal_mxfp8", qk_fmt="mxfp8")
 # The 4K causal prefill with 4-bit V (MXFP4 with 32-element blocks along the keys): same values as C1.
 C1_V4 = replace(C1, name="prefill_4k_causal_mxfp4_v4", v_fmt="mxfp4k")
+# The 4K causal prefill with the probabilities in MXFP4 (E8M0 scale per 32 keys) against FP8 V: same values.
+C1_P4 = replace(C1, name="prefill_4k_causal_mxfp4_p4", p_fmt="mxfp4")
 # The decode workload over an MXFP4 cache (E8M0 scale per 32 elements, no tensor scale): the same
 # sequences, lengths, pages and values as C3 (same workload id, hence the same seeds).
 C3_MX = replace(C3, name="decode_paged_mxfp4_gqa", kv_fmt="mxfp4")
