@@ -16,7 +16,8 @@ one online softmax), inputs resident in HBM. Each timed loop follows W untimed s
                 with tile selection also the error of the same kernel without selected tiles and the
                 share of that error the selected tiles remove;
   legs          the other prefill workloads (4K causal MXFP4; 128K chunked prefill with NVFP4 +
-                Hadamard and tile selection), each with its own roofline and error;
+                Hadamard and tile selection) and the 4K variants (4-bit V, MXFP8 Q/K, MXFP4
+                probabilities), each with its own roofline and error;
   decode        the paged NVFP4 decode step (64 sequences, 32 -> 8 GQA heads, contexts 8K-32K):
                 KV-cache GB/s, the decode kernels' HBM roofline and the error;
   decode_mxfp4, decode_p4, decode_mxfp4_p4
@@ -63,29 +64,31 @@ COPY_BYTES = 1 << 30                 # calibration copy: reads and writes this m
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 CSRC = os.path.join(ROOT, "fp8_quantized_attention_amd", "csrc")
 # Kernel instantiations whose counters are recorded, with the sources whose change invalidates them.
-# Attention kernel: <d, Q/K format (0 MXFP4, 1 NVFP4, 3 MXFP8), causal, selection, 4-bit V>
+# Attention kernel: <d, Q/K format (0 MXFP4, 1 NVFP4, 3 MXFP8), causal, selection, 4-bit V, MXFP4 P>
 # (MXFP4 without selection: 4K causal; MXFP4 with selection: 32K; NVFP4 with selection: the 128K
-# chunked prefill). Decode: <cache format (1 NVFP4, 0 MXFP4), probability format (0 FP8, 1 NVFP4)>.
+# chunked prefill; MXFP4 probabilities: 4K causal). Decode: <cache format (1 NVFP4, 0 MXFP4), probability format (0 FP8, 1 NVFP4)>.
 ATTN_SRC = ["attn_fwd.hip", "fa4_device.h"]
 DEC_SRC = ["decode.hip", "fa4_device.h"]
 KERNEL_SOURCES = {
-    "attn_fwd_kernel<128, 0, true, false, false>": ATTN_SRC,
-    "attn_fwd_kernel<128, 0, true, true, false>": ATTN_SRC,
-    "attn_fwd_kernel<128, 1, true, true, false>": ATTN_SRC,
+    "attn_fwd_kernel<128, 0, true, false, false, false>": ATTN_SRC,
+    "attn_fwd_kernel<128, 0, true, true, false, false>": ATTN_SRC,
+    "attn_fwd_kernel<128, 1, true, true, false, false>": ATTN_SRC,
+    "attn_fwd_kernel<128, 0, true, false, false, true>": ATTN_SRC,
     "decode_split_kernel<1, 0>": DEC_SRC,
     "decode_split_kernel<0, 0>": DEC_SRC,
     "decode_split_kernel<1, 1>": DEC_SRC,
     "decode_split_kernel<0, 1>": DEC_SRC,
     "decode_mla_kernel": ["decode_mla.hip", "fa4_device.h"],
 }
-PREFILL = [W.C1, W.C2, W.C4, W.C1_MX8, W.C1_V4]
+PREFILL = [W.C1, W.C2, W.C4, W.C1_MX8, W.C1_V4, W.C1_P4]
 
 
 def attn_kernel_name(cfg, select):
     """The attention kernel instantiation fa4_attn_fwd launches for this workload."""
     fmt = {"mxfp4": 0, "nvfp4": 1, "mxfp8": 3}[cfg.qk_fmt]
     b = lambda x: "true" if x else "false"   # noqa: E731
-    return f"attn_fwd_kernel<{cfg.d}, {fmt}, {b(cfg.causal)}, {b(select)}, {b(cfg.v_fmt == 'mxfp4k')}>"
+    return (f"attn_fwd_kernel<{cfg.d}, {fmt}, {b(cfg.causal)}, {b(select)}, {b(cfg.v_fmt == 'mxfp4k')}, "
+            f"{b(cfg.p_fmt == 'mxfp4')}>")
 
 
 def sources_sha(kernel):
@@ -272,8 +275,10 @@ def time_prefill(fa4, cfg, steps, warmup, quick=False, error=True):
     q, k, v = (t.cuda() for t in W.prefill_inputs(cfg))
     fmt = {"mxfp4": fa4.FA4_MXFP4, "nvfp4": fa4.FA4_NVFP4, "mxfp8": fa4.FA4_MXFP8}[cfg.qk_fmt]
     vf = fa4.FA4_MXFP4_KEYS if cfg.v_fmt == "mxfp4k" else fa4.FA4_FP8_TOKEN
+    pf = fa4.FA4_P_MXFP4 if cfg.p_fmt == "mxfp4" else fa4.FA4_P_FP8
     select = (5, 100) if cfg.select else None
-    run = fa4.PrefillRunner(q, k, v, cfg.causal, fmt=fmt, hadamard=cfg.hadamard, select=select, v_fmt=vf)
+    run = fa4.PrefillRunner(q, k, v, cfg.causal, fmt=fmt, hadamard=cfg.hadamard, select=select, v_fmt=vf,
+                            p_fmt=pf)
     _warm(run.run, warmup, quick)
     step_ms = _time_loop(run.run, steps)
     attn_ms = _time_loop(run.attention, steps)
@@ -284,7 +289,7 @@ def time_prefill(fa4, cfg, steps, warmup, quick=False, error=True):
         outs = {"gpu": run.o}
         if select is not None:          # the same quantized operands without selected tiles
             o_ns, _ = fa4.attn_fwd(run.qq, run.kq, run.vq, cfg.causal, fmt, cfg.Hq, cfg.Hkv, cfg.Lq, cfg.Lk, cfg.d,
-                                   B=cfg.B, want_lse=False, v_fmt=vf)
+                                   B=cfg.B, want_lse=False, v_fmt=vf, p_fmt=pf)
             outs["gpu_no_selection"] = o_ns
         torch.cuda.synchronize()
         err = prefill_error(cfg, q, k, v, outs)
@@ -305,7 +310,8 @@ def prefill_record(fa4, cfg, args, headline=False):
     kname = attn_kernel_name(cfg, cfg.select)
     rec = {
         "workload": cfg.name, "value": flops / (step_ms * 1e-3) / 1e12, "unit": "TFLOP/s", "ms_per_step": step_ms,
-        "dtype": cfg.qk_fmt + ("+fp4v" if cfg.v_fmt == "mxfp4k" else "+fp8") + ("+bf16tiles" if cfg.select else ""),
+        "dtype": cfg.qk_fmt + ("+fp4v" if cfg.v_fmt == "mxfp4k" else "+fp8") + ("+fp4p" if cfg.p_fmt == "mxfp4" else "")
+        + ("+bf16tiles" if cfg.select else ""),
         "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "Lq": cfg.Lq, "Lk": cfg.Lk,
                    "d": cfg.d, "causal": cfg.causal, "qk_format": cfg.qk_fmt, "hadamard": cfg.hadamard,
                    "bf16_tiles": "5%" if cfg.select else "none", "algorithmic_flops": flops},
@@ -516,7 +522,7 @@ def main():
     }
     if not args.no_legs:
         line["legs"] = {}
-        for lcfg in (W.C1, W.C2, W.C4):
+        for lcfg in (W.C1, W.C2, W.C4, W.C1_V4, W.C1_MX8, W.C1_P4):
             if lcfg.name != cfg.name:
                 line["legs"][lcfg.name] = prefill_record(fa4, lcfg, args)
     if not args.no_decode:
