@@ -36,6 +36,8 @@ tiles of 128 keys; column c of tile j is unmasked when not causal or c <= r + of
   4. m_r = max_j r_rj, D_r = sum_j 2^(r_rj - m_r) sum_c P'_rc (unquantized P'),
      N_r = sum_j 2^(r_rj - m_r) T_rj; O_r = N_r / D_r (returned as float32),
      LSE_r = m_r ln 2 + ln D_r.
+  MXFP4 probabilities with 4-bit V (p_fmt = "mxfp4", v_deq given): P^ = the MXFP4 quantization of P'
+     over the same 32-key blocks (no per-token scale to fold, no 448), T_rj = sum_c P^_rc v_deq_c.
   MXFP4 probabilities (p_fmt = "mxfp4", FP8 V, unselected tiles): in step 3 P^ is the MXFP4
      quantization of the row of P'_rc w_c over 32 consecutive keys of the tile (keys 128 j + 32 b ..
      + 31): per block the MX scale 2^e_b (the smallest power of two with 6 * 2^e_b >= the block's
@@ -102,7 +104,7 @@ def mxfp4_tie_delta(arg, eps):
 def _tile_terms(S, unmasked, sel, vq_vals, s_v, v_orig, round_p=True, v_deq=None, p_fmt="fp8"):
     """Per-row (r, sum P', T) of one key tile, r the tile's power-of-two row reference in log2 units.
     S: [R, n] float64 scores (already scaled). v_deq: the tile's dequantized 4-bit V (else FP8 V).
-    p_fmt: "fp8" (P^ in E4M3) or "mxfp4" (P^ in MXFP4 over 32-key blocks; FP8 V only)."""
+    p_fmt: "fp8" (P^ in E4M3) or "mxfp4" (P^ in MXFP4 over 32-key blocks)."""
     X = np.where(unmasked, S * np.log2(np.e), -np.inf)
     has = unmasked.any(axis=1)
     r = np.where(has, np.ceil(X.max(axis=1, initial=-np.inf)), 0.0)
@@ -111,6 +113,9 @@ def _tile_terms(S, unmasked, sel, vq_vals, s_v, v_orig, round_p=True, v_deq=None
     if sel:
         Pt = bf16_round(P) if round_p else P
         T = Pt @ v_orig
+    elif v_deq is not None and p_fmt == "mxfp4":
+        Ph = mxfp4_rows(P) if round_p else P
+        T = Ph @ v_deq
     elif v_deq is not None:
         Ph = e4m3_decode(e4m3_encode(E4M3_MAX * P)) if round_p else E4M3_MAX * P
         T = (Ph @ v_deq) / E4M3_MAX
@@ -260,7 +265,10 @@ def rounding_slack(rows, q_rows, k_deq, v_codes, s_v, scale, Lq, Lk, causal,
             e = fold_exponent(float(np.max(s_v[cs])))
             w = s_v[cs].astype(np.float64) * 2.0 ** -e
             rnd, arg, vabs, unit = (lambda x: e4m3_decode(e4m3_encode(x))), P * w[None, :], np.abs(vq_vals[cs]), 2.0 ** e
-        if p_fmt == "mxfp4" and not sel and v_deq is None:
+        if p_fmt == "mxfp4" and not sel and v_deq is not None:
+            arg, vabs, unit = P, np.abs(v_deq[cs]), 1.0
+            delta = mxfp4_tie_delta(arg, np.where(unmasked, eps, 0.0))
+        elif p_fmt == "mxfp4" and not sel:
             delta = mxfp4_tie_delta(arg, np.where(unmasked, eps, 0.0))
         else:
             mid = rnd(arg)
@@ -311,7 +319,7 @@ def attention_prefill(q_deq, k_deq, v_codes, s_v, causal, scale=None,
     """O8 over a batch: q_deq [B, Hq, Lq, d]; k_deq [B, Hkv, Lk, d]; v_codes [B, Hkv, Lk, d]
     (E4M3 codes, token-major); s_v [B, Hkv, Lk]; optional originals (bf16 values as float64)
     and bitmap [B, Hq, nq, nk]; v_deq [B, Hkv, Lk, d]: dequantized 4-bit V instead of v_codes, s_v;
-    p_fmt: "fp8" or "mxfp4" (the probabilities of the unselected tiles; FP8 V).
+    p_fmt: "fp8" or "mxfp4" (the probabilities of the unselected tiles).
 
     rows: optional array of query rows to compute (default all); heads: optional
     list of (b, h) pairs (default all). Returns (O float32 [B, Hq, R, d],

@@ -145,8 +145,9 @@ def attention_rows(rows, Q, K, Vc, sv, Qo, Ko, Vo, sel, Lq, Lk, causal, scale, r
                    p_fmt="fp8"):
     """O8 by loops. Q/K: dequantized rows (lists); Vc: E4M3 codes; sv: per-key scales;
     Qo/Ko/Vo: original values for selected tiles; sel(i, j) -> bool. Vd: dequantized 4-bit V rows
-    (then P^ = E4M3(448 P), T = sum P^ v / 448, and Vc, sv are not used). p_fmt "mxfp4" (FP8 V): the
-    tile's P' w (masked keys 0) is MXFP4-quantized over blocks of 32 consecutive keys by mxfp4_row.
+    (then P^ = E4M3(448 P), T = sum P^ v / 448, and Vc, sv are not used). p_fmt "mxfp4": the tile's
+    P' w (FP8 V) or P' (4-bit V) is MXFP4-quantized over blocks of 32 consecutive keys by mxfp4_row
+    (masked keys 0), T = sum P^ v.
     Returns output rows."""
     off = Lk - Lq
     d = len((Vc if Vd is None else Vd)[0])
@@ -173,6 +174,12 @@ def attention_rows(rows, Q, K, Vc, sv, Qo, Ko, Vo, sel, Lq, Lk, causal, scale, r
                     p = bf16(P[c]) if round_p else P[c]
                     for t in range(d):
                         T[t] += p * Vo[c][t]
+            elif Vd is not None and p_fmt == "mxfp4" and round_p:
+                row = [P.get(c, 0.0) for c in range(128 * j, 128 * j + 128)]
+                vals = mxfp4_row_values(*mxfp4_row(row))
+                for c in cols:
+                    for t in range(d):
+                        T[t] += vals[c - 128 * j] * Vd[c][t]
             elif Vd is not None:
                 for c in cols:
                     p = e4m3_value(e4m3_encode(448.0 * P[c])) if round_p else 448.0 * P[c]

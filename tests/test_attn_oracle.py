@@ -455,3 +455,58 @@ def test_rounding_slack_mxfp4_block_scale_tie():
             delta[32 * b:32 * b + 32] = np.abs(coarse - fine)
     want = 2.0 ** e * (delta @ vals8) / 128.0
     assert delta.max() > 0 and np.allclose(sl[0], want, rtol=1e-12, atol=0)
+
+
+# ---- MXFP4 probabilities with 4-bit V: P' itself (no fold, no 448) in MXFP4 over 32 consecutive keys
+
+def test_v4_p4_bruteforce_online_causal_offset_with_selection():
+    cfg = SMALL_GQA_OFF.scaled(Hq=2, Hkv=1, Lq=128, Lk=384, qk_fmt="mxfp4", hadamard=False)
+    q, k, v, qd, kd, vc, sv = _prepare(cfg)
+    vd = _v4(v)
+    bitmap = np.zeros((1, 2, 1, 3), np.uint8); bitmap[0, 1, 0, 1] = 1
+    rows = np.array([0, 3, 64, 127])
+    O, _ = A.attention_prefill(qd, kd, None, None, True, q_orig=q, k_orig=k, v_orig=v, bitmap=bitmap, rows=rows,
+                               v_deq=vd, p_fmt="mxfp4")
+    O8, _ = A.attention_prefill(qd, kd, None, None, True, q_orig=q, k_orig=k, v_orig=v, bitmap=bitmap, rows=rows,
+                                v_deq=vd)
+    assert np.abs(O - O8).max() > 1e-3 * np.abs(O).max()
+    for h in range(2):
+        ref = bf.attention_rows(rows.tolist(), qd[0, h].tolist(), kd[0, 0].tolist(), None, None, q[0, h].tolist(),
+                                k[0, 0].tolist(), v[0, 0].tolist(), lambda i, j, h=h: bool(bitmap[0, h, i, j]), 128,
+                                384, True, 1 / np.sqrt(128), Vd=vd[0, 0].tolist(), p_fmt="mxfp4")
+        assert np.abs(O[0, h] - np.array(ref)).max() <= 1e-6 * np.abs(ref).max()
+        on, _ = A.attend_rows_online(rows, qd[0, h, rows], kd[0, 0], None, None, 1 / np.sqrt(128), 128, 384, True,
+                                     q_orig_rows=q[0, h, rows], k_orig=k[0, 0], v_orig=v[0, 0],
+                                     sel_row=bitmap[0, h, 0], tile_order=[2, 0, 1], v_deq=vd[0, 0], p_fmt="mxfp4")
+        assert np.abs(on - O[0, h]).max() <= 1e-6 * np.abs(O[0, h]).max()
+
+
+def test_v4_p4_without_rounding_is_sdpa_on_dequantized():
+    cfg = SMALL.scaled(Hq=1, Hkv=1, Lq=256, Lk=256)
+    q, k, v, qd, kd, vc, sv = _prepare(cfg)
+    vd = _v4(v)
+    O, _ = A.attention_prefill(qd, kd, None, None, True, round_p=False, v_deq=vd, p_fmt="mxfp4")
+    ref = _sdpa(qd, kd, vd, True, 1 / np.sqrt(128))
+    assert np.abs(O - ref).max() <= 1e-5 * np.abs(ref).max()
+
+
+def test_rounding_slack_v4_p4_block_scale_tie():
+    # 4-bit V: P' = 2^(x - r) with the row maximum 1 (x = 0, block 0) and block 1's maximum at 0.75 =
+    # 6 * 2^-3, a scale boundary (up to the float64 rounding of the scores). Block 1 also holds 0.1875, which
+    # the fine scale 2^-3 keeps (1.5) and the coarse scale 2^-2 puts on the midpoint 0.75 of 0.5 and 1, so
+    # either neighbour is 0.0625 away; every other key has P' = 2^-60, zero at any of these scales. The
+    # slack must be exactly that one change times |v| over the denominator.
+    from oracle import quant as Qm
+    d = 16
+    x = np.full(128, -60.0)
+    x[0] = 0.0
+    x[32] = np.log2(0.75)
+    x[33] = np.log2(0.1875)
+    rng = np.random.default_rng(8)
+    q = np.zeros((1, d)); q[0, 0] = 1.0
+    k = np.zeros((128, d)); k[:, 0] = x / np.log2(np.e)
+    vd = Qm.mxfp4_keys_dequantize(*Qm.mxfp4_keys_quantize(rng.standard_normal((128, d))))
+    sl = A.rounding_slack(np.array([0]), q, k, None, None, 1.0, 1, 128, False, v_deq=vd, p_fmt="mxfp4")
+    D = 1.0 + 0.75 + 0.1875 + 125 * 2.0 ** -60
+    want = 0.0625 * np.abs(vd[33]) / D
+    assert np.allclose(sl[0], want, rtol=1e-6, atol=0) and want.max() > 0
