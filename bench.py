@@ -17,7 +17,7 @@ one online softmax), inputs resident in HBM. Each timed loop follows W untimed s
                 share of that error the selected tiles remove;
   legs          the other prefill workloads (4K causal MXFP4; 128K chunked prefill with NVFP4 +
                 Hadamard and tile selection) and the 4K variants (4-bit V, MXFP8 Q/K, MXFP4
-                probabilities), each with its own roofline and error;
+                probabilities, and both), each with its own roofline and error;
   decode        the paged NVFP4 decode step (64 sequences, 32 -> 8 GQA heads, contexts 8K-32K):
                 KV-cache GB/s, the decode kernels' HBM roofline and the error;
   decode_mxfp4, decode_p4, decode_mxfp4_p4
@@ -74,13 +74,14 @@ KERNEL_SOURCES = {
     "attn_fwd_kernel<128, 0, true, true, false, false>": ATTN_SRC,
     "attn_fwd_kernel<128, 1, true, true, false, false>": ATTN_SRC,
     "attn_fwd_kernel<128, 0, true, false, false, true>": ATTN_SRC,
+    "attn_fwd_kernel<128, 0, true, false, true, true>": ATTN_SRC,
     "decode_split_kernel<1, 0>": DEC_SRC,
     "decode_split_kernel<0, 0>": DEC_SRC,
     "decode_split_kernel<1, 1>": DEC_SRC,
     "decode_split_kernel<0, 1>": DEC_SRC,
     "decode_mla_kernel": ["decode_mla.hip", "fa4_device.h"],
 }
-PREFILL = [W.C1, W.C2, W.C4, W.C1_MX8, W.C1_V4, W.C1_P4]
+PREFILL = [W.C1, W.C2, W.C4, W.C1_MX8, W.C1_V4, W.C1_P4, W.C1_V4P4]
 
 
 def attn_kernel_name(cfg, select):
@@ -258,10 +259,10 @@ def mixed_ceiling_tflops(cfg, bf16_frac):
     """The dense-MFMA ceiling of the workload's mix of products: half of the flops are QK^T at the Q/K
     format's rate (MXFP4 10.1 PF and MXFP8 5.0 PF, both with native block scales; NVFP4, whose E4M3
     scales on 16 elements the matrix cores do not take, at the fp16 rate 2.5 PF), half PV at the V/P
-    rate (FP8 5.0 PF; 4-bit V times FP8 P also runs at the FP8 rate), and the selected tiles' share of
-    both at the bf16 rate (2.5 PF)."""
+    rate (FP8 5.0 PF; 4-bit V times FP8 P and FP8 V times FP4 P also run at the FP8 rate, 4-bit V times
+    FP4 P at the FP4 rate), and the selected tiles' share of both at the bf16 rate (2.5 PF)."""
     qk = {"mxfp4": MXFP4_PEAK_TFLOPS, "nvfp4": BF16_PEAK_TFLOPS, "mxfp8": FP8_PEAK_TFLOPS}[cfg.qk_fmt]
-    pv = FP8_PEAK_TFLOPS
+    pv = MXFP4_PEAK_TFLOPS if (cfg.v_fmt == "mxfp4k" and cfg.p_fmt == "mxfp4") else FP8_PEAK_TFLOPS
     f = bf16_frac
     per_tflop = 0.5 * ((1 - f) / qk + f / BF16_PEAK_TFLOPS) + 0.5 * ((1 - f) / pv + f / BF16_PEAK_TFLOPS)
     return 1.0 / per_tflop
@@ -522,7 +523,7 @@ def main():
     }
     if not args.no_legs:
         line["legs"] = {}
-        for lcfg in (W.C1, W.C2, W.C4, W.C1_V4, W.C1_MX8, W.C1_P4):
+        for lcfg in (W.C1, W.C2, W.C4, W.C1_V4, W.C1_MX8, W.C1_P4, W.C1_V4P4):
             if lcfg.name != cfg.name:
                 line["legs"][lcfg.name] = prefill_record(fa4, lcfg, args)
     if not args.no_decode:

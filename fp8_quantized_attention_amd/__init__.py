@@ -260,7 +260,7 @@ def attn_fwd(q, k, v, causal, fmt, Hq, Hkv, Lq, Lk, d, B=1, bitmap=None, q_bf16=
 
     q/k hold MXFP4, NVFP4 or MXFP8 codes and scales; v holds FP8 per-token codes and scales
     (v_fmt FA4_FP8_TOKEN) or 4-bit V (v_fmt FA4_MXFP4_KEYS, MXFP4 Q/K only; selected tiles read v_bf16).
-    p_fmt: probabilities of the quantized tiles, FA4_P_FP8 or FA4_P_MXFP4 (MXFP4 Q/K, FP8 V, d = 128).
+    p_fmt: probabilities of the quantized tiles, FA4_P_FP8 or FA4_P_MXFP4 (MXFP4 Q/K, d = 128; FP8 or 4-bit V).
     Returns (o [B, Hq, Lq, d] float32, lse [B, Hq, Lq] float32 or None).
     """
     v4 = v_fmt == FA4_MXFP4_KEYS

@@ -300,7 +300,9 @@ __device__ __forceinline__ void fp8_block_w(const v16f &Skb, const float4 *w4, f
 }
 
 // MXFP4 probabilities: this lane's half of one 32-key block (keys 32 kb + 8 a4 + 4 hh + u, element
-// 4 a4 + u of Skb) becomes P' w_c in place; ts sums P' and am takes the largest P' w_c.
+// 4 a4 + u of Skb) becomes P' w_c in place (4-bit V: P' itself, nothing to fold); ts sums P' and am
+// takes the block's largest value.
+template <bool V4>
 __device__ __forceinline__ void p4_block_w(v16f &Skb, const float4 *w4, float cs, float rr0, float &ts, float &am) {
 #pragma unroll
   for (int a4 = 0; a4 < 4; a4++) {
@@ -309,7 +311,7 @@ __device__ __forceinline__ void p4_block_w(v16f &Skb, const float4 *w4, float cs
     for (int u = 0; u < 4; u++) {
       const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(Skb[4 * a4 + u], cs, -rr0));
       ts = (a4 == 0 && u == 0) ? p : ts + p;
-      Skb[4 * a4 + u] = p * wv[u];
+      Skb[4 * a4 + u] = V4 ? p : p * wv[u];
     }
   }
   am = block_max(Skb);
@@ -855,7 +857,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
             if constexpr (P4) {
               // MXFP4 P: P' w in place; after each pair of blocks, their FP4 operand (the next tile's QK^T
               // into those registers waits for it)
-              p4_block_w(S[r], w4, cs, rr0, ts[r], am[r & 1]);
+              p4_block_w<V4>(S[r], w4, cs, rr0, ts[r], am[r & 1]);
               if (r & 1) pop[r >> 1] = p4_operand(S[r - 1], S[r], am[0], am[1], hh, kBc, psb[r >> 1]);
             } else {
               int x0, x1, x2, x3;
@@ -877,7 +879,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
             for (int mb = 0; mb < 4; mb++) {
               if constexpr (V4)
-                acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vpend[mb], ppend, acc[mb], 4, 0, 2, vspend[mb], 0,
+                acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vpend[mb], ppend, acc[mb], 4, P4 ? 4 : 0, 2, vspend[mb], 0,
                                                                           kpend + 127);
               else
                 acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vpend[mb], ppend, acc[mb], 0, P4 ? 4 : 0, 0, spend,
@@ -889,7 +891,10 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
             if (r == 2) {
 #pragma unroll
               for (int mb = 0; mb < 4; mb++) {
-                if constexpr (V4)
+                if constexpr (V4 && P4)
+                  acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[mb], pop[0], acc[mb], 4, 4, 0, vsw[mb], 0,
+                                                                            psb[0]);
+                else if constexpr (V4)
                   acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[mb], pop[0], acc[mb], 4, 0, 0, vsw[mb], 0,
                                                                             kBc + 127);
                 else if constexpr (P4)
@@ -939,7 +944,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
         kpend = P4 ? psb[1] - 127 : kBc;
         spend = scA;
         const float tsum = (ts[0] + ts[1]) + (ts[2] + ts[3]);
-        lsum += __builtin_ldexpf(V4 ? tsum * (1.0f / 448.0f) : tsum, kB);
+        lsum += __builtin_ldexpf(V4 && !P4 ? tsum * (1.0f / 448.0f) : tsum, kB);
         if (!has_next) break;
         float mS;
         if (diag_next) {
@@ -966,7 +971,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int mb = 0; mb < 4; mb++) {
         if constexpr (V4)
-          acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vpend[mb], ppend, acc[mb], 4, 0, 2, vspend[mb], 0,
+          acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vpend[mb], ppend, acc[mb], 4, P4 ? 4 : 0, 2, vspend[mb], 0,
                                                                     kpend + 127);
         else
           acc[mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vpend[mb], ppend, acc[mb], 0, P4 ? 4 : 0, 0, spend, 0,
@@ -1114,7 +1119,7 @@ __global__ void __launch_bounds__(ATT_THREADS, 2) attn_fwd_kernel(AttnArgs a) {
       FA4_TILE_STEP(true, false, kt, nullptr, nullptr, vbuf_of(vb), w_of(vb));
     }
   }
-  if constexpr (V4) {
+  if constexpr (V4 && !P4) {
     // 4-bit V: the quantized tiles' P^ carried a factor 448 (their sums did not); bf16 tiles carry none
 #pragma unroll
     for (int i = 0; i < NDB; i++) acc[i] *= 1.0f / 448.0f;
@@ -1220,6 +1225,21 @@ static hipError_t launch_attn_v4(const AttnArgs &x, bool causal, bool sel, hipSt
   if (causal) return sel ? launch_attn_v4_t<true, true>(x, s) : launch_attn_v4_t<true, false>(x, s);
   return sel ? launch_attn_v4_t<false, true>(x, s) : launch_attn_v4_t<false, false>(x, s);
 }
+// 4-bit V with MXFP4 probabilities: FP4 V^T x FP4 P^T
+template <bool CAUSAL, bool SEL>
+static hipError_t launch_attn_v4p4_t(const AttnArgs &x, hipStream_t s) {
+  dim3 grid((unsigned)((int64_t)(x.Lq / 128) * x.Hq * x.B));
+  hipError_t e = allow_lds<128, FA4_MXFP4, CAUSAL, SEL, true, true>();
+  if (e != hipSuccess) return e;
+  constexpr size_t lds_bytes = AttnLds<128, FA4_MXFP4, SEL>::BYTES;
+  hipLaunchKernelGGL((attn_fwd_kernel<128, FA4_MXFP4, CAUSAL, SEL, true, true>), grid, dim3(ATT_THREADS), lds_bytes,
+                     s, x);
+  return hipGetLastError();
+}
+static hipError_t launch_attn_v4p4(const AttnArgs &x, bool causal, bool sel, hipStream_t s) {
+  if (causal) return sel ? launch_attn_v4p4_t<true, true>(x, s) : launch_attn_v4p4_t<true, false>(x, s);
+  return sel ? launch_attn_v4p4_t<false, true>(x, s) : launch_attn_v4p4_t<false, false>(x, s);
+}
 
 // MXFP4 Q/K, FP8 V, MXFP4 probabilities (d = 128)
 template <bool CAUSAL, bool SEL>
@@ -1268,7 +1288,8 @@ hipError_t launch_attn(const fa4_attn_args *p, hipStream_t s) {
   x.o = p->o; x.lse = p->lse;
   if (x.B == 0 || x.Hq == 0 || x.Lq == 0) return hipSuccess;
   const bool causal = p->causal != 0, sel = p->bitmap != nullptr;
-  if (p->v_fmt == FA4_MXFP4_KEYS) return launch_attn_v4(x, causal, sel, s);
+  if (p->v_fmt == FA4_MXFP4_KEYS)
+    return p->p_fmt == FA4_P_MXFP4 ? launch_attn_v4p4(x, causal, sel, s) : launch_attn_v4(x, causal, sel, s);
   if (p->p_fmt == FA4_P_MXFP4) return launch_attn_p4(x, causal, sel, s);
   if (p->fmt == FA4_MXFP4) {
     if (p->d == 64) return launch_attn_t<64, FA4_MXFP4>(x, causal, false, s);

@@ -230,8 +230,7 @@ fa4_status fa4_attn_fwd(const fa4_attn_args *a, void *stream) {
   REQUIRE(a->p_fmt == FA4_P_FP8 || a->p_fmt == FA4_P_MXFP4, FA4_ERR_UNSUPPORTED, "attn: probability format %d",
           a->p_fmt);
   if (a->p_fmt == FA4_P_MXFP4)
-    REQUIRE(a->fmt == FA4_MXFP4 && a->d == 128 && !v4, FA4_ERR_UNSUPPORTED,
-            "attn: MXFP4 probabilities need MXFP4 Q/K, FP8 V and d=128");
+    REQUIRE(a->fmt == FA4_MXFP4 && a->d == 128, FA4_ERR_UNSUPPORTED, "attn: MXFP4 probabilities need MXFP4 Q/K and d=128");
   if (a->B == 0 || a->Lq == 0) return ok();
   if (v4)
     REQUIRE(a->q_codes && a->q_scales && a->k_codes && a->k_scales && a->v_codes && a->v_block_scales && a->o,

@@ -221,12 +221,14 @@ fa4_status fa4_select_tiles(const float *q_norm2, const float *k_norm2, int32_t 
  * fa4_quantize_blockscaled's FA4_MXFP4_KEYS output; v_scales and v_fold_* are not read. Quantized tiles
  * then take P^ = E4M3(448 P') and T = (1/448) sum_c P^ v^_c with the dequantized 4-bit values v^ (FP4
  * V^T times FP8 P^T in one block-scaled MFMA); selected tiles (with a bitmap) read v_bf16 as usual.
- * FP4 probabilities (p_fmt = FA4_P_MXFP4; MXFP4 Q/K, FP8 V, d = 128; "BitDecoding-FP4": probabilities
+ * FP4 probabilities (p_fmt = FA4_P_MXFP4; MXFP4 Q/K, d = 128; "BitDecoding-FP4": probabilities
  * in FP4 under a scale that cannot underflow, "MXFP vs NVFP4" section 2.1: the MX block): in each
  * unselected tile row, P' w_c over 32 consecutive keys (keys 128 j + 32 b .. + 31) is one MXFP4 block:
  * 2^e_b = the smallest power of two with 6 * 2^e_b >= its largest P' w, P^ = E2M1(P' w 2^-e_b) 2^e_b,
  * T = 2^e * sum_c P^ * E4M3value(Vcode_c) (FP8 V^T times FP4 P^T in one block-scaled MFMA, e_b and the
- * tile weight as P^T's E8M0 operand scale). p_fmt = 0 (FA4_P_FP8) keeps the FP8 probabilities above.
+ * tile weight as P^T's E8M0 operand scale). With 4-bit V the block is P' itself (nothing to fold, no 448)
+ * and T = sum_c P^ v^_c: FP4 V^T times FP4 P^T, both block scales inside the product. p_fmt = 0
+ * (FA4_P_FP8) keeps the FP8 probabilities above.
  */
 typedef struct {
   int32_t fmt;                                  /* FA4_MXFP4, FA4_NVFP4 or FA4_MXFP8 (Q and K) */

@@ -195,7 +195,8 @@ def test_attention_rejects_before_launch():
     # MXFP4 probabilities: MXFP4 Q/K, FP8 V, d = 128 (validated before the empty-shape early return)
     assert call(_attn(p_fmt=fa4.FA4_P_NVFP4)) == fa4.FA4_ERR_UNSUPPORTED
     assert call(_attn(p_fmt=9)) == fa4.FA4_ERR_UNSUPPORTED
-    assert call(_attn(p_fmt=fa4.FA4_P_MXFP4, **v4)) == fa4.FA4_ERR_UNSUPPORTED
+    assert call(_attn(p_fmt=fa4.FA4_P_MXFP4, **v4, Lq=0)) == fa4.FA4_OK         # 4-bit V x FP4 P
+    assert call(_attn(p_fmt=fa4.FA4_P_MXFP4, **v4, d=64)) == fa4.FA4_ERR_UNSUPPORTED
     assert call(_attn(p_fmt=fa4.FA4_P_MXFP4, fmt=fa4.FA4_NVFP4, q_tscale=256, k_tscale=256)) == fa4.FA4_ERR_UNSUPPORTED
     assert call(_attn(p_fmt=fa4.FA4_P_MXFP4, fmt=fa4.FA4_MXFP8)) == fa4.FA4_ERR_UNSUPPORTED
     assert call(_attn(p_fmt=fa4.FA4_P_MXFP4, d=64)) == fa4.FA4_ERR_UNSUPPORTED

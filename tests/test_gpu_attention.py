@@ -334,3 +334,23 @@ def test_full_size_prefill_4k_p4(fa4):
 
 def test_full_size_prefill_32k_p4_selection(fa4):
     _sampled(fa4, W.C2.scaled(p_fmt="mxfp4"), heads=[(0, 9)], nrows=16, select=(5, 100))
+
+
+# ---- 4-bit V with MXFP4 probabilities (FP4 V^T x FP4 P^T, both block scales inside the product)
+
+def test_v4p4_causal_small(fa4):
+    _check_full(fa4, W.C1_V4P4.scaled(Hq=2, Hkv=2, Lq=512, Lk=512))
+
+
+@pytest.mark.parametrize("causal", [True, False], ids=["causal", "noncausal"])
+def test_v4p4_gqa_offset(fa4, causal):
+    _check_full(fa4, W.C1_V4P4.scaled(Hq=4, Hkv=2, Lq=256, Lk=768, causal=causal), seed=1)
+
+
+@pytest.mark.parametrize("select", [(5, 100), (100, 100)], ids=["sel5", "all"])
+def test_v4p4_with_selection(fa4, select):
+    _check_full(fa4, W.C1_V4P4.scaled(Hq=2, Hkv=2, Lq=512, Lk=512), select=select)
+
+
+def test_full_size_prefill_4k_v4p4(fa4):
+    _sampled(fa4, W.C1_V4P4, heads=[(0, 4), (0, 30)], nrows=96, select=None)

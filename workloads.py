@@ -95,6 +95,8 @@ C1_MX8 = replace(C1, name="prefill_4k_causal_mxfp8", qk_fmt="mxfp8")
 C1_V4 = replace(C1, name="prefill_4k_causal_mxfp4_v4", v_fmt="mxfp4k")
 # The 4K causal prefill with the probabilities in MXFP4 (E8M0 scale per 32 keys) against FP8 V: same values.
 C1_P4 = replace(C1, name="prefill_4k_causal_mxfp4_p4", p_fmt="mxfp4")
+# 4-bit V and MXFP4 probabilities together (both PV operands FP4, block-scaled along the keys): same values.
+C1_V4P4 = replace(C1_V4, name="prefill_4k_causal_mxfp4_v4p4", p_fmt="mxfp4")
 # The decode workload over an MXFP4 cache (E8M0 scale per 32 elements, no tensor scale): the same
 # sequences, lengths, pages and values as C3 (same workload id, hence the same seeds).
 C3_MX = replace(C3, name="decode_paged_mxfp4_gqa", kv_fmt="mxfp4")
