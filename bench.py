@@ -66,7 +66,7 @@ CSRC = os.path.join(ROOT, "fp8_quantized_attention_amd", "csrc")
 # Kernel instantiations whose counters are recorded, with the sources whose change invalidates them.
 # Attention kernel: <d, Q/K format (0 MXFP4, 1 NVFP4, 3 MXFP8), causal, selection, 4-bit V, MXFP4 P>
 # (MXFP4 without selection: 4K causal; MXFP4 with selection: 32K; NVFP4 with selection: the 128K
-# chunked prefill; MXFP4 probabilities: 4K causal). Decode: <cache format (1 NVFP4, 0 MXFP4), probability format (0 FP8, 1 NVFP4)>.
+# chunked prefill; MXFP4 probabilities, 4-bit V, both, and MXFP8: 4K causal). Decode: <cache format (1 NVFP4, 0 MXFP4), probability format (0 FP8, 1 NVFP4)>.
 ATTN_SRC = ["attn_fwd.hip", "fa4_device.h"]
 DEC_SRC = ["decode.hip", "fa4_device.h"]
 KERNEL_SOURCES = {
@@ -75,6 +75,8 @@ KERNEL_SOURCES = {
     "attn_fwd_kernel<128, 1, true, true, false, false>": ATTN_SRC,
     "attn_fwd_kernel<128, 0, true, false, false, true>": ATTN_SRC,
     "attn_fwd_kernel<128, 0, true, false, true, true>": ATTN_SRC,
+    "attn_fwd_kernel<128, 0, true, false, true, false>": ATTN_SRC,
+    "attn_fwd_kernel<128, 3, true, false, false, false>": ATTN_SRC,
     "decode_split_kernel<1, 0>": DEC_SRC,
     "decode_split_kernel<0, 0>": DEC_SRC,
     "decode_split_kernel<1, 1>": DEC_SRC,
