@@ -267,35 +267,42 @@ def _jump_inputs(causal, factors, seed=31):
                          ids=["raise_once", "raise_past_smallest_weight"])
 @pytest.mark.parametrize("select", [None, (25, 100)])
 @pytest.mark.parametrize("p4", [False, True], ids=["p8", "p4"])
-def test_reference_jumps(fa4, causal, factors, select, p4):
+@pytest.mark.parametrize("v4", [False, True], ids=["v8", "v4"])
+def test_reference_jumps(fa4, causal, factors, select, p4, v4):
     # p4: MXFP4 probabilities, whose per-block E8M0 scale carries the tile weight (and the pending half's
-    # weight follows a raised reference)
+    # weight follows a raised reference); v4: 4-bit V (its 448 and its division with FP8 probabilities)
     from oracle import quant as Q
     from oracle import selection as S
     q, k, v = _jump_inputs(causal, factors)
     L = q.shape[2]
     pf = "mxfp4" if p4 else "fp8"
     res = fa4.prefill(q.cuda(), k.cuda(), v.cuda(), causal, fmt=fa4.FA4_MXFP4, select=select,
-                      p_fmt=fa4.FA4_P_MXFP4 if p4 else fa4.FA4_P_FP8)
+                      p_fmt=fa4.FA4_P_MXFP4 if p4 else fa4.FA4_P_FP8,
+                      v_fmt=fa4.FA4_MXFP4_KEYS if v4 else fa4.FA4_FP8_TOKEN)
     torch.cuda.synchronize()
     qd, kd, vd = (t.double().numpy() for t in (q, k, v))
     qq = Q.mxfp4_dequantize(*Q.mxfp4_quantize(qd))
     kk = Q.mxfp4_dequantize(*Q.mxfp4_quantize(kd))
-    vc, sv = Q.fp8_per_token_quantize(vd)
+    if v4:
+        vc, sv = None, None
+        v_deq = Q.mxfp4_keys_dequantize(*Q.mxfp4_keys_quantize(vd))
+    else:
+        (vc, sv), v_deq = Q.fp8_per_token_quantize(vd), None
     bm = None
     if select is not None:
         bm, _ = S.select_tiles(Q.row_norm2(qd), Q.row_norm2(kd), L, L, causal, *select)
         assert np.array_equal(res["bitmap"].cpu().numpy(), bm)
-    O, lse = A.attention_prefill(qq, kk, vc, sv, causal, q_orig=qd, k_orig=kd, v_orig=vd, bitmap=bm, p_fmt=pf)
+    O, lse = A.attention_prefill(qq, kk, vc, sv, causal, q_orig=qd, k_orig=kd, v_orig=vd, bitmap=bm, p_fmt=pf,
+                                 v_deq=v_deq)
     # Conditioning of this input: scores reach ~230 in log2 units, where the float32 rounding of the
     # exponent's argument (2^-24 relative) already flips bf16 and E4M3 probability codes of rows that one
     # key dominates. The oracle itself, with its softmax scale moved by one float32 ulp, differs by
     # delta; the max-abs bound is max(2e-3, 2 delta), the relative-L2 bound stays 1e-3.
     O1, _ = A.attention_prefill(qq, kk, vc, sv, causal, scale=(1.0 + 2.0 ** -23) / np.sqrt(128), q_orig=qd,
-                                k_orig=kd, v_orig=vd, bitmap=bm, p_fmt=pf)
+                                k_orig=kd, v_orig=vd, bitmap=bm, p_fmt=pf, v_deq=v_deq)
     _, delta = rel_errors(O1, O)
     rel, mx = rel_errors(res["o"].cpu().numpy(), O)
-    what = f"jumps {factors} causal={causal} select={select} p={pf}"
+    what = f"jumps {factors} causal={causal} select={select} p={pf} v4={v4}"
     assert rel <= 1e-3 and mx <= max(2e-3, 2 * delta), f"{what}: rel-L2 {rel:.3e} max-abs/max {mx:.3e} (delta {delta:.2e})"
     # LSE: the scores themselves are float32 sums of 128 products here reaching ~1e4, so their rounding
     # (about 2^-23 of sum |q_i k_i| per score, in units of the softmax scale) bounds the LSE agreement
