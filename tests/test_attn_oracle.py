@@ -510,3 +510,65 @@ def test_rounding_slack_v4_p4_block_scale_tie():
     D = 1.0 + 0.75 + 0.1875 + 125 * 2.0 ** -60
     want = 0.0625 * np.abs(vd[33]) / D
     assert np.allclose(sl[0], want, rtol=1e-6, atol=0) and want.max() > 0
+
+
+def _fp32_prefill_rows_p4(rows, qd, kd, vc, sv, scale, Lq, Lk):
+    """As _fp32_prefill_rows (not causal) with MXFP4 probabilities: P' w evaluated in float32 and quantized
+    by the loop brute force over 32-key blocks; also counts the blocks whose scale differs from float64's."""
+    f32 = np.float32
+    vals = np.vectorize(bf.e4m3_value)(vc).astype(np.float64)
+    terms, scale_flips = [], 0
+    for j in range(Lk // 128):
+        cs = np.arange(128 * j, 128 * j + 128)
+        S = (qd[rows].astype(f32) @ kd[cs].astype(f32).T) * f32(scale * np.log2(np.e))
+        X = S.astype(np.float64)
+        r = np.ceil(X.max(axis=1))
+        P = np.exp2((X - r[:, None]).astype(f32)).astype(f32).astype(np.float64)
+        e = A.fold_exponent(float(sv[cs].max()))
+        w = sv[cs].astype(np.float64) * 2.0 ** -e
+        pw32 = (P * w[None, :]).astype(f32).astype(np.float64)
+        X64 = scale * (qd[rows] @ kd[cs].T) * np.log2(np.e)
+        pw64 = np.exp2(X64 - np.ceil(X64.max(axis=1))[:, None]) * w[None, :]
+        Ph = np.zeros_like(pw32)
+        for i in range(len(rows)):
+            codes, scs = bf.mxfp4_row(pw32[i].tolist())
+            Ph[i] = bf.mxfp4_row_values(codes, scs)
+            scale_flips += sum(int(a != b) for a, b in zip(scs, bf.mxfp4_row(pw64[i].tolist())[1]))
+        terms.append((r, P.sum(axis=1), 2.0 ** e * (Ph @ vals[cs])))
+    m = np.max([t[0] for t in terms], axis=0)
+    num, den = 0.0, 0.0
+    for r, l, T in terms:
+        f = np.exp2(r - m)
+        num, den = num + f[:, None] * T, den + f * l
+    return num / den[:, None], scale_flips
+
+
+def test_rounding_slack_mxfp4_covers_an_fp32_evaluation():
+    # Block-scale ties planted where they matter: for 32 rows, the V scale of the row's largest-probability
+    # key in tile 0 is set so that its P' w lands on 6 * 2^k, a block-scale boundary (to within the float32
+    # rounding of the scale). A float32 evaluation then takes the other scale for some of those blocks, which
+    # requantizes the whole block; the oracle's O plus its slack must still cover the result.
+    cfg = W.C1.scaled(Hq=1, Hkv=1, Lq=128, Lk=256, causal=False)
+    _, _, _, qd, kd, vc, sv = _prepare(cfg)
+    qd, kd, vc, sv = qd[0, 0], kd[0, 0], vc[0, 0], sv[0, 0].copy()
+    scale, rows = 1 / np.sqrt(128), np.arange(128)
+    X = scale * (qd @ kd[:128].T) * np.log2(np.e)
+    P = np.exp2(X - np.ceil(X.max(axis=1))[:, None])
+    e = A.fold_exponent(float(sv[:128].max()))
+    planted = set()
+    for row in range(0, 128, 4):
+        c = int(np.argmax(P[row]))
+        pw = P[row, c] * float(sv[c]) * 2.0 ** -e
+        k = int(np.floor(np.log2(pw / 6.0)))
+        s_new = np.float32(6.0 * 2.0 ** k / P[row, c] * 2.0 ** e)
+        if c in planted or s_new > sv[:128].max():
+            continue
+        sv[c] = s_new
+        planted.add(c)
+    assert A.fold_exponent(float(sv[:128].max())) == e and len(planted) >= 16
+    O, _ = A.attend_rows(rows, qd, kd, vc, sv, scale, 128, 256, False, p_fmt="mxfp4")
+    sl = A.rounding_slack(rows, qd, kd, vc, sv, scale, 128, 256, False, p_fmt="mxfp4")
+    O32, scale_flips = _fp32_prefill_rows_p4(rows, qd, kd, vc, sv, scale, 128, 256)
+    dif = np.abs(O32 - O)
+    assert scale_flips >= 1 and dif.max() > 1e-3 * np.abs(O).max()     # the flips move O well past noise
+    assert np.all(dif <= sl + 1e-5 * np.abs(O).max())
