@@ -361,3 +361,13 @@ def test_v4p4_with_selection(fa4, select):
 
 def test_full_size_prefill_4k_v4p4(fa4):
     _sampled(fa4, W.C1_V4P4, heads=[(0, 4), (0, 30)], nrows=96, select=None)
+
+
+@pytest.mark.parametrize("cfg", [W.C1_P4, W.C1_V4P4], ids=["p4", "v4p4"])
+def test_p4_deterministic(fa4, cfg):
+    """The MXFP4-probability kernels give bitwise the same output on a rerun (no atomics or order-dependent
+    sums in the attention kernel)."""
+    c = cfg.scaled(Hq=4, Hkv=2, Lq=1024, Lk=1024)
+    (_, _, _), r1 = _run(fa4, c, select=(5, 100))
+    (_, _, _), r2 = _run(fa4, c, select=(5, 100))
+    assert torch.equal(r1["o"], r2["o"]) and torch.equal(r1["lse"], r2["lse"])
